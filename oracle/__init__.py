@@ -1,0 +1,305 @@
+"""CPU oracle for SageAttention-style quantized attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never loads it and
+shares no code with it.
+
+This module is bookkeeping only: it builds/loads ``liboracle.so`` (the plain C
+reference in ``sage_oracle.c``), cuts heads out of HND/NHD tensors and passes
+them to the C functions, which do all of the method's arithmetic.
+
+Layouts: ``HND`` = [B, H, S, D], ``NHD`` = [B, S, H, D] ("完整指南" page,
+section 五分钟跑通第一个加速样例: tensor_layout).  Inputs are the raw 16-bit
+codes (``numpy.uint16``) of fp16 or bf16 tensors, exactly the bytes uploaded to
+the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sage_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16 = 0, 1
+PV_FP8, PV_FP16 = 0, 1
+DTYPES = {"fp16": F16, "bf16": BF16}
+CFLAGS = ["-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so from sage_oracle.c (always recompiles)."""
+    tmp = _SO + ".tmp"
+    cmd = ["gcc"] + CFLAGS + [_SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    os.replace(tmp, _SO)
+    return _SO
+
+
+def _p(a, ct):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def lib():
+    """Load liboracle.so, building it first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        L.orc_e4m3_decode.restype = ctypes.c_float
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        for name in ("orc_decode16", "orc_encode16", "orc_e4m3_encode_n", "orc_int8_quant_block",
+                     "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_v_head",
+                     "orc_qk_int32_head", "orc_attn_head_rows", "orc_attn_exact_head"):
+            getattr(L, name).restype = None
+        _lib = L
+    return _lib
+
+
+class use_library:
+    """Context manager: route every call in this module to another build of the
+    oracle source (the test suite uses it to run the pins against copies of the
+    oracle with a deliberately planted mistake)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = None
+        saved_so = globals()["_SO"]
+        globals()["_SO"] = self.path
+        try:
+            lib()
+        finally:
+            globals()["_SO"] = saved_so
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def build_variant(src: str, out_so: str) -> str:
+    """Compile another copy of the oracle source with the same flags."""
+    subprocess.run(["gcc"] + CFLAGS + ["-I", _HERE, src, "-o", out_so, "-lm"], check=True)
+    return out_so
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- formats
+def decode16(codes: np.ndarray, dtype: int) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint16)
+    out = np.empty(c.shape, np.float32)
+    lib().orc_decode16(_p(c, ctypes.c_uint16), ctypes.c_size_t(c.size), dtype, _p(out, ctypes.c_float))
+    return out
+
+
+def encode16(x: np.ndarray, dtype: int) -> np.ndarray:
+    x = _f32(x)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_encode16(_p(x, ctypes.c_float), ctypes.c_size_t(x.size), dtype, _p(out, ctypes.c_uint16))
+    return out
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib().orc_e4m3_decode(int(v)) for v in c.ravel()], np.float32).reshape(c.shape)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    x = _f32(x)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode_n(_p(x, ctypes.c_float), ctypes.c_size_t(x.size), _p(out, ctypes.c_uint8))
+    return out
+
+
+def int8_quant_block(x: np.ndarray):
+    x = _f32(x)
+    codes = np.empty(x.shape, np.int8)
+    scale = ctypes.c_float()
+    lib().orc_int8_quant_block(_p(x, ctypes.c_float), ctypes.c_size_t(x.size), _p(codes, ctypes.c_int8),
+                               ctypes.byref(scale))
+    return codes, np.float32(scale.value)
+
+
+def channel_mean(x: np.ndarray) -> np.ndarray:
+    x = _f32(x)
+    S, D = x.shape
+    out = np.empty(D, np.float32)
+    lib().orc_channel_mean(_p(x, ctypes.c_float), S, D, _p(out, ctypes.c_float))
+    return out
+
+
+# ---------------------------------------------------------------- per head
+def head(x: np.ndarray, layout: str, b: int, h: int) -> np.ndarray:
+    """Return head (b, h) of a physical HND/NHD tensor as a contiguous [S, D] array."""
+    if layout == "HND":
+        return np.ascontiguousarray(x[b, h])
+    if layout == "NHD":
+        return np.ascontiguousarray(x[b, :, h, :])
+    raise ValueError(layout)
+
+
+def quant_q_head(qf: np.ndarray, blk: int):
+    qf = _f32(qf)
+    S, D = qf.shape
+    codes = np.empty((S, D), np.int8)
+    scales = np.empty((S + blk - 1) // blk, np.float32)
+    lib().orc_quant_q_head(_p(qf, ctypes.c_float), S, D, blk, _p(codes, ctypes.c_int8), _p(scales, ctypes.c_float))
+    return codes, scales
+
+
+def quant_k_head(kf: np.ndarray, blk: int, smooth: bool = True):
+    kf = _f32(kf)
+    S, D = kf.shape
+    codes = np.empty((S, D), np.int8)
+    scales = np.empty((S + blk - 1) // blk, np.float32)
+    mean = np.empty(D, np.float32)
+    lib().orc_quant_k_head(_p(kf, ctypes.c_float), S, D, blk, int(smooth), _p(codes, ctypes.c_int8),
+                           _p(scales, ctypes.c_float), _p(mean, ctypes.c_float))
+    return codes, scales, mean
+
+
+def quant_v_head(vf: np.ndarray):
+    vf = _f32(vf)
+    S, D = vf.shape
+    codes = np.empty((S, D), np.uint8)
+    scales = np.empty(D, np.float32)
+    lib().orc_quant_v_head(_p(vf, ctypes.c_float), S, D, _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_float))
+    return codes, scales
+
+
+def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
+    q8 = np.ascontiguousarray(q8, np.int8)
+    k8 = np.ascontiguousarray(k8, np.int8)
+    S, D = q8.shape
+    out = np.empty((S, S), np.int32)
+    lib().orc_qk_int32_head(_p(q8, ctypes.c_int8), _p(k8, ctypes.c_int8), S, D, _p(out, ctypes.c_int32))
+    return out
+
+
+def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
+                   pv_mode, rows=None, blk_q=32, blk_k=64) -> np.ndarray:
+    """Quantized attention for the given query rows of one head (fp32 [len(rows), D])."""
+    S, D = q8.shape
+    rows = np.arange(S, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    out = np.empty((rows.size, D), np.float32)
+    q8 = np.ascontiguousarray(q8, np.int8)
+    k8 = np.ascontiguousarray(k8, np.int8)
+    q_scale = _f32(q_scale)
+    k_scale = _f32(k_scale)
+    v8 = np.ascontiguousarray(v8 if v8 is not None else np.zeros((S, D), np.uint8), np.uint8)
+    v_scale = _f32(v_scale if v_scale is not None else np.zeros(D, np.float32))
+    vf = _f32(vf if vf is not None else np.zeros((S, D), np.float32))
+    lib().orc_attn_head_rows(_p(q8, ctypes.c_int8), _p(q_scale, ctypes.c_float), blk_q,
+                             _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k,
+                             _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float), _p(vf, ctypes.c_float),
+                             in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
+                             _p(rows, ctypes.c_int), rows.size, _p(out, ctypes.c_float))
+    return out
+
+
+def attn_exact_head(qf, kf, vf, *, is_causal, sm_scale, rows=None) -> np.ndarray:
+    qf, kf, vf = _f32(qf), _f32(kf), _f32(vf)
+    S, D = qf.shape
+    rows = np.arange(S, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    out = np.empty((rows.size, D), np.float64)
+    lib().orc_attn_exact_head(_p(qf, ctypes.c_float), _p(kf, ctypes.c_float), _p(vf, ctypes.c_float), S, D,
+                              int(bool(is_causal)), ctypes.c_double(sm_scale), _p(rows, ctypes.c_int), rows.size,
+                              _p(out, ctypes.c_double))
+    return out
+
+
+# ---------------------------------------------------------------- whole tensors
+def smooth_quant_qk(q, k, dtype: int, layout: str, blk_q: int = 32, blk_k: int = 64, smooth: bool = True):
+    """Quantise physical Q, K (uint16 codes) -> logical [B,H,S,D] codes + scales + K means."""
+    B, H, S, D = logical_shape(q.shape, layout)
+    nq, nk = (S + blk_q - 1) // blk_q, (S + blk_k - 1) // blk_k
+    q8 = np.empty((B, H, S, D), np.int8)
+    k8 = np.empty((B, H, S, D), np.int8)
+    qs = np.empty((B, H, nq), np.float32)
+    ks = np.empty((B, H, nk), np.float32)
+    km = np.empty((B, H, D), np.float32)
+    for b in range(B):
+        for h in range(H):
+            q8[b, h], qs[b, h] = quant_q_head(decode16(head(q, layout, b, h), dtype), blk_q)
+            k8[b, h], ks[b, h], km[b, h] = quant_k_head(decode16(head(k, layout, b, h), dtype), blk_k, smooth)
+    return q8, qs, k8, ks, km
+
+
+def quant_v(v, dtype: int, layout: str):
+    """Quantise physical V (uint16 codes) -> logical [B,H,S,D] E4M3 codes + [B,H,D] scales."""
+    B, H, S, D = logical_shape(v.shape, layout)
+    v8 = np.empty((B, H, S, D), np.uint8)
+    vs = np.empty((B, H, D), np.float32)
+    for b in range(B):
+        for h in range(H):
+            v8[b, h], vs[b, h] = quant_v_head(decode16(head(v, layout, b, h), dtype))
+    return v8, vs
+
+
+def default_sm_scale(D: int) -> float:
+    """1/sqrt(D) rounded once to fp32 (the usual softmax temperature)."""
+    return float(np.float32(1.0 / np.sqrt(np.float64(D))))
+
+
+def logical_shape(shape, layout):
+    if layout == "HND":
+        return tuple(shape)
+    B, S, H, D = shape
+    return B, H, S, D
+
+
+def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
+         heads=None, rows=None, blk_q=32, blk_k=64, smooth=True):
+    """Full pipeline (smooth + quantise + attention) for the given heads/rows.
+
+    Returns {(b, h): fp32 [len(rows), D]}; rows default to all S rows.
+    """
+    B, H, S, D = logical_shape(q.shape, layout)
+    if sm_scale is None:
+        sm_scale = default_sm_scale(D)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    res = {}
+    for (b, h) in heads:
+        qf = decode16(head(q, layout, b, h), dtype)
+        kf = decode16(head(k, layout, b, h), dtype)
+        vf = decode16(head(v, layout, b, h), dtype)
+        q8, qs = quant_q_head(qf, blk_q)
+        k8, ks, _ = quant_k_head(kf, blk_k, smooth)
+        if pv_mode == PV_FP8:
+            v8, vs = quant_v_head(vf)
+        else:
+            v8, vs = None, None
+        res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
+                                     sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k)
+    return res
+
+
+def attn_exact(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, heads=None, rows=None):
+    B, H, S, D = logical_shape(q.shape, layout)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    res = {}
+    for (b, h) in heads:
+        res[(b, h)] = attn_exact_head(decode16(head(q, layout, b, h), dtype), decode16(head(k, layout, b, h), dtype),
+                                      decode16(head(v, layout, b, h), dtype), is_causal=is_causal,
+                                      sm_scale=sm_scale, rows=rows)
+    return res

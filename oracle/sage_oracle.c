@@ -1,0 +1,373 @@
+/*
+ * sage_oracle.c -- plain, slow, step-by-step CPU reference for SageAttention-
+ * style quantized attention.  TEST INFRASTRUCTURE ONLY (see sage_oracle.h):
+ * nothing in the product path may load or call it.
+ *
+ * Each function follows one step of the method in the order the pages give it;
+ * there is no tiling, fusion or reordering beyond what the method itself
+ * states.  The one blocking that IS part of the method -- FlashAttention-style
+ * key blocks with an online softmax [SA2, 相关工作] -- is kept, because the
+ * FP8 quantisation of P~ is taken relative to the running maximum.
+ *
+ * Build: gcc -O2 -std=c99 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include "sage_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ===================================================================== */
+/* Number formats                                                         */
+/* ===================================================================== */
+
+/*
+ * Nearest value, ties to even, of a binary floating-point format that has
+ * `mbits` stored fraction bits and smallest normal exponent `emin` (values
+ * below 2^emin are subnormal with the fixed quantum 2^(emin-mbits)).
+ * `a` must be finite and >= 0.  Exponent range at the top is NOT limited here;
+ * the callers handle overflow.  All arithmetic is exact in binary64 (a / q and
+ * m * q only shift exponents), so the single rounding is nearbyint's, which is
+ * round-half-to-even in the default rounding mode.
+ */
+static double round_to_format(double a, int mbits, int emin) {
+    if (a == 0.0) return 0.0;
+    int e = ilogb(a);
+    if (e < emin) e = emin;
+    double q = ldexp(1.0, e - mbits);
+    return nearbyint(a / q) * q;
+}
+
+/* IEEE binary16: 5 exponent bits (bias 15), 10 fraction bits. */
+static float f16_bits_to_float(uint16_t h) {
+    int sign = h >> 15, ex = (h >> 10) & 31, fr = h & 1023;
+    double v;
+    if (ex == 31) v = fr ? NAN : INFINITY;
+    else if (ex == 0) v = ldexp((double)fr, -24);
+    else v = ldexp(1.0 + fr / 1024.0, ex - 15);
+    return (float)(sign ? -v : v);
+}
+
+static uint16_t float_to_f16_bits(float x) {
+    if (isnan(x)) return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double v = round_to_format(fabs((double)x), 10, -14);
+    if (v >= 65536.0) return sign | 0x7c00; /* overflow -> inf */
+    if (v < ldexp(1.0, -14)) return sign | (uint16_t)(v / ldexp(1.0, -24));
+    int e = ilogb(v);
+    uint16_t fr = (uint16_t)(ldexp(v, -e) * 1024.0 - 1024.0);
+    return sign | (uint16_t)((e + 15) << 10) | fr;
+}
+
+/* bfloat16: the upper half of an IEEE binary32 (8 exponent bits, 7 fraction bits). */
+static float bf16_bits_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint16_t float_to_bf16_bits(float x) {
+    if (isnan(x)) return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double v = round_to_format(fabs((double)x), 7, -126);
+    if (v >= ldexp(1.0, 128)) return sign | 0x7f80;
+    if (v < ldexp(1.0, -126)) return sign | (uint16_t)(v / ldexp(1.0, -133));
+    int e = ilogb(v);
+    uint16_t fr = (uint16_t)(ldexp(v, -e) * 128.0 - 128.0);
+    return sign | (uint16_t)((e + 127) << 7) | fr;
+}
+
+void orc_decode16(const uint16_t *x, size_t n, int dtype, float *out) {
+    for (size_t i = 0; i < n; ++i)
+        out[i] = dtype == ORC_BF16 ? bf16_bits_to_float(x[i]) : f16_bits_to_float(x[i]);
+}
+
+void orc_encode16(const float *x, size_t n, int dtype, uint16_t *out) {
+    for (size_t i = 0; i < n; ++i)
+        out[i] = dtype == ORC_BF16 ? float_to_bf16_bits(x[i]) : float_to_f16_bits(x[i]);
+}
+
+/* fp32 -> nearest fp16 value, returned as fp32 (used for P and V in pv fp16 mode). */
+static float round_f16(float x) { return f16_bits_to_float(float_to_f16_bits(x)); }
+
+/*
+ * FP8 E4M3 as in [OCP] "E4M3FN": 1 sign bit, 4 exponent bits (bias 7), 3
+ * fraction bits; exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN;
+ * there is no infinity; the largest finite magnitude is 1.75 * 2^8 = 448.
+ * [SA2, SageAttention2方法] names E4M3 for P~ and V.
+ */
+float orc_e4m3_decode(uint8_t c) {
+    int sign = c >> 7, ex = (c >> 3) & 15, fr = c & 7;
+    if (ex == 15 && fr == 7) return NAN;
+    double v = ex == 0 ? ldexp((double)fr, -9) : ldexp(1.0 + fr / 8.0, ex - 7);
+    return (float)(sign ? -v : v);
+}
+
+/* Round to nearest, ties to even; magnitudes beyond 448 saturate to 448. */
+uint8_t orc_e4m3_encode(float x) {
+    if (isnan(x)) return 0x7f;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double v = round_to_format(fabs((double)x), 3, -6);
+    if (v >= 448.0) return sign | 0x7e; /* 0x7e = 1.75 * 2^8 */
+    if (v < ldexp(1.0, -6)) return sign | (uint8_t)(v / ldexp(1.0, -9));
+    int e = ilogb(v);
+    uint8_t fr = (uint8_t)(ldexp(v, -e) * 8.0 - 8.0);
+    return sign | (uint8_t)((e + 7) << 3) | fr;
+}
+
+void orc_e4m3_encode_n(const float *x, size_t n, uint8_t *out) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(x[i]);
+}
+
+/* ===================================================================== */
+/* Quantisation                                                           */
+/* ===================================================================== */
+
+/*
+ * Symmetric INT8 quantisation of one block with one fp32 scale
+ * ([KAI, 2.2] per-block INT8 for QK^T; [SA2, 相关工作] Q and K to INT8).
+ * Reading of the unstated details: range +-127, scale = amax / 127,
+ * code = round-half-even(x * (127 / amax)), an all-zero block gets scale 0 and
+ * codes 0.  Every step is one correctly rounded fp32 operation.
+ */
+void orc_int8_quant_block(const float *x, size_t n, int8_t *codes, float *scale) {
+    float amax = 0.0f;
+    for (size_t i = 0; i < n; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale = 0.0f;
+        memset(codes, 0, n);
+        return;
+    }
+    float inv = 127.0f / amax;
+    *scale = amax / 127.0f;
+    for (size_t i = 0; i < n; ++i) {
+        float t = rintf(x[i] * inv);
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        codes[i] = (int8_t)t;
+    }
+}
+
+/*
+ * K smoothing statistic: the mean of each channel over all S tokens of the
+ * head ([SA2, 相关工作] K is pre-processed; [SA2, SageAttention2方法] K smoothing).
+ * Sum in binary64 over tokens in order, divide by S in binary64, round once
+ * to fp32.
+ */
+void orc_channel_mean(const float *x, int S, int D, float *mean) {
+    for (int d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int t = 0; t < S; ++t) s += (double)x[(size_t)t * D + d];
+        mean[d] = (float)(s / (double)S);
+    }
+}
+
+/* Q: INT8 blocks of `blk` consecutive tokens (all D channels share a scale). */
+void orc_quant_q_head(const float *q, int S, int D, int blk, int8_t *codes, float *scales) {
+    int nb = (S + blk - 1) / blk;
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < nb; ++b) {
+        int r0 = b * blk, r1 = r0 + blk < S ? r0 + blk : S;
+        size_t off = (size_t)r0 * D;
+        orc_int8_quant_block(q + off, (size_t)(r1 - r0) * D, codes + off, &scales[b]);
+    }
+}
+
+/*
+ * K: optionally subtract the channel mean (one fp32 subtraction per element),
+ * then INT8 blocks of `blk` tokens.  `mean` receives the channel means (zeros
+ * when smooth == 0).
+ */
+void orc_quant_k_head(const float *k, int S, int D, int blk, int smooth, int8_t *codes,
+                      float *scales, float *mean) {
+    size_t n = (size_t)S * D;
+    float *ks = (float *)malloc(n * sizeof(float));
+    if (smooth) orc_channel_mean(k, S, D, mean);
+    else memset(mean, 0, (size_t)D * sizeof(float));
+    for (size_t i = 0; i < n; ++i) ks[i] = k[i] - mean[i % D];
+    orc_quant_q_head(ks, S, D, blk, codes, scales);
+    free(ks);
+}
+
+/*
+ * V: per-channel FP8 E4M3 ([SA2, SageAttention2方法]: V to FP8 with per-channel
+ * quantisation).  scale[d] = amax_d / 448, code = E4M3(v * (448 / amax_d));
+ * an all-zero channel gets scale 0 and codes 0.
+ */
+void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scales) {
+    for (int d = 0; d < D; ++d) {
+        float amax = 0.0f;
+        for (int t = 0; t < S; ++t) {
+            float a = fabsf(v[(size_t)t * D + d]);
+            if (a > amax) amax = a;
+        }
+        if (amax == 0.0f) {
+            scales[d] = 0.0f;
+            for (int t = 0; t < S; ++t) codes[(size_t)t * D + d] = 0;
+            continue;
+        }
+        float inv = 448.0f / amax;
+        scales[d] = amax / 448.0f;
+        for (int t = 0; t < S; ++t)
+            codes[(size_t)t * D + d] = orc_e4m3_encode(v[(size_t)t * D + d] * inv);
+    }
+}
+
+/* ===================================================================== */
+/* Attention                                                              */
+/* ===================================================================== */
+
+static int32_t dot_i8(const int8_t *a, const int8_t *b, int D) {
+    int32_t s = 0;
+    for (int d = 0; d < D; ++d) s += (int32_t)a[d] * (int32_t)b[d];
+    return s;
+}
+
+/* Integer Q K^T of one head: out[i][n] = sum_d q8[i][d] * k8[n][d] (exact). */
+void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < S; ++i)
+        for (int n = 0; n < S; ++n)
+            out[(size_t)i * S + n] = dot_i8(q8 + (size_t)i * D, k8 + (size_t)n * D, D);
+}
+
+/*
+ * Quantized attention for selected query rows of one head.
+ *
+ * Key blocks of `blk_k` tokens are visited in order with an online softmax
+ * whose running max m and running sum l are fp32 ([SA2, 相关工作]: token-dim
+ * blocking of FlashAttention; SageAttention builds on that blocking).  Per key block:
+ *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_j) * sm_scale)          (dequantise)
+ *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal)
+ *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first block)
+ *   p_n   = exp(s_n - m')                                            (fp32)
+ *   l     = alpha * l + sum_n p_n                (uses the unquantised p_n)
+ * pv fp8 ([SA2, SageAttention2方法]: P~ to E4M3 with a static scale, V per channel;
+ *         FP32 buffer for the two-level accumulation):
+ *   P8_n  = E4M3(p_n * 448)                 (static scale 1/448: p = 1 -> 448)
+ *   inner = sum_n dec(P8_n) * dec(v8_n,d)   (fresh per key block, rounded once to fp32)
+ *   O_d   = alpha * O_d + inner_d                                    (fp32 buffer)
+ *   out   = O_d * (dv_d / (448 * l))
+ * pv fp16 ([KAI, 2.1] sm80 row: INT8 QK^T, FP16 PV, fp32 accumulation):
+ *   P_n   = fp16(p_n), V in fp16 (bf16 inputs rounded to fp16),
+ *   O_d   = alpha * O_d + sum_n P_n * V_n,d;   out = O_d / l
+ * `v` (fp32 values of the original V) is read only in pv fp16 mode; `v8`,
+ * `v_scale` only in pv fp8 mode.  out is [nrows][D] fp32 (before the final
+ * rounding to the input dtype).
+ */
+void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
+                        const int8_t *k8, const float *k_scale, int blk_k,
+                        const uint8_t *v8, const float *v_scale, const float *v,
+                        int in_dtype, int S, int D, int is_causal, float sm_scale,
+                        int pv_mode, const int *rows, int nrows, float *out) {
+    int nblk = (S + blk_k - 1) / blk_k;
+#pragma omp parallel
+    {
+        float *s = (float *)malloc((size_t)blk_k * sizeof(float));
+        float *p = (float *)malloc((size_t)blk_k * sizeof(float));
+        float *pq = (float *)malloc((size_t)blk_k * sizeof(float));
+        float *O = (float *)malloc((size_t)D * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            int i = rows[r];
+            float m = -INFINITY, l = 0.0f;
+            for (int d = 0; d < D; ++d) O[d] = 0.0f;
+            float dq = q_scale[i / blk_q];
+            for (int j = 0; j < nblk; ++j) {
+                int n0 = j * blk_k;
+                if (is_causal && n0 > i) break; /* block entirely in the future */
+                float c = (dq * k_scale[j]) * sm_scale;
+                float mt = -INFINITY;
+                for (int t = 0; t < blk_k; ++t) {
+                    int n = n0 + t;
+                    if (n >= S || (is_causal && n > i)) {
+                        s[t] = -INFINITY;
+                    } else {
+                        s[t] = (float)dot_i8(q8 + (size_t)i * D, k8 + (size_t)n * D, D) * c;
+                    }
+                    if (s[t] > mt) mt = s[t];
+                }
+                float mnew = m > mt ? m : mt;
+                float alpha = (m == -INFINITY) ? 0.0f : expf(m - mnew);
+                float psum = 0.0f;
+                for (int t = 0; t < blk_k; ++t) {
+                    p[t] = (s[t] == -INFINITY) ? 0.0f : expf(s[t] - mnew);
+                    psum += p[t];
+                }
+                l = alpha * l + psum;
+                if (pv_mode == ORC_PV_FP8) {
+                    for (int t = 0; t < blk_k; ++t) pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));
+                    for (int d = 0; d < D; ++d) {
+                        double acc = 0.0;
+                        for (int t = 0; t < blk_k && n0 + t < S; ++t)
+                            acc += (double)pq[t] * (double)orc_e4m3_decode(v8[(size_t)(n0 + t) * D + d]);
+                        O[d] = alpha * O[d] + (float)acc;
+                    }
+                } else {
+                    for (int t = 0; t < blk_k; ++t) pq[t] = round_f16(p[t]);
+                    for (int d = 0; d < D; ++d) {
+                        double acc = 0.0;
+                        for (int t = 0; t < blk_k && n0 + t < S; ++t) {
+                            float vv = v[(size_t)(n0 + t) * D + d];
+                            if (in_dtype == ORC_BF16) vv = round_f16(vv);
+                            acc += (double)pq[t] * (double)vv;
+                        }
+                        O[d] = alpha * O[d] + (float)acc;
+                    }
+                }
+                m = mnew;
+            }
+            float *o = out + (size_t)r * D;
+            if (pv_mode == ORC_PV_FP8) {
+                for (int d = 0; d < D; ++d) o[d] = O[d] * (v_scale[d] / (448.0f * l));
+            } else {
+                for (int d = 0; d < D; ++d) o[d] = O[d] / l;
+            }
+        }
+        free(s);
+        free(p);
+        free(pq);
+        free(O);
+    }
+}
+
+/*
+ * Exact attention in binary64, no smoothing and no quantisation:
+ * out_i = sum_n softmax_n(sm_scale * q_i . k_n) v_n, keys n > i excluded when causal.
+ */
+void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, int D,
+                         int is_causal, double sm_scale, const int *rows, int nrows,
+                         double *out) {
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)S * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            int i = rows[r];
+            int nvis = is_causal ? i + 1 : S;
+            double mx = -INFINITY;
+            for (int n = 0; n < nvis; ++n) {
+                double a = 0.0;
+                for (int d = 0; d < D; ++d) a += (double)q[(size_t)i * D + d] * (double)k[(size_t)n * D + d];
+                s[n] = a * sm_scale;
+                if (s[n] > mx) mx = s[n];
+            }
+            double den = 0.0;
+            for (int n = 0; n < nvis; ++n) {
+                s[n] = exp(s[n] - mx);
+                den += s[n];
+            }
+            double *o = out + (size_t)r * D;
+            for (int d = 0; d < D; ++d) {
+                double a = 0.0;
+                for (int n = 0; n < nvis; ++n) a += s[n] * (double)v[(size_t)n * D + d];
+                o[d] = a / den;
+            }
+        }
+        free(s);
+    }
+}

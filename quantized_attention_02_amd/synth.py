@@ -1,0 +1,111 @@
+"""Seeded synthetic attention inputs (Q, K, V) -- no part of the method's arithmetic.
+
+Both the GPU library and the CPU oracle are fed from here; this module only
+draws random numbers and casts them to the 16-bit input dtype.  Shapes and
+value recipes model the workloads the SageAttention pages talk about:
+
+* the two usage snippets ("完整指南" page, section 五分钟跑通第一个加速样例:
+  B=2, H=32, S=4096, D=128, fp16, HND; "Thư viện" page, section Dùng
+  SageAttention trong code của bạn: B=1, H=16, S=512, D=64, fp16, HND);
+* long-context LLM prefill (causal, NHD, bf16) and a video-DiT shape
+  (model dim 2560 = 20 heads x 128, "Kairos" page section 四);
+* K carries a per-channel bias shared by all tokens -- the outlier structure
+  that K smoothing removes ("SageAttention2" page, section SageAttention2方法).
+
+Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this order):
+  1. Q, K, V base values ~ N(0, 1), float32, logical [B, H, S, D];
+  2. the K bias c[h, d] ~ N(0, bias_sigma^2), shared over b and s;
+  3. (outlier_p > 0) Bernoulli(outlier_p) masks for Q, then K;
+  4. (token_norm) per-token factors r ~ U(0.5, 2) drawn per (b, s) for Q, K, V.
+Application: x *= r (token norm), K += c, then masked entries of Q and K *= 20.
+Then cast round-to-nearest-even to fp16 (numpy) or bf16 (torch CPU) and, for
+NHD, permute to [B, S, H, D].  Returned arrays are the raw uint16 codes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: str  # "fp16" | "bf16"
+    layout: str  # "HND" | "NHD"
+    bias_sigma: float
+    outlier_p: float = 0.0
+    token_norm: bool = False
+    causal: tuple = (False,)
+    pv_modes: tuple = ("fp8",)
+    seed: int = 42
+
+    def ops(self, causal: bool) -> float:
+        """Attention operations per call: 4*B*H*S^2*D, halved for causal."""
+        n = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return n / 2 if causal else n
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_b1h2s256d64", 1, 2, 256, 64, "fp16", "HND", 2.0, seed=42),
+        Workload("snippet_b1h16s512d64", 1, 16, 512, 64, "fp16", "HND", 2.0, causal=(False, True), seed=43),
+        Workload("snippet_b2h32s4096d128", 2, 32, 4096, 128, "fp16", "HND", 3.0, outlier_p=1e-3,
+                 pv_modes=("fp8", "fp16"), seed=44),
+        Workload("prefill_b1h32s32768d128", 1, 32, 32768, 128, "bf16", "NHD", 3.0, causal=(True,), seed=45),
+        Workload("dit_b1h20s16384d128", 1, 20, 16384, 128, "bf16", "NHD", 3.0, token_norm=True, seed=46),
+    ]
+}
+HEADLINE = "snippet_b2h32s4096d128"
+
+
+def _cast16(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        import torch
+
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(dtype)
+
+
+def make_qkv(w: Workload, seed: int | None = None):
+    """Return (q, k, v) as uint16 codes in the workload's physical layout."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.S, w.D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    c = (rng.standard_normal((w.H, w.D), dtype=np.float32) * np.float32(w.bias_sigma)).astype(np.float32)
+    if w.outlier_p > 0:
+        mq = rng.random(shape) < w.outlier_p
+        mk = rng.random(shape) < w.outlier_p
+    if w.token_norm:
+        for x in (q, k, v):
+            r = rng.uniform(0.5, 2.0, size=(w.B, w.S)).astype(np.float32)
+            x *= r[:, None, :, None]
+    k += c[None, :, None, :]
+    if w.outlier_p > 0:
+        q[mq] *= np.float32(20.0)
+        k[mk] *= np.float32(20.0)
+    out = []
+    for x in (q, k, v):
+        if w.layout == "NHD":
+            x = np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+        out.append(_cast16(x, w.dtype))
+    return tuple(out)
+
+
+def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0, token_norm=False, seed=0):
+    """An ad-hoc workload (edge shapes in tests)."""
+    return Workload(f"custom_b{B}h{H}s{S}d{D}", B, H, S, D, dtype, layout, bias_sigma, outlier_p, token_norm,
+                    seed=seed)

@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in copies of the oracle source and check that the
+pins catch every one of them (a mutant that passes all pins would mean the pins
+do not constrain that part of the oracle)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sage_oracle.c")
+
+# (id, original text, planted mistake)
+MUTANTS = [
+    ("O_update_drops_alpha", "O[d] = alpha * O[d] + (float)acc;", "O[d] = O[d] + (float)acc;"),
+    ("l_update_drops_alpha", "l = alpha * l + psum;", "l = l + psum;"),
+    ("alpha_wrong_sign", "expf(m - mnew)", "expf(mnew - m)"),
+    ("p_wrong_sign", "expf(s[t] - mnew)", "expf(mnew - s[t])"),
+    ("qk_transposed_out", "out[(size_t)i * S + n] = dot_i8", "out[(size_t)n * S + i] = dot_i8"),
+    ("int8_range_128", "float inv = 127.0f / amax;", "float inv = 128.0f / amax;"),
+    ("int8_scale_128", "*scale = amax / 127.0f;", "*scale = amax / 128.0f;"),
+    ("no_k_smoothing", "ks[i] = k[i] - mean[i % D];", "ks[i] = k[i];"),
+    ("mean_divides_by_D", "mean[d] = (float)(s / (double)S);", "mean[d] = (float)(s / (double)D);"),
+    ("p_static_scale_240", "orc_e4m3_encode(p[t] * 448.0f)", "orc_e4m3_encode(p[t] * 240.0f)"),
+    ("v_scale_wrong_channel", "v_scale[d] / (448.0f * l)", "v_scale[0] / (448.0f * l)"),
+    ("v_quant_scale_240", "float inv = 448.0f / amax;", "float inv = 240.0f / amax;"),
+    ("causal_masks_diagonal", "(is_causal && n > i)", "(is_causal && n >= i)"),
+    ("round_ties_away", "return nearbyint(a / q) * q;", "return round(a / q) * q;"),
+    ("e4m3_bias_8", "ldexp(1.0 + fr / 8.0, ex - 7)", "ldexp(1.0 + fr / 8.0, ex - 8)"),
+    ("missing_sm_scale", "float c = (dq * k_scale[j]) * sm_scale;", "float c = dq * k_scale[j];"),
+    ("q_scale_wrong_block", "float dq = q_scale[i / blk_q];", "float dq = q_scale[i / blk_k];"),
+    ("exact_causal_off_by_one", "int nvis = is_causal ? i + 1 : S;", "int nvis = is_causal ? (i > 0 ? i : 1) : S;"),
+    ("fp16_pv_no_rounding", "pq[t] = round_f16(p[t]);", "pq[t] = p[t];"),
+    ("fp8_p_not_quantised", "pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));", "pq[t] = p[t] * 448.0f;"),
+    ("f16_decode_bias", "ldexp(1.0 + fr / 1024.0, ex - 15)", "ldexp(1.0 + fr / 1024.0, ex - 14)"),
+]
+
+RUNNER = r"""
+import sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, oracle_pins
+with oracle.use_library({so!r}):
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            print("caught by", pin.__name__)
+            sys.exit(0)
+print("survived every pin")
+sys.exit(3)
+"""
+
+
+@pytest.mark.parametrize("mid,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(orc, tmp_path, mid, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation site vanished from the oracle source"
+    mutated = src.replace(old, new, 1)
+    c = tmp_path / "mutant.c"
+    c.write_text(mutated)
+    so = str(tmp_path / "libmutant.so")
+    orc.build_variant(str(c), so)
+    code = RUNNER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), so=so)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 3, f"mutant {mid} survived: {r.stdout[-500:]}"
+    assert r.returncode == 0, f"mutant {mid} crashed the runner (rc={r.returncode}): {r.stderr[-800:]}"
