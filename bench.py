@@ -1,0 +1,167 @@
+"""Benchmark of the quantized-attention hot path on one MI355X.
+
+A step = one pass of the whole path over one batch of synthetic input already
+resident in HBM: sage_smooth_quant_qk (K mean, INT8 Q/K), sage_quant_v (FP8 V)
+and sage_attn_fwd (INT8 QK^T, online softmax, FP8 PV), all on one stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1] [--pv fp8|fp16]
+
+Prints one JSON line.  `value` is attention TOPS of the whole step
+(4*B*H*S^2*D per step, halved when causal); the attention kernel alone is
+reported in `roofline` (MFMA bound: INT8 and FP8 dense peak 5.0 POP/s), timed
+with HIP events around each launch on the launch stream.  `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TOPS = 5000.0  # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s) = 5.0 P
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "quantized_attention_02_amd", "csrc", "attn.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--causal", type=int, default=None)
+    p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU-oracle sample")
+    return p.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(kernel_hash, workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source and this workload."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("attn_src_sha256_16") != kernel_hash or rec.get("workload") != workload:
+        return None
+    return rec
+
+
+def cpu_baseline(w, causal, pv, nheads):
+    import numpy as np
+
+    import oracle as O
+    from quantized_attention_02_amd import synth
+
+    q, k, v = synth.make_qkv(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:nheads]
+    t0 = time.perf_counter()
+    O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal),
+           pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=heads)
+    dt = time.perf_counter() - t0
+    ops = 4.0 * len(heads) * w.S * w.S * w.D / (2 if causal else 1)
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{len(heads)} of {w.B * w.H} heads of {w.name}, all {w.S} query rows "
+                      f"(quantisation of Q/K/V + attention), {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the path has no multi-GPU part; see the sharding note in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_attention_02_amd as qa
+    from quantized_attention_02_amd import synth
+
+    name = args.workload or synth.HEADLINE
+    w = synth.WORKLOADS[name]
+    causal = w.causal[0] if args.causal is None else bool(args.causal)
+    ops = w.ops(causal)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = synth.make_qkv(w)
+    tdt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
+    bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev)
+    out = torch.empty_like(qd)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record()
+        qa.quantize(qd, kd, vd, w.layout, args.pv, bufs)
+        if e is not None:
+            e[1].record()
+        qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
+        if e is not None:
+            e[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite attention output")
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_tops = ops / (attn_ms * 1e-3) / 1e12
+    khash = source_hash(ATTN_SRC)
+    trec = traffic_record(khash, name)
+    traffic = None if trec is None else trec["hbm_bytes_per_launch"]
+
+    res = {
+        "metric": "attention TOPS (4*B*H*S^2*D per step, halved if causal): smooth+quantise Q/K, quantise V, "
+                  "fused INT8-QK/FP8-PV attention",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+fp8" if args.pv == "fp8" else "i8+f16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "input_dtype": w.dtype,
+                   "layout": w.layout, "causal": causal, "pv_mode": args.pv},
+        "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
+        "attn_fwd_tops": round(attn_tops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": MFMA_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tops / MFMA_PEAK_TOPS, 4), "traffic": traffic,
+                     "kernel": "k_attn (sage_attn_fwd)", "algorithmic_ops_per_launch": ops,
+                     "attn_src_sha256_16": khash},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

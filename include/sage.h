@@ -1,0 +1,161 @@
+/*
+ * sage.h -- C ABI of libsage: SageAttention-style quantized attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (web pages describing SageAttention, cited by title and section):
+ *   [SA2]   "SageAttention2" paper summary, sections 相关工作 and SageAttention2方法:
+ *           FlashAttention token-dim blocking; Q, K quantised to INT8 with K
+ *           pre-processed (smoothed); P~ and V quantised to FP8 E4M3, P~ with a
+ *           static scale and V per channel; a two-level accumulation into an
+ *           FP32 buffer for the FP8 PV product.
+ *   [KAI]   "Kairos的注意力加速利器：SageAttention INT8/FP8量化内核与FLA线性注意力解析指南",
+ *           section 2.1 (INT8 QK^T with FP16 PV and fp32 accumulation, or FP8 PV
+ *           with two-level accumulation) and 2.2 (per-block INT8, smoothing).
+ *   [GUIDE] "SageAttention量化加速框架完整指南：从安装配置到性能调优的实战之路",
+ *           section 五分钟跑通第一个加速样例 (sageattn(q, k, v, tensor_layout, is_causal),
+ *           HND = (batch, head, seq, dim), NHD = (batch, seq, head, dim)),
+ *           section 性能调优实战 (PV precision choice; layout and causality must match
+ *           the tensors), section 替换时的三个注意事项 (no attention_mask argument) and
+ *           section 最容易踩的四个安装坑 (unsupported GPUs raise an error).
+ *
+ * Pipeline: sage_smooth_quant_qk -> sage_quant_v (pv fp8 only) -> sage_attn_fwd.
+ *
+ * Common rules for every entry point:
+ *  - Tensor pointers are DEVICE pointers; every call only enqueues work on
+ *    `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *    returns.  Inputs must stay alive and unmodified, and outputs untouched,
+ *    until the stream has passed the call.  The caller owns all memory; the
+ *    library allocates no device memory and keeps no per-call state.
+ *  - Tensor pointers (q, k, v, out, q_i8, k_i8, v_fp8, dump buffers) must be
+ *    16-byte aligned; scale / mean arrays 4-byte aligned.  Outputs must not
+ *    overlap inputs.
+ *  - Shapes: B, H >= 1; 1 <= S <= SAGE_MAX_S; D in {64, 128};
+ *    B * H <= SAGE_MAX_BH.
+ *  - Errors are reported only through the return code.  All argument checks
+ *    happen before anything is enqueued; on an error nothing is enqueued.
+ *    SAGE_ERR_UNSUPPORTED means the current device is not gfx950.
+ *  - Thread safety: calls may be made from several host threads; the only
+ *    shared state is a per-device cache of the architecture check.
+ *
+ * Internal buffer layouts (all row-major, "[a][b]" = a outer):
+ *   S_q = roundup(S, SAGE_BLK_Q), S_k = roundup(S, SAGE_BLK_K),
+ *   nq = S_q / SAGE_BLK_Q, nk = S_k / SAGE_BLK_K.
+ *   q_i8    int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
+ *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens.
+ *   k_i8    int8  [B][H][S_k][D]   INT8 codes of K - k_mean; rows >= S are 0.
+ *   k_scale float [B][H][nk]       one scale per block of SAGE_BLK_K tokens.
+ *   k_mean  float [B][H][D]        per-channel mean of K over the S tokens.
+ *   v_fp8   uint8 [B][H][nk][D][64] E4M3 codes of V, one 64-key tile after the
+ *           other, each tile stored channel-major; inside a tile, byte p of
+ *           channel d holds key  SAGE_VPOS_KEY(p)  of that tile (keys >= S are 0).
+ *   v_scale float [B][H][D]        one scale per channel.
+ *   out: same dtype and layout (HND or NHD) as q.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define SAGE_OK 0
+#define SAGE_ERR_INVALID_ARG 1 /* a null pointer, a bad shape / enum / alignment / sm_scale */
+#define SAGE_ERR_UNSUPPORTED 2 /* the current device is not gfx950 */
+#define SAGE_ERR_NO_DEVICE 3   /* no HIP device could be queried */
+#define SAGE_ERR_LAUNCH 4      /* the HIP runtime rejected a kernel launch */
+
+/* ---- enums ---- */
+#define SAGE_LAYOUT_HND 0 /* [B][H][S][D] */
+#define SAGE_LAYOUT_NHD 1 /* [B][S][H][D] */
+#define SAGE_DTYPE_F16 0
+#define SAGE_DTYPE_BF16 1
+#define SAGE_PV_FP8 0  /* P~ and V in E4M3, two-level fp32 accumulation ([SA2]) */
+#define SAGE_PV_FP16 1 /* P~ and V in fp16, fp32 accumulation ([KAI] 2.1, sm80 row) */
+
+/* ---- limits and granularity ---- */
+#define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
+#define SAGE_BLK_K 64 /* K tokens per INT8 scale: one 64-key tile of the attention loop */
+#define SAGE_MAX_S (1 << 20)
+#define SAGE_MAX_BH (1 << 16)
+/* key held by byte p (0..63) of a v_fp8 tile row */
+#define SAGE_VPOS_KEY(p) (32 * (((p) & 31) >> 4) + 8 * (((p) & 15) >> 2) + 4 * ((p) >> 5) + ((p) & 3))
+
+/* Quantisation granularity (tokens per scale) used by every entry point. */
+int sage_get_config(int *blk_q, int *blk_k);
+
+/* Bytes of each intermediate buffer for a problem shape (see the layouts
+ * above).  Any output pointer may be NULL. */
+int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8,
+                      size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
+
+/*
+ * K smoothing + per-block INT8 quantisation of Q and K ([SA2] 相关工作,
+ * SageAttention2方法; [KAI] 2.2).
+ *   k_mean[d] = fp32( (sum_s K[s][d], summed in binary64) / S )
+ *   blocks of SAGE_BLK_Q tokens of Q, and of SAGE_BLK_K tokens of K - k_mean
+ *   (one fp32 subtraction per element), each over all D channels:
+ *     amax = max |x|;  scale = amax / 127;  code = rint(x * (127 / amax)) in [-127, 127];
+ *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
+ * q, k: dtype (SAGE_DTYPE_*) tensors in `layout` (SAGE_LAYOUT_*).
+ * Writes q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).
+ */
+int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int S, int D, int layout,
+                         int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
+                         void *stream);
+
+/*
+ * Per-channel FP8 E4M3 quantisation of V ([SA2] SageAttention2方法):
+ *   amax_d = max_s |V[s][d]|;  v_scale[d] = amax_d / 448;
+ *   code = E4M3(V[s][d] * (448 / amax_d)), round to nearest even, |x| clamped to 448;
+ *   an all-zero channel has scale 0 and codes 0.
+ * Writes v_fp8 in the tiled layout above and v_scale.
+ */
+int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8,
+                 float *v_scale, void *stream);
+
+/*
+ * Fused quantized attention ([SA2]; [KAI] 2.1; [GUIDE] 五分钟跑通, 性能调优实战).
+ * For each query row i, key tiles of SAGE_BLK_K keys in order, fp32 online softmax:
+ *   s_n = float(q_i8[i] . k_i8[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA, int32 sums)
+ *   keys n >= S, and n > i when is_causal (square, top-left aligned), are excluded
+ *   m' = max(m, max_n s_n);  alpha = exp(m - m');  p_n = exp(s_n - m');  l = alpha*l + sum p_n
+ *   pv fp8 : P = E4M3(448 * p_n) (static scale), inner = P . V_fp8 (FP8 MFMA, fresh per tile),
+ *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
+ *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
+ * q_i8 .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
+ * sage_quant_v.  pv fp16: v = the original V tensor (dtype, layout), v_scale = NULL
+ * (bf16 V is rounded to fp16).  out: dtype tensor in `layout`, shape of q.
+ * is_causal in {0, 1}; sm_scale finite and > 0 (the usual choice is 1/sqrt(D)).
+ */
+int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+                  const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,
+                  int layout, int is_causal, float sm_scale, int pv_mode, void *stream);
+
+/*
+ * Debug variant of sage_attn_fwd: the same kernel code, which additionally
+ * writes the int32 accumulators of Q K^T for head (b, h) to qk, an int32 [S][S]
+ * array (qk[i][n] = sum_d q_i8[i][d] * k_i8[n][d]).  Entries of 64-key tiles
+ * that the causal mask skips entirely are left unwritten.  `out` is written as
+ * by sage_attn_fwd.
+ */
+int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S,
+                          int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
+                          int32_t *qk, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *sage_status_str(int status);
+
+/* Pure check of an architecture name as reported by hipDeviceProp_t::gcnArchName
+ * (e.g. "gfx950:sramecc+:xnack-"): SAGE_OK for gfx950, else SAGE_ERR_UNSUPPORTED
+ * (SAGE_ERR_INVALID_ARG for NULL).  Touches no device. */
+int sage_check_arch(const char *gcn_arch_name);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

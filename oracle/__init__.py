@@ -98,6 +98,11 @@ def build_variant(src: str, out_so: str) -> str:
     return out_so
 
 
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
+
+
 def _f32(a):
     return np.ascontiguousarray(a, dtype=np.float32)
 

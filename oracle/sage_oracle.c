@@ -16,6 +16,18 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of OpenMP threads the parallel loops below use (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ===================================================================== */
 /* Number formats                                                         */

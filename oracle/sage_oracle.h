@@ -41,6 +41,8 @@ extern "C" {
 #define ORC_PV_FP8 0
 #define ORC_PV_FP16 1
 
+int orc_num_threads(void);
+
 /* ---- number formats --------------------------------------------------- */
 void orc_decode16(const uint16_t *x, size_t n, int dtype, float *out);
 void orc_encode16(const float *x, size_t n, int dtype, uint16_t *out);

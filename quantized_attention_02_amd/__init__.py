@@ -1,0 +1,221 @@
+"""SageAttention-style quantized attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libsage.so`` (C ABI in ``include/sage.h``).  The
+functions named ``sage_*`` mirror the C entry points one to one and only
+marshal arguments: every step of the method runs in the HIP kernels.  PyTorch
+is used for device memory and streams only.
+
+``sageattn(q, k, v, tensor_layout="HND", is_causal=False, ...)`` chains the
+three entry points the way the pages' high-level API is used ("完整指南" page,
+section 五分钟跑通第一个加速样例): it allocates the intermediate buffers with
+torch and returns a tensor shaped like ``q``.
+
+There is no CPU fallback: if ``libsage.so`` is missing or the device is not a
+gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsage.so")
+
+SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ERR_LAUNCH = 0, 1, 2, 3, 4
+LAYOUT = {"HND": 0, "NHD": 1}
+DTYPE = {"fp16": 0, "bf16": 1}
+PV = {"fp8": 0, "fp16": 1}
+BLK_Q, BLK_K = 32, 64
+
+EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_attn_fwd",
+            "sage_attn_fwd_dump_qk", "sage_status_str", "sage_check_arch"]
+
+_lib = None
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsage.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m quantized_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        c_int, c_float, c_void_p, c_size_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+        L.sage_get_config.argtypes = [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+        L.sage_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 7
+        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 6 + [c_void_p] * 5 + [c_void_p]
+        L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p, c_void_p, c_void_p]
+        attn = [c_void_p] * 7 + [c_int] * 7 + [c_float, c_int]
+        L.sage_attn_fwd.argtypes = attn + [c_void_p]
+        L.sage_attn_fwd_dump_qk.argtypes = attn + [c_int, c_int, c_void_p, c_void_p]
+        L.sage_status_str.argtypes = [c_int]
+        L.sage_status_str.restype = ctypes.c_char_p
+        L.sage_check_arch.argtypes = [ctypes.c_char_p]
+        for n in EXPORTED:
+            if n != "sage_status_str":
+                getattr(L, n).restype = c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().sage_status_str(status).decode()
+
+
+def _check(status: int, what: str):
+    if status == SAGE_ERR_UNSUPPORTED:
+        raise ValueError(f"{what}: {status_str(status)}")
+    if status != SAGE_OK:
+        raise SageError(status, what)
+
+
+# ----------------------------------------------------------------- raw entry points
+def sage_get_config():
+    bq, bk = ctypes.c_int(), ctypes.c_int()
+    _check(lib().sage_get_config(ctypes.byref(bq), ctypes.byref(bk)), "sage_get_config")
+    return bq.value, bk.value
+
+
+def sage_buffer_sizes(B, H, S, D):
+    vals = [ctypes.c_size_t() for _ in range(7)]
+    _check(lib().sage_buffer_sizes(B, H, S, D, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
+    names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
+    return {n: v.value for n, v in zip(names, vals)}
+
+
+def sage_smooth_quant_qk(q, k, dtype, B, H, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+    """All tensor arguments are device pointers (ints); returns the status code."""
+    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean, stream)
+
+
+def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream):
+    return lib().sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream)
+
+
+def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal, sm_scale,
+                  pv_mode, stream):
+    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal,
+                               sm_scale, pv_mode, stream)
+
+
+def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal,
+                          sm_scale, pv_mode, b, h, qk, stream):
+    return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout,
+                                       is_causal, sm_scale, pv_mode, b, h, qk, stream)
+
+
+def sage_status_str(status):
+    return status_str(status)
+
+
+def sage_check_arch(name: str) -> int:
+    return lib().sage_check_arch(None if name is None else name.encode())
+
+
+# ----------------------------------------------------------------- torch helpers
+def default_sm_scale(D: int) -> float:
+    """1/sqrt(D), rounded once to fp32."""
+    import numpy as np
+
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _shape(t, layout):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-d tensor")
+    if layout == "HND":
+        B, H, S, D = t.shape
+    elif layout == "NHD":
+        B, S, H, D = t.shape
+    else:
+        raise ValueError(f"tensor_layout must be HND or NHD, got {layout!r}")
+    return B, H, S, D
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float16:
+        return DTYPE["fp16"]
+    if t.dtype == torch.bfloat16:
+        return DTYPE["bf16"]
+    raise ValueError(f"q/k/v must be float16 or bfloat16, got {t.dtype}")
+
+
+class Quantized:
+    """Device buffers produced by the two quantisation entry points."""
+
+    def __init__(self, B, H, S, D, device):
+        import torch
+
+        sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + BLK_K - 1) // BLK_K * BLK_K
+        self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
+        self.q_scale = torch.empty((B, H, sq // BLK_Q), dtype=torch.float32, device=device)
+        self.k_i8 = torch.empty((B, H, sk, D), dtype=torch.int8, device=device)
+        self.k_scale = torch.empty((B, H, sk // BLK_K), dtype=torch.float32, device=device)
+        self.k_mean = torch.empty((B, H, D), dtype=torch.float32, device=device)
+        self.v_fp8 = torch.empty((B, H, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
+        self.v_scale = torch.empty((B, H, D), dtype=torch.float32, device=device)
+
+
+def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None) -> Quantized:
+    """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors."""
+    layout = LAYOUT[tensor_layout]
+    B, H, S, D = _shape(q, tensor_layout)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    dt = _dtype_code(q)
+    bufs = bufs or Quantized(B, H, S, D, q.device)
+    st = _stream()
+    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, S, D, layout, bufs.q_i8.data_ptr(),
+                                bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
+                                bufs.k_mean.data_ptr(), st), "sage_smooth_quant_qk")
+    if pv_mode == "fp8":
+        _check(sage_quant_v(v.data_ptr(), dt, B, H, S, D, layout, bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), st),
+               "sage_quant_v")
+    return bufs
+
+
+def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8",
+             dump_head=None, dump=None):
+    """Run sage_attn_fwd (or the dump variant when dump_head=(b, h)) into `out`."""
+    layout = LAYOUT[tensor_layout]
+    B, H, S, D = _shape(out, tensor_layout)
+    dt = _dtype_code(out)
+    sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    pv = PV[pv_mode]
+    vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
+    vs = bufs.v_scale.data_ptr() if pv == 0 else None
+    args = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs,
+            out.data_ptr(), dt, B, H, S, D, layout, int(bool(is_causal)), sm, pv)
+    if dump_head is None:
+        _check(sage_attn_fwd(*args, _stream()), "sage_attn_fwd")
+    else:
+        _check(sage_attn_fwd_dump_qk(*args, dump_head[0], dump_head[1], dump.data_ptr(), _stream()),
+               "sage_attn_fwd_dump_qk")
+    return out
+
+
+def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8"):
+    """Quantized attention: same shape, dtype and layout out as q."""
+    import torch
+
+    bufs = quantize(q, k, v, tensor_layout, pv_mode)
+    out = torch.empty_like(q)
+    return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)

@@ -1,0 +1,228 @@
+// api.cpp -- the C ABI of libsage (declared in include/sage.h): argument
+// checks, the gfx950 check, buffer geometry and kernel launches.  No compute
+// happens here; every step of the method runs in the HIP kernels.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/sage.h"
+#include "sage_impl.h"
+
+using namespace sage;
+
+static_assert(SAGE_BLK_Q == kBlkQ && SAGE_BLK_K == kBlkK, "granularity constants disagree");
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+int roundup(int x, int m) { return (x + m - 1) / m * m; }
+
+int check_shape(int B, int H, int S, int D) {
+  if (B < 1 || H < 1 || S < 1 || S > SAGE_MAX_S) return SAGE_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SAGE_ERR_INVALID_ARG;
+  if ((long long)B * H > SAGE_MAX_BH) return SAGE_ERR_INVALID_ARG;
+  // grid sizes: B*H*(S_q / 32) must fit in a 32-bit launch dimension
+  if ((long long)B * H * (roundup(S, kBlkQ) / kBlkQ + 8) >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
+int check_enums(int dtype, int layout) {
+  if (dtype != SAGE_DTYPE_F16 && dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARG;
+  if (layout != SAGE_LAYOUT_HND && layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
+// The current device must be gfx950.  Cached per device.
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SAGE_ERR_NO_DEVICE;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SAGE_ERR_NO_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return SAGE_ERR_NO_DEVICE;
+    }
+    st = sage_check_arch(prop.gcnArchName) == SAGE_OK ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
+
+int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+                const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,
+                int layout, int is_causal, float sm_scale, int pv_mode, int dump_b, int dump_h, int32_t *qk,
+                bool dump, void *stream) {
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, layout))) return rc;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)))
+    return SAGE_ERR_INVALID_ARG;
+  if (dump) {
+    if (!qk || !aligned(qk, 16)) return SAGE_ERR_INVALID_ARG;
+    if (dump_b < 0 || dump_b >= B || dump_h < 0 || dump_h >= H) return SAGE_ERR_INVALID_ARG;
+  }
+  if ((rc = check_device())) return rc;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q_i8 = q_i8;
+  a.k_i8 = k_i8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v = v;
+  a.v_scale = v_scale;
+  a.out = out;
+  a.dump = qk;
+  a.dump_bh = dump ? dump_b * H + dump_h : -1;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.layout = layout;
+  a.dtype = dtype;
+  a.causal = is_causal;
+  a.pv = pv_mode;
+  a.S_q = roundup(S, kBlkQ);
+  a.S_k = roundup(S, kBlkK);
+  a.nq = a.S_q / kBlkQ;
+  a.nk = a.S_k / kBlkK;
+  a.nmblk = (S + 127) / 128;
+  a.sm2 = sm_scale * 1.4426950408889634f;
+  return launch_status(launch_attn(a, dump, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_get_config(int *blk_q, int *blk_k) {
+  if (!blk_q || !blk_k) return SAGE_ERR_INVALID_ARG;
+  *blk_q = SAGE_BLK_Q;
+  *blk_k = SAGE_BLK_K;
+  return SAGE_OK;
+}
+
+int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8, size_t *k_scale,
+                      size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  const size_t bh = (size_t)B * H;
+  const size_t S_q = roundup(S, kBlkQ), S_k = roundup(S, kBlkK);
+  if (q_i8) *q_i8 = bh * S_q * D;
+  if (q_scale) *q_scale = bh * (S_q / kBlkQ) * sizeof(float);
+  if (k_i8) *k_i8 = bh * S_k * D;
+  if (k_scale) *k_scale = bh * (S_k / kBlkK) * sizeof(float);
+  if (k_mean) *k_mean = bh * D * sizeof(float);
+  if (v_fp8) *v_fp8 = bh * S_k * D;
+  if (v_scale) *v_scale = bh * D * sizeof(float);
+  return SAGE_OK;
+}
+
+int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int S, int D, int layout,
+                         int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
+                         void *stream) {
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, layout))) return rc;
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4)) return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantQKArgs a;
+  a.q = q;
+  a.k = k;
+  a.q_i8 = q_i8;
+  a.k_i8 = k_i8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.k_mean = k_mean;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.layout = layout;
+  a.dtype = dtype;
+  a.S_q = roundup(S, kBlkQ);
+  a.S_k = roundup(S, kBlkK);
+  a.nq = a.S_q / kBlkQ;
+  a.nk = a.S_k / kBlkK;
+  return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
+}
+
+int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8, float *v_scale,
+                 void *stream) {
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, layout))) return rc;
+  if (!v || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4)) return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantVArgs a;
+  a.v = v;
+  a.v_fp8 = v_fp8;
+  a.v_scale = v_scale;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.layout = layout;
+  a.dtype = dtype;
+  a.nk = roundup(S, kBlkK) / kBlkK;
+  return launch_status(launch_quant_v(a, (hipStream_t)stream));
+}
+
+int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale, const void *v,
+                  const float *v_scale, void *out, int dtype, int B, int H, int S, int D, int layout, int is_causal,
+                  float sm_scale, int pv_mode, void *stream) {
+  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal, sm_scale,
+                     pv_mode, 0, 0, nullptr, false, stream);
+}
+
+int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,
+                          int layout, int is_causal, float sm_scale, int pv_mode, int b, int h, int32_t *qk,
+                          void *stream) {
+  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal, sm_scale,
+                     pv_mode, b, h, qk, true, stream);
+}
+
+const char *sage_status_str(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_INVALID_ARG: return "invalid argument";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported device (gfx950 required)";
+    case SAGE_ERR_NO_DEVICE: return "no HIP device";
+    case SAGE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int sage_check_arch(const char *name) {
+  if (!name) return SAGE_ERR_INVALID_ARG;
+  if (strncmp(name, "gfx950", 6) != 0) return SAGE_ERR_UNSUPPORTED;
+  const char c = name[6];
+  return (c == '\0' || c == ':') ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// sage_impl.h -- internals shared by the libsage kernels and the C ABI layer.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kBlkQ = 32;  // Q tokens per INT8 scale (one wavefront's MFMA row tile)
+constexpr int kBlkK = 64;  // K tokens per INT8 scale = keys per attention tile
+
+// Geometry of one attention head inside a physical HND / NHD tensor:
+// element (s, d) of head (b, h) lives at base + s * tok_stride + d.
+struct HeadView {
+  long long base;
+  long long tok_stride;
+};
+
+__host__ __device__ inline HeadView head_view(int layout, int b, int h, int H, int S, int D) {
+  HeadView v;
+  if (layout == 0) {  // HND [B][H][S][D]
+    v.base = ((long long)b * H + h) * S * D;
+    v.tok_stride = D;
+  } else {  // NHD [B][S][H][D]
+    v.base = ((long long)b * S * H + h) * D;
+    v.tok_stride = (long long)H * D;
+  }
+  return v;
+}
+
+// 16-bit input codes -> fp32 (exact for both formats).
+__device__ inline float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+template <int DT>
+__device__ inline float in_to_f32(uint32_t bits16) {
+  return DT == 0 ? f16_to_f32(bits16) : bf16_to_f32(bits16);
+}
+
+// fp32 -> 16-bit codes, round to nearest even (hardware conversion for fp16;
+// carry-propagating rounding on the bit pattern for bf16, finite inputs).
+__device__ inline uint32_t f32_to_f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ inline uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+template <int DT>
+__device__ inline uint32_t f32_to_out_bits(float x) {
+  return DT == 0 ? f32_to_f16_bits(x) : f32_to_bf16_bits(x);
+}
+
+// Byte p (0..63) of a V tile row holds key vpos_key(p) of the tile; the inverse
+// maps a key to its byte.  This is the key order in which the attention kernel
+// holds P~ in registers after the K.Q^T MFMA (see attn.hip).
+__host__ __device__ constexpr int vpos_key(int p) {
+  return 32 * ((p & 31) >> 4) + 8 * ((p & 15) >> 2) + 4 * (p >> 5) + (p & 3);
+}
+__host__ __device__ constexpr int key_vpos(int n) {
+  return 32 * ((n >> 2) & 1) + 16 * (n >> 5) + 4 * ((n & 31) >> 3) + (n & 3);
+}
+
+struct QuantQKArgs {
+  const void *q, *k;
+  int8_t *q_i8, *k_i8;
+  float *q_scale, *k_scale, *k_mean;
+  int B, H, S, D, layout, dtype;
+  int S_q, S_k, nq, nk;
+};
+
+struct QuantVArgs {
+  const void *v;
+  uint8_t *v_fp8;
+  float *v_scale;
+  int B, H, S, D, layout, dtype;
+  int nk;
+};
+
+struct AttnArgs {
+  const int8_t *q_i8, *k_i8;
+  const float *q_scale, *k_scale;
+  const void *v;
+  const float *v_scale;
+  void *out;
+  int32_t *dump;
+  int dump_bh;
+  int B, H, S, D, layout, dtype, causal, pv;
+  int S_q, S_k, nq, nk, nmblk;
+  float sm2;  // sm_scale * log2(e)
+};
+
+hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);
+hipError_t launch_quant_v(const QuantVArgs &a, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs &a, bool dump, hipStream_t stream);
+
+}  // namespace sage

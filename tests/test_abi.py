@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point that include/sage.h declares, and rejects bad arguments
+before touching a device."""
+import os
+import re
+
+import pytest
+
+import quantized_attention_02_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char|void)\s*\*?\s*(sage_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(qa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = qa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    nm = os.popen(f"nm -D --defined-only {qa.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_config_and_sizes():
+    assert qa.sage_get_config() == (32, 64)
+    s = qa.sage_buffer_sizes(2, 3, 100, 64)
+    assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 4 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 2 * 4,
+                 "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4}
+    L = qa.lib()
+    assert L.sage_get_config(None, None) == qa.SAGE_ERR_INVALID_ARG
+    for bad in [(0, 1, 1, 64), (1, 0, 1, 64), (1, 1, 0, 64), (1, 1, 1, 96), (1, 1, (1 << 20) + 1, 64)]:
+        assert L.sage_buffer_sizes(*bad, *([None] * 7)) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_arch_check():
+    assert qa.sage_check_arch("gfx950") == qa.SAGE_OK
+    assert qa.sage_check_arch("gfx950:sramecc+:xnack-") == qa.SAGE_OK
+    for other in ("gfx942", "gfx942:sramecc+:xnack-", "gfx90a", "gfx9500", "sm_90", ""):
+        assert qa.sage_check_arch(other) == qa.SAGE_ERR_UNSUPPORTED, other
+    assert qa.sage_check_arch(None) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert qa.status_str(s) and qa.status_str(s) != "unknown status"
+    assert qa.status_str(99) == "unknown status"
+
+
+def test_vpos_key_is_a_permutation():
+    f = lambda p: 32 * ((p & 31) >> 4) + 8 * ((p & 15) >> 2) + 4 * (p >> 5) + (p & 3)
+    assert sorted(f(p) for p in range(64)) == list(range(64))
+
+
+# a valid-looking set of (fake, aligned, non-null) device pointers
+P = 1 << 12
+GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, q_i8=P, q_scale=P, k_i8=P, k_scale=P,
+               k_mean=P, stream=None)
+GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, stream=None)
+GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, out=P, dtype=0, B=1, H=2, S=100, D=64,
+                 layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, stream=None)
+
+BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict(q_scale=P + 2), dict(dtype=2),
+          dict(layout=-1), dict(B=0), dict(H=-1), dict(S=0), dict(D=32), dict(D=256), dict(S=(1 << 20) + 1),
+          dict(B=1 << 9, H=1 << 8)]
+BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80)]
+BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
+            dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
+            dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0)]
+
+
+def _call_qk(**kw):
+    a = {**GOOD_QK, **kw}
+    return qa.sage_smooth_quant_qk(*a.values())
+
+
+def _call_v(**kw):
+    a = {**GOOD_V, **kw}
+    return qa.sage_quant_v(*a.values())
+
+
+def _call_attn(**kw):
+    a = {**GOOD_ATTN, **kw}
+    return qa.sage_attn_fwd(*a.values())
+
+
+@pytest.mark.parametrize("bad", BAD_QK, ids=[str(b) for b in BAD_QK])
+def test_smooth_quant_qk_rejects(bad):
+    assert _call_qk(**bad) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_V, ids=[str(b) for b in BAD_V])
+def test_quant_v_rejects(bad):
+    assert _call_v(**bad) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_ATTN, ids=[str(b) for b in BAD_ATTN])
+def test_attn_fwd_rejects(bad):
+    assert _call_attn(**bad) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_attn_fp16_mode_accepts_null_v_scale_then_needs_device():
+    rc = _call_attn(pv_mode=1, v_scale=None)
+    assert rc in (qa.SAGE_ERR_NO_DEVICE, qa.SAGE_OK, qa.SAGE_ERR_UNSUPPORTED) or rc != qa.SAGE_ERR_INVALID_ARG
+
+
+def test_dump_rejects_bad_head_and_buffer():
+    a = list(GOOD_ATTN.values())[:-1]
+    assert qa.sage_attn_fwd_dump_qk(*a, 0, 2, P, None) == qa.SAGE_ERR_INVALID_ARG  # h out of range
+    assert qa.sage_attn_fwd_dump_qk(*a, -1, 0, P, None) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_fwd_dump_qk(*a, 0, 0, None, None) == qa.SAGE_ERR_INVALID_ARG
+
+
+def _no_gpu():
+    import torch
+
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
+def test_valid_arguments_without_a_device_report_no_device():
+    assert _call_qk() == qa.SAGE_ERR_NO_DEVICE
+    assert _call_v() == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn() == qa.SAGE_ERR_NO_DEVICE
+
+
+def test_python_wrapper_maps_unsupported_to_value_error(monkeypatch):
+    with pytest.raises(ValueError):
+        qa._check(qa.SAGE_ERR_UNSUPPORTED, "x")
+    with pytest.raises(qa.SageError):
+        qa._check(qa.SAGE_ERR_INVALID_ARG, "x")
