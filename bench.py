@@ -39,8 +39,23 @@ def parse():
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU-oracle sample")
+    p.add_argument("--cpu-heads", type=int, default=10, help="heads in the CPU-oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 512 MiB read + 512 MiB written per launch."""
+    import torch
+
+    n = 512 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
 
 
 def source_hash(path):
@@ -84,6 +99,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "the path has no multi-GPU part; see the sharding note in DESIGN.md", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch

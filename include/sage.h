@@ -38,12 +38,13 @@
  *    shared state is a per-device cache of the architecture check.
  *
  * Internal buffer layouts (all row-major, "[a][b]" = a outer):
- *   S_q = roundup(S, SAGE_BLK_Q), S_k = roundup(S, SAGE_BLK_K),
+ *   S_q = roundup(S, SAGE_BLK_Q), S_k = roundup(S, SAGE_KV_PAD),
  *   nq = S_q / SAGE_BLK_Q, nk = S_k / SAGE_BLK_K.
  *   q_i8    int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
  *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens.
  *   k_i8    int8  [B][H][S_k][D]   INT8 codes of K - k_mean; rows >= S are 0.
- *   k_scale float [B][H][nk]       one scale per block of SAGE_BLK_K tokens.
+ *   k_scale float [B][H][nk]       one scale per block of SAGE_BLK_K tokens (0 for blocks
+ *                                  made only of padding keys).
  *   k_mean  float [B][H][D]        per-channel mean of K over the S tokens.
  *   v_fp8   uint8 [B][H][nk][D][64] E4M3 codes of V, one 64-key tile after the
  *           other, each tile stored channel-major; inside a tile, byte p of
@@ -78,7 +79,8 @@ extern "C" {
 
 /* ---- limits and granularity ---- */
 #define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
-#define SAGE_BLK_K 64 /* K tokens per INT8 scale: one 64-key tile of the attention loop */
+#define SAGE_BLK_K 64 /* K tokens per INT8 scale: one 64-key block of the attention loop */
+#define SAGE_KV_PAD 128 /* K / V buffers are padded to whole 128-key tiles */
 #define SAGE_MAX_S (1 << 20)
 #define SAGE_MAX_BH (1 << 16)
 /* key held by byte p (0..63) of a v_fp8 tile row */

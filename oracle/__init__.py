@@ -27,6 +27,9 @@ _SO = os.path.join(_HERE, "liboracle.so")
 
 F16, BF16 = 0, 1
 PV_FP8, PV_FP16 = 0, 1
+# Method parameters used by default: INT8 scale blocks of 32 Q tokens and 64 K
+# tokens, online-softmax tiles of 128 keys.
+BLK_Q, BLK_K, TILE_K = 32, 64, 128
 DTYPES = {"fp16": F16, "bf16": BF16}
 CFLAGS = ["-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
           "-Wall", "-Wextra"]
@@ -200,8 +203,11 @@ def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 
 def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
-                   pv_mode, rows=None, blk_q=32, blk_k=64) -> np.ndarray:
-    """Quantized attention for the given query rows of one head (fp32 [len(rows), D])."""
+                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K) -> np.ndarray:
+    """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
+
+    blk_q / blk_k: tokens per INT8 scale of Q / K; tile_k: keys per online-softmax
+    tile (the two-level accumulation folds once per tile)."""
     S, D = q8.shape
     rows = np.arange(S, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
     out = np.empty((rows.size, D), np.float32)
@@ -213,7 +219,7 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     v_scale = _f32(v_scale if v_scale is not None else np.zeros(D, np.float32))
     vf = _f32(vf if vf is not None else np.zeros((S, D), np.float32))
     lib().orc_attn_head_rows(_p(q8, ctypes.c_int8), _p(q_scale, ctypes.c_float), blk_q,
-                             _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k,
+                             _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k, tile_k,
                              _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float), _p(vf, ctypes.c_float),
                              in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
                              _p(rows, ctypes.c_int), rows.size, _p(out, ctypes.c_float))
@@ -272,7 +278,7 @@ def logical_shape(shape, layout):
 
 
 def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
-         heads=None, rows=None, blk_q=32, blk_k=64, smooth=True):
+         heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
 
     Returns {(b, h): fp32 [len(rows), D]}; rows default to all S rows.
@@ -293,7 +299,8 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         else:
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
-                                     sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k)
+                                     sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k,
+                                     tile_k=tile_k)
     return res
 
 

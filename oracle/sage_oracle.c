@@ -250,18 +250,21 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
 /*
  * Quantized attention for selected query rows of one head.
  *
- * Key blocks of `blk_k` tokens are visited in order with an online softmax
+ * Key tiles of `tile_k` tokens are visited in order with an online softmax
  * whose running max m and running sum l are fp32 ([SA2, 相关工作]: token-dim
- * blocking of FlashAttention; SageAttention builds on that blocking).  Per key block:
- *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_j) * sm_scale)          (dequantise)
+ * blocking of FlashAttention; SageAttention builds on that blocking).  The tile
+ * size is a free parameter of that blocking; it is independent of the INT8
+ * scale blocks of K (`blk_k` tokens each, key n uses k_scale[n / blk_k]).
+ * Per key tile:
+ *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_blk(n)) * sm_scale)     (dequantise)
  *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal)
- *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first block)
+ *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first tile)
  *   p_n   = exp(s_n - m')                                            (fp32)
  *   l     = alpha * l + sum_n p_n                (uses the unquantised p_n)
  * pv fp8 ([SA2, SageAttention2方法]: P~ to E4M3 with a static scale, V per channel;
  *         FP32 buffer for the two-level accumulation):
  *   P8_n  = E4M3(p_n * 448)                 (static scale 1/448: p = 1 -> 448)
- *   inner = sum_n dec(P8_n) * dec(v8_n,d)   (fresh per key block, rounded once to fp32)
+ *   inner = sum_n dec(P8_n) * dec(v8_n,d)   (fresh per key tile, rounded once to fp32)
  *   O_d   = alpha * O_d + inner_d                                    (fp32 buffer)
  *   out   = O_d * (dv_d / (448 * l))
  * pv fp16 ([KAI, 2.1] sm80 row: INT8 QK^T, FP16 PV, fp32 accumulation):
@@ -272,16 +275,16 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  * rounding to the input dtype).
  */
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
-                        const int8_t *k8, const float *k_scale, int blk_k,
+                        const int8_t *k8, const float *k_scale, int blk_k, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, float *out) {
-    int nblk = (S + blk_k - 1) / blk_k;
+    int ntile = (S + tile_k - 1) / tile_k;
 #pragma omp parallel
     {
-        float *s = (float *)malloc((size_t)blk_k * sizeof(float));
-        float *p = (float *)malloc((size_t)blk_k * sizeof(float));
-        float *pq = (float *)malloc((size_t)blk_k * sizeof(float));
+        float *s = (float *)malloc((size_t)tile_k * sizeof(float));
+        float *p = (float *)malloc((size_t)tile_k * sizeof(float));
+        float *pq = (float *)malloc((size_t)tile_k * sizeof(float));
         float *O = (float *)malloc((size_t)D * sizeof(float));
 #pragma omp for schedule(dynamic, 1)
         for (int r = 0; r < nrows; ++r) {
@@ -289,16 +292,16 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
             float m = -INFINITY, l = 0.0f;
             for (int d = 0; d < D; ++d) O[d] = 0.0f;
             float dq = q_scale[i / blk_q];
-            for (int j = 0; j < nblk; ++j) {
-                int n0 = j * blk_k;
-                if (is_causal && n0 > i) break; /* block entirely in the future */
-                float c = (dq * k_scale[j]) * sm_scale;
+            for (int j = 0; j < ntile; ++j) {
+                int n0 = j * tile_k;
+                if (is_causal && n0 > i) break; /* tile entirely in the future */
                 float mt = -INFINITY;
-                for (int t = 0; t < blk_k; ++t) {
+                for (int t = 0; t < tile_k; ++t) {
                     int n = n0 + t;
                     if (n >= S || (is_causal && n > i)) {
                         s[t] = -INFINITY;
                     } else {
+                        float c = (dq * k_scale[n / blk_k]) * sm_scale;
                         s[t] = (float)dot_i8(q8 + (size_t)i * D, k8 + (size_t)n * D, D) * c;
                     }
                     if (s[t] > mt) mt = s[t];
@@ -306,24 +309,24 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                 float mnew = m > mt ? m : mt;
                 float alpha = (m == -INFINITY) ? 0.0f : expf(m - mnew);
                 float psum = 0.0f;
-                for (int t = 0; t < blk_k; ++t) {
+                for (int t = 0; t < tile_k; ++t) {
                     p[t] = (s[t] == -INFINITY) ? 0.0f : expf(s[t] - mnew);
                     psum += p[t];
                 }
                 l = alpha * l + psum;
                 if (pv_mode == ORC_PV_FP8) {
-                    for (int t = 0; t < blk_k; ++t) pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));
+                    for (int t = 0; t < tile_k; ++t) pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));
                     for (int d = 0; d < D; ++d) {
                         double acc = 0.0;
-                        for (int t = 0; t < blk_k && n0 + t < S; ++t)
+                        for (int t = 0; t < tile_k && n0 + t < S; ++t)
                             acc += (double)pq[t] * (double)orc_e4m3_decode(v8[(size_t)(n0 + t) * D + d]);
                         O[d] = alpha * O[d] + (float)acc;
                     }
                 } else {
-                    for (int t = 0; t < blk_k; ++t) pq[t] = round_f16(p[t]);
+                    for (int t = 0; t < tile_k; ++t) pq[t] = round_f16(p[t]);
                     for (int d = 0; d < D; ++d) {
                         double acc = 0.0;
-                        for (int t = 0; t < blk_k && n0 + t < S; ++t) {
+                        for (int t = 0; t < tile_k && n0 + t < S; ++t) {
                             float vv = v[(size_t)(n0 + t) * D + d];
                             if (in_dtype == ORC_BF16) vv = round_f16(vv);
                             acc += (double)pq[t] * (double)vv;

@@ -61,7 +61,7 @@ void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scale
 /* ---- attention (per head) ---------------------------------------------- */
 void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t *out);
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
-                        const int8_t *k8, const float *k_scale, int blk_k,
+                        const int8_t *k8, const float *k_scale, int blk_k, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, float *out);

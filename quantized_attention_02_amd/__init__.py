@@ -26,7 +26,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ER
 LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
 PV = {"fp8": 0, "fp16": 1}
-BLK_Q, BLK_K = 32, 64
+BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 
 EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_attn_fwd",
             "sage_attn_fwd_dump_qk", "sage_status_str", "sage_check_arch"]
@@ -161,7 +161,7 @@ class Quantized:
     def __init__(self, B, H, S, D, device):
         import torch
 
-        sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + BLK_K - 1) // BLK_K * BLK_K
+        sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + KV_PAD - 1) // KV_PAD * KV_PAD
         self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
         self.q_scale = torch.empty((B, H, sq // BLK_Q), dtype=torch.float32, device=device)
         self.k_i8 = torch.empty((B, H, sk, D), dtype=torch.int8, device=device)

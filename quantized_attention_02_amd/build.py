@@ -19,6 +19,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results stay in ordinary VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -12,7 +12,7 @@
 
 using namespace sage;
 
-static_assert(SAGE_BLK_Q == kBlkQ && SAGE_BLK_K == kBlkK, "granularity constants disagree");
+static_assert(SAGE_BLK_Q == kBlkQ && SAGE_BLK_K == kBlkK && SAGE_KV_PAD == kKvPad, "granularity constants disagree");
 
 namespace {
 
@@ -104,7 +104,7 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   a.causal = is_causal;
   a.pv = pv_mode;
   a.S_q = roundup(S, kBlkQ);
-  a.S_k = roundup(S, kBlkK);
+  a.S_k = roundup(S, kKvPad);
   a.nq = a.S_q / kBlkQ;
   a.nk = a.S_k / kBlkK;
   a.nmblk = (S + 127) / 128;
@@ -128,7 +128,7 @@ int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale,
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   const size_t bh = (size_t)B * H;
-  const size_t S_q = roundup(S, kBlkQ), S_k = roundup(S, kBlkK);
+  const size_t S_q = roundup(S, kBlkQ), S_k = roundup(S, kKvPad);
   if (q_i8) *q_i8 = bh * S_q * D;
   if (q_scale) *q_scale = bh * (S_q / kBlkQ) * sizeof(float);
   if (k_i8) *k_i8 = bh * S_k * D;
@@ -164,7 +164,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   a.layout = layout;
   a.dtype = dtype;
   a.S_q = roundup(S, kBlkQ);
-  a.S_k = roundup(S, kBlkK);
+  a.S_k = roundup(S, kKvPad);
   a.nq = a.S_q / kBlkQ;
   a.nk = a.S_k / kBlkK;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
@@ -188,7 +188,7 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
   a.D = D;
   a.layout = layout;
   a.dtype = dtype;
-  a.nk = roundup(S, kBlkK) / kBlkK;
+  a.nk = roundup(S, kKvPad) / kBlkK;
   return launch_status(launch_quant_v(a, (hipStream_t)stream));
 }
 

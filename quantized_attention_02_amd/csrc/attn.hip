@@ -3,30 +3,33 @@
 // Method ("SageAttention2" summary, sections 相关工作 and SageAttention2方法;
 // "Kairos" guide, sections 2.1 and 2.2): INT8 Q.K^T with int32 accumulation,
 // dequantised by the product of the Q-block and K-block scales; an online
-// fp32 softmax over 64-key tiles (FlashAttention blocking); P~ quantised to
-// FP8 E4M3 with the static scale 448 and multiplied with per-channel FP8 V;
-// the FP8 products of one tile are summed by the MFMA into a fresh accumulator
-// and then folded into an fp32 output buffer (two-level accumulation).  A pv
-// fp16 mode keeps P~ and V in fp16 with fp32 accumulation.
+// fp32 softmax over key tiles (FlashAttention blocking); P~ quantised to FP8
+// E4M3 with the static scale 448 and multiplied with per-channel FP8 V; the
+// FP8 products of one tile are summed by the MFMA into a fresh accumulator and
+// then folded into an fp32 output buffer (two-level accumulation).  A pv fp16
+// mode keeps P~ and V in fp16 with fp32 accumulation.
 //
 // Mapping onto CDNA4:
-//  * one work-group = 4 wavefronts = 128 query rows; one wavefront owns 32
-//    query rows for the whole key loop (Q fragments stay in VGPRs);
-//  * per 64-key tile the work-group stages the INT8 K tile (64 x D) and the
-//    FP8 V tile (D x 64, channel-major, produced in that form by the V
-//    quantiser) in LDS, XOR-swizzled by 16-byte chunk against bank conflicts;
-//  * the wavefront computes S^T = K . Q^T with v_mfma_i32_32x32x32_i8, so the
-//    32x32 result holds one query per lane column: lane (q, half) owns 16 keys
-//    of each 32-key half tile, the row max / sum need one exchange with the
-//    other half-wave, and the running max, sum and rescale factor stay in the
-//    lane that uses them;
-//  * the same registers, converted to E4M3 (v_cvt_pk_fp8_f32), are directly
-//    the B operand of O^T = V^T . P^T on v_mfma_f32_32x32x64_f8f6f4: the key
-//    order they imply is the order the V tile is stored in (vpos_key), so no
-//    LDS round trip is needed for P;
+//  * one work-group = 4 wavefronts = 128 query rows; a wavefront owns 32 query
+//    rows for the whole key loop (Q fragments stay in VGPRs);
+//  * the key loop walks 128-key tiles (two 64-key INT8 scale blocks).  K and
+//    FP8 V tiles are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging), double-buffered: the copy of tile j+1 is in flight while tile j
+//    is computed, and one barrier per tile publishes it.  The 16-byte chunks
+//    of each LDS row are XOR-swizzled (applied to the source address of the
+//    copy) so that the MFMA operand reads are bank-conflict free;
+//  * the wavefront computes S^T = K . Q^T with v_mfma_i32_32x32x32_i8: the
+//    32x32 result holds one query per lane column, so lane (q, half) owns 16
+//    keys of every 32-key sub-tile, the row max needs one exchange with the
+//    other half-wave, and the running max, sum and rescale factor live in the
+//    lane that uses them.  The row max is taken on the int32 sums (one scale
+//    per 64-key block), so each score costs one convert, one FMA and one exp2;
+//  * the exp2 results, converted to E4M3 (v_cvt_pk_fp8_f32), are directly the
+//    B operand of O^T = V^T . P^T on v_mfma_f32_32x32x64_f8f6f4: the key order
+//    they imply is the order the V quantiser stores each 64-key block in
+//    (vpos_key), so P never goes through LDS;
 //  * work-groups are numbered so that each XCD (own L2) works through whole
-//    heads, keeping one head's K/V tiles in one L2; causal work is issued
-//    longest query blocks first.
+//    heads; causal work is issued longest query blocks first.
 #include <math.h>
 
 #include "sage_impl.h"
@@ -36,60 +39,136 @@ namespace sage {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kWaves * 32;
+constexpr int kTileN = 128;  // keys per loop iteration (two INT8 K blocks)
 constexpr float kLog2_448 = 8.807354922057604f;  // log2(448): folds the static P~ scale into exp2
 
-// XOR swizzle of the 16-byte chunks of an LDS row, so that the 8 (or 16)
-// consecutive rows a ds_read_b128 serves in one pass hit distinct banks.
-// CH = chunks per row: 8 for 128-byte rows, 4 for 64-byte rows.
+// XOR swizzle of the 16-byte chunks of an LDS row (CH = chunks per row) so that
+// the 16 lanes an LDS read serves together hit 16 distinct bank groups when
+// they read the same logical chunk of consecutive rows.
 template <int CH>
-__device__ inline int swz(int chunk, int row) {
+__device__ __forceinline__ int swz(int chunk, int row) {
   if (CH == 8) return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
-  return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
+  return chunk ^ ((row >> 2) & 3);
 }
 
+// One wavefront-wide LDS DMA: lane i copies 16 bytes from `src` to
+// lds_base + 16 * i (lds_base is the same for the whole wavefront).
+__device__ __forceinline__ void dma16(const void *src, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      src, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 16, 0, 0);
+}
+
+// Two consecutive floats at a wave-uniform address, read with a scalar load
+// (constant address space), which the vector-memory counter does not track.
+__device__ __forceinline__ float2 load2_uniform(const float *p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  typedef const __attribute__((address_space(4))) float2 *cptr;
+  return *(cptr)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
 template <int DT>
-__device__ inline void store4(void *out, long long off, float a, float b, float c, float d) {
+__device__ __forceinline__ void store4(void *out, long long off, float a, float b, float c, float d) {
   const uint32_t lo = f32_to_out_bits<DT>(a) | (f32_to_out_bits<DT>(b) << 16);
   const uint32_t hi = f32_to_out_bits<DT>(c) | (f32_to_out_bits<DT>(d) << 16);
   v2i w = {(int)lo, (int)hi};
   *reinterpret_cast<v2i *>(reinterpret_cast<uint16_t *>(out) + off) = w;
 }
 
+// Copy a K tile (128 x D int8) and, in pv fp8 mode, its two FP8 V blocks
+// (2 x D x 64, contiguous in HBM) into LDS, swizzled.  Each wavefront issues
+// its share of the 1 KiB wave-copies.
+template <int D, int PV>
+__device__ __forceinline__ void issue_tile(const int8_t *kt, const uint8_t *vt, uint8_t *kbuf, uint8_t *vbuf,
+                                           int wave, int lane) {
+  constexpr int KCH = D / 16;
+  constexpr int KLOADS = kTileN * D / 1024;
+  constexpr int KROWS = 1024 / D;
+#pragma unroll
+  for (int i = 0; i < KLOADS / kWaves; ++i) {
+    const int w = wave + kWaves * i;
+    const int row = w * KROWS + lane / KCH;
+    dma16(kt + row * D + 16 * swz<KCH>(lane % KCH, row), kbuf + w * 1024);
+  }
+  if (PV == 0) {
+    constexpr int VLOADS = 2 * D * 64 / 1024;
+#pragma unroll
+    for (int i = 0; i < VLOADS / kWaves; ++i) {
+      const int w = wave + kWaves * i;
+      const int row = w * 16 + (lane >> 2);
+      dma16(vt + row * 64 + 16 * swz<4>(lane & 3, row), vbuf + w * 1024);
+    }
+  }
+}
+
+// pv fp16: original 16-bit V rows [n0, n0 + 64) -> fp16 V^T rows (128 bytes,
+// vpos_key order, swizzled) in `vb`.  Staged through VGPRs: the layout change
+// and the bf16 -> fp16 rounding need the values in registers anyway.
+template <int D, int DT>
+__device__ __forceinline__ void stage_v16(const AttnArgs &a, const HeadView &hv, int n0, uint8_t *vb, int tid) {
+  const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(a.v);
+  constexpr int NU = 32 * (D / 8);  // key pairs x 8-channel groups
+#pragma unroll
+  for (int u = tid; u < NU; u += kThreads) {
+    const int pair = u / (D / 8), c8 = (u % (D / 8)) * 8;
+    const int n = n0 + 2 * pair;
+    v4i t0 = {0, 0, 0, 0}, t1 = {0, 0, 0, 0};
+    if (n < a.S) t0 = *reinterpret_cast<const v4i *>(vsrc + hv.base + (long long)n * hv.tok_stride + c8);
+    if (n + 1 < a.S) t1 = *reinterpret_cast<const v4i *>(vsrc + hv.base + (long long)(n + 1) * hv.tok_stride + c8);
+    const int pos = key_vpos(2 * pair);  // even key; its odd partner sits at pos + 1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t e0 = ((uint32_t)t0[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      uint32_t e1 = ((uint32_t)t1[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      if (DT == 1) {  // bf16 -> fp16, round to nearest even
+        e0 = f32_to_f16_bits(bf16_to_f32(e0));
+        e1 = f32_to_f16_bits(bf16_to_f32(e1));
+      }
+      const int row = c8 + i, byte = 2 * pos;
+      *reinterpret_cast<uint32_t *>(vb + row * 128 + 16 * swz<8>(byte >> 4, row) + (byte & 15)) = e0 | (e1 << 16);
+    }
+  }
+}
+
 template <int D, int PV, int DT, bool CAUSAL, bool DUMP>
-__global__ __launch_bounds__(kThreads) void k_attn(const AttnArgs a) {
-  constexpr int NC = D / 32;                      // 32-channel chunks of the head dim
-  constexpr int KCH = D / 16;                     // 16-byte chunks per K row
-  constexpr int VROW = PV == 0 ? 64 : 128;        // bytes per V^T row in LDS
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[64 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * VROW];
+__global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
+  constexpr int NC = D / 32;
+  constexpr int KCH = D / 16;
+  constexpr int KBYTES = kTileN * D;                         // K tile
+  constexpr int VBYTES = PV == 0 ? 2 * D * 64 : D * 128;     // fp8: two 64-key blocks; fp16: one block
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[PV == 0 ? VBYTES : 1024];
+  __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, qn = lane & 31;
 
   // ---- work-group -> (head, query block), XCD-aware
-  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int wg = blockIdx.x;
   const int nbh = a.B * a.H;
   int bh, mrank;
   if ((nbh & 7) == 0) {
     const int heads_per_xcd = nbh >> 3;
     const int xcd = wg & 7, idx = wg >> 3;
-    if (CAUSAL) {  // longest blocks first, heads of this XCD interleaved
+    if (CAUSAL) {  // longest blocks first; the XCD's heads interleaved
       bh = xcd * heads_per_xcd + idx % heads_per_xcd;
       mrank = idx / heads_per_xcd;
     } else {  // one head after the other inside this XCD
       bh = xcd * heads_per_xcd + idx / a.nmblk;
       mrank = idx % a.nmblk;
     }
+  } else if (CAUSAL) {
+    bh = wg % nbh;
+    mrank = wg / nbh;
   } else {
-    if (CAUSAL) {
-      bh = wg % nbh;
-      mrank = wg / nbh;
-    } else {
-      bh = wg / a.nmblk;
-      mrank = wg % a.nmblk;
-    }
+    bh = wg / a.nmblk;
+    mrank = wg % a.nmblk;
   }
-  (void)nwg;
   const int mblk = CAUSAL ? a.nmblk - 1 - mrank : mrank;
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = mblk * kBlockM;
@@ -111,14 +190,11 @@ __global__ __launch_bounds__(kThreads) void k_attn(const AttnArgs a) {
     for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
   }
 
-  int ntiles = a.nk;
-  if (CAUSAL) {
-    const int last_q = min(q0 + kBlockM - 1, a.S - 1);
-    ntiles = min(a.nk, last_q / 64 + 1);
-  }
+  int ntiles = a.S_k / kTileN;
+  if (CAUSAL) ntiles = min(ntiles, min(q0 + kBlockM - 1, a.S - 1) / kTileN + 1);
 
   float m = -INFINITY;  // running max (log2 domain, scaled scores)
-  float l = 0.0f;       // running sum of this half-wave's keys
+  float l = 0.0f;       // running sum over this half-wave's keys
   v16f O[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
@@ -126,163 +202,175 @@ __global__ __launch_bounds__(kThreads) void k_attn(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) O[c][r] = 0.0f;
 
   const int8_t *kbase = a.k_i8 + (long long)bh * a.S_k * D;
+  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + (long long)bh * a.S_k * D;
   const float *kscale = a.k_scale + (long long)bh * a.nk;
+  const HeadView hv = head_view(a.layout, b, h, a.H, a.S, D);
 
-  for (int j = 0; j < ntiles; ++j) {
-    __syncthreads();  // every wave is done with the previous tile
-    // ---- stage K tile (64 x D int8, contiguous in HBM)
-    {
-      const v4i *src = reinterpret_cast<const v4i *>(kbase + (long long)j * 64 * D);
+  // One 128-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
+  auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
+    const int key0 = j * kTileN;
+    const bool work = active && !(CAUSAL && key0 > qw + 31);
+    // the tile's two K-block scales, read through a wave-uniform address (scalar loads)
+    const float2 ksv = load2_uniform(kscale + 2 * j);
+    const float ks[2] = {ksv.x, ksv.y};
+    float p[64];
 #pragma unroll
-      for (int u = tid; u < 64 * KCH; u += kThreads) {
-        const int row = u / KCH, ch = u % KCH;
-        *reinterpret_cast<v4i *>(k_lds + row * D + 16 * swz<KCH>(ch, row)) = src[u];
-      }
-    }
-    // ---- stage V tile
-    if (PV == 0) {
-      const v4i *src = reinterpret_cast<const v4i *>(reinterpret_cast<const uint8_t *>(a.v) +
-                                                     ((long long)bh * a.nk + j) * D * 64);
+    for (int i = 0; i < 64; ++i) p[i] = 0.0f;
+    float alpha = 1.0f;
+    if (work) {
+      // ---- S^T = K . Q^T for four 32-key sub-tiles; per 32-channel chunk the
+      //      four K fragments are read together, then four MFMAs consume them
+      v16i s[4];
 #pragma unroll
-      for (int u = tid; u < D * 4; u += kThreads) {
-        const int row = u >> 2, ch = u & 3;
-        *reinterpret_cast<v4i *>(v_lds + row * 64 + 16 * swz<4>(ch, row)) = src[u];
-      }
-    } else {
-      // original 16-bit V (key-major) -> fp16 V^T rows in the vpos_key order.
-      // thread: key pair (2e, 2e+1) x 8 channels; writes 8 x (2 halves).
-      const HeadView hv = head_view(a.layout, b, h, a.H, a.S, D);
-      const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(a.v);
-      constexpr int NU = 32 * (D / 8);  // key pairs x channel groups
-#pragma unroll
-      for (int u = tid; u < NU; u += kThreads) {
-        const int pair = u / (D / 8), c8 = (u % (D / 8)) * 8;
-        const int n0 = j * 64 + 2 * pair;
-        uint32_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
-        if (n0 < a.S) {
-          const v4i t0 = *reinterpret_cast<const v4i *>(vsrc + hv.base + (long long)n0 * hv.tok_stride + c8);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w0[i] = (uint32_t)t0[i];
-        }
-        if (n0 + 1 < a.S) {
-          const v4i t1 = *reinterpret_cast<const v4i *>(vsrc + hv.base + (long long)(n0 + 1) * hv.tok_stride + c8);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w1[i] = (uint32_t)t1[i];
-        }
-        const int pos = key_vpos(2 * pair);  // even key; its odd partner sits at pos + 1
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t e0 = (w0[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-          uint32_t e1 = (w1[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-          if (DT == 1) {  // bf16 -> fp16, round to nearest even
-            e0 = f32_to_f16_bits(bf16_to_f32(e0));
-            e1 = f32_to_f16_bits(bf16_to_f32(e1));
-          }
-          const int row = c8 + i;
-          const int byte = 2 * pos;  // 16-bit element pos, within a 128-byte row
-          const int ch = byte >> 4, within = byte & 15;
-          *reinterpret_cast<uint32_t *>(v_lds + row * 128 + 16 * swz<8>(ch, row) + within) = e0 | (e1 << 16);
-        }
-      }
-    }
-    __syncthreads();
-
-    if (!active) continue;
-    if (CAUSAL && j * 64 > qw + 31) continue;  // every key of the tile is in this wave's future
-
-    // ---- S^T = K . Q^T : two 32-key halves, int32 accumulators
-    v16i st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      const int row = 32 * t + qn;
+      for (int t = 0; t < 4; ++t) s[t] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const v4i kf = *reinterpret_cast<const v4i *>(k_lds + row * D + 16 * swz<KCH>(2 * c + hh, row));
-        st[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[c], st[t], 0, 0, 0);
-      }
-    }
-
-    if (DUMP && bh == a.dump_bh && qi < a.S) {
+        v4i kf[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 4; ++t) {
+          const int row = 32 * t + qn;
+          kf[t] = *reinterpret_cast<const v4i *>(kb + row * D + 16 * swz<KCH>(2 * c + hh, row));
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t], qf[c], s[t], 0, 0, 0);
+      }
+      if (DUMP && bh == a.dump_bh && qi < a.S) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key < a.S) a.dump[(long long)qi * a.S + key] = s[t][r];
+          }
+      }
+      float c2[2];
+      c2[0] = (dq * ks[0]) * a.sm2;
+      c2[1] = (dq * ks[1]) * a.sm2;
+      // ---- mask: only tiles that reach past S or cross the causal diagonal
+      const bool need_mask = (key0 + kTileN > a.S) || (CAUSAL && key0 + kTileN - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= a.S || (CAUSAL && key > qi)) s[t][r] = INT_MIN;
+          }
+      }
+      // ---- row max on the int32 sums (c2 > 0 per 64-key block)
+      float mt = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        int mx = INT_MIN;
+#pragma unroll
+        for (int t = 2 * blk; t < 2 * blk + 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = max(mx, s[t][r]);
+        if (mx != INT_MIN) mt = fmaxf(mt, (float)mx * c2[blk]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m, mt);
+      alpha = __builtin_amdgcn_exp2f(m - mn);
+      const float sub = PV == 0 ? mn - kLog2_448 : mn;
+      m = mn;
+      // ---- p = exp2(s * c2 - sub)  (= 448 p~ in fp8 mode), row sum
+      float ps = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * 64 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key < a.S) a.dump[(long long)qi * a.S + key] = st[t][r];
+          float x = __builtin_fmaf((float)s[t][r], c2[t >> 1], -sub);
+          if (need_mask && s[t][r] == INT_MIN) x = -INFINITY;
+          p[16 * t + r] = __builtin_amdgcn_exp2f(x);
+          ps += p[16 * t + r];
         }
+      l = alpha * l + ps;
     }
 
-    // ---- dequantise (log2 domain), mask, online softmax
-    const float c2 = (dq * kscale[j]) * a.sm2;
-    const bool need_mask = (j * 64 + 64 > a.S) || (CAUSAL && j * 64 + 63 > qw);
-    float x[32];
-    float mt = -INFINITY;
+    if constexpr (PV == 0) {
+      if (work) {
+        // ---- P~ -> E4M3: byte 16t' + r of operand blk = key of s[2 blk + t'][r]
+        v8i pk[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = (float)st[t][r] * c2;
-        if (need_mask) {
-          const int key = j * 64 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= a.S || (CAUSAL && key > qi)) v = -INFINITY;
+          for (int w = 0; w < 8; ++w) {
+            const int i0 = 32 * blk + 4 * w;
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0], p[i0 + 1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0 + 2], p[i0 + 3], word, true);
+            pk[blk][w] = word;
+          }
+        // ---- O^T = alpha * O^T + V^T . P^T (inner sum over the tile's 128 keys)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          v16f inner = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const int row = blk * D + 32 * c + qn;
+            const v4i lo = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh, row));
+            const v4i hi = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh + 1, row));
+            const v8i vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            inner = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk[blk], inner, 0, 0, 0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[c][r] = alpha * O[c][r] + inner[r];
         }
-        x[16 * t + r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    const float sub = PV == 0 ? mn - kLog2_448 : mn;
-    float ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(x[i] - sub);
-      ps += x[i];
-    }
-    l = alpha * l + ps;
-    m = mn;
-
-    if (PV == 0) {
-      // ---- P~ -> E4M3 (byte 16t + r = key of st[t][r]), then O^T += V^T . P^T
-      v8i pk;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w], x[4 * w + 1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], word, true);
-        pk[w] = word;
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int row = 32 * c + qn;
-        const v4i lo = *reinterpret_cast<const v4i *>(v_lds + row * 64 + 16 * swz<4>(2 * hh, row));
-        const v4i hi = *reinterpret_cast<const v4i *>(v_lds + row * 64 + 16 * swz<4>(2 * hh + 1, row));
-        const v8i vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const v16f zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        const v16f inner = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[c][r] = alpha * O[c][r] + inner[r];
       }
     } else {
-      // ---- P~ -> fp16, O^T += V^T . P^T with four K=16 steps per tile
-      v8h ph[4];
+      // ---- pv fp16: P~ -> fp16, O rescaled, then O^T += V^T . P^T with fp32
+      //      accumulation in the MFMA; V is staged one 64-key block at a time
+      //      by the whole work-group (every wavefront takes part in the barriers)
+      v8h ph[8];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s8 = 0; s8 < 8; ++s8)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ph[s][i] = (_Float16)x[8 * s + i];
+        for (int i = 0; i < 8; ++i) ph[s8][i] = (_Float16)p[8 * s8 + i];
+      if (work) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int row = 32 * c + qn;
-        v16f inner = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const v8h vf = *reinterpret_cast<const v8h *>(v_lds + row * 128 + 16 * swz<8>(4 * hh + s, row));
-          inner = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ph[s], inner, 0, 0, 0);
+          for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
+      }
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        stage_v16<D, DT>(a, hv, key0 + 64 * blk, vb, tid);
+        __syncthreads();
+        if (work) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int row = 32 * c + qn;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const v8h vf = *reinterpret_cast<const v8h *>(vb + row * 128 + 16 * swz<8>(4 * hh + s4, row));
+              O[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ph[4 * blk + s4], O[c], 0, 0, 0);
+            }
+          }
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[c][r] = alpha * O[c][r] + inner[r];
+        __syncthreads();
       }
     }
+  };
+
+  if (PV == 0 && tid < D) vsc[tid] = a.v_scale[(long long)bh * D + tid];
+
+  // ---- main loop: tile j computed from buffer j % 2 while tile j + 1 lands in the other
+  issue_tile<D, PV>(kbase, vbase, kbuf0, vbuf0, wave, lane);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles)
+      issue_tile<D, PV>(kbase + (long long)(j + 1) * kTileN * D, vbase + (long long)(j + 1) * kTileN * D, kbuf1,
+                        vbuf1, wave, lane);
+    tile(j, kbuf0, vbuf0);
+    wait_dma();
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles)
+      issue_tile<D, PV>(kbase + (long long)(j + 2) * kTileN * D, vbase + (long long)(j + 2) * kTileN * D, kbuf0,
+                        vbuf0, wave, lane);
+    tile(j + 1, kbuf1, PV == 0 ? vbuf1 : vbuf0);
+    wait_dma();
+    __syncthreads();
   }
 
   if (!active) return;
@@ -300,9 +388,11 @@ __global__ __launch_bounds__(kThreads) void k_attn(const AttnArgs a) {
       const int d0 = 32 * c + 8 * g + 4 * hh;
       float o[4];
       if (PV == 0) {
-        const float *vs = a.v_scale + (long long)bh * D + d0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = O[c][4 * g + i] * (vs[i] * rl);
+        const float4 vs = *reinterpret_cast<const float4 *>(vsc + d0);
+        o[0] = O[c][4 * g + 0] * (vs.x * rl);
+        o[1] = O[c][4 * g + 1] * (vs.y * rl);
+        o[2] = O[c][4 * g + 2] * (vs.z * rl);
+        o[3] = O[c][4 * g + 3] * (vs.w * rl);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = O[c][4 * g + i] * rl;

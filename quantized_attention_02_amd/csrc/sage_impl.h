@@ -16,7 +16,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kBlkQ = 32;  // Q tokens per INT8 scale (one wavefront's MFMA row tile)
-constexpr int kBlkK = 64;  // K tokens per INT8 scale = keys per attention tile
+constexpr int kBlkK = 64;  // K tokens per INT8 scale (one 64-key block)
+constexpr int kKvPad = 128;  // K / V buffers hold roundup(S, 128) keys: whole 128-key tiles
 
 // Geometry of one attention head inside a physical HND / NHD tensor:
 // element (s, d) of head (b, h) lives at base + s * tok_stride + d.

@@ -302,24 +302,44 @@ def pin_smoothing_invariance_random_shift():
     assert cos(b, ex) >= 0.999
 
 
-def pin_single_block_equals_blocked():
-    """With one key block the online softmax reduces to the plain one.  K is
-    quantised with one scale for the whole head in both runs, so the runs differ
-    only in where p~ is rounded (relative to the running max vs the global max)."""
+def pin_single_tile_equals_tiled():
+    """With one key tile (tile_k = S) the online softmax reduces to the plain
+    one; smaller tiles differ only in where p~ is rounded (relative to the
+    running max of the tiles seen so far instead of the global max)."""
     S, D = 256, 64
     qf, kf, vf = _rand_head(S, D, seed=31)
     q8, qs = O.quant_q_head(qf, 32)
-    k8, ks1, _ = O.quant_k_head(kf, S, True)
+    k8, ks, _ = O.quant_k_head(kf, 64, True)
     v8, vs = O.quant_v_head(vf)
     res = {}
     for pv in (O.PV_FP8, O.PV_FP16):
-        for blk in (64, S):
-            ks = np.repeat(ks1, S // blk)
-            res[pv, blk] = O.attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=F16, is_causal=False,
-                                            sm_scale=0.125, pv_mode=pv, blk_k=blk)
-    assert cos(res[O.PV_FP8, 64], res[O.PV_FP8, S]) >= 0.999
-    # fp16 keeps 11 significant bits of p~, so blocking changes almost nothing
-    assert rel_l1(res[O.PV_FP16, 64], res[O.PV_FP16, S]) < 1e-3, rel_l1(res[O.PV_FP16, 64], res[O.PV_FP16, S])
+        for tile in (64, 128, S):
+            res[pv, tile] = O.attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=F16, is_causal=False,
+                                             sm_scale=0.125, pv_mode=pv, blk_k=64, tile_k=tile)
+    for tile in (64, 128):
+        assert cos(res[O.PV_FP8, tile], res[O.PV_FP8, S]) >= 0.999
+        # fp16 keeps 11 significant bits of p~, so tiling changes almost nothing
+        assert rel_l1(res[O.PV_FP16, tile], res[O.PV_FP16, S]) < 1e-3
+    # the tile must not change which INT8 scale a key uses: with all-equal K
+    # scales, tiles of 64 and 128 give identical fp16-mode results up to rounding
+    assert rel_l1(res[O.PV_FP16, 64], res[O.PV_FP16, 128]) < 1e-3
+
+
+def pin_k_scale_per_block():
+    """Each key uses the scale of its own 64-token INT8 block: with one K block
+    100x larger than the others, the output still tracks exact attention only
+    if every key is dequantised with its own block's scale."""
+    S, D = 256, 64
+    qf, kf, vf = _rand_head(S, D, seed=33, bias_sigma=0.0)
+    k2 = kf.copy()
+    k2[64:128] *= 100.0  # block 1 dominates in scale
+    ex = O.attn_exact_head(qf, k2, vf, is_causal=False, sm_scale=0.125 / 10)
+    q8, qs = O.quant_q_head(qf, 32)
+    k8, ks, _ = O.quant_k_head(k2, 64, False)
+    v8, vs = O.quant_v_head(vf)
+    got = O.attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=F16, is_causal=False, sm_scale=0.125 / 10,
+                           pv_mode=O.PV_FP8)
+    assert cos(got, ex) >= 0.999, cos(got, ex)
 
 
 def pin_v_ones_row_sums():

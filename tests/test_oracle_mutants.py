@@ -2,6 +2,7 @@
 pins catch every one of them (a mutant that passes all pins would mean the pins
 do not constrain that part of the oracle)."""
 import os
+import re
 import subprocess
 import sys
 
@@ -27,7 +28,9 @@ MUTANTS = [
     ("causal_masks_diagonal", "(is_causal && n > i)", "(is_causal && n >= i)"),
     ("round_ties_away", "return nearbyint(a / q) * q;", "return round(a / q) * q;"),
     ("e4m3_bias_8", "ldexp(1.0 + fr / 8.0, ex - 7)", "ldexp(1.0 + fr / 8.0, ex - 8)"),
-    ("missing_sm_scale", "float c = (dq * k_scale[j]) * sm_scale;", "float c = dq * k_scale[j];"),
+    ("missing_sm_scale", "float c = (dq * k_scale[n / blk_k]) * sm_scale;", "float c = dq * k_scale[n / blk_k];"),
+    ("k_scale_indexed_by_tile", "float c = (dq * k_scale[n / blk_k])", "float c = (dq * k_scale[n / tile_k])"),
+    ("k_scale_first_block_only", "float c = (dq * k_scale[n / blk_k])", "float c = (dq * k_scale[0])"),
     ("q_scale_wrong_block", "float dq = q_scale[i / blk_q];", "float dq = q_scale[i / blk_k];"),
     ("exact_causal_off_by_one", "int nvis = is_causal ? i + 1 : S;", "int nvis = is_causal ? (i > 0 ? i : 1) : S;"),
     ("fp16_pv_no_rounding", "pq[t] = round_f16(p[t]);", "pq[t] = p[t];"),
@@ -54,8 +57,17 @@ sys.exit(3)
 @pytest.mark.parametrize("mid,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_planted_mistake_is_caught(orc, tmp_path, mid, old, new):
     src = open(SRC).read()
-    assert src.count(old) >= 1, "mutation site vanished from the oracle source"
-    mutated = src.replace(old, new, 1)
+    code_only = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    assert code_only.count(old) >= 1, "mutation site vanished from the oracle code"
+    # mutate the first occurrence that lies in code, not in a comment
+    pos, start = -1, 0
+    while True:
+        pos = src.index(old, start)
+        opened, closed = src.rfind("/*", 0, pos), src.rfind("*/", 0, pos)
+        if opened <= closed:
+            break
+        start = pos + 1
+    mutated = src[:pos] + new + src[pos + len(old):]
     c = tmp_path / "mutant.c"
     c.write_text(mutated)
     so = str(tmp_path / "libmutant.so")
