@@ -81,13 +81,18 @@ extern "C" {
 #define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
 #define SAGE_BLK_K 64 /* K tokens per INT8 scale: one 64-key block of the attention loop */
 #define SAGE_KV_PAD 128 /* K / V buffers are padded to whole 128-key tiles */
+/* Keys per online-softmax tile of sage_attn_fwd (FlashAttention blocking); the
+ * FP8 rounding of P~ and the fold of the two-level accumulation happen per tile. */
+#define SAGE_TILE_K_FP8 128
+#define SAGE_TILE_K_FP16 128
 #define SAGE_MAX_S (1 << 20)
 #define SAGE_MAX_BH (1 << 16)
 /* key held by byte p (0..63) of a v_fp8 tile row */
 #define SAGE_VPOS_KEY(p) (32 * (((p) & 31) >> 4) + 8 * (((p) & 15) >> 2) + 4 * ((p) >> 5) + ((p) & 3))
 
-/* Quantisation granularity (tokens per scale) used by every entry point. */
-int sage_get_config(int *blk_q, int *blk_k);
+/* Quantisation granularity (tokens per scale) and the attention key tile per
+ * pv mode used by every entry point (the constants above). */
+int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16);
 
 /* Bytes of each intermediate buffer for a problem shape (see the layouts
  * above).  Any output pointer may be NULL. */
@@ -121,7 +126,8 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
 
 /*
  * Fused quantized attention ([SA2]; [KAI] 2.1; [GUIDE] 五分钟跑通, 性能调优实战).
- * For each query row i, key tiles of SAGE_BLK_K keys in order, fp32 online softmax:
+ * For each query row i, key tiles (SAGE_TILE_K_FP8 / SAGE_TILE_K_FP16 keys) in order,
+ * fp32 online softmax:
  *   s_n = float(q_i8[i] . k_i8[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA, int32 sums)
  *   keys n >= S, and n > i when is_causal (square, top-left aligned), are excluded
  *   m' = max(m, max_n s_n);  alpha = exp(m - m');  p_n = exp(s_n - m');  l = alpha*l + sum p_n

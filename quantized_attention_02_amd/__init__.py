@@ -27,6 +27,7 @@ LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
 PV = {"fp8": 0, "fp16": 1}
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
+TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
 EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_attn_fwd",
             "sage_attn_fwd_dump_qk", "sage_status_str", "sage_check_arch"]
@@ -48,7 +49,7 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: run `python -m quantized_attention_02_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         c_int, c_float, c_void_p, c_size_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
-        L.sage_get_config.argtypes = [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+        L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
         L.sage_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 7
         L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 6 + [c_void_p] * 5 + [c_void_p]
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p, c_void_p, c_void_p]
@@ -78,9 +79,10 @@ def _check(status: int, what: str):
 
 # ----------------------------------------------------------------- raw entry points
 def sage_get_config():
-    bq, bk = ctypes.c_int(), ctypes.c_int()
-    _check(lib().sage_get_config(ctypes.byref(bq), ctypes.byref(bk)), "sage_get_config")
-    return bq.value, bk.value
+    """(blk_q, blk_k, tile_k_fp8, tile_k_fp16)"""
+    v = [ctypes.c_int() for _ in range(4)]
+    _check(lib().sage_get_config(*[ctypes.byref(x) for x in v]), "sage_get_config")
+    return tuple(x.value for x in v)
 
 
 def sage_buffer_sizes(B, H, S, D):

@@ -116,10 +116,12 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
 
 extern "C" {
 
-int sage_get_config(int *blk_q, int *blk_k) {
-  if (!blk_q || !blk_k) return SAGE_ERR_INVALID_ARG;
+int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16) {
+  if (!blk_q || !blk_k || !tile_k_fp8 || !tile_k_fp16) return SAGE_ERR_INVALID_ARG;
   *blk_q = SAGE_BLK_Q;
   *blk_k = SAGE_BLK_K;
+  *tile_k_fp8 = attn_tile_keys(SAGE_PV_FP8);
+  *tile_k_fp16 = attn_tile_keys(SAGE_PV_FP16);
   return SAGE_OK;
 }
 

@@ -36,11 +36,23 @@
 
 namespace sage {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kWaves * 32;
-constexpr int kTileN = 128;  // keys per loop iteration (two INT8 K blocks)
-constexpr float kLog2_448 = 8.807354922057604f;  // log2(448): folds the static P~ scale into exp2
+constexpr float kLog2_448 = 8.807354922057604f;
+
+#ifndef SAGE_ATTN_TN_FP8
+#define SAGE_ATTN_TN_FP8 128
+#endif
+#ifndef SAGE_ATTN_WPS_FP8
+#define SAGE_ATTN_WPS_FP8 2
+#endif
+#ifndef SAGE_ATTN_WAVES_FP8
+#define SAGE_ATTN_WAVES_FP8 4
+#endif
+#ifndef SAGE_ATTN_SETPRIO
+#define SAGE_ATTN_SETPRIO 0
+#endif
+#ifndef SAGE_ATTN_NBUF_FP8
+#define SAGE_ATTN_NBUF_FP8 2
+#endif  // log2(448): folds the static P~ scale into exp2
 
 // XOR swizzle of the 16-byte chunks of an LDS row (CH = chunks per row) so that
 // the 16 lanes an LDS read serves together hit 16 distinct bank groups when
@@ -60,15 +72,45 @@ __device__ __forceinline__ void dma16(const void *src, uint8_t *lds_base) {
 
 // Two consecutive floats at a wave-uniform address, read with a scalar load
 // (constant address space), which the vector-memory counter does not track.
+__device__ __forceinline__ float load1_uniform(const float *p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  typedef const __attribute__((address_space(4))) float *cptr;
+  return *(cptr)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float2 load2_uniform(const float *p) {
   const uint64_t u = (uint64_t)p;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  typedef const __attribute__((address_space(4))) float2 *cptr;
-  return *(cptr)(((uint64_t)hi << 32) | lo);
+  typedef const __attribute__((address_space(4))) float *cptr;
+  const cptr q = (cptr)(((uint64_t)hi << 32) | lo);
+  float2 r;
+  r.x = q[0];
+  r.y = q[1];
+  return r;
 }
 
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// s_waitcnt vmcnt(N) (expcnt / lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Max / sum of a value over the two half-waves (lanes i and i ^ 32 hold the
+// same query row).  v_permlane32_swap exchanges the halves between its two
+// outputs; one output then holds the lane's own value and the other its
+// partner's, so the pair's max and sum need no lane-dependent select.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int DT>
 __device__ __forceinline__ void store4(void *out, long long off, float a, float b, float c, float d) {
@@ -78,26 +120,26 @@ __device__ __forceinline__ void store4(void *out, long long off, float a, float 
   *reinterpret_cast<v2i *>(reinterpret_cast<uint16_t *>(out) + off) = w;
 }
 
-// Copy a K tile (128 x D int8) and, in pv fp8 mode, its two FP8 V blocks
-// (2 x D x 64, contiguous in HBM) into LDS, swizzled.  Each wavefront issues
-// its share of the 1 KiB wave-copies.
-template <int D, int PV>
+// Copy a K tile (TN x D int8) and, in pv fp8 mode, its FP8 V blocks
+// (TN/64 x D x 64, contiguous in HBM) into LDS, swizzled.  Each wavefront
+// issues its share of the 1 KiB wave-copies.
+template <int D, int PV, int TN, int WAVES>
 __device__ __forceinline__ void issue_tile(const int8_t *kt, const uint8_t *vt, uint8_t *kbuf, uint8_t *vbuf,
                                            int wave, int lane) {
   constexpr int KCH = D / 16;
-  constexpr int KLOADS = kTileN * D / 1024;
+  constexpr int KLOADS = TN * D / 1024;
   constexpr int KROWS = 1024 / D;
 #pragma unroll
-  for (int i = 0; i < KLOADS / kWaves; ++i) {
-    const int w = wave + kWaves * i;
+  for (int i = 0; i < KLOADS / WAVES; ++i) {
+    const int w = wave + WAVES * i;
     const int row = w * KROWS + lane / KCH;
     dma16(kt + row * D + 16 * swz<KCH>(lane % KCH, row), kbuf + w * 1024);
   }
   if (PV == 0) {
-    constexpr int VLOADS = 2 * D * 64 / 1024;
+    constexpr int VLOADS = TN * D / 1024;
 #pragma unroll
-    for (int i = 0; i < VLOADS / kWaves; ++i) {
-      const int w = wave + kWaves * i;
+    for (int i = 0; i < VLOADS / WAVES; ++i) {
+      const int w = wave + WAVES * i;
       const int row = w * 16 + (lane >> 2);
       dma16(vt + row * 64 + 16 * swz<4>(lane & 3, row), vbuf + w * 1024);
     }
@@ -107,12 +149,12 @@ __device__ __forceinline__ void issue_tile(const int8_t *kt, const uint8_t *vt, 
 // pv fp16: original 16-bit V rows [n0, n0 + 64) -> fp16 V^T rows (128 bytes,
 // vpos_key order, swizzled) in `vb`.  Staged through VGPRs: the layout change
 // and the bf16 -> fp16 rounding need the values in registers anyway.
-template <int D, int DT>
+template <int D, int DT, int THREADS>
 __device__ __forceinline__ void stage_v16(const AttnArgs &a, const HeadView &hv, int n0, uint8_t *vb, int tid) {
   const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(a.v);
   constexpr int NU = 32 * (D / 8);  // key pairs x 8-channel groups
 #pragma unroll
-  for (int u = tid; u < NU; u += kThreads) {
+  for (int u = tid; u < NU; u += THREADS) {
     const int pair = u / (D / 8), c8 = (u % (D / 8)) * 8;
     const int n = n0 + 2 * pair;
     v4i t0 = {0, 0, 0, 0}, t1 = {0, 0, 0, 0};
@@ -133,16 +175,24 @@ __device__ __forceinline__ void stage_v16(const AttnArgs &a, const HeadView &hv,
   }
 }
 
-template <int D, int PV, int DT, bool CAUSAL, bool DUMP>
-__global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
+// TN: keys per loop iteration (64 or 128, i.e. one or two INT8 K blocks);
+// WPS: wavefronts per SIMD the register budget is sized for; WAVES: wavefronts
+// per work-group (32 query rows each); NBUF: LDS tile buffers (prefetch
+// distance NBUF - 1).
+template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int TN, int WPS, int WAVES, int NBUF>
+__global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
+k_attn(const AttnArgs a) {
+  constexpr int kThreads = WAVES * 64;
+  constexpr int kBlockM = WAVES * 32;
   constexpr int NC = D / 32;
   constexpr int KCH = D / 16;
-  constexpr int KBYTES = kTileN * D;                         // K tile
-  constexpr int VBYTES = PV == 0 ? 2 * D * 64 : D * 128;     // fp8: two 64-key blocks; fp16: one block
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[VBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[PV == 0 ? VBYTES : 1024];
+  constexpr int NB = TN / 64;                                // INT8 K blocks per tile
+  constexpr int NT = TN / 32;                                // 32-key sub-tiles per tile
+  constexpr int KBYTES = TN * D;                             // K tile
+  constexpr int VBYTES = PV == 0 ? TN * D : D * 128;         // fp8: NB 64-key blocks; fp16: one block
+  constexpr int NVBUF = PV == 0 ? NBUF : 1;                 // fp16 V is staged through VGPRs, one buffer
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -190,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
     for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
   }
 
-  int ntiles = a.S_k / kTileN;
-  if (CAUSAL) ntiles = min(ntiles, min(q0 + kBlockM - 1, a.S - 1) / kTileN + 1);
+  int ntiles = a.S_k / TN;
+  if (CAUSAL) ntiles = min(ntiles, min(q0 + kBlockM - 1, a.S - 1) / TN + 1);
 
   float m = -INFINITY;  // running max (log2 domain, scaled scores)
   float l = 0.0f;       // running sum over this half-wave's keys
@@ -206,61 +256,68 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
   const float *kscale = a.k_scale + (long long)bh * a.nk;
   const HeadView hv = head_view(a.layout, b, h, a.H, a.S, D);
 
-  // One 128-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
+  // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
   auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
-    const int key0 = j * kTileN;
+    const int key0 = j * TN;
     const bool work = active && !(CAUSAL && key0 > qw + 31);
-    // the tile's two K-block scales, read through a wave-uniform address (scalar loads)
-    const float2 ksv = load2_uniform(kscale + 2 * j);
-    const float ks[2] = {ksv.x, ksv.y};
-    float p[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) p[i] = 0.0f;
+    // the tile's K-block scales, read through a wave-uniform address (scalar loads)
+    float ks[NB];
+    if (NB == 2) {
+      const float2 ksv = load2_uniform(kscale + 2 * j);
+      ks[0] = ksv.x;
+      ks[NB - 1] = ksv.y;
+    } else {
+      ks[0] = load1_uniform(kscale + j);
+    }
+    float p[16 * NT];
     float alpha = 1.0f;
     if (work) {
-      // ---- S^T = K . Q^T for four 32-key sub-tiles; per 32-channel chunk the
-      //      four K fragments are read together, then four MFMAs consume them
-      v16i s[4];
+      // ---- S^T = K . Q^T for the NT 32-key sub-tiles; per 32-channel chunk the
+      //      NT K fragments are read together, then NT MFMAs consume them
+      v16i s[NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s[t] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < NT; ++t) s[t] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      if (SAGE_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        v4i kf[4];
+        v4i kf[NT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NT; ++t) {
           const int row = 32 * t + qn;
           kf[t] = *reinterpret_cast<const v4i *>(kb + row * D + 16 * swz<KCH>(2 * c + hh, row));
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t], qf[c], s[t], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t], qf[c], s[t], 0, 0, 0);
       }
+      if (SAGE_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       if (DUMP && bh == a.dump_bh && qi < a.S) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (key < a.S) a.dump[(long long)qi * a.S + key] = s[t][r];
           }
       }
-      float c2[2];
-      c2[0] = (dq * ks[0]) * a.sm2;
-      c2[1] = (dq * ks[1]) * a.sm2;
+      float c2[NB];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
       // ---- mask: only tiles that reach past S or cross the causal diagonal
-      const bool need_mask = (key0 + kTileN > a.S) || (CAUSAL && key0 + kTileN - 1 > qw);
+      // key (key0 + 4hh + kofs(t, r)) is excluded iff kofs(t, r) > lim, where
+      // kofs is a compile-time constant of the register slot
+      const bool need_mask = (key0 + TN > a.S) || (CAUSAL && key0 + TN - 1 > qw);
+      const int lim = (CAUSAL ? min(a.S - 1, qi) : a.S - 1) - key0 - 4 * hh;
       if (need_mask) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= a.S || (CAUSAL && key > qi)) s[t][r] = INT_MIN;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = INT_MIN;
       }
       // ---- row max on the int32 sums (c2 > 0 per 64-key block)
       float mt = -INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < NB; ++blk) {
         int mx = INT_MIN;
 #pragma unroll
         for (int t = 2 * blk; t < 2 * blk + 2; ++t)
@@ -268,72 +325,85 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
           for (int r = 0; r < 16; ++r) mx = max(mx, s[t][r]);
         if (mx != INT_MIN) mt = fmaxf(mt, (float)mx * c2[blk]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = halves_max(mt);
       const float mn = fmaxf(m, mt);
       alpha = __builtin_amdgcn_exp2f(m - mn);
       const float sub = PV == 0 ? mn - kLog2_448 : mn;
       m = mn;
-      // ---- p = exp2(s * c2 - sub)  (= 448 p~ in fp8 mode), row sum
+      // ---- p = exp2(s * c2 - sub)  (= 448 p~ in fp8 mode); masked keys are then
+      //      zeroed in a separate pass that only boundary tiles take; row sum
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2[t >> 1], -sub));
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * t + 8 * (r >> 2) + (r & 3) > lim) p[16 * t + r] = 0.0f;
+      }
       float ps = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = __builtin_fmaf((float)s[t][r], c2[t >> 1], -sub);
-          if (need_mask && s[t][r] == INT_MIN) x = -INFINITY;
-          p[16 * t + r] = __builtin_amdgcn_exp2f(x);
-          ps += p[16 * t + r];
-        }
+      for (int i = 0; i < 16 * NT; ++i) ps += p[i];
       l = alpha * l + ps;
     }
 
     if constexpr (PV == 0) {
       if (work) {
         // ---- P~ -> E4M3: byte 16t' + r of operand blk = key of s[2 blk + t'][r]
-        v8i pk[2];
+        v8i pk[NB];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int i0 = 32 * blk + 4 * w;
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0], p[i0 + 1], 0, false);
+            // the word's upper half is written by the next conversion, so its
+            // initial content is left unspecified (no register copy for it)
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0], p[i0 + 1], __builtin_nondeterministic_value(0), false);
             word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0 + 2], p[i0 + 3], word, true);
             pk[blk][w] = word;
           }
-        // ---- O^T = alpha * O^T + V^T . P^T (inner sum over the tile's 128 keys)
+        // ---- O^T = alpha * O^T + V^T . P^T.  Two-level accumulation: each MFMA
+        //      sums its 64 FP8 products in the matrix core's own accumulator
+        //      (level 1) and adds that partial sum to the fp32 O registers passed
+        //      as its C operand (level 2).  O is rescaled in place first; the
+        //      rescale is skipped when no row of the wavefront changed its max.
+        const bool rescale = __any(alpha != 1.0f);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          v16f inner = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+          if (rescale) {
 #pragma unroll
-          for (int blk = 0; blk < 2; ++blk) {
+            for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
+          }
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) {
             const int row = blk * D + 32 * c + qn;
             const v4i lo = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh, row));
             const v4i hi = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh + 1, row));
-            const v8i vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            inner = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk[blk], inner, 0, 0, 0, 0, 0, 0);
+            const v8i vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            O[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk[blk], O[c], 0, 0, 0, 0, 0, 0);
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[c][r] = alpha * O[c][r] + inner[r];
         }
       }
     } else {
       // ---- pv fp16: P~ -> fp16, O rescaled, then O^T += V^T . P^T with fp32
       //      accumulation in the MFMA; V is staged one 64-key block at a time
       //      by the whole work-group (every wavefront takes part in the barriers)
-      v8h ph[8];
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ph[s8][i] = (_Float16)p[8 * s8 + i];
+      v8h ph[2 * NT];
       if (work) {
+#pragma unroll
+        for (int s8 = 0; s8 < 2 * NT; ++s8)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ph[s8][i] = (_Float16)p[8 * s8 + i];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
       }
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        stage_v16<D, DT>(a, hv, key0 + 64 * blk, vb, tid);
+      for (int blk = 0; blk < NB; ++blk) {
+        stage_v16<D, DT, kThreads>(a, hv, key0 + 64 * blk, vb, tid);
         __syncthreads();
         if (work) {
 #pragma unroll
@@ -353,29 +423,36 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
 
   if (PV == 0 && tid < D) vsc[tid] = a.v_scale[(long long)bh * D + tid];
 
-  // ---- main loop: tile j computed from buffer j % 2 while tile j + 1 lands in the other
-  issue_tile<D, PV>(kbase, vbase, kbuf0, vbuf0, wave, lane);
-  wait_dma();
+  // ---- main loop: tile j is computed from buffer j % NBUF while tiles
+  //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next
+  constexpr int LPT = (PV == 0 ? 2 : 1) * TN * D / 1024 / WAVES;  // DMA instructions per tile per wavefront
+  const long long tile_bytes = (long long)TN * D;
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u)
+    if (u < ntiles) issue_tile<D, PV, TN, WAVES>(kbase + u * tile_bytes, vbase + u * tile_bytes, kbuf[u],
+                                                 vbuf[PV == 0 ? u : 0], wave, lane);
+  wait_vm<0>();
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles)
-      issue_tile<D, PV>(kbase + (long long)(j + 1) * kTileN * D, vbase + (long long)(j + 1) * kTileN * D, kbuf1,
-                        vbuf1, wave, lane);
-    tile(j, kbuf0, vbuf0);
-    wait_dma();
-    __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles)
-      issue_tile<D, PV>(kbase + (long long)(j + 2) * kTileN * D, vbase + (long long)(j + 2) * kTileN * D, kbuf0,
-                        vbuf0, wave, lane);
-    tile(j + 1, kbuf1, PV == 0 ? vbuf1 : vbuf0);
-    wait_dma();
-    __syncthreads();
+  for (int j0 = 0; j0 < ntiles; j0 += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int j = j0 + u;
+      if (j >= ntiles) break;
+      const int jn = j + NBUF - 1;  // prefetch target, into the buffer freed by tile j - 1
+      const int un = (u + NBUF - 1) % NBUF;
+      if (jn < ntiles)
+        issue_tile<D, PV, TN, WAVES>(kbase + jn * tile_bytes, vbase + jn * tile_bytes, kbuf[un],
+                                     vbuf[PV == 0 ? un : 0], wave, lane);
+      tile(j, kbuf[u], vbuf[PV == 0 ? u : 0]);
+      if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
+      else wait_vm<0>();
+      __syncthreads();
+    }
   }
 
   if (!active) return;
   // ---- epilogue: combine the two half-wave sums, normalise, store
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = halves_sum(l);
   if (qi >= a.S) return;
   const float rl = 1.0f / lt;
   long long off;
@@ -401,31 +478,47 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn(const AttnArgs a) {
     }
 }
 
+// Tile shape per mode: 128-key tiles at 2 wavefronts per SIMD (measured on
+// MI355X against 64-key tiles at 2 and 3 wavefronts per SIMD: fewer row-max
+// exchanges and O rescales per key outweigh the lower occupancy).
+template <int PV>
+struct TileCfg {
+  static constexpr int TN = PV == 0 ? SAGE_ATTN_TN_FP8 : 128;
+  static constexpr int WPS = PV == 0 ? SAGE_ATTN_WPS_FP8 : 2;
+  static constexpr int WAVES = PV == 0 ? SAGE_ATTN_WAVES_FP8 : 4;
+  static constexpr int NBUF = PV == 0 ? SAGE_ATTN_NBUF_FP8 : 2;
+};
+
 template <int D, int PV, int DT, bool CAUSAL>
-static hipError_t launch4(const AttnArgs &a, bool dump, dim3 grid, hipStream_t st) {
-  if (dump) hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, true>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false>), grid, dim3(kThreads), 0, st, a);
+static hipError_t launch4(const AttnArgs &a, bool dump, hipStream_t st) {
+  using C = TileCfg<PV>;
+  AttnArgs b = a;
+  b.nmblk = (a.S + 32 * C::WAVES - 1) / (32 * C::WAVES);
+  const dim3 grid(a.B * a.H * b.nmblk), block(64 * C::WAVES);
+  if (dump) hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, true, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st, b);
+  else hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st, b);
   return hipGetLastError();
 }
 
 template <int D, int PV, int DT>
-static hipError_t launch3(const AttnArgs &a, bool dump, dim3 grid, hipStream_t st) {
-  return a.causal ? launch4<D, PV, DT, true>(a, dump, grid, st) : launch4<D, PV, DT, false>(a, dump, grid, st);
+static hipError_t launch3(const AttnArgs &a, bool dump, hipStream_t st) {
+  return a.causal ? launch4<D, PV, DT, true>(a, dump, st) : launch4<D, PV, DT, false>(a, dump, st);
 }
 
 template <int D, int PV>
-static hipError_t launch2(const AttnArgs &a, bool dump, dim3 grid, hipStream_t st) {
-  return a.dtype == 0 ? launch3<D, PV, 0>(a, dump, grid, st) : launch3<D, PV, 1>(a, dump, grid, st);
+static hipError_t launch2(const AttnArgs &a, bool dump, hipStream_t st) {
+  return a.dtype == 0 ? launch3<D, PV, 0>(a, dump, st) : launch3<D, PV, 1>(a, dump, st);
 }
 
 template <int D>
-static hipError_t launch1(const AttnArgs &a, bool dump, dim3 grid, hipStream_t st) {
-  return a.pv == 0 ? launch2<D, 0>(a, dump, grid, st) : launch2<D, 1>(a, dump, grid, st);
+static hipError_t launch1(const AttnArgs &a, bool dump, hipStream_t st) {
+  return a.pv == 0 ? launch2<D, 0>(a, dump, st) : launch2<D, 1>(a, dump, st);
 }
 
+int attn_tile_keys(int pv_mode) { return pv_mode == 0 ? TileCfg<0>::TN : TileCfg<1>::TN; }
+
 hipError_t launch_attn(const AttnArgs &a, bool dump, hipStream_t stream) {
-  const dim3 grid(a.B * a.H * a.nmblk);
-  return a.D == 64 ? launch1<64>(a, dump, grid, stream) : launch1<128>(a, dump, grid, stream);
+  return a.D == 64 ? launch1<64>(a, dump, stream) : launch1<128>(a, dump, stream);
 }
 
 }  // namespace sage

@@ -104,5 +104,6 @@ struct AttnArgs {
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);
 hipError_t launch_quant_v(const QuantVArgs &a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs &a, bool dump, hipStream_t stream);
+int attn_tile_keys(int pv_mode);  // keys per online-softmax tile of the attention kernel
 
 }  // namespace sage

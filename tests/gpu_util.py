@@ -11,6 +11,9 @@ import oracle as O
 import quantized_attention_02_amd as qa
 from quantized_attention_02_amd import synth
 
+# Method parameters of the attention kernel (include/sage.h): keys per online-
+# softmax tile in each pv mode; the oracle is run with the same tiling.
+TILE_K = {"fp8": 128, "fp16": 128}
 VPOS_KEY = np.array([32 * ((p & 31) >> 4) + 8 * ((p & 15) >> 2) + 4 * (p >> 5) + (p & 3) for p in range(64)])
 
 

@@ -32,12 +32,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_and_sizes():
-    assert qa.sage_get_config() == (32, 64)
+    assert qa.sage_get_config() == (32, 64, qa.TILE_K["fp8"], qa.TILE_K["fp16"])
     s = qa.sage_buffer_sizes(2, 3, 100, 64)
     assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 4 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 2 * 4,
                  "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4}
     L = qa.lib()
-    assert L.sage_get_config(None, None) == qa.SAGE_ERR_INVALID_ARG
+    assert L.sage_get_config(None, None, None, None) == qa.SAGE_ERR_INVALID_ARG
     for bad in [(0, 1, 1, 64), (1, 0, 1, 64), (1, 1, 0, 64), (1, 1, 1, 96), (1, 1, (1 << 20) + 1, 64)]:
         assert L.sage_buffer_sizes(*bad, *([None] * 7)) == qa.SAGE_ERR_INVALID_ARG
 

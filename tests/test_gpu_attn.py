@@ -50,7 +50,7 @@ def _ids(cases):
 def _oracle_rows(w, b, h, rows, causal, pv):
     q, k, v = G.inputs(w)
     res = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal,
-                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=[(b, h)], rows=rows)
+                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=[(b, h)], rows=rows, tile_k=G.TILE_K[pv])
     return res[(b, h)]
 
 
@@ -60,7 +60,7 @@ def test_attn_matches_oracle_small(w, causal, pv):
     got = G.out_logical(out, w)
     q, k, v = G.inputs(w)
     ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal,
-                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16)
+                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, tile_k=G.TILE_K[pv])
     ref = np.stack([np.stack([ref[(b, h)] for h in range(w.H)]) for b in range(w.B)])
     assert np.isfinite(got).all()
     c, r = G.cos(got, ref), G.rel_l1(got, ref)
@@ -124,6 +124,12 @@ def test_qk_int32_dump_bit_exact(w, causal, head):
     assert np.array_equal(G.to_u16(out), G.to_u16(out2))
 
 
+def test_library_reports_the_documented_tiles():
+    import quantized_attention_02_amd as qa
+
+    assert qa.sage_get_config() == (32, 64, G.TILE_K["fp8"], G.TILE_K["fp16"])
+
+
 def test_deterministic_bitwise():
     w = synth.custom(2, 4, 700, 128, seed=401)
     for causal, pv in ((False, "fp8"), (True, "fp16")):
@@ -153,6 +159,6 @@ def test_sm_scale_is_applied():
         _, out, _ = G.run(w, sm_scale=sm)
         got = G.out_logical(out, w)
         q, k, v = G.inputs(w)
-        ref = O.attn(q, k, v, O.F16, "HND", sm_scale=sm)
+        ref = O.attn(q, k, v, O.F16, "HND", sm_scale=sm, tile_k=G.TILE_K["fp8"])
         ref = np.stack([ref[(0, h)] for h in range(2)])[None]
         assert G.cos(got, ref) >= COS_MIN and G.rel_l1(got, ref) <= REL_L1_MAX
