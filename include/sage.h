@@ -146,9 +146,10 @@ int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, 
 /*
  * Debug variant of sage_attn_fwd: the same kernel code, which additionally
  * writes the int32 accumulators of Q K^T for head (b, h) to qk, an int32 [S][S]
- * array (qk[i][n] = sum_d q_i8[i][d] * k_i8[n][d]).  Entries of 64-key tiles
- * that the causal mask skips entirely are left unwritten.  `out` is written as
- * by sage_attn_fwd.
+ * array (qk[i][n] = sum_d q_i8[i][d] * k_i8[n][d]).  With is_causal, entries
+ * with n > i may be left unwritten (key tiles the mask excludes for a whole
+ * work-group are skipped); every entry with n <= i is written.  `out` is
+ * written as by sage_attn_fwd.
  */
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
                           const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S,
