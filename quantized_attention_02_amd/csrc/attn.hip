@@ -32,6 +32,8 @@
 //    heads; causal work is issued longest query blocks first.
 #include <math.h>
 
+#include <type_traits>
+
 #include "sage_impl.h"
 
 namespace sage {
@@ -47,9 +49,6 @@ constexpr float kLog2_448 = 8.807354922057604f;
 #ifndef SAGE_ATTN_WAVES_FP8
 #define SAGE_ATTN_WAVES_FP8 4
 #endif
-#ifndef SAGE_ATTN_SETPRIO
-#define SAGE_ATTN_SETPRIO 0
-#endif
 #ifndef SAGE_ATTN_NBUF_FP8
 #define SAGE_ATTN_NBUF_FP8 2
 #endif  // log2(448): folds the static P~ scale into exp2
@@ -63,11 +62,19 @@ __device__ __forceinline__ int swz(int chunk, int row) {
   return chunk ^ ((row >> 2) & 3);
 }
 
-// One wavefront-wide LDS DMA: lane i copies 16 bytes from `src` to
-// lds_base + 16 * i (lds_base is the same for the whole wavefront).
-__device__ __forceinline__ void dma16(const void *src, uint8_t *lds_base) {
-  __builtin_amdgcn_global_load_lds(
-      src, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 16, 0, 0);
+// Buffer resource for `bytes` bytes at `base` (raw buffer: stride 0, 32-bit
+// data format).  Loads through it past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// One wavefront-wide buffer load into LDS: lane i copies 16 bytes from
+// resource offset soff + voff (voff per lane, soff wave-uniform) to
+// lds_base + 16 * i.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 16, voff,
+      soff, 0, 0);
 }
 
 // Two consecutive floats at a wave-uniform address, read with a scalar load
@@ -120,31 +127,47 @@ __device__ __forceinline__ void store4(void *out, long long off, float a, float 
   *reinterpret_cast<v2i *>(reinterpret_cast<uint16_t *>(out) + off) = w;
 }
 
-// Copy a K tile (TN x D int8) and, in pv fp8 mode, its FP8 V blocks
-// (TN/64 x D x 64, contiguous in HBM) into LDS, swizzled.  Each wavefront
-// issues its share of the 1 KiB wave-copies.
-template <int D, int PV, int TN, int WAVES>
-__device__ __forceinline__ void issue_tile(const int8_t *kt, const uint8_t *vt, uint8_t *kbuf, uint8_t *vbuf,
-                                           int wave, int lane) {
-  constexpr int KCH = D / 16;
-  constexpr int KLOADS = TN * D / 1024;
-  constexpr int KROWS = 1024 / D;
-#pragma unroll
-  for (int i = 0; i < KLOADS / WAVES; ++i) {
-    const int w = wave + WAVES * i;
-    const int row = w * KROWS + lane / KCH;
-    dma16(kt + row * D + 16 * swz<KCH>(lane % KCH, row), kbuf + w * 1024);
-  }
-  if (PV == 0) {
-    constexpr int VLOADS = TN * D / 1024;
-#pragma unroll
-    for (int i = 0; i < VLOADS / WAVES; ++i) {
-      const int w = wave + WAVES * i;
-      const int row = w * 16 + (lane >> 2);
-      dma16(vt + row * 64 + 16 * swz<4>(lane & 3, row), vbuf + w * 1024);
-    }
+// Sum of N floats as a balanced tree (independent adds instead of one serial
+// dependency chain).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float *x) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    return tree_sum<N / 2>(x) + tree_sum<N - N / 2>(x + N / 2);
   }
 }
+
+// Copy a K tile (TN x D int8) and, in pv fp8 mode, its FP8 V blocks
+// (TN/64 x D x 64, contiguous in HBM) into LDS, swizzled.  Each wavefront
+// issues its share of the 1 KiB wave-copies as buffer loads: scalar resource
+// and tile offset, per-lane offsets koff / voff computed once (tile_offsets).
+template <int D, int TN, int WAVES>
+struct TileCopy {
+  static constexpr int KCH = D / 16;
+  static constexpr int LOADS = TN * D / 1024 / WAVES;  // per wavefront, for K and again for V
+  uint32_t koff[LOADS], voff[LOADS];
+  __device__ __forceinline__ TileCopy(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int w = wave + WAVES * i;
+      const int krow = w * (1024 / D) + lane / KCH;
+      koff[i] = (uint32_t)(krow * D + 16 * swz<KCH>(lane % KCH, krow));
+      const int vrow = w * 16 + (lane >> 2);
+      voff[i] = (uint32_t)(vrow * 64 + 16 * swz<4>(lane & 3, vrow));
+    }
+  }
+  template <bool WITH_V>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int tile_off,
+                                        uint8_t *kbuf, uint8_t *vbuf, int wave) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) dma16_buf(krs, koff[i], tile_off, kbuf + (wave + WAVES * i) * 1024);
+    if (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) dma16_buf(vrs, voff[i], tile_off, vbuf + (wave + WAVES * i) * 1024);
+    }
+  }
+};
 
 // pv fp16: original 16-bit V rows [n0, n0 + 64) -> fp16 V^T rows (128 bytes,
 // vpos_key order, swizzled) in `vb`.  Staged through VGPRs: the layout change
@@ -195,7 +218,8 @@ k_attn(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
   const int hh = lane >> 5, qn = lane & 31;
 
   // ---- work-group -> (head, query block), XCD-aware
@@ -255,6 +279,9 @@ k_attn(const AttnArgs a) {
   const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + (long long)bh * a.S_k * D;
   const float *kscale = a.k_scale + (long long)bh * a.nk;
   const HeadView hv = head_view(a.layout, b, h, a.H, a.S, D);
+  const TileCopy<D, TN, WAVES> copy(wave, lane);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, a.S_k * D);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase, a.S_k * D);
 
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
   auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
@@ -272,33 +299,33 @@ k_attn(const AttnArgs a) {
     float p[16 * NT];
     float alpha = 1.0f;
     if (work) {
-      // ---- S^T = K . Q^T for the NT 32-key sub-tiles; per 32-channel chunk the
-      //      NT K fragments are read together, then NT MFMAs consume them
+      // ---- S^T = K . Q^T for the NT 32-key sub-tiles, one INT8 K block (two
+      //      sub-tiles) after the other, so that the first block's row max and
+      //      int -> float conversion can run while the second block's MFMAs do
       v16i s[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) s[t] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      if (SAGE_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      auto qk_block = [&](int blk) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        v4i kf[NT];
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int row = 32 * t + qn;
-          kf[t] = *reinterpret_cast<const v4i *>(kb + row * D + 16 * swz<KCH>(2 * c + hh, row));
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t], qf[c], s[t], 0, 0, 0);
-      }
-      if (SAGE_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-      if (DUMP && bh == a.dump_bh && qi < a.S) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key < a.S) a.dump[(long long)qi * a.S + key] = s[t][r];
+          for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
+            const int row = 32 * t + qn;
+            const v4i kf = *reinterpret_cast<const v4i *>(kb + row * D + 16 * swz<KCH>(2 * c + hh, row));
+            s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[c], s[t], 0, 0, 0);
           }
-      }
+      };
+      auto dump_s = [&]() {
+        if (DUMP && bh == a.dump_bh && qi < a.S) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (key < a.S) a.dump[(long long)qi * a.S + key] = s[t][r];
+            }
+        }
+      };
       float c2[NB];
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
@@ -307,24 +334,48 @@ k_attn(const AttnArgs a) {
       // kofs is a compile-time constant of the register slot
       const bool need_mask = (key0 + TN > a.S) || (CAUSAL && key0 + TN - 1 > qw);
       const int lim = (CAUSAL ? min(a.S - 1, qi) : a.S - 1) - key0 - 4 * hh;
-      if (need_mask) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = INT_MIN;
-      }
-      // ---- row max on the int32 sums (c2 > 0 per 64-key block)
-      float mt = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
+      // ---- per INT8 block: row max of the int32 sums (c2 > 0 per block) and
+      //      the sums converted to float
+      int mxb[NB];
+      float f[16 * NT];
+      auto max_convert = [&](int blk, int mlim, auto mask_tag) {
         int mx = INT_MIN;
 #pragma unroll
         for (int t = 2 * blk; t < 2 * blk + 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = max(mx, s[t][r]);
-        if (mx != INT_MIN) mt = fmaxf(mt, (float)mx * c2[blk]);
+          for (int r = 0; r < 16; ++r) {
+            const bool out = decltype(mask_tag)::value && 32 * t + 8 * (r >> 2) + (r & 3) > mlim;
+            mx = max(mx, out ? INT_MIN : s[t][r]);
+            f[16 * t + r] = out ? -INFINITY : (float)s[t][r];
+          }
+        mxb[blk] = mx;
+      };
+      // The MFMAs are issued inside each arm so that the unmasked arm's max and
+      // conversion sit in the same basic block as the MFMAs and can fill their
+      // issue gaps (the asm markers keep the compiler from hoisting the common
+      // MFMA code above the branch).
+      if (!need_mask) {
+        asm volatile("; unmasked tile" ::: "memory");
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) qk_block(blk);
+        dump_s();
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) max_convert(blk, 0, std::false_type());
+      } else {
+        // the mask bound passes through the asm so that its 64 comparisons
+        // stay in this arm rather than being hoisted into the common path
+        int mlim = lim;
+        asm volatile("; masked tile" : "+v"(mlim) :: "memory");
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) qk_block(blk);
+        dump_s();
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) max_convert(blk, mlim, std::true_type());
       }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+        if (mxb[blk] != INT_MIN) mt = fmaxf(mt, (float)mxb[blk] * c2[blk]);
       mt = halves_max(mt);
       const float mn = fmaxf(m, mt);
       alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -335,18 +386,17 @@ k_attn(const AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2[t >> 1], -sub));
+        for (int r = 0; r < 16; ++r) p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[16 * t + r], c2[t >> 1], -sub));
       if (need_mask) {
+        int mlim = lim;
+        asm volatile("; zero masked p" : "+v"(mlim) :: "memory");
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * t + 8 * (r >> 2) + (r & 3) > lim) p[16 * t + r] = 0.0f;
+            if (32 * t + 8 * (r >> 2) + (r & 3) > mlim) p[16 * t + r] = 0.0f;
       }
-      float ps = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16 * NT; ++i) ps += p[i];
-      l = alpha * l + ps;
+      l = alpha * l + tree_sum<16 * NT>(p);
     }
 
     if constexpr (PV == 0) {
@@ -358,9 +408,9 @@ k_attn(const AttnArgs a) {
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int i0 = 32 * blk + 4 * w;
-            // the word's upper half is written by the next conversion, so its
-            // initial content is left unspecified (no register copy for it)
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0], p[i0 + 1], __builtin_nondeterministic_value(0), false);
+            // the word's upper half is written by the next conversion; its
+            // initial content is p[i0]'s register, dead after this use
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0], p[i0 + 1], __float_as_int(p[i0]), false);
             word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0 + 2], p[i0 + 3], word, true);
             pk[blk][w] = word;
           }
@@ -369,13 +419,14 @@ k_attn(const AttnArgs a) {
         //      (level 1) and adds that partial sum to the fp32 O registers passed
         //      as its C operand (level 2).  O is rescaled in place first; the
         //      rescale is skipped when no row of the wavefront changed its max.
-        const bool rescale = __any(alpha != 1.0f);
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if (rescale) {
+          for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
-          }
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
 #pragma unroll
           for (int blk = 0; blk < NB; ++blk) {
             const int row = blk * D + 32 * c + qn;
@@ -426,11 +477,9 @@ k_attn(const AttnArgs a) {
   // ---- main loop: tile j is computed from buffer j % NBUF while tiles
   //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next
   constexpr int LPT = (PV == 0 ? 2 : 1) * TN * D / 1024 / WAVES;  // DMA instructions per tile per wavefront
-  const long long tile_bytes = (long long)TN * D;
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
-    if (u < ntiles) issue_tile<D, PV, TN, WAVES>(kbase + u * tile_bytes, vbase + u * tile_bytes, kbuf[u],
-                                                 vbuf[PV == 0 ? u : 0], wave, lane);
+    if (u < ntiles) copy.template issue<PV == 0>(krs, vrs, u * TN * D, kbuf[u], vbuf[PV == 0 ? u : 0], wave);
   wait_vm<0>();
   __syncthreads();
   for (int j0 = 0; j0 < ntiles; j0 += NBUF) {
@@ -440,9 +489,7 @@ k_attn(const AttnArgs a) {
       if (j >= ntiles) break;
       const int jn = j + NBUF - 1;  // prefetch target, into the buffer freed by tile j - 1
       const int un = (u + NBUF - 1) % NBUF;
-      if (jn < ntiles)
-        issue_tile<D, PV, TN, WAVES>(kbase + jn * tile_bytes, vbase + jn * tile_bytes, kbuf[un],
-                                     vbuf[PV == 0 ? un : 0], wave, lane);
+      if (jn < ntiles) copy.template issue<PV == 0>(krs, vrs, jn * TN * D, kbuf[un], vbuf[PV == 0 ? un : 0], wave);
       tile(j, kbuf[u], vbuf[PV == 0 ? u : 0]);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
