@@ -12,6 +12,8 @@
 // HND and the NHD layout.  Quantisation decisions are single, correctly
 // rounded fp32 operations (no contraction), so codes are reproducible
 // bit for bit on any IEEE machine.
+#include <type_traits>
+
 #include "sage_impl.h"
 
 #pragma clang fp contract(off)
@@ -22,7 +24,6 @@ static_assert(vpos_key(key_vpos(0)) == 0 && vpos_key(key_vpos(37)) == 37 && vpos
               "V tile key order must be a bijection");
 
 constexpr int kThreads = 256;
-constexpr int kSliceCh = 32;  // channels per work-group in the column passes (64 B of a 16-bit row)
 
 __device__ inline float wave_max(float x) {
 #pragma unroll
@@ -61,52 +62,107 @@ __device__ inline int8_t to_i8(float x, float inv) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1 (one launch, two roles by blockIdx):
-//   [0, B*H*D/32)        channel sums of K over all S tokens -> k_mean
-//   [B*H*D/32, + B*H*nq) INT8 quantisation of one 32-token block of Q
+// Per-channel reductions over the tokens of a head (the K channel sums and the
+// V channel abs-max) run as a two-level reduction: one work-group per
+// (head, chunk of tokens) writes per-chunk partials, and a small kernel
+// combines a head's partials.  The partials live in the head's region of the
+// output buffer that the next pass overwrites (k_i8 for K, v_fp8 for V), so
+// the entry points need no workspace: a chunk has at least 256 tokens, and
+// its 256 * D bytes of codes hold its D partials (8 bytes each) with room to
+// spare.
 // ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_kmean_qquant(const QuantQKArgs a) {
-  __shared__ double part[kThreads][8];
+constexpr int kMaxChunks = 32;
+
+// Tokens per chunk: a multiple of 256 such that a head has at most kMaxChunks
+// chunks (256 up to S = 8192).
+__host__ __device__ inline int chunk_tokens(int S) {
+  const int per = (S + kMaxChunks - 1) / kMaxChunks;
+  return ((per + 255) / 256) * 256;
+}
+__host__ __device__ inline int n_chunks(int S) {
+  const int c = chunk_tokens(S);
+  return (S + c - 1) / c;
+}
+
+// Thread layout of the chunk passes: G = D / 8 channel groups (16 bytes of a
+// 16-bit row) x R = 256 / G rows; the chunk's rows are loaded kUnroll at a
+// time so that many 16-byte loads are in flight per thread.
+template <int D>
+struct ChunkMap {
+  static constexpr int G = D / 8;
+  static constexpr int R = kThreads / G;
+  static constexpr int kUnroll = 8;
+};
+
+// K channel sums (binary64) of one chunk -> partials[chunk][D]; or, with
+// ABSMAX, V channel abs-max (fp32) of one chunk.
+template <int DT, int D, bool ABSMAX>
+__device__ inline void chunk_reduce(const uint16_t *x, const HeadView &hv, int S, int chunk, void *partials) {
+  using M = ChunkMap<D>;
+  typedef typename std::conditional<ABSMAX, float, double>::type acc_t;
+  __shared__ acc_t part[M::R][D];
+  const int tid = threadIdx.x, g = tid % M::G, r = tid / M::G;
+  const int ct = chunk_tokens(S);
+  const int s_end = min(S, (chunk + 1) * ct);
+  acc_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0;
+  for (int s0 = chunk * ct + r; s0 < s_end; s0 += M::R * M::kUnroll) {
+    float v[M::kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int s = s0 + u * M::R;
+      if (s < s_end) {
+        load8<DT>(x + hv.base + (long long)s * hv.tok_stride + 8 * g, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (ABSMAX) acc[i] = fmaxf(acc[i], fabsf(v[u][i]));
+        else acc[i] += (double)v[u][i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[r][8 * g + i] = acc[i];
+  __syncthreads();
+  if (tid < D) {
+    acc_t t = part[0][tid];
+    for (int rr = 1; rr < M::R; ++rr) {
+      if (ABSMAX) t = fmaxf(t, part[rr][tid]);
+      else t += part[rr][tid];
+    }
+    reinterpret_cast<acc_t *>(partials)[(long long)chunk * D + tid] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K channel sums of one chunk of tokens -> partials (k_i8 region of the head).
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
+  const int nch = n_chunks(a.S);
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  chunk_reduce<DT, D, false>((const uint16_t *)a.k, hv, a.S, chunk, a.k_i8 + (long long)bh * a.S_k * D);
+}
+
+// ---------------------------------------------------------------------------
+// INT8 quantisation of one 32-token block of Q.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
   __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x;
-  const int nslice = a.D / kSliceCh;
-  const int nsum = a.B * a.H * nslice;
-  const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k;
-
-  if ((int)blockIdx.x < nsum) {
-    // ---- K channel mean: thread = (row offset tid/4, 8-channel group tid%4)
-    const int bh = blockIdx.x / nslice, slice = blockIdx.x % nslice;
-    const int b = bh / a.H, h = bh % a.H;
-    const HeadView hv = head_view(a.layout, b, h, a.H, a.S, a.D);
-    const int grp = tid & 3, r0 = tid >> 2;
-    const int d0 = slice * kSliceCh + grp * 8;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s = r0; s < a.S; s += kThreads / 4) {
-      float x[8];
-      load8<DT>(k + hv.base + (long long)s * hv.tok_stride + d0, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part[tid][i] = acc[i];
-    __syncthreads();
-    if (tid < kSliceCh) {
-      const int g = tid >> 3, i = tid & 7;
-      double s = 0.0;
-      for (int r = 0; r < kThreads / 4; ++r) s += part[r * 4 + g][i];
-      a.k_mean[(long long)bh * a.D + slice * kSliceCh + tid] = (float)(s / (double)a.S);
-    }
-    return;
-  }
-
-  // ---- Q block quantisation
-  const int idx = blockIdx.x - nsum;
-  const int bh = idx / a.nq, blk = idx % a.nq;
-  const int b = bh / a.H, h = bh % a.H;
-  const HeadView hv = head_view(a.layout, b, h, a.H, a.S, a.D);
-  const int vec_per_row = a.D / 8;
-  const int nvec = kBlkQ * vec_per_row;  // <= 512: at most 2 per thread
+  const int bh = blockIdx.x / a.nq, blk = blockIdx.x % a.nq;
+  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  const uint16_t *q = (const uint16_t *)a.q;
+  constexpr int vec_per_row = D / 8;
+  constexpr int nvec = kBlkQ * vec_per_row;  // <= 512: at most 2 per thread
   float x[2][8];
   float amax = 0.0f;
 #pragma unroll
@@ -135,26 +191,42 @@ __global__ __launch_bounds__(kThreads) void k_kmean_qquant(const QuantQKArgs a) 
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
-    *reinterpret_cast<v2i *>(a.q_i8 + ((long long)bh * a.S_q + blk * kBlkQ + row) * a.D + c8) = out;
+    *reinterpret_cast<v2i *>(a.q_i8 + ((long long)bh * a.S_q + blk * kBlkQ + row) * D + c8) = out;
   }
+}
+
+// k_mean[bh][d] = fp32(sum over the head's chunk partials / S); thread = (bh, d)
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)a.B * a.H * D) return;
+  const int bh = (int)(i / D), d = (int)(i % D);
+  const double *part = reinterpret_cast<const double *>(a.k_i8 + (long long)bh * a.S_k * D);
+  const int nch = n_chunks(a.S);
+  double v[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0;  // all loads in flight
+  double t = 0.0;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) t += v[c];
+  a.k_mean[i] = (float)(t / (double)a.S);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: INT8 quantisation of one 64-token block of K - k_mean.
 // ---------------------------------------------------------------------------
-template <int DT>
+template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
   __shared__ float red[kThreads / 64];
-  __shared__ float mean[128];
+  __shared__ float mean[D];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / a.nk, blk = blockIdx.x % a.nk;
-  const int b = bh / a.H, h = bh % a.H;
-  const HeadView hv = head_view(a.layout, b, h, a.H, a.S, a.D);
+  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
   const uint16_t *k = (const uint16_t *)a.k;
-  if (tid < a.D) mean[tid] = a.k_mean[(long long)bh * a.D + tid];
+  if (tid < D) mean[tid] = a.k_mean[(long long)bh * D + tid];
   __syncthreads();
-  const int vec_per_row = a.D / 8;
-  const int nvec = kBlkK * vec_per_row;  // <= 1024: at most 4 per thread
+  constexpr int vec_per_row = D / 8;
+  constexpr int nvec = kBlkK * vec_per_row;  // <= 1024: at most 4 per thread
   float x[4][8];
   float amax = 0.0f;
 #pragma unroll
@@ -185,93 +257,128 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
-    *reinterpret_cast<v2i *>(a.k_i8 + ((long long)bh * a.S_k + blk * kBlkK + row) * a.D + c8) = out;
+    *reinterpret_cast<v2i *>(a.k_i8 + ((long long)bh * a.S_k + blk * kBlkK + row) * D + c8) = out;
   }
 }
 
 // ---------------------------------------------------------------------------
-// V: one work-group per (head, 32-channel slice).  Pass A: channel amax over S.
-// Pass B: per 64-key tile, convert to E4M3, transpose through LDS into the
-// channel-major tile layout with the attention kernel's key order, and store
-// the slice's 32 x 64 bytes with 16-byte vector stores.
+// V, four short launches:
+//   k_vamax_part   per (head, chunk): channel abs-max partials -> v_fp8 region
+//   k_vamax        per (head, channel): v_scale <- amax (held there until the end)
+//   k_vconvert     per (head, 64-key tile): E4M3 codes in the tiled key order
+//   k_vscale       per (head, channel): v_scale <- amax / 448
 // ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_vquant(const QuantVArgs a) {
-  __shared__ float pmax[kThreads][8];
-  __shared__ float inv_s[kSliceCh];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kSliceCh * kBlkK];
-  const int tid = threadIdx.x;
-  const int nslice = a.D / kSliceCh;
-  const int bh = blockIdx.x / nslice, slice = blockIdx.x % nslice;
-  const int b = bh / a.H, h = bh % a.H;
-  const HeadView hv = head_view(a.layout, b, h, a.H, a.S, a.D);
-  const uint16_t *v = (const uint16_t *)a.v;
-  const int grp = tid & 3, r0 = tid >> 2;  // 64 rows x 4 groups of 8 channels
-  const int d0 = slice * kSliceCh + grp * 8;
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_vamax_part(const QuantVArgs a) {
+  const int nch = n_chunks(a.S);
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  chunk_reduce<DT, D, true>((const uint16_t *)a.v, hv, a.S, chunk, a.v_fp8 + (long long)bh * a.nk * kBlkK * D);
+}
 
-  float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = r0; s < a.S; s += kThreads / 4) {
-    float x[8];
-    load8<DT>(v + hv.base + (long long)s * hv.tok_stride + d0, x);
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)a.B * a.H * D) return;
+  const int bh = (int)(i / D), d = (int)(i % D);
+  const float *part = reinterpret_cast<const float *>(a.v_fp8 + (long long)bh * a.nk * kBlkK * D);
+  const int nch = n_chunks(a.S);
+  float v[kMaxChunks];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(x[i]));
-  }
+  for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0f;
+  float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pmax[tid][i] = mx[i];
-  __syncthreads();
-  if (tid < kSliceCh) {
-    const int g = tid >> 3, i = tid & 7;
-    float m = 0.0f;
-    for (int r = 0; r < kThreads / 4; ++r) m = fmaxf(m, pmax[r * 4 + g][i]);
-    inv_s[tid] = m > 0.0f ? 448.0f / m : 0.0f;
-    a.v_scale[(long long)bh * a.D + slice * kSliceCh + tid] = m > 0.0f ? m / 448.0f : 0.0f;
-  }
-  __syncthreads();
+  for (int c = 0; c < kMaxChunks; ++c) m = fmaxf(m, v[c]);
+  a.v_scale[i] = m;
+}
+
+// One 64-key tile of one head: thread (q, g) converts keys 4q .. 4q + 3 of
+// channels 8g .. 8g + 7.  The four keys are consecutive in the tile's key
+// order (key_vpos(4q + i) = key_vpos(4q) + i), so each channel's four codes
+// form one 32-bit word of the channel's 64-byte row; the 16 threads of a
+// channel group together write whole rows.
+template <int DT, int D>
+__global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
+  const int tid = threadIdx.x, q = tid & 15, g = tid >> 4;
+  const int bh = blockIdx.x / a.nk, t = blockIdx.x % a.nk;
+  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  const uint16_t *v = (const uint16_t *)a.v;
   float inv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) inv[i] = inv_s[grp * 8 + i];
-
-  const int pos = key_vpos(r0);
-  for (int t = 0; t < a.nk; ++t) {
-    const int s = t * kBlkK + r0;
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (s < a.S) load8<DT>(v + hv.base + (long long)s * hv.tok_stride + d0, x);
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float y0 = fminf(fmaxf(x[i] * inv[i], -448.0f), 448.0f);
-      const float y1 = fminf(fmaxf(x[i + 1] * inv[i + 1], -448.0f), 448.0f);
-      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      tile[(grp * 8 + i) * kBlkK + pos] = (uint8_t)(pk & 0xff);
-      tile[(grp * 8 + i + 1) * kBlkK + pos] = (uint8_t)((pk >> 8) & 0xff);
-    }
-    __syncthreads();
-    if (tid < kSliceCh * kBlkK / 16) {
-      const v4i val = reinterpret_cast<const v4i *>(tile)[tid];
-      uint8_t *dst = a.v_fp8 + (((long long)bh * a.nk + t) * a.D + slice * kSliceCh) * kBlkK;
-      reinterpret_cast<v4i *>(dst)[tid] = val;
-    }
-    __syncthreads();
+  for (int i = 0; i < 8; ++i) {
+    const float m = a.v_scale[(long long)bh * D + 8 * g + i];  // the channel's amax at this point
+    inv[i] = m > 0.0f ? 448.0f / m : 0.0f;
   }
+  float x[4][8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int s = t * kBlkK + 4 * q + k;
+    if (s < a.S) {
+      load8<DT>(v + hv.base + (long long)s * hv.tok_stride + 8 * g, x[k]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[k][i] = 0.0f;
+    }
+  }
+  uint8_t *dst = a.v_fp8 + (((long long)bh * a.nk + t) * D + 8 * g) * kBlkK + key_vpos(4 * q);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(x[k][i] * inv[i], -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+    *reinterpret_cast<int *>(dst + i * kBlkK) = w;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_vscale(const QuantVArgs a) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)a.B * a.H * D) return;
+  const float m = a.v_scale[i];
+  a.v_scale[i] = m > 0.0f ? m / 448.0f : 0.0f;
+}
+
+template <int DT, int D>
+static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
+  const int bh = a.B * a.H;
+  const int gd = (bh * D + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bh * n_chunks(a.S)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_qquant<DT, D>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_kquant<DT, D>), dim3(bh * a.nk), dim3(kThreads), 0, stream, a);
+}
+
+template <int DT, int D>
+static void launch_v(const QuantVArgs &a, hipStream_t stream) {
+  const int bh = a.B * a.H;
+  const int gd = (bh * D + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((k_vamax_part<DT, D>), dim3(bh * n_chunks(a.S)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_vamax<D>), dim3(gd), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_vconvert<DT, D>), dim3(bh * a.nk), dim3(2 * D), 0, stream, a);
+  hipLaunchKernelGGL((k_vscale<D>), dim3(gd), dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream) {
-  const int nslice = a.D / kSliceCh;
-  const int g1 = a.B * a.H * nslice + a.B * a.H * a.nq;
-  const int g2 = a.B * a.H * a.nk;
-  if (a.dtype == 0) {
-    hipLaunchKernelGGL(k_kmean_qquant<0>, dim3(g1), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(k_kquant<0>, dim3(g2), dim3(kThreads), 0, stream, a);
+  if (a.D == 64) {
+    if (a.dtype == 0) launch_qk<0, 64>(a, stream);
+    else launch_qk<1, 64>(a, stream);
   } else {
-    hipLaunchKernelGGL(k_kmean_qquant<1>, dim3(g1), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(k_kquant<1>, dim3(g2), dim3(kThreads), 0, stream, a);
+    if (a.dtype == 0) launch_qk<0, 128>(a, stream);
+    else launch_qk<1, 128>(a, stream);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_v(const QuantVArgs &a, hipStream_t stream) {
-  const int g = a.B * a.H * (a.D / kSliceCh);
-  if (a.dtype == 0) hipLaunchKernelGGL(k_vquant<0>, dim3(g), dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL(k_vquant<1>, dim3(g), dim3(kThreads), 0, stream, a);
+  if (a.D == 64) {
+    if (a.dtype == 0) launch_v<0, 64>(a, stream);
+    else launch_v<1, 64>(a, stream);
+  } else {
+    if (a.dtype == 0) launch_v<0, 128>(a, stream);
+    else launch_v<1, 128>(a, stream);
+  }
   return hipGetLastError();
 }
 
