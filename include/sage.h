@@ -108,7 +108,10 @@ int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale,
  *     amax = max |x|;  scale = amax / 127;  code = rint(x * (127 / amax)) in [-127, 127];
  *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
  * q, k: dtype (SAGE_DTYPE_*) tensors in `layout` (SAGE_LAYOUT_*).
- * Writes q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).
+ * Writes q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).  The call is
+ * several kernel launches; while it runs, k_i8 also holds intermediate
+ * per-chunk channel sums, so its content is defined only after the stream has
+ * passed the call.
  */
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int S, int D, int layout,
                          int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
@@ -119,7 +122,9 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
  *   amax_d = max_s |V[s][d]|;  v_scale[d] = amax_d / 448;
  *   code = E4M3(V[s][d] * (448 / amax_d)), round to nearest even, |x| clamped to 448;
  *   an all-zero channel has scale 0 and codes 0.
- * Writes v_fp8 in the tiled layout above and v_scale.
+ * Writes v_fp8 in the tiled layout above and v_scale.  While the call's
+ * launches run, v_fp8 and v_scale hold intermediate per-channel maxima, so
+ * both are defined only after the stream has passed the call.
  */
 int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8,
                  float *v_scale, void *stream);
