@@ -145,7 +145,8 @@ __device__ __forceinline__ float tree_sum(const float *x) {
 template <int D, int TN, int WAVES>
 struct TileCopy {
   static constexpr int KCH = D / 16;
-  static constexpr int LOADS = TN * D / 1024 / WAVES;  // per wavefront, for K and again for V
+  static constexpr int NCOPY = TN * D / 1024;                 // 1 KiB wave-copies per K (or V) tile
+  static constexpr int LOADS = (NCOPY + WAVES - 1) / WAVES;  // per wavefront (the last round may be partial)
   uint32_t koff[LOADS], voff[LOADS];
   __device__ __forceinline__ TileCopy(int wave, int lane) {
 #pragma unroll
@@ -161,10 +162,14 @@ struct TileCopy {
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int tile_off,
                                         uint8_t *kbuf, uint8_t *vbuf, int wave) const {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) dma16_buf(krs, koff[i], tile_off, kbuf + (wave + WAVES * i) * 1024);
+    for (int i = 0; i < LOADS; ++i)
+      if (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY)
+        dma16_buf(krs, koff[i], tile_off, kbuf + (wave + WAVES * i) * 1024);
     if (WITH_V) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16_buf(vrs, voff[i], tile_off, vbuf + (wave + WAVES * i) * 1024);
+      for (int i = 0; i < LOADS; ++i)
+        if (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY)
+          dma16_buf(vrs, voff[i], tile_off, vbuf + (wave + WAVES * i) * 1024);
     }
   }
 };
@@ -477,6 +482,7 @@ k_attn(const AttnArgs a) {
   // ---- main loop: tile j is computed from buffer j % NBUF while tiles
   //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next
   constexpr int LPT = (PV == 0 ? 2 : 1) * TN * D / 1024 / WAVES;  // DMA instructions per tile per wavefront
+  static_assert(NBUF == 2 || (TN * D / 1024) % WAVES == 0, "partial vm waits need an even copy split");
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
     if (u < ntiles) copy.template issue<PV == 0>(krs, vrs, u * TN * D, kbuf[u], vbuf[PV == 0 ? u : 0], wave);
