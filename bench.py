@@ -25,6 +25,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TOPS = 5000.0  # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s) = 5.0 P
+FP16_PEAK_TOPS = 2500.0  # MI355X dense FP16 (PFLOP/s) = 2.5 P
+
+
+def mfma_peak(pv):
+    """Peak of the attention kernel's contraction mix: half its operations are
+    the INT8 Q.K^T and half the P.V product (FP8, or FP16 in pv fp16 mode), so
+    the peak is the harmonic combination of the two dense peaks."""
+    pv_peak = MFMA_PEAK_TOPS if pv == "fp8" else FP16_PEAK_TOPS
+    return 2.0 / (1.0 / MFMA_PEAK_TOPS + 1.0 / pv_peak)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "quantized_attention_02_amd", "csrc", "attn.hip")
@@ -172,8 +181,8 @@ def main():
                    "layout": w.layout, "causal": causal, "pv_mode": args.pv},
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": MFMA_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tops / MFMA_PEAK_TOPS, 4), "traffic": traffic,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv), 1), "unit": "TFLOP/s",
+                     "frac": round(attn_tops / mfma_peak(args.pv), 4), "traffic": traffic,
                      "kernel": "k_attn (sage_attn_fwd)", "algorithmic_ops_per_launch": ops,
                      "attn_src_sha256_16": khash},
     }

@@ -74,6 +74,9 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
+  // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
+  if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H * D * 2 * kKvPad >= (1LL << 31))
+    return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16))
     return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)))

@@ -174,33 +174,76 @@ struct TileCopy {
   }
 };
 
-// pv fp16: original 16-bit V rows [n0, n0 + 64) -> fp16 V^T rows (128 bytes,
-// vpos_key order, swizzled) in `vb`.  Staged through VGPRs: the layout change
-// and the bf16 -> fp16 rounding need the values in registers anyway.
-template <int D, int DT, int THREADS>
-__device__ __forceinline__ void stage_v16(const AttnArgs &a, const HeadView &hv, int n0, uint8_t *vb, int tid) {
-  const uint16_t *vsrc = reinterpret_cast<const uint16_t *>(a.v);
-  constexpr int NU = 32 * (D / 8);  // key pairs x 8-channel groups
+// pv fp16: the tile's raw 16-bit V rows (TN keys x D channels, 2D bytes a
+// row, as stored in the caller's layout) are copied into LDS as they are;
+// the PV MFMA's V^T operand is then read with the transposing LDS load
+// ds_read_b64_tr_b16.  Within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes 4 j + i / 4 (j = 0..3): with
+// lane p pointing at V[key0 + p / 4][c0 + 4 (p % 4) ..], lane i obtains
+// channel c0 + i for keys key0 .. key0 + 3.
+//
+// 16-byte chunks of a V row are XOR-swizzled by the row so that the 32 lanes
+// an LDS read serves together (4 rows x 16 chunks of 16 bytes for D = 128)
+// hit 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int swz16(int chunk, int row) {
+  if (D == 128) return chunk ^ (4 * (row & 3));
+  return chunk ^ (4 * ((row >> 1) & 1));
+}
+
+template <int D, int TN, int WAVES>
+struct VCopy16 {
+  static constexpr int ROWB = 2 * D;                // bytes of a V row
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int RPC = 1024 / ROWB;           // rows per 1 KiB wave-copy
+  static constexpr int NCOPY = TN * ROWB / 1024;    // wave-copies per tile
+  static constexpr int LOADS = NCOPY / WAVES;
+  static_assert(NCOPY % WAVES == 0, "even split of the V copies");
+  int lrow;       // row of this lane inside a wave-copy
+  uint32_t lcol;  // byte offset of this lane's (swizzled) source chunk in its row
+  __device__ __forceinline__ VCopy16(int lane) {
+    lrow = lane / CPR;
+    // the swizzle depends on row & 3 (D = 128) or (row >> 1) & 1 (D = 64) only,
+    // and a copy's first row is a multiple of RPC (4 or 8): lrow decides it
+    lcol = (uint32_t)(16 * swz16<D>(lane % CPR, lrow));
+  }
+  // rows key0 .. key0 + TN - 1 of the head; rows at or past S are outside the
+  // buffer resource's range and read as zeros
+  __device__ __forceinline__ void issue(const uint16_t *v, const HeadView &hv, int key0, int S, uint8_t *vb,
+                                        int wave) const {
+    const int nvalid = min(TN, S - key0);
+    const long long ts2 = 2 * hv.tok_stride;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(v + hv.base + (long long)key0 * hv.tok_stride, (int)(nvalid * ts2));
 #pragma unroll
-  for (int u = tid; u < NU; u += THREADS) {
-    const int pair = u / (D / 8), c8 = (u % (D / 8)) * 8;
-    const int n = n0 + 2 * pair;
-    v4i t0 = {0, 0, 0, 0}, t1 = {0, 0, 0, 0};
-    if (n < a.S) t0 = *reinterpret_cast<const v4i *>(vsrc + hv.base + (long long)n * hv.tok_stride + c8);
-    if (n + 1 < a.S) t1 = *reinterpret_cast<const v4i *>(vsrc + hv.base + (long long)(n + 1) * hv.tok_stride + c8);
-    const int pos = key_vpos(2 * pair);  // even key; its odd partner sits at pos + 1
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t e0 = ((uint32_t)t0[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-      uint32_t e1 = ((uint32_t)t1[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-      if (DT == 1) {  // bf16 -> fp16, round to nearest even
-        e0 = f32_to_f16_bits(bf16_to_f32(e0));
-        e1 = f32_to_f16_bits(bf16_to_f32(e1));
-      }
-      const int row = c8 + i, byte = 2 * pos;
-      *reinterpret_cast<uint32_t *>(vb + row * 128 + 16 * swz<8>(byte >> 4, row) + (byte & 15)) = e0 | (e1 << 16);
+    for (int i = 0; i < LOADS; ++i) {
+      const int k = wave + WAVES * i;
+      dma16_buf(rs, (uint32_t)((k * RPC + lrow) * ts2) + lcol, 0, vb + k * 1024);
     }
   }
+};
+
+// V^T fragment (channels 32 c .. 32 c + 31 down the lanes, keys 16 sb .. +15
+// across them in the MFMA k order of the P registers) for v_mfma_f32_32x32x16_f16.
+template <int D, int DT>
+__device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lane) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s *lds_v4s;
+  const int g = lane >> 4, p = lane & 15, hh = lane >> 5;
+  const int cb = 64 * c + 32 * (g & 1) + 8 * (p & 3);  // byte of the lane's 4 channels in a row
+  v4s h[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int key = 16 * sb + 8 * r + 4 * hh + (p >> 2);
+    const int off = key * (2 * D) + 16 * swz16<D>(cb >> 4, key) + (cb & 15);
+    h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)((__attribute__((address_space(3))) uint8_t *)vb + off));
+  }
+  v8h out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t bits = (uint32_t)(uint16_t)h[i >> 2][i & 3];
+    out[i] = DT == 0 ? __builtin_bit_cast(_Float16, (uint16_t)bits) : (_Float16)bf16_to_f32(bits);  // bf16 -> fp16, RNE
+  }
+  return out;
 }
 
 // TN: keys per loop iteration (64 or 128, i.e. one or two INT8 K blocks);
@@ -217,8 +260,8 @@ k_attn(const AttnArgs a) {
   constexpr int NB = TN / 64;                                // INT8 K blocks per tile
   constexpr int NT = TN / 32;                                // 32-key sub-tiles per tile
   constexpr int KBYTES = TN * D;                             // K tile
-  constexpr int VBYTES = PV == 0 ? TN * D : D * 128;         // fp8: NB 64-key blocks; fp16: one block
-  constexpr int NVBUF = PV == 0 ? NBUF : 1;                 // fp16 V is staged through VGPRs, one buffer
+  constexpr int VBYTES = PV == 0 ? TN * D : 2 * TN * D;     // fp8: NB 64-key blocks; fp16: TN raw 16-bit rows
+  constexpr int NVBUF = PV == 0 ? NBUF : 1;                 // fp16 V: one buffer, refilled every tile
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
@@ -285,6 +328,7 @@ k_attn(const AttnArgs a) {
   const float *kscale = a.k_scale + (long long)bh * a.nk;
   const HeadView hv = head_view(a.layout, b, h, a.H, a.S, D);
   const TileCopy<D, TN, WAVES> copy(wave, lane);
+  const VCopy16<D, TN, WAVES> vcopy(lane);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, a.S_k * D);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase, a.S_k * D);
 
@@ -292,6 +336,9 @@ k_attn(const AttnArgs a) {
   auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
     const int key0 = j * TN;
     const bool work = active && !(CAUSAL && key0 > qw + 31);
+    // pv fp16: this tile's V rows go into the single V buffer, which the
+    // barrier that ended the previous tile has released
+    if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, key0, a.S, vb, wave);
     // the tile's K-block scales, read through a wave-uniform address (scalar loads)
     float ks[NB];
     if (NB == 2) {
@@ -443,36 +490,30 @@ k_attn(const AttnArgs a) {
         }
       }
     } else {
-      // ---- pv fp16: P~ -> fp16, O rescaled, then O^T += V^T . P^T with fp32
-      //      accumulation in the MFMA; V is staged one 64-key block at a time
-      //      by the whole work-group (every wavefront takes part in the barriers)
+      // ---- pv fp16: P~ -> fp16 and O rescaled while the V copy lands; then
+      //      O^T += V^T . P^T with fp32 accumulation in the MFMA, V^T read from
+      //      the raw rows with transposing LDS loads
       v8h ph[2 * NT];
       if (work) {
 #pragma unroll
         for (int s8 = 0; s8 < 2 * NT; ++s8)
 #pragma unroll
           for (int i = 0; i < 8; ++i) ph[s8][i] = (_Float16)p[8 * s8 + i];
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+          for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
-      }
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        stage_v16<D, DT, kThreads>(a, hv, key0 + 64 * blk, vb, tid);
-        __syncthreads();
-        if (work) {
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int row = 32 * c + qn;
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-              const v8h vf = *reinterpret_cast<const v8h *>(vb + row * 128 + 16 * swz<8>(4 * hh + s4, row));
-              O[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ph[4 * blk + s4], O[c], 0, 0, 0);
-            }
-          }
+            for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
         }
-        __syncthreads();
+      }
+      wait_vm<0>();  // this wavefront's V (and next K) copies have landed ...
+      __syncthreads();  // ... and every other wavefront's too
+      if (work) {
+#pragma unroll
+        for (int sb = 0; sb < 2 * NT; ++sb)
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            O[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag16<D, DT>(vb, c, sb, lane), ph[sb], O[c], 0, 0, 0);
       }
     }
   };
