@@ -143,6 +143,8 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  * sage_quant_v.  pv fp16: v = the original V tensor (dtype, layout), v_scale = NULL
  * (bf16 V is rounded to fp16).  out: dtype tensor in `layout`, shape of q.
  * is_causal in {0, 1}; sm_scale finite and > 0 (the usual choice is 1/sqrt(D)).
+ * pv fp16 with NHD layout additionally needs H * D * 2 * SAGE_KV_PAD < 2^31
+ * (128-token slices of V are addressed through a 32-bit byte range).
  */
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
                   const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,

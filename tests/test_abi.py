@@ -75,7 +75,9 @@ BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict
 BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
             dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
-            dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0)]
+            dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
+            # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H * D * 2 * 128 < 2^31
+            dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, D=128)]
 
 
 def _call_qk(**kw):
@@ -111,6 +113,9 @@ def test_attn_fwd_rejects(bad):
 def test_attn_fp16_mode_accepts_null_v_scale_then_needs_device():
     rc = _call_attn(pv_mode=1, v_scale=None)
     assert rc in (qa.SAGE_ERR_NO_DEVICE, qa.SAGE_OK, qa.SAGE_ERR_UNSUPPORTED) or rc != qa.SAGE_ERR_INVALID_ARG
+    # the largest NHD head count the fp16 mode takes passes the argument checks
+    rc = _call_attn(pv_mode=1, v_scale=None, layout=1, B=1, H=(1 << 16) - 1, D=128)
+    assert rc != qa.SAGE_ERR_INVALID_ARG
 
 
 def test_dump_rejects_bad_head_and_buffer():
