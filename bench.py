@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TOPS = 5000.0  # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s) = 5.0 P
+CPU_SAMPLE_S = 12.0  # seconds of oracle work in the CPU baseline sample
 FP16_PEAK_TOPS = 2500.0  # MI355X dense FP16 (PFLOP/s) = 2.5 P
 
 
@@ -48,7 +49,8 @@ def parse():
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=10, help="heads in the CPU-oracle sample")
+    p.add_argument("--cpu-heads", type=int, default=0,
+                   help="heads in the CPU-oracle sample (0: as many as take about 12 s)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return p.parse_args()
@@ -71,16 +73,19 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_hash, workload):
+def traffic_record(kernel_hash, workload, pv, causal):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source and this workload."""
+    summaries, if one was taken on the current kernel source for this workload
+    and mode."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        recs = json.load(open(TRAFFIC_FILE))["records"]
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if rec.get("attn_src_sha256_16") != kernel_hash or rec.get("workload") != workload:
-        return None
-    return rec
+    for rec in recs:
+        if (rec.get("attn_src_sha256_16") == kernel_hash and rec.get("workload") == workload
+                and rec.get("pv_mode") == pv and rec.get("causal") == causal):
+            return rec
+    return None
 
 
 def cpu_baseline(w, causal, pv, nheads):
@@ -90,11 +95,19 @@ def cpu_baseline(w, causal, pv, nheads):
     from quantized_attention_02_amd import synth
 
     q, k, v = synth.make_qkv(w)
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:nheads]
-    t0 = time.perf_counter()
-    O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal),
-           pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=heads)
-    dt = time.perf_counter() - t0
+    all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(heads):
+        t0 = time.perf_counter()
+        O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal),
+               pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=heads)
+        return time.perf_counter() - t0
+
+    if nheads <= 0:  # size the sample to about CPU_SAMPLE_S seconds from a one-head probe
+        t1 = run(all_heads[-1:])
+        nheads = int(min(len(all_heads), max(1, round(CPU_SAMPLE_S / max(t1, 1e-3)))))
+    heads = all_heads[:nheads]
+    dt = run(heads)
     ops = 4.0 * len(heads) * w.S * w.S * w.D / (2 if causal else 1)
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"{len(heads)} of {w.B * w.H} heads of {w.name}, all {w.S} query rows "
@@ -160,7 +173,7 @@ def main():
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     khash = source_hash(ATTN_SRC)
-    trec = traffic_record(khash, name)
+    trec = traffic_record(khash, name, args.pv, bool(causal))
     traffic = None if trec is None else trec["hbm_bytes_per_launch"]
 
     res = {
