@@ -239,17 +239,20 @@ def attn_exact_head(qf, kf, vf, *, is_causal, sm_scale, rows=None) -> np.ndarray
 
 # ---------------------------------------------------------------- whole tensors
 def smooth_quant_qk(q, k, dtype: int, layout: str, blk_q: int = 32, blk_k: int = 64, smooth: bool = True):
-    """Quantise physical Q, K (uint16 codes) -> logical [B,H,S,D] codes + scales + K means."""
+    """Quantise physical Q, K (uint16 codes) -> logical [B,H,S,D] Q codes + scales and
+    [B,H_kv,S,D] K codes + scales + K means (K may have fewer heads than Q)."""
     B, H, S, D = logical_shape(q.shape, layout)
+    Hkv = logical_shape(k.shape, layout)[1]
     nq, nk = (S + blk_q - 1) // blk_q, (S + blk_k - 1) // blk_k
     q8 = np.empty((B, H, S, D), np.int8)
-    k8 = np.empty((B, H, S, D), np.int8)
+    k8 = np.empty((B, Hkv, S, D), np.int8)
     qs = np.empty((B, H, nq), np.float32)
-    ks = np.empty((B, H, nk), np.float32)
-    km = np.empty((B, H, D), np.float32)
+    ks = np.empty((B, Hkv, nk), np.float32)
+    km = np.empty((B, Hkv, D), np.float32)
     for b in range(B):
         for h in range(H):
             q8[b, h], qs[b, h] = quant_q_head(decode16(head(q, layout, b, h), dtype), blk_q)
+        for h in range(Hkv):
             k8[b, h], ks[b, h], km[b, h] = quant_k_head(decode16(head(k, layout, b, h), dtype), blk_k, smooth)
     return q8, qs, k8, ks, km
 
@@ -277,6 +280,16 @@ def logical_shape(shape, layout):
     return B, H, S, D
 
 
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """K/V head used by query head h when K and V have Hkv <= H heads (grouped-query
+    attention, "Thư viện SageAttention" page, feature list: native group-query
+    attention).  Reading: the usual grouping, H / Hkv consecutive query heads share
+    one K/V head."""
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"query heads {H} must be a multiple of K/V heads {Hkv}")
+    return h // (H // Hkv)
+
+
 def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
          heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
@@ -284,14 +297,16 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
     Returns {(b, h): fp32 [len(rows), D]}; rows default to all S rows.
     """
     B, H, S, D = logical_shape(q.shape, layout)
+    Hkv = logical_shape(k.shape, layout)[1]
     if sm_scale is None:
         sm_scale = default_sm_scale(D)
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     res = {}
     for (b, h) in heads:
+        hk = kv_head(h, H, Hkv)
         qf = decode16(head(q, layout, b, h), dtype)
-        kf = decode16(head(k, layout, b, h), dtype)
-        vf = decode16(head(v, layout, b, h), dtype)
+        kf = decode16(head(k, layout, b, hk), dtype)
+        vf = decode16(head(v, layout, b, hk), dtype)
         q8, qs = quant_q_head(qf, blk_q)
         k8, ks, _ = quant_k_head(kf, blk_k, smooth)
         if pv_mode == PV_FP8:
@@ -306,12 +321,14 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
 
 def attn_exact(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, heads=None, rows=None):
     B, H, S, D = logical_shape(q.shape, layout)
+    Hkv = logical_shape(k.shape, layout)[1]
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(D)
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     res = {}
     for (b, h) in heads:
-        res[(b, h)] = attn_exact_head(decode16(head(q, layout, b, h), dtype), decode16(head(k, layout, b, h), dtype),
-                                      decode16(head(v, layout, b, h), dtype), is_causal=is_causal,
+        hk = kv_head(h, H, Hkv)
+        res[(b, h)] = attn_exact_head(decode16(head(q, layout, b, h), dtype), decode16(head(k, layout, b, hk), dtype),
+                                      decode16(head(v, layout, b, hk), dtype), is_causal=is_causal,
                                       sm_scale=sm_scale, rows=rows)
     return res

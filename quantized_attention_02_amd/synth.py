@@ -13,8 +13,8 @@ value recipes model the workloads the SageAttention pages talk about:
   that K smoothing removes ("SageAttention2" page, section SageAttention2方法).
 
 Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this order):
-  1. Q, K, V base values ~ N(0, 1), float32, logical [B, H, S, D];
-  2. the K bias c[h, d] ~ N(0, bias_sigma^2), shared over b and s;
+  1. Q, K, V base values ~ N(0, 1), float32, logical [B, H, S, D] (K, V: [B, Hkv, S, D]);
+  2. the K bias c[h, d] ~ N(0, bias_sigma^2) per K head, shared over b and s;
   3. (outlier_p > 0) Bernoulli(outlier_p) masks for Q, then K;
   4. (token_norm) per-token factors r ~ U(0.5, 2) drawn per (b, s) for Q, K, V.
 Application: x *= r (token norm), K += c, then masked entries of Q and K *= 20.
@@ -43,6 +43,11 @@ class Workload:
     causal: tuple = (False,)
     pv_modes: tuple = ("fp8",)
     seed: int = 42
+    Hkv: int = 0  # K/V heads (grouped-query attention); 0: as many as Q
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     def ops(self, causal: bool) -> float:
         """Attention operations per call: 4*B*H*S^2*D, halved for causal."""
@@ -62,6 +67,8 @@ WORKLOADS = {
                  pv_modes=("fp8", "fp16"), seed=44),
         Workload("prefill_b1h32s32768d128", 1, 32, 32768, 128, "bf16", "NHD", 3.0, causal=(True,), seed=45),
         Workload("dit_b1h20s16384d128", 1, 20, 16384, 128, "bf16", "NHD", 3.0, token_norm=True, seed=46),
+        # grouped-query attention (4 query heads per K/V head), LLM prefill layout
+        Workload("gqa_b1h32kv8s8192d128", 1, 32, 8192, 128, "bf16", "NHD", 3.0, causal=(True,), seed=47, Hkv=8),
     ]
 }
 HEADLINE = "snippet_b2h32s4096d128"
@@ -82,13 +89,14 @@ def make_qkv(w: Workload, seed: int | None = None):
     """Return (q, k, v) as uint16 codes in the workload's physical layout."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
     shape = (w.B, w.H, w.S, w.D)
+    kv_shape = (w.B, w.kv_heads, w.S, w.D)
     q = rng.standard_normal(shape, dtype=np.float32)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    v = rng.standard_normal(shape, dtype=np.float32)
-    c = (rng.standard_normal((w.H, w.D), dtype=np.float32) * np.float32(w.bias_sigma)).astype(np.float32)
+    k = rng.standard_normal(kv_shape, dtype=np.float32)
+    v = rng.standard_normal(kv_shape, dtype=np.float32)
+    c = (rng.standard_normal((w.kv_heads, w.D), dtype=np.float32) * np.float32(w.bias_sigma)).astype(np.float32)
     if w.outlier_p > 0:
         mq = rng.random(shape) < w.outlier_p
-        mk = rng.random(shape) < w.outlier_p
+        mk = rng.random(kv_shape) < w.outlier_p
     if w.token_norm:
         for x in (q, k, v):
             r = rng.uniform(0.5, 2.0, size=(w.B, w.S)).astype(np.float32)
@@ -105,7 +113,8 @@ def make_qkv(w: Workload, seed: int | None = None):
     return tuple(out)
 
 
-def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0, token_norm=False, seed=0):
+def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0, token_norm=False, seed=0, Hkv=0):
     """An ad-hoc workload (edge shapes in tests)."""
-    return Workload(f"custom_b{B}h{H}s{S}d{D}", B, H, S, D, dtype, layout, bias_sigma, outlier_p, token_norm,
-                    seed=seed)
+    kv = f"kv{Hkv}" if Hkv else ""
+    return Workload(f"custom_b{B}h{H}{kv}s{S}d{D}", B, H, S, D, dtype, layout, bias_sigma, outlier_p, token_norm,
+                    seed=seed, Hkv=Hkv)

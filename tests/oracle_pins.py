@@ -423,4 +423,50 @@ def pin_p_rounded_to_pv_format():
         assert (r > 0).sum() > S  # many non-trivial weights took part
 
 
+# ------------------------------------------------------------------ grouped-query attention
+def pin_gqa_equals_replicated_kv():
+    """Query head h with H / Hkv query heads per K/V head is exactly multi-head
+    attention with each K/V head repeated for its group (repeat-interleave)."""
+    for layout in ("HND", "NHD"):
+        w = synth.custom(1, 6, 70, 64, layout=layout, seed=91, Hkv=2)
+        q, k, v = synth.make_qkv(w)
+        hax = 1 if layout == "HND" else 2
+        kr, vr = np.repeat(k, 3, axis=hax), np.repeat(v, 3, axis=hax)
+        assert kr.shape == q.shape
+        for causal in (False, True):
+            g = O.attn(q, k, v, F16, layout, is_causal=causal)
+            m = O.attn(q, kr, vr, F16, layout, is_causal=causal)
+            for hd in g:
+                assert np.array_equal(g[hd].view(np.uint32), m[hd].view(np.uint32)), (layout, causal, hd)
+            ge = O.attn_exact(q, k, v, F16, layout, is_causal=causal, heads=[(0, 5)])
+            me = O.attn_exact(q, kr, vr, F16, layout, is_causal=causal, heads=[(0, 5)])
+            assert np.array_equal(ge[(0, 5)], me[(0, 5)])
+    # ... and head by head, query head h of 6 reads K/V head h // 3 (worked
+    # out here without the oracle's own head bookkeeping)
+    res = O.attn(q, k, v, F16, "NHD")
+    for h in range(6):
+        qf = O.decode16(q[0, :, h, :], F16)
+        kf = O.decode16(k[0, :, h // 3, :], F16)
+        vf = O.decode16(v[0, :, h // 3, :], F16)
+        ref = _attn_f(qf, kf, vf)
+        assert np.array_equal(res[(0, h)].view(np.uint32), ref.view(np.uint32)), h
+    # K codes, scales and means are computed once per K head
+    q8, qs, k8, ks, km = O.smooth_quant_qk(q, k, F16, "NHD")
+    assert q8.shape[1] == 6 and k8.shape[1] == 2 and ks.shape[1] == 2 and km.shape == (1, 2, 64)
+    k8h, ksh, kmh = O.quant_k_head(O.decode16(O.head(k, "NHD", 0, 1), F16), 64, True)
+    assert np.array_equal(k8[0, 1], k8h) and np.array_equal(ks[0, 1], ksh) and np.array_equal(km[0, 1], kmh)
+
+
+def pin_gqa_group_mapping():
+    assert [O.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [O.kv_head(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+    for H, Hkv in ((6, 4), (4, 0)):
+        try:
+            O.kv_head(0, H, Hkv)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError((H, Hkv))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -76,3 +76,19 @@ def test_planted_mistake_is_caught(orc, tmp_path, mid, old, new):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode != 3, f"mutant {mid} survived: {r.stdout[-500:]}"
     assert r.returncode == 0, f"mutant {mid} crashed the runner (rc={r.returncode}): {r.stderr[-800:]}"
+
+
+# planted mistakes in the oracle's Python head bookkeeping (grouped-query attention)
+PY_MUTANTS = [
+    ("kv_head_modulo", lambda h, H, Hkv: h % Hkv),
+    ("kv_head_first", lambda h, H, Hkv: 0),
+]
+
+
+@pytest.mark.parametrize("mid,fn", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_python_mistake_is_caught(orc, monkeypatch, mid, fn):
+    import oracle_pins
+
+    monkeypatch.setattr(orc, "kv_head", fn)
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_gqa_equals_replicated_kv()
