@@ -142,7 +142,7 @@ def main():
     q, k, v = synth.make_qkv(w)
     tdt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
     qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
-    bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev)
+    bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads)
     out = torch.empty_like(qd)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -190,7 +190,7 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+fp8" if args.pv == "fp8" else "i8+f16",
         "data": "synthetic",
-        "config": {"workload": name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "input_dtype": w.dtype,
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D, "input_dtype": w.dtype,
                    "layout": w.layout, "causal": causal, "pv_mode": args.pv},
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),

@@ -30,7 +30,9 @@
  *    16-byte aligned; scale / mean arrays 4-byte aligned.  Outputs must not
  *    overlap inputs.
  *  - Shapes: B, H >= 1; 1 <= S <= SAGE_MAX_S; D in {64, 128};
- *    B * H <= SAGE_MAX_BH.
+ *    B * H <= SAGE_MAX_BH.  K and V may have fewer heads than Q (grouped-query
+ *    attention, [REPO] feature list): H_kv >= 1 divides H, and query head h
+ *    uses K/V head h / (H / H_kv); H_kv = H is ordinary multi-head attention.
  *  - Errors are reported only through the return code.  All argument checks
  *    happen before anything is enqueued; on an error nothing is enqueued.
  *    SAGE_ERR_UNSUPPORTED means the current device is not gfx950.
@@ -42,14 +44,14 @@
  *   nq = S_q / SAGE_BLK_Q, nk = S_k / SAGE_BLK_K.
  *   q_i8    int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
  *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens.
- *   k_i8    int8  [B][H][S_k][D]   INT8 codes of K - k_mean; rows >= S are 0.
- *   k_scale float [B][H][nk]       one scale per block of SAGE_BLK_K tokens (0 for blocks
+ *   k_i8    int8  [B][H_kv][S_k][D] INT8 codes of K - k_mean; rows >= S are 0.
+ *   k_scale float [B][H_kv][nk]    one scale per block of SAGE_BLK_K tokens (0 for blocks
  *                                  made only of padding keys).
- *   k_mean  float [B][H][D]        per-channel mean of K over the S tokens.
- *   v_fp8   uint8 [B][H][nk][D][64] E4M3 codes of V, one 64-key tile after the
+ *   k_mean  float [B][H_kv][D]     per-channel mean of K over the S tokens.
+ *   v_fp8   uint8 [B][H_kv][nk][D][64] E4M3 codes of V, one 64-key tile after the
  *           other, each tile stored channel-major; inside a tile, byte p of
  *           channel d holds key  SAGE_VPOS_KEY(p)  of that tile (keys >= S are 0).
- *   v_scale float [B][H][D]        one scale per channel.
+ *   v_scale float [B][H_kv][D]     one scale per channel.
  *   out: same dtype and layout (HND or NHD) as q.
  */
 #ifndef SAGE_H
@@ -96,7 +98,7 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16);
 
 /* Bytes of each intermediate buffer for a problem shape (see the layouts
  * above).  Any output pointer may be NULL. */
-int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8,
+int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8,
                       size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
 
 /*
@@ -107,14 +109,15 @@ int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale,
  *   (one fp32 subtraction per element), each over all D channels:
  *     amax = max |x|;  scale = amax / 127;  code = rint(x * (127 / amax)) in [-127, 127];
  *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
- * q, k: dtype (SAGE_DTYPE_*) tensors in `layout` (SAGE_LAYOUT_*).
+ * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
+ * same with H_kv heads.
  * Writes q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).  The call is
  * several kernel launches; while it runs, k_i8 also holds intermediate
  * per-chunk channel sums, so its content is defined only after the stream has
  * passed the call.
  */
-int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int S, int D, int layout,
-                         int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
+int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
+                         int layout, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
                          void *stream);
 
 /*
@@ -122,6 +125,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
  *   amax_d = max_s |V[s][d]|;  v_scale[d] = amax_d / 448;
  *   code = E4M3(V[s][d] * (448 / amax_d)), round to nearest even, |x| clamped to 448;
  *   an all-zero channel has scale 0 and codes 0.
+ * H is the number of V heads (H_kv of the other entry points).
  * Writes v_fp8 in the tiled layout above and v_scale.  While the call's
  * launches run, v_fp8 and v_scale hold intermediate per-channel maxima, so
  * both are defined only after the stream has passed the call.
@@ -140,27 +144,28 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
  * q_i8 .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
- * sage_quant_v.  pv fp16: v = the original V tensor (dtype, layout), v_scale = NULL
- * (bf16 V is rounded to fp16).  out: dtype tensor in `layout`, shape of q.
+ * sage_quant_v.  pv fp16: v = the original V tensor (dtype, layout, H_kv heads),
+ * v_scale = NULL (bf16 V is rounded to fp16).  out: dtype tensor in `layout`, shape
+ * of q.  Query head h reads K/V head h / (H / H_kv).
  * is_causal in {0, 1}; sm_scale finite and > 0 (the usual choice is 1/sqrt(D)).
- * pv fp16 with NHD layout additionally needs H * D * 2 * SAGE_KV_PAD < 2^31
+ * pv fp16 with NHD layout additionally needs H_kv * D * 2 * SAGE_KV_PAD < 2^31
  * (128-token slices of V are addressed through a 32-bit byte range).
  */
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                  const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,
-                  int layout, int is_causal, float sm_scale, int pv_mode, void *stream);
+                  const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S,
+                  int D, int layout, int is_causal, float sm_scale, int pv_mode, void *stream);
 
 /*
  * Debug variant of sage_attn_fwd: the same kernel code, which additionally
- * writes the int32 accumulators of Q K^T for head (b, h) to qk, an int32 [S][S]
+ * writes the int32 accumulators of Q K^T for query head (b, h) to qk, an int32 [S][S]
  * array (qk[i][n] = sum_d q_i8[i][d] * k_i8[n][d]).  With is_causal, entries
  * with n > i may be left unwritten (key tiles the mask excludes for a whole
  * work-group are skipped); every entry with n <= i is written.  `out` is
  * written as by sage_attn_fwd.
  */
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S,
-                          int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
+                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
+                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
                           int32_t *qk, void *stream);
 
 /* Human-readable name of a status code (static string). */

@@ -50,10 +50,10 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         c_int, c_float, c_void_p, c_size_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
         L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
-        L.sage_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 7
-        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 6 + [c_void_p] * 5 + [c_void_p]
+        L.sage_buffer_sizes.argtypes = [c_int] * 5 + [c_size_p] * 7
+        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 7 + [c_void_p] * 5 + [c_void_p]
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p, c_void_p, c_void_p]
-        attn = [c_void_p] * 7 + [c_int] * 7 + [c_float, c_int]
+        attn = [c_void_p] * 7 + [c_int] * 8 + [c_float, c_int]
         L.sage_attn_fwd.argtypes = attn + [c_void_p]
         L.sage_attn_fwd_dump_qk.argtypes = attn + [c_int, c_int, c_void_p, c_void_p]
         L.sage_status_str.argtypes = [c_int]
@@ -85,32 +85,33 @@ def sage_get_config():
     return tuple(x.value for x in v)
 
 
-def sage_buffer_sizes(B, H, S, D):
+def sage_buffer_sizes(B, H, H_kv, S, D):
     vals = [ctypes.c_size_t() for _ in range(7)]
-    _check(lib().sage_buffer_sizes(B, H, S, D, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
+    _check(lib().sage_buffer_sizes(B, H, H_kv, S, D, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
     names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
     return {n: v.value for n, v in zip(names, vals)}
 
 
-def sage_smooth_quant_qk(q, k, dtype, B, H, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
     """All tensor arguments are device pointers (ints); returns the status code."""
-    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean, stream)
+    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                      stream)
 
 
 def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream):
     return lib().sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream)
 
 
-def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal, sm_scale,
-                  pv_mode, stream):
-    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal,
-                               sm_scale, pv_mode, stream)
+def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
+                  sm_scale, pv_mode, stream):
+    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout,
+                               is_causal, sm_scale, pv_mode, stream)
 
 
-def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal,
+def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
                           sm_scale, pv_mode, b, h, qk, stream):
-    return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout,
-                                       is_causal, sm_scale, pv_mode, b, h, qk, stream)
+    return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D,
+                                       layout, is_causal, sm_scale, pv_mode, b, h, qk, stream)
 
 
 def sage_status_str(status):
@@ -158,39 +159,55 @@ def _dtype_code(t):
 
 
 class Quantized:
-    """Device buffers produced by the two quantisation entry points."""
+    """Device buffers produced by the two quantisation entry points (K and V
+    buffers have H_kv heads; H_kv = H unless K/V are grouped)."""
 
-    def __init__(self, B, H, S, D, device):
+    def __init__(self, B, H, S, D, device, H_kv=None):
         import torch
 
+        H_kv = H if H_kv is None else H_kv
+        self.B, self.H, self.H_kv, self.S, self.D = B, H, H_kv, S, D
         sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + KV_PAD - 1) // KV_PAD * KV_PAD
         self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
         self.q_scale = torch.empty((B, H, sq // BLK_Q), dtype=torch.float32, device=device)
-        self.k_i8 = torch.empty((B, H, sk, D), dtype=torch.int8, device=device)
-        self.k_scale = torch.empty((B, H, sk // BLK_K), dtype=torch.float32, device=device)
-        self.k_mean = torch.empty((B, H, D), dtype=torch.float32, device=device)
-        self.v_fp8 = torch.empty((B, H, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
-        self.v_scale = torch.empty((B, H, D), dtype=torch.float32, device=device)
+        self.k_i8 = torch.empty((B, H_kv, sk, D), dtype=torch.int8, device=device)
+        self.k_scale = torch.empty((B, H_kv, sk // BLK_K), dtype=torch.float32, device=device)
+        self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.v_fp8 = torch.empty((B, H_kv, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
+        self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+
+
+def _kv_heads(q, k, v, tensor_layout):
+    """Number of K/V heads; checks that k, v match q apart from the head count."""
+    B, H, S, D = _shape(q, tensor_layout)
+    kb, H_kv, ks, kd = _shape(k, tensor_layout)
+    if (kb, ks, kd) != (B, S, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must match q in batch, sequence length, head dim and dtype, and each other")
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"the number of query heads ({H}) must be a multiple of the K/V heads ({H_kv})")
+    return H_kv
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None) -> Quantized:
-    """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors."""
+    """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors.
+    k and v may have fewer heads than q (grouped-query attention)."""
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must have the same shape and dtype")
+    H_kv = _kv_heads(q, k, v, tensor_layout)
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
     dt = _dtype_code(q)
-    bufs = bufs or Quantized(B, H, S, D, q.device)
+    bufs = bufs or Quantized(B, H, S, D, q.device, H_kv)
+    if (bufs.B, bufs.H, bufs.H_kv, bufs.S, bufs.D) != (B, H, H_kv, S, D):
+        raise ValueError("bufs were allocated for another shape")
     st = _stream()
-    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, S, D, layout, bufs.q_i8.data_ptr(),
+    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.q_i8.data_ptr(),
                                 bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
                                 bufs.k_mean.data_ptr(), st), "sage_smooth_quant_qk")
     if pv_mode == "fp8":
-        _check(sage_quant_v(v.data_ptr(), dt, B, H, S, D, layout, bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), st),
-               "sage_quant_v")
+        _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
+                            st), "sage_quant_v")
     return bufs
 
 
@@ -199,13 +216,18 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     """Run sage_attn_fwd (or the dump variant when dump_head=(b, h)) into `out`."""
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(out, tensor_layout)
+    if (bufs.B, bufs.H, bufs.S, bufs.D) != (B, H, S, D):
+        raise ValueError("out does not match the quantised buffers' shape")
+    H_kv = bufs.H_kv
+    if pv_mode == "fp16" and (_shape(v, tensor_layout) != (B, H_kv, S, D) or not v.is_contiguous()):
+        raise ValueError("pv fp16 reads the original V: it must be contiguous with H_kv heads")
     dt = _dtype_code(out)
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
     pv = PV[pv_mode]
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
     args = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs,
-            out.data_ptr(), dt, B, H, S, D, layout, int(bool(is_causal)), sm, pv)
+            out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv)
     if dump_head is None:
         _check(sage_attn_fwd(*args, _stream()), "sage_attn_fwd")
     else:

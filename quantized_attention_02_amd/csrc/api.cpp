@@ -33,6 +33,12 @@ int check_shape(int B, int H, int S, int D) {
   return SAGE_OK;
 }
 
+// grouped-query attention: H_kv K/V heads, each shared by H / H_kv query heads
+int check_kv_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
 int check_enums(int dtype, int layout) {
   if (dtype != SAGE_DTYPE_F16 && dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARG;
   if (layout != SAGE_LAYOUT_HND && layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
@@ -63,11 +69,12 @@ int check_device() {
 int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
 
 int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,
-                int layout, int is_causal, float sm_scale, int pv_mode, int dump_b, int dump_h, int32_t *qk,
-                bool dump, void *stream) {
+                const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S,
+                int D, int layout, int is_causal, float sm_scale, int pv_mode, int dump_b, int dump_h,
+                int32_t *qk, bool dump, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
@@ -75,7 +82,7 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
-  if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H * D * 2 * kKvPad >= (1LL << 31))
+  if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16))
     return SAGE_ERR_INVALID_ARG;
@@ -100,6 +107,7 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   a.dump_bh = dump ? dump_b * H + dump_h : -1;
   a.B = B;
   a.H = H;
+  a.H_kv = H_kv;
   a.S = S;
   a.D = D;
   a.layout = layout;
@@ -128,27 +136,29 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16) {
   return SAGE_OK;
 }
 
-int sage_buffer_sizes(int B, int H, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8, size_t *k_scale,
-                      size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
+int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8,
+                      size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
-  const size_t bh = (size_t)B * H;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
+  const size_t bh = (size_t)B * H, bhk = (size_t)B * H_kv;
   const size_t S_q = roundup(S, kBlkQ), S_k = roundup(S, kKvPad);
   if (q_i8) *q_i8 = bh * S_q * D;
   if (q_scale) *q_scale = bh * (S_q / kBlkQ) * sizeof(float);
-  if (k_i8) *k_i8 = bh * S_k * D;
-  if (k_scale) *k_scale = bh * (S_k / kBlkK) * sizeof(float);
-  if (k_mean) *k_mean = bh * D * sizeof(float);
-  if (v_fp8) *v_fp8 = bh * S_k * D;
-  if (v_scale) *v_scale = bh * D * sizeof(float);
+  if (k_i8) *k_i8 = bhk * S_k * D;
+  if (k_scale) *k_scale = bhk * (S_k / kBlkK) * sizeof(float);
+  if (k_mean) *k_mean = bhk * D * sizeof(float);
+  if (v_fp8) *v_fp8 = bhk * S_k * D;
+  if (v_scale) *v_scale = bhk * D * sizeof(float);
   return SAGE_OK;
 }
 
-int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int S, int D, int layout,
-                         int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
+int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
+                         int layout, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
                          void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16)) return SAGE_ERR_INVALID_ARG;
@@ -164,6 +174,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   a.k_mean = k_mean;
   a.B = B;
   a.H = H;
+  a.H_kv = H_kv;
   a.S = S;
   a.D = D;
   a.layout = layout;
@@ -198,18 +209,18 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
 }
 
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale, const void *v,
-                  const float *v_scale, void *out, int dtype, int B, int H, int S, int D, int layout, int is_causal,
-                  float sm_scale, int pv_mode, void *stream) {
-  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal, sm_scale,
-                     pv_mode, 0, 0, nullptr, false, stream);
+                  const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout,
+                  int is_causal, float sm_scale, int pv_mode, void *stream) {
+  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
+                     sm_scale, pv_mode, 0, 0, nullptr, false, stream);
 }
 
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int S, int D,
-                          int layout, int is_causal, float sm_scale, int pv_mode, int b, int h, int32_t *qk,
-                          void *stream) {
-  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, S, D, layout, is_causal, sm_scale,
-                     pv_mode, b, h, qk, true, stream);
+                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
+                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
+                          int32_t *qk, void *stream) {
+  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
+                     sm_scale, pv_mode, b, h, qk, true, stream);
 }
 
 const char *sage_status_str(int status) {

@@ -293,6 +293,8 @@ k_attn(const AttnArgs a) {
   }
   const int mblk = CAUSAL ? a.nmblk - 1 - mrank : mrank;
   const int b = bh / a.H, h = bh % a.H;
+  // grouped-query attention: H / H_kv consecutive query heads read one K/V head
+  const int hk = h / (a.H / a.H_kv), bhk = b * a.H_kv + hk;
   const int q0 = mblk * kBlockM;
   const int qw = q0 + 32 * wave;  // first query row of this wavefront
   const bool active = qw < a.S;
@@ -323,10 +325,10 @@ k_attn(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[c][r] = 0.0f;
 
-  const int8_t *kbase = a.k_i8 + (long long)bh * a.S_k * D;
-  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + (long long)bh * a.S_k * D;
-  const float *kscale = a.k_scale + (long long)bh * a.nk;
-  const HeadView hv = head_view(a.layout, b, h, a.H, a.S, D);
+  const int8_t *kbase = a.k_i8 + (long long)bhk * a.S_k * D;
+  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + (long long)bhk * a.S_k * D;
+  const float *kscale = a.k_scale + (long long)bhk * a.nk;
+  const HeadView hv = head_view(a.layout, b, hk, a.H_kv, a.S, D);  // pv fp16: the caller's V
   const TileCopy<D, TN, WAVES> copy(wave, lane);
   const VCopy16<D, TN, WAVES> vcopy(lane);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, a.S_k * D);
@@ -518,7 +520,7 @@ k_attn(const AttnArgs a) {
     }
   };
 
-  if (PV == 0 && tid < D) vsc[tid] = a.v_scale[(long long)bh * D + tid];
+  if (PV == 0 && tid < D) vsc[tid] = a.v_scale[(long long)bhk * D + tid];
 
   // ---- main loop: tile j is computed from buffer j % NBUF while tiles
   //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next

@@ -146,8 +146,8 @@ __device__ inline void chunk_reduce(const uint16_t *x, const HeadView &hv, int S
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
   const int nch = n_chunks(a.S);
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
-  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;  // bh: K head (b, h_kv)
+  const HeadView hv = head_view(a.layout, bh / a.H_kv, bh % a.H_kv, a.H_kv, a.S, D);
   chunk_reduce<DT, D, false>((const uint16_t *)a.k, hv, a.S, chunk, a.k_i8 + (long long)bh * a.S_k * D);
 }
 
@@ -195,11 +195,11 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
   }
 }
 
-// k_mean[bh][d] = fp32(sum over the head's chunk partials / S); thread = (bh, d)
+// k_mean[bh][d] = fp32(sum over the head's chunk partials / S); thread = (K head bh, d)
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= (long long)a.B * a.H * D) return;
+  if (i >= (long long)a.B * a.H_kv * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
   const double *part = reinterpret_cast<const double *>(a.k_i8 + (long long)bh * a.S_k * D);
   const int nch = n_chunks(a.S);
@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
   __shared__ float red[kThreads / 64];
   __shared__ float mean[D];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x / a.nk, blk = blockIdx.x % a.nk;
-  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  const int bh = blockIdx.x / a.nk, blk = blockIdx.x % a.nk;  // bh: K head (b, h_kv)
+  const HeadView hv = head_view(a.layout, bh / a.H_kv, bh % a.H_kv, a.H_kv, a.S, D);
   const uint16_t *k = (const uint16_t *)a.k;
   if (tid < D) mean[tid] = a.k_mean[(long long)bh * D + tid];
   __syncthreads();
@@ -342,12 +342,12 @@ __global__ __launch_bounds__(kThreads) void k_vscale(const QuantVArgs a) {
 
 template <int DT, int D>
 static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
-  const int bh = a.B * a.H;
-  const int gd = (bh * D + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bh * n_chunks(a.S)), dim3(kThreads), 0, stream, a);
+  const int bh = a.B * a.H, bhk = a.B * a.H_kv;
+  const int gd = (bhk * D + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * n_chunks(a.S)), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_qquant<DT, D>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((k_kquant<DT, D>), dim3(bh * a.nk), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_kquant<DT, D>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
 }
 
 template <int DT, int D>

@@ -76,7 +76,7 @@ struct QuantQKArgs {
   const void *q, *k;
   int8_t *q_i8, *k_i8;
   float *q_scale, *k_scale, *k_mean;
-  int B, H, S, D, layout, dtype;
+  int B, H, H_kv, S, D, layout, dtype;  // K has H_kv heads
   int S_q, S_k, nq, nk;
 };
 
@@ -96,7 +96,7 @@ struct AttnArgs {
   void *out;
   int32_t *dump;
   int dump_bh;
-  int B, H, S, D, layout, dtype, causal, pv;
+  int B, H, H_kv, S, D, layout, dtype, causal, pv;  // K and V have H_kv heads
   int S_q, S_k, nq, nk, nmblk;
   float sm2;  // sm_scale * log2(e)
 };

@@ -33,12 +33,17 @@ def test_library_exports_every_declared_symbol():
 
 def test_config_and_sizes():
     assert qa.sage_get_config() == (32, 64, qa.TILE_K["fp8"], qa.TILE_K["fp16"])
-    s = qa.sage_buffer_sizes(2, 3, 100, 64)
+    s = qa.sage_buffer_sizes(2, 3, 3, 100, 64)
     assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 4 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 2 * 4,
                  "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4}
+    # grouped K/V: the K and V buffers hold B * H_kv heads
+    s = qa.sage_buffer_sizes(2, 6, 2, 100, 64)
+    assert s == {"q_i8": 12 * 128 * 64, "q_scale": 12 * 4 * 4, "k_i8": 4 * 128 * 64, "k_scale": 4 * 2 * 4,
+                 "k_mean": 4 * 64 * 4, "v_fp8": 4 * 128 * 64, "v_scale": 4 * 64 * 4}
     L = qa.lib()
     assert L.sage_get_config(None, None, None, None) == qa.SAGE_ERR_INVALID_ARG
-    for bad in [(0, 1, 1, 64), (1, 0, 1, 64), (1, 1, 0, 64), (1, 1, 1, 96), (1, 1, (1 << 20) + 1, 64)]:
+    for bad in [(0, 1, 1, 1, 64), (1, 0, 1, 1, 64), (1, 1, 1, 0, 64), (1, 1, 1, 1, 96), (1, 1, 1, (1 << 20) + 1, 64),
+                (1, 4, 0, 1, 64), (1, 4, 3, 1, 64), (1, 4, 8, 1, 64), (1, 4, -4, 1, 64)]:
         assert L.sage_buffer_sizes(*bad, *([None] * 7)) == qa.SAGE_ERR_INVALID_ARG
 
 
@@ -63,21 +68,22 @@ def test_vpos_key_is_a_permutation():
 
 # a valid-looking set of (fake, aligned, non-null) device pointers
 P = 1 << 12
-GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, q_i8=P, q_scale=P, k_i8=P, k_scale=P,
+GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, H_kv=2, S=100, D=64, layout=0, q_i8=P, q_scale=P, k_i8=P, k_scale=P,
                k_mean=P, stream=None)
 GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, stream=None)
-GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, out=P, dtype=0, B=1, H=2, S=100, D=64,
-                 layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, stream=None)
+GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, out=P, dtype=0, B=1, H=2, H_kv=2, S=100,
+                 D=64, layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, stream=None)
 
 BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict(q_scale=P + 2), dict(dtype=2),
           dict(layout=-1), dict(B=0), dict(H=-1), dict(S=0), dict(D=32), dict(D=256), dict(S=(1 << 20) + 1),
-          dict(B=1 << 9, H=1 << 8)]
+          dict(B=1 << 9, H=1 << 8, H_kv=1 << 8), dict(H_kv=0), dict(H_kv=3), dict(H=3, H_kv=2), dict(H_kv=-2)]
 BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
             dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
             dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
-            # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H * D * 2 * 128 < 2^31
-            dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, D=128)]
+            dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1),
+            # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
+            dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
 
 
 def _call_qk(**kw):
@@ -114,7 +120,10 @@ def test_attn_fp16_mode_accepts_null_v_scale_then_needs_device():
     rc = _call_attn(pv_mode=1, v_scale=None)
     assert rc in (qa.SAGE_ERR_NO_DEVICE, qa.SAGE_OK, qa.SAGE_ERR_UNSUPPORTED) or rc != qa.SAGE_ERR_INVALID_ARG
     # the largest NHD head count the fp16 mode takes passes the argument checks
-    rc = _call_attn(pv_mode=1, v_scale=None, layout=1, B=1, H=(1 << 16) - 1, D=128)
+    rc = _call_attn(pv_mode=1, v_scale=None, layout=1, B=1, H=(1 << 16) - 1, H_kv=(1 << 16) - 1, D=128)
+    assert rc != qa.SAGE_ERR_INVALID_ARG
+    # the limit is on the V tensor's heads: many query heads over few K/V heads pass
+    rc = _call_attn(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 10, D=128)
     assert rc != qa.SAGE_ERR_INVALID_ARG
 
 
@@ -134,6 +143,8 @@ def _no_gpu():
 @pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
 def test_valid_arguments_without_a_device_report_no_device():
     assert _call_qk() == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qk(H=8, H_kv=2) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v() == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn() == qa.SAGE_ERR_NO_DEVICE
 

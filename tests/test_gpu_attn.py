@@ -34,12 +34,19 @@ SMALL_CASES = [
     (synth.custom(1, 2, 257, 128, dtype="bf16", layout="NHD", seed=206), False, "fp16"),
     (synth.custom(1, 3, 1000, 128, token_norm=True, seed=207), True, "fp8"),
     (synth.custom(1, 2, 640, 128, seed=208), False, "fp8"),
+    # grouped-query attention (query heads h*G .. h*G+G-1 share K/V head h)
+    (synth.custom(2, 6, 300, 64, Hkv=2, seed=209), False, "fp8"),
+    (synth.custom(2, 6, 300, 64, Hkv=2, seed=209), True, "fp16"),
+    (synth.custom(1, 8, 257, 128, dtype="bf16", layout="NHD", Hkv=1, seed=210), True, "fp8"),
+    (synth.custom(1, 8, 257, 128, dtype="bf16", layout="NHD", Hkv=4, seed=211), False, "fp16"),
 ]
 FULL_CASES = [
     (W["snippet_b2h32s4096d128"], False, "fp8"),
     (W["snippet_b2h32s4096d128"], False, "fp16"),
     (W["prefill_b1h32s32768d128"], True, "fp8"),
     (W["dit_b1h20s16384d128"], False, "fp8"),
+    (W["gqa_b1h32kv8s8192d128"], True, "fp8"),
+    (W["gqa_b1h32kv8s8192d128"], True, "fp16"),
 ]
 
 
@@ -93,6 +100,7 @@ DUMP_CASES = [
     (synth.custom(1, 2, 100, 128, seed=301), True, (0, 1)),
     (synth.custom(2, 2, 257, 64, layout="NHD", dtype="bf16", seed=302), False, (1, 0)),
     (W["snippet_b2h32s4096d128"], False, (1, 17)),
+    (synth.custom(2, 6, 300, 64, Hkv=2, seed=303), True, (1, 5)),
 ]
 
 
@@ -100,14 +108,15 @@ DUMP_CASES = [
 def test_qk_int32_dump_bit_exact(w, causal, head):
     bufs, out, dump = G.run(w, causal=causal, dump_head=head)
     b, h = head
+    hk = O.kv_head(h, w.H, w.kv_heads)
     q8 = bufs.q_i8.cpu().numpy()[b, h, :w.S]
-    k8 = bufs.k_i8.cpu().numpy()[b, h, :w.S]
+    k8 = bufs.k_i8.cpu().numpy()[b, hk, :w.S]
     # the oracle's integer GEMM on the oracle's own codes (themselves bit-exact
     # with the GPU's, checked in test_gpu_quant)
     q, k, _ = G.inputs(w)
     dt = O.DTYPES[w.dtype]
     rq8, _ = O.quant_q_head(O.decode16(O.head(q, w.layout, b, h), dt), 32)
-    rk8, _, _ = O.quant_k_head(O.decode16(O.head(k, w.layout, b, h), dt), 64, True)
+    rk8, _, _ = O.quant_k_head(O.decode16(O.head(k, w.layout, b, hk), dt), 64, True)
     assert np.array_equal(q8, rq8) and np.array_equal(k8, rk8)
     ref = O.qk_int32_head(rq8, rk8)
     got = dump.cpu().numpy()
@@ -162,3 +171,22 @@ def test_sm_scale_is_applied():
         ref = O.attn(q, k, v, O.F16, "HND", sm_scale=sm, tile_k=G.TILE_K["fp8"])
         ref = np.stack([ref[(0, h)] for h in range(2)])[None]
         assert G.cos(got, ref) >= COS_MIN and G.rel_l1(got, ref) <= REL_L1_MAX
+
+
+@pytest.mark.parametrize("layout,pv", [("HND", "fp8"), ("NHD", "fp16")])
+def test_gqa_equals_replicated_kv_bitwise(layout, pv):
+    """Grouped K/V heads give bit-for-bit the output of the same K/V copied to
+    every query head of the group (H_kv = H)."""
+    import torch
+
+    import quantized_attention_02_amd as qa
+
+    w = synth.custom(1, 6, 333, 128, layout=layout, Hkv=2, seed=601)
+    q, k, v = (G.to_device(x, w.dtype) for x in G.inputs(w))
+    hd = 1 if layout == "HND" else 2
+    kr, vr = (x.repeat_interleave(3, dim=hd).contiguous() for x in (k, v))
+    for causal in (False, True):
+        out = qa.sageattn(q, k, v, tensor_layout=layout, is_causal=causal, pv_mode=pv)
+        ref = qa.sageattn(q, kr, vr, tensor_layout=layout, is_causal=causal, pv_mode=pv)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), causal
