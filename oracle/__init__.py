@@ -207,9 +207,13 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
 
     blk_q / blk_k: tokens per INT8 scale of Q / K; tile_k: keys per online-softmax
-    tile (the two-level accumulation folds once per tile)."""
-    S, D = q8.shape
-    rows = np.arange(S, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    tile (the two-level accumulation folds once per tile).  The query rows (q8)
+    and the keys (k8, v8, vf) may differ in number."""
+    Sq, D = q8.shape
+    S = k8.shape[0]  # keys
+    rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    if rows.size and (rows.min() < 0 or rows.max() >= Sq):
+        raise ValueError("query row out of range")
     out = np.empty((rows.size, D), np.float32)
     q8 = np.ascontiguousarray(q8, np.int8)
     k8 = np.ascontiguousarray(k8, np.int8)
@@ -228,8 +232,9 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
 
 def attn_exact_head(qf, kf, vf, *, is_causal, sm_scale, rows=None) -> np.ndarray:
     qf, kf, vf = _f32(qf), _f32(kf), _f32(vf)
-    S, D = qf.shape
-    rows = np.arange(S, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    Sq, D = qf.shape
+    S = kf.shape[0]  # keys
+    rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
     out = np.empty((rows.size, D), np.float64)
     lib().orc_attn_exact_head(_p(qf, ctypes.c_float), _p(kf, ctypes.c_float), _p(vf, ctypes.c_float), S, D,
                               int(bool(is_causal)), ctypes.c_double(sm_scale), _p(rows, ctypes.c_int), rows.size,
@@ -331,4 +336,44 @@ def attn_exact(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=No
         res[(b, h)] = attn_exact_head(decode16(head(q, layout, b, h), dtype), decode16(head(k, layout, b, hk), dtype),
                                       decode16(head(v, layout, b, hk), dtype), is_causal=is_causal,
                                       sm_scale=sm_scale, rows=rows)
+    return res
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+def seq_slices(cu_seqlens) -> list:
+    """[(start, end)] of each sequence from the prefix sums cu_seqlens[0..B]."""
+    cu = [int(x) for x in cu_seqlens]
+    if not cu or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0 and not decrease")
+    return list(zip(cu[:-1], cu[1:]))
+
+
+def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
+                heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True):
+    """Quantized attention over a packed batch of sequences of different lengths
+    ("Thư viện SageAttention" page, feature list: variable-length sequences through
+    sageattn_varlen).
+
+    q: [Tq, H, D] and k, v: [Tk, Hkv, D] uint16 codes, the tokens of sequence b
+    at rows cu_q[b] .. cu_q[b+1] of q and cu_k[b] .. cu_k[b+1] of k and v.
+    Reading: each sequence is attended on its own, exactly as a batch of one
+    (the K mean, the INT8 blocks, the V scales and the causal mask all start
+    at the sequence's first token); query and key counts may differ, causal
+    keeps key n for query i when n <= i, and a sequence without keys gives 0.
+
+    heads: [(b, h)] (default: all); rows: query rows within each sequence.
+    Returns {(b, h): fp32 [rows, D]}.
+    """
+    sq, sk = seq_slices(cu_q), seq_slices(cu_k)
+    if len(sq) != len(sk) or sq[-1][1] != q.shape[0] or sk[-1][1] != k.shape[0] or v.shape != k.shape:
+        raise ValueError("cu_seqlens do not describe q / k / v")
+    H, Hkv = q.shape[1], k.shape[1]
+    heads = [(b, h) for b in range(len(sq)) for h in range(H)] if heads is None else heads
+    res = {}
+    for (b, h) in heads:
+        (q0, q1), (k0, k1) = sq[b], sk[b]
+        one = attn(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype, "NHD", is_causal=is_causal,
+                   sm_scale=sm_scale, pv_mode=pv_mode, heads=[(0, h)], rows=rows, blk_q=blk_q, blk_k=blk_k,
+                   tile_k=tile_k, smooth=smooth)
+        res[(b, h)] = one[(0, h)]
     return res

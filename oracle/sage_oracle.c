@@ -168,13 +168,14 @@ void orc_int8_quant_block(const float *x, size_t n, int8_t *codes, float *scale)
  * K smoothing statistic: the mean of each channel over all S tokens of the
  * head ([SA2, 相关工作] K is pre-processed; [SA2, SageAttention2方法] K smoothing).
  * Sum in binary64 over tokens in order, divide by S in binary64, round once
- * to fp32.
+ * to fp32.  A head with no tokens (an empty sequence of a packed batch) has
+ * mean 0.
  */
 void orc_channel_mean(const float *x, int S, int D, float *mean) {
     for (int d = 0; d < D; ++d) {
         double s = 0.0;
         for (int t = 0; t < S; ++t) s += (double)x[(size_t)t * D + d];
-        mean[d] = (float)(s / (double)S);
+        mean[d] = S > 0 ? (float)(s / (double)S) : 0.0f;
     }
 }
 
@@ -248,7 +249,8 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
 }
 
 /*
- * Quantized attention for selected query rows of one head.
+ * Quantized attention for selected query rows of one head over its S keys
+ * (query rows index q8; the number of query rows may differ from S).
  *
  * Key tiles of `tile_k` tokens are visited in order with an online softmax
  * whose running max m and running sum l are fp32 ([SA2, 相关工作]: token-dim
@@ -257,7 +259,8 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  * scale blocks of K (`blk_k` tokens each, key n uses k_scale[n / blk_k]).
  * Per key tile:
  *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_blk(n)) * sm_scale)     (dequantise)
- *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal)
+ *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal;
+ *           key n and query i count from the start of their sequences)
  *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first tile)
  *   p_n   = exp(s_n - m')                                            (fp32)
  *   l     = alpha * l + sum_n p_n                (uses the unquantised p_n)
@@ -272,7 +275,7 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  *   O_d   = alpha * O_d + sum_n P_n * V_n,d;   out = O_d / l
  * `v` (fp32 values of the original V) is read only in pv fp16 mode; `v8`,
  * `v_scale` only in pv fp8 mode.  out is [nrows][D] fp32 (before the final
- * rounding to the input dtype).
+ * rounding to the input dtype).  A row that sees no key at all (S = 0) is 0.
  */
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int tile_k,
@@ -337,7 +340,9 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                 m = mnew;
             }
             float *o = out + (size_t)r * D;
-            if (pv_mode == ORC_PV_FP8) {
+            if (l == 0.0f) {
+                for (int d = 0; d < D; ++d) o[d] = 0.0f;
+            } else if (pv_mode == ORC_PV_FP8) {
                 for (int d = 0; d < D; ++d) o[d] = O[d] * (v_scale[d] / (448.0f * l));
             } else {
                 for (int d = 0; d < D; ++d) o[d] = O[d] / l;
@@ -352,7 +357,8 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
 
 /*
  * Exact attention in binary64, no smoothing and no quantisation:
- * out_i = sum_n softmax_n(sm_scale * q_i . k_n) v_n, keys n > i excluded when causal.
+ * out_i = sum_n softmax_n(sm_scale * q_i . k_n) v_n over the S keys, keys n > i
+ * excluded when causal; a row with no visible key is 0.
  */
 void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, int D,
                          int is_causal, double sm_scale, const int *rows, int nrows,
@@ -363,7 +369,7 @@ void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, 
 #pragma omp for schedule(dynamic, 1)
         for (int r = 0; r < nrows; ++r) {
             int i = rows[r];
-            int nvis = is_causal ? i + 1 : S;
+            int nvis = is_causal ? (i + 1 < S ? i + 1 : S) : S;
             double mx = -INFINITY;
             for (int n = 0; n < nvis; ++n) {
                 double a = 0.0;
@@ -380,7 +386,7 @@ void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, 
             for (int d = 0; d < D; ++d) {
                 double a = 0.0;
                 for (int n = 0; n < nvis; ++n) a += s[n] * (double)v[(size_t)n * D + d];
-                o[d] = a / den;
+                o[d] = nvis > 0 ? a / den : 0.0;
             }
         }
         free(s);

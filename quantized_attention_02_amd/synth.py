@@ -20,6 +20,13 @@ Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this order
 Application: x *= r (token norm), K += c, then masked entries of Q and K *= 20.
 Then cast round-to-nearest-even to fp16 (numpy) or bf16 (torch CPU) and, for
 NHD, permute to [B, S, H, D].  Returned arrays are the raw uint16 codes.
+
+Packed variable-length batches (``VarlenWorkload``): Q is the recipe above
+with B = 1, S = total query tokens, NHD, seed s; K and V the same with S =
+total key tokens, Hkv heads, seed s + 1; the batch axis is dropped, giving
+token-major [T, H, D].  Sequence lengths come from ``mixed_lengths``: draws
+log-uniform in [lo, hi] (rounded) until the total is reached, the last one cut
+to fit -- a serving-style mix of short and long prompts.
 """
 from __future__ import annotations
 
@@ -118,3 +125,85 @@ def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0
     kv = f"kv{Hkv}" if Hkv else ""
     return Workload(f"custom_b{B}h{H}{kv}s{S}d{D}", B, H, S, D, dtype, layout, bias_sigma, outlier_p, token_norm,
                     seed=seed, Hkv=Hkv)
+
+
+def mixed_lengths(total: int, lo: int, hi: int, seed: int) -> tuple:
+    """Sequence lengths summing to `total`, log-uniform in [lo, hi]."""
+    rng = np.random.default_rng(seed)
+    out, left = [], total
+    while left > 0:
+        n = int(round(float(np.exp(rng.uniform(np.log(lo), np.log(hi))))))
+        n = max(1, min(n, left))
+        out.append(n)
+        left -= n
+    return tuple(out)
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    H: int
+    Hkv: int
+    D: int
+    dtype: str
+    seqlens_q: tuple
+    seqlens_k: tuple
+    bias_sigma: float = 3.0
+    causal: tuple = (True,)
+    pv_modes: tuple = ("fp8",)
+    seed: int = 0
+
+    @property
+    def B(self) -> int:
+        return len(self.seqlens_q)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.seqlens_q))
+
+    @property
+    def total_k(self) -> int:
+        return int(sum(self.seqlens_k))
+
+    def cu_seqlens(self):
+        """(cu_q, cu_k): int32 prefix sums [B + 1]."""
+        cq = np.concatenate([[0], np.cumsum(self.seqlens_q)]).astype(np.int32)
+        ck = np.concatenate([[0], np.cumsum(self.seqlens_k)]).astype(np.int32)
+        return cq, ck
+
+    def ops(self, causal: bool) -> float:
+        """Attention operations per call: 4*H*D*sum(Sq*Sk), the causal mask keeping
+        about half (sum of min(i + 1, Sk) over the query rows i)."""
+        n = 0.0
+        for sq, sk in zip(self.seqlens_q, self.seqlens_k):
+            if causal:
+                m = min(sq, sk)
+                n += m * (m + 1) / 2 + (sq - m) * sk
+            else:
+                n += sq * sk
+        return 4.0 * self.H * self.D * n
+
+
+def varlen(name, H, Hkv, D, seqlens_q, seqlens_k=None, dtype="fp16", bias_sigma=2.0, causal=(False,),
+           pv_modes=("fp8",), seed=0) -> VarlenWorkload:
+    return VarlenWorkload(name, H, Hkv, D, dtype, tuple(seqlens_q), tuple(seqlens_k or seqlens_q), bias_sigma,
+                          causal, pv_modes, seed)
+
+
+def make_qkv_varlen(w: VarlenWorkload):
+    """(q [Tq, H, D], k [Tk, Hkv, D], v [Tk, Hkv, D]) uint16 codes, token-major."""
+    wq = Workload(w.name + "_q", 1, w.H, w.total_q, w.D, w.dtype, "NHD", w.bias_sigma, seed=w.seed)
+    wk = Workload(w.name + "_kv", 1, w.H, w.total_k, w.D, w.dtype, "NHD", w.bias_sigma, seed=w.seed + 1, Hkv=w.Hkv)
+    q = make_qkv(wq)[0][0]
+    _, k, v = make_qkv(wk)
+    return q, k[0], v[0]
+
+
+VARLEN_WORKLOADS = {
+    w.name: w
+    for w in [
+        # LLM prefill of a batch of prompts of mixed lengths, 32768 tokens in all, GQA 32/8
+        varlen("varlen_h32kv8t32768d128", 32, 8, 128, mixed_lengths(32768, 128, 8192, seed=48), dtype="bf16",
+               bias_sigma=3.0, causal=(True,), pv_modes=("fp8", "fp16"), seed=48),
+    ]
+}

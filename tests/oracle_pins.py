@@ -470,3 +470,92 @@ def pin_gqa_group_mapping():
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+# ------------------------------------------------------------------ packed variable-length batches
+def _packed(lengths_q, lengths_k, H, Hkv, D, seed0, dtype="fp16"):
+    """Sequences generated one by one (each its own seeded draw), then packed
+    token-major: returns (q, k, v, cu_q, cu_k, per-sequence [B=1, S, H, D] arrays)."""
+    seqs = []
+    for i, (sq, sk) in enumerate(zip(lengths_q, lengths_k)):
+        wq = synth.custom(1, H, sq, D, dtype=dtype, layout="NHD", seed=seed0 + i)
+        wk = synth.custom(1, H, sk, D, dtype=dtype, layout="NHD", Hkv=Hkv, seed=seed0 + 100 + i)
+        q = synth.make_qkv(wq)[0]
+        _, k, v = synth.make_qkv(wk)
+        seqs.append((q, k, v))
+    q = np.concatenate([s[0][0] for s in seqs], axis=0)
+    k = np.concatenate([s[1][0] for s in seqs], axis=0)
+    v = np.concatenate([s[2][0] for s in seqs], axis=0)
+    cu_q = np.concatenate([[0], np.cumsum(lengths_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lengths_k)]).astype(np.int32)
+    return q, k, v, cu_q, cu_k, seqs
+
+
+def pin_varlen_matches_separate_sequences():
+    """A packed batch gives, sequence by sequence, bit for bit what each sequence
+    gives on its own (generated separately, not cut out of the packed arrays):
+    self-attention lengths, a sequence shorter than one Q block, one that is
+    not a multiple of a K block, GQA heads."""
+    lengths = [200, 7, 64, 129]
+    q, k, v, cu_q, cu_k, seqs = _packed(lengths, lengths, 4, 2, 64, seed0=700)
+    for causal in (False, True):
+        for pv in (O.PV_FP8, O.PV_FP16):
+            got = O.attn_varlen(q, k, v, cu_q, cu_k, F16, is_causal=causal, pv_mode=pv)
+            for b, (sq, sk, sv) in enumerate(seqs):
+                ref = O.attn(sq, sk, sv, F16, "NHD", is_causal=causal, pv_mode=pv)
+                for h in range(4):
+                    assert got[(b, h)].shape == (lengths[b], 64)
+                    assert np.array_equal(got[(b, h)].view(np.uint32), ref[(0, h)].view(np.uint32)), (b, h, causal)
+    # query and key lengths that differ per sequence (cross-attention shapes)
+    lq, lk = [33, 90, 5], [150, 12, 64]
+    q, k, v, cu_q, cu_k, seqs = _packed(lq, lk, 2, 1, 64, seed0=720)
+    for causal in (False, True):
+        got = O.attn_varlen(q, k, v, cu_q, cu_k, F16, is_causal=causal)
+        for b, (sq, sk, sv) in enumerate(seqs):
+            ref = O.attn(sq, sk, sv, F16, "NHD", is_causal=causal)
+            for h in range(2):
+                assert np.array_equal(got[(b, h)].view(np.uint32), ref[(0, h)].view(np.uint32)), (b, h, causal)
+
+
+def pin_cross_lengths_textbook():
+    """Query and key counts that differ: exact attention is the textbook softmax
+    (causal keeps key n <= query i, counted from the sequence start), and the
+    quantized pipeline tracks it."""
+    from scipy.special import softmax
+
+    for Sq, Sk in ((40, 150), (150, 40)):
+        qf = _rand_head(Sq, 64, seed=31)[0]
+        _, kf, vf = _rand_head(Sk, 64, seed=32)
+        for causal in (False, True):
+            s = (qf.astype(np.float64) @ kf.astype(np.float64).T) * 0.125
+            if causal:
+                s = np.where(np.arange(Sk)[None, :] <= np.arange(Sq)[:, None], s, -np.inf)
+            ref = softmax(s, axis=1) @ vf.astype(np.float64)
+            ex = O.attn_exact_head(qf, kf, vf, is_causal=causal, sm_scale=0.125)
+            assert ex.shape == (Sq, 64) and np.allclose(ex, ref, rtol=1e-12, atol=1e-12), (Sq, Sk, causal)
+            for pv in (O.PV_FP8, O.PV_FP16):
+                q8, qs, k8, ks, _, v8, vs = _quant_head(qf, kf, vf)
+                got = O.attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=F16, is_causal=causal, sm_scale=0.125,
+                                       pv_mode=pv)
+                assert got.shape == (Sq, 64)
+                assert cos(got, ref) >= 0.999 and rel_l1(got, ref) < 0.05, (Sq, Sk, causal, pv, cos(got, ref))
+
+
+def pin_no_keys_gives_zero():
+    """A sequence with queries but no keys: every output row is 0 (no NaN); a
+    sequence with no queries has no output rows."""
+    qf = _rand_head(20, 64, seed=33)[0]
+    empty = np.zeros((0, 64), np.float32)
+    for causal in (False, True):
+        ex = O.attn_exact_head(qf, empty, empty, is_causal=causal, sm_scale=0.125)
+        assert ex.shape == (20, 64) and not ex.any()
+        q8, qs, k8, ks, km, v8, vs = _quant_head(qf, empty, empty)
+        assert not km.any() and ks.size == 0 and vs.shape == (64,) and not vs.any()
+        for pv in (O.PV_FP8, O.PV_FP16):
+            got = O.attn_head_rows(q8, qs, k8, ks, v8, vs, empty, in_dtype=F16, is_causal=causal,
+                                   sm_scale=0.125, pv_mode=pv)
+            assert got.shape == (20, 64) and np.isfinite(got).all() and not got.any()
+    q, k, v, cu_q, cu_k, _ = _packed([0, 50], [30, 0], 2, 2, 64, seed0=740)
+    got = O.attn_varlen(q, k, v, cu_q, cu_k, F16)
+    assert got[(0, 1)].shape == (0, 64)
+    assert got[(1, 0)].shape == (50, 64) and not got[(1, 0)].any()

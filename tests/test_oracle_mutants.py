@@ -21,7 +21,7 @@ MUTANTS = [
     ("int8_range_128", "float inv = 127.0f / amax;", "float inv = 128.0f / amax;"),
     ("int8_scale_128", "*scale = amax / 127.0f;", "*scale = amax / 128.0f;"),
     ("no_k_smoothing", "ks[i] = k[i] - mean[i % D];", "ks[i] = k[i];"),
-    ("mean_divides_by_D", "mean[d] = (float)(s / (double)S);", "mean[d] = (float)(s / (double)D);"),
+    ("mean_divides_by_D", "(float)(s / (double)S)", "(float)(s / (double)D)"),
     ("p_static_scale_240", "orc_e4m3_encode(p[t] * 448.0f)", "orc_e4m3_encode(p[t] * 240.0f)"),
     ("v_scale_wrong_channel", "v_scale[d] / (448.0f * l)", "v_scale[0] / (448.0f * l)"),
     ("v_quant_scale_240", "float inv = 448.0f / amax;", "float inv = 240.0f / amax;"),
@@ -32,7 +32,8 @@ MUTANTS = [
     ("k_scale_indexed_by_tile", "float c = (dq * k_scale[n / blk_k])", "float c = (dq * k_scale[n / tile_k])"),
     ("k_scale_first_block_only", "float c = (dq * k_scale[n / blk_k])", "float c = (dq * k_scale[0])"),
     ("q_scale_wrong_block", "float dq = q_scale[i / blk_q];", "float dq = q_scale[i / blk_k];"),
-    ("exact_causal_off_by_one", "int nvis = is_causal ? i + 1 : S;", "int nvis = is_causal ? (i > 0 ? i : 1) : S;"),
+    ("exact_causal_off_by_one", "int nvis = is_causal ? (i + 1 < S ? i + 1 : S) : S;",
+     "int nvis = is_causal ? (i < S ? (i > 0 ? i : 1) : S) : S;"),
     ("fp16_pv_no_rounding", "pq[t] = round_f16(p[t]);", "pq[t] = p[t];"),
     ("fp8_p_not_quantised", "pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));", "pq[t] = p[t] * 448.0f;"),
     ("f16_decode_bias", "ldexp(1.0 + fr / 1024.0, ex - 15)", "ldexp(1.0 + fr / 1024.0, ex - 14)"),
@@ -92,3 +93,34 @@ def test_planted_python_mistake_is_caught(orc, monkeypatch, mid, fn):
     monkeypatch.setattr(orc, "kv_head", fn)
     with pytest.raises(AssertionError):
         oracle_pins.pin_gqa_equals_replicated_kv()
+
+
+# planted mistakes in the oracle's packed-batch bookkeeping, applied to the
+# function's own source text
+PY_SRC_MUTANTS = [
+    ("varlen_k_uses_q_offsets", "attn_varlen", "(q0, q1), (k0, k1) = sq[b], sk[b]", "(q0, q1), (k0, k1) = sq[b], sq[b]"),
+    ("varlen_v_uses_q_offsets", "attn_varlen", "v[None, k0:k1]", "v[None, q0:q1]"),
+    ("varlen_start_off_by_one", "seq_slices", "return list(zip(cu[:-1], cu[1:]))",
+     "return list(zip([c + (c > 0) for c in cu[:-1]], cu[1:]))"),
+]
+
+
+@pytest.mark.parametrize("mid,fname,old,new", PY_SRC_MUTANTS, ids=[m[0] for m in PY_SRC_MUTANTS])
+def test_planted_python_source_mistake_is_caught(orc, monkeypatch, mid, fname, old, new):
+    import inspect
+
+    import oracle_pins
+
+    src = inspect.getsource(getattr(orc, fname))
+    assert src.count(old) == 1, "mutation site vanished from the oracle code"
+    ns = dict(vars(orc))
+    exec(compile(src.replace(old, new), f"<mutant {mid}>", "exec"), ns)
+    monkeypatch.setattr(orc, fname, ns[fname])
+    caught = None
+    for pin in (oracle_pins.pin_varlen_matches_separate_sequences, oracle_pins.pin_no_keys_gives_zero):
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError) as e:
+            caught = (pin.__name__, type(e).__name__)
+            break
+    assert caught, f"mutant {mid} survived"
