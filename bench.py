@@ -94,23 +94,50 @@ def cpu_baseline(w, causal, pv, nheads):
     import oracle as O
     from quantized_attention_02_amd import synth
 
-    q, k, v = synth.make_qkv(w)
-    all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    pvm = O.PV_FP8 if pv == "fp8" else O.PV_FP16
+    if isinstance(w, synth.VarlenWorkload):
+        q, k, v = synth.make_qkv_varlen(w)
+        cq, ck = w.cu_seqlens()
+        # sequences in a seeded random order, so that the sample mixes lengths
+        order = np.random.default_rng(0).permutation(w.B)
+        all_heads = [(int(b), h) for b in order for h in range(w.H)]
 
-    def run(heads):
-        t0 = time.perf_counter()
-        O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal),
-               pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=heads)
-        return time.perf_counter() - t0
+        def head_ops(b, h):
+            one = synth.varlen("x", 1, 1, w.D, [w.seqlens_q[b]], [w.seqlens_k[b]])
+            return one.ops(causal)
+
+        def run(heads):
+            t0 = time.perf_counter()
+            O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=bool(causal), pv_mode=pvm, heads=heads)
+            return time.perf_counter() - t0
+        what = "sequence-heads"
+    else:
+        q, k, v = synth.make_qkv(w)
+        all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+        def head_ops(b, h):
+            return 4.0 * w.S * w.S * w.D / (2 if causal else 1)
+
+        def run(heads):
+            t0 = time.perf_counter()
+            O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal), pv_mode=pvm, heads=heads)
+            return time.perf_counter() - t0
+        what = "heads"
 
     if nheads <= 0:  # size the sample to about CPU_SAMPLE_S seconds from a one-head probe
         t1 = run(all_heads[-1:])
-        nheads = int(min(len(all_heads), max(1, round(CPU_SAMPLE_S / max(t1, 1e-3)))))
+        per_op = t1 / head_ops(*all_heads[-1])
+        nheads, acc = 0, 0.0
+        for hd in all_heads:
+            if nheads and acc + head_ops(*hd) * per_op > CPU_SAMPLE_S:
+                break
+            acc += head_ops(*hd) * per_op
+            nheads += 1
     heads = all_heads[:nheads]
     dt = run(heads)
-    ops = 4.0 * len(heads) * w.S * w.S * w.D / (2 if causal else 1)
+    ops = sum(head_ops(*hd) for hd in heads)
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{len(heads)} of {w.B * w.H} heads of {w.name}, all {w.S} query rows "
+            "sample": f"{len(heads)} of {len(all_heads)} {what} of {w.name}, all query rows "
                       f"(quantisation of Q/K/V + attention), {dt:.2f} s wall"}
 
 
@@ -133,27 +160,45 @@ def main():
     from quantized_attention_02_amd import synth
 
     name = args.workload or synth.HEADLINE
-    w = synth.WORKLOADS[name]
+    varlen = name in synth.VARLEN_WORKLOADS
+    w = synth.VARLEN_WORKLOADS[name] if varlen else synth.WORKLOADS[name]
     causal = w.causal[0] if args.causal is None else bool(args.causal)
     ops = w.ops(causal)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v = synth.make_qkv(w)
+    q, k, v = synth.make_qkv_varlen(w) if varlen else synth.make_qkv(w)
     tdt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
     qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
-    bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads)
     out = torch.empty_like(qd)
+    if varlen:
+        cq, ck = (torch.from_numpy(c).to(dev) for c in w.cu_seqlens())
+        mq, mk = max(w.seqlens_q), max(w.seqlens_k)
+        bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev)
+
+        def quant():
+            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs)
+
+        def attn():
+            qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)
+    else:
+        bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads)
+
+        def quant():
+            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs)
+
+        def attn():
+            qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
     def step(e=None):
         if e is not None:
             e[0].record()
-        qa.quantize(qd, kd, vd, w.layout, args.pv, bufs)
+        quant()
         if e is not None:
             e[1].record()
-        qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
+        attn()
         if e is not None:
             e[2].record()
 
@@ -190,8 +235,11 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+fp8" if args.pv == "fp8" else "i8+f16",
         "data": "synthetic",
-        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D, "input_dtype": w.dtype,
-                   "layout": w.layout, "causal": causal, "pv_mode": args.pv},
+        "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
+                    "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,
+                    "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv} if varlen else
+                   {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
+                    "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv}),
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv), 1), "unit": "TFLOP/s",

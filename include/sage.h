@@ -17,6 +17,9 @@
  *           section 性能调优实战 (PV precision choice; layout and causality must match
  *           the tensors), section 替换时的三个注意事项 (no attention_mask argument) and
  *           section 最容易踩的四个安装坑 (unsupported GPUs raise an error).
+ *   [REPO]  "SageAttention: Thư viện Attention lượng tử hóa" repository summary page,
+ *           feature list (variable-length sequences through sageattn_varlen,
+ *           native grouped-query attention).
  *
  * Pipeline: sage_smooth_quant_qk -> sage_quant_v (pv fp8 only) -> sage_attn_fwd.
  *
@@ -167,6 +170,61 @@ int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t
                           const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
                           int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
                           int32_t *qk, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Packed variable-length batches ([REPO] feature list: variable-length
+ * sequences through sageattn_varlen).
+ *
+ * q: [total_q][H][D], k and v: [total_k][H_kv][D], token-major (NHD without
+ * the batch axis), dtype as above.  Sequence b owns rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1 of k and v.  cu_seqlens_q, cu_seqlens_k: device int32
+ * arrays of B + 1 entries that start at 0, do not decrease and end at total_q /
+ * total_k.  max_seqlen_q, max_seqlen_k: host-side bounds of every sequence
+ * length, 1 .. SAGE_MAX_S (launch sizes follow them, so tight bounds are
+ * faster).  The tables live on the device and are not checked: entries that
+ * break these rules cannot make any access leave the buffers (each length is
+ * clamped to [0, total] and to max_seqlen) but give unspecified results.
+ *
+ * Each sequence is attended on its own, exactly as a fixed-length batch of one:
+ * its own K mean, INT8 blocks, V scales and causal mask (key n is kept for
+ * query i when n <= i, both counted from the sequence's first token; query and
+ * key lengths may differ).  A query row that sees no key (a sequence with no
+ * keys) is 0.
+ *
+ * Intermediate buffers (sizes from sage_varlen_buffer_sizes).  Per head, the
+ * rows of sequence b start at
+ *   rq(b) = 32 * (cu_seqlens_q[b] / 32 + b),  rk(b) = 128 * (cu_seqlens_k[b] / 128 + b)
+ * of RQ = 32 * (total_q / 32 + B + 1) and RK = 128 * (total_k / 128 + B + 1) rows:
+ *   q_i8    int8  [H][RQ][D]          q_scale float [H][RQ / 32]
+ *   k_i8    int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64]
+ *   k_mean  float [B][H_kv][D]        v_scale float [B][H_kv][D]
+ *   v_fp8   uint8 [H_kv][RK / 64][D][64]  (64-key tiles as in the fixed layout)
+ * A sequence's rows past its length, up to the next multiple of 32 (Q) or 128
+ * (K, V), hold zero codes; rows between sequences are neither written nor read.
+ * Other rules (alignment, errors, stream order, staging) as above.
+ * ------------------------------------------------------------------------ */
+int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, size_t *q_i8,
+                             size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8,
+                             size_t *v_scale);
+
+/* sage_smooth_quant_qk for a packed batch. */
+int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
+                                const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
+                                int max_seqlen_q, int max_seqlen_k, int D, int8_t *q_i8, float *q_scale,
+                                int8_t *k_i8, float *k_scale, float *k_mean, void *stream);
+
+/* sage_quant_v for a packed batch (v: [total_k][H_kv][D]). */
+int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
+                        int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, void *stream);
+
+/* sage_attn_fwd for a packed batch.  pv fp16: v = the original [total_k][H_kv][D]
+ * V, v_scale = NULL.  out: [total_q][H][D] in dtype. */
+int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+                         const void *v, const float *v_scale, void *out, int dtype, const int32_t *cu_seqlens_q,
+                         const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
+                         void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *sage_status_str(int status);

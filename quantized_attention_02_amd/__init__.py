@@ -30,7 +30,8 @@ BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
 EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_attn_fwd",
-            "sage_attn_fwd_dump_qk", "sage_status_str", "sage_check_arch"]
+            "sage_attn_fwd_dump_qk", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
+            "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch"]
 
 _lib = None
 
@@ -56,6 +57,12 @@ def lib() -> ctypes.CDLL:
         attn = [c_void_p] * 7 + [c_int] * 8 + [c_float, c_int]
         L.sage_attn_fwd.argtypes = attn + [c_void_p]
         L.sage_attn_fwd_dump_qk.argtypes = attn + [c_int, c_int, c_void_p, c_void_p]
+        L.sage_varlen_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 7
+        L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 8 + \
+            [c_void_p] * 5 + [c_void_p]
+        L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 3
+        L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 7 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
+            [c_int, c_float, c_int, c_void_p]
         L.sage_status_str.argtypes = [c_int]
         L.sage_status_str.restype = ctypes.c_char_p
         L.sage_check_arch.argtypes = [ctypes.c_char_p]
@@ -112,6 +119,33 @@ def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, 
                           sm_scale, pv_mode, b, h, qk, stream):
     return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D,
                                        layout, is_causal, sm_scale, pv_mode, b, h, qk, stream)
+
+
+def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D):
+    vals = [ctypes.c_size_t() for _ in range(7)]
+    _check(lib().sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, *[ctypes.byref(v) for v in vals]),
+           "sage_varlen_buffer_sizes")
+    names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
+    return {n: v.value for n, v in zip(names, vals)}
+
+
+def sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
+                                max_seqlen_k, D, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+    return lib().sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k,
+                                             max_seqlen_q, max_seqlen_k, D, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                             stream)
+
+
+def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale, stream):
+    return lib().sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale,
+                                     stream)
+
+
+def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode, stream):
+    return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, cu_seqlens_q,
+                                      cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
+                                      is_causal, sm_scale, pv_mode, stream)
 
 
 def sage_status_str(status):
@@ -243,3 +277,108 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mo
     bufs = quantize(q, k, v, tensor_layout, pv_mode)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
+
+
+# ----------------------------------------------------------------- packed variable-length batches
+def varlen_rows(total: int, B: int, pad: int) -> int:
+    """Rows per head of a packed batch's quantised buffer (include/sage.h)."""
+    return pad * (total // pad + B + 1)
+
+
+def varlen_row0(start: int, b: int, pad: int) -> int:
+    """First buffer row of sequence b, whose first token is `start`."""
+    return pad * (start // pad + b)
+
+
+class QuantizedVarlen:
+    """Device buffers of the packed-batch quantisation entry points."""
+
+    def __init__(self, B, H, H_kv, total_q, total_k, D, device):
+        import torch
+
+        self.B, self.H, self.H_kv, self.total_q, self.total_k, self.D = B, H, H_kv, total_q, total_k, D
+        rq, rk = varlen_rows(total_q, B, BLK_Q), varlen_rows(total_k, B, KV_PAD)
+        self.rows_q, self.rows_k = rq, rk
+        self.q_i8 = torch.empty((H, rq, D), dtype=torch.int8, device=device)
+        self.q_scale = torch.empty((H, rq // BLK_Q), dtype=torch.float32, device=device)
+        self.k_i8 = torch.empty((H_kv, rk, D), dtype=torch.int8, device=device)
+        self.k_scale = torch.empty((H_kv, rk // BLK_K), dtype=torch.float32, device=device)
+        self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.v_fp8 = torch.empty((H_kv, rk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
+        self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+
+
+def _cu(t, name):
+    import torch
+
+    if not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    return t
+
+
+def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
+                    bufs: QuantizedVarlen | None = None) -> QuantizedVarlen:
+    """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode) on a packed
+    batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_q, H, D] and k, v [total_k, H_kv, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    if cq.numel() != ck.numel() or cq.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 >= 2 entries")
+    B = cq.numel() - 1
+    (total_q, H, D), (total_k, H_kv, _) = q.shape, k.shape
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"the number of query heads ({H}) must be a multiple of the K/V heads ({H_kv})")
+    dt = _dtype_code(q)
+    bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device)
+    if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D) != (B, H, H_kv, total_q, total_k, D):
+        raise ValueError("bufs were allocated for another shape")
+    bufs.max_seqlen_q, bufs.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    st = _stream()
+    _check(sage_smooth_quant_qk_varlen(q.data_ptr(), k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
+                                       total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D,
+                                       bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
+                                       bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
+           "sage_smooth_quant_qk_varlen")
+    if pv_mode == "fp8":
+        _check(sage_quant_v_varlen(v.data_ptr(), dt, ck.data_ptr(), B, H_kv, total_k, bufs.max_seqlen_k, D,
+                                   bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), st), "sage_quant_v_varlen")
+    return bufs
+
+
+def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, is_causal=False, sm_scale=None,
+                    pv_mode="fp8"):
+    """sage_attn_fwd_varlen into out [total_q, H, D]."""
+    B, H, H_kv, D = bufs.B, bufs.H, bufs.H_kv, bufs.D
+    if tuple(out.shape) != (bufs.total_q, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [total_q, H, D] tensor")
+    if pv_mode == "fp16" and (tuple(v.shape) != (bufs.total_k, H_kv, D) or not v.is_contiguous()):
+        raise ValueError("pv fp16 reads the original V: it must be a contiguous [total_k, H_kv, D] tensor")
+    cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    pv = PV[pv_mode]
+    sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
+    vs = bufs.v_scale.data_ptr() if pv == 0 else None
+    _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
+                                bufs.k_scale.data_ptr(), vptr, vs, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
+                                ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k, bufs.max_seqlen_q,
+                                bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, _stream()),
+           "sage_attn_fwd_varlen")
+    return out
+
+
+def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False, sm_scale=None,
+                    pv_mode="fp8"):
+    """Quantized attention over a packed batch of sequences ("SageAttention: Thư viện
+    Attention lượng tử hóa" page, feature list: sageattn_varlen):
+    q [total_q, H, D], k / v [total_k, H_kv, D]; returns [total_q, H, D]."""
+    import torch
+
+    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode)
+    out = torch.empty_like(q)
+    return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)

@@ -24,6 +24,8 @@ bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
 int roundup(int x, int m) { return (x + m - 1) / m * m; }
 
+constexpr int kMaxTotal = 1 << 30;  // tokens of a packed batch
+
 int check_shape(int B, int H, int S, int D) {
   if (B < 1 || H < 1 || S < 1 || S > SAGE_MAX_S) return SAGE_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return SAGE_ERR_INVALID_ARG;
@@ -165,6 +167,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantQKArgs a;
+  memset(&a, 0, sizeof a);
   a.q = q;
   a.k = k;
   a.q_i8 = q_i8;
@@ -195,6 +198,7 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
   if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantVArgs a;
+  memset(&a, 0, sizeof a);
   a.v = v;
   a.v_fp8 = v_fp8;
   a.v_scale = v_scale;
@@ -221,6 +225,148 @@ int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t
                           int32_t *qk, void *stream) {
   return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
                      sm_scale, pv_mode, b, h, qk, true, stream);
+}
+
+// ---- packed variable-length batches
+static int check_varlen(int B, int H, int H_kv, int total_q, int total_k, int max_q, int max_k, int D) {
+  if (B < 1 || total_q < 0 || total_k < 0 || total_q > kMaxTotal || total_k > kMaxTotal) return SAGE_ERR_INVALID_ARG;
+  int rc = check_shape(B, H, max_q, D);  // max_q in 1 .. SAGE_MAX_S, launch sizes
+  if (rc) return rc;
+  if ((rc = check_shape(B, H, max_k, D))) return rc;
+  return check_kv_heads(H, H_kv);
+}
+
+int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, size_t *q_i8,
+                             size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8,
+                             size_t *v_scale) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, 1, 1, D);
+  if (rc) return rc;
+  const size_t rq = (size_t)varlen_rows(total_q, B, kBlkQ), rk = (size_t)varlen_rows(total_k, B, kKvPad);
+  if (q_i8) *q_i8 = (size_t)H * rq * D;
+  if (q_scale) *q_scale = (size_t)H * (rq / kBlkQ) * sizeof(float);
+  if (k_i8) *k_i8 = (size_t)H_kv * rk * D;
+  if (k_scale) *k_scale = (size_t)H_kv * (rk / kBlkK) * sizeof(float);
+  if (k_mean) *k_mean = (size_t)B * H_kv * D * sizeof(float);
+  if (v_fp8) *v_fp8 = (size_t)H_kv * rk * D;
+  if (v_scale) *v_scale = (size_t)B * H_kv * D * sizeof(float);
+  return SAGE_OK;
+}
+
+int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
+                                const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
+                                int max_seqlen_q, int max_seqlen_k, int D, int8_t *q_i8, float *q_scale,
+                                int8_t *k_i8, float *k_scale, float *k_mean, void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
+  if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean)
+    return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(cu_seqlens_q, 4) ||
+      !aligned(cu_seqlens_k, 4))
+    return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantQKArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.q_i8 = q_i8;
+  a.k_i8 = k_i8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.k_mean = k_mean;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.S = max_seqlen_k;
+  a.D = D;
+  a.layout = SAGE_LAYOUT_NHD;
+  a.dtype = dtype;
+  a.nq = roundup(max_seqlen_q, kBlkQ) / kBlkQ;
+  a.nk = roundup(max_seqlen_k, kKvPad) / kBlkK;
+  a.varlen = 1;
+  a.sq = SeqTable{cu_seqlens_q, total_q, max_seqlen_q};
+  a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
+  a.rows_q = varlen_rows(total_q, B, kBlkQ);
+  a.rows_k = varlen_rows(total_k, B, kKvPad);
+  return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
+}
+
+int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
+                        int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, void *stream) {
+  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
+  if (!v || !cu_seqlens_k || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4) || !aligned(cu_seqlens_k, 4))
+    return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantVArgs a;
+  memset(&a, 0, sizeof a);
+  a.v = v;
+  a.v_fp8 = v_fp8;
+  a.v_scale = v_scale;
+  a.B = B;
+  a.H = H_kv;
+  a.S = max_seqlen_k;
+  a.D = D;
+  a.layout = SAGE_LAYOUT_NHD;
+  a.dtype = dtype;
+  a.nk = roundup(max_seqlen_k, kKvPad) / kBlkK;
+  a.varlen = 1;
+  a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
+  a.rows_k = varlen_rows(total_k, B, kKvPad);
+  return launch_status(launch_quant_v(a, (hipStream_t)stream));
+}
+
+int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+                         const void *v, const float *v_scale, void *out, int dtype, const int32_t *cu_seqlens_q,
+                         const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
+                         void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+    return SAGE_ERR_INVALID_ARG;
+  if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
+  // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
+  if (pv_mode == SAGE_PV_FP16 && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q_i8 = q_i8;
+  a.k_i8 = k_i8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v = v;
+  a.v_scale = v_scale;
+  a.out = out;
+  a.dump = nullptr;
+  a.dump_bh = -1;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.S = max_seqlen_q;  // query blocks per (sequence, head) in the grid
+  a.D = D;
+  a.layout = SAGE_LAYOUT_NHD;
+  a.dtype = dtype;
+  a.causal = is_causal;
+  a.pv = pv_mode;
+  a.sm2 = sm_scale * 1.4426950408889634f;
+  a.varlen = 1;
+  a.sq = SeqTable{cu_seqlens_q, total_q, max_seqlen_q};
+  a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
+  a.rows_q = varlen_rows(total_q, B, kBlkQ);
+  a.rows_k = varlen_rows(total_k, B, kKvPad);
+  return launch_status(launch_attn(a, false, (hipStream_t)stream));
 }
 
 const char *sage_status_str(int status) {

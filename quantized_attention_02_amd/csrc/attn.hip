@@ -274,7 +274,22 @@ k_attn(const AttnArgs a) {
   const int wg = blockIdx.x;
   const int nbh = a.B * a.H;
   int bh, mrank;
-  if ((nbh & 7) == 0) {
+  if (a.varlen && (a.H & 7) == 0) {
+    // packed batches: sequences differ in length, so every XCD takes the same
+    // share of every sequence: XCD x owns heads [x H/8, (x+1) H/8) of each one
+    // (consecutive heads, so a grouped-query K/V head stays in one L2)
+    const int hx = a.H >> 3, xcd = wg & 7, idx = wg >> 3;
+    const int pairs = a.B * hx;  // (sequence, head) pairs of this XCD
+    int pair;
+    if (CAUSAL) {  // longest blocks first
+      pair = idx % pairs;
+      mrank = idx / pairs;
+    } else {
+      pair = idx / a.nmblk;
+      mrank = idx % a.nmblk;
+    }
+    bh = (pair / hx) * a.H + xcd * hx + pair % hx;
+  } else if (!a.varlen && (nbh & 7) == 0) {
     const int heads_per_xcd = nbh >> 3;
     const int xcd = wg & 7, idx = wg >> 3;
     if (CAUSAL) {  // longest blocks first; the XCD's heads interleaved
@@ -295,9 +310,22 @@ k_attn(const AttnArgs a) {
   const int b = bh / a.H, h = bh % a.H;
   // grouped-query attention: H / H_kv consecutive query heads read one K/V head
   const int hk = h / (a.H / a.H_kv), bhk = b * a.H_kv + hk;
+
+  // ---- this head's queries and keys: a fixed-length batch entry, or one
+  //      sequence of a packed batch (its own lengths and buffer rows)
+  Seg qs, ks;  // rows of q_i8 / k_i8 and v_fp8; qs also places the output, ks the caller's V
+  if (a.varlen) {
+    qs = varlen_seg(a.sq, b, h, a.H, D, a.rows_q, kBlkQ);
+    ks = varlen_seg(a.sk, b, hk, a.H_kv, D, a.rows_k, kKvPad);
+  } else {
+    qs = fixed_seg(a.layout, b, h, a.H, a.S, a.S_q, D);
+    ks = fixed_seg(a.layout, b, hk, a.H_kv, a.S, a.S_k, D);
+  }
+  const int Sq = qs.S, Sk = ks.S;
   const int q0 = mblk * kBlockM;
+  if (q0 >= Sq) return;           // past a short sequence of a packed batch (whole work-group)
   const int qw = q0 + 32 * wave;  // first query row of this wavefront
-  const bool active = qw < a.S;
+  const bool active = qw < Sq;
   const int qi = qw + qn;         // this lane's query row
 
   // ---- Q fragments: B operand of S^T = K.Q^T; lane (q, half) holds
@@ -305,17 +333,17 @@ k_attn(const AttnArgs a) {
   v4i qf[NC];
   float dq = 0.0f;
   if (active) {
-    const int8_t *qrow = a.q_i8 + ((long long)bh * a.S_q + qi) * D;
+    const int8_t *qrow = a.q_i8 + (qs.row0 + qi) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
-    dq = a.q_scale[(long long)bh * a.nq + (qw >> 5)];
+    dq = a.q_scale[(qs.row0 + qw) >> 5];
   } else {
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
   }
 
-  int ntiles = a.S_k / TN;
-  if (CAUSAL) ntiles = min(ntiles, min(q0 + kBlockM - 1, a.S - 1) / TN + 1);
+  int ntiles = (Sk + TN - 1) / TN;
+  if (CAUSAL) ntiles = min(ntiles, min(q0 + kBlockM - 1, Sk - 1) / TN + 1);
 
   float m = -INFINITY;  // running max (log2 domain, scaled scores)
   float l = 0.0f;       // running sum over this half-wave's keys
@@ -325,14 +353,15 @@ k_attn(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[c][r] = 0.0f;
 
-  const int8_t *kbase = a.k_i8 + (long long)bhk * a.S_k * D;
-  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + (long long)bhk * a.S_k * D;
-  const float *kscale = a.k_scale + (long long)bhk * a.nk;
-  const HeadView hv = head_view(a.layout, b, hk, a.H_kv, a.S, D);  // pv fp16: the caller's V
+  const int8_t *kbase = a.k_i8 + ks.row0 * D;
+  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + ks.row0 * D;
+  const float *kscale = a.k_scale + (ks.row0 >> 6);
+  const HeadView hv{ks.base, ks.stride};  // pv fp16: the caller's V
   const TileCopy<D, TN, WAVES> copy(wave, lane);
   const VCopy16<D, TN, WAVES> vcopy(lane);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, a.S_k * D);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase, a.S_k * D);
+  const int kbytes = ntiles * TN * D;  // this head's K (and V) rows that the tiles read
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kbytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase, kbytes);
 
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
   auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
@@ -340,7 +369,7 @@ k_attn(const AttnArgs a) {
     const bool work = active && !(CAUSAL && key0 > qw + 31);
     // pv fp16: this tile's V rows go into the single V buffer, which the
     // barrier that ended the previous tile has released
-    if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, key0, a.S, vb, wave);
+    if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, key0, Sk, vb, wave);
     // the tile's K-block scales, read through a wave-uniform address (scalar loads)
     float ks[NB];
     if (NB == 2) {
@@ -386,8 +415,8 @@ k_attn(const AttnArgs a) {
       // ---- mask: only tiles that reach past S or cross the causal diagonal
       // key (key0 + 4hh + kofs(t, r)) is excluded iff kofs(t, r) > lim, where
       // kofs is a compile-time constant of the register slot
-      const bool need_mask = (key0 + TN > a.S) || (CAUSAL && key0 + TN - 1 > qw);
-      const int lim = (CAUSAL ? min(a.S - 1, qi) : a.S - 1) - key0 - 4 * hh;
+      const bool need_mask = (key0 + TN > Sk) || (CAUSAL && key0 + TN - 1 > qw);
+      const int lim = (CAUSAL ? min(Sk - 1, qi) : Sk - 1) - key0 - 4 * hh;
       // ---- per INT8 block: row max of the int32 sums (c2 > 0 per block) and
       //      the sums converted to float
       int mxb[NB];
@@ -549,11 +578,9 @@ k_attn(const AttnArgs a) {
   if (!active) return;
   // ---- epilogue: combine the two half-wave sums, normalise, store
   const float lt = halves_sum(l);
-  if (qi >= a.S) return;
-  const float rl = 1.0f / lt;
-  long long off;
-  if (a.layout == 0) off = (((long long)b * a.H + h) * a.S + qi) * D;
-  else off = (((long long)b * a.S + qi) * a.H + h) * D;
+  if (qi >= Sq) return;
+  const float rl = lt > 0.0f ? 1.0f / lt : 0.0f;  // a row without keys (empty sequence) is 0
+  const long long off = qs.base + (long long)qi * qs.stride;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll

@@ -77,12 +77,32 @@ constexpr int kMaxChunks = 32;
 // chunks (256 up to S = 8192).
 __host__ __device__ inline int chunk_tokens(int S) {
   const int per = (S + kMaxChunks - 1) / kMaxChunks;
-  return ((per + 255) / 256) * 256;
+  return max(256, ((per + 255) / 256) * 256);
 }
 __host__ __device__ inline int n_chunks(int S) {
   const int c = chunk_tokens(S);
   return (S + c - 1) / c;
 }
+// Chunk work-groups launched per head when heads have at most max_len tokens:
+// n_chunks(S) <= chunk_grid(max_len) for every S <= max_len.
+__host__ __device__ inline int chunk_grid(int max_len) { return min(kMaxChunks, (max_len + 255) / 256); }
+
+// The head (or sequence-head) of each pass: fixed-length batches or packed ones.
+template <int D>
+__device__ inline Seg q_seg(const QuantQKArgs &a, int b, int h) {
+  return a.varlen ? varlen_seg(a.sq, b, h, a.H, D, a.rows_q, kBlkQ) : fixed_seg(a.layout, b, h, a.H, a.S, a.S_q, D);
+}
+template <int D>
+__device__ inline Seg k_seg(const QuantQKArgs &a, int b, int h) {
+  return a.varlen ? varlen_seg(a.sk, b, h, a.H_kv, D, a.rows_k, kKvPad)
+                  : fixed_seg(a.layout, b, h, a.H_kv, a.S, a.S_k, D);
+}
+template <int D>
+__device__ inline Seg v_seg(const QuantVArgs &a, int b, int h) {
+  return a.varlen ? varlen_seg(a.sk, b, h, a.H, D, a.rows_k, kKvPad)
+                  : fixed_seg(a.layout, b, h, a.H, a.S, a.nk * kBlkK, D);
+}
+__device__ inline int ceil_div(int x, int m) { return (x + m - 1) / m; }
 
 // Thread layout of the chunk passes: G = D / 8 channel groups (16 bytes of a
 // 16-bit row) x R = 256 / G rows; the chunk's rows are loaded kUnroll at a
@@ -97,7 +117,8 @@ struct ChunkMap {
 // K channel sums (binary64) of one chunk -> partials[chunk][D]; or, with
 // ABSMAX, V channel abs-max (fp32) of one chunk.
 template <int DT, int D, bool ABSMAX>
-__device__ inline void chunk_reduce(const uint16_t *x, const HeadView &hv, int S, int chunk, void *partials) {
+__device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk, void *partials) {
+  const int S = hv.S;
   using M = ChunkMap<D>;
   typedef typename std::conditional<ABSMAX, float, double>::type acc_t;
   __shared__ acc_t part[M::R][D];
@@ -113,7 +134,7 @@ __device__ inline void chunk_reduce(const uint16_t *x, const HeadView &hv, int S
     for (int u = 0; u < M::kUnroll; ++u) {
       const int s = s0 + u * M::R;
       if (s < s_end) {
-        load8<DT>(x + hv.base + (long long)s * hv.tok_stride + 8 * g, v[u]);
+        load8<DT>(x + hv.base + (long long)s * hv.stride + 8 * g, v[u]);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
@@ -145,10 +166,11 @@ __device__ inline void chunk_reduce(const uint16_t *x, const HeadView &hv, int S
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
-  const int nch = n_chunks(a.S);
+  const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
   const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;  // bh: K head (b, h_kv)
-  const HeadView hv = head_view(a.layout, bh / a.H_kv, bh % a.H_kv, a.H_kv, a.S, D);
-  chunk_reduce<DT, D, false>((const uint16_t *)a.k, hv, a.S, chunk, a.k_i8 + (long long)bh * a.S_k * D);
+  const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
+  if (chunk >= n_chunks(sg.S)) return;
+  chunk_reduce<DT, D, false>((const uint16_t *)a.k, sg, chunk, a.k_i8 + sg.row0 * D);
 }
 
 // ---------------------------------------------------------------------------
@@ -159,7 +181,8 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
   __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / a.nq, blk = blockIdx.x % a.nq;
-  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  const Seg hv = q_seg<D>(a, bh / a.H, bh % a.H);
+  if (blk >= ceil_div(hv.S, kBlkQ)) return;  // past this sequence's blocks (packed batches)
   const uint16_t *q = (const uint16_t *)a.q;
   constexpr int vec_per_row = D / 8;
   constexpr int nvec = kBlkQ * vec_per_row;  // <= 512: at most 2 per thread
@@ -170,8 +193,8 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
     const int vi = tid + u * kThreads;
     const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
     const int s = blk * kBlkQ + row;
-    if (vi < nvec && s < a.S) {
-      load8<DT>(q + hv.base + (long long)s * hv.tok_stride + c8, x[u]);
+    if (vi < nvec && s < hv.S) {
+      load8<DT>(q + hv.base + (long long)s * hv.stride + c8, x[u]);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
@@ -181,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
   }
   amax = block_max(amax, red);
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (tid == 0) a.q_scale[(long long)bh * a.nq + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+  if (tid == 0) a.q_scale[(hv.row0 >> 5) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int vi = tid + u * kThreads;
@@ -191,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
-    *reinterpret_cast<v2i *>(a.q_i8 + ((long long)bh * a.S_q + blk * kBlkQ + row) * D + c8) = out;
+    *reinterpret_cast<v2i *>(a.q_i8 + (hv.row0 + blk * kBlkQ + row) * D + c8) = out;
   }
 }
 
@@ -201,15 +224,16 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (i >= (long long)a.B * a.H_kv * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
-  const double *part = reinterpret_cast<const double *>(a.k_i8 + (long long)bh * a.S_k * D);
-  const int nch = n_chunks(a.S);
+  const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
+  const double *part = reinterpret_cast<const double *>(a.k_i8 + sg.row0 * D);
+  const int nch = n_chunks(sg.S);
   double v[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0;  // all loads in flight
   double t = 0.0;
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) t += v[c];
-  a.k_mean[i] = (float)(t / (double)a.S);
+  a.k_mean[i] = sg.S > 0 ? (float)(t / (double)sg.S) : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -221,7 +245,8 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
   __shared__ float mean[D];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / a.nk, blk = blockIdx.x % a.nk;  // bh: K head (b, h_kv)
-  const HeadView hv = head_view(a.layout, bh / a.H_kv, bh % a.H_kv, a.H_kv, a.S, D);
+  const Seg hv = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
+  if (blk >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's rows
   const uint16_t *k = (const uint16_t *)a.k;
   if (tid < D) mean[tid] = a.k_mean[(long long)bh * D + tid];
   __syncthreads();
@@ -234,8 +259,8 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
     const int vi = tid + u * kThreads;
     const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
     const int s = blk * kBlkK + row;
-    if (vi < nvec && s < a.S) {
-      load8<DT>(k + hv.base + (long long)s * hv.tok_stride + c8, x[u]);
+    if (vi < nvec && s < hv.S) {
+      load8<DT>(k + hv.base + (long long)s * hv.stride + c8, x[u]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[u][i] = x[u][i] - mean[c8 + i];
     } else {
@@ -247,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
   }
   amax = block_max(amax, red);
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (tid == 0) a.k_scale[(long long)bh * a.nk + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+  if (tid == 0) a.k_scale[(hv.row0 >> 6) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int vi = tid + u * kThreads;
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
-    *reinterpret_cast<v2i *>(a.k_i8 + ((long long)bh * a.S_k + blk * kBlkK + row) * D + c8) = out;
+    *reinterpret_cast<v2i *>(a.k_i8 + (hv.row0 + blk * kBlkK + row) * D + c8) = out;
   }
 }
 
@@ -270,10 +295,11 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_vamax_part(const QuantVArgs a) {
-  const int nch = n_chunks(a.S);
+  const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
   const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
-  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
-  chunk_reduce<DT, D, true>((const uint16_t *)a.v, hv, a.S, chunk, a.v_fp8 + (long long)bh * a.nk * kBlkK * D);
+  const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
+  if (chunk >= n_chunks(sg.S)) return;
+  chunk_reduce<DT, D, true>((const uint16_t *)a.v, sg, chunk, a.v_fp8 + sg.row0 * D);
 }
 
 template <int D>
@@ -281,8 +307,9 @@ __global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) {
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (i >= (long long)a.B * a.H * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
-  const float *part = reinterpret_cast<const float *>(a.v_fp8 + (long long)bh * a.nk * kBlkK * D);
-  const int nch = n_chunks(a.S);
+  const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
+  const float *part = reinterpret_cast<const float *>(a.v_fp8 + sg.row0 * D);
+  const int nch = n_chunks(sg.S);
   float v[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0f;
@@ -301,7 +328,8 @@ template <int DT, int D>
 __global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
   const int tid = threadIdx.x, q = tid & 15, g = tid >> 4;
   const int bh = blockIdx.x / a.nk, t = blockIdx.x % a.nk;
-  const HeadView hv = head_view(a.layout, bh / a.H, bh % a.H, a.H, a.S, D);
+  const Seg hv = v_seg<D>(a, bh / a.H, bh % a.H);
+  if (t >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's tiles
   const uint16_t *v = (const uint16_t *)a.v;
   float inv[8];
 #pragma unroll
@@ -313,14 +341,14 @@ __global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int s = t * kBlkK + 4 * q + k;
-    if (s < a.S) {
-      load8<DT>(v + hv.base + (long long)s * hv.tok_stride + 8 * g, x[k]);
+    if (s < hv.S) {
+      load8<DT>(v + hv.base + (long long)s * hv.stride + 8 * g, x[k]);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[k][i] = 0.0f;
     }
   }
-  uint8_t *dst = a.v_fp8 + (((long long)bh * a.nk + t) * D + 8 * g) * kBlkK + key_vpos(4 * q);
+  uint8_t *dst = a.v_fp8 + (((hv.row0 >> 6) + t) * D + 8 * g) * kBlkK + key_vpos(4 * q);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float y[4];
@@ -344,7 +372,8 @@ template <int DT, int D>
 static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
   const int bh = a.B * a.H, bhk = a.B * a.H_kv;
   const int gd = (bhk * D + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * n_chunks(a.S)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads), 0,
+                     stream, a);
   hipLaunchKernelGGL((k_qquant<DT, D>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kquant<DT, D>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
@@ -354,7 +383,8 @@ template <int DT, int D>
 static void launch_v(const QuantVArgs &a, hipStream_t stream) {
   const int bh = a.B * a.H;
   const int gd = (bh * D + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((k_vamax_part<DT, D>), dim3(bh * n_chunks(a.S)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_vamax_part<DT, D>), dim3(bh * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads),
+                     0, stream, a);
   hipLaunchKernelGGL((k_vamax<D>), dim3(gd), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_vconvert<DT, D>), dim3(bh * a.nk), dim3(2 * D), 0, stream, a);
   hipLaunchKernelGGL((k_vscale<D>), dim3(gd), dim3(kThreads), 0, stream, a);

@@ -72,12 +72,63 @@ __host__ __device__ constexpr int key_vpos(int n) {
   return 32 * ((n >> 2) & 1) + 16 * (n >> 5) + 4 * ((n & 31) >> 3) + (n & 3);
 }
 
+// ---- packed variable-length batches
+// Sequence b owns tokens cu[b] .. cu[b+1] of a token-major [T][H][D] tensor.
+// In the quantised buffers each (sequence, head) gets its own run of rows:
+// a head's buffer has varlen_rows(T, B, pad) rows and sequence b starts at row
+// seq_row0(cu[b], b, pad), a multiple of pad (32 for Q, 128 for K and V), so
+// runs hold roundup(length, pad) rows without overlapping.
+struct SeqTable {
+  const int *cu;  // device, B + 1 entries
+  int total;      // tokens in the packed tensor
+  int max_len;    // upper bound of every length (host-side)
+};
+
+// Sequence b's first token and length, clamped to [0, total] and max_len so
+// that every access stays inside the buffers whatever the table holds.
+__device__ inline void seq_span(const SeqTable &t, int b, int &start, int &len) {
+  int c0 = t.cu[b], c1 = t.cu[b + 1];
+  c0 = min(max(c0, 0), t.total);
+  c1 = min(max(c1, c0), t.total);
+  start = c0;
+  len = min(c1 - c0, t.max_len);
+}
+__host__ __device__ inline long long seq_row0(int start, int b, int pad) {
+  return (long long)pad * (start / pad + b);
+}
+__host__ __device__ inline long long varlen_rows(int total, int B, int pad) {
+  return (long long)pad * (total / pad + B + 1);
+}
+
+// One (sequence or batch entry, head) of an input tensor and its rows in a
+// quantised buffer: element (s, d), s < S, is at base + s * stride + d of the
+// input; its buffer row is row0 + s.
+struct Seg {
+  int S;
+  long long base, stride, row0;
+};
+
+// fixed-length: head (b, h) of [B][H][S][D] / [B][S][H][D], buffers [B][H][S_pad][D]
+__host__ __device__ inline Seg fixed_seg(int layout, int b, int h, int H, int S, int S_pad, int D) {
+  const HeadView v = head_view(layout, b, h, H, S, D);
+  return Seg{S, v.base, v.tok_stride, ((long long)b * H + h) * S_pad};
+}
+// packed: head h of sequence b in [T][H][D], buffers [H][rows][D]
+__device__ inline Seg varlen_seg(const SeqTable &t, int b, int h, int H, int D, long long rows, int pad) {
+  int start, len;
+  seq_span(t, b, start, len);
+  return Seg{len, ((long long)start * H + h) * D, (long long)H * D, h * rows + seq_row0(start, b, pad)};
+}
+
 struct QuantQKArgs {
   const void *q, *k;
   int8_t *q_i8, *k_i8;
   float *q_scale, *k_scale, *k_mean;
   int B, H, H_kv, S, D, layout, dtype;  // K has H_kv heads
-  int S_q, S_k, nq, nk;
+  int S_q, S_k, nq, nk;                 // nq / nk: Q / K scale blocks per head (grid extent)
+  int varlen;                           // packed batch: tables below, S unused
+  SeqTable sq, sk;
+  long long rows_q, rows_k;  // buffer rows per head (packed batch)
 };
 
 struct QuantVArgs {
@@ -85,7 +136,10 @@ struct QuantVArgs {
   uint8_t *v_fp8;
   float *v_scale;
   int B, H, S, D, layout, dtype;
-  int nk;
+  int nk;  // 64-key tiles per head (grid extent)
+  int varlen;
+  SeqTable sk;
+  long long rows_k;
 };
 
 struct AttnArgs {
@@ -99,6 +153,9 @@ struct AttnArgs {
   int B, H, H_kv, S, D, layout, dtype, causal, pv;  // K and V have H_kv heads
   int S_q, S_k, nq, nk, nmblk;
   float sm2;  // sm_scale * log2(e)
+  int varlen;  // packed batch: tables below, S = the longest query sequence
+  SeqTable sq, sk;
+  long long rows_q, rows_k;
 };
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);

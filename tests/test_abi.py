@@ -154,3 +154,63 @@ def test_python_wrapper_maps_unsupported_to_value_error(monkeypatch):
         qa._check(qa.SAGE_ERR_UNSUPPORTED, "x")
     with pytest.raises(qa.SageError):
         qa._check(qa.SAGE_ERR_INVALID_ARG, "x")
+
+
+# ---- packed variable-length batches
+def test_varlen_buffer_sizes():
+    s = qa.sage_varlen_buffer_sizes(3, 4, 2, 100, 200, 64)
+    rq, rk = 32 * (100 // 32 + 3 + 1), 128 * (200 // 128 + 3 + 1)
+    assert (rq, rk) == (qa.varlen_rows(100, 3, 32), qa.varlen_rows(200, 3, 128)) == (224, 640)
+    assert s == {"q_i8": 4 * rq * 64, "q_scale": 4 * (rq // 32) * 4, "k_i8": 2 * rk * 64, "k_scale": 2 * (rk // 64) * 4,
+                 "k_mean": 3 * 2 * 64 * 4, "v_fp8": 2 * rk * 64, "v_scale": 3 * 2 * 64 * 4}
+    # every sequence's padded run fits in the buffer wherever the sequence starts
+    for total, B, pad in ((100, 3, 32), (200, 3, 128), (0, 1, 32), (4095, 7, 128)):
+        rows = qa.varlen_rows(total, B, pad)
+        for b in range(B):
+            for start in range(total + 1):
+                for n in (0, 1, pad - 1, pad, total - start):
+                    if 0 <= n <= total - start:
+                        r0 = qa.varlen_row0(start, b, pad)
+                        assert r0 % pad == 0 and r0 + -(-n // pad) * pad <= rows
+    L = qa.lib()
+    for bad in [(0, 1, 1, 1, 1, 64), (1, 4, 3, 1, 1, 64), (1, 1, 1, -1, 1, 64), (1, 1, 1, 1, -5, 64),
+                (1, 1, 1, 1, 1, 96), (1, 1, 1, (1 << 30) + 1, 1, 64)]:
+        assert L.sage_varlen_buffer_sizes(*bad, *([None] * 7)) == qa.SAGE_ERR_INVALID_ARG, bad
+
+
+GOOD_QK_VL = dict(q=P, k=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4, H_kv=2, total_q=100, total_k=200, max_q=50,
+                  max_k=90, D=64, q_i8=P, q_scale=P, k_i8=P, k_scale=P, k_mean=P, stream=None)
+GOOD_V_VL = dict(v=P, dtype=1, cu_k=P, B=3, H_kv=2, total_k=200, max_k=90, D=128, v_fp8=P, v_scale=P, stream=None)
+GOOD_ATTN_VL = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, out=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4,
+                    H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90, D=64, is_causal=1, sm_scale=0.125,
+                    pv_mode=0, stream=None)
+BAD_QK_VL = [dict(cu_q=None), dict(cu_k=P + 2), dict(B=0), dict(H_kv=3), dict(total_q=-1), dict(max_q=0),
+             dict(max_k=(1 << 20) + 1), dict(D=32), dict(dtype=3), dict(q=None), dict(k_i8=P + 1)]
+BAD_V_VL = [dict(cu_k=None), dict(v=P + 8), dict(max_k=0), dict(total_k=-3), dict(H_kv=0), dict(v_scale=None)]
+BAD_ATTN_VL = [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P + 1), dict(is_causal=3), dict(pv_mode=5),
+               dict(sm_scale=0.0), dict(v_scale=None), dict(out=P + 4), dict(H_kv=3), dict(max_q=0), dict(B=-1),
+               # pv fp16 reads 128-token slices of V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
+               dict(pv_mode=1, v_scale=None, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
+
+
+@pytest.mark.parametrize("bad", BAD_QK_VL, ids=[str(b) for b in BAD_QK_VL])
+def test_smooth_quant_qk_varlen_rejects(bad):
+    assert qa.sage_smooth_quant_qk_varlen(*{**GOOD_QK_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_V_VL, ids=[str(b) for b in BAD_V_VL])
+def test_quant_v_varlen_rejects(bad):
+    assert qa.sage_quant_v_varlen(*{**GOOD_V_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_ATTN_VL, ids=[str(b) for b in BAD_ATTN_VL])
+def test_attn_fwd_varlen_rejects(bad):
+    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
+def test_valid_varlen_arguments_without_a_device_report_no_device():
+    assert qa.sage_smooth_quant_qk_varlen(*GOOD_QK_VL.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_quant_v_varlen(*GOOD_V_VL.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen(*GOOD_ATTN_VL.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "pv_mode": 1, "v_scale": None}.values()) == qa.SAGE_ERR_NO_DEVICE
