@@ -54,7 +54,8 @@ def lib():
     """Load liboracle.so, building it first if it is missing."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_SO):
+        hdr = os.path.join(_HERE, "sage_oracle.h")
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < max(os.path.getmtime(_SRC), os.path.getmtime(hdr)):
             build()
         L = ctypes.CDLL(_SO)
         L.orc_e4m3_decode.restype = ctypes.c_float
@@ -62,9 +63,11 @@ def lib():
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_e4m3_encode.argtypes = [ctypes.c_float]
         for name in ("orc_decode16", "orc_encode16", "orc_e4m3_encode_n", "orc_int8_quant_block",
-                     "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_v_head",
-                     "orc_qk_int32_head", "orc_attn_head_rows", "orc_attn_exact_head"):
+                     "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_k_head_lane",
+                     "orc_quant_v_head", "orc_qk_int32_head", "orc_attn_head_rows", "orc_attn_exact_head"):
             getattr(L, name).restype = None
+        L.orc_lane_group.restype = ctypes.c_int
+        L.orc_lane_group.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -184,6 +187,23 @@ def quant_k_head(kf: np.ndarray, blk: int, smooth: bool = True):
     return codes, scales, mean
 
 
+def lane_group(n: int) -> int:
+    """K scale group of key n under thread-level granularity (see sage_oracle.c)."""
+    return int(lib().orc_lane_group(int(n)))
+
+
+def quant_k_head_lane(kf: np.ndarray, smooth: bool = True):
+    """K codes, one scale per 16-key lane group (2 * ceil(S / 32) scales), K mean."""
+    kf = _f32(kf)
+    S, D = kf.shape
+    codes = np.empty((S, D), np.int8)
+    scales = np.empty(2 * ((S + 31) // 32), np.float32)
+    mean = np.empty(D, np.float32)
+    lib().orc_quant_k_head_lane(_p(kf, ctypes.c_float), S, D, int(smooth), _p(codes, ctypes.c_int8),
+                                _p(scales, ctypes.c_float), _p(mean, ctypes.c_float))
+    return codes, scales, mean
+
+
 def quant_v_head(vf: np.ndarray):
     vf = _f32(vf)
     S, D = vf.shape
@@ -203,10 +223,11 @@ def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 
 def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
-                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K) -> np.ndarray:
+                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False) -> np.ndarray:
     """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
 
-    blk_q / blk_k: tokens per INT8 scale of Q / K; tile_k: keys per online-softmax
+    blk_q / blk_k: tokens per INT8 scale of Q / K (k_lane: K scales per lane group
+    instead of blocks, as quant_k_head_lane makes them); tile_k: keys per online-softmax
     tile (the two-level accumulation folds once per tile).  The query rows (q8)
     and the keys (k8, v8, vf) may differ in number."""
     Sq, D = q8.shape
@@ -223,7 +244,7 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     v_scale = _f32(v_scale if v_scale is not None else np.zeros(D, np.float32))
     vf = _f32(vf if vf is not None else np.zeros((S, D), np.float32))
     lib().orc_attn_head_rows(_p(q8, ctypes.c_int8), _p(q_scale, ctypes.c_float), blk_q,
-                             _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k, tile_k,
+                             _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k, int(bool(k_lane)), tile_k,
                              _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float), _p(vf, ctypes.c_float),
                              in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
                              _p(rows, ctypes.c_int), rows.size, _p(out, ctypes.c_float))
@@ -296,11 +317,18 @@ def kv_head(h: int, H: int, Hkv: int) -> int:
 
 
 def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
-         heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True):
+         heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block"):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
 
+    gran: "block" (blk_q / blk_k tokens per scale) or "lane" (thread-level: one
+    scale per Q token, one per 16-key lane group of K).
     Returns {(b, h): fp32 [len(rows), D]}; rows default to all S rows.
     """
+    if gran not in ("block", "lane"):
+        raise ValueError(gran)
+    lane = gran == "lane"
+    if lane:
+        blk_q = 1
     B, H, S, D = logical_shape(q.shape, layout)
     Hkv = logical_shape(k.shape, layout)[1]
     if sm_scale is None:
@@ -313,14 +341,14 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         kf = decode16(head(k, layout, b, hk), dtype)
         vf = decode16(head(v, layout, b, hk), dtype)
         q8, qs = quant_q_head(qf, blk_q)
-        k8, ks, _ = quant_k_head(kf, blk_k, smooth)
+        k8, ks, _ = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
         if pv_mode == PV_FP8:
             v8, vs = quant_v_head(vf)
         else:
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
                                      sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k,
-                                     tile_k=tile_k)
+                                     tile_k=tile_k, k_lane=lane)
     return res
 
 
@@ -349,7 +377,7 @@ def seq_slices(cu_seqlens) -> list:
 
 
 def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
-                heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True):
+                heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block"):
     """Quantized attention over a packed batch of sequences of different lengths
     ("Thư viện SageAttention" page, feature list: variable-length sequences through
     sageattn_varlen).
@@ -374,6 +402,6 @@ def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=No
         (q0, q1), (k0, k1) = sq[b], sk[b]
         one = attn(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype, "NHD", is_causal=is_causal,
                    sm_scale=sm_scale, pv_mode=pv_mode, heads=[(0, h)], rows=rows, blk_q=blk_q, blk_k=blk_k,
-                   tile_k=tile_k, smooth=smooth)
+                   tile_k=tile_k, smooth=smooth, gran=gran)
         res[(b, h)] = one[(0, h)]
     return res

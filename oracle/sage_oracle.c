@@ -207,6 +207,47 @@ void orc_quant_k_head(const float *k, int S, int D, int blk, int smooth, int8_t 
 }
 
 /*
+ * Thread-level granularity ([SA2, SageAttention2方法]: quantise at the
+ * granularity of the GPU threads' share of the matrix-multiply layout, so that
+ * dequantisation costs nothing extra).  On the 32 x 32 INT8 matrix core of
+ * gfx950 the score tile of 32 keys x 32 queries leaves each lane one query and
+ * 16 keys: the keys whose offset in the 32-key sub-tile has bit 2 equal to the
+ * lane's half of the wavefront.  Reading: Q gets one scale per token and K one
+ * scale per such 16-key group; group of key n = 2 * (n / 32) + bit 2 of n.
+ */
+int orc_lane_group(int n) { return 2 * (n >> 5) + ((n >> 2) & 1); }
+
+/*
+ * K with thread-level granularity: optional mean subtraction as in
+ * orc_quant_k_head, then one INT8 scale per key group of orc_lane_group
+ * (2 * ceil(S / 32) groups; a group without keys gets scale 0).
+ */
+void orc_quant_k_head_lane(const float *k, int S, int D, int smooth, int8_t *codes,
+                           float *scales, float *mean) {
+    size_t n = (size_t)S * D;
+    int ng = 2 * ((S + 31) / 32);
+    float *ks = (float *)malloc((n ? n : 1) * sizeof(float));
+    float *grp = (float *)malloc((size_t)16 * D * sizeof(float));
+    int8_t *gc = (int8_t *)malloc((size_t)16 * D);
+    int *rows = (int *)malloc(16 * sizeof(int));
+    if (smooth) orc_channel_mean(k, S, D, mean);
+    else memset(mean, 0, (size_t)D * sizeof(float));
+    for (size_t i = 0; i < n; ++i) ks[i] = k[i] - mean[i % D];
+    for (int g = 0; g < ng; ++g) {
+        int cnt = 0;
+        for (int t = 32 * (g / 2); t < S && t < 32 * (g / 2 + 1); ++t)
+            if (orc_lane_group(t) == g) rows[cnt++] = t;
+        for (int r = 0; r < cnt; ++r) memcpy(grp + (size_t)r * D, ks + (size_t)rows[r] * D, (size_t)D * sizeof(float));
+        orc_int8_quant_block(grp, (size_t)cnt * D, gc, &scales[g]);
+        for (int r = 0; r < cnt; ++r) memcpy(codes + (size_t)rows[r] * D, gc + (size_t)r * D, (size_t)D);
+    }
+    free(ks);
+    free(grp);
+    free(gc);
+    free(rows);
+}
+
+/*
  * V: per-channel FP8 E4M3 ([SA2, SageAttention2方法]: V to FP8 with per-channel
  * quantisation).  scale[d] = amax_d / 448, code = E4M3(v * (448 / amax_d));
  * an all-zero channel gets scale 0 and codes 0.
@@ -256,7 +297,8 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  * whose running max m and running sum l are fp32 ([SA2, 相关工作]: token-dim
  * blocking of FlashAttention; SageAttention builds on that blocking).  The tile
  * size is a free parameter of that blocking; it is independent of the INT8
- * scale blocks of K (`blk_k` tokens each, key n uses k_scale[n / blk_k]).
+ * scale blocks of K (`blk_k` tokens each, key n uses k_scale[n / blk_k]; with
+ * k_lane, key n uses k_scale[orc_lane_group(n)]).  Query i uses q_scale[i / blk_q].
  * Per key tile:
  *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_blk(n)) * sm_scale)     (dequantise)
  *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal;
@@ -278,7 +320,7 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  * rounding to the input dtype).  A row that sees no key at all (S = 0) is 0.
  */
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
-                        const int8_t *k8, const float *k_scale, int blk_k, int tile_k,
+                        const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, float *out) {
@@ -304,7 +346,8 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                     if (n >= S || (is_causal && n > i)) {
                         s[t] = -INFINITY;
                     } else {
-                        float c = (dq * k_scale[n / blk_k]) * sm_scale;
+                        int kg = k_lane ? orc_lane_group(n) : n / blk_k;
+                        float c = (dq * k_scale[kg]) * sm_scale;
                         s[t] = (float)dot_i8(q8 + (size_t)i * D, k8 + (size_t)n * D, D) * c;
                     }
                     if (s[t] > mt) mt = s[t];

@@ -56,12 +56,15 @@ void orc_channel_mean(const float *x, int S, int D, float *mean);
 void orc_quant_q_head(const float *q, int S, int D, int blk, int8_t *codes, float *scales);
 void orc_quant_k_head(const float *k, int S, int D, int blk, int smooth,
                       int8_t *codes, float *scales, float *mean);
+int orc_lane_group(int n);
+void orc_quant_k_head_lane(const float *k, int S, int D, int smooth,
+                           int8_t *codes, float *scales, float *mean);
 void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scales);
 
 /* ---- attention (per head) ---------------------------------------------- */
 void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t *out);
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
-                        const int8_t *k8, const float *k_scale, int blk_k, int tile_k,
+                        const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, float *out);

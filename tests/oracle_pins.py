@@ -469,7 +469,6 @@ def pin_gqa_group_mapping():
             raise AssertionError((H, Hkv))
 
 
-ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
 # ------------------------------------------------------------------ packed variable-length batches
@@ -559,3 +558,101 @@ def pin_no_keys_gives_zero():
     got = O.attn_varlen(q, k, v, cu_q, cu_k, F16)
     assert got[(0, 1)].shape == (0, 64)
     assert got[(1, 0)].shape == (50, 64) and not got[(1, 0)].any()
+
+
+# ------------------------------------------------------------------ thread-level (lane) granularity
+def pin_lane_groups_follow_mfma_layout():
+    """The K groups are exactly the 16 keys one lane half holds of each 32-key
+    sub-tile in the 32 x 32 MFMA result layout (lane l, accumulator r holds row
+    8 * (r // 4) + 4 * (l // 32) + r % 4), numbered 2 * sub-tile + half."""
+    for j in range(5):
+        for half in (0, 1):
+            keys = {32 * j + 8 * (r // 4) + 4 * half + r % 4 for r in range(16)}
+            assert len(keys) == 16
+            assert {O.lane_group(n) for n in keys} == {2 * j + half}, (j, half)
+
+
+def pin_lane_quant_scales():
+    """Lane-granular K: each group's scale is its own amax / 127 (after the mean
+    subtraction), codes follow the INT8 rule inside the group; Q per token."""
+    S, D = 150, 64
+    qf, kf, _ = _rand_head(S, D, seed=41)
+    kf = kf.copy()
+    kf[37, 5] = 60.0  # an outlier in group 3 only
+    k8, ks, km = O.quant_k_head_lane(kf, True)
+    assert ks.size == 2 * 5
+    kc = kf.astype(np.float32) - km[None, :]
+    groups = np.array([2 * (n // 32) + ((n % 32) // 4) % 2 for n in range(S)])
+    for g in range(ks.size):
+        x = kc[groups == g]
+        if x.size == 0:
+            assert ks[g] == 0
+            continue
+        amax = np.abs(x).max()
+        assert ks[g] == np.float32(amax) / np.float32(127), g
+        inv = np.float32(127) / np.float32(amax)
+        ref = np.clip(np.rint(x * inv), -127, 127).astype(np.int8)
+        assert np.array_equal(k8[groups == g], ref), g
+    assert ks[3] > 4 * np.median(ks)  # the outlier raised its own group's scale only
+    q8, qs = O.quant_q_head(qf, 1)
+    assert np.array_equal(qs, (np.abs(qf).max(axis=1).astype(np.float32) / np.float32(127)))
+
+
+def pin_lane_equals_block_when_scales_agree():
+    """When every token and every key reaches the same amax (one entry +-A per
+    row dominates), per-token/per-group scales equal the block scales, so lane
+    and block granularity give bit-identical attention."""
+    S, D = 200, 64
+    qf, kf, vf = _rand_head(S, D, seed=42)
+    rng = np.random.default_rng(7)
+    for x in (qf, kf):
+        x[np.arange(S), rng.integers(0, D, S)] = np.float32(16.0) * rng.choice([-1, 1], S).astype(np.float32)
+    q, k, v = (_f16(x)[None, None] for x in (qf, kf, vf))
+    for causal in (False, True):
+        for pv in (O.PV_FP8, O.PV_FP16):
+            a = O.attn(q, k, v, F16, "HND", is_causal=causal, pv_mode=pv, smooth=False, gran="lane")[(0, 0)]
+            b = O.attn(q, k, v, F16, "HND", is_causal=causal, pv_mode=pv, smooth=False, gran="block")[(0, 0)]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (causal, pv)
+
+
+def pin_lane_more_accurate_on_varying_tokens():
+    """Per-token / per-group scales follow tokens of very different norms more
+    closely than per-block scales: smaller error against exact attention."""
+    w = synth.custom(1, 2, 512, 128, token_norm=True, outlier_p=0.01, bias_sigma=3.0, seed=43)
+    q, k, v = synth.make_qkv(w)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    for causal in (False,):
+        lane = O.attn(q, k, v, F16, "HND", is_causal=causal, gran="lane")
+        blk = O.attn(q, k, v, F16, "HND", is_causal=causal, gran="block")
+        for hd in ex:
+            el, eb = rel_l1(lane[hd], ex[hd]), rel_l1(blk[hd], ex[hd])
+            assert el < eb, (hd, el, eb)
+
+
+def pin_lane_attention_uses_group_scales():
+    """Attention on lane-granular codes dequantises key n with its group's scale:
+    against softmax(dq_i * dk_g(n) * sm * (q8 . k8)) @ V worked out here in
+    binary64 from the same codes (pv fp16 rounds only P and V to fp16)."""
+    from scipy.special import softmax
+
+    S, D = 150, 64
+    qf, kf, vf = _rand_head(S, D, seed=44)
+    kf = kf.copy()
+    kf[37, 5] = 60.0
+    kf[101, 9] = -45.0
+    q8, qs = O.quant_q_head(qf, 1)
+    k8, ks, _ = O.quant_k_head_lane(kf, True)
+    groups = np.array([2 * (n // 32) + ((n % 32) // 4) % 2 for n in range(S)])
+    sm = 0.125
+    s = (q8.astype(np.float64) @ k8.astype(np.float64).T) * qs[:, None].astype(np.float64) \
+        * ks[groups][None, :].astype(np.float64) * sm
+    for causal in (False, True):
+        if causal:
+            s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+        ref = softmax(s, axis=1) @ vf.astype(np.float64)
+        got = O.attn_head_rows(q8, qs, k8, ks, None, None, vf, in_dtype=F16, is_causal=causal, sm_scale=sm,
+                               pv_mode=O.PV_FP16, blk_q=1, k_lane=True)
+        assert cos(got, ref) >= 0.99999 and rel_l1(got, ref) < 2e-3, (causal, cos(got, ref), rel_l1(got, ref))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

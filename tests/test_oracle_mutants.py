@@ -28,9 +28,15 @@ MUTANTS = [
     ("causal_masks_diagonal", "(is_causal && n > i)", "(is_causal && n >= i)"),
     ("round_ties_away", "return nearbyint(a / q) * q;", "return round(a / q) * q;"),
     ("e4m3_bias_8", "ldexp(1.0 + fr / 8.0, ex - 7)", "ldexp(1.0 + fr / 8.0, ex - 8)"),
-    ("missing_sm_scale", "float c = (dq * k_scale[n / blk_k]) * sm_scale;", "float c = dq * k_scale[n / blk_k];"),
-    ("k_scale_indexed_by_tile", "float c = (dq * k_scale[n / blk_k])", "float c = (dq * k_scale[n / tile_k])"),
-    ("k_scale_first_block_only", "float c = (dq * k_scale[n / blk_k])", "float c = (dq * k_scale[0])"),
+    ("missing_sm_scale", "float c = (dq * k_scale[kg]) * sm_scale;", "float c = dq * k_scale[kg];"),
+    ("k_scale_indexed_by_tile", "int kg = k_lane ? orc_lane_group(n) : n / blk_k;",
+     "int kg = k_lane ? orc_lane_group(n) : n / tile_k;"),
+    ("k_scale_first_block_only", "float c = (dq * k_scale[kg])", "float c = (dq * k_scale[0])"),
+    ("k_lane_scale_by_block", "int kg = k_lane ? orc_lane_group(n) : n / blk_k;", "int kg = n / blk_k;"),
+    ("lane_group_wrong_bit", "return 2 * (n >> 5) + ((n >> 2) & 1);", "return 2 * (n >> 5) + ((n >> 3) & 1);"),
+    ("lane_group_no_subtile", "return 2 * (n >> 5) + ((n >> 2) & 1);", "return (n >> 5) + ((n >> 2) & 1);"),
+    ("lane_k_not_smoothed", "for (size_t i = 0; i < n; ++i) ks[i] = k[i] - mean[i % D];\n    for (int g = 0;",
+     "for (size_t i = 0; i < n; ++i) ks[i] = k[i];\n    for (int g = 0;"),
     ("q_scale_wrong_block", "float dq = q_scale[i / blk_q];", "float dq = q_scale[i / blk_k];"),
     ("exact_causal_off_by_one", "int nvis = is_causal ? (i + 1 < S ? i + 1 : S) : S;",
      "int nvis = is_causal ? (i < S ? (i > 0 ? i : 1) : S) : S;"),

@@ -8,3 +8,8 @@ import oracle_pins as P
 @pytest.mark.parametrize("pin", P.ALL_PINS, ids=[p.__name__ for p in P.ALL_PINS])
 def test_pin(orc, pin):
     pin()
+
+
+def test_every_pin_is_collected():
+    names = {n for n in dir(P) if n.startswith("pin_") and callable(getattr(P, n))}
+    assert names == {p.__name__ for p in P.ALL_PINS}
