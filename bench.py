@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default=None)
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
+    p.add_argument("--qk-gran", default="block", choices=["block", "lane"],
+                   help="INT8 scale granularity of Q and K: per block, or per token / 16-key lane group")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-oracle sample (0: as many as take about 12 s)")
@@ -73,7 +75,7 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_hash, workload, pv, causal):
+def traffic_record(kernel_hash, workload, pv, causal, gran="block"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summaries, if one was taken on the current kernel source for this workload
     and mode."""
@@ -83,12 +85,12 @@ def traffic_record(kernel_hash, workload, pv, causal):
         return None
     for rec in recs:
         if (rec.get("attn_src_sha256_16") == kernel_hash and rec.get("workload") == workload
-                and rec.get("pv_mode") == pv and rec.get("causal") == causal):
+                and rec.get("pv_mode") == pv and rec.get("causal") == causal and rec.get("qk_gran", "block") == gran):
             return rec
     return None
 
 
-def cpu_baseline(w, causal, pv, nheads):
+def cpu_baseline(w, causal, pv, nheads, gran="block"):
     import numpy as np
 
     import oracle as O
@@ -108,7 +110,8 @@ def cpu_baseline(w, causal, pv, nheads):
 
         def run(heads):
             t0 = time.perf_counter()
-            O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=bool(causal), pv_mode=pvm, heads=heads)
+            O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=bool(causal), pv_mode=pvm, heads=heads,
+                          gran=gran)
             return time.perf_counter() - t0
         what = "sequence-heads"
     else:
@@ -120,7 +123,8 @@ def cpu_baseline(w, causal, pv, nheads):
 
         def run(heads):
             t0 = time.perf_counter()
-            O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal), pv_mode=pvm, heads=heads)
+            O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal), pv_mode=pvm, heads=heads,
+                   gran=gran)
             return time.perf_counter() - t0
         what = "heads"
 
@@ -174,18 +178,18 @@ def main():
     if varlen:
         cq, ck = (torch.from_numpy(c).to(dev) for c in w.cu_seqlens())
         mq, mk = max(w.seqlens_q), max(w.seqlens_k)
-        bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev)
+        bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev, args.qk_gran)
 
         def quant():
-            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs)
+            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_gran=args.qk_gran)
 
         def attn():
             qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)
     else:
-        bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads)
+        bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_gran)
 
         def quant():
-            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs)
+            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_gran=args.qk_gran)
 
         def attn():
             qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
@@ -218,7 +222,7 @@ def main():
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     khash = source_hash(ATTN_SRC)
-    trec = traffic_record(khash, name, args.pv, bool(causal))
+    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_gran)
     traffic = None if trec is None else trec["hbm_bytes_per_launch"]
 
     res = {
@@ -237,9 +241,11 @@ def main():
         "data": "synthetic",
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,
-                    "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv} if varlen else
+                    "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv,
+                    "qk_gran": args.qk_gran} if varlen else
                    {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
-                    "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv}),
+                    "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv,
+                    "qk_gran": args.qk_gran}),
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv), 1), "unit": "TFLOP/s",
@@ -248,7 +254,7 @@ def main():
                      "attn_src_sha256_16": khash},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_gran)
     print(json.dumps(res))
 
 

@@ -46,10 +46,12 @@
  *   S_q = roundup(S, SAGE_BLK_Q), S_k = roundup(S, SAGE_KV_PAD),
  *   nq = S_q / SAGE_BLK_Q, nk = S_k / SAGE_BLK_K.
  *   q_i8    int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
- *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens.
+ *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens
+ *                                  (SAGE_GRAN_LANE: [B][H][S_q], one per token).
  *   k_i8    int8  [B][H_kv][S_k][D] INT8 codes of K - k_mean; rows >= S are 0.
  *   k_scale float [B][H_kv][nk]    one scale per block of SAGE_BLK_K tokens (0 for blocks
- *                                  made only of padding keys).
+ *                                  made only of padding keys; SAGE_GRAN_LANE:
+ *                                  [B][H_kv][S_k / 16], one per lane group).
  *   k_mean  float [B][H_kv][D]     per-channel mean of K over the S tokens.
  *   v_fp8   uint8 [B][H_kv][nk][D][64] E4M3 codes of V, one 64-key tile after the
  *           other, each tile stored channel-major; inside a tile, byte p of
@@ -81,6 +83,13 @@ extern "C" {
 #define SAGE_DTYPE_BF16 1
 #define SAGE_PV_FP8 0  /* P~ and V in E4M3, two-level fp32 accumulation ([SA2]) */
 #define SAGE_PV_FP16 1 /* P~ and V in fp16, fp32 accumulation ([KAI] 2.1, sm80 row) */
+/* INT8 scale granularity of Q and K ([KAI] 2.2 per_block / per_warp choice; [SA2]
+ * SageAttention2方法, thread-level quantisation): */
+#define SAGE_GRAN_BLOCK 0 /* one scale per SAGE_BLK_Q query tokens / SAGE_BLK_K keys */
+#define SAGE_GRAN_LANE 1  /* one scale per query token and per 16-key lane group: the
+                             keys one half-wave holds of each 32-key sub-tile of the
+                             32 x 32 INT8 MFMA result, group of key n = 2 (n / 32) +
+                             ((n / 4) mod 2); every lane dequantises with one scale */
 
 /* ---- limits and granularity ---- */
 #define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
@@ -101,8 +110,8 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16);
 
 /* Bytes of each intermediate buffer for a problem shape (see the layouts
  * above).  Any output pointer may be NULL. */
-int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8,
-                      size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
+int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_gran, size_t *q_i8, size_t *q_scale,
+                      size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
 
 /*
  * K smoothing + per-block INT8 quantisation of Q and K ([SA2] 相关工作,
@@ -112,6 +121,8 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t
  *   (one fp32 subtraction per element), each over all D channels:
  *     amax = max |x|;  scale = amax / 127;  code = rint(x * (127 / amax)) in [-127, 127];
  *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
+ *   qk_gran = SAGE_GRAN_LANE: the same rule with each Q token, and each 16-key lane
+ *   group of K - k_mean, as its own block.
  * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
  * same with H_kv heads.
  * Writes q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).  The call is
@@ -120,8 +131,8 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t
  * passed the call.
  */
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
-                         int layout, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
-                         void *stream);
+                         int layout, int qk_gran, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale,
+                         float *k_mean, void *stream);
 
 /*
  * Per-channel FP8 E4M3 quantisation of V ([SA2] SageAttention2方法):
@@ -140,7 +151,9 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  * Fused quantized attention ([SA2]; [KAI] 2.1; [GUIDE] 五分钟跑通, 性能调优实战).
  * For each query row i, key tiles (SAGE_TILE_K_FP8 / SAGE_TILE_K_FP16 keys) in order,
  * fp32 online softmax:
- *   s_n = float(q_i8[i] . k_i8[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA, int32 sums)
+ *   s_n = float(q_i8[i] . k_i8[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA, int32 sums;
+ *         the scales of query i's block and key n's block, or lane group: qk_gran must
+ *         be the granularity the codes were made with)
  *   keys n >= S, and n > i when is_causal (square, top-left aligned), are excluded
  *   m' = max(m, max_n s_n);  alpha = exp(m - m');  p_n = exp(s_n - m');  l = alpha*l + sum p_n
  *   pv fp8 : P = E4M3(448 * p_n) (static scale), inner = P . V_fp8 (FP8 MFMA, fresh per tile),
@@ -156,7 +169,7 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  */
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
                   const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S,
-                  int D, int layout, int is_causal, float sm_scale, int pv_mode, void *stream);
+                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream);
 
 /*
  * Debug variant of sage_attn_fwd: the same kernel code, which additionally
@@ -168,8 +181,8 @@ int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, 
  */
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
                           const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
-                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
-                          int32_t *qk, void *stream);
+                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran,
+                          int b, int h, int32_t *qk, void *stream);
 
 /* ------------------------------------------------------------------------
  * Packed variable-length batches ([REPO] feature list: variable-length
@@ -196,23 +209,23 @@ int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t
  * rows of sequence b start at
  *   rq(b) = 32 * (cu_seqlens_q[b] / 32 + b),  rk(b) = 128 * (cu_seqlens_k[b] / 128 + b)
  * of RQ = 32 * (total_q / 32 + B + 1) and RK = 128 * (total_k / 128 + B + 1) rows:
- *   q_i8    int8  [H][RQ][D]          q_scale float [H][RQ / 32]
- *   k_i8    int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64]
+ *   q_i8    int8  [H][RQ][D]          q_scale float [H][RQ / 32]    (lane: [H][RQ])
+ *   k_i8    int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64] (lane: [H_kv][RK / 16])
  *   k_mean  float [B][H_kv][D]        v_scale float [B][H_kv][D]
  *   v_fp8   uint8 [H_kv][RK / 64][D][64]  (64-key tiles as in the fixed layout)
  * A sequence's rows past its length, up to the next multiple of 32 (Q) or 128
  * (K, V), hold zero codes; rows between sequences are neither written nor read.
  * Other rules (alignment, errors, stream order, staging) as above.
  * ------------------------------------------------------------------------ */
-int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, size_t *q_i8,
-                             size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8,
-                             size_t *v_scale);
+int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, int qk_gran,
+                             size_t *q_i8, size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean,
+                             size_t *v_fp8, size_t *v_scale);
 
 /* sage_smooth_quant_qk for a packed batch. */
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
-                                int max_seqlen_q, int max_seqlen_k, int D, int8_t *q_i8, float *q_scale,
-                                int8_t *k_i8, float *k_scale, float *k_mean, void *stream);
+                                int max_seqlen_q, int max_seqlen_k, int D, int qk_gran, int8_t *q_i8,
+                                float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean, void *stream);
 
 /* sage_quant_v for a packed batch (v: [total_k][H_kv][D]). */
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
@@ -224,7 +237,7 @@ int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t 
                          const void *v, const float *v_scale, void *out, int dtype, const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
-                         void *stream);
+                         int qk_gran, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *sage_status_str(int status);

@@ -26,6 +26,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ER
 LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
 PV = {"fp8": 0, "fp16": 1}
+GRAN = {"block": 0, "lane": 1}  # INT8 scale granularity of Q and K (include/sage.h SAGE_GRAN_*)
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
@@ -51,18 +52,18 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         c_int, c_float, c_void_p, c_size_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
         L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
-        L.sage_buffer_sizes.argtypes = [c_int] * 5 + [c_size_p] * 7
-        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 7 + [c_void_p] * 5 + [c_void_p]
+        L.sage_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 7
+        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 5 + [c_void_p]
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p, c_void_p, c_void_p]
-        attn = [c_void_p] * 7 + [c_int] * 8 + [c_float, c_int]
+        attn = [c_void_p] * 7 + [c_int] * 8 + [c_float, c_int, c_int]
         L.sage_attn_fwd.argtypes = attn + [c_void_p]
         L.sage_attn_fwd_dump_qk.argtypes = attn + [c_int, c_int, c_void_p, c_void_p]
-        L.sage_varlen_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 7
-        L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 8 + \
+        L.sage_varlen_buffer_sizes.argtypes = [c_int] * 7 + [c_size_p] * 7
+        L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + \
             [c_void_p] * 5 + [c_void_p]
         L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 3
         L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 7 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
-            [c_int, c_float, c_int, c_void_p]
+            [c_int, c_float, c_int, c_int, c_void_p]
         L.sage_status_str.argtypes = [c_int]
         L.sage_status_str.restype = ctypes.c_char_p
         L.sage_check_arch.argtypes = [ctypes.c_char_p]
@@ -92,17 +93,18 @@ def sage_get_config():
     return tuple(x.value for x in v)
 
 
-def sage_buffer_sizes(B, H, H_kv, S, D):
+def sage_buffer_sizes(B, H, H_kv, S, D, qk_gran=0):
     vals = [ctypes.c_size_t() for _ in range(7)]
-    _check(lib().sage_buffer_sizes(B, H, H_kv, S, D, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
+    _check(lib().sage_buffer_sizes(B, H, H_kv, S, D, qk_gran, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
     names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
     return {n: v.value for n, v in zip(names, vals)}
 
 
-def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_gran, q_i8, q_scale, k_i8, k_scale, k_mean,
+                         stream):
     """All tensor arguments are device pointers (ints); returns the status code."""
-    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, q_i8, q_scale, k_i8, k_scale, k_mean,
-                                      stream)
+    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_gran, q_i8, q_scale, k_i8, k_scale,
+                                      k_mean, stream)
 
 
 def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream):
@@ -110,30 +112,30 @@ def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream):
 
 
 def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                  sm_scale, pv_mode, stream):
+                  sm_scale, pv_mode, qk_gran, stream):
     return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout,
-                               is_causal, sm_scale, pv_mode, stream)
+                               is_causal, sm_scale, pv_mode, qk_gran, stream)
 
 
 def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                          sm_scale, pv_mode, b, h, qk, stream):
+                          sm_scale, pv_mode, qk_gran, b, h, qk, stream):
     return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D,
-                                       layout, is_causal, sm_scale, pv_mode, b, h, qk, stream)
+                                       layout, is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, stream)
 
 
-def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D):
+def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_gran=0):
     vals = [ctypes.c_size_t() for _ in range(7)]
-    _check(lib().sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, *[ctypes.byref(v) for v in vals]),
-           "sage_varlen_buffer_sizes")
+    _check(lib().sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_gran,
+                                          *[ctypes.byref(v) for v in vals]), "sage_varlen_buffer_sizes")
     names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
     return {n: v.value for n, v in zip(names, vals)}
 
 
 def sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
-                                max_seqlen_k, D, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+                                max_seqlen_k, D, qk_gran, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
     return lib().sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k,
-                                             max_seqlen_q, max_seqlen_k, D, q_i8, q_scale, k_i8, k_scale, k_mean,
-                                             stream)
+                                             max_seqlen_q, max_seqlen_k, D, qk_gran, q_i8, q_scale, k_i8, k_scale,
+                                             k_mean, stream)
 
 
 def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale, stream):
@@ -142,10 +144,11 @@ def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, 
 
 
 def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv,
-                         total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode, stream):
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode, qk_gran,
+                         stream):
     return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, cu_seqlens_q,
                                       cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
-                                      is_causal, sm_scale, pv_mode, stream)
+                                      is_causal, sm_scale, pv_mode, qk_gran, stream)
 
 
 def sage_status_str(status):
@@ -196,16 +199,17 @@ class Quantized:
     """Device buffers produced by the two quantisation entry points (K and V
     buffers have H_kv heads; H_kv = H unless K/V are grouped)."""
 
-    def __init__(self, B, H, S, D, device, H_kv=None):
+    def __init__(self, B, H, S, D, device, H_kv=None, qk_gran="block"):
         import torch
 
         H_kv = H if H_kv is None else H_kv
-        self.B, self.H, self.H_kv, self.S, self.D = B, H, H_kv, S, D
+        self.B, self.H, self.H_kv, self.S, self.D, self.gran = B, H, H_kv, S, D, GRAN[qk_gran]
         sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + KV_PAD - 1) // KV_PAD * KV_PAD
+        lane = self.gran == GRAN["lane"]
         self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
-        self.q_scale = torch.empty((B, H, sq // BLK_Q), dtype=torch.float32, device=device)
+        self.q_scale = torch.empty((B, H, sq if lane else sq // BLK_Q), dtype=torch.float32, device=device)
         self.k_i8 = torch.empty((B, H_kv, sk, D), dtype=torch.int8, device=device)
-        self.k_scale = torch.empty((B, H_kv, sk // BLK_K), dtype=torch.float32, device=device)
+        self.k_scale = torch.empty((B, H_kv, sk // 16 if lane else sk // BLK_K), dtype=torch.float32, device=device)
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((B, H_kv, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
@@ -222,9 +226,11 @@ def _kv_heads(q, k, v, tensor_layout):
     return H_kv
 
 
-def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None) -> Quantized:
+def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
+             qk_gran="block") -> Quantized:
     """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors.
-    k and v may have fewer heads than q (grouped-query attention)."""
+    k and v may have fewer heads than q (grouped-query attention); qk_gran "block"
+    or "lane" (one scale per Q token and per 16-key lane group of K)."""
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
     H_kv = _kv_heads(q, k, v, tensor_layout)
@@ -232,11 +238,12 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
     dt = _dtype_code(q)
-    bufs = bufs or Quantized(B, H, S, D, q.device, H_kv)
-    if (bufs.B, bufs.H, bufs.H_kv, bufs.S, bufs.D) != (B, H, H_kv, S, D):
-        raise ValueError("bufs were allocated for another shape")
+    bufs = bufs or Quantized(B, H, S, D, q.device, H_kv, qk_gran)
+    if (bufs.B, bufs.H, bufs.H_kv, bufs.S, bufs.D, bufs.gran) != (B, H, H_kv, S, D, GRAN[qk_gran]):
+        raise ValueError("bufs were allocated for another shape or granularity")
     st = _stream()
-    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.q_i8.data_ptr(),
+    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.gran,
+                                bufs.q_i8.data_ptr(),
                                 bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
                                 bufs.k_mean.data_ptr(), st), "sage_smooth_quant_qk")
     if pv_mode == "fp8":
@@ -261,7 +268,7 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
     args = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs,
-            out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv)
+            out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.gran)
     if dump_head is None:
         _check(sage_attn_fwd(*args, _stream()), "sage_attn_fwd")
     else:
@@ -270,11 +277,11 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     return out
 
 
-def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8"):
+def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_gran="block"):
     """Quantized attention: same shape, dtype and layout out as q."""
     import torch
 
-    bufs = quantize(q, k, v, tensor_layout, pv_mode)
+    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_gran=qk_gran)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
 
@@ -293,16 +300,18 @@ def varlen_row0(start: int, b: int, pad: int) -> int:
 class QuantizedVarlen:
     """Device buffers of the packed-batch quantisation entry points."""
 
-    def __init__(self, B, H, H_kv, total_q, total_k, D, device):
+    def __init__(self, B, H, H_kv, total_q, total_k, D, device, qk_gran="block"):
         import torch
 
         self.B, self.H, self.H_kv, self.total_q, self.total_k, self.D = B, H, H_kv, total_q, total_k, D
+        self.gran = GRAN[qk_gran]
+        lane = self.gran == GRAN["lane"]
         rq, rk = varlen_rows(total_q, B, BLK_Q), varlen_rows(total_k, B, KV_PAD)
         self.rows_q, self.rows_k = rq, rk
         self.q_i8 = torch.empty((H, rq, D), dtype=torch.int8, device=device)
-        self.q_scale = torch.empty((H, rq // BLK_Q), dtype=torch.float32, device=device)
+        self.q_scale = torch.empty((H, rq if lane else rq // BLK_Q), dtype=torch.float32, device=device)
         self.k_i8 = torch.empty((H_kv, rk, D), dtype=torch.int8, device=device)
-        self.k_scale = torch.empty((H_kv, rk // BLK_K), dtype=torch.float32, device=device)
+        self.k_scale = torch.empty((H_kv, rk // 16 if lane else rk // BLK_K), dtype=torch.float32, device=device)
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((H_kv, rk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
@@ -317,7 +326,7 @@ def _cu(t, name):
 
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
-                    bufs: QuantizedVarlen | None = None) -> QuantizedVarlen:
+                    bufs: QuantizedVarlen | None = None, qk_gran="block") -> QuantizedVarlen:
     """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode) on a packed
     batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
@@ -335,13 +344,14 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     if H_kv < 1 or H % H_kv:
         raise ValueError(f"the number of query heads ({H}) must be a multiple of the K/V heads ({H_kv})")
     dt = _dtype_code(q)
-    bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device)
-    if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D) != (B, H, H_kv, total_q, total_k, D):
-        raise ValueError("bufs were allocated for another shape")
+    bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device, qk_gran)
+    if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D, bufs.gran) != \
+            (B, H, H_kv, total_q, total_k, D, GRAN[qk_gran]):
+        raise ValueError("bufs were allocated for another shape or granularity")
     bufs.max_seqlen_q, bufs.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
     st = _stream()
     _check(sage_smooth_quant_qk_varlen(q.data_ptr(), k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
-                                       total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D,
+                                       total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.gran,
                                        bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                        bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
            "sage_smooth_quant_qk_varlen")
@@ -367,18 +377,18 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                 bufs.k_scale.data_ptr(), vptr, vs, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
                                 ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k, bufs.max_seqlen_q,
-                                bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, _stream()),
+                                bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, bufs.gran, _stream()),
            "sage_attn_fwd_varlen")
     return out
 
 
 def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False, sm_scale=None,
-                    pv_mode="fp8"):
+                    pv_mode="fp8", qk_gran="block"):
     """Quantized attention over a packed batch of sequences ("SageAttention: Thư viện
     Attention lượng tử hóa" page, feature list: sageattn_varlen):
     q [total_q, H, D], k / v [total_k, H_kv, D]; returns [total_q, H, D]."""
     import torch
 
-    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode)
+    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_gran=qk_gran)
     out = torch.empty_like(q)
     return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)

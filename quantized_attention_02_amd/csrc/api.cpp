@@ -41,6 +41,14 @@ int check_kv_heads(int H, int H_kv) {
   return SAGE_OK;
 }
 
+int check_gran(int qk_gran) {
+  return (qk_gran == SAGE_GRAN_BLOCK || qk_gran == SAGE_GRAN_LANE) ? SAGE_OK : SAGE_ERR_INVALID_ARG;
+}
+
+// scale entries per head: Q per block of kBlkQ rows or per row; K per kBlkK-row block or 16-row group
+size_t q_scales(size_t rows, int gran) { return gran == SAGE_GRAN_LANE ? rows : rows / kBlkQ; }
+size_t k_scales(size_t rows, int gran) { return gran == SAGE_GRAN_LANE ? rows / 16 : rows / kBlkK; }
+
 int check_enums(int dtype, int layout) {
   if (dtype != SAGE_DTYPE_F16 && dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARG;
   if (layout != SAGE_LAYOUT_HND && layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARG;
@@ -72,11 +80,12 @@ int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LA
 
 int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
                 const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S,
-                int D, int layout, int is_causal, float sm_scale, int pv_mode, int dump_b, int dump_h,
-                int32_t *qk, bool dump, void *stream) {
+                int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, int dump_b,
+                int dump_h, int32_t *qk, bool dump, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
+  if ((rc = check_gran(qk_gran))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
@@ -122,6 +131,7 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   a.nk = a.S_k / kBlkK;
   a.nmblk = (S + 127) / 128;
   a.sm2 = sm_scale * 1.4426950408889634f;
+  a.gran = qk_gran;
   return launch_status(launch_attn(a, dump, (hipStream_t)stream));
 }
 
@@ -138,17 +148,18 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16) {
   return SAGE_OK;
 }
 
-int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t *q_scale, size_t *k_i8,
-                      size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
+int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_gran, size_t *q_i8, size_t *q_scale,
+                      size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
+  if ((rc = check_gran(qk_gran))) return rc;
   const size_t bh = (size_t)B * H, bhk = (size_t)B * H_kv;
   const size_t S_q = roundup(S, kBlkQ), S_k = roundup(S, kKvPad);
   if (q_i8) *q_i8 = bh * S_q * D;
-  if (q_scale) *q_scale = bh * (S_q / kBlkQ) * sizeof(float);
+  if (q_scale) *q_scale = bh * q_scales(S_q, qk_gran) * sizeof(float);
   if (k_i8) *k_i8 = bhk * S_k * D;
-  if (k_scale) *k_scale = bhk * (S_k / kBlkK) * sizeof(float);
+  if (k_scale) *k_scale = bhk * k_scales(S_k, qk_gran) * sizeof(float);
   if (k_mean) *k_mean = bhk * D * sizeof(float);
   if (v_fp8) *v_fp8 = bhk * S_k * D;
   if (v_scale) *v_scale = bhk * D * sizeof(float);
@@ -156,11 +167,12 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, size_t *q_i8, size_t
 }
 
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
-                         int layout, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean,
-                         void *stream) {
+                         int layout, int qk_gran, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale,
+                         float *k_mean, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
+  if ((rc = check_gran(qk_gran))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16)) return SAGE_ERR_INVALID_ARG;
@@ -186,6 +198,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   a.S_k = roundup(S, kKvPad);
   a.nq = a.S_q / kBlkQ;
   a.nk = a.S_k / kBlkK;
+  a.gran = qk_gran;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
 }
 
@@ -214,38 +227,40 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
 
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale, const void *v,
                   const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout,
-                  int is_causal, float sm_scale, int pv_mode, void *stream) {
+                  int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream) {
   return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                     sm_scale, pv_mode, 0, 0, nullptr, false, stream);
+                     sm_scale, pv_mode, qk_gran, 0, 0, nullptr, false, stream);
 }
 
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
                           const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
-                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int b, int h,
-                          int32_t *qk, void *stream) {
+                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran,
+                          int b, int h, int32_t *qk, void *stream) {
   return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                     sm_scale, pv_mode, b, h, qk, true, stream);
+                     sm_scale, pv_mode, qk_gran, b, h, qk, true, stream);
 }
 
 // ---- packed variable-length batches
-static int check_varlen(int B, int H, int H_kv, int total_q, int total_k, int max_q, int max_k, int D) {
+static int check_varlen(int B, int H, int H_kv, int total_q, int total_k, int max_q, int max_k, int D,
+                        int qk_gran) {
   if (B < 1 || total_q < 0 || total_k < 0 || total_q > kMaxTotal || total_k > kMaxTotal) return SAGE_ERR_INVALID_ARG;
   int rc = check_shape(B, H, max_q, D);  // max_q in 1 .. SAGE_MAX_S, launch sizes
   if (rc) return rc;
   if ((rc = check_shape(B, H, max_k, D))) return rc;
+  if ((rc = check_gran(qk_gran))) return rc;
   return check_kv_heads(H, H_kv);
 }
 
-int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, size_t *q_i8,
-                             size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8,
-                             size_t *v_scale) {
-  int rc = check_varlen(B, H, H_kv, total_q, total_k, 1, 1, D);
+int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, int qk_gran,
+                             size_t *q_i8, size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean,
+                             size_t *v_fp8, size_t *v_scale) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, 1, 1, D, qk_gran);
   if (rc) return rc;
   const size_t rq = (size_t)varlen_rows(total_q, B, kBlkQ), rk = (size_t)varlen_rows(total_k, B, kKvPad);
   if (q_i8) *q_i8 = (size_t)H * rq * D;
-  if (q_scale) *q_scale = (size_t)H * (rq / kBlkQ) * sizeof(float);
+  if (q_scale) *q_scale = (size_t)H * q_scales(rq, qk_gran) * sizeof(float);
   if (k_i8) *k_i8 = (size_t)H_kv * rk * D;
-  if (k_scale) *k_scale = (size_t)H_kv * (rk / kBlkK) * sizeof(float);
+  if (k_scale) *k_scale = (size_t)H_kv * k_scales(rk, qk_gran) * sizeof(float);
   if (k_mean) *k_mean = (size_t)B * H_kv * D * sizeof(float);
   if (v_fp8) *v_fp8 = (size_t)H_kv * rk * D;
   if (v_scale) *v_scale = (size_t)B * H_kv * D * sizeof(float);
@@ -254,9 +269,9 @@ int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, i
 
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
-                                int max_seqlen_q, int max_seqlen_k, int D, int8_t *q_i8, float *q_scale,
-                                int8_t *k_i8, float *k_scale, float *k_mean, void *stream) {
-  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D);
+                                int max_seqlen_q, int max_seqlen_k, int D, int qk_gran, int8_t *q_i8,
+                                float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean, void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_gran);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean)
@@ -289,12 +304,13 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
   a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
+  a.gran = qk_gran;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
 }
 
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
                         int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, void *stream) {
-  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D);
+  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D, SAGE_GRAN_BLOCK);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (!v || !cu_seqlens_k || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
@@ -323,8 +339,8 @@ int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t 
                          const void *v, const float *v_scale, void *out, int dtype, const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
-                         void *stream) {
-  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D);
+                         int qk_gran, void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_gran);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
@@ -366,6 +382,7 @@ int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t 
   a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
+  a.gran = qk_gran;
   return launch_status(launch_attn(a, false, (hipStream_t)stream));
 }
 

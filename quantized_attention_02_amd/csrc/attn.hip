@@ -87,6 +87,18 @@ __device__ __forceinline__ float load1_uniform(const float *p) {
   return *(cptr)(((uint64_t)hi << 32) | lo);
 }
 
+// n consecutive floats through a wave-uniform address (scalar loads)
+template <int N>
+__device__ __forceinline__ void loadn_uniform(const float *p, float *out) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  typedef const __attribute__((address_space(4))) float *cptr;
+  const cptr q = (cptr)(((uint64_t)hi << 32) | lo);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = q[i];
+}
+
 __device__ __forceinline__ float2 load2_uniform(const float *p) {
   const uint64_t u = (uint64_t)p;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
@@ -249,8 +261,12 @@ __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lan
 // TN: keys per loop iteration (64 or 128, i.e. one or two INT8 K blocks);
 // WPS: wavefronts per SIMD the register budget is sized for; WAVES: wavefronts
 // per work-group (32 query rows each); NBUF: LDS tile buffers (prefetch
-// distance NBUF - 1).
-template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int TN, int WPS, int WAVES, int NBUF>
+// distance NBUF - 1).  LANE: thread-level scale granularity -- one Q scale per
+// token (this lane's query) and one K scale per 16-key lane group (the keys
+// this half-wave holds of each 32-key sub-tile), so every lane dequantises
+// each sub-tile with one scale of its own; otherwise one scale per 32-query
+// block and per 64-key block.
+template <int D, int PV, int DT, bool CAUSAL, bool DUMP, bool LANE, int TN, int WPS, int WAVES, int NBUF>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
   constexpr int kThreads = WAVES * 64;
@@ -336,7 +352,7 @@ k_attn(const AttnArgs a) {
     const int8_t *qrow = a.q_i8 + (qs.row0 + qi) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
-    dq = a.q_scale[(qs.row0 + qw) >> 5];
+    dq = LANE ? a.q_scale[qs.row0 + qi] : a.q_scale[(qs.row0 + qw) >> 5];
   } else {
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
@@ -355,7 +371,7 @@ k_attn(const AttnArgs a) {
 
   const int8_t *kbase = a.k_i8 + ks.row0 * D;
   const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + ks.row0 * D;
-  const float *kscale = a.k_scale + (ks.row0 >> 6);
+  const float *kscale = a.k_scale + (LANE ? ks.row0 >> 4 : ks.row0 >> 6);
   const HeadView hv{ks.base, ks.stride};  // pv fp16: the caller's V
   const TileCopy<D, TN, WAVES> copy(wave, lane);
   const VCopy16<D, TN, WAVES> vcopy(lane);
@@ -370,9 +386,12 @@ k_attn(const AttnArgs a) {
     // pv fp16: this tile's V rows go into the single V buffer, which the
     // barrier that ended the previous tile has released
     if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, key0, Sk, vb, wave);
-    // the tile's K-block scales, read through a wave-uniform address (scalar loads)
-    float ks[NB];
-    if (NB == 2) {
+    // the tile's K scales, read through a wave-uniform address (scalar loads)
+    constexpr int NKS = LANE ? 2 * NT : NB;  // per lane group, or per 64-key block
+    float ks[NKS];
+    if constexpr (LANE) {
+      loadn_uniform<NKS>(kscale + NKS * j, ks);
+    } else if (NB == 2) {
       const float2 ksv = load2_uniform(kscale + 2 * j);
       ks[0] = ksv.x;
       ks[NB - 1] = ksv.y;
@@ -409,9 +428,17 @@ k_attn(const AttnArgs a) {
             }
         }
       };
-      float c2[NB];
+      // dequantisation factors: per 64-key block, or (LANE) per 32-key sub-tile
+      // with this half-wave's group scale
+      constexpr int NC2 = LANE ? NT : NB;
+      float c2[NC2];
+      if constexpr (LANE) {
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
+        for (int t = 0; t < NT; ++t) c2[t] = (dq * (hh ? ks[2 * t + 1] : ks[2 * t])) * a.sm2;
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
+      }
       // ---- mask: only tiles that reach past S or cross the causal diagonal
       // key (key0 + 4hh + kofs(t, r)) is excluded iff kofs(t, r) > lim, where
       // kofs is a compile-time constant of the register slot
@@ -419,19 +446,24 @@ k_attn(const AttnArgs a) {
       const int lim = (CAUSAL ? min(Sk - 1, qi) : Sk - 1) - key0 - 4 * hh;
       // ---- per INT8 block: row max of the int32 sums (c2 > 0 per block) and
       //      the sums converted to float
-      int mxb[NB];
+      int mxb[NC2];  // int32 max per scale (one c2 each)
       float f[16 * NT];
       auto max_convert = [&](int blk, int mlim, auto mask_tag) {
         int mx = INT_MIN;
 #pragma unroll
-        for (int t = 2 * blk; t < 2 * blk + 2; ++t)
+        for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const bool out = decltype(mask_tag)::value && 32 * t + 8 * (r >> 2) + (r & 3) > mlim;
             mx = max(mx, out ? INT_MIN : s[t][r]);
             f[16 * t + r] = out ? -INFINITY : (float)s[t][r];
           }
-        mxb[blk] = mx;
+          if constexpr (LANE) {
+            mxb[t] = mx;
+            mx = INT_MIN;
+          }
+        }
+        if constexpr (!LANE) mxb[blk] = mx;
       };
       // The MFMAs are issued inside each arm so that the unmasked arm's max and
       // conversion sit in the same basic block as the MFMAs and can fill their
@@ -457,8 +489,8 @@ k_attn(const AttnArgs a) {
       }
       float mt = -INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
-        if (mxb[blk] != INT_MIN) mt = fmaxf(mt, (float)mxb[blk] * c2[blk]);
+      for (int i = 0; i < NC2; ++i)
+        if (mxb[i] != INT_MIN) mt = fmaxf(mt, (float)mxb[i] * c2[i]);
       mt = halves_max(mt);
       const float mn = fmaxf(m, mt);
       alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -469,7 +501,7 @@ k_attn(const AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[16 * t + r], c2[t >> 1], -sub));
+        for (int r = 0; r < 16; ++r) p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[16 * t + r], c2[LANE ? t : t >> 1], -sub));
       if (need_mask) {
         int mlim = lim;
         asm volatile("; zero masked p" : "+v"(mlim) :: "memory");
@@ -612,15 +644,23 @@ struct TileCfg {
   static constexpr int NBUF = PV == 0 ? SAGE_ATTN_NBUF_FP8 : 2;
 };
 
-template <int D, int PV, int DT, bool CAUSAL>
-static hipError_t launch4(const AttnArgs &a, bool dump, hipStream_t st) {
+template <int D, int PV, int DT, bool CAUSAL, bool LANE>
+static hipError_t launch5(const AttnArgs &a, bool dump, hipStream_t st) {
   using C = TileCfg<PV>;
   AttnArgs b = a;
   b.nmblk = (a.S + 32 * C::WAVES - 1) / (32 * C::WAVES);
   const dim3 grid(a.B * a.H * b.nmblk), block(64 * C::WAVES);
-  if (dump) hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, true, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st, b);
-  else hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st, b);
+  if (dump)
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, true, LANE, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st, b);
+  else
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, LANE, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st,
+                       b);
   return hipGetLastError();
+}
+
+template <int D, int PV, int DT, bool CAUSAL>
+static hipError_t launch4(const AttnArgs &a, bool dump, hipStream_t st) {
+  return a.gran == 1 ? launch5<D, PV, DT, CAUSAL, true>(a, dump, st) : launch5<D, PV, DT, CAUSAL, false>(a, dump, st);
 }
 
 template <int D, int PV, int DT>

@@ -174,9 +174,11 @@ __global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// INT8 quantisation of one 32-token block of Q.
+// INT8 quantisation of one 32-token block of Q: one scale for the block, or
+// (LANE) one scale per token -- the query a lane column holds in the 32 x 32
+// INT8 MFMA layout of the attention kernel.
 // ---------------------------------------------------------------------------
-template <int DT, int D>
+template <int DT, int D, bool LANE>
 __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
   __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x;
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
   constexpr int vec_per_row = D / 8;
   constexpr int nvec = kBlkQ * vec_per_row;  // <= 512: at most 2 per thread
   float x[2][8];
-  float amax = 0.0f;
+  float amax = 0.0f, ramax[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int vi = tid + u * kThreads;
@@ -200,11 +202,26 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
       for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[u][i]));
+    for (int i = 0; i < 8; ++i) ramax[u] = fmaxf(ramax[u], fabsf(x[u][i]));
+    amax = fmaxf(amax, ramax[u]);
   }
-  amax = block_max(amax, red);
-  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (tid == 0) a.q_scale[(hv.row0 >> 5) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+  float inv[2];
+  if constexpr (LANE) {
+    // a token's vec_per_row vectors sit in consecutive lanes of one wavefront
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int o = vec_per_row / 2; o >= 1; o >>= 1) ramax[u] = fmaxf(ramax[u], __shfl_xor(ramax[u], o, 64));
+      inv[u] = ramax[u] > 0.0f ? 127.0f / ramax[u] : 0.0f;
+      const int vi = tid + u * kThreads;
+      if (vi < nvec && vi % vec_per_row == 0)
+        a.q_scale[hv.row0 + blk * kBlkQ + vi / vec_per_row] = ramax[u] > 0.0f ? ramax[u] / 127.0f : 0.0f;
+    }
+  } else {
+    amax = block_max(amax, red);
+    inv[0] = inv[1] = amax > 0.0f ? 127.0f / amax : 0.0f;
+    if (tid == 0) a.q_scale[(hv.row0 >> 5) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int vi = tid + u * kThreads;
@@ -212,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
     const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
     uint32_t w[2] = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv[u]) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
     *reinterpret_cast<v2i *>(a.q_i8 + (hv.row0 + blk * kBlkQ + row) * D + c8) = out;
   }
@@ -237,11 +254,16 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: INT8 quantisation of one 64-token block of K - k_mean.
+// Pass 2: INT8 quantisation of one 64-token block of K - k_mean: one scale for
+// the block, or (LANE) one per 16-key lane group -- the keys one half of a
+// wavefront holds of each 32-key sub-tile in the attention kernel's 32 x 32
+// MFMA result, group 2 * (n / 32) + bit 2 of n (4 groups per block).
 // ---------------------------------------------------------------------------
-template <int DT, int D>
+__device__ inline int lane_group_in_block(int row) { return 2 * (row >> 5) + ((row >> 2) & 1); }
+
+template <int DT, int D, bool LANE>
 __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[4][kThreads / 64];
   __shared__ float mean[D];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / a.nk, blk = blockIdx.x % a.nk;  // bh: K head (b, h_kv)
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
   constexpr int vec_per_row = D / 8;
   constexpr int nvec = kBlkK * vec_per_row;  // <= 1024: at most 4 per thread
   float x[4][8];
-  float amax = 0.0f;
+  float amax = 0.0f, gmax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int vi = tid + u * kThreads;
@@ -267,12 +289,53 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
     }
+    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[u][i]));
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[u][i]));
+    amax = fmaxf(amax, m);
+    if (LANE && vi < nvec) {
+      const int g = lane_group_in_block(row);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) gmax[gg] = g == gg ? fmaxf(gmax[gg], m) : gmax[gg];
+    }
   }
-  amax = block_max(amax, red);
-  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (tid == 0) a.k_scale[(hv.row0 >> 6) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+  float inv[4];
+  if constexpr (LANE) {
+    const int w = tid >> 6;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float r = wave_max(gmax[g]);
+      if ((tid & 63) == 0) red[g][w] = r;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float r = red[g][0];
+#pragma unroll
+      for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[g][i]);
+      gmax[g] = r;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = (tid + u * kThreads) / vec_per_row;
+      const int g = lane_group_in_block(row & (kBlkK - 1));
+      float m = gmax[0];
+#pragma unroll
+      for (int gg = 1; gg < 4; ++gg) m = g == gg ? gmax[gg] : m;
+      inv[u] = m > 0.0f ? 127.0f / m : 0.0f;
+    }
+    if (tid < 4) {
+      float m = gmax[0];
+#pragma unroll
+      for (int gg = 1; gg < 4; ++gg) m = tid == gg ? gmax[gg] : m;
+      a.k_scale[(hv.row0 >> 4) + 4 * blk + tid] = m > 0.0f ? m / 127.0f : 0.0f;
+    }
+  } else {
+    amax = block_max(amax, red[0]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) inv[u] = amax > 0.0f ? 127.0f / amax : 0.0f;
+    if (tid == 0) a.k_scale[(hv.row0 >> 6) + blk] = amax > 0.0f ? amax / 127.0f : 0.0f;
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int vi = tid + u * kThreads;
@@ -280,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
     const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
     uint32_t w[2] = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv[u]) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
     *reinterpret_cast<v2i *>(a.k_i8 + (hv.row0 + blk * kBlkK + row) * D + c8) = out;
   }
@@ -374,9 +437,11 @@ static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
   const int gd = (bhk * D + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads), 0,
                      stream, a);
-  hipLaunchKernelGGL((k_qquant<DT, D>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
+  if (a.gran == 1) hipLaunchKernelGGL((k_qquant<DT, D, true>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_qquant<DT, D, false>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((k_kquant<DT, D>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
+  if (a.gran == 1) hipLaunchKernelGGL((k_kquant<DT, D, true>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_kquant<DT, D, false>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
 }
 
 template <int DT, int D>

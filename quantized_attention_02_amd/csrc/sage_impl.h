@@ -129,6 +129,7 @@ struct QuantQKArgs {
   int varlen;                           // packed batch: tables below, S unused
   SeqTable sq, sk;
   long long rows_q, rows_k;  // buffer rows per head (packed batch)
+  int gran;                  // 0: per-block scales, 1: per-lane (Q per token, K per 16-key group)
 };
 
 struct QuantVArgs {
@@ -156,6 +157,7 @@ struct AttnArgs {
   int varlen;  // packed batch: tables below, S = the longest query sequence
   SeqTable sq, sk;
   long long rows_q, rows_k;
+  int gran;  // scale granularity of q_scale / k_scale (as QuantQKArgs::gran)
 };
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);

@@ -43,13 +43,14 @@ def _inputs(w):
     return (q, k, v, cq, ck), dev, cud
 
 
-def _run(w, causal, pv, dev, cud):
+def _run(w, causal, pv, dev, cud, gran="block"):
     import torch
 
     import quantized_attention_02_amd as qa
 
     qd, kd, vd = dev
-    bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max(w.seqlens_q), max(max(w.seqlens_k), 1), pv)
+    bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max(w.seqlens_q), max(max(w.seqlens_k), 1), pv,
+                              qk_gran=gran)
     out = torch.full_like(qd, float("nan"))
     qa.attn_fwd_varlen(bufs, vd, out, cud[0], cud[1], causal, None, pv)
     torch.cuda.synchronize()
@@ -170,3 +171,37 @@ def test_varlen_full_size_sampled(pv):
             c, r = G.cos(g, ref), G.rel_l1(g, ref)
             print(f"{w.name} seq {b} (S={S}) head {h}: cos={c:.6f} rel_l1={r:.2e}")
             assert c >= COS_MIN and r <= REL_L1_MAX, (b, h, c, r)
+
+
+@pytest.mark.parametrize("w", [SMALL[2], SMALL[4]], ids=[SMALL[2].name, SMALL[4].name])
+def test_varlen_lane_granularity(w):
+    """Packed batches with lane granularity: codes bit-exact per sequence, output
+    within the bars of the oracle at the same granularity."""
+    import quantized_attention_02_amd as qa
+
+    (q, k, v, cq, ck), dev, cud = _inputs(w)
+    bufs, out = _run(w, True, "fp8", dev, cud, gran="lane")
+    dt = O.DTYPES[w.dtype]
+    qs, ks = bufs.q_scale.cpu().numpy(), bufs.k_scale.cpu().numpy()
+    for b in range(w.B):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        rq, rk = qa.varlen_row0(q0, b, 32), qa.varlen_row0(k0, b, 128)
+        for h in range(w.H):
+            _, rqs = O.quant_q_head(O.decode16(q[q0:q1, h], dt), 1)
+            assert np.array_equal(qs[h, rq:rq + q1 - q0].view(np.uint32), rqs.view(np.uint32)), (b, h)
+        for h in range(w.Hkv):
+            _, rks, _ = O.quant_k_head_lane(O.decode16(k[k0:k1, h], dt), True)
+            assert np.array_equal(ks[h, rk // 16:rk // 16 + rks.size].view(np.uint32), rks.view(np.uint32)), (b, h)
+    got = O.decode16(G.to_u16(out), dt)
+    ref = O.attn_varlen(q, k, v, cq, ck, dt, is_causal=True, tile_k=G.TILE_K["fp8"], gran="lane")
+    g_all, r_all = [], []
+    for b in range(w.B):
+        if ck[b + 1] == ck[b]:
+            continue
+        for h in range(w.H):
+            g_all.append(got[cq[b]:cq[b + 1], h])
+            r_all.append(ref[(b, h)])
+    g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
+    c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
+    print(f"{w.name} lane: cos={c:.6f} rel_l1={r:.2e}")
+    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
