@@ -64,7 +64,8 @@ def lib():
         L.orc_e4m3_encode.argtypes = [ctypes.c_float]
         for name in ("orc_decode16", "orc_encode16", "orc_e4m3_encode_n", "orc_int8_quant_block",
                      "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_k_head_lane",
-                     "orc_quant_v_head", "orc_qk_int32_head", "orc_attn_head_rows", "orc_attn_exact_head"):
+                     "orc_quant_v_head", "orc_quant_v_head_smooth", "orc_qk_int32_head", "orc_attn_head_rows",
+                     "orc_attn_exact_head"):
             getattr(L, name).restype = None
         L.orc_lane_group.restype = ctypes.c_int
         L.orc_lane_group.argtypes = [ctypes.c_int]
@@ -204,11 +205,18 @@ def quant_k_head_lane(kf: np.ndarray, smooth: bool = True):
     return codes, scales, mean
 
 
-def quant_v_head(vf: np.ndarray):
+def quant_v_head(vf: np.ndarray, smooth: bool = False):
+    """E4M3 codes + per-channel scales of V; with smooth, of V minus its channel
+    mean, which is returned as a third value."""
     vf = _f32(vf)
     S, D = vf.shape
     codes = np.empty((S, D), np.uint8)
     scales = np.empty(D, np.float32)
+    if smooth:
+        mean = np.empty(D, np.float32)
+        lib().orc_quant_v_head_smooth(_p(vf, ctypes.c_float), S, D, _p(codes, ctypes.c_uint8),
+                                      _p(scales, ctypes.c_float), _p(mean, ctypes.c_float))
+        return codes, scales, mean
     lib().orc_quant_v_head(_p(vf, ctypes.c_float), S, D, _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_float))
     return codes, scales
 
@@ -223,7 +231,7 @@ def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 
 def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
-                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False) -> np.ndarray:
+                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False, v_mean=None) -> np.ndarray:
     """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
 
     blk_q / blk_k: tokens per INT8 scale of Q / K (k_lane: K scales per lane group
@@ -243,9 +251,13 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     v8 = np.ascontiguousarray(v8 if v8 is not None else np.zeros((S, D), np.uint8), np.uint8)
     v_scale = _f32(v_scale if v_scale is not None else np.zeros(D, np.float32))
     vf = _f32(vf if vf is not None else np.zeros((S, D), np.float32))
+    vm = None if v_mean is None else _f32(v_mean)
+    if vm is not None and pv_mode != PV_FP8:
+        raise ValueError("V smoothing applies to the FP8 PV product only")
     lib().orc_attn_head_rows(_p(q8, ctypes.c_int8), _p(q_scale, ctypes.c_float), blk_q,
                              _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k, int(bool(k_lane)), tile_k,
-                             _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float), _p(vf, ctypes.c_float),
+                             _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float),
+                             None if vm is None else _p(vm, ctypes.c_float), _p(vf, ctypes.c_float),
                              in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
                              _p(rows, ctypes.c_int), rows.size, _p(out, ctypes.c_float))
     return out
@@ -317,8 +329,12 @@ def kv_head(h: int, H: int, Hkv: int) -> int:
 
 
 def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
-         heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block"):
+         heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block",
+         smooth_v=False):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
+
+    smooth_v (pv fp8 only): V minus its channel mean is quantised, and the mean
+    is added back to the output.
 
     gran: "block" (blk_q / blk_k tokens per scale) or "lane" (thread-level: one
     scale per Q token, one per 16-key lane group of K).
@@ -342,13 +358,16 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         vf = decode16(head(v, layout, b, hk), dtype)
         q8, qs = quant_q_head(qf, blk_q)
         k8, ks, _ = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
-        if pv_mode == PV_FP8:
+        vm = None
+        if pv_mode == PV_FP8 and smooth_v:
+            v8, vs, vm = quant_v_head(vf, True)
+        elif pv_mode == PV_FP8:
             v8, vs = quant_v_head(vf)
         else:
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
                                      sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k,
-                                     tile_k=tile_k, k_lane=lane)
+                                     tile_k=tile_k, k_lane=lane, v_mean=vm)
     return res
 
 
@@ -377,7 +396,8 @@ def seq_slices(cu_seqlens) -> list:
 
 
 def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
-                heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block"):
+                heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block",
+                smooth_v=False):
     """Quantized attention over a packed batch of sequences of different lengths
     ("Thư viện SageAttention" page, feature list: variable-length sequences through
     sageattn_varlen).
@@ -402,6 +422,6 @@ def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=No
         (q0, q1), (k0, k1) = sq[b], sk[b]
         one = attn(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype, "NHD", is_causal=is_causal,
                    sm_scale=sm_scale, pv_mode=pv_mode, heads=[(0, h)], rows=rows, blk_q=blk_q, blk_k=blk_k,
-                   tile_k=tile_k, smooth=smooth, gran=gran)
+                   tile_k=tile_k, smooth=smooth, gran=gran, smooth_v=smooth_v)
         res[(b, h)] = one[(0, h)]
     return res

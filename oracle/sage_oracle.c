@@ -271,6 +271,22 @@ void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scale
     }
 }
 
+/*
+ * Smoothed V ([SA2, SageAttention2方法]: an optional V smoothing for the FP8 PV
+ * product).  Reading: the same statistic as K smoothing -- the channel mean of V
+ * over the head's S tokens (orc_channel_mean) -- is subtracted, one fp32
+ * subtraction per element, and the result quantised per channel as above; the
+ * attention adds the mean back after normalising (softmax weights sum to 1).
+ */
+void orc_quant_v_head_smooth(const float *v, int S, int D, uint8_t *codes, float *scales, float *mean) {
+    size_t n = (size_t)S * D;
+    float *vs = (float *)malloc((n ? n : 1) * sizeof(float));
+    orc_channel_mean(v, S, D, mean);
+    for (size_t i = 0; i < n; ++i) vs[i] = v[i] - mean[i % D];
+    orc_quant_v_head(vs, S, D, codes, scales);
+    free(vs);
+}
+
 /* ===================================================================== */
 /* Attention                                                              */
 /* ===================================================================== */
@@ -311,7 +327,7 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  *   P8_n  = E4M3(p_n * 448)                 (static scale 1/448: p = 1 -> 448)
  *   inner = sum_n dec(P8_n) * dec(v8_n,d)   (fresh per key tile, rounded once to fp32)
  *   O_d   = alpha * O_d + inner_d                                    (fp32 buffer)
- *   out   = O_d * (dv_d / (448 * l))
+ *   out   = O_d * (dv_d / (448 * l))  (+ v_mean_d when V was smoothed, v_mean != NULL)
  * pv fp16 ([KAI, 2.1] sm80 row: INT8 QK^T, FP16 PV, fp32 accumulation):
  *   P_n   = fp16(p_n), V in fp16 (bf16 inputs rounded to fp16),
  *   O_d   = alpha * O_d + sum_n P_n * V_n,d;   out = O_d / l
@@ -321,7 +337,7 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  */
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
-                        const uint8_t *v8, const float *v_scale, const float *v,
+                        const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, float *out) {
     int ntile = (S + tile_k - 1) / tile_k;
@@ -387,6 +403,8 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                 for (int d = 0; d < D; ++d) o[d] = 0.0f;
             } else if (pv_mode == ORC_PV_FP8) {
                 for (int d = 0; d < D; ++d) o[d] = O[d] * (v_scale[d] / (448.0f * l));
+                if (v_mean)
+                    for (int d = 0; d < D; ++d) o[d] = o[d] + v_mean[d];
             } else {
                 for (int d = 0; d < D; ++d) o[d] = O[d] / l;
             }

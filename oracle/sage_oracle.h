@@ -60,12 +60,13 @@ int orc_lane_group(int n);
 void orc_quant_k_head_lane(const float *k, int S, int D, int smooth,
                            int8_t *codes, float *scales, float *mean);
 void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scales);
+void orc_quant_v_head_smooth(const float *v, int S, int D, uint8_t *codes, float *scales, float *mean);
 
 /* ---- attention (per head) ---------------------------------------------- */
 void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t *out);
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
-                        const uint8_t *v8, const float *v_scale, const float *v,
+                        const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, float *out);
 void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, int D,

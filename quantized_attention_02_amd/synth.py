@@ -16,8 +16,10 @@ Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this order
   1. Q, K, V base values ~ N(0, 1), float32, logical [B, H, S, D] (K, V: [B, Hkv, S, D]);
   2. the K bias c[h, d] ~ N(0, bias_sigma^2) per K head, shared over b and s;
   3. (outlier_p > 0) Bernoulli(outlier_p) masks for Q, then K;
-  4. (token_norm) per-token factors r ~ U(0.5, 2) drawn per (b, s) for Q, K, V.
-Application: x *= r (token norm), K += c, then masked entries of Q and K *= 20.
+  4. (token_norm) per-token factors r ~ U(0.5, 2) drawn per (b, s) for Q, K, V;
+  5. (v_bias_sigma > 0) a V bias c_v[h, d] ~ N(0, v_bias_sigma^2) per V head.
+Application: x *= r (token norm), K += c, V += c_v, then masked entries of Q and
+K *= 20.
 Then cast round-to-nearest-even to fp16 (numpy) or bf16 (torch CPU) and, for
 NHD, permute to [B, S, H, D].  Returned arrays are the raw uint16 codes.
 
@@ -51,6 +53,7 @@ class Workload:
     pv_modes: tuple = ("fp8",)
     seed: int = 42
     Hkv: int = 0  # K/V heads (grouped-query attention); 0: as many as Q
+    v_bias_sigma: float = 0.0  # per-channel V offset shared by all tokens (drawn last)
 
     @property
     def kv_heads(self) -> int:
@@ -109,6 +112,9 @@ def make_qkv(w: Workload, seed: int | None = None):
             r = rng.uniform(0.5, 2.0, size=(w.B, w.S)).astype(np.float32)
             x *= r[:, None, :, None]
     k += c[None, :, None, :]
+    if w.v_bias_sigma > 0:
+        cv = (rng.standard_normal((w.kv_heads, w.D), dtype=np.float32) * np.float32(w.v_bias_sigma)).astype(np.float32)
+        v += cv[None, :, None, :]
     if w.outlier_p > 0:
         q[mq] *= np.float32(20.0)
         k[mk] *= np.float32(20.0)
@@ -120,11 +126,12 @@ def make_qkv(w: Workload, seed: int | None = None):
     return tuple(out)
 
 
-def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0, token_norm=False, seed=0, Hkv=0):
+def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0, token_norm=False, seed=0, Hkv=0,
+           v_bias_sigma=0.0):
     """An ad-hoc workload (edge shapes in tests)."""
     kv = f"kv{Hkv}" if Hkv else ""
     return Workload(f"custom_b{B}h{H}{kv}s{S}d{D}", B, H, S, D, dtype, layout, bias_sigma, outlier_p, token_norm,
-                    seed=seed, Hkv=Hkv)
+                    seed=seed, Hkv=Hkv, v_bias_sigma=v_bias_sigma)
 
 
 def mixed_lengths(total: int, lo: int, hi: int, seed: int) -> tuple:

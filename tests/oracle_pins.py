@@ -655,4 +655,67 @@ def pin_lane_attention_uses_group_scales():
         assert cos(got, ref) >= 0.99999 and rel_l1(got, ref) < 2e-3, (causal, cos(got, ref), rel_l1(got, ref))
 
 
+# ------------------------------------------------------------------ V smoothing
+def pin_smooth_v_quant():
+    """Smoothed V: the mean is the channel mean, and the codes and scales are the
+    per-channel FP8 rule applied to V minus that mean (one fp32 subtraction)."""
+    _, _, vf = _rand_head(150, 64, seed=51)
+    vf = vf + np.float32(3.0)
+    v8, vs, vm = O.quant_v_head(vf, True)
+    assert np.array_equal(vm.view(np.uint32), O.channel_mean(vf).view(np.uint32))
+    r8, rs = O.quant_v_head((vf.astype(np.float32) - vm[None, :]).astype(np.float32))
+    assert np.array_equal(v8, r8) and np.array_equal(vs.view(np.uint32), rs.view(np.uint32))
+    # the scale now follows the spread around the mean, not the offset
+    assert vs.max() < O.quant_v_head(vf)[1].min()
+
+
+def pin_smooth_v_constant_channels():
+    """V equal for every token: smoothed codes and scales are 0 and the output
+    is that V row exactly, as in exact attention."""
+    S, D = 100, 64
+    qf, kf, _ = _rand_head(S, D, seed=52)
+    c = np.linspace(-3, 5, D).astype(np.float32)
+    vf = np.repeat(c[None, :], S, axis=0)
+    v8, vs, vm = O.quant_v_head(vf, True)
+    assert not v8.any() and not vs.any() and np.array_equal(vm, c)
+    q8, qs, k8, ks, _, _, _ = _quant_head(qf, kf, vf)
+    for causal in (False, True):
+        got = O.attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=F16, is_causal=causal, sm_scale=0.125,
+                               pv_mode=O.PV_FP8, v_mean=vm)
+        assert np.array_equal(got, np.repeat(c[None, :], S, axis=0)), causal
+
+
+def pin_smooth_v_shift_equivariance():
+    """On grid inputs, adding a per-channel constant c to V leaves the smoothed
+    codes and scales bit-identical and moves the output by c (up to the
+    rounding of the final addition)."""
+    S, D = 128, 64
+    rng = np.random.default_rng(53)
+    qf, kf, _ = _rand_head(S, D, seed=53)
+    vf = (rng.integers(-64, 65, size=(S, D)) / 16.0).astype(np.float32)
+    c = rng.integers(-8, 9, size=D).astype(np.float32)
+    a8, as_, am = O.quant_v_head(vf, True)
+    b8, bs, bm = O.quant_v_head(vf + c[None, :], True)
+    assert np.array_equal(a8, b8) and np.array_equal(as_, bs) and np.array_equal(bm, am + c)
+    q8, qs, k8, ks, _, _, _ = _quant_head(qf, kf, vf)
+    oa = O.attn_head_rows(q8, qs, k8, ks, a8, as_, vf, in_dtype=F16, is_causal=True, sm_scale=0.125,
+                          pv_mode=O.PV_FP8, v_mean=am)
+    ob = O.attn_head_rows(q8, qs, k8, ks, b8, bs, vf, in_dtype=F16, is_causal=True, sm_scale=0.125,
+                          pv_mode=O.PV_FP8, v_mean=bm)
+    assert np.allclose(ob - c[None, :], oa, rtol=0, atol=4 * 2.0 ** -20 * (1 + np.abs(c).max()))
+
+
+def pin_smooth_v_more_accurate_with_v_offsets():
+    """A per-channel V offset costs the FP8 V codes their resolution; smoothing
+    recovers it: closer to exact attention."""
+    w = synth.custom(1, 2, 512, 128, v_bias_sigma=6.0, seed=54)
+    q, k, v = synth.make_qkv(w)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    sm = O.attn(q, k, v, F16, "HND", smooth_v=True)
+    pl = O.attn(q, k, v, F16, "HND")
+    for hd in ex:
+        es, ep = rel_l1(sm[hd], ex[hd]), rel_l1(pl[hd], ex[hd])
+        assert es < 0.5 * ep, (hd, es, ep)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,8 @@ MUTANTS = [
      "int nvis = is_causal ? (i < S ? (i > 0 ? i : 1) : S) : S;"),
     ("fp16_pv_no_rounding", "pq[t] = round_f16(p[t]);", "pq[t] = p[t];"),
     ("fp8_p_not_quantised", "pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));", "pq[t] = p[t] * 448.0f;"),
+    ("smooth_v_mean_not_added", "o[d] = o[d] + v_mean[d];", "o[d] = o[d];"),
+    ("smooth_v_not_subtracted", "vs[i] = v[i] - mean[i % D];", "vs[i] = v[i];"),
     ("f16_decode_bias", "ldexp(1.0 + fr / 1024.0, ex - 15)", "ldexp(1.0 + fr / 1024.0, ex - 14)"),
 ]
 
