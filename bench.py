@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--workload", default=None)
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
+    p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
     p.add_argument("--qk-gran", default="block", choices=["block", "lane"],
                    help="INT8 scale granularity of Q and K: per block, or per token / 16-key lane group")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -181,7 +182,7 @@ def main():
         bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev, args.qk_gran)
 
         def quant():
-            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_gran=args.qk_gran)
+            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_gran=args.qk_gran, smooth_v=args.smooth_v)
 
         def attn():
             qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)
@@ -189,7 +190,7 @@ def main():
         bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_gran)
 
         def quant():
-            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_gran=args.qk_gran)
+            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_gran=args.qk_gran, smooth_v=args.smooth_v)
 
         def attn():
             qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
@@ -242,10 +243,10 @@ def main():
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,
                     "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv,
-                    "qk_gran": args.qk_gran} if varlen else
+                    "qk_gran": args.qk_gran, "smooth_v": args.smooth_v} if varlen else
                    {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
                     "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv,
-                    "qk_gran": args.qk_gran}),
+                    "qk_gran": args.qk_gran, "smooth_v": args.smooth_v}),
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv), 1), "unit": "TFLOP/s",

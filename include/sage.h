@@ -57,6 +57,8 @@
  *           other, each tile stored channel-major; inside a tile, byte p of
  *           channel d holds key  SAGE_VPOS_KEY(p)  of that tile (keys >= S are 0).
  *   v_scale float [B][H_kv][D]     one scale per channel.
+ *   v_mean  float [B][H_kv][D]     V smoothing only: the channel means subtracted from V
+ *                                  before quantisation (same size as v_scale).
  *   out: same dtype and layout (HND or NHD) as q.
  */
 #ifndef SAGE_H
@@ -140,12 +142,15 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
  *   code = E4M3(V[s][d] * (448 / amax_d)), round to nearest even, |x| clamped to 448;
  *   an all-zero channel has scale 0 and codes 0.
  * H is the number of V heads (H_kv of the other entry points).
- * Writes v_fp8 in the tiled layout above and v_scale.  While the call's
- * launches run, v_fp8 and v_scale hold intermediate per-channel maxima, so
- * both are defined only after the stream has passed the call.
+ * v_mean non-NULL selects V smoothing ([SA2] SageAttention2方法, optional smooth V):
+ *   v_mean[d] = fp32( (sum_s V[s][d], binary64) / S ), the rule above is applied to
+ *   V[s][d] - v_mean[d] (one fp32 subtraction), and sage_attn_fwd adds v_mean back.
+ * Writes v_fp8 in the tiled layout above, v_scale (and v_mean).  While the call's
+ * launches run, v_fp8 and v_scale hold intermediate per-channel statistics, so
+ * they are defined only after the stream has passed the call.
  */
 int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8,
-                 float *v_scale, void *stream);
+                 float *v_scale, float *v_mean, void *stream);
 
 /*
  * Fused quantized attention ([SA2]; [KAI] 2.1; [GUIDE] 五分钟跑通, 性能调优实战).
@@ -158,17 +163,20 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  *   m' = max(m, max_n s_n);  alpha = exp(m - m');  p_n = exp(s_n - m');  l = alpha*l + sum p_n
  *   pv fp8 : P = E4M3(448 * p_n) (static scale), inner = P . V_fp8 (FP8 MFMA, fresh per tile),
  *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
+ *            (+ v_mean[d] when v_mean is non-NULL: V was smoothed by sage_quant_v)
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
  * q_i8 .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
- * sage_quant_v.  pv fp16: v = the original V tensor (dtype, layout, H_kv heads),
- * v_scale = NULL (bf16 V is rounded to fp16).  out: dtype tensor in `layout`, shape
+ * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the
+ * original V tensor (dtype, layout, H_kv heads), v_scale = v_mean = NULL (bf16 V is
+ * rounded to fp16).  out: dtype tensor in `layout`, shape
  * of q.  Query head h reads K/V head h / (H / H_kv).
  * is_causal in {0, 1}; sm_scale finite and > 0 (the usual choice is 1/sqrt(D)).
  * pv fp16 with NHD layout additionally needs H_kv * D * 2 * SAGE_KV_PAD < 2^31
  * (128-token slices of V are addressed through a 32-bit byte range).
  */
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                  const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S,
+                  const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H,
+                  int H_kv, int S,
                   int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream);
 
 /*
@@ -180,7 +188,8 @@ int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, 
  * written as by sage_attn_fwd.
  */
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
+                          const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
+                          int H, int H_kv,
                           int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran,
                           int b, int h, int32_t *qk, void *stream);
 
@@ -227,14 +236,15 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
                                 int max_seqlen_q, int max_seqlen_k, int D, int qk_gran, int8_t *q_i8,
                                 float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean, void *stream);
 
-/* sage_quant_v for a packed batch (v: [total_k][H_kv][D]). */
+/* sage_quant_v for a packed batch (v: [total_k][H_kv][D]); v_mean as there. */
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
-                        int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, void *stream);
+                        int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, float *v_mean, void *stream);
 
 /* sage_attn_fwd for a packed batch.  pv fp16: v = the original [total_k][H_kv][D]
- * V, v_scale = NULL.  out: [total_q][H][D] in dtype. */
+ * V, v_scale = v_mean = NULL.  out: [total_q][H][D] in dtype. */
 int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                         const void *v, const float *v_scale, void *out, int dtype, const int32_t *cu_seqlens_q,
+                         const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
+                         const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
                          int qk_gran, void *stream);

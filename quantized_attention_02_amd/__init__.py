@@ -54,15 +54,15 @@ def lib() -> ctypes.CDLL:
         L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
         L.sage_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 7
         L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 5 + [c_void_p]
-        L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p, c_void_p, c_void_p]
-        attn = [c_void_p] * 7 + [c_int] * 8 + [c_float, c_int, c_int]
+        L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
+        attn = [c_void_p] * 8 + [c_int] * 8 + [c_float, c_int, c_int]
         L.sage_attn_fwd.argtypes = attn + [c_void_p]
         L.sage_attn_fwd_dump_qk.argtypes = attn + [c_int, c_int, c_void_p, c_void_p]
         L.sage_varlen_buffer_sizes.argtypes = [c_int] * 7 + [c_size_p] * 7
         L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + \
             [c_void_p] * 5 + [c_void_p]
-        L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 3
-        L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 7 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
+        L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
+        L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 8 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
             [c_int, c_float, c_int, c_int, c_void_p]
         L.sage_status_str.argtypes = [c_int]
         L.sage_status_str.restype = ctypes.c_char_p
@@ -107,20 +107,20 @@ def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_gran, q_i8, q
                                       k_mean, stream)
 
 
-def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream):
-    return lib().sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, stream)
+def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream):
+    return lib().sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream)
 
 
-def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
+def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout, is_causal,
                   sm_scale, pv_mode, qk_gran, stream):
-    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout,
+    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
                                is_causal, sm_scale, pv_mode, qk_gran, stream)
 
 
-def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                          sm_scale, pv_mode, qk_gran, b, h, qk, stream):
-    return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D,
-                                       layout, is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, stream)
+def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
+                          is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, stream):
+    return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S,
+                                       D, layout, is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, stream)
 
 
 def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_gran=0):
@@ -138,15 +138,15 @@ def sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H
                                              k_mean, stream)
 
 
-def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale, stream):
+def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale, v_mean, stream):
     return lib().sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale,
-                                     stream)
+                                     v_mean, stream)
 
 
-def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv,
-                         total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode, qk_gran,
-                         stream):
-    return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, cu_seqlens_q,
+def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q, cu_seqlens_k, B,
+                         H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode,
+                         qk_gran, stream):
+    return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q,
                                       cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
                                       is_causal, sm_scale, pv_mode, qk_gran, stream)
 
@@ -213,6 +213,8 @@ class Quantized:
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((B, H_kv, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.smooth_v = False  # set by quantize: whether v_fp8 holds V minus v_mean
 
 
 def _kv_heads(q, k, v, tensor_layout):
@@ -227,10 +229,13 @@ def _kv_heads(q, k, v, tensor_layout):
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
-             qk_gran="block") -> Quantized:
+             qk_gran="block", smooth_v=False) -> Quantized:
     """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors.
     k and v may have fewer heads than q (grouped-query attention); qk_gran "block"
-    or "lane" (one scale per Q token and per 16-key lane group of K)."""
+    or "lane" (one scale per Q token and per 16-key lane group of K); smooth_v
+    (pv fp8): quantise V minus its channel mean."""
+    if smooth_v and pv_mode != "fp8":
+        raise ValueError("smooth_v applies to pv_mode='fp8' only")
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
     H_kv = _kv_heads(q, k, v, tensor_layout)
@@ -246,9 +251,10 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
                                 bufs.q_i8.data_ptr(),
                                 bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
                                 bufs.k_mean.data_ptr(), st), "sage_smooth_quant_qk")
+    bufs.smooth_v = bool(smooth_v)
     if pv_mode == "fp8":
         _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
-                            st), "sage_quant_v")
+                            bufs.v_mean.data_ptr() if smooth_v else None, st), "sage_quant_v")
     return bufs
 
 
@@ -267,8 +273,9 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     pv = PV[pv_mode]
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
+    vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
     args = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs,
-            out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.gran)
+            vm, out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.gran)
     if dump_head is None:
         _check(sage_attn_fwd(*args, _stream()), "sage_attn_fwd")
     else:
@@ -277,11 +284,12 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     return out
 
 
-def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_gran="block"):
+def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_gran="block",
+             smooth_v=False):
     """Quantized attention: same shape, dtype and layout out as q."""
     import torch
 
-    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_gran=qk_gran)
+    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_gran=qk_gran, smooth_v=smooth_v)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
 
@@ -315,6 +323,8 @@ class QuantizedVarlen:
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((H_kv, rk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.smooth_v = False
 
 
 def _cu(t, name):
@@ -326,7 +336,7 @@ def _cu(t, name):
 
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
-                    bufs: QuantizedVarlen | None = None, qk_gran="block") -> QuantizedVarlen:
+                    bufs: QuantizedVarlen | None = None, qk_gran="block", smooth_v=False) -> QuantizedVarlen:
     """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode) on a packed
     batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
@@ -355,9 +365,13 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                        bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                        bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
            "sage_smooth_quant_qk_varlen")
+    if smooth_v and pv_mode != "fp8":
+        raise ValueError("smooth_v applies to pv_mode='fp8' only")
+    bufs.smooth_v = bool(smooth_v)
     if pv_mode == "fp8":
         _check(sage_quant_v_varlen(v.data_ptr(), dt, ck.data_ptr(), B, H_kv, total_k, bufs.max_seqlen_k, D,
-                                   bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), st), "sage_quant_v_varlen")
+                                   bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
+                                   bufs.v_mean.data_ptr() if smooth_v else None, st), "sage_quant_v_varlen")
     return bufs
 
 
@@ -374,8 +388,9 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
+    vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
     _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
-                                bufs.k_scale.data_ptr(), vptr, vs, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
+                                bufs.k_scale.data_ptr(), vptr, vs, vm, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
                                 ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k, bufs.max_seqlen_q,
                                 bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, bufs.gran, _stream()),
            "sage_attn_fwd_varlen")
@@ -383,12 +398,13 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
 
 
 def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False, sm_scale=None,
-                    pv_mode="fp8", qk_gran="block"):
+                    pv_mode="fp8", qk_gran="block", smooth_v=False):
     """Quantized attention over a packed batch of sequences ("SageAttention: Thư viện
     Attention lượng tử hóa" page, feature list: sageattn_varlen):
     q [total_q, H, D], k / v [total_k, H_kv, D]; returns [total_q, H, D]."""
     import torch
 
-    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_gran=qk_gran)
+    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_gran=qk_gran,
+                           smooth_v=smooth_v)
     out = torch.empty_like(q)
     return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)

@@ -79,7 +79,8 @@ int check_device() {
 int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
 
 int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S,
+                const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H,
+                int H_kv, int S,
                 int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, int dump_b,
                 int dump_h, int32_t *qk, bool dump, void *stream) {
   int rc = check_shape(B, H, S, D);
@@ -92,6 +93,8 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;  // smoothing is for the FP8 V codes
+  if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
@@ -113,6 +116,7 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   a.k_scale = k_scale;
   a.v = v;
   a.v_scale = v_scale;
+  a.v_mean = v_mean;
   a.out = out;
   a.dump = qk;
   a.dump_bh = dump ? dump_b * H + dump_h : -1;
@@ -203,18 +207,20 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
 }
 
 int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8, float *v_scale,
-                 void *stream) {
+                 float *v_mean, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!v || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4) || (v_mean && !aligned(v_mean, 4)))
+    return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantVArgs a;
   memset(&a, 0, sizeof a);
   a.v = v;
   a.v_fp8 = v_fp8;
   a.v_scale = v_scale;
+  a.v_mean = v_mean;
   a.B = B;
   a.H = H;
   a.S = S;
@@ -226,18 +232,18 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
 }
 
 int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale, const void *v,
-                  const float *v_scale, void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout,
-                  int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream) {
-  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                     sm_scale, pv_mode, qk_gran, 0, 0, nullptr, false, stream);
+                  const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H, int H_kv, int S,
+                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream) {
+  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
+                     is_causal, sm_scale, pv_mode, qk_gran, 0, 0, nullptr, false, stream);
 }
 
 int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                          const void *v, const float *v_scale, void *out, int dtype, int B, int H, int H_kv,
-                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran,
-                          int b, int h, int32_t *qk, void *stream) {
-  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                     sm_scale, pv_mode, qk_gran, b, h, qk, true, stream);
+                          const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
+                          int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode,
+                          int qk_gran, int b, int h, int32_t *qk, void *stream) {
+  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
+                     is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, true, stream);
 }
 
 // ---- packed variable-length batches
@@ -309,12 +315,13 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
 }
 
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
-                        int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, void *stream) {
+                        int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, float *v_mean, void *stream) {
   int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D, SAGE_GRAN_BLOCK);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (!v || !cu_seqlens_k || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4) || !aligned(cu_seqlens_k, 4))
+  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4) || !aligned(cu_seqlens_k, 4) ||
+      (v_mean && !aligned(v_mean, 4)))
     return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantVArgs a;
@@ -322,6 +329,7 @@ int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, i
   a.v = v;
   a.v_fp8 = v_fp8;
   a.v_scale = v_scale;
+  a.v_mean = v_mean;
   a.B = B;
   a.H = H_kv;
   a.S = max_seqlen_k;
@@ -336,7 +344,8 @@ int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, i
 }
 
 int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
-                         const void *v, const float *v_scale, void *out, int dtype, const int32_t *cu_seqlens_q,
+                         const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
+                         const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
                          int qk_gran, void *stream) {
@@ -349,6 +358,8 @@ int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t 
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
     return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;
+  if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
@@ -364,6 +375,7 @@ int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t 
   a.k_scale = k_scale;
   a.v = v;
   a.v_scale = v_scale;
+  a.v_mean = v_mean;
   a.out = out;
   a.dump = nullptr;
   a.dump_bh = -1;

@@ -281,6 +281,7 @@ k_attn(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
+  __shared__ __attribute__((aligned(16))) float vmn[D];  // its channel means when V was smoothed
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
@@ -581,7 +582,10 @@ k_attn(const AttnArgs a) {
     }
   };
 
-  if (PV == 0 && tid < D) vsc[tid] = a.v_scale[(long long)bhk * D + tid];
+  if (PV == 0 && tid < D) {
+    vsc[tid] = a.v_scale[(long long)bhk * D + tid];
+    vmn[tid] = a.v_mean ? a.v_mean[(long long)bhk * D + tid] : 0.0f;
+  }
 
   // ---- main loop: tile j is computed from buffer j % NBUF while tiles
   //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next
@@ -625,6 +629,13 @@ k_attn(const AttnArgs a) {
         o[1] = O[c][4 * g + 1] * (vs.y * rl);
         o[2] = O[c][4 * g + 2] * (vs.z * rl);
         o[3] = O[c][4 * g + 3] * (vs.w * rl);
+        if (a.v_mean) {  // smoothed V: add the channel means back
+          const float4 vm = *reinterpret_cast<const float4 *>(vmn + d0);
+          o[0] += vm.x;
+          o[1] += vm.y;
+          o[2] += vm.z;
+          o[3] += vm.w;
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = O[c][4 * g + i] * rl;

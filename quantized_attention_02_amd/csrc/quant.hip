@@ -352,10 +352,86 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
 // ---------------------------------------------------------------------------
 // V, four short launches:
 //   k_vamax_part   per (head, chunk): channel abs-max partials -> v_fp8 region
+//                  (smoothing: k_vstats_part, channel sum, max and min)
 //   k_vamax        per (head, channel): v_scale <- amax (held there until the end)
+//                  (smoothing: v_mean <- mean, v_scale <- amax of V - mean)
 //   k_vconvert     per (head, 64-key tile): E4M3 codes in the tiled key order
 //   k_vscale       per (head, channel): v_scale <- amax / 448
+// V smoothing ("SageAttention2" summary, SageAttention2方法: optional smooth V)
+// quantises V - mean with mean = the channel mean over the head's tokens (the
+// K-smoothing statistic).  Its abs-max needs no second pass over V: fp32
+// subtraction is monotonic and symmetric, so max_s |fl(V[s] - mean)| =
+// max(fl(max V - mean), fl(mean - min V)).
 // ---------------------------------------------------------------------------
+// Channel sum (binary64), max and min of one chunk -> partials at 16 D bytes
+// per chunk: [D doubles | D floats | D floats].
+template <int DT, int D>
+__device__ inline void chunk_stats(const uint16_t *x, const Seg &hv, int chunk, uint8_t *partials) {
+  using M = ChunkMap<D>;
+  __shared__ double psum[M::R][D];
+  __shared__ float pmax[M::R][D], pmin[M::R][D];
+  const int tid = threadIdx.x, g = tid % M::G, r = tid / M::G;
+  const int S = hv.S;
+  const int ct = chunk_tokens(S);
+  const int s_end = min(S, (chunk + 1) * ct);
+  double sum[8];
+  float mx[8], mn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    sum[i] = 0.0;
+    mx[i] = -INFINITY;
+    mn[i] = INFINITY;
+  }
+  for (int s0 = chunk * ct + r; s0 < s_end; s0 += M::R * M::kUnroll) {
+    float v[M::kUnroll][8];
+    bool ok[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int s = s0 + u * M::R;
+      ok[u] = s < s_end;
+      if (ok[u]) load8<DT>(x + hv.base + (long long)s * hv.stride + 8 * g, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u)
+      if (ok[u])
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sum[i] += (double)v[u][i];
+          mx[i] = fmaxf(mx[i], v[u][i]);
+          mn[i] = fminf(mn[i], v[u][i]);
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    psum[r][8 * g + i] = sum[i];
+    pmax[r][8 * g + i] = mx[i];
+    pmin[r][8 * g + i] = mn[i];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double t = psum[0][tid];
+    float a = pmax[0][tid], b = pmin[0][tid];
+    for (int rr = 1; rr < M::R; ++rr) {
+      t += psum[rr][tid];
+      a = fmaxf(a, pmax[rr][tid]);
+      b = fminf(b, pmin[rr][tid]);
+    }
+    uint8_t *base = partials + (long long)chunk * 16 * D;
+    reinterpret_cast<double *>(base)[tid] = t;
+    reinterpret_cast<float *>(base + 8 * D)[tid] = a;
+    reinterpret_cast<float *>(base + 12 * D)[tid] = b;
+  }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_vstats_part(const QuantVArgs a) {
+  const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
+  if (chunk >= n_chunks(sg.S)) return;
+  chunk_stats<DT, D>((const uint16_t *)a.v, sg, chunk, a.v_fp8 + sg.row0 * D);
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_vamax_part(const QuantVArgs a) {
   const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
@@ -371,8 +447,23 @@ __global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) {
   if (i >= (long long)a.B * a.H * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
-  const float *part = reinterpret_cast<const float *>(a.v_fp8 + sg.row0 * D);
   const int nch = n_chunks(sg.S);
+  if (a.v_mean) {  // smoothing: combine sums, maxima and minima
+    const uint8_t *base = a.v_fp8 + sg.row0 * D;
+    double t = 0.0;
+    float hi = -INFINITY, lo = INFINITY;
+    for (int c = 0; c < nch; ++c) {
+      const uint8_t *pc = base + (long long)c * 16 * D;
+      t += reinterpret_cast<const double *>(pc)[d];
+      hi = fmaxf(hi, reinterpret_cast<const float *>(pc + 8 * D)[d]);
+      lo = fminf(lo, reinterpret_cast<const float *>(pc + 12 * D)[d]);
+    }
+    const float mean = sg.S > 0 ? (float)(t / (double)sg.S) : 0.0f;
+    a.v_mean[i] = mean;
+    a.v_scale[i] = sg.S > 0 ? fmaxf(hi - mean, mean - lo) : 0.0f;
+    return;
+  }
+  const float *part = reinterpret_cast<const float *>(a.v_fp8 + sg.row0 * D);
   float v[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0f;
@@ -394,11 +485,12 @@ __global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
   const Seg hv = v_seg<D>(a, bh / a.H, bh % a.H);
   if (t >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's tiles
   const uint16_t *v = (const uint16_t *)a.v;
-  float inv[8];
+  float inv[8], mean[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float m = a.v_scale[(long long)bh * D + 8 * g + i];  // the channel's amax at this point
     inv[i] = m > 0.0f ? 448.0f / m : 0.0f;
+    mean[i] = a.v_mean ? a.v_mean[(long long)bh * D + 8 * g + i] : 0.0f;
   }
   float x[4][8];
 #pragma unroll
@@ -406,6 +498,9 @@ __global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
     const int s = t * kBlkK + 4 * q + k;
     if (s < hv.S) {
       load8<DT>(v + hv.base + (long long)s * hv.stride + 8 * g, x[k]);
+      if (a.v_mean)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[k][i] = x[k][i] - mean[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[k][i] = 0.0f;
@@ -448,8 +543,9 @@ template <int DT, int D>
 static void launch_v(const QuantVArgs &a, hipStream_t stream) {
   const int bh = a.B * a.H;
   const int gd = (bh * D + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((k_vamax_part<DT, D>), dim3(bh * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads),
-                     0, stream, a);
+  const dim3 parts(bh * chunk_grid(a.varlen ? a.sk.max_len : a.S));
+  if (a.v_mean) hipLaunchKernelGGL((k_vstats_part<DT, D>), parts, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_vamax_part<DT, D>), parts, dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_vamax<D>), dim3(gd), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_vconvert<DT, D>), dim3(bh * a.nk), dim3(2 * D), 0, stream, a);
   hipLaunchKernelGGL((k_vscale<D>), dim3(gd), dim3(kThreads), 0, stream, a);

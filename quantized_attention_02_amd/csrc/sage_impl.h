@@ -136,6 +136,7 @@ struct QuantVArgs {
   const void *v;
   uint8_t *v_fp8;
   float *v_scale;
+  float *v_mean;  // V smoothing: channel means out (nullptr: no smoothing)
   int B, H, S, D, layout, dtype;
   int nk;  // 64-key tiles per head (grid extent)
   int varlen;
@@ -148,6 +149,7 @@ struct AttnArgs {
   const float *q_scale, *k_scale;
   const void *v;
   const float *v_scale;
+  const float *v_mean;  // smoothed V: channel means added to the output (nullptr: none)
   void *out;
   int32_t *dump;
   int dump_bh;

@@ -75,19 +75,22 @@ def test_vpos_key_is_a_permutation():
 P = 1 << 12
 GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, H_kv=2, S=100, D=64, layout=0, qk_gran=0, q_i8=P, q_scale=P, k_i8=P,
                k_scale=P, k_mean=P, stream=None)
-GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, stream=None)
-GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, out=P, dtype=0, B=1, H=2, H_kv=2, S=100,
+GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, v_mean=None, stream=None)
+GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, out=P, dtype=0, B=1, H=2, H_kv=2,
+                 S=100,
                  D=64, layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, qk_gran=0, stream=None)
 
 BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict(q_scale=P + 2), dict(dtype=2),
           dict(layout=-1), dict(B=0), dict(H=-1), dict(S=0), dict(D=32), dict(D=256), dict(S=(1 << 20) + 1),
           dict(B=1 << 9, H=1 << 8, H_kv=1 << 8), dict(H_kv=0), dict(H_kv=3), dict(H=3, H_kv=2), dict(H_kv=-2),
           dict(qk_gran=2), dict(qk_gran=-1)]
-BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80)]
+BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80),
+         dict(v_mean=P + 2)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
             dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
             dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
             dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_gran=3),
+            dict(v_mean=P + 1), dict(pv_mode=1, v_scale=None, v_mean=P),  # smoothing is for the FP8 V codes
             # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
             dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
 
@@ -155,6 +158,8 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_qk(H=8, H_kv=2) == qa.SAGE_ERR_NO_DEVICE
     assert _call_qk(qk_gran=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(qk_gran=1) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_v(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v() == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn() == qa.SAGE_ERR_NO_DEVICE
@@ -193,14 +198,18 @@ def test_varlen_buffer_sizes():
 
 GOOD_QK_VL = dict(q=P, k=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4, H_kv=2, total_q=100, total_k=200, max_q=50,
                   max_k=90, D=64, qk_gran=1, q_i8=P, q_scale=P, k_i8=P, k_scale=P, k_mean=P, stream=None)
-GOOD_V_VL = dict(v=P, dtype=1, cu_k=P, B=3, H_kv=2, total_k=200, max_k=90, D=128, v_fp8=P, v_scale=P, stream=None)
-GOOD_ATTN_VL = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, out=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4,
+GOOD_V_VL = dict(v=P, dtype=1, cu_k=P, B=3, H_kv=2, total_k=200, max_k=90, D=128, v_fp8=P, v_scale=P, v_mean=P,
+                 stream=None)
+GOOD_ATTN_VL = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=P, out=P, dtype=0, cu_q=P, cu_k=P,
+                    B=3, H=4,
                     H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90, D=64, is_causal=1, sm_scale=0.125,
                     pv_mode=0, qk_gran=0, stream=None)
 BAD_QK_VL = [dict(cu_q=None), dict(cu_k=P + 2), dict(B=0), dict(H_kv=3), dict(total_q=-1), dict(max_q=0),
              dict(max_k=(1 << 20) + 1), dict(D=32), dict(dtype=3), dict(q=None), dict(k_i8=P + 1), dict(qk_gran=2)]
-BAD_V_VL = [dict(cu_k=None), dict(v=P + 8), dict(max_k=0), dict(total_k=-3), dict(H_kv=0), dict(v_scale=None)]
+BAD_V_VL = [dict(cu_k=None), dict(v=P + 8), dict(max_k=0), dict(total_k=-3), dict(H_kv=0), dict(v_scale=None),
+            dict(v_mean=P + 2)]
 BAD_ATTN_VL = [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P + 1), dict(is_causal=3), dict(pv_mode=5), dict(qk_gran=7),
+               dict(v_mean=P + 3), dict(pv_mode=1, v_scale=None),
                dict(sm_scale=0.0), dict(v_scale=None), dict(out=P + 4), dict(H_kv=3), dict(max_q=0), dict(B=-1),
                # pv fp16 reads 128-token slices of V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
                dict(pv_mode=1, v_scale=None, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
@@ -226,4 +235,5 @@ def test_valid_varlen_arguments_without_a_device_report_no_device():
     assert qa.sage_smooth_quant_qk_varlen(*GOOD_QK_VL.values()) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_quant_v_varlen(*GOOD_V_VL.values()) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_attn_fwd_varlen(*GOOD_ATTN_VL.values()) == qa.SAGE_ERR_NO_DEVICE
-    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "pv_mode": 1, "v_scale": None}.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "pv_mode": 1, "v_scale": None, "v_mean": None}.values()) == \
+        qa.SAGE_ERR_NO_DEVICE
