@@ -62,10 +62,14 @@ def lib():
         L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e2m1_decode.restype = ctypes.c_float
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_e2m1_encode.argtypes = [ctypes.c_float]
         for name in ("orc_decode16", "orc_encode16", "orc_e4m3_encode_n", "orc_int8_quant_block",
                      "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_k_head_lane",
                      "orc_quant_v_head", "orc_quant_v_head_smooth", "orc_qk_int32_head", "orc_attn_head_rows",
-                     "orc_attn_exact_head"):
+                     "orc_attn_exact_head", "orc_mxfp4_quant_rows", "orc_quant_k_head_mxfp4", "orc_qk_mxfp4_rows"):
             getattr(L, name).restype = None
         L.orc_lane_group.restype = ctypes.c_int
         L.orc_lane_group.argtypes = [ctypes.c_int]
@@ -205,6 +209,50 @@ def quant_k_head_lane(kf: np.ndarray, smooth: bool = True):
     return codes, scales, mean
 
 
+def e2m1_decode(codes) -> np.ndarray:
+    codes = np.asarray(codes, np.uint8)
+    return np.array([lib().orc_e2m1_decode(int(c)) for c in codes.ravel()], np.float32).reshape(codes.shape)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    x = np.asarray(x, np.float32)
+    return np.array([lib().orc_e2m1_encode(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def quant_mxfp4_rows(xf: np.ndarray):
+    """MXFP4 of each row: (E2M1 codes [S, D] one per byte, E8M0 scales [S, D / 32])."""
+    xf = _f32(xf)
+    S, D = xf.shape
+    codes = np.empty((S, D), np.uint8)
+    e8m0 = np.empty((S, D // 32), np.uint8)
+    lib().orc_mxfp4_quant_rows(_p(xf, ctypes.c_float), S, D, _p(codes, ctypes.c_uint8), _p(e8m0, ctypes.c_uint8))
+    return codes, e8m0
+
+
+def quant_k_head_mxfp4(kf: np.ndarray, smooth: bool = True):
+    """K for the FP4 product: (codes, e8m0, mean) of K minus its channel mean."""
+    kf = _f32(kf)
+    S, D = kf.shape
+    codes = np.empty((S, D), np.uint8)
+    e8m0 = np.empty((S, D // 32), np.uint8)
+    mean = np.empty(D, np.float32)
+    lib().orc_quant_k_head_mxfp4(_p(kf, ctypes.c_float), S, D, int(smooth), _p(codes, ctypes.c_uint8),
+                                 _p(e8m0, ctypes.c_uint8), _p(mean, ctypes.c_float))
+    return codes, e8m0, mean
+
+
+def qk_mxfp4_rows(q4, qe, k4, ke, rows=None) -> np.ndarray:
+    """fp32 Q K^T of MXFP4 rows (exact dot products, rounded once): [len(rows), S_k]."""
+    q4, qe, k4, ke = (np.ascontiguousarray(a, np.uint8) for a in (q4, qe, k4, ke))
+    Sq, D = q4.shape
+    S = k4.shape[0]
+    rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    out = np.empty((rows.size, S), np.float32)
+    lib().orc_qk_mxfp4_rows(_p(q4, ctypes.c_uint8), _p(qe, ctypes.c_uint8), _p(k4, ctypes.c_uint8),
+                            _p(ke, ctypes.c_uint8), S, D, _p(rows, ctypes.c_int), rows.size, _p(out, ctypes.c_float))
+    return out
+
+
 def quant_v_head(vf: np.ndarray, smooth: bool = False):
     """E4M3 codes + per-channel scales of V; with smooth, of V minus its channel
     mean, which is returned as a third value."""
@@ -231,13 +279,15 @@ def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 
 def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
-                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False, v_mean=None) -> np.ndarray:
+                   pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False, v_mean=None,
+                   qk=None) -> np.ndarray:
     """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
 
     blk_q / blk_k: tokens per INT8 scale of Q / K (k_lane: K scales per lane group
     instead of blocks, as quant_k_head_lane makes them); tile_k: keys per online-softmax
     tile (the two-level accumulation folds once per tile).  The query rows (q8)
-    and the keys (k8, v8, vf) may differ in number."""
+    and the keys (k8, v8, vf) may differ in number.  qk: fp32 Q K^T of the FP4
+    product for these rows (qk_mxfp4_rows); then q8 .. k_scale are not used."""
     Sq, D = q8.shape
     S = k8.shape[0]  # keys
     rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
@@ -254,12 +304,18 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     vm = None if v_mean is None else _f32(v_mean)
     if vm is not None and pv_mode != PV_FP8:
         raise ValueError("V smoothing applies to the FP8 PV product only")
+    qkr = None
+    if qk is not None:
+        qkr = np.ascontiguousarray(qk, np.float32)
+        if qkr.shape != (rows.size, S):
+            raise ValueError("qk must be [len(rows), S_k]")
     lib().orc_attn_head_rows(_p(q8, ctypes.c_int8), _p(q_scale, ctypes.c_float), blk_q,
                              _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k, int(bool(k_lane)), tile_k,
                              _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float),
                              None if vm is None else _p(vm, ctypes.c_float), _p(vf, ctypes.c_float),
                              in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
-                             _p(rows, ctypes.c_int), rows.size, _p(out, ctypes.c_float))
+                             _p(rows, ctypes.c_int), rows.size, None if qkr is None else _p(qkr, ctypes.c_float),
+                             _p(out, ctypes.c_float))
     return out
 
 
@@ -330,8 +386,11 @@ def kv_head(h: int, H: int, Hkv: int) -> int:
 
 def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
          heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block",
-         smooth_v=False):
+         smooth_v=False, qk_format="int8"):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
+
+    qk_format "fp4": Q and K - mean in MXFP4 (E2M1 with an E8M0 scale per 32
+    channels of a token) instead of INT8 blocks; gran is then not used.
 
     smooth_v (pv fp8 only): V minus its channel mean is quantised, and the mean
     is added back to the output.
@@ -356,8 +415,18 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         qf = decode16(head(q, layout, b, h), dtype)
         kf = decode16(head(k, layout, b, hk), dtype)
         vf = decode16(head(v, layout, b, hk), dtype)
-        q8, qs = quant_q_head(qf, blk_q)
-        k8, ks, _ = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
+        qk = None
+        if qk_format == "fp4":
+            q4, qe = quant_mxfp4_rows(qf)
+            k4, ke, _ = quant_k_head_mxfp4(kf, smooth)
+            qk = qk_mxfp4_rows(q4, qe, k4, ke, rows)
+            q8, qs = np.zeros(qf.shape, np.int8), np.zeros(1, np.float32)
+            k8, ks = np.zeros(kf.shape, np.int8), np.zeros(1, np.float32)
+        elif qk_format == "int8":
+            q8, qs = quant_q_head(qf, blk_q)
+            k8, ks, _ = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
+        else:
+            raise ValueError(qk_format)
         vm = None
         if pv_mode == PV_FP8 and smooth_v:
             v8, vs, vm = quant_v_head(vf, True)
@@ -367,7 +436,7 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
                                      sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k,
-                                     tile_k=tile_k, k_lane=lane, v_mean=vm)
+                                     tile_k=tile_k, k_lane=lane, v_mean=vm, qk=qk)
     return res
 
 
@@ -397,7 +466,7 @@ def seq_slices(cu_seqlens) -> list:
 
 def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
                 heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block",
-                smooth_v=False):
+                smooth_v=False, qk_format="int8"):
     """Quantized attention over a packed batch of sequences of different lengths
     ("Thư viện SageAttention" page, feature list: variable-length sequences through
     sageattn_varlen).
@@ -422,6 +491,6 @@ def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=No
         (q0, q1), (k0, k1) = sq[b], sk[b]
         one = attn(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype, "NHD", is_causal=is_causal,
                    sm_scale=sm_scale, pv_mode=pv_mode, heads=[(0, h)], rows=rows, blk_q=blk_q, blk_k=blk_k,
-                   tile_k=tile_k, smooth=smooth, gran=gran, smooth_v=smooth_v)
+                   tile_k=tile_k, smooth=smooth, gran=gran, smooth_v=smooth_v, qk_format=qk_format)
         res[(b, h)] = one[(0, h)]
     return res

@@ -132,6 +132,27 @@ void orc_e4m3_encode_n(const float *x, size_t n, uint8_t *out) {
     for (size_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(x[i]);
 }
 
+/*
+ * FP4 E2M1 as in [OCP-MX] (the element format of MXFP4): 1 sign bit, 2 exponent
+ * bits (bias 1), 1 fraction bit; exponent field 0 holds the subnormal 0.5; no
+ * infinity or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Encoding rounds to
+ * nearest, ties to even, saturates at 6; the sign bit is set iff x < 0.
+ */
+float orc_e2m1_decode(uint8_t c) {
+    static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    return (c & 8) ? -mag[c & 7] : mag[c & 7];
+}
+
+uint8_t orc_e2m1_encode(float x) {
+    uint8_t sign = x < 0.0f ? 8 : 0;
+    double v = round_to_format(fabs((double)x), 1, 0);
+    if (v >= 6.0) return sign | 7;
+    if (v < 1.0) return sign | (uint8_t)(v / 0.5); /* 0 or the subnormal 0.5 */
+    int e = ilogb(v);
+    uint8_t fr = (uint8_t)(ldexp(v, -e) * 2.0 - 2.0);
+    return sign | (uint8_t)((e + 1) << 1) | fr;
+}
+
 /* ===================================================================== */
 /* Quantisation                                                           */
 /* ===================================================================== */
@@ -272,6 +293,73 @@ void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scale
 }
 
 /*
+ * MX micro-scaled FP4 ("Kairos" guide 2.2 and the full guide's 下一步 section:
+ * FP4 micro-scaled attention; scale rule of [OCP-MX]): each block of 32
+ * consecutive channels of a token shares an E8M0 scale 2^e,
+ *   e = floor(log2(amax)) - 2        (2 = the largest exponent of E2M1),
+ * clamped to [-127, 127] (an all-zero block gets -127); the elements are
+ * E2M1(x / 2^e), which saturates the few values in (6, 8) * 2^e to 6 * 2^e.
+ * codes: one E2M1 code per element (low 4 bits); e8m0: e + 127 per block.
+ */
+void orc_mxfp4_quant_rows(const float *x, int S, int D, uint8_t *codes, uint8_t *e8m0) {
+    int nb = D / 32;
+    for (int t = 0; t < S; ++t)
+        for (int b = 0; b < nb; ++b) {
+            const float *xb = x + (size_t)t * D + 32 * b;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(xb[i]) > amax) amax = fabsf(xb[i]);
+            int e = -127;
+            if (amax > 0.0f) {
+                int fe;
+                frexp((double)amax, &fe); /* amax = m * 2^fe, m in [0.5, 1): floor(log2) = fe - 1 */
+                e = fe - 1 - 2;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            e8m0[(size_t)t * nb + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i)
+                codes[(size_t)t * D + 32 * b + i] = orc_e2m1_encode((float)ldexp((double)xb[i], -e));
+        }
+}
+
+/* K for the FP4 product: optional mean subtraction as in orc_quant_k_head, then MXFP4. */
+void orc_quant_k_head_mxfp4(const float *k, int S, int D, int smooth, uint8_t *codes, uint8_t *e8m0,
+                            float *mean) {
+    size_t n = (size_t)S * D;
+    float *ks = (float *)malloc((n ? n : 1) * sizeof(float));
+    if (smooth) orc_channel_mean(k, S, D, mean);
+    else memset(mean, 0, (size_t)D * sizeof(float));
+    for (size_t i = 0; i < n; ++i) ks[i] = k[i] - mean[i % D];
+    orc_mxfp4_quant_rows(ks, S, D, codes, e8m0);
+    free(ks);
+}
+
+/*
+ * Q K^T of MXFP4 rows: out[r][n] = fp32( sum_d dec(q[rows[r]][d]) dec(k[n][d]) ), with
+ * dec(x) = E2M1 value * 2^(e8m0 - 127) of x's block.  Every product is exact and
+ * the sum is exact in binary64, so the only rounding is the final one to fp32.
+ */
+void orc_qk_mxfp4_rows(const uint8_t *q4, const uint8_t *qe, const uint8_t *k4, const uint8_t *ke, int S,
+                       int D, const int *rows, int nrows, float *out) {
+    int nb = D / 32;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < nrows; ++r) {
+        int i = rows[r];
+        for (int n = 0; n < S; ++n) {
+            double acc = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                double blk = 0.0;
+                for (int d = 32 * b; d < 32 * b + 32; ++d)
+                    blk += (double)orc_e2m1_decode(q4[(size_t)i * D + d]) * (double)orc_e2m1_decode(k4[(size_t)n * D + d]);
+                acc += ldexp(blk, (int)qe[(size_t)i * nb + b] - 127 + (int)ke[(size_t)n * nb + b] - 127);
+            }
+            out[(size_t)r * S + n] = (float)acc;
+        }
+    }
+}
+
+/*
  * Smoothed V ([SA2, SageAttention2方法]: an optional V smoothing for the FP8 PV
  * product).  Reading: the same statistic as K smoothing -- the channel mean of V
  * over the head's S tokens (orc_channel_mean) -- is subtracted, one fp32
@@ -317,6 +405,8 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  * k_lane, key n uses k_scale[orc_lane_group(n)]).  Query i uses q_scale[i / blk_q].
  * Per key tile:
  *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_blk(n)) * sm_scale)     (dequantise)
+ *           or, with the FP4 product (qk != NULL): s_n = qk[r][n] * sm_scale, qk from
+ *           orc_qk_mxfp4_rows (already dequantised by the micro-scales)
  *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal;
  *           key n and query i count from the start of their sequences)
  *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first tile)
@@ -339,7 +429,7 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
-                        int pv_mode, const int *rows, int nrows, float *out) {
+                        int pv_mode, const int *rows, int nrows, const float *qk, float *out) {
     int ntile = (S + tile_k - 1) / tile_k;
 #pragma omp parallel
     {
@@ -352,7 +442,7 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
             int i = rows[r];
             float m = -INFINITY, l = 0.0f;
             for (int d = 0; d < D; ++d) O[d] = 0.0f;
-            float dq = q_scale[i / blk_q];
+            float dq = qk ? 0.0f : q_scale[i / blk_q];
             for (int j = 0; j < ntile; ++j) {
                 int n0 = j * tile_k;
                 if (is_causal && n0 > i) break; /* tile entirely in the future */
@@ -361,6 +451,8 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                     int n = n0 + t;
                     if (n >= S || (is_causal && n > i)) {
                         s[t] = -INFINITY;
+                    } else if (qk) {
+                        s[t] = qk[(size_t)r * S + n] * sm_scale;
                     } else {
                         int kg = k_lane ? orc_lane_group(n) : n / blk_k;
                         float c = (dq * k_scale[kg]) * sm_scale;

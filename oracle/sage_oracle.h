@@ -22,6 +22,9 @@
  *           sections 五分钟跑通第一个加速样例 and 性能调优实战.
  *   [OCP]   OCP 8-bit floating point specification (E4M3 encoding), the format
  *           named by [SA2] for P~ and V.
+ *   [OCP-MX] OCP Microscaling (MX) formats specification: the E2M1 element format
+ *           and the E8M0 shared-scale rule of MXFP4, the micro-scaled FP4 that
+ *           [KAI] 2.2 names for the next-generation kernels.
  */
 #ifndef SAGE_ORACLE_H
 #define SAGE_ORACLE_H
@@ -49,6 +52,8 @@ void orc_encode16(const float *x, size_t n, int dtype, uint16_t *out);
 float orc_e4m3_decode(uint8_t code);
 uint8_t orc_e4m3_encode(float x);
 void orc_e4m3_encode_n(const float *x, size_t n, uint8_t *out);
+float orc_e2m1_decode(uint8_t code);
+uint8_t orc_e2m1_encode(float x);
 
 /* ---- quantisation (per head) ----------------------------------------- */
 void orc_int8_quant_block(const float *x, size_t n, int8_t *codes, float *scale);
@@ -60,6 +65,11 @@ int orc_lane_group(int n);
 void orc_quant_k_head_lane(const float *k, int S, int D, int smooth,
                            int8_t *codes, float *scales, float *mean);
 void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scales);
+void orc_mxfp4_quant_rows(const float *x, int S, int D, uint8_t *codes, uint8_t *e8m0);
+void orc_quant_k_head_mxfp4(const float *k, int S, int D, int smooth, uint8_t *codes, uint8_t *e8m0,
+                            float *mean);
+void orc_qk_mxfp4_rows(const uint8_t *q4, const uint8_t *qe, const uint8_t *k4, const uint8_t *ke, int S,
+                       int D, const int *rows, int nrows, float *out);
 void orc_quant_v_head_smooth(const float *v, int S, int D, uint8_t *codes, float *scales, float *mean);
 
 /* ---- attention (per head) ---------------------------------------------- */
@@ -68,7 +78,7 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
-                        int pv_mode, const int *rows, int nrows, float *out);
+                        int pv_mode, const int *rows, int nrows, const float *qk, float *out);
 void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, int D,
                          int is_causal, double sm_scale, const int *rows, int nrows,
                          double *out);

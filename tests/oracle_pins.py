@@ -718,4 +718,100 @@ def pin_smooth_v_more_accurate_with_v_offsets():
         assert es < 0.5 * ep, (hd, es, ep)
 
 
+# ------------------------------------------------------------------ MXFP4 (FP4 micro-scaled Q K^T)
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # OCP MX E2M1 magnitudes, codes 0..7
+
+
+def pin_e2m1_table():
+    got = [float(O.e2m1_decode(np.uint8(c))) for c in range(16)]
+    assert got[:8] == E2M1_VALUES and got[8:] == [-v for v in E2M1_VALUES]
+    # every value encodes back to its code (negative zero aside)
+    for c in range(16):
+        if c != 8:
+            assert int(O.e2m1_encode(np.float32(got[c]))) == c, c
+
+
+def pin_e2m1_golden():
+    for line in open(os.path.join(GOLDEN, "e2m1_cases.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        v, c = line.split()
+        assert int(O.e2m1_encode(np.float32(float(v)))) == int(c), (v, c)
+
+
+def pin_mxfp4_block_golden():
+    for line in open(os.path.join(GOLDEN, "mxfp4_block_cases.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        head, _, body = line.partition("|")
+        x = np.zeros((1, 32), np.float32)
+        want = np.zeros(32, np.uint8)
+        for i, item in enumerate(body.split()):
+            v, c = item.split(":")
+            x[0, i], want[i] = np.float32(float(v)), int(c)
+        codes, e8m0 = O.quant_mxfp4_rows(x)
+        assert int(e8m0[0, 0]) == int(head), (line, int(e8m0[0, 0]))
+        assert np.array_equal(codes[0], want), (line, codes[0][:6])
+
+
+def _mx_decode(codes, e8m0):
+    val = np.array(E2M1_VALUES + [-v for v in E2M1_VALUES], np.float64)[codes]
+    return val * np.ldexp(1.0, np.repeat(e8m0.astype(np.int64) - 127, 32, axis=1))
+
+
+def pin_mxfp4_qk_exact():
+    """The FP4 product is the exact dot product of the dequantised rows, rounded
+    once to fp32 (worked out here in binary64 from the codes)."""
+    qf, kf, _ = _rand_head(70, 128, seed=61)
+    q4, qe = O.quant_mxfp4_rows(qf)
+    k4, ke, _ = O.quant_k_head_mxfp4(kf, True)
+    got = O.qk_mxfp4_rows(q4, qe, k4, ke)
+    ref = (_mx_decode(q4, qe) @ _mx_decode(k4, ke).T).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # the rows are the MX rule applied to each 32-channel block of each token
+    kc = (kf - O.channel_mean(kf)[None, :]).astype(np.float32)
+    for t in (0, 33, 69):
+        for b in range(4):
+            blk = kc[t, 32 * b:32 * b + 32]
+            e = int(np.floor(np.log2(np.abs(blk).max()))) - 2
+            assert int(ke[t, b]) == e + 127
+            assert np.array_equal(k4[t, 32 * b:32 * b + 32], O.e2m1_encode(np.ldexp(blk, -e).astype(np.float32)))
+
+
+def pin_fp4_lossless_on_the_grid():
+    """Q and K whose every 32-channel block lies on the E2M1 grid with amax 4 or 6
+    (shared exponent 0) are represented exactly: the FP4 attention equals the
+    attention computed from the exact scores (fp32), bit for bit."""
+    S, D = 96, 64
+    rng = np.random.default_rng(62)
+    grid = np.array(E2M1_VALUES[1:] + [-v for v in E2M1_VALUES[1:]], np.float32)
+    qf = rng.choice(grid, size=(S, D)).astype(np.float32)
+    kf = rng.choice(grid, size=(S, D)).astype(np.float32)
+    for x in (qf, kf):
+        x[:, ::32] = 6.0  # every block reaches amax 6
+    _, _, vf = _rand_head(S, D, seed=62)
+    q, k, v = (_f16(x)[None, None] for x in (qf, kf, vf))
+    ex_scores = (qf.astype(np.float64) @ kf.astype(np.float64).T).astype(np.float32)
+    v8, vs = O.quant_v_head(vf)
+    for causal in (False, True):
+        got = O.attn(q, k, v, F16, "HND", is_causal=causal, smooth=False, qk_format="fp4")[(0, 0)]
+        z8, z1 = np.zeros((S, D), np.int8), np.zeros(1, np.float32)
+        ref = O.attn_head_rows(z8, z1, z8, z1, v8, vs, vf, in_dtype=F16, is_causal=causal,
+                               sm_scale=O.default_sm_scale(D), pv_mode=O.PV_FP8, qk=ex_scores)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), causal
+
+
+def pin_fp4_pipeline_vs_exact():
+    """FP4 Q K^T tracks exact attention (cos >= 0.98 on N(0,1) inputs; measured
+    about 0.986) but less closely than INT8 -- FP4 is not lossless."""
+    w = synth.custom(1, 2, 256, 128, seed=63)
+    q, k, v = synth.make_qkv(w)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    f4 = O.attn(q, k, v, F16, "HND", qk_format="fp4")
+    i8 = O.attn(q, k, v, F16, "HND")
+    for hd in ex:
+        assert cos(f4[hd], ex[hd]) >= 0.98, (hd, cos(f4[hd], ex[hd]))
+        assert rel_l1(f4[hd], ex[hd]) > rel_l1(i8[hd], ex[hd])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -37,13 +37,19 @@ MUTANTS = [
     ("lane_group_no_subtile", "return 2 * (n >> 5) + ((n >> 2) & 1);", "return (n >> 5) + ((n >> 2) & 1);"),
     ("lane_k_not_smoothed", "for (size_t i = 0; i < n; ++i) ks[i] = k[i] - mean[i % D];\n    for (int g = 0;",
      "for (size_t i = 0; i < n; ++i) ks[i] = k[i];\n    for (int g = 0;"),
-    ("q_scale_wrong_block", "float dq = q_scale[i / blk_q];", "float dq = q_scale[i / blk_k];"),
+    ("q_scale_wrong_block", "float dq = qk ? 0.0f : q_scale[i / blk_q];", "float dq = qk ? 0.0f : q_scale[i / blk_k];"),
     ("exact_causal_off_by_one", "int nvis = is_causal ? (i + 1 < S ? i + 1 : S) : S;",
      "int nvis = is_causal ? (i < S ? (i > 0 ? i : 1) : S) : S;"),
     ("fp16_pv_no_rounding", "pq[t] = round_f16(p[t]);", "pq[t] = p[t];"),
     ("fp8_p_not_quantised", "pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));", "pq[t] = p[t] * 448.0f;"),
     ("smooth_v_mean_not_added", "o[d] = o[d] + v_mean[d];", "o[d] = o[d];"),
     ("smooth_v_not_subtracted", "vs[i] = v[i] - mean[i % D];", "vs[i] = v[i];"),
+    ("e2m1_ties_away", "double v = round_to_format(fabs((double)x), 1, 0);",
+     "double v = fabs((double)x) < 6.0 ? round(fabs((double)x) * 2.0) / 2.0 : 6.0;"),
+    ("mx_scale_exponent_off_by_one", "e = fe - 1 - 2;", "e = fe - 1 - 1;"),
+    ("mx_qk_first_block_scale", "ldexp(blk, (int)qe[(size_t)i * nb + b] - 127", "ldexp(blk, (int)qe[(size_t)i * nb] - 127"),
+    ("mx_qk_scale_sign", "+ (int)ke[(size_t)n * nb + b] - 127);", "- (int)ke[(size_t)n * nb + b] + 127);"),
+    ("fp4_scores_without_sm_scale", "s[t] = qk[(size_t)r * S + n] * sm_scale;", "s[t] = qk[(size_t)r * S + n];"),
     ("f16_decode_bias", "ldexp(1.0 + fr / 1024.0, ex - 15)", "ldexp(1.0 + fr / 1024.0, ex - 14)"),
 ]
 
