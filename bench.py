@@ -27,14 +27,17 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TOPS = 5000.0  # MI355X dense INT8 (POP/s) = dense FP8 (PFLOP/s) = 5.0 P
 CPU_SAMPLE_S = 12.0  # seconds of oracle work in the CPU baseline sample
 FP16_PEAK_TOPS = 2500.0  # MI355X dense FP16 (PFLOP/s) = 2.5 P
+FP4_PEAK_TOPS = 10100.0  # MI355X dense FP4 / FP6 (PFLOP/s) = 10.1 P
 
 
-def mfma_peak(pv):
+def mfma_peak(pv, qk="int8"):
     """Peak of the attention kernel's contraction mix: half its operations are
-    the INT8 Q.K^T and half the P.V product (FP8, or FP16 in pv fp16 mode), so
-    the peak is the harmonic combination of the two dense peaks."""
+    the Q.K^T product (INT8, or FP4 with MXFP4) and half the P.V product (FP8,
+    or FP16 in pv fp16 mode), so the peak is the harmonic combination of the
+    two dense peaks."""
+    qk_peak = FP4_PEAK_TOPS if qk == "mxfp4" else MFMA_PEAK_TOPS
     pv_peak = MFMA_PEAK_TOPS if pv == "fp8" else FP16_PEAK_TOPS
-    return 2.0 / (1.0 / MFMA_PEAK_TOPS + 1.0 / pv_peak)
+    return 2.0 / (1.0 / qk_peak + 1.0 / pv_peak)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "quantized_attention_02_amd", "csrc", "attn.hip")
@@ -49,8 +52,8 @@ def parse():
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
-    p.add_argument("--qk-gran", default="block", choices=["block", "lane"],
-                   help="INT8 scale granularity of Q and K: per block, or per token / 16-key lane group")
+    p.add_argument("--qk-quant", default="int8", choices=["int8", "int8_lane", "mxfp4"],
+                   help="Q/K quantisation: INT8 per block, INT8 per token / 16-key lane group, or MXFP4")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-oracle sample (0: as many as take about 12 s)")
@@ -76,7 +79,7 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_hash, workload, pv, causal, gran="block"):
+def traffic_record(kernel_hash, workload, pv, causal, qk="int8"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summaries, if one was taken on the current kernel source for this workload
     and mode."""
@@ -86,12 +89,17 @@ def traffic_record(kernel_hash, workload, pv, causal, gran="block"):
         return None
     for rec in recs:
         if (rec.get("attn_src_sha256_16") == kernel_hash and rec.get("workload") == workload
-                and rec.get("pv_mode") == pv and rec.get("causal") == causal and rec.get("qk_gran", "block") == gran):
+                and rec.get("pv_mode") == pv and rec.get("causal") == causal and rec.get("qk_quant", "int8") == qk):
             return rec
     return None
 
 
-def cpu_baseline(w, causal, pv, nheads, gran="block"):
+def oracle_qk(qk):
+    """The oracle's keyword arguments for a Q/K quantisation mode."""
+    return {"int8": {}, "int8_lane": {"gran": "lane"}, "mxfp4": {"qk_format": "fp4"}}[qk]
+
+
+def cpu_baseline(w, causal, pv, nheads, qk="int8"):
     import numpy as np
 
     import oracle as O
@@ -112,7 +120,7 @@ def cpu_baseline(w, causal, pv, nheads, gran="block"):
         def run(heads):
             t0 = time.perf_counter()
             O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=bool(causal), pv_mode=pvm, heads=heads,
-                          gran=gran)
+                          **oracle_qk(qk))
             return time.perf_counter() - t0
         what = "sequence-heads"
     else:
@@ -125,7 +133,7 @@ def cpu_baseline(w, causal, pv, nheads, gran="block"):
         def run(heads):
             t0 = time.perf_counter()
             O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal), pv_mode=pvm, heads=heads,
-                   gran=gran)
+                   **oracle_qk(qk))
             return time.perf_counter() - t0
         what = "heads"
 
@@ -179,18 +187,18 @@ def main():
     if varlen:
         cq, ck = (torch.from_numpy(c).to(dev) for c in w.cu_seqlens())
         mq, mk = max(w.seqlens_q), max(w.seqlens_k)
-        bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev, args.qk_gran)
+        bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev, args.qk_quant)
 
         def quant():
-            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_gran=args.qk_gran, smooth_v=args.smooth_v)
+            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v)
 
         def attn():
             qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)
     else:
-        bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_gran)
+        bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_quant)
 
         def quant():
-            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_gran=args.qk_gran, smooth_v=args.smooth_v)
+            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v)
 
         def attn():
             qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
@@ -223,7 +231,7 @@ def main():
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     khash = source_hash(ATTN_SRC)
-    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_gran)
+    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_quant)
     traffic = None if trec is None else trec["hbm_bytes_per_launch"]
 
     res = {
@@ -238,24 +246,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8+fp8" if args.pv == "fp8" else "i8+f16",
+        "dtype": {"int8": "i8", "int8_lane": "i8", "mxfp4": "mxfp4"}[args.qk_quant] + ("+fp8" if args.pv == "fp8" else "+f16"),
         "data": "synthetic",
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,
                     "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv,
-                    "qk_gran": args.qk_gran, "smooth_v": args.smooth_v} if varlen else
+                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v} if varlen else
                    {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
                     "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv,
-                    "qk_gran": args.qk_gran, "smooth_v": args.smooth_v}),
+                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v}),
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv), 1), "unit": "TFLOP/s",
-                     "frac": round(attn_tops / mfma_peak(args.pv), 4), "traffic": traffic,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv, args.qk_quant), 1), "unit": "TFLOP/s",
+                     "frac": round(attn_tops / mfma_peak(args.pv, args.qk_quant), 4), "traffic": traffic,
                      "kernel": "k_attn (sage_attn_fwd)", "algorithmic_ops_per_launch": ops,
                      "attn_src_sha256_16": khash},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_gran)
+        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_quant)
     print(json.dumps(res))
 
 

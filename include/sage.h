@@ -29,7 +29,7 @@
  *    returns.  Inputs must stay alive and unmodified, and outputs untouched,
  *    until the stream has passed the call.  The caller owns all memory; the
  *    library allocates no device memory and keeps no per-call state.
- *  - Tensor pointers (q, k, v, out, q_i8, k_i8, v_fp8, dump buffers) must be
+ *  - Tensor pointers (q, k, v, out, q_codes, k_codes, v_fp8, dump buffers) must be
  *    16-byte aligned; scale / mean arrays 4-byte aligned.  Outputs must not
  *    overlap inputs.
  *  - Shapes: B, H >= 1; 1 <= S <= SAGE_MAX_S; D in {64, 128};
@@ -45,12 +45,12 @@
  * Internal buffer layouts (all row-major, "[a][b]" = a outer):
  *   S_q = roundup(S, SAGE_BLK_Q), S_k = roundup(S, SAGE_KV_PAD),
  *   nq = S_q / SAGE_BLK_Q, nk = S_k / SAGE_BLK_K.
- *   q_i8    int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
+ *   q_codes int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
  *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens
- *                                  (SAGE_GRAN_LANE: [B][H][S_q], one per token).
- *   k_i8    int8  [B][H_kv][S_k][D] INT8 codes of K - k_mean; rows >= S are 0.
+ *                                  (SAGE_QK_INT8_LANE: [B][H][S_q], one per token).
+ *   k_codes int8  [B][H_kv][S_k][D] INT8 codes of K - k_mean; rows >= S are 0.
  *   k_scale float [B][H_kv][nk]    one scale per block of SAGE_BLK_K tokens (0 for blocks
- *                                  made only of padding keys; SAGE_GRAN_LANE:
+ *                                  made only of padding keys; SAGE_QK_INT8_LANE:
  *                                  [B][H_kv][S_k / 16], one per lane group).
  *   k_mean  float [B][H_kv][D]     per-channel mean of K over the S tokens.
  *   v_fp8   uint8 [B][H_kv][nk][D][64] E4M3 codes of V, one 64-key tile after the
@@ -59,6 +59,12 @@
  *   v_scale float [B][H_kv][D]     one scale per channel.
  *   v_mean  float [B][H_kv][D]     V smoothing only: the channel means subtracted from V
  *                                  before quantisation (same size as v_scale).
+ *   SAGE_QK_MXFP4 replaces the Q/K codes and scales by (D / 2 and D / 32 bytes a row):
+ *   q_codes uint8 [B][H][S_q][D/2]  E2M1 codes of Q, two per byte (channel 2j in the low
+ *                                   nibble of byte j); q_scale uint8 [B][H][S_q][D/32], the
+ *                                   E8M0 byte (e + 127) of each 32-channel block;
+ *   k_codes uint8 [B][H_kv][S_k][D/2], k_scale uint8 [B][H_kv][S_k][D/32] likewise for
+ *                                   K - k_mean.  Padding rows hold zero codes and byte 0.
  *   out: same dtype and layout (HND or NHD) as q.
  */
 #ifndef SAGE_H
@@ -85,13 +91,19 @@ extern "C" {
 #define SAGE_DTYPE_BF16 1
 #define SAGE_PV_FP8 0  /* P~ and V in E4M3, two-level fp32 accumulation ([SA2]) */
 #define SAGE_PV_FP16 1 /* P~ and V in fp16, fp32 accumulation ([KAI] 2.1, sm80 row) */
-/* INT8 scale granularity of Q and K ([KAI] 2.2 per_block / per_warp choice; [SA2]
- * SageAttention2方法, thread-level quantisation): */
-#define SAGE_GRAN_BLOCK 0 /* one scale per SAGE_BLK_Q query tokens / SAGE_BLK_K keys */
-#define SAGE_GRAN_LANE 1  /* one scale per query token and per 16-key lane group: the
-                             keys one half-wave holds of each 32-key sub-tile of the
-                             32 x 32 INT8 MFMA result, group of key n = 2 (n / 32) +
-                             ((n / 4) mod 2); every lane dequantises with one scale */
+/* Quantisation of Q and K for the Q K^T product (qk_quant):
+ * INT8 with a scale granularity ([KAI] 2.2 per_block / per_warp choice; [SA2]
+ * SageAttention2方法, thread-level quantisation), or micro-scaled FP4 ([KAI] 2.2,
+ * the FP4 micro-scaling kernels of the next generation). */
+#define SAGE_QK_INT8_BLOCK 0 /* INT8, one scale per SAGE_BLK_Q query tokens / SAGE_BLK_K keys */
+#define SAGE_QK_INT8_LANE 1  /* INT8, one scale per query token and per 16-key lane group:
+                                the keys one half-wave holds of each 32-key sub-tile of the
+                                32 x 32 INT8 MFMA result, group of key n = 2 (n / 32) +
+                                ((n / 4) mod 2); every lane dequantises with one scale */
+#define SAGE_QK_MXFP4 2      /* MXFP4 ([OCP-MX]): E2M1 codes, each 32-channel block of a
+                                token sharing an E8M0 scale 2^e, e = floor(log2 amax) - 2,
+                                clamped to [-127, 127] (-127 for an all-zero block); codes
+                                E2M1(x / 2^e), round to nearest even, saturating at 6 */
 
 /* ---- limits and granularity ---- */
 #define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
@@ -112,8 +124,8 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16);
 
 /* Bytes of each intermediate buffer for a problem shape (see the layouts
  * above).  Any output pointer may be NULL. */
-int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_gran, size_t *q_i8, size_t *q_scale,
-                      size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
+int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t *q_codes, size_t *q_scale,
+                      size_t *k_codes, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
 
 /*
  * K smoothing + per-block INT8 quantisation of Q and K ([SA2] 相关工作,
@@ -123,17 +135,19 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_gran, size_t 
  *   (one fp32 subtraction per element), each over all D channels:
  *     amax = max |x|;  scale = amax / 127;  code = rint(x * (127 / amax)) in [-127, 127];
  *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
- *   qk_gran = SAGE_GRAN_LANE: the same rule with each Q token, and each 16-key lane
- *   group of K - k_mean, as its own block.
+ *   qk_quant = SAGE_QK_INT8_LANE: the same rule with each Q token, and each 16-key lane
+ *   group of K - k_mean, as its own block; SAGE_QK_MXFP4: the MXFP4 rule above on each
+ *   32-channel block of every Q token and of every token of K - k_mean.
  * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
  * same with H_kv heads.
- * Writes q_i8, q_scale, k_i8, k_scale, k_mean (layouts above).  The call is
- * several kernel launches; while it runs, k_i8 also holds intermediate
+ * Writes q_codes, q_scale, k_codes, k_scale, k_mean (layouts above; their element
+ * types follow qk_quant).  The call is several kernel launches; while it runs,
+ * k_codes also holds intermediate
  * per-chunk channel sums, so its content is defined only after the stream has
  * passed the call.
  */
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
-                         int layout, int qk_gran, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale,
+                         int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
                          float *k_mean, void *stream);
 
 /*
@@ -156,16 +170,18 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  * Fused quantized attention ([SA2]; [KAI] 2.1; [GUIDE] 五分钟跑通, 性能调优实战).
  * For each query row i, key tiles (SAGE_TILE_K_FP8 / SAGE_TILE_K_FP16 keys) in order,
  * fp32 online softmax:
- *   s_n = float(q_i8[i] . k_i8[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA, int32 sums;
- *         the scales of query i's block and key n's block, or lane group: qk_gran must
- *         be the granularity the codes were made with)
+ *   s_n = float(q_codes[i] . k_codes[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA,
+ *         int32 sums; the scales of query i's block and key n's block, or lane group);
+ *         SAGE_QK_MXFP4: s_n = (sum_d Q~[i][d] K~[n][d]) * sm_scale over the dequantised
+ *         E2M1 * 2^e values (scaled FP4 MFMA, fp32 sums).  qk_quant must be the mode
+ *         the codes were made with.
  *   keys n >= S, and n > i when is_causal (square, top-left aligned), are excluded
  *   m' = max(m, max_n s_n);  alpha = exp(m - m');  p_n = exp(s_n - m');  l = alpha*l + sum p_n
  *   pv fp8 : P = E4M3(448 * p_n) (static scale), inner = P . V_fp8 (FP8 MFMA, fresh per tile),
  *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
  *            (+ v_mean[d] when v_mean is non-NULL: V was smoothed by sage_quant_v)
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
- * q_i8 .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
+ * q_codes .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
  * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the
  * original V tensor (dtype, layout, H_kv heads), v_scale = v_mean = NULL (bf16 V is
  * rounded to fp16).  out: dtype tensor in `layout`, shape
@@ -174,23 +190,23 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  * pv fp16 with NHD layout additionally needs H_kv * D * 2 * SAGE_KV_PAD < 2^31
  * (128-token slices of V are addressed through a 32-bit byte range).
  */
-int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                   const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H,
                   int H_kv, int S,
-                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream);
+                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, void *stream);
 
 /*
  * Debug variant of sage_attn_fwd: the same kernel code, which additionally
  * writes the int32 accumulators of Q K^T for query head (b, h) to qk, an int32 [S][S]
- * array (qk[i][n] = sum_d q_i8[i][d] * k_i8[n][d]).  With is_causal, entries
+ * array (qk[i][n] = sum_d q_codes[i][d] * k_codes[n][d]; INT8 modes only).  With is_causal, entries
  * with n > i may be left unwritten (key tiles the mask excludes for a whole
  * work-group are skipped); every entry with n <= i is written.  `out` is
  * written as by sage_attn_fwd.
  */
-int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                           const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
                           int H, int H_kv,
-                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran,
+                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant,
                           int b, int h, int32_t *qk, void *stream);
 
 /* ------------------------------------------------------------------------
@@ -218,23 +234,24 @@ int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t
  * rows of sequence b start at
  *   rq(b) = 32 * (cu_seqlens_q[b] / 32 + b),  rk(b) = 128 * (cu_seqlens_k[b] / 128 + b)
  * of RQ = 32 * (total_q / 32 + B + 1) and RK = 128 * (total_k / 128 + B + 1) rows:
- *   q_i8    int8  [H][RQ][D]          q_scale float [H][RQ / 32]    (lane: [H][RQ])
- *   k_i8    int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64] (lane: [H_kv][RK / 16])
+ *   q_codes int8  [H][RQ][D]          q_scale float [H][RQ / 32]    (lane: [H][RQ])
+ *   k_codes int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64] (lane: [H_kv][RK / 16])
+ *   (MXFP4: codes D / 2 and scales D / 32 bytes a row, as in the fixed layout)
  *   k_mean  float [B][H_kv][D]        v_scale float [B][H_kv][D]
  *   v_fp8   uint8 [H_kv][RK / 64][D][64]  (64-key tiles as in the fixed layout)
  * A sequence's rows past its length, up to the next multiple of 32 (Q) or 128
  * (K, V), hold zero codes; rows between sequences are neither written nor read.
  * Other rules (alignment, errors, stream order, staging) as above.
  * ------------------------------------------------------------------------ */
-int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, int qk_gran,
-                             size_t *q_i8, size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean,
+int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, int qk_quant,
+                             size_t *q_codes, size_t *q_scale, size_t *k_codes, size_t *k_scale, size_t *k_mean,
                              size_t *v_fp8, size_t *v_scale);
 
 /* sage_smooth_quant_qk for a packed batch. */
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
-                                int max_seqlen_q, int max_seqlen_k, int D, int qk_gran, int8_t *q_i8,
-                                float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean, void *stream);
+                                int max_seqlen_q, int max_seqlen_k, int D, int qk_quant, void *q_codes,
+                                void *q_scale, void *k_codes, void *k_scale, float *k_mean, void *stream);
 
 /* sage_quant_v for a packed batch (v: [total_k][H_kv][D]); v_mean as there. */
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
@@ -242,12 +259,12 @@ int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, i
 
 /* sage_attn_fwd for a packed batch.  pv fp16: v = the original [total_k][H_kv][D]
  * V, v_scale = v_mean = NULL.  out: [total_q][H][D] in dtype. */
-int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                          const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
                          const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
-                         int qk_gran, void *stream);
+                         int qk_quant, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *sage_status_str(int status);

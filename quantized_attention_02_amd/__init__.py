@@ -26,7 +26,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ER
 LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
 PV = {"fp8": 0, "fp16": 1}
-GRAN = {"block": 0, "lane": 1}  # INT8 scale granularity of Q and K (include/sage.h SAGE_GRAN_*)
+QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2}  # Q/K quantisation (include/sage.h SAGE_QK_*)
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
@@ -93,17 +93,17 @@ def sage_get_config():
     return tuple(x.value for x in v)
 
 
-def sage_buffer_sizes(B, H, H_kv, S, D, qk_gran=0):
+def sage_buffer_sizes(B, H, H_kv, S, D, qk_quant=0):
     vals = [ctypes.c_size_t() for _ in range(7)]
-    _check(lib().sage_buffer_sizes(B, H, H_kv, S, D, qk_gran, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
+    _check(lib().sage_buffer_sizes(B, H, H_kv, S, D, qk_quant, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
     names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
     return {n: v.value for n, v in zip(names, vals)}
 
 
-def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_gran, q_i8, q_scale, k_i8, k_scale, k_mean,
+def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale, k_mean,
                          stream):
     """All tensor arguments are device pointers (ints); returns the status code."""
-    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_gran, q_i8, q_scale, k_i8, k_scale,
+    return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale,
                                       k_mean, stream)
 
 
@@ -112,29 +112,29 @@ def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream):
 
 
 def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                  sm_scale, pv_mode, qk_gran, stream):
+                  sm_scale, pv_mode, qk_quant, stream):
     return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                               is_causal, sm_scale, pv_mode, qk_gran, stream)
+                               is_causal, sm_scale, pv_mode, qk_quant, stream)
 
 
 def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                          is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, stream):
+                          is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, stream):
     return lib().sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S,
-                                       D, layout, is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, stream)
+                                       D, layout, is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, stream)
 
 
-def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_gran=0):
+def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_quant=0):
     vals = [ctypes.c_size_t() for _ in range(7)]
-    _check(lib().sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_gran,
+    _check(lib().sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_quant,
                                           *[ctypes.byref(v) for v in vals]), "sage_varlen_buffer_sizes")
     names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
     return {n: v.value for n, v in zip(names, vals)}
 
 
 def sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
-                                max_seqlen_k, D, qk_gran, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+                                max_seqlen_k, D, qk_quant, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
     return lib().sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k,
-                                             max_seqlen_q, max_seqlen_k, D, qk_gran, q_i8, q_scale, k_i8, k_scale,
+                                             max_seqlen_q, max_seqlen_k, D, qk_quant, q_i8, q_scale, k_i8, k_scale,
                                              k_mean, stream)
 
 
@@ -145,10 +145,10 @@ def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, 
 
 def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q, cu_seqlens_k, B,
                          H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode,
-                         qk_gran, stream):
+                         qk_quant, stream):
     return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q,
                                       cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
-                                      is_causal, sm_scale, pv_mode, qk_gran, stream)
+                                      is_causal, sm_scale, pv_mode, qk_quant, stream)
 
 
 def sage_status_str(status):
@@ -197,19 +197,28 @@ def _dtype_code(t):
 
 class Quantized:
     """Device buffers produced by the two quantisation entry points (K and V
-    buffers have H_kv heads; H_kv = H unless K/V are grouped)."""
+    buffers have H_kv heads; H_kv = H unless K/V are grouped).  q_i8 / k_i8 hold
+    the Q / K codes: INT8, or (qk_quant "mxfp4") packed E2M1 pairs, with
+    q_scale / k_scale then the E8M0 bytes of each 32-channel block."""
 
-    def __init__(self, B, H, S, D, device, H_kv=None, qk_gran="block"):
+    def __init__(self, B, H, S, D, device, H_kv=None, qk_quant="int8"):
         import torch
 
         H_kv = H if H_kv is None else H_kv
-        self.B, self.H, self.H_kv, self.S, self.D, self.gran = B, H, H_kv, S, D, GRAN[qk_gran]
+        self.B, self.H, self.H_kv, self.S, self.D, self.qk = B, H, H_kv, S, D, QK[qk_quant]
         sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + KV_PAD - 1) // KV_PAD * KV_PAD
-        lane = self.gran == GRAN["lane"]
-        self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
-        self.q_scale = torch.empty((B, H, sq if lane else sq // BLK_Q), dtype=torch.float32, device=device)
-        self.k_i8 = torch.empty((B, H_kv, sk, D), dtype=torch.int8, device=device)
-        self.k_scale = torch.empty((B, H_kv, sk // 16 if lane else sk // BLK_K), dtype=torch.float32, device=device)
+        lane = self.qk == QK["int8_lane"]
+        if self.qk == QK["mxfp4"]:  # packed E2M1 pairs and E8M0 bytes per 32 channels of a row
+            self.q_i8 = torch.empty((B, H, sq, D // 2), dtype=torch.uint8, device=device)
+            self.q_scale = torch.empty((B, H, sq, D // 32), dtype=torch.uint8, device=device)
+            self.k_i8 = torch.empty((B, H_kv, sk, D // 2), dtype=torch.uint8, device=device)
+            self.k_scale = torch.empty((B, H_kv, sk, D // 32), dtype=torch.uint8, device=device)
+        else:
+            self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
+            self.q_scale = torch.empty((B, H, sq if lane else sq // BLK_Q), dtype=torch.float32, device=device)
+            self.k_i8 = torch.empty((B, H_kv, sk, D), dtype=torch.int8, device=device)
+            self.k_scale = torch.empty((B, H_kv, sk // 16 if lane else sk // BLK_K), dtype=torch.float32,
+                                       device=device)
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((B, H_kv, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
@@ -229,9 +238,9 @@ def _kv_heads(q, k, v, tensor_layout):
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
-             qk_gran="block", smooth_v=False) -> Quantized:
+             qk_quant="int8", smooth_v=False) -> Quantized:
     """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors.
-    k and v may have fewer heads than q (grouped-query attention); qk_gran "block"
+    k and v may have fewer heads than q (grouped-query attention); qk_quant "block"
     or "lane" (one scale per Q token and per 16-key lane group of K); smooth_v
     (pv fp8): quantise V minus its channel mean."""
     if smooth_v and pv_mode != "fp8":
@@ -243,11 +252,11 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
     dt = _dtype_code(q)
-    bufs = bufs or Quantized(B, H, S, D, q.device, H_kv, qk_gran)
-    if (bufs.B, bufs.H, bufs.H_kv, bufs.S, bufs.D, bufs.gran) != (B, H, H_kv, S, D, GRAN[qk_gran]):
+    bufs = bufs or Quantized(B, H, S, D, q.device, H_kv, qk_quant)
+    if (bufs.B, bufs.H, bufs.H_kv, bufs.S, bufs.D, bufs.qk) != (B, H, H_kv, S, D, QK[qk_quant]):
         raise ValueError("bufs were allocated for another shape or granularity")
     st = _stream()
-    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.gran,
+    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
                                 bufs.q_i8.data_ptr(),
                                 bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
                                 bufs.k_mean.data_ptr(), st), "sage_smooth_quant_qk")
@@ -275,7 +284,7 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
     vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
     args = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs,
-            vm, out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.gran)
+            vm, out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.qk)
     if dump_head is None:
         _check(sage_attn_fwd(*args, _stream()), "sage_attn_fwd")
     else:
@@ -284,12 +293,12 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     return out
 
 
-def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_gran="block",
+def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_quant="int8",
              smooth_v=False):
     """Quantized attention: same shape, dtype and layout out as q."""
     import torch
 
-    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_gran=qk_gran, smooth_v=smooth_v)
+    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
 
@@ -308,18 +317,25 @@ def varlen_row0(start: int, b: int, pad: int) -> int:
 class QuantizedVarlen:
     """Device buffers of the packed-batch quantisation entry points."""
 
-    def __init__(self, B, H, H_kv, total_q, total_k, D, device, qk_gran="block"):
+    def __init__(self, B, H, H_kv, total_q, total_k, D, device, qk_quant="int8"):
         import torch
 
         self.B, self.H, self.H_kv, self.total_q, self.total_k, self.D = B, H, H_kv, total_q, total_k, D
-        self.gran = GRAN[qk_gran]
-        lane = self.gran == GRAN["lane"]
+        self.qk = QK[qk_quant]
+        lane = self.qk == QK["int8_lane"]
         rq, rk = varlen_rows(total_q, B, BLK_Q), varlen_rows(total_k, B, KV_PAD)
         self.rows_q, self.rows_k = rq, rk
-        self.q_i8 = torch.empty((H, rq, D), dtype=torch.int8, device=device)
-        self.q_scale = torch.empty((H, rq if lane else rq // BLK_Q), dtype=torch.float32, device=device)
-        self.k_i8 = torch.empty((H_kv, rk, D), dtype=torch.int8, device=device)
-        self.k_scale = torch.empty((H_kv, rk // 16 if lane else rk // BLK_K), dtype=torch.float32, device=device)
+        if self.qk == QK["mxfp4"]:
+            self.q_i8 = torch.empty((H, rq, D // 2), dtype=torch.uint8, device=device)
+            self.q_scale = torch.empty((H, rq, D // 32), dtype=torch.uint8, device=device)
+            self.k_i8 = torch.empty((H_kv, rk, D // 2), dtype=torch.uint8, device=device)
+            self.k_scale = torch.empty((H_kv, rk, D // 32), dtype=torch.uint8, device=device)
+        else:
+            self.q_i8 = torch.empty((H, rq, D), dtype=torch.int8, device=device)
+            self.q_scale = torch.empty((H, rq if lane else rq // BLK_Q), dtype=torch.float32, device=device)
+            self.k_i8 = torch.empty((H_kv, rk, D), dtype=torch.int8, device=device)
+            self.k_scale = torch.empty((H_kv, rk // 16 if lane else rk // BLK_K), dtype=torch.float32,
+                                       device=device)
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((H_kv, rk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
@@ -336,7 +352,7 @@ def _cu(t, name):
 
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
-                    bufs: QuantizedVarlen | None = None, qk_gran="block", smooth_v=False) -> QuantizedVarlen:
+                    bufs: QuantizedVarlen | None = None, qk_quant="int8", smooth_v=False) -> QuantizedVarlen:
     """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode) on a packed
     batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
@@ -354,14 +370,14 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     if H_kv < 1 or H % H_kv:
         raise ValueError(f"the number of query heads ({H}) must be a multiple of the K/V heads ({H_kv})")
     dt = _dtype_code(q)
-    bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device, qk_gran)
-    if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D, bufs.gran) != \
-            (B, H, H_kv, total_q, total_k, D, GRAN[qk_gran]):
+    bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device, qk_quant)
+    if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D, bufs.qk) != \
+            (B, H, H_kv, total_q, total_k, D, QK[qk_quant]):
         raise ValueError("bufs were allocated for another shape or granularity")
     bufs.max_seqlen_q, bufs.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
     st = _stream()
     _check(sage_smooth_quant_qk_varlen(q.data_ptr(), k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
-                                       total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.gran,
+                                       total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk,
                                        bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                        bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
            "sage_smooth_quant_qk_varlen")
@@ -392,19 +408,19 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                 bufs.k_scale.data_ptr(), vptr, vs, vm, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
                                 ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k, bufs.max_seqlen_q,
-                                bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, bufs.gran, _stream()),
+                                bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, bufs.qk, _stream()),
            "sage_attn_fwd_varlen")
     return out
 
 
 def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False, sm_scale=None,
-                    pv_mode="fp8", qk_gran="block", smooth_v=False):
+                    pv_mode="fp8", qk_quant="int8", smooth_v=False):
     """Quantized attention over a packed batch of sequences ("SageAttention: Thư viện
     Attention lượng tử hóa" page, feature list: sageattn_varlen):
     q [total_q, H, D], k / v [total_k, H_kv, D]; returns [total_q, H, D]."""
     import torch
 
-    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_gran=qk_gran,
+    bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_quant=qk_quant,
                            smooth_v=smooth_v)
     out = torch.empty_like(q)
     return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)

@@ -41,13 +41,23 @@ int check_kv_heads(int H, int H_kv) {
   return SAGE_OK;
 }
 
-int check_gran(int qk_gran) {
-  return (qk_gran == SAGE_GRAN_BLOCK || qk_gran == SAGE_GRAN_LANE) ? SAGE_OK : SAGE_ERR_INVALID_ARG;
+int check_qk_quant(int qk_quant) {
+  return (qk_quant == SAGE_QK_INT8_BLOCK || qk_quant == SAGE_QK_INT8_LANE || qk_quant == SAGE_QK_MXFP4)
+             ? SAGE_OK
+             : SAGE_ERR_INVALID_ARG;
 }
 
 // scale entries per head: Q per block of kBlkQ rows or per row; K per kBlkK-row block or 16-row group
-size_t q_scales(size_t rows, int gran) { return gran == SAGE_GRAN_LANE ? rows : rows / kBlkQ; }
-size_t k_scales(size_t rows, int gran) { return gran == SAGE_GRAN_LANE ? rows / 16 : rows / kBlkK; }
+// bytes per head of the Q / K codes and scales for `rows` buffer rows of D channels
+size_t code_bytes(size_t rows, int D, int qk) { return qk == SAGE_QK_MXFP4 ? rows * D / 2 : rows * D; }
+size_t q_scale_bytes(size_t rows, int D, int qk) {
+  if (qk == SAGE_QK_MXFP4) return rows * (D / 32);  // E8M0 bytes
+  return (qk == SAGE_QK_INT8_LANE ? rows : rows / kBlkQ) * sizeof(float);
+}
+size_t k_scale_bytes(size_t rows, int D, int qk) {
+  if (qk == SAGE_QK_MXFP4) return rows * (D / 32);
+  return (qk == SAGE_QK_INT8_LANE ? rows / 16 : rows / kBlkK) * sizeof(float);
+}
 
 int check_enums(int dtype, int layout) {
   if (dtype != SAGE_DTYPE_F16 && dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARG;
@@ -78,31 +88,32 @@ int check_device() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
 
-int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                 const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H,
                 int H_kv, int S,
-                int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, int dump_b,
+                int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, int dump_b,
                 int dump_h, int32_t *qk, bool dump, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
-  if ((rc = check_gran(qk_gran))) return rc;
+  if ((rc = check_qk_quant(qk_quant))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
-  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;  // smoothing is for the FP8 V codes
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16))
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16))
     return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)))
     return SAGE_ERR_INVALID_ARG;
   if (dump) {
+    if (qk_quant == SAGE_QK_MXFP4) return SAGE_ERR_INVALID_ARG;  // the dump holds INT8 sums
     if (!qk || !aligned(qk, 16)) return SAGE_ERR_INVALID_ARG;
     if (dump_b < 0 || dump_b >= B || dump_h < 0 || dump_h >= H) return SAGE_ERR_INVALID_ARG;
   }
@@ -110,10 +121,10 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
 
   AttnArgs a;
   memset(&a, 0, sizeof a);
-  a.q_i8 = q_i8;
-  a.k_i8 = k_i8;
-  a.q_scale = q_scale;
-  a.k_scale = k_scale;
+  a.q_i8 = (const int8_t *)q_codes;
+  a.k_i8 = (const int8_t *)k_codes;
+  a.q_scale = (const float *)q_scale;
+  a.k_scale = (const float *)k_scale;
   a.v = v;
   a.v_scale = v_scale;
   a.v_mean = v_mean;
@@ -135,7 +146,7 @@ int attn_common(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, co
   a.nk = a.S_k / kBlkK;
   a.nmblk = (S + 127) / 128;
   a.sm2 = sm_scale * 1.4426950408889634f;
-  a.gran = qk_gran;
+  a.qk = qk_quant;
   return launch_status(launch_attn(a, dump, (hipStream_t)stream));
 }
 
@@ -152,18 +163,18 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16) {
   return SAGE_OK;
 }
 
-int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_gran, size_t *q_i8, size_t *q_scale,
-                      size_t *k_i8, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
+int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t *q_codes, size_t *q_scale,
+                      size_t *k_codes, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
-  if ((rc = check_gran(qk_gran))) return rc;
+  if ((rc = check_qk_quant(qk_quant))) return rc;
   const size_t bh = (size_t)B * H, bhk = (size_t)B * H_kv;
   const size_t S_q = roundup(S, kBlkQ), S_k = roundup(S, kKvPad);
-  if (q_i8) *q_i8 = bh * S_q * D;
-  if (q_scale) *q_scale = bh * q_scales(S_q, qk_gran) * sizeof(float);
-  if (k_i8) *k_i8 = bhk * S_k * D;
-  if (k_scale) *k_scale = bhk * k_scales(S_k, qk_gran) * sizeof(float);
+  if (q_codes) *q_codes = bh * code_bytes(S_q, D, qk_quant);
+  if (q_scale) *q_scale = bh * q_scale_bytes(S_q, D, qk_quant);
+  if (k_codes) *k_codes = bhk * code_bytes(S_k, D, qk_quant);
+  if (k_scale) *k_scale = bhk * k_scale_bytes(S_k, D, qk_quant);
   if (k_mean) *k_mean = bhk * D * sizeof(float);
   if (v_fp8) *v_fp8 = bhk * S_k * D;
   if (v_scale) *v_scale = bhk * D * sizeof(float);
@@ -171,25 +182,25 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_gran, size_t 
 }
 
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
-                         int layout, int qk_gran, int8_t *q_i8, float *q_scale, int8_t *k_i8, float *k_scale,
+                         int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
                          float *k_mean, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
-  if ((rc = check_gran(qk_gran))) return rc;
+  if ((rc = check_qk_quant(qk_quant))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
-  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16)) return SAGE_ERR_INVALID_ARG;
+  if (!q || !k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantQKArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;
   a.k = k;
-  a.q_i8 = q_i8;
-  a.k_i8 = k_i8;
-  a.q_scale = q_scale;
-  a.k_scale = k_scale;
+  a.q_i8 = (int8_t *)q_codes;
+  a.k_i8 = (int8_t *)k_codes;
+  a.q_scale = (float *)q_scale;
+  a.k_scale = (float *)k_scale;
   a.k_mean = k_mean;
   a.B = B;
   a.H = H;
@@ -202,7 +213,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   a.S_k = roundup(S, kKvPad);
   a.nq = a.S_q / kBlkQ;
   a.nk = a.S_k / kBlkK;
-  a.gran = qk_gran;
+  a.qk = qk_quant;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
 }
 
@@ -231,42 +242,42 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
   return launch_status(launch_quant_v(a, (hipStream_t)stream));
 }
 
-int sage_attn_fwd(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale, const void *v,
+int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale, const void *v,
                   const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H, int H_kv, int S,
-                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_gran, void *stream) {
-  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                     is_causal, sm_scale, pv_mode, qk_gran, 0, 0, nullptr, false, stream);
+                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, void *stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
+                     is_causal, sm_scale, pv_mode, qk_quant, 0, 0, nullptr, false, stream);
 }
 
-int sage_attn_fwd_dump_qk(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                           const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
                           int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode,
-                          int qk_gran, int b, int h, int32_t *qk, void *stream) {
-  return attn_common(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                     is_causal, sm_scale, pv_mode, qk_gran, b, h, qk, true, stream);
+                          int qk_quant, int b, int h, int32_t *qk, void *stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
+                     is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, true, stream);
 }
 
 // ---- packed variable-length batches
 static int check_varlen(int B, int H, int H_kv, int total_q, int total_k, int max_q, int max_k, int D,
-                        int qk_gran) {
+                        int qk_quant) {
   if (B < 1 || total_q < 0 || total_k < 0 || total_q > kMaxTotal || total_k > kMaxTotal) return SAGE_ERR_INVALID_ARG;
   int rc = check_shape(B, H, max_q, D);  // max_q in 1 .. SAGE_MAX_S, launch sizes
   if (rc) return rc;
   if ((rc = check_shape(B, H, max_k, D))) return rc;
-  if ((rc = check_gran(qk_gran))) return rc;
+  if ((rc = check_qk_quant(qk_quant))) return rc;
   return check_kv_heads(H, H_kv);
 }
 
-int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, int qk_gran,
-                             size_t *q_i8, size_t *q_scale, size_t *k_i8, size_t *k_scale, size_t *k_mean,
+int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, int D, int qk_quant,
+                             size_t *q_codes, size_t *q_scale, size_t *k_codes, size_t *k_scale, size_t *k_mean,
                              size_t *v_fp8, size_t *v_scale) {
-  int rc = check_varlen(B, H, H_kv, total_q, total_k, 1, 1, D, qk_gran);
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, 1, 1, D, qk_quant);
   if (rc) return rc;
   const size_t rq = (size_t)varlen_rows(total_q, B, kBlkQ), rk = (size_t)varlen_rows(total_k, B, kKvPad);
-  if (q_i8) *q_i8 = (size_t)H * rq * D;
-  if (q_scale) *q_scale = (size_t)H * q_scales(rq, qk_gran) * sizeof(float);
-  if (k_i8) *k_i8 = (size_t)H_kv * rk * D;
-  if (k_scale) *k_scale = (size_t)H_kv * k_scales(rk, qk_gran) * sizeof(float);
+  if (q_codes) *q_codes = (size_t)H * code_bytes(rq, D, qk_quant);
+  if (q_scale) *q_scale = (size_t)H * q_scale_bytes(rq, D, qk_quant);
+  if (k_codes) *k_codes = (size_t)H_kv * code_bytes(rk, D, qk_quant);
+  if (k_scale) *k_scale = (size_t)H_kv * k_scale_bytes(rk, D, qk_quant);
   if (k_mean) *k_mean = (size_t)B * H_kv * D * sizeof(float);
   if (v_fp8) *v_fp8 = (size_t)H_kv * rk * D;
   if (v_scale) *v_scale = (size_t)B * H_kv * D * sizeof(float);
@@ -275,14 +286,14 @@ int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, i
 
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
-                                int max_seqlen_q, int max_seqlen_k, int D, int qk_gran, int8_t *q_i8,
-                                float *q_scale, int8_t *k_i8, float *k_scale, float *k_mean, void *stream) {
-  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_gran);
+                                int max_seqlen_q, int max_seqlen_k, int D, int qk_quant, void *q_codes,
+                                void *q_scale, void *k_codes, void *k_scale, float *k_mean, void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_quant);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
-  if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean)
+  if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean)
     return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(cu_seqlens_q, 4) ||
       !aligned(cu_seqlens_k, 4))
     return SAGE_ERR_INVALID_ARG;
@@ -291,10 +302,10 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
   memset(&a, 0, sizeof a);
   a.q = q;
   a.k = k;
-  a.q_i8 = q_i8;
-  a.k_i8 = k_i8;
-  a.q_scale = q_scale;
-  a.k_scale = k_scale;
+  a.q_i8 = (int8_t *)q_codes;
+  a.k_i8 = (int8_t *)k_codes;
+  a.q_scale = (float *)q_scale;
+  a.k_scale = (float *)k_scale;
   a.k_mean = k_mean;
   a.B = B;
   a.H = H;
@@ -310,13 +321,13 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
   a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
-  a.gran = qk_gran;
+  a.qk = qk_quant;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
 }
 
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
                         int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, float *v_mean, void *stream) {
-  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D, SAGE_GRAN_BLOCK);
+  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D, SAGE_QK_INT8_BLOCK);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (!v || !cu_seqlens_k || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
@@ -343,36 +354,36 @@ int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, i
   return launch_status(launch_quant_v(a, (hipStream_t)stream));
 }
 
-int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t *k_i8, const float *k_scale,
+int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                          const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
                          const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
-                         int qk_gran, void *stream) {
-  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_gran);
+                         int qk_quant, void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_quant);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
-  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
     return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)) ||
       !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
     return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   AttnArgs a;
   memset(&a, 0, sizeof a);
-  a.q_i8 = q_i8;
-  a.k_i8 = k_i8;
-  a.q_scale = q_scale;
-  a.k_scale = k_scale;
+  a.q_i8 = (const int8_t *)q_codes;
+  a.k_i8 = (const int8_t *)k_codes;
+  a.q_scale = (const float *)q_scale;
+  a.k_scale = (const float *)k_scale;
   a.v = v;
   a.v_scale = v_scale;
   a.v_mean = v_mean;
@@ -394,7 +405,7 @@ int sage_attn_fwd_varlen(const int8_t *q_i8, const float *q_scale, const int8_t 
   a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
-  a.gran = qk_gran;
+  a.qk = qk_quant;
   return launch_status(launch_attn(a, false, (hipStream_t)stream));
 }
 

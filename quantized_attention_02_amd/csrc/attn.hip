@@ -59,6 +59,7 @@ constexpr float kLog2_448 = 8.807354922057604f;
 template <int CH>
 __device__ __forceinline__ int swz(int chunk, int row) {
   if (CH == 8) return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+  if (CH == 2) return chunk ^ ((row >> 3) & 1);
   return chunk ^ ((row >> 2) & 3);
 }
 
@@ -74,6 +75,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint8_t *lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       rs, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 16, voff,
+      soff, 0, 0);
+}
+
+// As dma16_buf with 4 bytes a lane (lane i -> lds_base + 4 * i).
+__device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 4, voff,
       soff, 0, 0);
 }
 
@@ -186,6 +194,53 @@ struct TileCopy {
   }
 };
 
+// MXFP4 Q K^T: copy a K tile of packed E2M1 rows (TN x D/2 bytes, 16-byte
+// chunks swizzled by swz<D/32> so that the 16 lanes an LDS read serves hit 16
+// distinct bank groups), then its E8M0 scale bytes (TN x D/32, linear, 4 bytes
+// a lane), and, in pv fp8 mode, the FP8 V blocks as TileCopy does.
+template <int D, int TN, int WAVES>
+struct TileCopy4 {
+  static constexpr int ROWB = D / 2;                          // bytes of a packed K row
+  static constexpr int CPR = ROWB / 16;                       // 16-byte chunks a row (4 or 2)
+  static constexpr int NCOPY = TN * ROWB / 1024;              // 1 KiB wave-copies of codes
+  static constexpr int LOADS = (NCOPY + WAVES - 1) / WAVES;
+  static constexpr int SCB = TN * (D / 32);                   // scale bytes a tile
+  static constexpr int NSC = SCB / 256;                       // 256-byte wave-copies of scales
+  static constexpr int VCOPY = TN * D / 1024;                 // 1 KiB wave-copies of FP8 V
+  static constexpr int VLOADS = (VCOPY + WAVES - 1) / WAVES;
+  static_assert(NSC <= WAVES && SCB % 256 == 0, "scale copy split");
+  uint32_t koff[LOADS], voff[VLOADS];
+  __device__ __forceinline__ TileCopy4(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int krow = (wave + WAVES * i) * (1024 / ROWB) + lane / CPR;
+      koff[i] = (uint32_t)(krow * ROWB + 16 * swz<CPR>(lane % CPR, krow));
+    }
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int vrow = (wave + WAVES * i) * 16 + (lane >> 2);
+      voff[i] = (uint32_t)(vrow * 64 + 16 * swz<4>(lane & 3, vrow));
+    }
+  }
+  // tile j of the head: codes at j TN ROWB, scales at j SCB, V at j TN D
+  template <bool WITH_V>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t srs,
+                                        __amdgpu_buffer_rsrc_t vrs, int j, uint8_t *kbuf, uint8_t *vbuf, int wave,
+                                        int lane) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      if (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY)
+        dma16_buf(krs, koff[i], j * TN * ROWB, kbuf + (wave + WAVES * i) * 1024);
+    if (wave < NSC) dma4_buf(srs, (uint32_t)(4 * lane), j * SCB + 256 * wave, kbuf + TN * ROWB + 256 * wave);
+    if (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i)
+        if (VCOPY % WAVES == 0 || wave + WAVES * i < VCOPY)
+          dma16_buf(vrs, voff[i], j * TN * D, vbuf + (wave + WAVES * i) * 1024);
+    }
+  }
+};
+
 // pv fp16: the tile's raw 16-bit V rows (TN keys x D channels, 2D bytes a
 // row, as stored in the caller's layout) are copied into LDS as they are;
 // the PV MFMA's V^T operand is then read with the transposing LDS load
@@ -261,14 +316,17 @@ __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lan
 // TN: keys per loop iteration (64 or 128, i.e. one or two INT8 K blocks);
 // WPS: wavefronts per SIMD the register budget is sized for; WAVES: wavefronts
 // per work-group (32 query rows each); NBUF: LDS tile buffers (prefetch
-// distance NBUF - 1).  LANE: thread-level scale granularity -- one Q scale per
-// token (this lane's query) and one K scale per 16-key lane group (the keys
-// this half-wave holds of each 32-key sub-tile), so every lane dequantises
-// each sub-tile with one scale of its own; otherwise one scale per 32-query
-// block and per 64-key block.
-template <int D, int PV, int DT, bool CAUSAL, bool DUMP, bool LANE, int TN, int WPS, int WAVES, int NBUF>
+// distance NBUF - 1).  QK: the Q K^T operands.  0: INT8, one scale per
+// 32-query block and per 64-key block.  1 (LANE): INT8 with thread-level scale
+// granularity -- one Q scale per token (this lane's query) and one K scale per
+// 16-key lane group (the keys this half-wave holds of each 32-key sub-tile), so
+// every lane dequantises each sub-tile with one scale of its own.  2 (FP4):
+// MXFP4 -- E2M1 codes with an E8M0 scale per 32 channels of a token, on the
+// scaled FP4 MFMA, which applies the scales itself (fp32 scores).
+template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, int TN, int WPS, int WAVES, int NBUF>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
+  constexpr bool LANE = QK == 1, FP4 = QK == 2;
   constexpr int kThreads = WAVES * 64;
   constexpr int kBlockM = WAVES * 32;
   constexpr int NC = D / 32;
@@ -347,16 +405,27 @@ k_attn(const AttnArgs a) {
 
   // ---- Q fragments: B operand of S^T = K.Q^T; lane (q, half) holds
   //      Q[q][32c + 16*half .. +16] for chunk c
+  //      (FP4: Q[q][64c + 32*half .. +32] packed for chunk c < D / 64, and the
+  //      query's E8M0 bytes shifted so that byte 2c is this half's block of chunk c)
   v4i qf[NC];
   float dq = 0.0f;
+  uint32_t qsc = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
   if (active) {
-    const int8_t *qrow = a.q_i8 + (qs.row0 + qi) * D;
+    if constexpr (FP4) {
+      const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q_i8) + (qs.row0 + qi) * (D / 2);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
-    dq = LANE ? a.q_scale[qs.row0 + qi] : a.q_scale[(qs.row0 + qw) >> 5];
-  } else {
+      for (int c = 0; c < D / 64; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
+      const uint8_t *qsr = reinterpret_cast<const uint8_t *>(a.q_scale) + (qs.row0 + qi) * (D / 32);
+      const uint32_t w = D == 128 ? *reinterpret_cast<const uint32_t *>(qsr) : *reinterpret_cast<const uint16_t *>(qsr);
+      qsc = w >> (8 * hh);
+    } else {
+      const int8_t *qrow = a.q_i8 + (qs.row0 + qi) * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
+      dq = LANE ? a.q_scale[qs.row0 + qi] : a.q_scale[(qs.row0 + qw) >> 5];
+    }
   }
 
   int ntiles = (Sk + TN - 1) / TN;
@@ -370,15 +439,24 @@ k_attn(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[c][r] = 0.0f;
 
-  const int8_t *kbase = a.k_i8 + ks.row0 * D;
+  const int8_t *kbase = a.k_i8 + ks.row0 * (FP4 ? D / 2 : D);
   const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + ks.row0 * D;
-  const float *kscale = a.k_scale + (LANE ? ks.row0 >> 4 : ks.row0 >> 6);
+  const float *kscale = a.k_scale + (LANE ? ks.row0 >> 4 : ks.row0 >> 6);  // INT8 modes
+  const uint8_t *kscb = reinterpret_cast<const uint8_t *>(a.k_scale) + ks.row0 * (D / 32);  // FP4
   const HeadView hv{ks.base, ks.stride};  // pv fp16: the caller's V
-  const TileCopy<D, TN, WAVES> copy(wave, lane);
+  const TileCopy<D, TN, WAVES> copy(wave, lane);     // INT8 K
+  const TileCopy4<D, TN, WAVES> copy4(wave, lane);   // FP4 K
   const VCopy16<D, TN, WAVES> vcopy(lane);
-  const int kbytes = ntiles * TN * D;  // this head's K (and V) rows that the tiles read
+  const int vbytes = ntiles * TN * D;                // this head's V (and INT8 K) bytes that the tiles read
+  const int kbytes = FP4 ? vbytes / 2 : vbytes;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kbytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase, kbytes);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscb, ntiles * TN * (D / 32));  // FP4 K scales
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase,
+                                               PV == 0 ? vbytes : kbytes);  // (pv fp16 copies V itself)
+  auto issue_tile = [&](int j, uint8_t *kb, uint8_t *vb) {
+    if constexpr (FP4) copy4.template issue<PV == 0>(krs, srs, vrs, j, kb, vb, wave, lane);
+    else copy.template issue<PV == 0>(krs, vrs, j * TN * D, kb, vb, wave);
+  };
 
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
   auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
@@ -405,21 +483,44 @@ k_attn(const AttnArgs a) {
       // ---- S^T = K . Q^T for the NT 32-key sub-tiles, one INT8 K block (two
       //      sub-tiles) after the other, so that the first block's row max and
       //      int -> float conversion can run while the second block's MFMAs do
-      v16i s[NT];
+      using acc_t = typename std::conditional<FP4, v16f, v16i>::type;
+      acc_t s[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s[t] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[t][r] = 0;
       auto qk_block = [&](int blk) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
+        if constexpr (FP4) {
+          // per key: its E8M0 word, shifted so that byte 2c is this half's block of chunk c
 #pragma unroll
           for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
             const int row = 32 * t + qn;
-            const v4i kf = *reinterpret_cast<const v4i *>(kb + row * D + 16 * swz<KCH>(2 * c + hh, row));
-            s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[c], s[t], 0, 0, 0);
+            const uint8_t *ksr = kb + TN * (D / 2) + row * (D / 32);
+            const uint32_t kw =
+                D == 128 ? *reinterpret_cast<const uint32_t *>(ksr) : *reinterpret_cast<const uint16_t *>(ksr);
+            const uint32_t ksc = kw >> (8 * hh);
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) {
+              const v4i kf = *reinterpret_cast<const v4i *>(kb + row * (D / 2) + 16 * swz<D / 32>(2 * c + hh, row));
+              const v8i ka = {kf[0], kf[1], kf[2], kf[3], 0, 0, 0, 0};
+              const v8i qa = {qf[c][0], qf[c][1], qf[c][2], qf[c][3], 0, 0, 0, 0};
+              s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa, s[t], 4, 4, 0, (int)(ksc >> (16 * c)), 0,
+                                                                    (int)(qsc >> (16 * c)));
+            }
           }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
+              const int row = 32 * t + qn;
+              const v4i kf = *reinterpret_cast<const v4i *>(kb + row * D + 16 * swz<KCH>(2 * c + hh, row));
+              s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[c], s[t], 0, 0, 0);
+            }
+        }
       };
       auto dump_s = [&]() {
-        if (DUMP && bh == a.dump_bh && qi < a.S) {
+        if (DUMP && !FP4 && bh == a.dump_bh && qi < a.S) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -436,6 +537,9 @@ k_attn(const AttnArgs a) {
       if constexpr (LANE) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) c2[t] = (dq * (hh ? ks[2 * t + 1] : ks[2 * t])) * a.sm2;
+      } else if constexpr (FP4) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) c2[blk] = a.sm2;  // the MFMA applied the micro-scales
       } else {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
@@ -448,8 +552,22 @@ k_attn(const AttnArgs a) {
       // ---- per INT8 block: row max of the int32 sums (c2 > 0 per block) and
       //      the sums converted to float
       int mxb[NC2];  // int32 max per scale (one c2 each)
+      float mxf[NB];  // FP4: fp32 max per block
       float f[16 * NT];
       auto max_convert = [&](int blk, int mlim, auto mask_tag) {
+        if constexpr (FP4) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int t = 2 * blk; t < 2 * blk + 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool out = decltype(mask_tag)::value && 32 * t + 8 * (r >> 2) + (r & 3) > mlim;
+              f[16 * t + r] = out ? -INFINITY : s[t][r];
+              mx = fmaxf(mx, f[16 * t + r]);
+            }
+          mxf[blk] = mx;
+          return;
+        }
         int mx = INT_MIN;
 #pragma unroll
         for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
@@ -489,9 +607,14 @@ k_attn(const AttnArgs a) {
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, mlim, std::true_type());
       }
       float mt = -INFINITY;
+      if constexpr (FP4) {
 #pragma unroll
-      for (int i = 0; i < NC2; ++i)
-        if (mxb[i] != INT_MIN) mt = fmaxf(mt, (float)mxb[i] * c2[i]);
+        for (int blk = 0; blk < NB; ++blk) mt = fmaxf(mt, mxf[blk] * c2[blk]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NC2; ++i)
+          if (mxb[i] != INT_MIN) mt = fmaxf(mt, (float)mxb[i] * c2[i]);
+      }
       mt = halves_max(mt);
       const float mn = fmaxf(m, mt);
       alpha = __builtin_amdgcn_exp2f(m - mn);
@@ -591,9 +714,10 @@ k_attn(const AttnArgs a) {
   //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next
   constexpr int LPT = (PV == 0 ? 2 : 1) * TN * D / 1024 / WAVES;  // DMA instructions per tile per wavefront
   static_assert(NBUF == 2 || (TN * D / 1024) % WAVES == 0, "partial vm waits need an even copy split");
+  static_assert(NBUF == 2 || !FP4, "partial vm waits assume the INT8 copy counts");
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
-    if (u < ntiles) copy.template issue<PV == 0>(krs, vrs, u * TN * D, kbuf[u], vbuf[PV == 0 ? u : 0], wave);
+    if (u < ntiles) issue_tile(u, kbuf[u], vbuf[PV == 0 ? u : 0]);
   wait_vm<0>();
   __syncthreads();
   for (int j0 = 0; j0 < ntiles; j0 += NBUF) {
@@ -603,7 +727,7 @@ k_attn(const AttnArgs a) {
       if (j >= ntiles) break;
       const int jn = j + NBUF - 1;  // prefetch target, into the buffer freed by tile j - 1
       const int un = (u + NBUF - 1) % NBUF;
-      if (jn < ntiles) copy.template issue<PV == 0>(krs, vrs, jn * TN * D, kbuf[un], vbuf[PV == 0 ? un : 0], wave);
+      if (jn < ntiles) issue_tile(jn, kbuf[un], vbuf[PV == 0 ? un : 0]);
       tile(j, kbuf[u], vbuf[PV == 0 ? u : 0]);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
@@ -655,23 +779,25 @@ struct TileCfg {
   static constexpr int NBUF = PV == 0 ? SAGE_ATTN_NBUF_FP8 : 2;
 };
 
-template <int D, int PV, int DT, bool CAUSAL, bool LANE>
+template <int D, int PV, int DT, bool CAUSAL, int QK>
 static hipError_t launch5(const AttnArgs &a, bool dump, hipStream_t st) {
   using C = TileCfg<PV>;
   AttnArgs b = a;
   b.nmblk = (a.S + 32 * C::WAVES - 1) / (32 * C::WAVES);
   const dim3 grid(a.B * a.H * b.nmblk), block(64 * C::WAVES);
   if (dump)
-    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, true, LANE, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st, b);
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, QK != 2, QK, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st,
+                       b);  // (the API rejects the dump for MXFP4)
   else
-    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, LANE, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st,
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st,
                        b);
   return hipGetLastError();
 }
 
 template <int D, int PV, int DT, bool CAUSAL>
 static hipError_t launch4(const AttnArgs &a, bool dump, hipStream_t st) {
-  return a.gran == 1 ? launch5<D, PV, DT, CAUSAL, true>(a, dump, st) : launch5<D, PV, DT, CAUSAL, false>(a, dump, st);
+  if (a.qk == 2) return launch5<D, PV, DT, CAUSAL, 2>(a, dump, st);
+  return a.qk == 1 ? launch5<D, PV, DT, CAUSAL, 1>(a, dump, st) : launch5<D, PV, DT, CAUSAL, 0>(a, dump, st);
 }
 
 template <int D, int PV, int DT>

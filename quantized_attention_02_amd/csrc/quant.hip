@@ -103,6 +103,9 @@ __device__ inline Seg v_seg(const QuantVArgs &a, int b, int h) {
                   : fixed_seg(a.layout, b, h, a.H, a.S, a.nk * kBlkK, D);
 }
 __device__ inline int ceil_div(int x, int m) { return (x + m - 1) / m; }
+// bytes of one quantised Q/K row: INT8 codes, or packed E2M1 pairs (MXFP4)
+template <int D>
+__device__ inline int code_row_bytes(const QuantQKArgs &a) { return a.qk == 2 ? D / 2 : D; }
 
 // Thread layout of the chunk passes: G = D / 8 channel groups (16 bytes of a
 // 16-bit row) x R = 256 / G rows; the chunk's rows are loaded kUnroll at a
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
   const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;  // bh: K head (b, h_kv)
   const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
   if (chunk >= n_chunks(sg.S)) return;
-  chunk_reduce<DT, D, false>((const uint16_t *)a.k, sg, chunk, a.k_i8 + sg.row0 * D);
+  chunk_reduce<DT, D, false>((const uint16_t *)a.k, sg, chunk, a.k_i8 + sg.row0 * code_row_bytes<D>(a));
 }
 
 // ---------------------------------------------------------------------------
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
   if (i >= (long long)a.B * a.H_kv * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
   const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
-  const double *part = reinterpret_cast<const double *>(a.k_i8 + sg.row0 * D);
+  const double *part = reinterpret_cast<const double *>(a.k_i8 + sg.row0 * code_row_bytes<D>(a));
   const int nch = n_chunks(sg.S);
   double v[kMaxChunks];
 #pragma unroll
@@ -346,6 +349,81 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
     for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)(uint8_t)to_i8(x[u][i], inv[u]) << (8 * (i & 3));
     v2i out = {(int)w[0], (int)w[1]};
     *reinterpret_cast<v2i *>(a.k_i8 + (hv.row0 + blk * kBlkK + row) * D + c8) = out;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 quantisation of one block of ROWS tokens (32 of Q, or 64 of K - k_mean):
+// every 32-channel block of a token shares an E8M0 scale 2^e,
+// e = floor(log2(amax)) - 2 clamped to [-127, 127] (-127 when amax = 0), and
+// its values become E2M1(x / 2^e), round to nearest even, saturating at 6
+// (the OCP Microscaling shared-exponent rule; the FP4 micro-scaling of the
+// "Kairos" guide, section 2.2).  A thread converts 8 consecutive channels; the
+// 4 threads of a 32-channel block are consecutive lanes.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t e2m1_code(float y) {  // y = x / 2^e, |y| < 8
+  const float v = fabsf(y);
+  const uint32_t m = v <= 0.25f ? 0u : v < 0.75f ? 1u : v <= 1.25f ? 2u : v < 1.75f ? 3u
+                     : v <= 2.5f ? 4u : v < 3.5f ? 5u : v <= 5.0f ? 6u : 7u;  // ties to the even neighbour
+  return m | (y < 0.0f ? 8u : 0u);
+}
+
+__device__ inline int mx_exponent(float amax) {  // floor(log2(amax)) - 2, clamped; amax >= 0
+  if (amax == 0.0f) return -127;
+  const uint32_t b = __float_as_uint(amax);
+  const int ex = (int)(b >> 23);
+  const int fl = ex ? ex - 127 : 31 - __builtin_clz(b & 0x7fffffu) - 149;  // subnormal: leading mantissa bit
+  return min(max(fl - 2, -127), 127);
+}
+
+template <int DT, int D, bool IS_K>
+__global__ __launch_bounds__(kThreads) void k_mxfp4(const QuantQKArgs a) {
+  constexpr int ROWS = IS_K ? kBlkK : kBlkQ;
+  constexpr int vec_per_row = D / 8;
+  constexpr int nvec = ROWS * vec_per_row;
+  constexpr int U = (nvec + kThreads - 1) / kThreads;
+  __shared__ float mean[D];
+  const int tid = threadIdx.x;
+  const int nblk = IS_K ? a.nk : a.nq;
+  const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+  const int hn = IS_K ? a.H_kv : a.H;
+  const Seg hv = IS_K ? k_seg<D>(a, bh / hn, bh % hn) : q_seg<D>(a, bh / hn, bh % hn);
+  if (IS_K ? blk >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK) : blk >= ceil_div(hv.S, kBlkQ)) return;
+  if (IS_K) {
+    if (tid < D) mean[tid] = a.k_mean[(long long)bh * D + tid];
+    __syncthreads();
+  }
+  const uint16_t *x = (const uint16_t *)(IS_K ? a.k : a.q);
+  uint8_t *codes = reinterpret_cast<uint8_t *>(IS_K ? a.k_i8 : a.q_i8);
+  uint8_t *scales = reinterpret_cast<uint8_t *>(IS_K ? a.k_scale : a.q_scale);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = tid + u * kThreads;  // uniform over the wavefront: nvec is a multiple of 64
+    if (vi >= nvec) break;
+    const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
+    const int s = blk * ROWS + row;
+    float v[8];
+    if (s < hv.S) {
+      load8<DT>(x + hv.base + (long long)s * hv.stride + c8, v);
+      if (IS_K)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] - mean[c8 + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int e = mx_exponent(amax);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(__builtin_ldexpf(v[i], -e)) << (4 * i);
+    const long long r = hv.row0 + (long long)blk * ROWS + row;
+    *reinterpret_cast<uint32_t *>(codes + r * (D / 2) + c8 / 2) = w;
+    if (c8 % 32 == 0) scales[r * (D / 32) + c8 / 32] = (uint8_t)(e + 127);
   }
 }
 
@@ -532,10 +610,12 @@ static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
   const int gd = (bhk * D + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads), 0,
                      stream, a);
-  if (a.gran == 1) hipLaunchKernelGGL((k_qquant<DT, D, true>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
+  if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, false>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
+  else if (a.qk == 1) hipLaunchKernelGGL((k_qquant<DT, D, true>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((k_qquant<DT, D, false>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
-  if (a.gran == 1) hipLaunchKernelGGL((k_kquant<DT, D, true>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
+  if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, true>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
+  else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, true>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((k_kquant<DT, D, false>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
 }
 

@@ -129,7 +129,7 @@ struct QuantQKArgs {
   int varlen;                           // packed batch: tables below, S unused
   SeqTable sq, sk;
   long long rows_q, rows_k;  // buffer rows per head (packed batch)
-  int gran;                  // 0: per-block scales, 1: per-lane (Q per token, K per 16-key group)
+  int qk;                    // Q/K quantisation: 0 INT8 per block, 1 INT8 per lane, 2 MXFP4
 };
 
 struct QuantVArgs {
@@ -159,7 +159,7 @@ struct AttnArgs {
   int varlen;  // packed batch: tables below, S = the longest query sequence
   SeqTable sq, sk;
   long long rows_q, rows_k;
-  int gran;  // scale granularity of q_scale / k_scale (as QuantQKArgs::gran)
+  int qk;  // Q/K quantisation of q_codes / k_codes (as QuantQKArgs::qk)
 };
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);

@@ -31,7 +31,7 @@ QUANT_CASES = [
 @pytest.mark.parametrize("w", QUANT_CASES, ids=[w.name for w in QUANT_CASES])
 def test_lane_quant_bit_exact(w):
     q, k, v = G.inputs(w)
-    bufs, _, _ = G.run(w, gran="lane")
+    bufs, _, _ = G.run(w, qk_quant="int8_lane")
     dt = O.DTYPES[w.dtype]
     q8, qs = bufs.q_i8.cpu().numpy(), bufs.q_scale.cpu().numpy()
     k8, ks, km = bufs.k_i8.cpu().numpy(), bufs.k_scale.cpu().numpy(), bufs.k_mean.cpu().numpy()
@@ -70,7 +70,7 @@ def _ids(cases):
 
 @pytest.mark.parametrize("w,causal,pv", ATTN_CASES, ids=_ids(ATTN_CASES))
 def test_lane_attn_matches_oracle(w, causal, pv):
-    _, out, _ = G.run(w, causal=causal, pv=pv, gran="lane")
+    _, out, _ = G.run(w, causal=causal, pv=pv, qk_quant="int8_lane")
     got = G.out_logical(out, w)
     q, k, v = G.inputs(w)
     ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal,
@@ -85,7 +85,7 @@ def test_lane_attn_matches_oracle(w, causal, pv):
 def test_lane_qk_int32_dump_bit_exact():
     w = synth.custom(2, 4, 300, 128, Hkv=2, seed=921)
     b, h = 1, 3
-    bufs, out, dump = G.run(w, causal=True, dump_head=(b, h), gran="lane")
+    bufs, out, dump = G.run(w, causal=True, dump_head=(b, h), qk_quant="int8_lane")
     q, k, _ = G.inputs(w)
     dt = O.DTYPES[w.dtype]
     rq8, _ = O.quant_q_head(O.decode16(O.head(q, w.layout, b, h), dt), 1)
@@ -99,7 +99,7 @@ def test_lane_full_size_sampled():
     """The headline shape with lane granularity, in the benchmark's launch
     configuration: sampled rows of sampled heads."""
     w = W["snippet_b2h32s4096d128"]
-    _, out, _ = G.run(w, gran="lane")
+    _, out, _ = G.run(w, qk_quant="int8_lane")
     got = G.out_logical(out, w)
     assert np.isfinite(got).all()
     q, k, v = G.inputs(w)
@@ -121,7 +121,7 @@ def test_lane_closer_to_exact_on_varying_tokens():
     ex = np.stack([ex[(0, h)] for h in range(w.H)])[None]
     errs = {}
     for gran in ("block", "lane"):
-        _, out, _ = G.run(w, gran=gran)
+        _, out, _ = G.run(w, qk_quant={"block": "int8", "lane": "int8_lane"}[gran])
         errs[gran] = G.rel_l1(G.out_logical(out, w), ex)
     print("rel L1 vs exact:", errs)
     assert errs["lane"] < errs["block"], errs

@@ -71,7 +71,7 @@ def test_smooth_v_with_lane_granularity_and_varlen():
     qd, kd, vd = (G.to_device(x, w.dtype) for x in (q, k, v))
     cud = [torch.from_numpy(c).cuda() for c in (cq, ck)]
     out = qa.sageattn_varlen(qd, kd, vd, cud[0], cud[1], max(w.seqlens_q), max(w.seqlens_k), is_causal=True,
-                             qk_gran="lane", smooth_v=True)
+                             qk_quant="int8_lane", smooth_v=True)
     torch.cuda.synchronize()
     got = O.decode16(G.to_u16(out), O.F16)
     ref = O.attn_varlen(q, k, v, cq, ck, O.F16, is_causal=True, gran="lane", smooth_v=True)

@@ -43,14 +43,14 @@ def _inputs(w):
     return (q, k, v, cq, ck), dev, cud
 
 
-def _run(w, causal, pv, dev, cud, gran="block"):
+def _run(w, causal, pv, dev, cud, qk_quant="int8"):
     import torch
 
     import quantized_attention_02_amd as qa
 
     qd, kd, vd = dev
     bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max(w.seqlens_q), max(max(w.seqlens_k), 1), pv,
-                              qk_gran=gran)
+                              qk_quant=qk_quant)
     out = torch.full_like(qd, float("nan"))
     qa.attn_fwd_varlen(bufs, vd, out, cud[0], cud[1], causal, None, pv)
     torch.cuda.synchronize()
@@ -180,7 +180,7 @@ def test_varlen_lane_granularity(w):
     import quantized_attention_02_amd as qa
 
     (q, k, v, cq, ck), dev, cud = _inputs(w)
-    bufs, out = _run(w, True, "fp8", dev, cud, gran="lane")
+    bufs, out = _run(w, True, "fp8", dev, cud, qk_quant="int8_lane")
     dt = O.DTYPES[w.dtype]
     qs, ks = bufs.q_scale.cpu().numpy(), bufs.k_scale.cpu().numpy()
     for b in range(w.B):
