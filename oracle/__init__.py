@@ -69,7 +69,8 @@ def lib():
         for name in ("orc_decode16", "orc_encode16", "orc_e4m3_encode_n", "orc_int8_quant_block",
                      "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_k_head_lane",
                      "orc_quant_v_head", "orc_quant_v_head_smooth", "orc_qk_int32_head", "orc_attn_head_rows",
-                     "orc_attn_exact_head", "orc_mxfp4_quant_rows", "orc_quant_k_head_mxfp4", "orc_qk_mxfp4_rows"):
+                     "orc_attn_exact_head", "orc_mxfp4_quant_rows", "orc_quant_k_head_mxfp4", "orc_qk_mxfp4_rows",
+                     "orc_quant_q_head_smooth", "orc_qk_delta_head"):
             getattr(L, name).restype = None
         L.orc_lane_group.restype = ctypes.c_int
         L.orc_lane_group.argtypes = [ctypes.c_int]
@@ -192,6 +193,30 @@ def quant_k_head(kf: np.ndarray, blk: int, smooth: bool = True):
     return codes, scales, mean
 
 
+def quant_q_head_smooth(qf: np.ndarray, blk: int, blk_scale: int | None = None):
+    """Smoothed Q: (codes, scales, block means [nb, D]) of Q minus each blk-token
+    block's channel means; INT8 scale blocks of blk_scale tokens (default blk)."""
+    qf = _f32(qf)
+    S, D = qf.shape
+    bs = blk if blk_scale is None else blk_scale
+    codes = np.empty((S, D), np.int8)
+    scales = np.empty((S + bs - 1) // bs, np.float32)
+    qmean = np.empty(((S + blk - 1) // blk, D), np.float32)
+    lib().orc_quant_q_head_smooth(_p(qf, ctypes.c_float), S, D, blk, bs, _p(codes, ctypes.c_int8),
+                                  _p(scales, ctypes.c_float), _p(qmean, ctypes.c_float))
+    return codes, scales, qmean
+
+
+def qk_delta_head(qmean: np.ndarray, kc: np.ndarray) -> np.ndarray:
+    """delta[b][n] = qmean[b] . kc[n] (binary64, rounded to fp32); kc = K - k_mean."""
+    qmean, kc = _f32(qmean), _f32(kc)
+    nb, D = qmean.shape
+    S = kc.shape[0]
+    out = np.empty((nb, S), np.float32)
+    lib().orc_qk_delta_head(_p(qmean, ctypes.c_float), nb, _p(kc, ctypes.c_float), S, D, _p(out, ctypes.c_float))
+    return out
+
+
 def lane_group(n: int) -> int:
     """K scale group of key n under thread-level granularity (see sage_oracle.c)."""
     return int(lib().orc_lane_group(int(n)))
@@ -280,7 +305,7 @@ def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
                    pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False, v_mean=None,
-                   qk=None) -> np.ndarray:
+                   qk=None, delta=None, blk_d=BLK_Q) -> np.ndarray:
     """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
 
     blk_q / blk_k: tokens per INT8 scale of Q / K (k_lane: K scales per lane group
@@ -304,6 +329,11 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     vm = None if v_mean is None else _f32(v_mean)
     if vm is not None and pv_mode != PV_FP8:
         raise ValueError("V smoothing applies to the FP8 PV product only")
+    dl = None
+    if delta is not None:  # smoothed Q: [ceil(Sq / blk_q), S] fp32, the pre-processing stage
+        dl = _f32(delta)
+        if dl.shape != ((Sq + blk_d - 1) // blk_d, S):
+            raise ValueError("delta must be [query blocks, S_k]")
     qkr = None
     if qk is not None:
         qkr = np.ascontiguousarray(qk, np.float32)
@@ -315,7 +345,7 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
                              None if vm is None else _p(vm, ctypes.c_float), _p(vf, ctypes.c_float),
                              in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
                              _p(rows, ctypes.c_int), rows.size, None if qkr is None else _p(qkr, ctypes.c_float),
-                             _p(out, ctypes.c_float))
+                             None if dl is None else _p(dl, ctypes.c_float), blk_d, _p(out, ctypes.c_float))
     return out
 
 
@@ -386,8 +416,11 @@ def kv_head(h: int, H: int, Hkv: int) -> int:
 
 def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
          heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block",
-         smooth_v=False, qk_format="int8"):
+         smooth_v=False, qk_format="int8", smooth_q=False):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
+
+    smooth_q (INT8 Q K^T): Q minus its 32-token block means is quantised, and the
+    attention adds the pre-processing term (block mean . (K - k_mean)) * sm_scale.
 
     qk_format "fp4": Q and K - mean in MXFP4 (E2M1 with an E8M0 scale per 32
     channels of a token) instead of INT8 blocks; gran is then not used.
@@ -423,8 +456,11 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
             q8, qs = np.zeros(qf.shape, np.int8), np.zeros(1, np.float32)
             k8, ks = np.zeros(kf.shape, np.int8), np.zeros(1, np.float32)
         elif qk_format == "int8":
-            q8, qs = quant_q_head(qf, blk_q)
-            k8, ks, _ = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
+            if smooth_q:
+                q8, qs, qm = quant_q_head_smooth(qf, BLK_Q, blk_q)
+            else:
+                q8, qs = quant_q_head(qf, blk_q)
+            k8, ks, km = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
         else:
             raise ValueError(qk_format)
         vm = None
@@ -436,7 +472,9 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
                                      sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k,
-                                     tile_k=tile_k, k_lane=lane, v_mean=vm, qk=qk)
+                                     tile_k=tile_k, k_lane=lane, v_mean=vm, qk=qk,
+                                     delta=qk_delta_head(qm, (kf - km[None, :]).astype(np.float32)) if smooth_q
+                                     else None)
     return res
 
 

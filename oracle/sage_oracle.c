@@ -239,6 +239,45 @@ void orc_quant_k_head(const float *k, int S, int D, int blk, int smooth, int8_t 
 int orc_lane_group(int n) { return 2 * (n >> 5) + ((n >> 2) & 1); }
 
 /*
+ * Smoothed Q ([SA2, SageAttention2方法]: subtract the mean of each block of Q;
+ * together with K smoothing the product splits into a pre-processing stage and
+ * the attention stage).  Reading: the block is the INT8 scale block of `blk`
+ * tokens; its channel means are summed in binary64 over the block's tokens,
+ * divided by their number and rounded once to fp32; the block's values minus
+ * its means (one fp32 subtraction each) are quantised by orc_quant_q_head's
+ * rule with the same blocks (or per token, blk_scale = 1).  qmean: [nb][D].
+ */
+void orc_quant_q_head_smooth(const float *q, int S, int D, int blk, int blk_scale, int8_t *codes,
+                             float *scales, float *qmean) {
+    size_t n = (size_t)S * D;
+    int nb = (S + blk - 1) / blk;
+    float *qs = (float *)malloc((n ? n : 1) * sizeof(float));
+    for (int b = 0; b < nb; ++b) {
+        int r0 = b * blk, r1 = r0 + blk < S ? r0 + blk : S;
+        orc_channel_mean(q + (size_t)r0 * D, r1 - r0, D, qmean + (size_t)b * D);
+        for (int t = r0; t < r1; ++t)
+            for (int d = 0; d < D; ++d) qs[(size_t)t * D + d] = q[(size_t)t * D + d] - qmean[(size_t)b * D + d];
+    }
+    orc_quant_q_head(qs, S, D, blk_scale, codes, scales);
+    free(qs);
+}
+
+/*
+ * The pre-processing stage of smoothed Q: delta[b][n] = fp32( sum_d qmean[b][d] * kc[n][d] )
+ * in binary64, kc = K minus its channel mean (fp32 values, as orc_quant_k_head forms
+ * them).  The attention adds delta[query block][n] * sm_scale to the dequantised score.
+ */
+void orc_qk_delta_head(const float *qmean, int nb, const float *kc, int S, int D, float *delta) {
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < nb; ++b)
+        for (int n = 0; n < S; ++n) {
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d) acc += (double)qmean[(size_t)b * D + d] * (double)kc[(size_t)n * D + d];
+            delta[(size_t)b * S + n] = (float)acc;
+        }
+}
+
+/*
  * K with thread-level granularity: optional mean subtraction as in
  * orc_quant_k_head, then one INT8 scale per key group of orc_lane_group
  * (2 * ceil(S / 32) groups; a group without keys gets scale 0).
@@ -406,7 +445,9 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  * Per key tile:
  *   s_n   = float(q8_i . k8_n) * ((dq_i * dk_blk(n)) * sm_scale)     (dequantise)
  *           or, with the FP4 product (qk != NULL): s_n = qk[r][n] * sm_scale, qk from
- *           orc_qk_mxfp4_rows (already dequantised by the micro-scales)
+ *           orc_qk_mxfp4_rows (already dequantised by the micro-scales);
+ *           smoothed Q (delta != NULL): s_n += delta[i / blk_d][n] * sm_scale (blk_d: the
+ *           tokens of a Q smoothing block)
  *   s_n   = -inf for keys n >= S, and for n > i when causal ([GUIDE, 性能调优实战] is_causal;
  *           key n and query i count from the start of their sequences)
  *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first tile)
@@ -429,7 +470,8 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
-                        int pv_mode, const int *rows, int nrows, const float *qk, float *out) {
+                        int pv_mode, const int *rows, int nrows, const float *qk, const float *delta,
+                        int blk_d, float *out) {
     int ntile = (S + tile_k - 1) / tile_k;
 #pragma omp parallel
     {
@@ -458,6 +500,7 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         float c = (dq * k_scale[kg]) * sm_scale;
                         s[t] = (float)dot_i8(q8 + (size_t)i * D, k8 + (size_t)n * D, D) * c;
                     }
+                    if (delta && s[t] != -INFINITY) s[t] = s[t] + delta[(size_t)(i / blk_d) * S + n] * sm_scale;
                     if (s[t] > mt) mt = s[t];
                 }
                 float mnew = m > mt ? m : mt;

@@ -62,6 +62,9 @@ void orc_quant_q_head(const float *q, int S, int D, int blk, int8_t *codes, floa
 void orc_quant_k_head(const float *k, int S, int D, int blk, int smooth,
                       int8_t *codes, float *scales, float *mean);
 int orc_lane_group(int n);
+void orc_quant_q_head_smooth(const float *q, int S, int D, int blk, int blk_scale, int8_t *codes,
+                             float *scales, float *qmean);
+void orc_qk_delta_head(const float *qmean, int nb, const float *kc, int S, int D, float *delta);
 void orc_quant_k_head_lane(const float *k, int S, int D, int smooth,
                            int8_t *codes, float *scales, float *mean);
 void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scales);
@@ -78,7 +81,8 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
                         const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
                         int in_dtype, int S, int D, int is_causal, float sm_scale,
-                        int pv_mode, const int *rows, int nrows, const float *qk, float *out);
+                        int pv_mode, const int *rows, int nrows, const float *qk, const float *delta,
+                        int blk_d, float *out);
 void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, int D,
                          int is_causal, double sm_scale, const int *rows, int nrows,
                          double *out);

@@ -814,4 +814,72 @@ def pin_fp4_pipeline_vs_exact():
         assert rel_l1(f4[hd], ex[hd]) > rel_l1(i8[hd], ex[hd])
 
 
+# ------------------------------------------------------------------ Q smoothing
+def pin_smooth_q_means_and_codes():
+    """Smoothed Q: each 32-token block's channel means are the exact rational
+    means rounded once (ragged last block included), and the codes are the INT8
+    rule applied to Q minus the means (one fp32 subtraction each)."""
+    S, D = 75, 64  # blocks of 32, 32 and 11 tokens
+    qf = _rand_head(S, D, seed=81)[0] + np.float32(2.5)
+    q8, qs, qm = O.quant_q_head_smooth(qf, 32)
+    assert qm.shape == (3, D) and qs.shape == (3,)
+    for b, (r0, r1) in enumerate(((0, 32), (32, 64), (64, 75))):
+        for d in (0, 17, 63):
+            exact = sum(Fraction(float(x)) for x in qf[r0:r1, d]) / (r1 - r0)
+            assert qm[b, d] == np.float32(float(exact)), (b, d)
+    qc = np.concatenate([(qf[r0:r1] - qm[b][None, :]).astype(np.float32)
+                         for b, (r0, r1) in enumerate(((0, 32), (32, 64), (64, 75)))])
+    r8, rs = O.quant_q_head(qc, 32)
+    assert np.array_equal(q8, r8) and np.array_equal(qs.view(np.uint32), rs.view(np.uint32))
+    # per-token scales with the same 32-token means
+    l8, ls, lm = O.quant_q_head_smooth(qf, 32, 1)
+    assert np.array_equal(lm, qm) and np.array_equal(l8, O.quant_q_head(qc, 1)[0]) and ls.shape == (S,)
+
+
+def pin_qk_delta_bruteforce():
+    qm = _rand_head(5, 64, seed=82)[0]
+    kc = _rand_head(90, 64, seed=83)[1]
+    got = O.qk_delta_head(qm, kc)
+    ref = (qm.astype(np.float64) @ kc.astype(np.float64).T).astype(np.float32)
+    assert np.allclose(got, ref, rtol=2e-7, atol=1e-30)
+
+
+def pin_smooth_q_constant_blocks():
+    """Tokens equal within each 32-token block: the smoothed codes vanish and the
+    scores are the pre-processing term alone, i.e. fp32(q_b . (K - k_mean)) *
+    sm_scale -- the attention equals the one computed from those exact scores."""
+    S, D = 96, 64
+    qf, kf, vf = _rand_head(S, D, seed=84)
+    qf = np.repeat(qf[::32], 32, axis=0)[:S].copy()
+    q8, qs, qm = O.quant_q_head_smooth(qf, 32)
+    assert not q8.any() and not qs.any()
+    k8, ks, km = O.quant_k_head(kf, 64, True)
+    kc = (kf - km[None, :]).astype(np.float32)
+    delta = O.qk_delta_head(qm, kc)
+    exact_rows = (qf.astype(np.float64) @ kc.astype(np.float64).T).astype(np.float32)
+    assert np.allclose(delta[np.arange(S) // 32], exact_rows, rtol=1e-6, atol=1e-6)
+    v8, vs = O.quant_v_head(vf)
+    for causal in (False, True):
+        got = O.attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=F16, is_causal=causal, sm_scale=0.125,
+                               pv_mode=O.PV_FP8, delta=delta)
+        z8, z1 = np.zeros((S, D), np.int8), np.zeros(1, np.float32)
+        ref = O.attn_head_rows(z8, z1, z8, z1, v8, vs, vf, in_dtype=F16, is_causal=causal, sm_scale=0.125,
+                               pv_mode=O.PV_FP8, qk=delta[np.arange(S) // 32])
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), causal
+
+
+def pin_smooth_q_more_accurate_with_q_offsets():
+    """A per-channel Q offset inflates each block's INT8 scale; subtracting the
+    block means recovers the resolution: several times closer to exact attention."""
+    w = synth.custom(1, 2, 256, 64, seed=85)
+    q, k, v = synth.make_qkv(w)
+    rng = np.random.default_rng(85)
+    q = O.encode16(O.decode16(q, F16) + rng.normal(0, 8, (1, 2, 1, 64)).astype(np.float32), F16)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    sm = O.attn(q, k, v, F16, "HND", smooth_q=True, pv_mode=O.PV_FP16)
+    pl = O.attn(q, k, v, F16, "HND", pv_mode=O.PV_FP16)
+    for hd in ex:
+        assert rel_l1(sm[hd], ex[hd]) < 0.3 * rel_l1(pl[hd], ex[hd]), hd
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,6 +50,10 @@ MUTANTS = [
     ("mx_qk_first_block_scale", "ldexp(blk, (int)qe[(size_t)i * nb + b] - 127", "ldexp(blk, (int)qe[(size_t)i * nb] - 127"),
     ("mx_qk_scale_sign", "+ (int)ke[(size_t)n * nb + b] - 127);", "- (int)ke[(size_t)n * nb + b] + 127);"),
     ("fp4_scores_without_sm_scale", "s[t] = qk[(size_t)r * S + n] * sm_scale;", "s[t] = qk[(size_t)r * S + n];"),
+    ("smooth_q_not_subtracted", "qs[(size_t)t * D + d] = q[(size_t)t * D + d] - qmean[(size_t)b * D + d];",
+     "qs[(size_t)t * D + d] = q[(size_t)t * D + d];"),
+    ("delta_wrong_block", "delta[(size_t)(i / blk_d) * S + n] * sm_scale", "delta[(size_t)(i / blk_k) * S + n] * sm_scale"),
+    ("delta_without_sm_scale", "delta[(size_t)(i / blk_d) * S + n] * sm_scale;", "delta[(size_t)(i / blk_d) * S + n];"),
     ("f16_decode_bias", "ldexp(1.0 + fr / 1024.0, ex - 15)", "ldexp(1.0 + fr / 1024.0, ex - 14)"),
 ]
 
