@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
+    p.add_argument("--smooth-q", action="store_true",
+                   help="Q smoothing (INT8 Q K^T, fixed-length batches): quantise Q minus its 32-token block means")
     p.add_argument("--qk-quant", default="int8", choices=["int8", "int8_lane", "mxfp4"],
                    help="Q/K quantisation: INT8 per block, INT8 per token / 16-key lane group, or MXFP4")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -79,7 +81,7 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_hash, workload, pv, causal, qk="int8"):
+def traffic_record(kernel_hash, workload, pv, causal, qk="int8", smooth_v=False, smooth_q=False):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summaries, if one was taken on the current kernel source for this workload
     and mode."""
@@ -89,7 +91,8 @@ def traffic_record(kernel_hash, workload, pv, causal, qk="int8"):
         return None
     for rec in recs:
         if (rec.get("attn_src_sha256_16") == kernel_hash and rec.get("workload") == workload
-                and rec.get("pv_mode") == pv and rec.get("causal") == causal and rec.get("qk_quant", "int8") == qk):
+                and rec.get("pv_mode") == pv and rec.get("causal") == causal and rec.get("qk_quant", "int8") == qk
+                and rec.get("smooth_v", False) == smooth_v and rec.get("smooth_q", False) == smooth_q):
             return rec
     return None
 
@@ -99,7 +102,7 @@ def oracle_qk(qk):
     return {"int8": {}, "int8_lane": {"gran": "lane"}, "mxfp4": {"qk_format": "fp4"}}[qk]
 
 
-def cpu_baseline(w, causal, pv, nheads, qk="int8"):
+def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=False):
     import numpy as np
 
     import oracle as O
@@ -120,7 +123,7 @@ def cpu_baseline(w, causal, pv, nheads, qk="int8"):
         def run(heads):
             t0 = time.perf_counter()
             O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=bool(causal), pv_mode=pvm, heads=heads,
-                          **oracle_qk(qk))
+                          smooth_v=smooth_v, **oracle_qk(qk))
             return time.perf_counter() - t0
         what = "sequence-heads"
     else:
@@ -133,7 +136,7 @@ def cpu_baseline(w, causal, pv, nheads, qk="int8"):
         def run(heads):
             t0 = time.perf_counter()
             O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=bool(causal), pv_mode=pvm, heads=heads,
-                   **oracle_qk(qk))
+                   smooth_v=smooth_v, smooth_q=smooth_q, **oracle_qk(qk))
             return time.perf_counter() - t0
         what = "heads"
 
@@ -174,6 +177,10 @@ def main():
 
     name = args.workload or synth.HEADLINE
     varlen = name in synth.VARLEN_WORKLOADS
+    if args.smooth_q and (varlen or args.qk_quant == "mxfp4"):
+        sys.exit("--smooth-q applies to the INT8 Q K^T of fixed-length batches")
+    if args.smooth_v and args.pv != "fp8":
+        sys.exit("--smooth-v applies to pv fp8")
     w = synth.VARLEN_WORKLOADS[name] if varlen else synth.WORKLOADS[name]
     causal = w.causal[0] if args.causal is None else bool(args.causal)
     ops = w.ops(causal)
@@ -198,7 +205,8 @@ def main():
         bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_quant)
 
         def quant():
-            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v)
+            qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
+                        smooth_q=args.smooth_q)
 
         def attn():
             qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
@@ -231,7 +239,7 @@ def main():
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     khash = source_hash(ATTN_SRC)
-    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_quant)
+    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_quant, args.smooth_v, args.smooth_q)
     traffic = None if trec is None else trec["hbm_bytes_per_launch"]
 
     res = {
@@ -254,7 +262,7 @@ def main():
                     "qk_quant": args.qk_quant, "smooth_v": args.smooth_v} if varlen else
                    {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
                     "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv,
-                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v}),
+                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q}),
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv, args.qk_quant), 1), "unit": "TFLOP/s",
@@ -263,7 +271,8 @@ def main():
                      "attn_src_sha256_16": khash},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_quant)
+        res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_quant, args.smooth_v,
+                                           args.smooth_q)
     print(json.dumps(res))
 
 

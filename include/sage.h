@@ -125,7 +125,8 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16);
 /* Bytes of each intermediate buffer for a problem shape (see the layouts
  * above).  Any output pointer may be NULL. */
 int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t *q_codes, size_t *q_scale,
-                      size_t *k_codes, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale);
+                      size_t *k_codes, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale,
+                      size_t *q_mean, size_t *delta_s);
 
 /*
  * K smoothing + per-block INT8 quantisation of Q and K ([SA2] 相关工作,
@@ -140,6 +141,11 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
  *   32-channel block of every Q token and of every token of K - k_mean.
  * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
  * same with H_kv heads.
+ * q_mean non-NULL (INT8 modes only) selects smoothed Q ([SA2] SageAttention2方法): each
+ * SAGE_BLK_Q-token block's channel means (binary64 sums over its valid tokens divided
+ * by their number, rounded once) are written to q_mean, fp32 [B][H][nq][D], and
+ * subtracted (one fp32 subtraction) before the INT8 rule; sage_qk_delta then forms the
+ * term the attention adds back.
  * Writes q_codes, q_scale, k_codes, k_scale, k_mean (layouts above; their element
  * types follow qk_quant).  The call is several kernel launches; while it runs,
  * k_codes also holds intermediate
@@ -148,7 +154,21 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
  */
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
                          int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
-                         float *k_mean, void *stream);
+                         float *k_mean, float *q_mean, void *stream);
+
+/*
+ * The pre-processing stage of smoothed Q ([SA2] SageAttention2方法: Q minus its block
+ * means, with K smoothing, splits Q K^T into a pre-processing and an attention stage):
+ *   delta_s[b][h][blk][n] = sum_d q_mean[b][h][blk][d] * (K[b][h / (H / H_kv)][n][d] - k_mean[d])
+ * for n < S, 0 for the padding keys n < S_k, evaluated as q_mean . K - q_mean . k_mean
+ * with fp32 accumulation of exact products (q_mean enters as 16-bit pieces: 2^-22
+ * relative residual for fp16 inputs, exact for bf16).  q_mean and k_mean: from
+ * sage_smooth_quant_qk called with q_mean (16-byte aligned); k: the same K tensor.
+ * delta_s: fp32 [B][H][nq][S_k] (4-byte aligned).  The attention then adds
+ * delta_s[query block][key] * sm_scale to every score.
+ */
+int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, const float *q_mean,
+                  const float *k_mean, float *delta_s, void *stream);
 
 /*
  * Per-channel FP8 E4M3 quantisation of V ([SA2] SageAttention2方法):
@@ -180,6 +200,7 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  *   pv fp8 : P = E4M3(448 * p_n) (static scale), inner = P . V_fp8 (FP8 MFMA, fresh per tile),
  *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
  *            (+ v_mean[d] when v_mean is non-NULL: V was smoothed by sage_quant_v)
+ *   smoothed Q (delta_s non-NULL, INT8 modes): s_n += delta_s[query block][n] * sm_scale
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
  * q_codes .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
  * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the
@@ -191,8 +212,8 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  * (128-token slices of V are addressed through a 32-bit byte range).
  */
 int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                  const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H,
-                  int H_kv, int S,
+                  const void *v, const float *v_scale, const float *v_mean, const float *delta_s, void *out,
+                  int dtype, int B, int H, int H_kv, int S,
                   int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, void *stream);
 
 /*

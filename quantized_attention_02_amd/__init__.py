@@ -31,7 +31,7 @@ BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
 EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_attn_fwd",
-            "sage_attn_fwd_dump_qk", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
+            "sage_attn_fwd_dump_qk", "sage_qk_delta", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
             "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch"]
 
 _lib = None
@@ -52,12 +52,13 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         c_int, c_float, c_void_p, c_size_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
         L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
-        L.sage_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 7
-        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 5 + [c_void_p]
+        L.sage_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 9
+        L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 6 + [c_void_p]
+        L.sage_qk_delta.argtypes = [c_void_p] + [c_int] * 7 + [c_void_p] * 4
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
-        attn = [c_void_p] * 8 + [c_int] * 8 + [c_float, c_int, c_int]
-        L.sage_attn_fwd.argtypes = attn + [c_void_p]
-        L.sage_attn_fwd_dump_qk.argtypes = attn + [c_int, c_int, c_void_p, c_void_p]
+        tail = [c_int] * 8 + [c_float, c_int, c_int]
+        L.sage_attn_fwd.argtypes = [c_void_p] * 9 + tail + [c_void_p]
+        L.sage_attn_fwd_dump_qk.argtypes = [c_void_p] * 8 + tail + [c_int, c_int, c_void_p, c_void_p]
         L.sage_varlen_buffer_sizes.argtypes = [c_int] * 7 + [c_size_p] * 7
         L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + \
             [c_void_p] * 5 + [c_void_p]
@@ -94,27 +95,31 @@ def sage_get_config():
 
 
 def sage_buffer_sizes(B, H, H_kv, S, D, qk_quant=0):
-    vals = [ctypes.c_size_t() for _ in range(7)]
+    vals = [ctypes.c_size_t() for _ in range(9)]
     _check(lib().sage_buffer_sizes(B, H, H_kv, S, D, qk_quant, *[ctypes.byref(v) for v in vals]), "sage_buffer_sizes")
-    names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
+    names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale", "q_mean", "delta_s"]
     return {n: v.value for n, v in zip(names, vals)}
 
 
 def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale, k_mean,
-                         stream):
+                         q_mean, stream):
     """All tensor arguments are device pointers (ints); returns the status code."""
     return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale,
-                                      k_mean, stream)
+                                      k_mean, q_mean, stream)
+
+
+def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, q_mean, k_mean, delta_s, stream):
+    return lib().sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, q_mean, k_mean, delta_s, stream)
 
 
 def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream):
     return lib().sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream)
 
 
-def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout, is_causal,
-                  sm_scale, pv_mode, qk_quant, stream):
-    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                               is_causal, sm_scale, pv_mode, qk_quant, stream)
+def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D, layout,
+                  is_causal, sm_scale, pv_mode, qk_quant, stream):
+    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D,
+                               layout, is_causal, sm_scale, pv_mode, qk_quant, stream)
 
 
 def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
@@ -224,6 +229,9 @@ class Quantized:
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.smooth_v = False  # set by quantize: whether v_fp8 holds V minus v_mean
+        self.smooth_q = False  # set by quantize: whether q_i8 holds Q minus its block means
+        self.q_mean = self.delta_s = None  # smoothed Q: allocated on first use
+        self._device = device
 
 
 def _kv_heads(q, k, v, tensor_layout):
@@ -238,13 +246,16 @@ def _kv_heads(q, k, v, tensor_layout):
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
-             qk_quant="int8", smooth_v=False) -> Quantized:
+             qk_quant="int8", smooth_v=False, smooth_q=False) -> Quantized:
     """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors.
     k and v may have fewer heads than q (grouped-query attention); qk_quant "block"
     or "lane" (one scale per Q token and per 16-key lane group of K); smooth_v
-    (pv fp8): quantise V minus its channel mean."""
+    (pv fp8): quantise V minus its channel mean; smooth_q (INT8 modes): quantise
+    Q minus its 32-token block means and form the pre-processing term."""
     if smooth_v and pv_mode != "fp8":
         raise ValueError("smooth_v applies to pv_mode='fp8' only")
+    if smooth_q and qk_quant == "mxfp4":
+        raise ValueError("smooth_q applies to the INT8 Q K^T only")
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
     H_kv = _kv_heads(q, k, v, tensor_layout)
@@ -256,10 +267,21 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
     if (bufs.B, bufs.H, bufs.H_kv, bufs.S, bufs.D, bufs.qk) != (B, H, H_kv, S, D, QK[qk_quant]):
         raise ValueError("bufs were allocated for another shape or granularity")
     st = _stream()
+    if smooth_q and bufs.q_mean is None:
+        import torch
+
+        nq, sk = bufs.q_i8.shape[2] // BLK_Q, bufs.k_i8.shape[2]
+        bufs.q_mean = torch.empty((B, H, nq, D), dtype=torch.float32, device=q.device)
+        bufs.delta_s = torch.empty((B, H, nq, sk), dtype=torch.float32, device=q.device)
+    bufs.smooth_q = bool(smooth_q)
     _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
                                 bufs.q_i8.data_ptr(),
                                 bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
-                                bufs.k_mean.data_ptr(), st), "sage_smooth_quant_qk")
+                                bufs.k_mean.data_ptr(), bufs.q_mean.data_ptr() if smooth_q else None, st),
+           "sage_smooth_quant_qk")
+    if smooth_q:
+        _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.q_mean.data_ptr(), bufs.k_mean.data_ptr(),
+                             bufs.delta_s.data_ptr(), st), "sage_qk_delta")
     bufs.smooth_v = bool(smooth_v)
     if pv_mode == "fp8":
         _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
@@ -283,22 +305,25 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
     vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
-    args = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs,
-            vm, out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.qk)
+    ds = bufs.delta_s.data_ptr() if bufs.smooth_q else None
+    head = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs, vm)
+    tail = (out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.qk)
     if dump_head is None:
-        _check(sage_attn_fwd(*args, _stream()), "sage_attn_fwd")
+        _check(sage_attn_fwd(*head, ds, *tail, _stream()), "sage_attn_fwd")
     else:
-        _check(sage_attn_fwd_dump_qk(*args, dump_head[0], dump_head[1], dump.data_ptr(), _stream()),
+        if bufs.smooth_q:
+            raise ValueError("the Q K^T dump is not available with smooth_q")
+        _check(sage_attn_fwd_dump_qk(*head, *tail, dump_head[0], dump_head[1], dump.data_ptr(), _stream()),
                "sage_attn_fwd_dump_qk")
     return out
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_quant="int8",
-             smooth_v=False):
+             smooth_v=False, smooth_q=False):
     """Quantized attention: same shape, dtype and layout out as q."""
     import torch
 
-    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v)
+    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
 

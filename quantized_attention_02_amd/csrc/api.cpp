@@ -89,7 +89,8 @@ int check_device() {
 int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
 
 int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H,
+                const void *v, const float *v_scale, const float *v_mean, const float *delta_s, void *out, int dtype,
+                int B, int H,
                 int H_kv, int S,
                 int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, int dump_b,
                 int dump_h, int32_t *qk, bool dump, void *stream) {
@@ -105,6 +106,8 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;  // smoothing is for the FP8 V codes
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
+  // smoothed Q: the INT8 product only, 4-byte aligned, and not with the debug dump
+  if (delta_s && (qk_quant == SAGE_QK_MXFP4 || !aligned(delta_s, 4) || dump)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
@@ -128,6 +131,7 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   a.v = v;
   a.v_scale = v_scale;
   a.v_mean = v_mean;
+  a.delta_s = delta_s;
   a.out = out;
   a.dump = qk;
   a.dump_bh = dump ? dump_b * H + dump_h : -1;
@@ -164,7 +168,8 @@ int sage_get_config(int *blk_q, int *blk_k, int *tile_k_fp8, int *tile_k_fp16) {
 }
 
 int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t *q_codes, size_t *q_scale,
-                      size_t *k_codes, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale) {
+                      size_t *k_codes, size_t *k_scale, size_t *k_mean, size_t *v_fp8, size_t *v_scale,
+                      size_t *q_mean, size_t *delta_s) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
@@ -178,16 +183,19 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
   if (k_mean) *k_mean = bhk * D * sizeof(float);
   if (v_fp8) *v_fp8 = bhk * S_k * D;
   if (v_scale) *v_scale = bhk * D * sizeof(float);
+  if (q_mean) *q_mean = bh * (S_q / kBlkQ) * D * sizeof(float);
+  if (delta_s) *delta_s = bh * (S_q / kBlkQ) * S_k * sizeof(float);
   return SAGE_OK;
 }
 
 int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
                          int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
-                         float *k_mean, void *stream) {
+                         float *k_mean, float *q_mean, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_qk_quant(qk_quant))) return rc;
+  if (q_mean && (qk_quant == SAGE_QK_MXFP4 || !aligned(q_mean, 4))) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!q || !k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;
@@ -214,7 +222,37 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   a.nq = a.S_q / kBlkQ;
   a.nk = a.S_k / kBlkK;
   a.qk = qk_quant;
+  a.q_mean = q_mean;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
+}
+
+int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, const float *q_mean,
+                  const float *k_mean, float *delta_s, void *stream) {
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if ((rc = check_kv_heads(H, H_kv))) return rc;
+  if ((rc = check_enums(dtype, layout))) return rc;
+  if (!k || !q_mean || !k_mean || !delta_s) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(q_mean, 16) || !aligned(k_mean, 4) || !aligned(delta_s, 4))
+    return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantQKArgs a;
+  memset(&a, 0, sizeof a);
+  a.k = k;
+  a.k_mean = const_cast<float *>(k_mean);
+  a.q_mean = const_cast<float *>(q_mean);
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.S = S;
+  a.D = D;
+  a.layout = layout;
+  a.dtype = dtype;
+  a.S_q = roundup(S, kBlkQ);
+  a.S_k = roundup(S, kKvPad);
+  a.nq = a.S_q / kBlkQ;
+  a.nk = a.S_k / kBlkK;
+  return launch_status(launch_qk_delta(a, delta_s, (hipStream_t)stream));
 }
 
 int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8, float *v_scale,
@@ -243,18 +281,19 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
 }
 
 int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale, const void *v,
-                  const float *v_scale, const float *v_mean, void *out, int dtype, int B, int H, int H_kv, int S,
-                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, void *stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                     is_causal, sm_scale, pv_mode, qk_quant, 0, 0, nullptr, false, stream);
+                  const float *v_scale, const float *v_mean, const float *delta_s, void *out, int dtype, int B, int H,
+                  int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant,
+                  void *stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D,
+                     layout, is_causal, sm_scale, pv_mode, qk_quant, 0, 0, nullptr, false, stream);
 }
 
 int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                           const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
                           int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode,
                           int qk_quant, int b, int h, int32_t *qk, void *stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
-                     is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, true, stream);
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, nullptr, out, dtype, B, H, H_kv, S, D,
+                     layout, is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, true, stream);
 }
 
 // ---- packed variable-length batches

@@ -322,8 +322,10 @@ __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lan
 // 16-key lane group (the keys this half-wave holds of each 32-key sub-tile), so
 // every lane dequantises each sub-tile with one scale of its own.  2 (FP4):
 // MXFP4 -- E2M1 codes with an E8M0 scale per 32 channels of a token, on the
-// scaled FP4 MFMA, which applies the scales itself (fp32 scores).
-template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, int TN, int WPS, int WAVES, int NBUF>
+// scaled FP4 MFMA, which applies the scales itself (fp32 scores).  QS:
+// smoothed Q -- the scores gain the pre-processing term delta[query block][key]
+// (a wavefront's 32 queries share one block), staged in LDS with each tile.
+template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, bool QS, int TN, int WPS, int WAVES, int NBUF>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
   constexpr bool LANE = QK == 1, FP4 = QK == 2;
@@ -340,6 +342,8 @@ k_attn(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
   __shared__ __attribute__((aligned(16))) float vmn[D];  // its channel means when V was smoothed
+  // smoothed Q: each wavefront's row of the pre-processing term for the tile's keys
+  __shared__ __attribute__((aligned(16))) float dsbuf[QS ? NBUF : 1][QS ? WAVES : 1][QS ? TN : 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
@@ -453,13 +457,27 @@ k_attn(const AttnArgs a) {
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscb, ntiles * TN * (D / 32));  // FP4 K scales
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase,
                                                PV == 0 ? vbytes : kbytes);  // (pv fp16 copies V itself)
-  auto issue_tile = [&](int j, uint8_t *kb, uint8_t *vb) {
+  // smoothed Q: this wavefront's row of delta (its query block), tile j at byte j TN 4;
+  // only wavefronts with queries copy (a trailing wavefront's block may not exist)
+  const __amdgpu_buffer_rsrc_t drs =
+      make_rsrc(QS && active ? (const void *)(a.delta_s + ((long long)bh * a.nq + (qw >> 5)) * a.S_k) : (const void *)kbase,
+                QS && active ? a.S_k * 4 : 0);
+  auto issue_tile = [&](int j, int buf, uint8_t *kb, uint8_t *vb) {
     if constexpr (FP4) copy4.template issue<PV == 0>(krs, srs, vrs, j, kb, vb, wave, lane);
     else copy.template issue<PV == 0>(krs, vrs, j * TN * D, kb, vb, wave);
+    if constexpr (QS) {
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < TN / 64; ++i)
+          dma4_buf(drs, (uint32_t)(4 * lane), j * TN * 4 + 256 * i,
+                   reinterpret_cast<uint8_t *>(&dsbuf[buf][wave][0]) + 256 * i);
+      }
+    }
   };
 
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
-  auto tile = [&](int j, const uint8_t *kb, uint8_t *vb) {
+  auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb) {
+    const float *dsr = &dsbuf[QS ? buf : 0][QS ? wave : 0][0];  // smoothed Q: this wavefront's delta row
     const int key0 = j * TN;
     const bool work = active && !(CAUSAL && key0 > qw + 31);
     // pv fp16: this tile's V rows go into the single V buffer, which the
@@ -534,7 +552,14 @@ k_attn(const AttnArgs a) {
       // with this half-wave's group scale
       constexpr int NC2 = LANE ? NT : NB;
       float c2[NC2];
-      if constexpr (LANE) {
+      float cdq[NC2];  // smoothed Q: the dequantisation factor alone (sm_scale applied later)
+      if constexpr (QS) {
+#pragma unroll
+        for (int i = 0; i < NC2; ++i) {
+          cdq[i] = LANE ? dq * (hh ? ks[2 * i + 1] : ks[2 * i]) : dq * ks[i];
+          c2[i] = a.sm2;
+        }
+      } else if constexpr (LANE) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) c2[t] = (dq * (hh ? ks[2 * t + 1] : ks[2 * t])) * a.sm2;
       } else if constexpr (FP4) {
@@ -555,16 +580,29 @@ k_attn(const AttnArgs a) {
       float mxf[NB];  // FP4: fp32 max per block
       float f[16 * NT];
       auto max_convert = [&](int blk, int mlim, auto mask_tag) {
-        if constexpr (FP4) {
+        if constexpr (FP4 || QS) {  // fp32 scores: dequantised (+ delta), max in fp32
           float mx = -INFINITY;
 #pragma unroll
-          for (int t = 2 * blk; t < 2 * blk + 2; ++t)
+          for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
+            float4 dv[4];
+            if constexpr (QS)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) dv[g] = *reinterpret_cast<const float4 *>(dsr + 32 * t + 8 * g + 4 * hh);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = decltype(mask_tag)::value && 32 * t + 8 * (r >> 2) + (r & 3) > mlim;
-              f[16 * t + r] = out ? -INFINITY : s[t][r];
+              float val;
+              if constexpr (FP4) {
+                val = s[t][r];
+              } else {
+                const float4 d4 = dv[r >> 2];
+                const float dr = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
+                val = __builtin_fmaf((float)s[t][r], cdq[LANE ? t : blk], dr);
+              }
+              f[16 * t + r] = out ? -INFINITY : val;
               mx = fmaxf(mx, f[16 * t + r]);
             }
+          }
           mxf[blk] = mx;
           return;
         }
@@ -607,9 +645,9 @@ k_attn(const AttnArgs a) {
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, mlim, std::true_type());
       }
       float mt = -INFINITY;
-      if constexpr (FP4) {
+      if constexpr (FP4 || QS) {
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) mt = fmaxf(mt, mxf[blk] * c2[blk]);
+        for (int blk = 0; blk < NB; ++blk) mt = fmaxf(mt, mxf[blk] * a.sm2);
       } else {
 #pragma unroll
         for (int i = 0; i < NC2; ++i)
@@ -717,7 +755,7 @@ k_attn(const AttnArgs a) {
   static_assert(NBUF == 2 || !FP4, "partial vm waits assume the INT8 copy counts");
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
-    if (u < ntiles) issue_tile(u, kbuf[u], vbuf[PV == 0 ? u : 0]);
+    if (u < ntiles) issue_tile(u, u, kbuf[u], vbuf[PV == 0 ? u : 0]);
   wait_vm<0>();
   __syncthreads();
   for (int j0 = 0; j0 < ntiles; j0 += NBUF) {
@@ -727,8 +765,8 @@ k_attn(const AttnArgs a) {
       if (j >= ntiles) break;
       const int jn = j + NBUF - 1;  // prefetch target, into the buffer freed by tile j - 1
       const int un = (u + NBUF - 1) % NBUF;
-      if (jn < ntiles) issue_tile(jn, kbuf[un], vbuf[PV == 0 ? un : 0]);
-      tile(j, kbuf[u], vbuf[PV == 0 ? u : 0]);
+      if (jn < ntiles) issue_tile(jn, un, kbuf[un], vbuf[PV == 0 ? un : 0]);
+      tile(j, u, kbuf[u], vbuf[PV == 0 ? u : 0]);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
       __syncthreads();
@@ -785,12 +823,16 @@ static hipError_t launch5(const AttnArgs &a, bool dump, hipStream_t st) {
   AttnArgs b = a;
   b.nmblk = (a.S + 32 * C::WAVES - 1) / (32 * C::WAVES);
   const dim3 grid(a.B * a.H * b.nmblk), block(64 * C::WAVES);
-  if (dump)
-    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, QK != 2, QK, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st,
-                       b);  // (the API rejects the dump for MXFP4)
+  // (the API rejects the dump for MXFP4 and for smoothed Q, and smoothed Q for MXFP4)
+  if (a.delta_s && QK != 2)
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, QK != 2, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
+                       0, st, b);
+  else if (dump)
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, QK != 2, QK, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
+                       0, st, b);
   else
-    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block, 0, st,
-                       b);
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
+                       0, st, b);
   return hipGetLastError();
 }
 

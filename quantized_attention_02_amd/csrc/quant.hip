@@ -177,6 +177,191 @@ __global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Smoothed Q ("SageAttention2" summary, SageAttention2方法: subtract each block
+// of Q's mean; with K smoothing, Q K^T splits into a pre-processing stage and
+// the attention stage): the channel means of the block's valid tokens (binary64
+// sums -- exact for 32 values of a 16-bit format -- divided by their number,
+// rounded once) go to q_mean[block][D] and are subtracted from the block's
+// valid rows (padding rows stay 0).  x: the thread's two row vectors as
+// k_qquant loads them; nvalid: the block's valid rows; gblk: the block's index
+// in q_mean.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ inline void q_block_smooth(const QuantQKArgs &a, float (&x)[2][8], int nvalid, long long gblk) {
+  constexpr int vec_per_row = D / 8;
+  constexpr int RPP = kThreads / vec_per_row;  // rows a pass of the 256 threads covers
+  __shared__ double part[RPP][D];
+  __shared__ float mean[D];
+  const int tid = threadIdx.x, c8 = (tid % vec_per_row) * 8, r = tid / vec_per_row;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[r][c8 + i] = (double)x[0][i] + (double)x[1][i];  // rows r and r + RPP
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) t += part[j][tid];
+    const float m = nvalid > 0 ? (float)(t / (double)min(nvalid, kBlkQ)) : 0.0f;
+    mean[tid] = m;
+    a.q_mean[gblk * D + tid] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = (tid + u * kThreads) / vec_per_row;
+    if (tid + u * kThreads < kBlkQ * vec_per_row && row < nvalid)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[u][i] = x[u][i] - mean[c8 + i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The pre-processing stage of smoothed Q:
+//   delta[bh][blk][n] = sum_d q_mean[bh][blk][d] * (K[n][d] - k_mean[d])
+// for n < S (0 for the padding keys up to S_k): an [nq x D] . [D x S] product
+// per head, run on the 16-bit MFMA as
+//   delta = q_mean . K  -  q_mean . k_mean.
+// K enters the MFMA exactly (it is fp16 / bf16 already).  q_mean is split into
+// 16-bit pieces that sum to it: fp16 hi + lo (22 significant bits) for fp16
+// inputs, three truncated bf16 pieces (all 24 bits, exact) for bf16.  Products
+// of 16-bit values are exact in the fp32 accumulator, so the result carries fp32
+// summation rounding only (and 2^-22 of q_mean with fp16 inputs).
+// A work-group of four wavefronts owns 128 keys of one query head.  Each
+// wavefront keeps its 32 keys' K rows in registers (the B operand) and walks the
+// head's query blocks 32 at a time; the split means of those 32 blocks and their
+// dot products with k_mean are staged once per work-group in LDS (the A operand;
+// rows padded by 16 bytes against bank conflicts).  A lane ends with 16 results
+// of one key; for each, the 32 lanes of a half-wave fill one 128-byte row
+// segment of delta.
+// ---------------------------------------------------------------------------
+constexpr int kDeltaKeys = 128;
+static_assert(kDeltaKeys == kKvPad, "a delta work-group covers one 128-key K tile");
+
+template <int DT>
+struct DeltaMfma;
+
+template <>
+struct DeltaMfma<0> {  // fp16 inputs
+  typedef _Float16 T8 __attribute__((ext_vector_type(8)));
+  static constexpr int kSplit = 2;
+  __device__ static v16f mfma(T8 a, T8 b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+  // x = hi + lo + r with |r| <= 2^-22 |x| (+ 2^-25 near the fp16 subnormal range)
+  __device__ static void split(float x, uint16_t *p) {
+    const _Float16 hi = (_Float16)x;
+    const _Float16 lo = (_Float16)(x - (float)hi);  // x - hi is exact in fp32
+    p[0] = __builtin_bit_cast(uint16_t, hi);
+    p[1] = __builtin_bit_cast(uint16_t, lo);
+  }
+};
+
+template <>
+struct DeltaMfma<1> {  // bf16 inputs
+  typedef __bf16 T8 __attribute__((ext_vector_type(8)));
+  static constexpr int kSplit = 3;
+  __device__ static v16f mfma(T8 a, T8 b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+  // truncation to the top 8 significant bits, three times: the pieces hold all
+  // 24 bits of x, and each remainder is an exact fp32 subtraction
+  __device__ static void split(float x, uint16_t *p) {
+    float r = x;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint32_t u = __float_as_uint(r) & 0xffff0000u;
+      p[i] = (uint16_t)(u >> 16);
+      r = r - __uint_as_float(u);
+    }
+  }
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, float *delta) {
+  typedef DeltaMfma<DT> M;
+  typedef typename M::T8 T8;
+  constexpr int NS = M::kSplit;
+  constexpr int KSTEPS = D / 16;  // MFMA k steps over the channels
+  constexpr int RS = D + 8;       // LDS row stride (16-bit elements): 16 bytes of padding
+  constexpr int CPT = D / 8;      // channels per staging thread (8 threads per query block)
+  __shared__ __align__(16) uint16_t am[NS][32 * RS];
+  __shared__ float cs[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int nkt = a.S_k / kDeltaKeys;
+  // work-group -> (query head, key tile); with a grid that divides evenly, each
+  // XCD takes whole heads, so a head's block means are read through one L2
+  int wg = blockIdx.x;
+  if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
+  const int bh = wg / nkt, kt = wg % nkt;
+  const int b = bh / a.H, h = bh % a.H, hk = h / (a.H / a.H_kv);
+  const Seg ks = fixed_seg(a.layout, b, hk, a.H_kv, a.S, a.S_k, D);
+  const int n = kt * kDeltaKeys + 32 * wave + (lane & 31);  // this lane's key (< S_k)
+  // B operand: channels 16 s + 8 hh .. +7 of key n for each k step s
+  const uint16_t *k = (const uint16_t *)a.k;
+  T8 kf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    v4i u = {0, 0, 0, 0};
+    if (n < a.S) u = *reinterpret_cast<const v4i *>(k + ks.base + (long long)n * ks.stride + 16 * s + 8 * hh);
+    kf[s] = __builtin_bit_cast(T8, u);
+  }
+  // staging role: query block sb of a chunk, channels sc .. sc + CPT - 1
+  const int sb = tid >> 3, sc = (tid & 7) * CPT;
+  float km[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) km[i] = a.k_mean[((long long)b * a.H_kv + hk) * D + sc + i];
+  const float *qm = a.q_mean + (long long)bh * a.nq * D;
+  float *dst = delta + (long long)bh * a.nq * a.S_k + n;
+  for (int blk0 = 0; blk0 < a.nq; blk0 += 32) {
+    {
+      const int blk = blk0 + sb;
+      float x[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; i += 4) {
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (blk < a.nq) v = *reinterpret_cast<const float4 *>(qm + (long long)blk * D + sc + i);
+        x[i] = v.x;
+        x[i + 1] = v.y;
+        x[i + 2] = v.z;
+        x[i + 3] = v.w;
+      }
+      float c = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) c = __builtin_fmaf(x[i], km[i], c);
+      c += __shfl_xor(c, 1, 64);
+      c += __shfl_xor(c, 2, 64);
+      c += __shfl_xor(c, 4, 64);
+      if ((tid & 7) == 0) cs[sb] = c;
+      uint16_t p[CPT][NS];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) M::split(x[i], p[i]);
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+        for (int i = 0; i < CPT; i += 8) {
+          v4i u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) u[j] = (int)((uint32_t)p[i + 2 * j][sp] | ((uint32_t)p[i + 2 * j + 1][sp] << 16));
+          *reinterpret_cast<v4i *>(&am[sp][sb * RS + sc + i]) = u;
+        }
+    }
+    __syncthreads();
+    v16f acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) {
+        const v4i u = *reinterpret_cast<const v4i *>(&am[sp][(lane & 31) * RS + 16 * s + 8 * hh]);
+        acc = M::mfma(__builtin_bit_cast(T8, u), kf[s], acc);
+      }
+    // lane holds rows (query blocks) 8 (r / 4) + 4 hh + r % 4 of column n
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * hh + (r & 3), blk = blk0 + i;
+      if (blk < a.nq) dst[(long long)blk * a.S_k] = n < a.S ? acc[r] - cs[i] : 0.0f;
+    }
+    __syncthreads();  // am and cs are restaged for the next chunk
+  }
+}
+
+// ---------------------------------------------------------------------------
 // INT8 quantisation of one 32-token block of Q: one scale for the block, or
 // (LANE) one scale per token -- the query a lane column holds in the 32 x 32
 // INT8 MFMA layout of the attention kernel.
@@ -204,6 +389,12 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
     }
+  }
+  if (a.q_mean) {  // smoothed Q: subtract the block's channel means (fixed-length batches)
+    q_block_smooth<D>(a, x, hv.S - blk * kBlkQ, (hv.row0 >> 5) + blk);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ramax[u] = fmaxf(ramax[u], fabsf(x[u][i]));
     amax = fmaxf(amax, ramax[u]);
@@ -638,6 +829,18 @@ hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream) {
   } else {
     if (a.dtype == 0) launch_qk<0, 128>(a, stream);
     else launch_qk<1, 128>(a, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_delta(const QuantQKArgs &a, float *delta, hipStream_t stream) {
+  const dim3 grid(a.B * a.H * (a.S_k / kDeltaKeys));  // S_k: a multiple of 128
+  if (a.D == 64) {
+    if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 64>), grid, dim3(kThreads), 0, stream, a, delta);
+    else hipLaunchKernelGGL((k_qk_delta<1, 64>), grid, dim3(kThreads), 0, stream, a, delta);
+  } else {
+    if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 128>), grid, dim3(kThreads), 0, stream, a, delta);
+    else hipLaunchKernelGGL((k_qk_delta<1, 128>), grid, dim3(kThreads), 0, stream, a, delta);
   }
   return hipGetLastError();
 }

@@ -130,6 +130,7 @@ struct QuantQKArgs {
   SeqTable sq, sk;
   long long rows_q, rows_k;  // buffer rows per head (packed batch)
   int qk;                    // Q/K quantisation: 0 INT8 per block, 1 INT8 per lane, 2 MXFP4
+  float *q_mean;             // smoothed Q: block means [B][H][nq][D] (nullptr: no Q smoothing)
 };
 
 struct QuantVArgs {
@@ -150,6 +151,7 @@ struct AttnArgs {
   const void *v;
   const float *v_scale;
   const float *v_mean;  // smoothed V: channel means added to the output (nullptr: none)
+  const float *delta_s;  // smoothed Q: pre-processing term [B][H][nq][S_k] (nullptr: none)
   void *out;
   int32_t *dump;
   int dump_bh;
@@ -164,6 +166,8 @@ struct AttnArgs {
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);
 hipError_t launch_quant_v(const QuantVArgs &a, hipStream_t stream);
+// pre-processing term of smoothed Q, delta[B][H][nq][S_k] (a.q_mean and a.k_mean read)
+hipError_t launch_qk_delta(const QuantQKArgs &a, float *delta, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs &a, bool dump, hipStream_t stream);
 int attn_tile_keys(int pv_mode);  // keys per online-softmax tile of the attention kernel
 

@@ -17,9 +17,10 @@ Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this order
   2. the K bias c[h, d] ~ N(0, bias_sigma^2) per K head, shared over b and s;
   3. (outlier_p > 0) Bernoulli(outlier_p) masks for Q, then K;
   4. (token_norm) per-token factors r ~ U(0.5, 2) drawn per (b, s) for Q, K, V;
-  5. (v_bias_sigma > 0) a V bias c_v[h, d] ~ N(0, v_bias_sigma^2) per V head.
-Application: x *= r (token norm), K += c, V += c_v, then masked entries of Q and
-K *= 20.
+  5. (v_bias_sigma > 0) a V bias c_v[h, d] ~ N(0, v_bias_sigma^2) per V head;
+  6. (q_bias_sigma > 0) a Q bias c_q[h, d] ~ N(0, q_bias_sigma^2) per Q head.
+Application: x *= r (token norm), K += c, V += c_v, Q += c_q, then masked
+entries of Q and K *= 20.
 Then cast round-to-nearest-even to fp16 (numpy) or bf16 (torch CPU) and, for
 NHD, permute to [B, S, H, D].  Returned arrays are the raw uint16 codes.
 
@@ -53,7 +54,8 @@ class Workload:
     pv_modes: tuple = ("fp8",)
     seed: int = 42
     Hkv: int = 0  # K/V heads (grouped-query attention); 0: as many as Q
-    v_bias_sigma: float = 0.0  # per-channel V offset shared by all tokens (drawn last)
+    v_bias_sigma: float = 0.0  # per-channel V offset shared by all tokens (drawn after the rest)
+    q_bias_sigma: float = 0.0  # per-channel Q offset shared by all tokens (drawn last)
 
     @property
     def kv_heads(self) -> int:
@@ -115,6 +117,9 @@ def make_qkv(w: Workload, seed: int | None = None):
     if w.v_bias_sigma > 0:
         cv = (rng.standard_normal((w.kv_heads, w.D), dtype=np.float32) * np.float32(w.v_bias_sigma)).astype(np.float32)
         v += cv[None, :, None, :]
+    if w.q_bias_sigma > 0:
+        cq = (rng.standard_normal((w.H, w.D), dtype=np.float32) * np.float32(w.q_bias_sigma)).astype(np.float32)
+        q += cq[None, :, None, :]
     if w.outlier_p > 0:
         q[mq] *= np.float32(20.0)
         k[mk] *= np.float32(20.0)
@@ -127,11 +132,11 @@ def make_qkv(w: Workload, seed: int | None = None):
 
 
 def custom(B, H, S, D, dtype="fp16", layout="HND", bias_sigma=2.0, outlier_p=0.0, token_norm=False, seed=0, Hkv=0,
-           v_bias_sigma=0.0):
+           v_bias_sigma=0.0, q_bias_sigma=0.0):
     """An ad-hoc workload (edge shapes in tests)."""
     kv = f"kv{Hkv}" if Hkv else ""
     return Workload(f"custom_b{B}h{H}{kv}s{S}d{D}", B, H, S, D, dtype, layout, bias_sigma, outlier_p, token_norm,
-                    seed=seed, Hkv=Hkv, v_bias_sigma=v_bias_sigma)
+                    seed=seed, Hkv=Hkv, v_bias_sigma=v_bias_sigma, q_bias_sigma=q_bias_sigma)
 
 
 def mixed_lengths(total: int, lo: int, hi: int, seed: int) -> tuple:

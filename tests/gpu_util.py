@@ -40,13 +40,14 @@ def inputs(w: synth.Workload):
     return synth.make_qkv(w)
 
 
-def run(w: synth.Workload, *, causal=False, pv="fp8", sm_scale=None, dump_head=None, qk_quant="int8", smooth_v=False):
+def run(w: synth.Workload, *, causal=False, pv="fp8", sm_scale=None, dump_head=None, qk_quant="int8", smooth_v=False,
+        smooth_q=False):
     """Quantise and run attention on the GPU. Returns (bufs, out tensor, dump or None)."""
     import torch
 
     q, k, v = inputs(w)
     qd, kd, vd = (to_device(x, w.dtype) for x in (q, k, v))
-    bufs = qa.quantize(qd, kd, vd, w.layout, pv, qk_quant=qk_quant, smooth_v=smooth_v)
+    bufs = qa.quantize(qd, kd, vd, w.layout, pv, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q)
     out = torch.empty_like(qd)
     dump = None
     if dump_head is not None:

@@ -34,26 +34,28 @@ def test_library_exports_every_declared_symbol():
 def test_config_and_sizes():
     assert qa.sage_get_config() == (32, 64, qa.TILE_K["fp8"], qa.TILE_K["fp16"])
     s = qa.sage_buffer_sizes(2, 3, 3, 100, 64)
+    sq = {"q_mean": 6 * 4 * 64 * 4, "delta_s": 6 * 4 * 128 * 4}  # smoothed Q: [B][H][nq][D], [B][H][nq][S_k]
     assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 4 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 2 * 4,
-                 "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4}
+                 "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4, **sq}
     # lane granularity: one Q scale per (padded) token row, one K scale per 16-key group
     # MXFP4: D / 2 code bytes and D / 32 E8M0 bytes a row
     s4 = qa.sage_buffer_sizes(2, 3, 3, 100, 64, qa.QK["mxfp4"])
     assert s4 == {"q_i8": 6 * 128 * 32, "q_scale": 6 * 128 * 2, "k_i8": 6 * 128 * 32, "k_scale": 6 * 128 * 2,
-                  "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4}
+                  "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4, **sq}
     s = qa.sage_buffer_sizes(2, 3, 3, 100, 64, qa.QK["int8_lane"])
     assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 128 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 8 * 4,
-                 "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4}
+                 "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4, **sq}
     # grouped K/V: the K and V buffers hold B * H_kv heads
     s = qa.sage_buffer_sizes(2, 6, 2, 100, 64)
     assert s == {"q_i8": 12 * 128 * 64, "q_scale": 12 * 4 * 4, "k_i8": 4 * 128 * 64, "k_scale": 4 * 2 * 4,
-                 "k_mean": 4 * 64 * 4, "v_fp8": 4 * 128 * 64, "v_scale": 4 * 64 * 4}
+                 "k_mean": 4 * 64 * 4, "v_fp8": 4 * 128 * 64, "v_scale": 4 * 64 * 4,
+                 "q_mean": 12 * 4 * 64 * 4, "delta_s": 12 * 4 * 128 * 4}
     L = qa.lib()
     assert L.sage_get_config(None, None, None, None) == qa.SAGE_ERR_INVALID_ARG
     for bad in [(0, 1, 1, 1, 64, 0), (1, 0, 1, 1, 64, 0), (1, 1, 1, 0, 64, 0), (1, 1, 1, 1, 96, 0),
                 (1, 1, 1, (1 << 20) + 1, 64, 0), (1, 4, 0, 1, 64, 0), (1, 4, 3, 1, 64, 0), (1, 4, 8, 1, 64, 0),
                 (1, 4, -4, 1, 64, 0), (1, 1, 1, 1, 64, 3), (1, 1, 1, 1, 64, -1)]:
-        assert L.sage_buffer_sizes(*bad, *([None] * 7)) == qa.SAGE_ERR_INVALID_ARG
+        assert L.sage_buffer_sizes(*bad, *([None] * 9)) == qa.SAGE_ERR_INVALID_ARG
 
 
 def test_arch_check():
@@ -78,16 +80,19 @@ def test_vpos_key_is_a_permutation():
 # a valid-looking set of (fake, aligned, non-null) device pointers
 P = 1 << 12
 GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, H_kv=2, S=100, D=64, layout=0, qk_quant=0, q_i8=P, q_scale=P, k_i8=P,
-               k_scale=P, k_mean=P, stream=None)
+               k_scale=P, k_mean=P, q_mean=None, stream=None)
+GOOD_DELTA = dict(k=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64, layout=1, q_mean=P, k_mean=P, delta_s=P, stream=None)
 GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, v_mean=None, stream=None)
-GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, out=P, dtype=0, B=1, H=2, H_kv=2,
-                 S=100,
+GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, delta_s=None, out=P, dtype=0, B=1,
+                 H=2, H_kv=2, S=100,
                  D=64, layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, qk_quant=0, stream=None)
 
 BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict(q_scale=P + 2), dict(dtype=2),
           dict(layout=-1), dict(B=0), dict(H=-1), dict(S=0), dict(D=32), dict(D=256), dict(S=(1 << 20) + 1),
           dict(B=1 << 9, H=1 << 8, H_kv=1 << 8), dict(H_kv=0), dict(H_kv=3), dict(H=3, H_kv=2), dict(H_kv=-2),
-          dict(qk_quant=3), dict(qk_quant=-1)]
+          dict(qk_quant=3), dict(qk_quant=-1), dict(q_mean=P + 2), dict(q_mean=P, qk_quant=2)]
+BAD_DELTA = [dict(k=None), dict(q_mean=None), dict(k_mean=None), dict(delta_s=None), dict(q_mean=P + 4),
+             dict(delta_s=P + 2), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2), dict(dtype=4), dict(S=0)]
 BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80),
          dict(v_mean=P + 2)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
@@ -95,6 +100,7 @@ BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dic
             dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
             dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=3),
             dict(v_mean=P + 1), dict(pv_mode=1, v_scale=None, v_mean=P),  # smoothing is for the FP8 V codes
+            dict(delta_s=P + 2), dict(delta_s=P, qk_quant=2),  # smoothed Q: INT8 modes only
             # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
             dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
 
@@ -119,6 +125,11 @@ def test_smooth_quant_qk_rejects(bad):
     assert _call_qk(**bad) == qa.SAGE_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("bad", BAD_DELTA, ids=[str(b) for b in BAD_DELTA])
+def test_qk_delta_rejects(bad):
+    assert qa.sage_qk_delta(*{**GOOD_DELTA, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("bad", BAD_V, ids=[str(b) for b in BAD_V])
 def test_quant_v_rejects(bad):
     assert _call_v(**bad) == qa.SAGE_ERR_INVALID_ARG
@@ -141,7 +152,7 @@ def test_attn_fp16_mode_accepts_null_v_scale_then_needs_device():
 
 
 def test_dump_rejects_bad_head_and_buffer():
-    a = list(GOOD_ATTN.values())[:-1]
+    a = [v for k, v in GOOD_ATTN.items() if k not in ("delta_s", "stream")]  # the dump takes no smoothed-Q term
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 2, P, None) == qa.SAGE_ERR_INVALID_ARG  # h out of range
     a[-1] = 3
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 0, P, None) == qa.SAGE_ERR_INVALID_ARG  # bad Q/K mode
@@ -167,6 +178,9 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_qk(qk_quant=2) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(qk_quant=2) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qk(q_mean=P) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(delta_s=P) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_qk_delta(*GOOD_DELTA.values()) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v() == qa.SAGE_ERR_NO_DEVICE
