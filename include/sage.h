@@ -205,30 +205,31 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
  * q_codes .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
  * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the
  * original V tensor (dtype, layout, H_kv heads), v_scale = v_mean = NULL (bf16 V is
- * rounded to fp16).  out: dtype tensor in `layout`, shape
- * of q.  Query head h reads K/V head h / (H / H_kv).
+ * rounded to fp16).  delta_s: NULL, or the buffer sage_qk_delta filled for these
+ * codes.  out: dtype tensor in `layout`, shape of q.  Query head h reads K/V head
+ * h / (H / H_kv).
  * is_causal in {0, 1}; sm_scale finite and > 0 (the usual choice is 1/sqrt(D)).
  * pv fp16 with NHD layout additionally needs H_kv * D * 2 * SAGE_KV_PAD < 2^31
  * (128-token slices of V are addressed through a 32-bit byte range).
  */
 int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                   const void *v, const float *v_scale, const float *v_mean, const float *delta_s, void *out,
-                  int dtype, int B, int H, int H_kv, int S,
-                  int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, void *stream);
+                  int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale,
+                  int pv_mode, int qk_quant, void *stream);
 
 /*
- * Debug variant of sage_attn_fwd: the same kernel code, which additionally
- * writes the int32 accumulators of Q K^T for query head (b, h) to qk, an int32 [S][S]
- * array (qk[i][n] = sum_d q_codes[i][d] * k_codes[n][d]; INT8 modes only).  With is_causal, entries
- * with n > i may be left unwritten (key tiles the mask excludes for a whole
- * work-group are skipped); every entry with n <= i is written.  `out` is
- * written as by sage_attn_fwd.
+ * Debug variant of sage_attn_fwd (INT8 modes, no smoothed-Q term): the same
+ * kernel code, which additionally writes the int32 accumulators of Q K^T for
+ * query head (b, h) to qk, an int32 [S][S] array:
+ *   qk[i][n] = sum_d q_codes[i][d] * k_codes[n][d].
+ * With is_causal, entries with n > i may be left unwritten (key tiles the mask
+ * excludes for a whole work-group are skipped); every entry with n <= i is
+ * written.  `out` is written as by sage_attn_fwd.
  */
 int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                           const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
-                          int H, int H_kv,
-                          int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant,
-                          int b, int h, int32_t *qk, void *stream);
+                          int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode,
+                          int qk_quant, int b, int h, int32_t *qk, void *stream);
 
 /* ------------------------------------------------------------------------
  * Packed variable-length batches ([REPO] feature list: variable-length
