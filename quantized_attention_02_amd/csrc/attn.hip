@@ -126,6 +126,22 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
+// wait_vm with a wave-uniform count known at run time (at most 8 kept in
+// flight; a larger count waits for everything)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
+
 // Max / sum of a value over the two half-waves (lanes i and i ^ 32 hold the
 // same query row).  v_permlane32_swap exchanges the halves between its two
 // outputs; one output then holds the lane's own value and the other its
@@ -178,6 +194,13 @@ struct TileCopy {
       voff[i] = (uint32_t)(vrow * 64 + 16 * swz<4>(lane & 3, vrow));
     }
   }
+  // K copies a wavefront issues per tile
+  __device__ __forceinline__ static int k_loads(int wave) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) n += (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY) ? 1 : 0;
+    return n;
+  }
   template <bool WITH_V>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int tile_off,
                                         uint8_t *kbuf, uint8_t *vbuf, int wave) const {
@@ -221,6 +244,13 @@ struct TileCopy4 {
       const int vrow = (wave + WAVES * i) * 16 + (lane >> 2);
       voff[i] = (uint32_t)(vrow * 64 + 16 * swz<4>(lane & 3, vrow));
     }
+  }
+  // code and scale copies a wavefront issues per tile (without V)
+  __device__ __forceinline__ static int k_loads(int wave) {
+    int n = wave < NSC ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) n += (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY) ? 1 : 0;
+    return n;
   }
   // tile j of the head: codes at j TN ROWB, scales at j SCB, V at j TN D
   template <bool WITH_V>
@@ -287,11 +317,30 @@ struct VCopy16 {
       dma16_buf(rs, (uint32_t)((k * RPC + lrow) * ts2) + lcol, 0, vb + k * 1024);
     }
   }
+  // bf16 input: once this lane's copies have landed, round the 16-byte chunks
+  // it copied to fp16 in place (RNE), so that the tile is read as fp16 by every
+  // wavefront; chunk positions (and the swizzle) are unchanged
+  __device__ __forceinline__ void to_f16(uint8_t *vb, int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      v4i *c = reinterpret_cast<v4i *>(vb + (wave + WAVES * i) * 1024 + 16 * lane);
+      v4i u = *c;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = (uint32_t)u[w];
+        const _Float16 lo = (_Float16)__uint_as_float(x << 16);
+        const _Float16 hi = (_Float16)__uint_as_float(x & 0xffff0000u);
+        u[w] = (int)((uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16));
+      }
+      *c = u;
+    }
+  }
 };
 
 // V^T fragment (channels 32 c .. 32 c + 31 down the lanes, keys 16 sb .. +15
-// across them in the MFMA k order of the P registers) for v_mfma_f32_32x32x16_f16.
-template <int D, int DT>
+// across them in the MFMA k order of the P registers) for v_mfma_f32_32x32x16_f16,
+// from the fp16 tile in LDS.
+template <int D>
 __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lane) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4s *lds_v4s;
@@ -306,10 +355,7 @@ __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lan
   }
   v8h out;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t bits = (uint32_t)(uint16_t)h[i >> 2][i & 3];
-    out[i] = DT == 0 ? __builtin_bit_cast(_Float16, (uint16_t)bits) : (_Float16)bf16_to_f32(bits);  // bf16 -> fp16, RNE
-  }
+  for (int i = 0; i < 8; ++i) out[i] = __builtin_bit_cast(_Float16, (uint16_t)h[i >> 2][i & 3]);
   return out;
 }
 
@@ -462,27 +508,35 @@ k_attn(const AttnArgs a) {
   const __amdgpu_buffer_rsrc_t drs =
       make_rsrc(QS && active ? (const void *)(a.delta_s + ((long long)bh * a.nq + (qw >> 5)) * a.S_k) : (const void *)kbase,
                 QS && active ? a.S_k * 4 : 0);
-  auto issue_tile = [&](int j, int buf, uint8_t *kb, uint8_t *vb) {
-    if constexpr (FP4) copy4.template issue<PV == 0>(krs, srs, vrs, j, kb, vb, wave, lane);
-    else copy.template issue<PV == 0>(krs, vrs, j * TN * D, kb, vb, wave);
+  // copies of tile j into buffer buf; returns how many copy instructions this
+  // wavefront issued without V (pv fp16 counts them to wait for its V alone)
+  auto issue_tile = [&](int j, int buf, uint8_t *kb, uint8_t *vb) -> int {
+    int n;
+    if constexpr (FP4) {
+      copy4.template issue<PV == 0>(krs, srs, vrs, j, kb, vb, wave, lane);
+      n = copy4.k_loads(wave);
+    } else {
+      copy.template issue<PV == 0>(krs, vrs, j * TN * D, kb, vb, wave);
+      n = copy.k_loads(wave);
+    }
     if constexpr (QS) {
       if (active) {
 #pragma unroll
         for (int i = 0; i < TN / 64; ++i)
           dma4_buf(drs, (uint32_t)(4 * lane), j * TN * 4 + 256 * i,
                    reinterpret_cast<uint8_t *>(&dsbuf[buf][wave][0]) + 256 * i);
+        n += TN / 64;
       }
     }
+    return n;
   };
 
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
-  auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb) {
+  // pend (pv fp16): copy instructions this wavefront issued after the tile's V.
+  auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb, int pend) {
     const float *dsr = &dsbuf[QS ? buf : 0][QS ? wave : 0][0];  // smoothed Q: this wavefront's delta row
     const int key0 = j * TN;
     const bool work = active && !(CAUSAL && key0 > qw + 31);
-    // pv fp16: this tile's V rows go into the single V buffer, which the
-    // barrier that ended the previous tile has released
-    if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, key0, Sk, vb, wave);
     // the tile's K scales, read through a wave-uniform address (scalar loads)
     constexpr int NKS = LANE ? 2 * NT : NB;  // per lane group, or per 64-key block
     float ks[NKS];
@@ -731,14 +785,15 @@ k_attn(const AttnArgs a) {
             for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
         }
       }
-      wait_vm<0>();  // this wavefront's V (and next K) copies have landed ...
+      wait_vm_n(pend);  // this wavefront's V copies have landed (the next K may still fly) ...
+      if constexpr (DT == 1) vcopy.to_f16(vb, wave, lane);  // bf16 V: rounded to fp16 once per work-group
       __syncthreads();  // ... and every other wavefront's too
       if (work) {
 #pragma unroll
         for (int sb = 0; sb < 2 * NT; ++sb)
 #pragma unroll
           for (int c = 0; c < NC; ++c)
-            O[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag16<D, DT>(vb, c, sb, lane), ph[sb], O[c], 0, 0, 0);
+            O[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag16<D>(vb, c, sb, lane), ph[sb], O[c], 0, 0, 0);
       }
     }
   };
@@ -765,8 +820,13 @@ k_attn(const AttnArgs a) {
       if (j >= ntiles) break;
       const int jn = j + NBUF - 1;  // prefetch target, into the buffer freed by tile j - 1
       const int un = (u + NBUF - 1) % NBUF;
-      if (jn < ntiles) issue_tile(jn, un, kbuf[un], vbuf[PV == 0 ? un : 0]);
-      tile(j, u, kbuf[u], vbuf[PV == 0 ? u : 0]);
+      // pv fp16: this tile's V rows go into the single V buffer, which the
+      // barrier that ended the previous tile has released; issued ahead of the
+      // prefetch so that the tile can wait for its V alone
+      if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, j * TN, Sk, vbuf[0], wave);
+      int pend = 0;
+      if (jn < ntiles) pend = issue_tile(jn, un, kbuf[un], vbuf[PV == 0 ? un : 0]);
+      tile(j, u, kbuf[u], vbuf[PV == 0 ? u : 0], pend);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
       __syncthreads();
