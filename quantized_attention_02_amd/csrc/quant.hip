@@ -109,12 +109,13 @@ __device__ inline int code_row_bytes(const QuantQKArgs &a) { return a.qk == 2 ? 
 
 // Thread layout of the chunk passes: G = D / 8 channel groups (16 bytes of a
 // 16-bit row) x R = 256 / G rows; the chunk's rows are loaded kUnroll at a
-// time so that many 16-byte loads are in flight per thread.
+// time, 256 rows (a minimum-size chunk) per round, so that a chunk of 256
+// tokens is read with all of its loads in flight at once.
 template <int D>
 struct ChunkMap {
   static constexpr int G = D / 8;
   static constexpr int R = kThreads / G;
-  static constexpr int kUnroll = 8;
+  static constexpr int kUnroll = 256 / R;
 };
 
 // K channel sums (binary64) of one chunk -> partials[chunk][D]; or, with
@@ -132,23 +133,20 @@ __device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk,
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0;
   for (int s0 = chunk * ct + r; s0 < s_end; s0 += M::R * M::kUnroll) {
-    float v[M::kUnroll][8];
+    v4i raw[M::kUnroll];  // 16-bit pairs as loaded (zeros past the chunk)
 #pragma unroll
     for (int u = 0; u < M::kUnroll; ++u) {
       const int s = s0 + u * M::R;
-      if (s < s_end) {
-        load8<DT>(x + hv.base + (long long)s * hv.stride + 8 * g, v[u]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
-      }
+      raw[u] = s < s_end ? *reinterpret_cast<const v4i *>(x + hv.base + (long long)s * hv.stride + 8 * g)
+                         : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < M::kUnroll; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if (ABSMAX) acc[i] = fmaxf(acc[i], fabsf(v[u][i]));
-        else acc[i] += (double)v[u][i];
+        const float v = in_to_f32<DT>(i & 1 ? (uint32_t)raw[u][i >> 1] >> 16 : (uint32_t)raw[u][i >> 1] & 0xffffu);
+        if (ABSMAX) acc[i] = fmaxf(acc[i], fabsf(v));
+        else acc[i] += (double)v;
       }
   }
 #pragma unroll
@@ -652,22 +650,24 @@ __device__ inline void chunk_stats(const uint16_t *x, const Seg &hv, int chunk, 
     mn[i] = INFINITY;
   }
   for (int s0 = chunk * ct + r; s0 < s_end; s0 += M::R * M::kUnroll) {
-    float v[M::kUnroll][8];
+    v4i raw[M::kUnroll];  // 16-bit pairs as loaded
     bool ok[M::kUnroll];
 #pragma unroll
     for (int u = 0; u < M::kUnroll; ++u) {
       const int s = s0 + u * M::R;
       ok[u] = s < s_end;
-      if (ok[u]) load8<DT>(x + hv.base + (long long)s * hv.stride + 8 * g, v[u]);
+      raw[u] = ok[u] ? *reinterpret_cast<const v4i *>(x + hv.base + (long long)s * hv.stride + 8 * g)
+                     : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < M::kUnroll; ++u)
       if (ok[u])
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          sum[i] += (double)v[u][i];
-          mx[i] = fmaxf(mx[i], v[u][i]);
-          mn[i] = fminf(mn[i], v[u][i]);
+          const float v = in_to_f32<DT>(i & 1 ? (uint32_t)raw[u][i >> 1] >> 16 : (uint32_t)raw[u][i >> 1] & 0xffffu);
+          sum[i] += (double)v;
+          mx[i] = fmaxf(mx[i], v);
+          mn[i] = fminf(mn[i], v);
         }
   }
 #pragma unroll
