@@ -259,3 +259,18 @@ def test_valid_varlen_arguments_without_a_device_report_no_device():
     assert qa.sage_attn_fwd_varlen(*GOOD_ATTN_VL.values()) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "pv_mode": 1, "v_scale": None, "v_mean": None}.values()) == \
         qa.SAGE_ERR_NO_DEVICE
+
+
+def test_size_limits_in_the_header():
+    """The maximum sizes the GPU limit tests run at are the header's."""
+    import re
+
+    hdr = open(HEADER).read()
+    assert re.search(r"#define SAGE_MAX_S \(1 << 20\)", hdr)
+    assert re.search(r"#define SAGE_MAX_BH \(1 << 16\)", hdr)
+    assert qa.sage_buffer_sizes(1, 1, 1, 1 << 20, 128, 0)["q_i8"] == 1 << 27  # q codes of the longest head
+    with pytest.raises(qa.SageError):
+        qa.sage_buffer_sizes(1, 1, 1, (1 << 20) + 1, 128, 0)
+    assert qa.sage_buffer_sizes(256, 256, 64, 33, 64, 0)["k_i8"] == 256 * 64 * 128 * 64  # the most heads
+    with pytest.raises(qa.SageError):
+        qa.sage_buffer_sizes(257, 256, 64, 33, 64, 0)

@@ -1,0 +1,64 @@
+"""GPU parity at the boundary's documented maximum sizes.
+
+SAGE_MAX_S (2^20 tokens in one head) and SAGE_MAX_BH (65536 batch x head
+pairs) are the largest shapes the entry points accept.  At these sizes the
+buffers run to hundreds of MB, the key loop to 8192 tiles and the grids to
+hundreds of thousands of work-groups, so 64-bit offsets, buffer ranges and
+grid decompositions all reach their largest values.  Sampled output rows (and
+heads) are compared with the oracle at the attention bars (cosine >= 0.999,
+mean relative L1 <= 1e-2); codes and scales of sampled blocks bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from quantized_attention_02_amd import synth
+
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+COS_MIN, REL_L1_MAX = 0.999, 1e-2
+MAX_S = 1 << 20  # SAGE_MAX_S (checked against the header in test_abi)
+MAX_BH = 1 << 16  # SAGE_MAX_BH
+
+
+def _check_rows(w, got, b, h, rows, causal, pv):
+    q, k, v = G.inputs(w)
+    ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal,
+                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=[(b, h)], rows=rows,
+                 tile_k=G.TILE_K[pv])[(b, h)]
+    g = got[b, h, rows]
+    c, r = G.cos(g, ref), G.rel_l1(g, ref)
+    print(f"{w.name} head {(b, h)} causal={causal} pv={pv} rows {len(rows)}: cos={c:.6f} rel_l1={r:.2e}")
+    assert np.isfinite(g).all() and c >= COS_MIN and r <= REL_L1_MAX, ((b, h), c, r)
+
+
+@pytest.mark.parametrize("causal,pv", [(False, "fp8"), (True, "fp16")])
+def test_longest_sequence(causal, pv):
+    """One head of SAGE_MAX_S tokens (8192 key tiles)."""
+    w = synth.custom(1, 1, MAX_S, 128, seed=1301)
+    bufs, out, _ = G.run(w, causal=causal, pv=pv)
+    got = G.out_logical(out, w)
+    rows = np.unique(np.concatenate([G.sample_rows(MAX_S, 8, seed=1302), [MAX_S // 3, MAX_S - 129, MAX_S - 1]]))
+    _check_rows(w, got, 0, 0, rows.astype(np.int32), causal, pv)
+    # codes of the last Q and K blocks (their buffer offsets are the largest)
+    q, k, _ = G.inputs(w)
+    dt = O.DTYPES[w.dtype]
+    q8, qs = O.quant_q_head(O.decode16(O.head(q, w.layout, 0, 0), dt), 32)
+    assert np.array_equal(bufs.q_i8.cpu().numpy()[0, 0, MAX_S - 32:MAX_S], q8[-32:])
+    assert bufs.q_scale.cpu().numpy()[0, 0, -1].view(np.uint32) == qs[-1].view(np.uint32)
+    k8, ks, _ = O.quant_k_head(O.decode16(O.head(k, w.layout, 0, 0), dt), 64, True)
+    assert np.array_equal(bufs.k_i8.cpu().numpy()[0, 0, MAX_S - 64:MAX_S], k8[-64:])
+    assert bufs.k_scale.cpu().numpy()[0, 0, MAX_S // 64 - 1].view(np.uint32) == ks[-1].view(np.uint32)
+
+
+def test_most_heads():
+    """B * H = SAGE_MAX_BH with a ragged 33-token sequence (NHD, grouped K/V)."""
+    w = synth.custom(256, 256, 33, 64, layout="NHD", Hkv=64, seed=1311)
+    assert w.B * w.H == MAX_BH
+    _, out, _ = G.run(w, causal=True, pv="fp8")
+    got = G.out_logical(out, w)
+    rows = np.arange(33, dtype=np.int32)
+    for (b, h) in ((0, 0), (255, 255), (128, 77), (17, 200)):
+        _check_rows(w, got, b, h, rows, True, "fp8")
