@@ -272,7 +272,8 @@ struct TileCopy4 {
 };
 
 // pv fp16: the tile's raw 16-bit V rows (TN keys x D channels, 2D bytes a
-// row, as stored in the caller's layout) are copied into LDS as they are;
+// row, as stored in the caller's layout) are copied into LDS as they are (bf16
+// rows are then rounded to fp16 in place, each lane the chunks it copied);
 // the PV MFMA's V^T operand is then read with the transposing LDS load
 // ds_read_b64_tr_b16.  Within each 16-lane group, lane i receives element
 // i % 4 of the 8-byte pieces addressed by lanes 4 j + i / 4 (j = 0..3): with
