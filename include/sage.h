@@ -59,6 +59,10 @@
  *   v_scale float [B][H_kv][D]     one scale per channel.
  *   v_mean  float [B][H_kv][D]     V smoothing only: the channel means subtracted from V
  *                                  before quantisation (same size as v_scale).
+ *   q_mean  float [B][H][nq][D]    Q smoothing only: each Q block's channel means.
+ *   delta_s float [B][H][S_k/128][nq][128]  Q smoothing only: the pre-processing term
+ *           of query block blk and key n at [b][h][n / 128][blk][n % 128] (128-key
+ *           tiles one after the other, so that each tile's rows are contiguous).
  *   SAGE_QK_MXFP4 replaces the Q/K codes and scales by (D / 2 and D / 32 bytes a row):
  *   q_codes uint8 [B][H][S_q][D/2]  E2M1 codes of Q, two per byte (channel 2j in the low
  *                                   nibble of byte j); q_scale uint8 [B][H][S_q][D/32], the
@@ -164,7 +168,7 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
  * with fp32 accumulation of exact products (q_mean enters as 16-bit pieces: 2^-22
  * relative residual for fp16 inputs, exact for bf16).  q_mean and k_mean: from
  * sage_smooth_quant_qk called with q_mean (16-byte aligned); k: the same K tensor.
- * delta_s: fp32 [B][H][nq][S_k] (4-byte aligned).  The attention then adds
+ * delta_s: fp32, the tiled layout above (16-byte aligned).  The attention then adds
  * delta_s[query block][key] * sm_scale to every score.
  */
 int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, const float *q_mean,

@@ -272,7 +272,7 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
 
         nq, sk = bufs.q_i8.shape[2] // BLK_Q, bufs.k_i8.shape[2]
         bufs.q_mean = torch.empty((B, H, nq, D), dtype=torch.float32, device=q.device)
-        bufs.delta_s = torch.empty((B, H, nq, sk), dtype=torch.float32, device=q.device)
+        bufs.delta_s = torch.empty((B, H, sk // KV_PAD, nq, KV_PAD), dtype=torch.float32, device=q.device)
     bufs.smooth_q = bool(smooth_q)
     _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
                                 bufs.q_i8.data_ptr(),

@@ -233,7 +233,7 @@ int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D
   if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!k || !q_mean || !k_mean || !delta_s) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(k, 16) || !aligned(q_mean, 16) || !aligned(k_mean, 4) || !aligned(delta_s, 4))
+  if (!aligned(k, 16) || !aligned(q_mean, 16) || !aligned(k_mean, 4) || !aligned(delta_s, 16))
     return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantQKArgs a;

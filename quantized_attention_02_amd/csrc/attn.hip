@@ -63,12 +63,6 @@ __device__ __forceinline__ int swz(int chunk, int row) {
   return chunk ^ ((row >> 2) & 3);
 }
 
-// Buffer resource for `bytes` bytes at `base` (raw buffer: stride 0, 32-bit
-// data format).  Loads through it past `bytes` return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
-}
-
 // One wavefront-wide buffer load into LDS: lane i copies 16 bytes from
 // resource offset soff + voff (voff per lane, soff wave-uniform) to
 // lds_base + 16 * i.
@@ -504,11 +498,12 @@ k_attn(const AttnArgs a) {
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscb, ntiles * TN * (D / 32));  // FP4 K scales
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase,
                                                PV == 0 ? vbytes : kbytes);  // (pv fp16 copies V itself)
-  // smoothed Q: this wavefront's row of delta (its query block), tile j at byte j TN 4;
-  // only wavefronts with queries copy (a trailing wavefront's block may not exist)
-  const __amdgpu_buffer_rsrc_t drs =
-      make_rsrc(QS && active ? (const void *)(a.delta_s + ((long long)bh * a.nq + (qw >> 5)) * a.S_k) : (const void *)kbase,
-                QS && active ? a.S_k * 4 : 0);
+  // smoothed Q: delta is stored [bh][128-key tile][query block][128]; this
+  // wavefront's row of tile j (its query block) is 512 contiguous bytes at
+  // dbase + j * dtile; only wavefronts with queries copy (a trailing wavefront's
+  // block may not exist)
+  const float *dbase = QS ? a.delta_s + ((long long)bh * (a.S_k / kKvPad) * a.nq + (qw >> 5)) * kKvPad : nullptr;
+  const long long dtile = (long long)a.nq * kKvPad;  // floats from one tile to the next
   // copies of tile j into buffer buf; returns how many copy instructions this
   // wavefront issued without V (pv fp16 counts them to wait for its V alone)
   auto issue_tile = [&](int j, int buf, uint8_t *kb, uint8_t *vb) -> int {
@@ -523,9 +518,12 @@ k_attn(const AttnArgs a) {
     if constexpr (QS) {
       if (active) {
 #pragma unroll
-        for (int i = 0; i < TN / 64; ++i)
-          dma4_buf(drs, (uint32_t)(4 * lane), j * TN * 4 + 256 * i,
+        for (int i = 0; i < TN / 64; ++i) {
+          const int key = j * TN + 64 * i;  // first key of this 64-key half: its 128-key delta tile and half
+          const __amdgpu_buffer_rsrc_t drs = make_rsrc(dbase + (key / kKvPad) * dtile, kKvPad * 4);
+          dma4_buf(drs, (uint32_t)(4 * lane), 256 * ((key / 64) & 1),
                    reinterpret_cast<uint8_t *>(&dsbuf[buf][wave][0]) + 256 * i);
+        }
         n += TN / 64;
       }
     }

@@ -224,12 +224,14 @@ __device__ inline void q_block_smooth(const QuantQKArgs &a, float (&x)[2][8], in
 // of 16-bit values are exact in the fp32 accumulator, so the result carries fp32
 // summation rounding only (and 2^-22 of q_mean with fp16 inputs).
 // A work-group of four wavefronts owns 128 keys of one query head.  Each
-// wavefront keeps its 32 keys' K rows in registers (the B operand) and walks the
-// head's query blocks 32 at a time; the split means of those 32 blocks and their
-// dot products with k_mean are staged once per work-group in LDS (the A operand;
-// rows padded by 16 bytes against bank conflicts).  A lane ends with 16 results
-// of one key; for each, the 32 lanes of a half-wave fill one 128-byte row
-// segment of delta.
+// wavefront keeps its 32 keys' K rows in registers (the A operand) and walks the
+// head's query blocks 32 at a time.  The split means of those 32 blocks and their
+// dot products with k_mean are staged once per work-group in LDS (the B operand;
+// rows padded by 16 bytes against bank conflicts; two buffers, so one barrier a
+// chunk), and the means of the chunk after next load while a chunk is computed.  A
+// lane ends with 16 results of one query block: 4 runs of 4 consecutive keys,
+// stored as 4 float4.  delta is stored tile-major ([bh][key tile][block][128
+// keys]), so a work-group writes one contiguous 16 KB region per chunk.
 // ---------------------------------------------------------------------------
 constexpr int kDeltaKeys = 128;
 static_assert(kDeltaKeys == kKvPad, "a delta work-group covers one 128-key K tile");
@@ -277,10 +279,10 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   constexpr int KSTEPS = D / 16;  // MFMA k steps over the channels
   constexpr int RS = D + 8;       // LDS row stride (16-bit elements): 16 bytes of padding
   constexpr int CPT = D / 8;      // channels per staging thread (8 threads per query block)
-  __shared__ __align__(16) uint16_t am[NS][32 * RS];
-  __shared__ float cs[32];
+  __shared__ __align__(16) uint16_t am[2][NS][32 * RS];  // double-buffered by chunk
+  __shared__ float cs[2][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
-  const int nkt = a.S_k / kDeltaKeys;
+  const int nkt = a.S_k / kDeltaKeys + (a.S_k % kDeltaKeys != 0);
   // work-group -> (query head, key tile); with a grid that divides evenly, each
   // XCD takes whole heads, so a head's block means are read through one L2
   int wg = blockIdx.x;
@@ -288,8 +290,9 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   const int bh = wg / nkt, kt = wg % nkt;
   const int b = bh / a.H, h = bh % a.H, hk = h / (a.H / a.H_kv);
   const Seg ks = fixed_seg(a.layout, b, hk, a.H_kv, a.S, a.S_k, D);
-  const int n = kt * kDeltaKeys + 32 * wave + (lane & 31);  // this lane's key (< S_k)
-  // B operand: channels 16 s + 8 hh .. +7 of key n for each k step s
+  const int key0 = kt * kDeltaKeys + 32 * wave;  // this wavefront's 32 keys (< S_k)
+  const int n = key0 + (lane & 31);              // the key whose K row this lane holds
+  // A operand: channels 16 s + 8 hh .. +7 of key n for each k step s
   const uint16_t *k = (const uint16_t *)a.k;
   T8 kf[KSTEPS];
 #pragma unroll
@@ -303,42 +306,49 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   float km[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) km[i] = a.k_mean[((long long)b * a.H_kv + hk) * D + sc + i];
-  const float *qm = a.q_mean + (long long)bh * a.nq * D;
-  float *dst = delta + (long long)bh * a.nq * a.S_k + n;
-  for (int blk0 = 0; blk0 < a.nq; blk0 += 32) {
-    {
-      const int blk = blk0 + sb;
-      float x[CPT];
+  // The head's block means and this work-group's 128-key tile of delta go
+  // through buffer resources: loads past the last block return zeros and stores
+  // past it are dropped, so neither needs a branch, and the wait for a chunk's
+  // prefetched means leaves the previous chunk's stores in flight.
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q_mean + (long long)bh * a.nq * D, a.nq * D * 4);
+  const __amdgpu_buffer_rsrc_t drs =
+      make_rsrc(delta + ((long long)bh * nkt + kt) * a.nq * kDeltaKeys, a.nq * kDeltaKeys * 4);
+  // this thread's means of block blk0 + sb
+  auto load_means = [&](float (&x)[CPT], int blk0) {
 #pragma unroll
-      for (int i = 0; i < CPT; i += 4) {
-        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (blk < a.nq) v = *reinterpret_cast<const float4 *>(qm + (long long)blk * D + sc + i);
-        x[i] = v.x;
-        x[i + 1] = v.y;
-        x[i + 2] = v.z;
-        x[i + 3] = v.w;
-      }
-      float c = 0.0f;
+    for (int i = 0; i < CPT; i += 4) {
+      const v4i u = __builtin_amdgcn_raw_buffer_load_b128(qrs, ((blk0 + sb) * D + sc + i) * 4, 0, 0);
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) c = __builtin_fmaf(x[i], km[i], c);
-      c += __shfl_xor(c, 1, 64);
-      c += __shfl_xor(c, 2, 64);
-      c += __shfl_xor(c, 4, 64);
-      if ((tid & 7) == 0) cs[sb] = c;
-      uint16_t p[CPT][NS];
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) M::split(x[i], p[i]);
-#pragma unroll
-      for (int sp = 0; sp < NS; ++sp)
-#pragma unroll
-        for (int i = 0; i < CPT; i += 8) {
-          v4i u;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) u[j] = (int)((uint32_t)p[i + 2 * j][sp] | ((uint32_t)p[i + 2 * j + 1][sp] << 16));
-          *reinterpret_cast<v4i *>(&am[sp][sb * RS + sc + i]) = u;
-        }
+      for (int e = 0; e < 4; ++e) x[i + e] = __int_as_float(u[e]);
     }
-    __syncthreads();
+  };
+  // stage the means in x (one chunk) into buffer buf: split pieces and dot
+  // products with k_mean
+  auto stage = [&](const float (&x)[CPT], int buf) {
+    float c = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) c = __builtin_fmaf(x[i], km[i], c);
+    c += __shfl_xor(c, 1, 64);
+    c += __shfl_xor(c, 2, 64);
+    c += __shfl_xor(c, 4, 64);
+    if ((tid & 7) == 0) cs[buf][sb] = c;
+    uint16_t p[CPT][NS];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) M::split(x[i], p[i]);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+      for (int i = 0; i < CPT; i += 8) {
+        v4i u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = (int)((uint32_t)p[i + 2 * j][sp] | ((uint32_t)p[i + 2 * j + 1][sp] << 16));
+        *reinterpret_cast<v4i *>(&am[buf][sp][sb * RS + sc + i]) = u;
+      }
+  };
+  // chunk blk0 from buffer buf: MFMAs and stores
+  auto compute = [&](int blk0, int buf) {
+    // D[key][block] = K rows (A) . split means (B): the lane's column is query
+    // block blk0 + lane % 32, its rows the keys key0 + 8 g + 4 hh + 0..3 (g < 4)
     v16f acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
@@ -346,16 +356,40 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp) {
-        const v4i u = *reinterpret_cast<const v4i *>(&am[sp][(lane & 31) * RS + 16 * s + 8 * hh]);
-        acc = M::mfma(__builtin_bit_cast(T8, u), kf[s], acc);
+        const v4i u = *reinterpret_cast<const v4i *>(&am[buf][sp][(lane & 31) * RS + 16 * s + 8 * hh]);
+        acc = M::mfma(kf[s], __builtin_bit_cast(T8, u), acc);
       }
-    // lane holds rows (query blocks) 8 (r / 4) + 4 hh + r % 4 of column n
+    // row blk0 + lane % 32 of the tile (a store past the last block is dropped)
+    const float c = cs[buf][lane & 31];
+    const int row = (blk0 + (lane & 31)) * kDeltaKeys + 32 * wave + 4 * hh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 8 * (r >> 2) + 4 * hh + (r & 3), blk = blk0 + i;
-      if (blk < a.nq) dst[(long long)blk * a.S_k] = n < a.S ? acc[r] - cs[i] : 0.0f;
+    for (int g = 0; g < 4; ++g) {
+      const int k0 = key0 + 8 * g + 4 * hh;
+      v4i o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __float_as_int(k0 + e < a.S ? acc[4 * g + e] - c : 0.0f);  // padding keys: 0
+      __builtin_amdgcn_raw_buffer_store_b128(o, drs, (row + 8 * g) * 4, 0, 0);
     }
-    __syncthreads();  // am and cs are restaged for the next chunk
+  };
+  // Chunk c is computed from buffer c % 2 while the means of chunk c + 2 load
+  // (two register sets, so a load has two chunks' time to arrive; past the last
+  // chunk they read as zeros and are not used).  Chunk c + 1 is staged into the
+  // other buffer after chunk c's stores; that buffer's last readers (chunk c - 1)
+  // are past chunk c's barrier.
+  float xa[CPT], xb[CPT];
+  load_means(xa, 0);
+  load_means(xb, 32);
+  stage(xa, 0);
+  for (int blk0 = 0; blk0 < a.nq; blk0 += 64) {
+    __syncthreads();
+    load_means(xa, blk0 + 64);
+    compute(blk0, 0);
+    if (blk0 + 32 >= a.nq) break;
+    stage(xb, 1);
+    __syncthreads();
+    load_means(xb, blk0 + 96);
+    compute(blk0 + 32, 1);
+    if (blk0 + 64 < a.nq) stage(xa, 0);
   }
 }
 

@@ -103,6 +103,13 @@ __host__ __device__ inline long long varlen_rows(int total, int B, int pad) {
 // One (sequence or batch entry, head) of an input tensor and its rows in a
 // quantised buffer: element (s, d), s < S, is at base + s * stride + d of the
 // input; its buffer row is row0 + s.
+// Buffer resource for `bytes` bytes at `base` (raw buffer: stride 0, 32-bit
+// data format).  Loads through it past `bytes` return zeros; stores past it
+// are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
 struct Seg {
   int S;
   long long base, stride, row0;

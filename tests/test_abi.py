@@ -92,7 +92,8 @@ BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict
           dict(B=1 << 9, H=1 << 8, H_kv=1 << 8), dict(H_kv=0), dict(H_kv=3), dict(H=3, H_kv=2), dict(H_kv=-2),
           dict(qk_quant=3), dict(qk_quant=-1), dict(q_mean=P + 2), dict(q_mean=P, qk_quant=2)]
 BAD_DELTA = [dict(k=None), dict(q_mean=None), dict(k_mean=None), dict(delta_s=None), dict(q_mean=P + 4),
-             dict(delta_s=P + 2), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2), dict(dtype=4), dict(S=0)]
+             dict(delta_s=P + 2), dict(delta_s=P + 4), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2),
+             dict(dtype=4), dict(S=0)]
 BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80),
          dict(v_mean=P + 2)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),

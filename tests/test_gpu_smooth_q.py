@@ -40,7 +40,10 @@ def test_smooth_q_quant_and_delta(w, qk):
     bufs, _, _ = G.run(w, qk_quant=qk, smooth_q=True)
     dt = O.DTYPES[w.dtype]
     q8, qs = bufs.q_i8.cpu().numpy(), bufs.q_scale.cpu().numpy()
-    qm, ds = bufs.q_mean.cpu().numpy(), bufs.delta_s.cpu().numpy()
+    qm = bufs.q_mean.cpu().numpy()
+    # delta_s is stored [B][H][S_k / 128][nq][128]: back to [B][H][nq][S_k]
+    dt_ = bufs.delta_s.cpu().numpy()
+    ds = dt_.transpose(0, 1, 3, 2, 4).reshape(w.B, w.H, dt_.shape[3], -1)
     S, nq = w.S, (w.S + 31) // 32
     for b in range(w.B):
         for h in range(w.H):
