@@ -191,6 +191,17 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
                  float *v_scale, float *v_mean, void *stream);
 
 /*
+ * sage_smooth_quant_qk followed by sage_quant_v (on V's H_kv heads), in one call:
+ * the same arguments, checks and results (every output buffer bit for bit), with
+ * the passes that do not depend on each other sharing kernel launches (four
+ * launches instead of eight).  For pv fp8; v: the V tensor (dtype, layout,
+ * H_kv heads).  q_mean and v_mean select Q and V smoothing as in the two calls.
+ */
+int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, int B, int H, int H_kv, int S, int D,
+                      int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
+                      float *k_mean, float *q_mean, uint8_t *v_fp8, float *v_scale, float *v_mean, void *stream);
+
+/*
  * Fused quantized attention ([SA2]; [KAI] 2.1; [GUIDE] 五分钟跑通, 性能调优实战).
  * For each query row i, key tiles (SAGE_TILE_K_FP8 / SAGE_TILE_K_FP16 keys) in order,
  * fp32 online softmax:

@@ -30,7 +30,7 @@ QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2}  # Q/K quantisation (include/sage.h
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
-EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_attn_fwd",
+EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_quantize_qkv", "sage_attn_fwd",
             "sage_attn_fwd_dump_qk", "sage_qk_delta", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
             "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch"]
 
@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 6 + [c_void_p]
         L.sage_qk_delta.argtypes = [c_void_p] + [c_int] * 7 + [c_void_p] * 4
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
+        L.sage_quantize_qkv.argtypes = [c_void_p] * 3 + [c_int] * 8 + [c_void_p] * 10
         tail = [c_int] * 8 + [c_float, c_int, c_int]
         L.sage_attn_fwd.argtypes = [c_void_p] * 9 + tail + [c_void_p]
         L.sage_attn_fwd_dump_qk.argtypes = [c_void_p] * 8 + tail + [c_int, c_int, c_void_p, c_void_p]
@@ -106,6 +107,12 @@ def sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, 
     """All tensor arguments are device pointers (ints); returns the status code."""
     return lib().sage_smooth_quant_qk(q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale,
                                       k_mean, q_mean, stream)
+
+
+def sage_quantize_qkv(q, k, v, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale, k_mean,
+                      q_mean, v_fp8, v_scale, v_mean, stream):
+    return lib().sage_quantize_qkv(q, k, v, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, q_scale, k_i8, k_scale,
+                                   k_mean, q_mean, v_fp8, v_scale, v_mean, stream)
 
 
 def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, q_mean, k_mean, delta_s, stream):
@@ -246,8 +253,10 @@ def _kv_heads(q, k, v, tensor_layout):
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
-             qk_quant="int8", smooth_v=False, smooth_q=False) -> Quantized:
-    """Run sage_smooth_quant_qk (and sage_quant_v in pv fp8 mode) on torch tensors.
+             qk_quant="int8", smooth_v=False, smooth_q=False, fused=True) -> Quantized:
+    """Run sage_quantize_qkv in pv fp8 mode (fused=False: sage_smooth_quant_qk and
+    sage_quant_v, same results), or sage_smooth_quant_qk alone in pv fp16 mode, on
+    torch tensors.
     k and v may have fewer heads than q (grouped-query attention); qk_quant "block"
     or "lane" (one scale per Q token and per 16-key lane group of K); smooth_v
     (pv fp8): quantise V minus its channel mean; smooth_q (INT8 modes): quantise
@@ -274,18 +283,24 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         bufs.q_mean = torch.empty((B, H, nq, D), dtype=torch.float32, device=q.device)
         bufs.delta_s = torch.empty((B, H, sk // KV_PAD, nq, KV_PAD), dtype=torch.float32, device=q.device)
     bufs.smooth_q = bool(smooth_q)
-    _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
-                                bufs.q_i8.data_ptr(),
-                                bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(),
-                                bufs.k_mean.data_ptr(), bufs.q_mean.data_ptr() if smooth_q else None, st),
-           "sage_smooth_quant_qk")
+    bufs.smooth_v = bool(smooth_v)
+    qm = bufs.q_mean.data_ptr() if smooth_q else None
+    vm = bufs.v_mean.data_ptr() if smooth_v else None
+    if pv_mode == "fp8" and fused:
+        _check(sage_quantize_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
+                                 bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
+                                 bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, bufs.v_fp8.data_ptr(),
+                                 bufs.v_scale.data_ptr(), vm, st), "sage_quantize_qkv")
+    else:
+        _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
+                                    bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
+                                    bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, st), "sage_smooth_quant_qk")
+        if pv_mode == "fp8":
+            _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(),
+                                bufs.v_scale.data_ptr(), vm, st), "sage_quant_v")
     if smooth_q:
         _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.q_mean.data_ptr(), bufs.k_mean.data_ptr(),
                              bufs.delta_s.data_ptr(), st), "sage_qk_delta")
-    bufs.smooth_v = bool(smooth_v)
-    if pv_mode == "fp8":
-        _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
-                            bufs.v_mean.data_ptr() if smooth_v else None, st), "sage_quant_v")
     return bufs
 
 

@@ -188,9 +188,10 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
   return SAGE_OK;
 }
 
-int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
-                         int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
-                         float *k_mean, float *q_mean, void *stream) {
+// Argument checks and kernel arguments of the Q/K pass (no device check).
+static int qk_args(QuantQKArgs &a, const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
+                   int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
+                   float *k_mean, float *q_mean) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
@@ -200,8 +201,6 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   if (!q || !k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4)) return SAGE_ERR_INVALID_ARG;
-  if ((rc = check_device())) return rc;
-  QuantQKArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;
   a.k = k;
@@ -223,7 +222,55 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
   a.nk = a.S_k / kBlkK;
   a.qk = qk_quant;
   a.q_mean = q_mean;
+  return SAGE_OK;
+}
+
+// Argument checks and kernel arguments of the V pass (H: V heads; no device check).
+static int v_args(QuantVArgs &a, const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8,
+                  float *v_scale, float *v_mean) {
+  int rc = check_shape(B, H, S, D);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, layout))) return rc;
+  if (!v || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4) || (v_mean && !aligned(v_mean, 4)))
+    return SAGE_ERR_INVALID_ARG;
+  memset(&a, 0, sizeof a);
+  a.v = v;
+  a.v_fp8 = v_fp8;
+  a.v_scale = v_scale;
+  a.v_mean = v_mean;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.layout = layout;
+  a.dtype = dtype;
+  a.nk = roundup(S, kKvPad) / kBlkK;
+  return SAGE_OK;
+}
+
+int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, int H_kv, int S, int D,
+                         int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
+                         float *k_mean, float *q_mean, void *stream) {
+  QuantQKArgs a;
+  int rc = qk_args(a, q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_codes, q_scale, k_codes, k_scale, k_mean,
+                   q_mean);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
+}
+
+int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, int B, int H, int H_kv, int S, int D,
+                      int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
+                      float *k_mean, float *q_mean, uint8_t *v_fp8, float *v_scale, float *v_mean, void *stream) {
+  QuantQKArgs a;
+  QuantVArgs va;
+  int rc = qk_args(a, q, k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_codes, q_scale, k_codes, k_scale, k_mean,
+                   q_mean);
+  if (rc) return rc;
+  if ((rc = v_args(va, v, dtype, B, H_kv, S, D, layout, v_fp8, v_scale, v_mean))) return rc;
+  if ((rc = check_device())) return rc;
+  return launch_status(launch_quantize_qkv(a, va, (hipStream_t)stream));
 }
 
 int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, const float *q_mean,
@@ -257,26 +304,10 @@ int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D
 
 int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_fp8, float *v_scale,
                  float *v_mean, void *stream) {
-  int rc = check_shape(B, H, S, D);
-  if (rc) return rc;
-  if ((rc = check_enums(dtype, layout))) return rc;
-  if (!v || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(v, 16) || !aligned(v_fp8, 16) || !aligned(v_scale, 4) || (v_mean && !aligned(v_mean, 4)))
-    return SAGE_ERR_INVALID_ARG;
-  if ((rc = check_device())) return rc;
   QuantVArgs a;
-  memset(&a, 0, sizeof a);
-  a.v = v;
-  a.v_fp8 = v_fp8;
-  a.v_scale = v_scale;
-  a.v_mean = v_mean;
-  a.B = B;
-  a.H = H;
-  a.S = S;
-  a.D = D;
-  a.layout = layout;
-  a.dtype = dtype;
-  a.nk = roundup(S, kKvPad) / kBlkK;
+  int rc = v_args(a, v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
   return launch_status(launch_quant_v(a, (hipStream_t)stream));
 }
 

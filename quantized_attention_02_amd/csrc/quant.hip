@@ -166,13 +166,15 @@ __device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk,
 // K channel sums of one chunk of tokens -> partials (k_i8 region of the head).
 // ---------------------------------------------------------------------------
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) {
+__device__ inline void ksum_wg(const QuantQKArgs &a, int wg) {
   const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;  // bh: K head (b, h_kv)
+  const int bh = wg / nch, chunk = wg % nch;  // bh: K head (b, h_kv)
   const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
   if (chunk >= n_chunks(sg.S)) return;
   chunk_reduce<DT, D, false>((const uint16_t *)a.k, sg, chunk, a.k_i8 + sg.row0 * code_row_bytes<D>(a));
 }
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) { ksum_wg<DT, D>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Smoothed Q ("SageAttention2" summary, SageAttention2方法: subtract each block
@@ -399,10 +401,10 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
 // INT8 MFMA layout of the attention kernel.
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool LANE>
-__global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
+__device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
   __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x / a.nq, blk = blockIdx.x % a.nq;
+  const int bh = wg / a.nq, blk = wg % a.nq;
   const Seg hv = q_seg<D>(a, bh / a.H, bh % a.H);
   if (blk >= ceil_div(hv.S, kBlkQ)) return;  // past this sequence's blocks (packed batches)
   const uint16_t *q = (const uint16_t *)a.q;
@@ -460,11 +462,13 @@ __global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
     *reinterpret_cast<v2i *>(a.q_i8 + (hv.row0 + blk * kBlkQ + row) * D + c8) = out;
   }
 }
+template <int DT, int D, bool LANE>
+__global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) { qquant_wg<DT, D, LANE>(a, blockIdx.x); }
 
 // k_mean[bh][d] = fp32(sum over the head's chunk partials / S); thread = (K head bh, d)
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+__device__ inline void kmean_wg(const QuantQKArgs &a, int wg) {
+  const long long i = (long long)wg * kThreads + threadIdx.x;
   if (i >= (long long)a.B * a.H_kv * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
   const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
@@ -478,6 +482,8 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
   for (int c = 0; c < kMaxChunks; ++c) t += v[c];
   a.k_mean[i] = sg.S > 0 ? (float)(t / (double)sg.S) : 0.0f;
 }
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) { kmean_wg<D>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Pass 2: INT8 quantisation of one 64-token block of K - k_mean: one scale for
@@ -488,11 +494,11 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) {
 __device__ inline int lane_group_in_block(int row) { return 2 * (row >> 5) + ((row >> 2) & 1); }
 
 template <int DT, int D, bool LANE>
-__global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
+__device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
   __shared__ float red[4][kThreads / 64];
   __shared__ float mean[D];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x / a.nk, blk = blockIdx.x % a.nk;  // bh: K head (b, h_kv)
+  const int bh = wg / a.nk, blk = wg % a.nk;  // bh: K head (b, h_kv)
   const Seg hv = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
   if (blk >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's rows
   const uint16_t *k = (const uint16_t *)a.k;
@@ -574,6 +580,8 @@ __global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) {
     *reinterpret_cast<v2i *>(a.k_i8 + (hv.row0 + blk * kBlkK + row) * D + c8) = out;
   }
 }
+template <int DT, int D, bool LANE>
+__global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) { kquant_wg<DT, D, LANE>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // MXFP4 quantisation of one block of ROWS tokens (32 of Q, or 64 of K - k_mean):
@@ -600,7 +608,7 @@ __device__ inline int mx_exponent(float amax) {  // floor(log2(amax)) - 2, clamp
 }
 
 template <int DT, int D, bool IS_K>
-__global__ __launch_bounds__(kThreads) void k_mxfp4(const QuantQKArgs a) {
+__device__ inline void mxfp4_wg(const QuantQKArgs &a, int wg) {
   constexpr int ROWS = IS_K ? kBlkK : kBlkQ;
   constexpr int vec_per_row = D / 8;
   constexpr int nvec = ROWS * vec_per_row;
@@ -608,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4(const QuantQKArgs a) {
   __shared__ float mean[D];
   const int tid = threadIdx.x;
   const int nblk = IS_K ? a.nk : a.nq;
-  const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+  const int bh = wg / nblk, blk = wg % nblk;
   const int hn = IS_K ? a.H_kv : a.H;
   const Seg hv = IS_K ? k_seg<D>(a, bh / hn, bh % hn) : q_seg<D>(a, bh / hn, bh % hn);
   if (IS_K ? blk >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK) : blk >= ceil_div(hv.S, kBlkQ)) return;
@@ -649,6 +657,8 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4(const QuantQKArgs a) {
     if (c8 % 32 == 0) scales[r * (D / 32) + c8 / 32] = (uint8_t)(e + 127);
   }
 }
+template <int DT, int D, bool IS_K>
+__global__ __launch_bounds__(kThreads) void k_mxfp4(const QuantQKArgs a) { mxfp4_wg<DT, D, IS_K>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // V, four short launches:
@@ -727,26 +737,30 @@ __device__ inline void chunk_stats(const uint16_t *x, const Seg &hv, int chunk, 
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void k_vstats_part(const QuantVArgs a) {
+__device__ inline void vstats_part_wg(const QuantVArgs &a, int wg) {
   const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  const int bh = wg / nch, chunk = wg % nch;
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
   if (chunk >= n_chunks(sg.S)) return;
   chunk_stats<DT, D>((const uint16_t *)a.v, sg, chunk, a.v_fp8 + sg.row0 * D);
 }
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_vstats_part(const QuantVArgs a) { vstats_part_wg<DT, D>(a, blockIdx.x); }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void k_vamax_part(const QuantVArgs a) {
+__device__ inline void vamax_part_wg(const QuantVArgs &a, int wg) {
   const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  const int bh = wg / nch, chunk = wg % nch;
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
   if (chunk >= n_chunks(sg.S)) return;
   chunk_reduce<DT, D, true>((const uint16_t *)a.v, sg, chunk, a.v_fp8 + sg.row0 * D);
 }
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_vamax_part(const QuantVArgs a) { vamax_part_wg<DT, D>(a, blockIdx.x); }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) {
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+__device__ inline void vamax_wg(const QuantVArgs &a, int wg) {
+  const long long i = (long long)wg * kThreads + threadIdx.x;
   if (i >= (long long)a.B * a.H * D) return;
   const int bh = (int)(i / D), d = (int)(i % D);
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
@@ -775,6 +789,8 @@ __global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) {
   for (int c = 0; c < kMaxChunks; ++c) m = fmaxf(m, v[c]);
   a.v_scale[i] = m;
 }
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) { vamax_wg<D>(a, blockIdx.x); }
 
 // One 64-key tile of one head: thread (q, g) converts keys 4q .. 4q + 3 of
 // channels 8g .. 8g + 7.  The four keys are consecutive in the tile's key
@@ -782,9 +798,9 @@ __global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) {
 // form one 32-bit word of the channel's 64-byte row; the 16 threads of a
 // channel group together write whole rows.
 template <int DT, int D>
-__global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
-  const int tid = threadIdx.x, q = tid & 15, g = tid >> 4;
-  const int bh = blockIdx.x / a.nk, t = blockIdx.x % a.nk;
+__device__ inline void vconvert_wg(const QuantVArgs &a, int wg, int tid) {
+  const int q = tid & 15, g = tid >> 4;
+  const int bh = wg / a.nk, t = wg % a.nk;
   const Seg hv = v_seg<D>(a, bh / a.H, bh % a.H);
   if (t >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's tiles
   const uint16_t *v = (const uint16_t *)a.v;
@@ -820,14 +836,18 @@ __global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) {
     *reinterpret_cast<int *>(dst + i * kBlkK) = w;
   }
 }
+template <int DT, int D>
+__global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) { vconvert_wg<DT, D>(a, blockIdx.x, threadIdx.x); }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_vscale(const QuantVArgs a) {
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+__device__ inline void vscale_wg(const QuantVArgs &a, int wg) {
+  const long long i = (long long)wg * kThreads + threadIdx.x;
   if (i >= (long long)a.B * a.H * D) return;
   const float m = a.v_scale[i];
   a.v_scale[i] = m > 0.0f ? m / 448.0f : 0.0f;
 }
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_vscale(const QuantVArgs a) { vscale_wg<D>(a, blockIdx.x); }
 
 template <int DT, int D>
 static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
@@ -854,6 +874,86 @@ static void launch_v(const QuantVArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((k_vamax<D>), dim3(gd), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_vconvert<DT, D>), dim3(bh * a.nk), dim3(2 * D), 0, stream, a);
   hipLaunchKernelGGL((k_vscale<D>), dim3(gd), dim3(kThreads), 0, stream, a);
+}
+
+// ---------------------------------------------------------------------------
+// Q, K and V quantisation in four launches (sage_quantize_qkv): the passes of
+// sage_smooth_quant_qk and sage_quant_v that do not depend on each other share
+// a launch, each work-group taking one role by its index:
+//   1. K chunk sums | V chunk statistics
+//   2. Q quantisation | K means | V abs-max (and means) from the chunk partials
+//   3. K quantisation | V FP8 conversion
+//   4. V scales
+// Every pass that overwrites a buffer holding chunk partials (K and V codes)
+// runs in a later launch than the work-groups that read them.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool VSTATS>
+__global__ __launch_bounds__(kThreads) void k_qkv1(const QuantQKArgs a, const QuantVArgs v) {
+  const int n_k = a.B * a.H_kv * chunk_grid(a.S);
+  const int wg = blockIdx.x;
+  if (wg < n_k) ksum_wg<DT, D>(a, wg);
+  else if constexpr (VSTATS) vstats_part_wg<DT, D>(v, wg - n_k);
+  else vamax_part_wg<DT, D>(v, wg - n_k);
+}
+
+template <int DT, int D, int QK>
+__global__ __launch_bounds__(kThreads) void k_qkv2(const QuantQKArgs a, const QuantVArgs v) {
+  const int n_q = a.B * a.H * a.nq, n_m = ceil_div(a.B * a.H_kv * D, kThreads);
+  const int wg = blockIdx.x;
+  if (wg < n_q) {
+    if constexpr (QK == 2) mxfp4_wg<DT, D, false>(a, wg);
+    else qquant_wg<DT, D, QK == 1>(a, wg);
+  } else if (wg < n_q + n_m) {
+    kmean_wg<D>(a, wg - n_q);
+  } else {
+    vamax_wg<D>(v, wg - n_q - n_m);
+  }
+}
+
+template <int DT, int D, int QK>
+__global__ __launch_bounds__(kThreads) void k_qkv3(const QuantQKArgs a, const QuantVArgs v) {
+  constexpr int TPW = kThreads / (2 * D);  // 64-key V tiles a work-group converts (2 D threads each)
+  const int n_k = a.B * a.H_kv * a.nk;
+  const int wg = blockIdx.x;
+  if (wg < n_k) {
+    if constexpr (QK == 2) mxfp4_wg<DT, D, true>(a, wg);
+    else kquant_wg<DT, D, QK == 1>(a, wg);
+  } else {
+    const int t = (wg - n_k) * TPW + (int)threadIdx.x / (2 * D);
+    if (t < v.B * v.H * v.nk) vconvert_wg<DT, D>(v, t, (int)threadIdx.x % (2 * D));
+  }
+}
+
+template <int DT, int D, int QK>
+static void launch_qkv3(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t st) {
+  const int bhk = a.B * a.H_kv, gm = (bhk * D + kThreads - 1) / kThreads;
+  constexpr int TPW = kThreads / (2 * D);
+  hipLaunchKernelGGL((k_qkv2<DT, D, QK>), dim3(a.B * a.H * a.nq + 2 * gm), dim3(kThreads), 0, st, a, v);
+  hipLaunchKernelGGL((k_qkv3<DT, D, QK>), dim3(bhk * a.nk + (bhk * v.nk + TPW - 1) / TPW), dim3(kThreads), 0, st,
+                     a, v);
+}
+
+template <int DT, int D>
+static void launch_qkv(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t st) {
+  const int bhk = a.B * a.H_kv, gm = (bhk * D + kThreads - 1) / kThreads;
+  const dim3 g1(2 * bhk * chunk_grid(a.S));  // K chunks, then as many V chunks (V has H_kv heads)
+  if (v.v_mean) hipLaunchKernelGGL((k_qkv1<DT, D, true>), g1, dim3(kThreads), 0, st, a, v);
+  else hipLaunchKernelGGL((k_qkv1<DT, D, false>), g1, dim3(kThreads), 0, st, a, v);
+  if (a.qk == 2) launch_qkv3<DT, D, 2>(a, v, st);
+  else if (a.qk == 1) launch_qkv3<DT, D, 1>(a, v, st);
+  else launch_qkv3<DT, D, 0>(a, v, st);
+  hipLaunchKernelGGL((k_vscale<D>), dim3(gm), dim3(kThreads), 0, st, v);
+}
+
+hipError_t launch_quantize_qkv(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t stream) {
+  if (a.D == 64) {
+    if (a.dtype == 0) launch_qkv<0, 64>(a, v, stream);
+    else launch_qkv<1, 64>(a, v, stream);
+  } else {
+    if (a.dtype == 0) launch_qkv<0, 128>(a, v, stream);
+    else launch_qkv<1, 128>(a, v, stream);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream) {

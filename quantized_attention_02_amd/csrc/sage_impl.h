@@ -174,6 +174,7 @@ struct AttnArgs {
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);
 hipError_t launch_quant_v(const QuantVArgs &a, hipStream_t stream);
 // pre-processing term of smoothed Q, delta[B][H][nq][S_k] (a.q_mean and a.k_mean read)
+hipError_t launch_quantize_qkv(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t stream);
 hipError_t launch_qk_delta(const QuantQKArgs &a, float *delta, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs &a, bool dump, hipStream_t stream);
 int attn_tile_keys(int pv_mode);  // keys per online-softmax tile of the attention kernel

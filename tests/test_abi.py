@@ -106,6 +106,24 @@ BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dic
             dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
 
 
+GOOD_QKV = dict(q=P, k=P, v=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64, layout=0, qk_quant=0, q_i8=P, q_scale=P,
+                k_i8=P, k_scale=P, k_mean=P, q_mean=None, v_fp8=P, v_scale=P, v_mean=None, stream=None)
+# every check of the Q/K call and of the V call (on the H_kv V heads)
+BAD_QKV = [b for b in BAD_QK if "H" not in b and "B" not in b] + [dict(v=None), dict(v=P + 2), dict(v_fp8=P + 4),
+                                                                   dict(v_scale=None), dict(v_scale=P + 1),
+                                                                   dict(v_mean=P + 2), dict(H_kv=3), dict(H=3)]
+
+
+def _call_qkv(**kw):
+    a = {**GOOD_QKV, **kw}
+    return qa.sage_quantize_qkv(*a.values())
+
+
+@pytest.mark.parametrize("bad", BAD_QKV, ids=[str(b) for b in BAD_QKV])
+def test_quantize_qkv_rejects(bad):
+    assert _call_qkv(**bad) == qa.SAGE_ERR_INVALID_ARG
+
+
 def _call_qk(**kw):
     a = {**GOOD_QK, **kw}
     return qa.sage_smooth_quant_qk(*a.values())
@@ -186,6 +204,9 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_attn(H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v() == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn() == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qkv() == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qkv(q_mean=P, v_mean=P, qk_quant=1) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qkv(qk_quant=2, H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
 
 
 def test_python_wrapper_maps_unsupported_to_value_error(monkeypatch):

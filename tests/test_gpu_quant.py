@@ -90,3 +90,44 @@ def test_quant_all_zero_inputs():
         assert not t.any() and torch.isfinite(t).all()
     for t in (bufs.q_i8, bufs.k_i8, bufs.v_fp8):
         assert not t.any()
+
+
+FUSED_CASES = [
+    (synth.custom(1, 2, 256, 64, seed=1401), "int8", False, False),
+    (synth.custom(2, 6, 300, 128, layout="NHD", Hkv=2, seed=1402), "int8", True, False),
+    (synth.custom(1, 4, 257, 128, dtype="bf16", layout="NHD", seed=1403), "int8_lane", False, True),
+    (synth.custom(2, 3, 100, 64, dtype="bf16", seed=1404), "mxfp4", True, False),
+    (synth.custom(1, 8, 1000, 128, Hkv=4, token_norm=True, q_bias_sigma=3.0, seed=1405), "int8", True, True),
+    (synth.custom(1, 2, 1, 64, seed=1406), "int8_lane", True, True),
+    (synth.WORKLOADS["snippet_b2h32s4096d128"], "int8", False, False),
+]
+
+
+@pytest.mark.parametrize("w,qk,smooth_v,smooth_q", FUSED_CASES,
+                         ids=[f"{w.name}-{qk}-sv{int(sv)}-sq{int(sq)}" for w, qk, sv, sq in FUSED_CASES])
+def test_quantize_qkv_equals_the_two_calls(w, qk, smooth_v, smooth_q):
+    """sage_quantize_qkv (four launches) writes every buffer bit for bit as
+    sage_smooth_quant_qk followed by sage_quant_v does."""
+    import quantized_attention_02_amd as qa
+
+    import torch
+
+    q, k, v = (G.to_device(x, w.dtype) for x in G.inputs(w))
+    res = []
+    for fused in (True, False):
+        # every buffer starts as the same byte pattern, so a byte that only one
+        # of the two paths writes shows up as a difference
+        bufs = qa.Quantized(w.B, w.H, w.S, w.D, q.device, w.kv_heads, qk)
+        nq, sk = bufs.q_i8.shape[2] // qa.BLK_Q, bufs.k_i8.shape[2]
+        bufs.q_mean = torch.empty((w.B, w.H, nq, w.D), dtype=torch.float32, device=q.device)
+        bufs.delta_s = torch.empty((w.B, w.H, sk // qa.KV_PAD, nq, qa.KV_PAD), dtype=torch.float32, device=q.device)
+        for n in ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale", "v_mean", "q_mean", "delta_s"):
+            getattr(bufs, n).view(torch.uint8).fill_(0xA5)
+        qa.quantize(q, k, v, w.layout, "fp8", bufs, qk_quant=qk, smooth_v=smooth_v, smooth_q=smooth_q, fused=fused)
+        torch.cuda.synchronize()
+        names = ["q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"]
+        names += ["v_mean"] if smooth_v else []
+        names += ["q_mean", "delta_s"] if smooth_q else []
+        res.append({n: getattr(bufs, n).cpu().numpy().view(np.uint8) for n in names})
+    for n in res[0]:
+        assert np.array_equal(res[0][n], res[1][n]), n
