@@ -1,8 +1,9 @@
 """Benchmark of the quantized-attention hot path on one MI355X.
 
 A step = one pass of the whole path over one batch of synthetic input already
-resident in HBM: sage_smooth_quant_qk (K mean, INT8 Q/K), sage_quant_v (FP8 V)
-and sage_attn_fwd (INT8 QK^T, online softmax, FP8 PV), all on one stream.
+resident in HBM: sage_quantize_qkv (K mean, INT8 Q/K, FP8 V; in pv fp16 mode
+sage_smooth_quant_qk alone; packed batches: the varlen calls) and sage_attn_fwd
+(INT8 QK^T, online softmax, FP8 PV), all on one stream.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1] [--pv fp8|fp16]
 
