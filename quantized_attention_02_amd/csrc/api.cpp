@@ -335,6 +335,10 @@ static int check_varlen(int B, int H, int H_kv, int total_q, int total_k, int ma
   if (rc) return rc;
   if ((rc = check_shape(B, H, max_k, D))) return rc;
   if ((rc = check_qk_quant(qk_quant))) return rc;
+  // the per-block passes launch one work-group per block of each head's buffer
+  if ((long long)H * (varlen_rows(total_q, B, kBlkQ) / kBlkQ) >= (1LL << 31) ||
+      (long long)H * (varlen_rows(total_k, B, kKvPad) / kBlkK) >= (1LL << 31))
+    return SAGE_ERR_INVALID_ARG;
   return check_kv_heads(H, H_kv);
 }
 

@@ -103,6 +103,39 @@ __device__ inline Seg v_seg(const QuantVArgs &a, int b, int h) {
                   : fixed_seg(a.layout, b, h, a.H, a.S, a.nk * kBlkK, D);
 }
 __device__ inline int ceil_div(int x, int m) { return (x + m - 1) / m; }
+
+// Work-group -> (batch entry or sequence b, head h, block blk) of a per-block
+// pass.  Fixed-length batches: wg = (b H + h) nblk + blk.  Packed batches: the
+// grid covers each head's whole buffer, wg = h (rows / brows) + kb in blocks of
+// brows rows; sequence b's run starts at row seq_row0(start_b, b, pad), which
+// strictly increases with b, so b is found by binary search over the table
+// (wave-uniform loads).  Callers compare blk with the sequence's block count: a
+// block in the gap after a run has none (and a malformed table only moves the
+// block to another clamped sequence).
+__device__ inline void block_of(bool varlen, const SeqTable &t, int B, int H, int nblk, long long rows, int pad,
+                                int brows, int wg, int &b, int &h, int &blk) {
+  if (!varlen) {
+    const int bh = wg / nblk;
+    b = bh / H;
+    h = bh % H;
+    blk = wg % nblk;
+    return;
+  }
+  const int nb = (int)(rows / brows);
+  h = wg / nb;
+  const long long r = (long long)(wg % nb) * brows;  // the block's first row in the head's buffer
+  int lo = 0, hi = B - 1, start, len;
+  while (lo < hi) {  // the last sequence whose run starts at or before row r
+    const int mid = (lo + hi + 1) >> 1;
+    seq_span(t, mid, start, len);
+    if (seq_row0(start, mid, pad) <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  b = lo;
+  seq_span(t, b, start, len);
+  const long long off = r - seq_row0(start, b, pad);
+  blk = off < 0 ? INT_MAX : (int)(off / brows);
+}
 // bytes of one quantised Q/K row: INT8 codes, or packed E2M1 pairs (MXFP4)
 template <int D>
 __device__ inline int code_row_bytes(const QuantQKArgs &a) { return a.qk == 2 ? D / 2 : D; }
@@ -404,8 +437,9 @@ template <int DT, int D, bool LANE>
 __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
   __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x;
-  const int bh = wg / a.nq, blk = wg % a.nq;
-  const Seg hv = q_seg<D>(a, bh / a.H, bh % a.H);
+  int b, h, blk;
+  block_of(a.varlen, a.sq, a.B, a.H, a.nq, a.rows_q, kBlkQ, kBlkQ, wg, b, h, blk);
+  const Seg hv = q_seg<D>(a, b, h);
   if (blk >= ceil_div(hv.S, kBlkQ)) return;  // past this sequence's blocks (packed batches)
   const uint16_t *q = (const uint16_t *)a.q;
   constexpr int vec_per_row = D / 8;
@@ -498,8 +532,10 @@ __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
   __shared__ float red[4][kThreads / 64];
   __shared__ float mean[D];
   const int tid = threadIdx.x;
-  const int bh = wg / a.nk, blk = wg % a.nk;  // bh: K head (b, h_kv)
-  const Seg hv = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
+  int b, h, blk;
+  block_of(a.varlen, a.sk, a.B, a.H_kv, a.nk, a.rows_k, kKvPad, kBlkK, wg, b, h, blk);
+  const int bh = b * a.H_kv + h;  // K head (b, h_kv)
+  const Seg hv = k_seg<D>(a, b, h);
   if (blk >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's rows
   const uint16_t *k = (const uint16_t *)a.k;
   if (tid < D) mean[tid] = a.k_mean[(long long)bh * D + tid];
@@ -615,10 +651,12 @@ __device__ inline void mxfp4_wg(const QuantQKArgs &a, int wg) {
   constexpr int U = (nvec + kThreads - 1) / kThreads;
   __shared__ float mean[D];
   const int tid = threadIdx.x;
-  const int nblk = IS_K ? a.nk : a.nq;
-  const int bh = wg / nblk, blk = wg % nblk;
   const int hn = IS_K ? a.H_kv : a.H;
-  const Seg hv = IS_K ? k_seg<D>(a, bh / hn, bh % hn) : q_seg<D>(a, bh / hn, bh % hn);
+  int b, h, blk;
+  if (IS_K) block_of(a.varlen, a.sk, a.B, hn, a.nk, a.rows_k, kKvPad, kBlkK, wg, b, h, blk);
+  else block_of(a.varlen, a.sq, a.B, hn, a.nq, a.rows_q, kBlkQ, kBlkQ, wg, b, h, blk);
+  const int bh = b * hn + h;
+  const Seg hv = IS_K ? k_seg<D>(a, b, h) : q_seg<D>(a, b, h);
   if (IS_K ? blk >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK) : blk >= ceil_div(hv.S, kBlkQ)) return;
   if (IS_K) {
     if (tid < D) mean[tid] = a.k_mean[(long long)bh * D + tid];
@@ -800,8 +838,10 @@ __global__ __launch_bounds__(kThreads) void k_vamax(const QuantVArgs a) { vamax_
 template <int DT, int D>
 __device__ inline void vconvert_wg(const QuantVArgs &a, int wg, int tid) {
   const int q = tid & 15, g = tid >> 4;
-  const int bh = wg / a.nk, t = wg % a.nk;
-  const Seg hv = v_seg<D>(a, bh / a.H, bh % a.H);
+  int b, h, t;
+  block_of(a.varlen, a.sk, a.B, a.H, a.nk, a.rows_k, kKvPad, kBlkK, wg, b, h, t);
+  const int bh = b * a.H + h;
+  const Seg hv = v_seg<D>(a, b, h);
   if (t >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's tiles
   const uint16_t *v = (const uint16_t *)a.v;
   float inv[8], mean[8];
@@ -851,17 +891,20 @@ __global__ __launch_bounds__(kThreads) void k_vscale(const QuantVArgs a) { vscal
 
 template <int DT, int D>
 static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
-  const int bh = a.B * a.H, bhk = a.B * a.H_kv;
+  const int bhk = a.B * a.H_kv;
   const int gd = (bhk * D + kThreads - 1) / kThreads;
+  // per-block passes: every block of every (entry, head), or of each head's packed buffer
+  const dim3 gq(a.varlen ? a.H * (int)(a.rows_q / kBlkQ) : a.B * a.H * a.nq);
+  const dim3 gk(a.varlen ? a.H_kv * (int)(a.rows_k / kBlkK) : bhk * a.nk);
   hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads), 0,
                      stream, a);
-  if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, false>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
-  else if (a.qk == 1) hipLaunchKernelGGL((k_qquant<DT, D, true>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((k_qquant<DT, D, false>), dim3(bh * a.nq), dim3(kThreads), 0, stream, a);
+  if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
+  else if (a.qk == 1) hipLaunchKernelGGL((k_qquant<DT, D, true>), gq, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_qquant<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
-  if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, true>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
-  else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, true>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((k_kquant<DT, D, false>), dim3(bhk * a.nk), dim3(kThreads), 0, stream, a);
+  if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, true>), gk, dim3(kThreads), 0, stream, a);
+  else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, true>), gk, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_kquant<DT, D, false>), gk, dim3(kThreads), 0, stream, a);
 }
 
 template <int DT, int D>
@@ -872,7 +915,8 @@ static void launch_v(const QuantVArgs &a, hipStream_t stream) {
   if (a.v_mean) hipLaunchKernelGGL((k_vstats_part<DT, D>), parts, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((k_vamax_part<DT, D>), parts, dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_vamax<D>), dim3(gd), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((k_vconvert<DT, D>), dim3(bh * a.nk), dim3(2 * D), 0, stream, a);
+  const dim3 gv(a.varlen ? a.H * (int)(a.rows_k / kBlkK) : bh * a.nk);  // 64-key tiles, as the K blocks
+  hipLaunchKernelGGL((k_vconvert<DT, D>), gv, dim3(2 * D), 0, stream, a);
   hipLaunchKernelGGL((k_vscale<D>), dim3(gd), dim3(kThreads), 0, stream, a);
 }
 
