@@ -269,6 +269,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv, args.qk_quant), 1), "unit": "TFLOP/s",
                      "frac": round(attn_tops / mfma_peak(args.pv, args.qk_quant), 4), "traffic": traffic,
                      "kernel": "k_attn (sage_attn_fwd)", "algorithmic_ops_per_launch": ops,
+                     "limiter": "VALU issue of the fp32 online softmax (per score: int->fp32 convert, FMA, exp2, "
+                                "add, half an FP8 pack; 64-multiply O rescale on most tiles), not the MFMAs",
                      "attn_src_sha256_16": khash},
     }
     if not args.no_cpu_baseline:
