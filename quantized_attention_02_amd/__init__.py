@@ -333,11 +333,23 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     return out
 
 
+# pv_accum_dtype names of the P V accumulation -> pv mode.  The FP8 P V product's
+# two accumulation levels are the MFMA's internal sum and the fp32 output
+# registers, so "fp32+fp16" and "fp32+fp32" select the same kernel; "fp32" is
+# the fp16 P V product with fp32 accumulation.
+PV_ACCUM = {"fp32+fp32": "fp8", "fp32+fp16": "fp8", "fp32": "fp16"}
+
+
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_quant="int8",
-             smooth_v=False, smooth_q=False):
-    """Quantized attention: same shape, dtype and layout out as q."""
+             smooth_v=False, smooth_q=False, pv_accum_dtype=None):
+    """Quantized attention: same shape, dtype and layout out as q.  pv_accum_dtype,
+    when given, selects pv_mode by its accumulation name (PV_ACCUM)."""
     import torch
 
+    if pv_accum_dtype is not None:
+        if pv_accum_dtype not in PV_ACCUM:
+            raise ValueError(f"pv_accum_dtype must be one of {sorted(PV_ACCUM)}")
+        pv_mode = PV_ACCUM[pv_accum_dtype]
     bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)

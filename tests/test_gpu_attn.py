@@ -190,3 +190,20 @@ def test_gqa_equals_replicated_kv_bitwise(layout, pv):
         ref = qa.sageattn(q, kr, vr, tensor_layout=layout, is_causal=causal, pv_mode=pv)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), causal
+
+
+def test_pv_accum_dtype_selects_the_pv_mode():
+    """The accumulation names select the FP8 (two-level fp32) or FP16 P V product."""
+    import torch
+
+    import quantized_attention_02_amd as qa
+
+    w = synth.custom(1, 2, 200, 64, seed=502)
+    q, k, v = (G.to_device(x, w.dtype) for x in G.inputs(w))
+    for name, pv in (("fp32+fp32", "fp8"), ("fp32+fp16", "fp8"), ("fp32", "fp16")):
+        got = qa.sageattn(q, k, v, pv_accum_dtype=name)
+        ref = qa.sageattn(q, k, v, pv_mode=pv)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), name
+    with pytest.raises(ValueError):
+        qa.sageattn(q, k, v, pv_accum_dtype="fp16")
