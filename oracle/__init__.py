@@ -419,8 +419,8 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
          smooth_v=False, qk_format="int8", smooth_q=False):
     """Full pipeline (smooth + quantise + attention) for the given heads/rows.
 
-    smooth_q (INT8 Q K^T): Q minus its 32-token block means is quantised, and the
-    attention adds the pre-processing term (block mean . (K - k_mean)) * sm_scale.
+    smooth_q: Q minus its 32-token block means is quantised (INT8 or MXFP4), and
+    the attention adds the pre-processing term (block mean . (K - k_mean)) * sm_scale.
 
     qk_format "fp4": Q and K - mean in MXFP4 (E2M1 with an E8M0 scale per 32
     channels of a token) instead of INT8 blocks; gran is then not used.
@@ -450,8 +450,12 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         vf = decode16(head(v, layout, b, hk), dtype)
         qk = None
         if qk_format == "fp4":
-            q4, qe = quant_mxfp4_rows(qf)
-            k4, ke, _ = quant_k_head_mxfp4(kf, smooth)
+            if smooth_q:  # Q minus its 32-token block means (one fp32 subtraction), then the MXFP4 rule
+                _, _, qm = quant_q_head_smooth(qf, BLK_Q)
+                q4, qe = quant_mxfp4_rows((qf - np.repeat(qm, BLK_Q, axis=0)[:qf.shape[0]]).astype(np.float32))
+            else:
+                q4, qe = quant_mxfp4_rows(qf)
+            k4, ke, km = quant_k_head_mxfp4(kf, smooth)
             qk = qk_mxfp4_rows(q4, qe, k4, ke, rows)
             q8, qs = np.zeros(qf.shape, np.int8), np.zeros(1, np.float32)
             k8, ks = np.zeros(kf.shape, np.int8), np.zeros(1, np.float32)

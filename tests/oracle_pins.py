@@ -882,4 +882,42 @@ def pin_smooth_q_more_accurate_with_q_offsets():
         assert rel_l1(sm[hd], ex[hd]) < 0.3 * rel_l1(pl[hd], ex[hd]), hd
 
 
+def pin_smooth_q_fp4_constant_blocks():
+    """MXFP4 with smoothed Q: tokens equal within each 32-token block leave a zero
+    smoothed Q (all E2M1 codes 0, so the FP4 scores are exactly 0) and the scores
+    are the pre-processing term alone -- the attention equals the one computed
+    from those scores, bit for bit."""
+    S, D = 96, 64
+    qf, kf, vf = _rand_head(S, D, seed=86)
+    qf = np.repeat(qf[::32], 32, axis=0)[:S].copy()
+    q = qf.astype(np.float16).view(np.uint16)[None, None]
+    k = kf.astype(np.float16).view(np.uint16)[None, None]
+    v = vf.astype(np.float16).view(np.uint16)[None, None]
+    _, _, qm = O.quant_q_head_smooth(qf, 32)
+    _, _, km = O.quant_k_head_mxfp4(kf, True)
+    delta = O.qk_delta_head(qm, (kf - km[None, :]).astype(np.float32))
+    v8, vs = O.quant_v_head(vf)
+    z8, z1 = np.zeros((S, D), np.int8), np.zeros(1, np.float32)
+    for causal in (False, True):
+        got = O.attn(q, k, v, F16, "HND", is_causal=causal, sm_scale=0.125, qk_format="fp4", smooth_q=True)[(0, 0)]
+        ref = O.attn_head_rows(z8, z1, z8, z1, v8, vs, vf, in_dtype=F16, is_causal=causal, sm_scale=0.125,
+                               pv_mode=O.PV_FP8, qk=delta[np.arange(S) // 32])
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), causal
+
+
+def pin_smooth_q_fp4_more_accurate_with_q_offsets():
+    """A per-channel Q offset takes E2M1's few levels away from the token's own
+    variation; with the block means subtracted the MXFP4 path is several times
+    closer to exact attention."""
+    w = synth.custom(1, 2, 256, 64, seed=87)
+    q, k, v = synth.make_qkv(w)
+    rng = np.random.default_rng(87)
+    q = O.encode16(O.decode16(q, F16) + rng.normal(0, 8, (1, 2, 1, 64)).astype(np.float32), F16)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    sm = O.attn(q, k, v, F16, "HND", smooth_q=True, qk_format="fp4", pv_mode=O.PV_FP16)
+    pl = O.attn(q, k, v, F16, "HND", qk_format="fp4", pv_mode=O.PV_FP16)
+    for hd in ex:
+        assert rel_l1(sm[hd], ex[hd]) < 0.25 * rel_l1(pl[hd], ex[hd]), (hd, rel_l1(sm[hd], ex[hd]), rel_l1(pl[hd], ex[hd]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
