@@ -54,7 +54,7 @@ def parse():
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
     p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
     p.add_argument("--smooth-q", action="store_true",
-                   help="Q smoothing (INT8 Q K^T, fixed-length batches): quantise Q minus its 32-token block means")
+                   help="Q smoothing (fixed-length batches): quantise Q minus its 32-token block means")
     p.add_argument("--qk-quant", default="int8", choices=["int8", "int8_lane", "mxfp4"],
                    help="Q/K quantisation: INT8 per block, INT8 per token / 16-key lane group, or MXFP4")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,8 +178,8 @@ def main():
 
     name = args.workload or synth.HEADLINE
     varlen = name in synth.VARLEN_WORKLOADS
-    if args.smooth_q and (varlen or args.qk_quant == "mxfp4"):
-        sys.exit("--smooth-q applies to the INT8 Q K^T of fixed-length batches")
+    if args.smooth_q and varlen:
+        sys.exit("--smooth-q applies to fixed-length batches")
     if args.smooth_v and args.pv != "fp8":
         sys.exit("--smooth-v applies to pv fp8")
     w = synth.VARLEN_WORKLOADS[name] if varlen else synth.WORKLOADS[name]

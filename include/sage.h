@@ -145,10 +145,10 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
  *   32-channel block of every Q token and of every token of K - k_mean.
  * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
  * same with H_kv heads.
- * q_mean non-NULL (INT8 modes only) selects smoothed Q ([SA2] SageAttention2方法): each
+ * q_mean non-NULL selects smoothed Q ([SA2] SageAttention2方法; any qk_quant): each
  * SAGE_BLK_Q-token block's channel means (binary64 sums over its valid tokens divided
  * by their number, rounded once) are written to q_mean, fp32 [B][H][nq][D], and
- * subtracted (one fp32 subtraction) before the INT8 rule; sage_qk_delta then forms the
+ * subtracted (one fp32 subtraction) before the INT8 or MXFP4 rule; sage_qk_delta then forms the
  * term the attention adds back.
  * Writes q_codes, q_scale, k_codes, k_scale, k_mean (layouts above; their element
  * types follow qk_quant).  The call is several kernel launches; while it runs,
@@ -215,7 +215,8 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  *   pv fp8 : P = E4M3(448 * p_n) (static scale), inner = P . V_fp8 (FP8 MFMA, fresh per tile),
  *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
  *            (+ v_mean[d] when v_mean is non-NULL: V was smoothed by sage_quant_v)
- *   smoothed Q (delta_s non-NULL, INT8 modes): s_n += delta_s[query block][n] * sm_scale
+ *   smoothed Q (delta_s non-NULL): s_n += delta_s[query block][n] * sm_scale (MXFP4: the
+ *         term is the starting value of the fp32 accumulator the FP4 MFMA adds to)
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
  * q_codes .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
  * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the

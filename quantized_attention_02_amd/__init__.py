@@ -259,12 +259,10 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
     torch tensors.
     k and v may have fewer heads than q (grouped-query attention); qk_quant "block"
     or "lane" (one scale per Q token and per 16-key lane group of K); smooth_v
-    (pv fp8): quantise V minus its channel mean; smooth_q (INT8 modes): quantise
-    Q minus its 32-token block means and form the pre-processing term."""
+    (pv fp8): quantise V minus its channel mean; smooth_q: quantise Q minus its
+    32-token block means and form the pre-processing term."""
     if smooth_v and pv_mode != "fp8":
         raise ValueError("smooth_v applies to pv_mode='fp8' only")
-    if smooth_q and qk_quant == "mxfp4":
-        raise ValueError("smooth_q applies to the INT8 Q K^T only")
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
     H_kv = _kv_heads(q, k, v, tensor_layout)

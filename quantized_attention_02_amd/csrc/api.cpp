@@ -107,7 +107,7 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;  // smoothing is for the FP8 V codes
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // smoothed Q: the INT8 product only, 4-byte aligned, and not with the debug dump
-  if (delta_s && (qk_quant == SAGE_QK_MXFP4 || !aligned(delta_s, 4) || dump)) return SAGE_ERR_INVALID_ARG;
+  if (delta_s && (!aligned(delta_s, 4) || dump)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
@@ -196,7 +196,7 @@ static int qk_args(QuantQKArgs &a, const void *q, const void *k, int dtype, int 
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_qk_quant(qk_quant))) return rc;
-  if (q_mean && (qk_quant == SAGE_QK_MXFP4 || !aligned(q_mean, 4))) return SAGE_ERR_INVALID_ARG;
+  if (q_mean && !aligned(q_mean, 4)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!q || !k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;

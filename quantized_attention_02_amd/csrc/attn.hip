@@ -370,7 +370,6 @@ template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, bool QS, int TN
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
   constexpr bool LANE = QK == 1, FP4 = QK == 2;
-  constexpr int kThreads = WAVES * 64;
   constexpr int kBlockM = WAVES * 32;
   constexpr int NC = D / 32;
   constexpr int KCH = D / 16;
@@ -556,10 +555,26 @@ k_attn(const AttnArgs a) {
       //      int -> float conversion can run while the second block's MFMAs do
       using acc_t = typename std::conditional<FP4, v16f, v16i>::type;
       acc_t s[NT];
+      if constexpr (FP4 && QS) {
+        // smoothed Q on the FP4 product: the scaled MFMA accumulates in fp32 on top of
+        // its C operand, so the pre-processing term of each key is the accumulator's
+        // starting value (keys 8 (r / 4) + 4 hh + r % 4 of the sub-tile)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[t][r] = 0;
+          for (int g = 0; g < 4; ++g) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(dsr + 32 * t + 8 * g + 4 * hh);
+            s[t][4 * g] = d4.x;
+            s[t][4 * g + 1] = d4.y;
+            s[t][4 * g + 2] = d4.z;
+            s[t][4 * g + 3] = d4.w;
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[t][r] = 0;
+      }
       auto qk_block = [&](int blk) {
         if constexpr (FP4) {
           // per key: its E8M0 word, shifted so that byte 2c is this half's block of chunk c
@@ -638,7 +653,7 @@ k_attn(const AttnArgs a) {
 #pragma unroll
           for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
             float4 dv[4];
-            if constexpr (QS)
+            if constexpr (QS && !FP4)
 #pragma unroll
               for (int g = 0; g < 4; ++g) dv[g] = *reinterpret_cast<const float4 *>(dsr + 32 * t + 8 * g + 4 * hh);
 #pragma unroll
@@ -882,9 +897,9 @@ static hipError_t launch5(const AttnArgs &a, bool dump, hipStream_t st) {
   AttnArgs b = a;
   b.nmblk = (a.S + 32 * C::WAVES - 1) / (32 * C::WAVES);
   const dim3 grid(a.B * a.H * b.nmblk), block(64 * C::WAVES);
-  // (the API rejects the dump for MXFP4 and for smoothed Q, and smoothed Q for MXFP4)
-  if (a.delta_s && QK != 2)
-    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, QK != 2, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
+  // (the API rejects the dump for MXFP4 and for smoothed Q)
+  if (a.delta_s)
+    hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, true, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
                        0, st, b);
   else if (dump)
     hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, QK != 2, QK, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,

@@ -665,6 +665,25 @@ __device__ inline void mxfp4_wg(const QuantQKArgs &a, int wg) {
   const uint16_t *x = (const uint16_t *)(IS_K ? a.k : a.q);
   uint8_t *codes = reinterpret_cast<uint8_t *>(IS_K ? a.k_i8 : a.q_i8);
   uint8_t *scales = reinterpret_cast<uint8_t *>(IS_K ? a.k_scale : a.q_scale);
+  // Q: both row vectors of the thread first (U <= 2), so that smoothed Q can
+  // subtract the block's channel means before the E2M1 rule
+  float xq[2][8];
+  if constexpr (!IS_K) {
+    static_assert(U <= 2, "a Q block is at most two vectors a thread");
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int vi = tid + u * kThreads;
+      const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
+      const int s = blk * ROWS + row;
+      if (vi < nvec && s < hv.S) {
+        load8<DT>(x + hv.base + (long long)s * hv.stride + c8, xq[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xq[u][i] = 0.0f;
+      }
+    }
+    if (a.q_mean) q_block_smooth<D>(a, xq, hv.S - blk * kBlkQ, (hv.row0 >> 5) + blk);
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = tid + u * kThreads;  // uniform over the wavefront: nvec is a multiple of 64
@@ -672,11 +691,13 @@ __device__ inline void mxfp4_wg(const QuantQKArgs &a, int wg) {
     const int row = vi / vec_per_row, c8 = (vi % vec_per_row) * 8;
     const int s = blk * ROWS + row;
     float v[8];
-    if (s < hv.S) {
-      load8<DT>(x + hv.base + (long long)s * hv.stride + c8, v);
-      if (IS_K)
+    if constexpr (!IS_K) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] - mean[c8 + i];
+      for (int i = 0; i < 8; ++i) v[i] = xq[u][i];
+    } else if (s < hv.S) {
+      load8<DT>(x + hv.base + (long long)s * hv.stride + c8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] - mean[c8 + i];
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;

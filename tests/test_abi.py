@@ -90,7 +90,7 @@ GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=No
 BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict(q_scale=P + 2), dict(dtype=2),
           dict(layout=-1), dict(B=0), dict(H=-1), dict(S=0), dict(D=32), dict(D=256), dict(S=(1 << 20) + 1),
           dict(B=1 << 9, H=1 << 8, H_kv=1 << 8), dict(H_kv=0), dict(H_kv=3), dict(H=3, H_kv=2), dict(H_kv=-2),
-          dict(qk_quant=3), dict(qk_quant=-1), dict(q_mean=P + 2), dict(q_mean=P, qk_quant=2)]
+          dict(qk_quant=3), dict(qk_quant=-1), dict(q_mean=P + 2)]
 BAD_DELTA = [dict(k=None), dict(q_mean=None), dict(k_mean=None), dict(delta_s=None), dict(q_mean=P + 4),
              dict(delta_s=P + 2), dict(delta_s=P + 4), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2),
              dict(dtype=4), dict(S=0)]
@@ -101,7 +101,7 @@ BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dic
             dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
             dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=3),
             dict(v_mean=P + 1), dict(pv_mode=1, v_scale=None, v_mean=P),  # smoothing is for the FP8 V codes
-            dict(delta_s=P + 2), dict(delta_s=P, qk_quant=2),  # smoothed Q: INT8 modes only
+            dict(delta_s=P + 2),
             # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
             dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
 
@@ -207,6 +207,8 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_qkv() == qa.SAGE_ERR_NO_DEVICE
     assert _call_qkv(q_mean=P, v_mean=P, qk_quant=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_qkv(qk_quant=2, H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qk(q_mean=P, qk_quant=2) == qa.SAGE_ERR_NO_DEVICE  # smoothed Q with MXFP4
+    assert _call_attn(delta_s=P, qk_quant=2) == qa.SAGE_ERR_NO_DEVICE
 
 
 def test_python_wrapper_maps_unsupported_to_value_error(monkeypatch):

@@ -100,6 +100,7 @@ FUSED_CASES = [
     (synth.custom(1, 8, 1000, 128, Hkv=4, token_norm=True, q_bias_sigma=3.0, seed=1405), "int8", True, True),
     (synth.custom(1, 2, 1, 64, seed=1406), "int8_lane", True, True),
     (synth.WORKLOADS["snippet_b2h32s4096d128"], "int8", False, False),
+    (synth.custom(2, 4, 130, 128, layout="NHD", Hkv=2, q_bias_sigma=3.0, seed=1407), "mxfp4", True, True),
 ]
 
 

@@ -1,6 +1,6 @@
 """GPU smoothed Q vs the oracle: Q minus its 32-token block means is quantised
-to INT8, a pre-processing pass forms delta = block mean . (K - k_mean), and the
-attention adds delta * sm_scale to the scores.
+(INT8 per block or per token, or MXFP4), a pre-processing pass forms delta =
+block mean . (K - k_mean), and the attention adds delta * sm_scale to the scores.
 
 Block means, codes and scales are bit-identical to the oracle's.  delta is
 checked against the oracle's binary64 value with the error bound of its
@@ -33,7 +33,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("qk", ["int8", "int8_lane"])
+def unpack(packed: np.ndarray) -> np.ndarray:
+    """[..., D/2] bytes -> [..., D] E2M1 codes (channel 2j in the low nibble of byte j)."""
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = packed & 15
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+@pytest.mark.parametrize("qk", ["int8", "int8_lane", "mxfp4"])
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_smooth_q_quant_and_delta(w, qk):
     q, k, _ = G.inputs(w)
@@ -47,13 +55,20 @@ def test_smooth_q_quant_and_delta(w, qk):
     S, nq = w.S, (w.S + 31) // 32
     for b in range(w.B):
         for h in range(w.H):
-            r8, rs, rm = O.quant_q_head_smooth(O.decode16(O.head(q, w.layout, b, h), dt), 32,
-                                               1 if qk == "int8_lane" else 32)
+            qf = O.decode16(O.head(q, w.layout, b, h), dt)
+            r8, rs, rm = O.quant_q_head_smooth(qf, 32, 1 if qk == "int8_lane" else 32)
             assert np.array_equal(qm[b, h, :nq].view(np.uint32), rm.view(np.uint32)), (b, h)
-            assert np.array_equal(q8[b, h, :S], r8), (b, h, int((q8[b, h, :S] != r8).sum()))
-            assert np.array_equal(qs[b, h, :rs.size].view(np.uint32), rs.view(np.uint32)), (b, h)
+            if qk == "mxfp4":  # the MXFP4 rule on Q minus the block means
+                r4, re = O.quant_mxfp4_rows((qf - np.repeat(rm, 32, axis=0)[:S]).astype(np.float32))
+                assert np.array_equal(unpack(q8[b, h, :S]), r4), (b, h)
+                assert np.array_equal(qs[b, h, :S], re), (b, h)
+            else:
+                assert np.array_equal(q8[b, h, :S], r8), (b, h, int((q8[b, h, :S] != r8).sum()))
+                assert np.array_equal(qs[b, h, :rs.size].view(np.uint32), rs.view(np.uint32)), (b, h)
             kf = O.decode16(O.head(k, w.layout, b, O.kv_head(h, w.H, w.kv_heads)), dt)
             km = O.channel_mean(kf)
+            assert np.array_equal(bufs.k_mean.cpu().numpy()[b, O.kv_head(h, w.H, w.kv_heads)].view(np.uint32),
+                                  km.view(np.uint32))
             rd = O.qk_delta_head(rm, (kf - km[None, :]).astype(np.float32))
             bound = 2.0 ** -14 * (np.abs(rm).astype(np.float64) @ (np.abs(kf) + np.abs(km)[None, :]).T)
             err = np.abs(ds[b, h, :nq, :S].astype(np.float64) - rd)
@@ -61,16 +76,18 @@ def test_smooth_q_quant_and_delta(w, qk):
             assert not ds[b, h, :nq, S:].any()
 
 
-@pytest.mark.parametrize("w,causal,pv,qk", [(w, c, pv, qk) for w in CASES for c, pv, qk in
-                                            ((False, "fp8", "int8"), (True, "fp16", "int8_lane"))],
-                         ids=[f"{w.name}-{c}-{pv}-{qk}" for w in CASES for c, pv, qk in
-                              ((False, "fp8", "int8"), (True, "fp16", "int8_lane"))])
+MODES = ((False, "fp8", "int8"), (True, "fp16", "int8_lane"), (False, "fp8", "mxfp4"), (True, "fp16", "mxfp4"))
+
+
+@pytest.mark.parametrize("w,causal,pv,qk", [(w, c, pv, qk) for w in CASES for c, pv, qk in MODES],
+                         ids=[f"{w.name}-{c}-{pv}-{qk}" for w in CASES for c, pv, qk in MODES])
 def test_smooth_q_attn_matches_oracle(w, causal, pv, qk):
     _, out, _ = G.run(w, causal=causal, pv=pv, qk_quant=qk, smooth_q=True)
     got = G.out_logical(out, w)
     q, k, v = G.inputs(w)
     ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal, pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16,
-                 tile_k=G.TILE_K[pv], smooth_q=True, gran="lane" if qk == "int8_lane" else "block")
+                 tile_k=G.TILE_K[pv], smooth_q=True, gran="lane" if qk == "int8_lane" else "block",
+                 qk_format="fp4" if qk == "mxfp4" else "int8")
     ref = np.stack([np.stack([ref[(b, h)] for h in range(w.H)]) for b in range(w.B)])
     assert np.isfinite(got).all()
     c, r = G.cos(got, ref), G.rel_l1(got, ref)
@@ -89,6 +106,21 @@ def test_smooth_q_closer_to_exact_with_q_offsets():
         errs[sq] = G.rel_l1(G.out_logical(out, w), ex)
     print("rel L1 vs exact (smooth_q False/True):", errs)
     assert errs[True] < 0.5 * errs[False], errs
+
+
+def test_smooth_q_fp4_closer_to_exact_with_q_offsets():
+    """With MXFP4 the per-channel Q offsets cost far more than with INT8; the
+    smoothed MXFP4 output is several times closer to exact attention."""
+    w = synth.custom(1, 4, 1024, 128, q_bias_sigma=8.0, seed=1212)
+    q, k, v = G.inputs(w)
+    ex = O.attn_exact(q, k, v, O.DTYPES[w.dtype], w.layout)
+    ex = np.stack([ex[(0, h)] for h in range(w.H)])[None]
+    errs = {}
+    for sq in (False, True):
+        _, out, _ = G.run(w, pv="fp16", qk_quant="mxfp4", smooth_q=sq)
+        errs[sq] = G.rel_l1(G.out_logical(out, w), ex)
+    print("MXFP4 rel L1 vs exact (smooth_q False/True):", errs)
+    assert errs[True] < 0.25 * errs[False], errs
 
 
 def test_smooth_q_full_size_sampled():
