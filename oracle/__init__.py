@@ -428,15 +428,18 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
     smooth_v (pv fp8 only): V minus its channel mean is quantised, and the mean
     is added back to the output.
 
-    gran: "block" (blk_q / blk_k tokens per scale) or "lane" (thread-level: one
-    scale per Q token, one per 16-key lane group of K).
+    gran: "block" (blk_q / blk_k tokens per scale), "lane" (thread-level: one
+    scale per Q token, one per 16-key lane group of K) or "token" (one scale per
+    Q token and per K token: the block rule with blocks of one token).
     Returns {(b, h): fp32 [len(rows), D]}; rows default to all S rows.
     """
-    if gran not in ("block", "lane"):
+    if gran not in ("block", "lane", "token"):
         raise ValueError(gran)
     lane = gran == "lane"
     if lane:
         blk_q = 1
+    if gran == "token":
+        blk_q = blk_k = 1
     B, H, S, D = logical_shape(q.shape, layout)
     Hkv = logical_shape(k.shape, layout)[1]
     if sm_scale is None:

@@ -655,6 +655,60 @@ def pin_lane_attention_uses_group_scales():
         assert cos(got, ref) >= 0.99999 and rel_l1(got, ref) < 2e-3, (causal, cos(got, ref), rel_l1(got, ref))
 
 
+def pin_token_codes_are_per_row():
+    """Per-token granularity: a row's codes and scale depend on that row alone.
+    Scaling row j of Q (or of unsmoothed K) by 4 leaves every code unchanged,
+    multiplies row j's scale by 4 and leaves every other scale unchanged."""
+    S, D = 70, 64
+    qf, kf, _ = _rand_head(S, D, seed=45)
+    for x, quant in ((qf, lambda a: O.quant_q_head(a, 1)), (kf, lambda a: O.quant_k_head(a, 1, False)[:2])):
+        c0, s0 = quant(x)
+        assert s0.shape == (S,)
+        for j in (0, 33, S - 1):
+            x2 = x.copy()
+            x2[j] *= 4.0
+            c1, s1 = quant(x2)
+            assert np.array_equal(c0, c1), j
+            assert s1[j] == 4 * s0[j] and np.array_equal(np.delete(s1, j), np.delete(s0, j)), j
+
+
+def pin_token_more_accurate_than_block():
+    """Scales that follow every token track tokens of very different norms more
+    closely than one scale per block: smaller error against exact attention."""
+    w = synth.custom(1, 2, 512, 128, token_norm=True, outlier_p=0.01, bias_sigma=3.0, seed=46)
+    q, k, v = synth.make_qkv(w)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    tok = O.attn(q, k, v, F16, "HND", gran="token")
+    blk = O.attn(q, k, v, F16, "HND", gran="block")
+    for hd in ex:
+        assert rel_l1(tok[hd], ex[hd]) < rel_l1(blk[hd], ex[hd]), hd
+
+
+def pin_token_attention_uses_key_scales():
+    """Attention on per-token codes dequantises key n with its own scale: against
+    softmax(dq_i * dk_n * sm * (q8 . k8)) @ V worked out here in binary64 from the
+    same codes (pv fp16 rounds only P and V to fp16)."""
+    from scipy.special import softmax
+
+    S, D = 150, 64
+    qf, kf, vf = _rand_head(S, D, seed=47)
+    kf = kf.copy()
+    kf[37] *= 30.0
+    kf[101] *= 0.01
+    q8, qs = O.quant_q_head(qf, 1)
+    k8, ks, _ = O.quant_k_head(kf, 1, True)
+    sm = 0.125
+    s = (q8.astype(np.float64) @ k8.astype(np.float64).T) * qs[:, None].astype(np.float64) \
+        * ks[None, :].astype(np.float64) * sm
+    for causal in (False, True):
+        if causal:
+            s = np.where(np.tril(np.ones((S, S), bool)), s, -np.inf)
+        ref = softmax(s, axis=1) @ vf.astype(np.float64)
+        got = O.attn_head_rows(q8, qs, k8, ks, None, None, vf, in_dtype=F16, is_causal=causal, sm_scale=sm,
+                               pv_mode=O.PV_FP16, blk_q=1, blk_k=1)
+        assert cos(got, ref) >= 0.99999 and rel_l1(got, ref) < 2e-3, (causal, cos(got, ref), rel_l1(got, ref))
+
+
 # ------------------------------------------------------------------ V smoothing
 def pin_smooth_v_quant():
     """Smoothed V: the mean is the channel mean, and the codes and scales are the
