@@ -47,11 +47,13 @@
  *   nq = S_q / SAGE_BLK_Q, nk = S_k / SAGE_BLK_K.
  *   q_codes int8  [B][H][S_q][D]   INT8 codes of Q; rows >= S are 0.
  *   q_scale float [B][H][nq]       one scale per block of SAGE_BLK_Q tokens
- *                                  (SAGE_QK_INT8_LANE: [B][H][S_q], one per token).
+ *                                  (SAGE_QK_INT8_LANE, SAGE_QK_INT8_TOKEN: [B][H][S_q],
+ *                                  one per token).
  *   k_codes int8  [B][H_kv][S_k][D] INT8 codes of K - k_mean; rows >= S are 0.
  *   k_scale float [B][H_kv][nk]    one scale per block of SAGE_BLK_K tokens (0 for blocks
  *                                  made only of padding keys; SAGE_QK_INT8_LANE:
- *                                  [B][H_kv][S_k / 16], one per lane group).
+ *                                  [B][H_kv][S_k / 16], one per lane group;
+ *                                  SAGE_QK_INT8_TOKEN: [B][H_kv][S_k], one per token).
  *   k_mean  float [B][H_kv][D]     per-channel mean of K over the S tokens.
  *   v_fp8   uint8 [B][H_kv][nk][D][64] E4M3 codes of V, one 64-key tile after the
  *           other, each tile stored channel-major; inside a tile, byte p of
@@ -108,6 +110,8 @@ extern "C" {
                                 token sharing an E8M0 scale 2^e, e = floor(log2 amax) - 2,
                                 clamped to [-127, 127] (-127 for an all-zero block); codes
                                 E2M1(x / 2^e), round to nearest even, saturating at 6 */
+#define SAGE_QK_INT8_TOKEN 3 /* INT8, one scale per query token and per key token ([REPO]
+                                feature list: granularity per token, per head or per thread) */
 
 /* ---- limits and granularity ---- */
 #define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
@@ -141,7 +145,8 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
  *     amax = max |x|;  scale = amax / 127;  code = rint(x * (127 / amax)) in [-127, 127];
  *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
  *   qk_quant = SAGE_QK_INT8_LANE: the same rule with each Q token, and each 16-key lane
- *   group of K - k_mean, as its own block; SAGE_QK_MXFP4: the MXFP4 rule above on each
+ *   group of K - k_mean, as its own block; SAGE_QK_INT8_TOKEN: with each Q token and
+ *   each token of K - k_mean as its own block; SAGE_QK_MXFP4: the MXFP4 rule above on each
  *   32-channel block of every Q token and of every token of K - k_mean.
  * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
  * same with H_kv heads.
@@ -206,7 +211,8 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  * For each query row i, key tiles (SAGE_TILE_K_FP8 / SAGE_TILE_K_FP16 keys) in order,
  * fp32 online softmax:
  *   s_n = float(q_codes[i] . k_codes[n]) * (q_scale * k_scale) * sm_scale   (INT8 MFMA,
- *         int32 sums; the scales of query i's block and key n's block, or lane group);
+ *         int32 sums; the scales of query i's block and key n's block, lane group or
+ *         token);
  *         SAGE_QK_MXFP4: s_n = (sum_d Q~[i][d] K~[n][d]) * sm_scale over the dequantised
  *         E2M1 * 2^e values (scaled FP4 MFMA, fp32 sums).  qk_quant must be the mode
  *         the codes were made with.
@@ -272,8 +278,9 @@ int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *
  * rows of sequence b start at
  *   rq(b) = 32 * (cu_seqlens_q[b] / 32 + b),  rk(b) = 128 * (cu_seqlens_k[b] / 128 + b)
  * of RQ = 32 * (total_q / 32 + B + 1) and RK = 128 * (total_k / 128 + B + 1) rows:
- *   q_codes int8  [H][RQ][D]          q_scale float [H][RQ / 32]    (lane: [H][RQ])
- *   k_codes int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64] (lane: [H_kv][RK / 16])
+ *   q_codes int8  [H][RQ][D]          q_scale float [H][RQ / 32]    (lane, token: [H][RQ])
+ *   k_codes int8  [H_kv][RK][D]       k_scale float [H_kv][RK / 64] (lane: [H_kv][RK / 16];
+ *                                                                    token: [H_kv][RK])
  *   (MXFP4: codes D / 2 and scales D / 32 bytes a row, as in the fixed layout)
  *   k_mean  float [B][H_kv][D]        v_scale float [B][H_kv][D]
  *   v_fp8   uint8 [H_kv][RK / 64][D][64]  (64-key tiles as in the fixed layout)

@@ -26,7 +26,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ER
 LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
 PV = {"fp8": 0, "fp16": 1}
-QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2}  # Q/K quantisation (include/sage.h SAGE_QK_*)
+QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2, "int8_token": 3}  # Q/K quantisation (include/sage.h SAGE_QK_*)
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
@@ -219,7 +219,7 @@ class Quantized:
         H_kv = H if H_kv is None else H_kv
         self.B, self.H, self.H_kv, self.S, self.D, self.qk = B, H, H_kv, S, D, QK[qk_quant]
         sq, sk = (S + BLK_Q - 1) // BLK_Q * BLK_Q, (S + KV_PAD - 1) // KV_PAD * KV_PAD
-        lane = self.qk == QK["int8_lane"]
+        lane, token = self.qk == QK["int8_lane"], self.qk == QK["int8_token"]
         if self.qk == QK["mxfp4"]:  # packed E2M1 pairs and E8M0 bytes per 32 channels of a row
             self.q_i8 = torch.empty((B, H, sq, D // 2), dtype=torch.uint8, device=device)
             self.q_scale = torch.empty((B, H, sq, D // 32), dtype=torch.uint8, device=device)
@@ -227,10 +227,11 @@ class Quantized:
             self.k_scale = torch.empty((B, H_kv, sk, D // 32), dtype=torch.uint8, device=device)
         else:
             self.q_i8 = torch.empty((B, H, sq, D), dtype=torch.int8, device=device)
-            self.q_scale = torch.empty((B, H, sq if lane else sq // BLK_Q), dtype=torch.float32, device=device)
-            self.k_i8 = torch.empty((B, H_kv, sk, D), dtype=torch.int8, device=device)
-            self.k_scale = torch.empty((B, H_kv, sk // 16 if lane else sk // BLK_K), dtype=torch.float32,
+            self.q_scale = torch.empty((B, H, sq if lane or token else sq // BLK_Q), dtype=torch.float32,
                                        device=device)
+            self.k_i8 = torch.empty((B, H_kv, sk, D), dtype=torch.int8, device=device)
+            self.k_scale = torch.empty((B, H_kv, sk if token else sk // 16 if lane else sk // BLK_K),
+                                       dtype=torch.float32, device=device)
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((B, H_kv, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
@@ -257,8 +258,9 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
     """Run sage_quantize_qkv in pv fp8 mode (fused=False: sage_smooth_quant_qk and
     sage_quant_v, same results), or sage_smooth_quant_qk alone in pv fp16 mode, on
     torch tensors.
-    k and v may have fewer heads than q (grouped-query attention); qk_quant "block"
-    or "lane" (one scale per Q token and per 16-key lane group of K); smooth_v
+    k and v may have fewer heads than q (grouped-query attention); qk_quant "int8"
+    (per block), "int8_lane" (one scale per Q token and per 16-key lane group of
+    K), "int8_token" (one per Q token and per K token) or "mxfp4"; smooth_v
     (pv fp8): quantise V minus its channel mean; smooth_q: quantise Q minus its
     32-token block means and form the pre-processing term."""
     if smooth_v and pv_mode != "fp8":
@@ -372,7 +374,7 @@ class QuantizedVarlen:
 
         self.B, self.H, self.H_kv, self.total_q, self.total_k, self.D = B, H, H_kv, total_q, total_k, D
         self.qk = QK[qk_quant]
-        lane = self.qk == QK["int8_lane"]
+        lane, token = self.qk == QK["int8_lane"], self.qk == QK["int8_token"]
         rq, rk = varlen_rows(total_q, B, BLK_Q), varlen_rows(total_k, B, KV_PAD)
         self.rows_q, self.rows_k = rq, rk
         if self.qk == QK["mxfp4"]:
@@ -382,10 +384,11 @@ class QuantizedVarlen:
             self.k_scale = torch.empty((H_kv, rk, D // 32), dtype=torch.uint8, device=device)
         else:
             self.q_i8 = torch.empty((H, rq, D), dtype=torch.int8, device=device)
-            self.q_scale = torch.empty((H, rq if lane else rq // BLK_Q), dtype=torch.float32, device=device)
-            self.k_i8 = torch.empty((H_kv, rk, D), dtype=torch.int8, device=device)
-            self.k_scale = torch.empty((H_kv, rk // 16 if lane else rk // BLK_K), dtype=torch.float32,
+            self.q_scale = torch.empty((H, rq if lane or token else rq // BLK_Q), dtype=torch.float32,
                                        device=device)
+            self.k_i8 = torch.empty((H_kv, rk, D), dtype=torch.int8, device=device)
+            self.k_scale = torch.empty((H_kv, rk if token else rk // 16 if lane else rk // BLK_K),
+                                       dtype=torch.float32, device=device)
         self.k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_fp8 = torch.empty((H_kv, rk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)

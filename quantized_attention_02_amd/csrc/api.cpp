@@ -42,20 +42,22 @@ int check_kv_heads(int H, int H_kv) {
 }
 
 int check_qk_quant(int qk_quant) {
-  return (qk_quant == SAGE_QK_INT8_BLOCK || qk_quant == SAGE_QK_INT8_LANE || qk_quant == SAGE_QK_MXFP4)
+  return (qk_quant == SAGE_QK_INT8_BLOCK || qk_quant == SAGE_QK_INT8_LANE || qk_quant == SAGE_QK_MXFP4 ||
+          qk_quant == SAGE_QK_INT8_TOKEN)
              ? SAGE_OK
              : SAGE_ERR_INVALID_ARG;
 }
 
-// scale entries per head: Q per block of kBlkQ rows or per row; K per kBlkK-row block or 16-row group
+// scale entries per head: Q per block of kBlkQ rows or per row; K per kBlkK-row block, 16-row group or row
 // bytes per head of the Q / K codes and scales for `rows` buffer rows of D channels
 size_t code_bytes(size_t rows, int D, int qk) { return qk == SAGE_QK_MXFP4 ? rows * D / 2 : rows * D; }
 size_t q_scale_bytes(size_t rows, int D, int qk) {
   if (qk == SAGE_QK_MXFP4) return rows * (D / 32);  // E8M0 bytes
-  return (qk == SAGE_QK_INT8_LANE ? rows : rows / kBlkQ) * sizeof(float);
+  return (qk == SAGE_QK_INT8_LANE || qk == SAGE_QK_INT8_TOKEN ? rows : rows / kBlkQ) * sizeof(float);
 }
 size_t k_scale_bytes(size_t rows, int D, int qk) {
   if (qk == SAGE_QK_MXFP4) return rows * (D / 32);
+  if (qk == SAGE_QK_INT8_TOKEN) return rows * sizeof(float);
   return (qk == SAGE_QK_INT8_LANE ? rows / 16 : rows / kBlkK) * sizeof(float);
 }
 

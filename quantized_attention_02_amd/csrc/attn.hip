@@ -363,13 +363,17 @@ __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lan
 // 16-key lane group (the keys this half-wave holds of each 32-key sub-tile), so
 // every lane dequantises each sub-tile with one scale of its own.  2 (FP4):
 // MXFP4 -- E2M1 codes with an E8M0 scale per 32 channels of a token, on the
-// scaled FP4 MFMA, which applies the scales itself (fp32 scores).  QS:
+// scaled FP4 MFMA, which applies the scales itself (fp32 scores).  3 (TOKEN):
+// INT8 with one Q scale per token and one K scale per key; the tile's key
+// scales are staged in LDS with the tile, and each score is dequantised by its
+// key's scale in fp32 before the row max (the query's scale and sm_scale are
+// one factor per lane, applied in the exponent).  QS:
 // smoothed Q -- the scores gain the pre-processing term delta[query block][key]
 // (a wavefront's 32 queries share one block), staged in LDS with each tile.
 template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, bool QS, int TN, int WPS, int WAVES, int NBUF>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
-  constexpr bool LANE = QK == 1, FP4 = QK == 2;
+  constexpr bool LANE = QK == 1, FP4 = QK == 2, TOKEN = QK == 3;
   constexpr int kBlockM = WAVES * 32;
   constexpr int NC = D / 32;
   constexpr int KCH = D / 16;
@@ -384,6 +388,9 @@ k_attn(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float vmn[D];  // its channel means when V was smoothed
   // smoothed Q: each wavefront's row of the pre-processing term for the tile's keys
   __shared__ __attribute__((aligned(16))) float dsbuf[QS ? NBUF : 1][QS ? WAVES : 1][QS ? TN : 4];
+  // per-token K scales: the tile's key scales (copied by the first TN / 64 wavefronts)
+  __shared__ __attribute__((aligned(16))) float ksbuf[TOKEN ? NBUF : 1][TOKEN ? TN : 4];
+  static_assert(!TOKEN || (TN / 64 <= WAVES && NBUF == 2), "key-scale copy split and whole-tile vm waits");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
@@ -468,7 +475,7 @@ k_attn(const AttnArgs a) {
       const int8_t *qrow = a.q_i8 + (qs.row0 + qi) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
-      dq = LANE ? a.q_scale[qs.row0 + qi] : a.q_scale[(qs.row0 + qw) >> 5];
+      dq = LANE || TOKEN ? a.q_scale[qs.row0 + qi] : a.q_scale[(qs.row0 + qw) >> 5];
     }
   }
 
@@ -485,7 +492,7 @@ k_attn(const AttnArgs a) {
 
   const int8_t *kbase = a.k_i8 + ks.row0 * (FP4 ? D / 2 : D);
   const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + ks.row0 * D;
-  const float *kscale = a.k_scale + (LANE ? ks.row0 >> 4 : ks.row0 >> 6);  // INT8 modes
+  const float *kscale = a.k_scale + (TOKEN ? ks.row0 : LANE ? ks.row0 >> 4 : ks.row0 >> 6);  // INT8 modes
   const uint8_t *kscb = reinterpret_cast<const uint8_t *>(a.k_scale) + ks.row0 * (D / 32);  // FP4
   const HeadView hv{ks.base, ks.stride};  // pv fp16: the caller's V
   const TileCopy<D, TN, WAVES> copy(wave, lane);     // INT8 K
@@ -494,7 +501,8 @@ k_attn(const AttnArgs a) {
   const int vbytes = ntiles * TN * D;                // this head's V (and INT8 K) bytes that the tiles read
   const int kbytes = FP4 ? vbytes / 2 : vbytes;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kbytes);
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(kscb, ntiles * TN * (D / 32));  // FP4 K scales
+  const __amdgpu_buffer_rsrc_t srs = TOKEN ? make_rsrc(kscale, ntiles * TN * 4)  // per-key K scales
+                                           : make_rsrc(kscb, ntiles * TN * (D / 32));  // FP4 K scales
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase,
                                                PV == 0 ? vbytes : kbytes);  // (pv fp16 copies V itself)
   // smoothed Q: delta is stored [bh][128-key tile][query block][128]; this
@@ -513,6 +521,15 @@ k_attn(const AttnArgs a) {
     } else {
       copy.template issue<PV == 0>(krs, vrs, j * TN * D, kb, vb, wave);
       n = copy.k_loads(wave);
+    }
+    if constexpr (TOKEN) {
+      // every wavefront needs every key's scale: the first TN / 64 copy them,
+      // whether or not they have queries of their own
+      if (wave < TN / 64) {
+        dma4_buf(srs, (uint32_t)(4 * lane), 4 * (j * TN + 64 * wave),
+                 reinterpret_cast<uint8_t *>(&ksbuf[buf][0]) + 256 * wave);
+        n += 1;
+      }
     }
     if constexpr (QS) {
       if (active) {
@@ -533,12 +550,15 @@ k_attn(const AttnArgs a) {
   // pend (pv fp16): copy instructions this wavefront issued after the tile's V.
   auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb, int pend) {
     const float *dsr = &dsbuf[QS ? buf : 0][QS ? wave : 0][0];  // smoothed Q: this wavefront's delta row
+    const float *ksr = &ksbuf[TOKEN ? buf : 0][0];               // per-token K: the tile's key scales
     const int key0 = j * TN;
     const bool work = active && !(CAUSAL && key0 > qw + 31);
     // the tile's K scales, read through a wave-uniform address (scalar loads)
     constexpr int NKS = LANE ? 2 * NT : NB;  // per lane group, or per 64-key block
     float ks[NKS];
-    if constexpr (LANE) {
+    if constexpr (TOKEN) {
+      // (per-key scales: read from ksr with the scores)
+    } else if constexpr (LANE) {
       loadn_uniform<NKS>(kscale + NKS * j, ks);
     } else if (NB == 2) {
       const float2 ksv = load2_uniform(kscale + 2 * j);
@@ -624,7 +644,7 @@ k_attn(const AttnArgs a) {
       if constexpr (QS) {
 #pragma unroll
         for (int i = 0; i < NC2; ++i) {
-          cdq[i] = LANE ? dq * (hh ? ks[2 * i + 1] : ks[2 * i]) : dq * ks[i];
+          cdq[i] = TOKEN ? dq : LANE ? dq * (hh ? ks[2 * i + 1] : ks[2 * i]) : dq * ks[i];
           c2[i] = a.sm2;
         }
       } else if constexpr (LANE) {
@@ -633,6 +653,9 @@ k_attn(const AttnArgs a) {
       } else if constexpr (FP4) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) c2[blk] = a.sm2;  // the MFMA applied the micro-scales
+      } else if constexpr (TOKEN) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) c2[blk] = dq * a.sm2;  // the key scales are in the scores
       } else {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
@@ -648,20 +671,33 @@ k_attn(const AttnArgs a) {
       float mxf[NB];  // FP4: fp32 max per block
       float f[16 * NT];
       auto max_convert = [&](int blk, int mlim, auto mask_tag) {
-        if constexpr (FP4 || QS) {  // fp32 scores: dequantised (+ delta), max in fp32
+        if constexpr (FP4 || QS || TOKEN) {  // fp32 scores: dequantised (+ delta), max in fp32
           float mx = -INFINITY;
 #pragma unroll
           for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
-            float4 dv[4];
+            float4 dv[4], kv[4];
             if constexpr (QS && !FP4)
 #pragma unroll
               for (int g = 0; g < 4; ++g) dv[g] = *reinterpret_cast<const float4 *>(dsr + 32 * t + 8 * g + 4 * hh);
+            if constexpr (TOKEN)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) kv[g] = *reinterpret_cast<const float4 *>(ksr + 32 * t + 8 * g + 4 * hh);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = decltype(mask_tag)::value && 32 * t + 8 * (r >> 2) + (r & 3) > mlim;
               float val;
               if constexpr (FP4) {
                 val = s[t][r];
+              } else if constexpr (TOKEN) {
+                const float4 k4 = kv[r >> 2];
+                const float kr = (r & 3) == 0 ? k4.x : (r & 3) == 1 ? k4.y : (r & 3) == 2 ? k4.z : k4.w;
+                if constexpr (QS) {
+                  const float4 d4 = dv[r >> 2];
+                  const float dr = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
+                  val = __builtin_fmaf((float)s[t][r] * kr, cdq[blk], dr);
+                } else {
+                  val = (float)s[t][r] * kr;  // x dq sm_scale in the exponent
+                }
               } else {
                 const float4 d4 = dv[r >> 2];
                 const float dr = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
@@ -716,6 +752,10 @@ k_attn(const AttnArgs a) {
       if constexpr (FP4 || QS) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) mt = fmaxf(mt, mxf[blk] * a.sm2);
+      } else if constexpr (TOKEN) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+          if (mxf[blk] != -INFINITY) mt = fmaxf(mt, mxf[blk] * c2[blk]);  // (c2 may be 0)
       } else {
 #pragma unroll
         for (int i = 0; i < NC2; ++i)
@@ -913,6 +953,7 @@ static hipError_t launch5(const AttnArgs &a, bool dump, hipStream_t st) {
 template <int D, int PV, int DT, bool CAUSAL>
 static hipError_t launch4(const AttnArgs &a, bool dump, hipStream_t st) {
   if (a.qk == 2) return launch5<D, PV, DT, CAUSAL, 2>(a, dump, st);
+  if (a.qk == 3) return launch5<D, PV, DT, CAUSAL, 3>(a, dump, st);
   return a.qk == 1 ? launch5<D, PV, DT, CAUSAL, 1>(a, dump, st) : launch5<D, PV, DT, CAUSAL, 0>(a, dump, st);
 }
 

@@ -431,7 +431,8 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
 // ---------------------------------------------------------------------------
 // INT8 quantisation of one 32-token block of Q: one scale for the block, or
 // (LANE) one scale per token -- the query a lane column holds in the 32 x 32
-// INT8 MFMA layout of the attention kernel.
+// INT8 MFMA layout of the attention kernel (per-token granularity of Q and K
+// uses the same Q pass).
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool LANE>
 __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
@@ -521,14 +522,16 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) { kmean
 
 // ---------------------------------------------------------------------------
 // Pass 2: INT8 quantisation of one 64-token block of K - k_mean: one scale for
-// the block, or (LANE) one per 16-key lane group -- the keys one half of a
-// wavefront holds of each 32-key sub-tile in the attention kernel's 32 x 32
-// MFMA result, group 2 * (n / 32) + bit 2 of n (4 groups per block).
+// the block (QK 0), or (QK 1, LANE) one per 16-key lane group -- the keys one
+// half of a wavefront holds of each 32-key sub-tile in the attention kernel's
+// 32 x 32 MFMA result, group 2 * (n / 32) + bit 2 of n (4 groups per block) --
+// or (QK 3, TOKEN) one per token.
 // ---------------------------------------------------------------------------
 __device__ inline int lane_group_in_block(int row) { return 2 * (row >> 5) + ((row >> 2) & 1); }
 
-template <int DT, int D, bool LANE>
+template <int DT, int D, int QK>
 __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
+  constexpr bool LANE = QK == 1, TOKEN = QK == 3;
   __shared__ float red[4][kThreads / 64];
   __shared__ float mean[D];
   const int tid = threadIdx.x;
@@ -543,7 +546,7 @@ __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
   constexpr int vec_per_row = D / 8;
   constexpr int nvec = kBlkK * vec_per_row;  // <= 1024: at most 4 per thread
   float x[4][8];
-  float amax = 0.0f, gmax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float amax = 0.0f, gmax[4] = {0.0f, 0.0f, 0.0f, 0.0f}, rmax[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int vi = tid + u * kThreads;
@@ -561,6 +564,7 @@ __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[u][i]));
     amax = fmaxf(amax, m);
+    rmax[u] = m;
     if (LANE && vi < nvec) {
       const int g = lane_group_in_block(row);
 #pragma unroll
@@ -598,6 +602,17 @@ __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
       for (int gg = 1; gg < 4; ++gg) m = tid == gg ? gmax[gg] : m;
       a.k_scale[(hv.row0 >> 4) + 4 * blk + tid] = m > 0.0f ? m / 127.0f : 0.0f;
     }
+  } else if constexpr (TOKEN) {
+    // a token's vec_per_row vectors sit in consecutive lanes of one wavefront
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int o = vec_per_row / 2; o >= 1; o >>= 1) rmax[u] = fmaxf(rmax[u], __shfl_xor(rmax[u], o, 64));
+      inv[u] = rmax[u] > 0.0f ? 127.0f / rmax[u] : 0.0f;
+      const int vi = tid + u * kThreads;
+      if (vi < nvec && vi % vec_per_row == 0)
+        a.k_scale[hv.row0 + blk * kBlkK + vi / vec_per_row] = rmax[u] > 0.0f ? rmax[u] / 127.0f : 0.0f;
+    }
   } else {
     amax = block_max(amax, red[0]);
 #pragma unroll
@@ -616,8 +631,8 @@ __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
     *reinterpret_cast<v2i *>(a.k_i8 + (hv.row0 + blk * kBlkK + row) * D + c8) = out;
   }
 }
-template <int DT, int D, bool LANE>
-__global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) { kquant_wg<DT, D, LANE>(a, blockIdx.x); }
+template <int DT, int D, int QK>
+__global__ __launch_bounds__(kThreads) void k_kquant(const QuantQKArgs a) { kquant_wg<DT, D, QK>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // MXFP4 quantisation of one block of ROWS tokens (32 of Q, or 64 of K - k_mean):
@@ -920,12 +935,13 @@ static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads), 0,
                      stream, a);
   if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
-  else if (a.qk == 1) hipLaunchKernelGGL((k_qquant<DT, D, true>), gq, dim3(kThreads), 0, stream, a);
+  else if (a.qk == 1 || a.qk == 3) hipLaunchKernelGGL((k_qquant<DT, D, true>), gq, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((k_qquant<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
   if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, true>), gk, dim3(kThreads), 0, stream, a);
-  else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, true>), gk, dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((k_kquant<DT, D, false>), gk, dim3(kThreads), 0, stream, a);
+  else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, 1>), gk, dim3(kThreads), 0, stream, a);
+  else if (a.qk == 3) hipLaunchKernelGGL((k_kquant<DT, D, 3>), gk, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_kquant<DT, D, 0>), gk, dim3(kThreads), 0, stream, a);
 }
 
 template <int DT, int D>
@@ -967,7 +983,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv2(const QuantQKArgs a, const Qu
   const int wg = blockIdx.x;
   if (wg < n_q) {
     if constexpr (QK == 2) mxfp4_wg<DT, D, false>(a, wg);
-    else qquant_wg<DT, D, QK == 1>(a, wg);
+    else qquant_wg<DT, D, QK == 1 || QK == 3>(a, wg);  // one scale per token (LANE, TOKEN)
   } else if (wg < n_q + n_m) {
     kmean_wg<D>(a, wg - n_q);
   } else {
@@ -982,7 +998,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv3(const QuantQKArgs a, const Qu
   const int wg = blockIdx.x;
   if (wg < n_k) {
     if constexpr (QK == 2) mxfp4_wg<DT, D, true>(a, wg);
-    else kquant_wg<DT, D, QK == 1>(a, wg);
+    else kquant_wg<DT, D, QK>(a, wg);
   } else {
     const int t = (wg - n_k) * TPW + (int)threadIdx.x / (2 * D);
     if (t < v.B * v.H * v.nk) vconvert_wg<DT, D>(v, t, (int)threadIdx.x % (2 * D));
@@ -1006,6 +1022,7 @@ static void launch_qkv(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t st
   else hipLaunchKernelGGL((k_qkv1<DT, D, false>), g1, dim3(kThreads), 0, st, a, v);
   if (a.qk == 2) launch_qkv3<DT, D, 2>(a, v, st);
   else if (a.qk == 1) launch_qkv3<DT, D, 1>(a, v, st);
+  else if (a.qk == 3) launch_qkv3<DT, D, 3>(a, v, st);
   else launch_qkv3<DT, D, 0>(a, v, st);
   hipLaunchKernelGGL((k_vscale<D>), dim3(gm), dim3(kThreads), 0, st, v);
 }

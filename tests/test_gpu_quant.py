@@ -101,6 +101,8 @@ FUSED_CASES = [
     (synth.custom(1, 2, 1, 64, seed=1406), "int8_lane", True, True),
     (synth.WORKLOADS["snippet_b2h32s4096d128"], "int8", False, False),
     (synth.custom(2, 4, 130, 128, layout="NHD", Hkv=2, q_bias_sigma=3.0, seed=1407), "mxfp4", True, True),
+    (synth.custom(2, 4, 300, 64, Hkv=2, token_norm=True, seed=1408), "int8_token", True, False),
+    (synth.custom(1, 2, 129, 128, dtype="bf16", layout="NHD", q_bias_sigma=3.0, seed=1409), "int8_token", False, True),
 ]
 
 

@@ -41,7 +41,7 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-@pytest.mark.parametrize("qk", ["int8", "int8_lane", "mxfp4"])
+@pytest.mark.parametrize("qk", ["int8", "int8_lane", "int8_token", "mxfp4"])
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_smooth_q_quant_and_delta(w, qk):
     q, k, _ = G.inputs(w)
@@ -56,7 +56,7 @@ def test_smooth_q_quant_and_delta(w, qk):
     for b in range(w.B):
         for h in range(w.H):
             qf = O.decode16(O.head(q, w.layout, b, h), dt)
-            r8, rs, rm = O.quant_q_head_smooth(qf, 32, 1 if qk == "int8_lane" else 32)
+            r8, rs, rm = O.quant_q_head_smooth(qf, 32, 1 if qk in ("int8_lane", "int8_token") else 32)
             assert np.array_equal(qm[b, h, :nq].view(np.uint32), rm.view(np.uint32)), (b, h)
             if qk == "mxfp4":  # the MXFP4 rule on Q minus the block means
                 r4, re = O.quant_mxfp4_rows((qf - np.repeat(rm, 32, axis=0)[:S]).astype(np.float32))
@@ -76,7 +76,9 @@ def test_smooth_q_quant_and_delta(w, qk):
             assert not ds[b, h, :nq, S:].any()
 
 
-MODES = ((False, "fp8", "int8"), (True, "fp16", "int8_lane"), (False, "fp8", "mxfp4"), (True, "fp16", "mxfp4"))
+MODES = ((False, "fp8", "int8"), (True, "fp16", "int8_lane"), (False, "fp8", "mxfp4"), (True, "fp16", "mxfp4"),
+         (True, "fp8", "int8_token"))
+GRAN = {"int8_lane": "lane", "int8_token": "token"}
 
 
 @pytest.mark.parametrize("w,causal,pv,qk", [(w, c, pv, qk) for w in CASES for c, pv, qk in MODES],
@@ -86,7 +88,7 @@ def test_smooth_q_attn_matches_oracle(w, causal, pv, qk):
     got = G.out_logical(out, w)
     q, k, v = G.inputs(w)
     ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal, pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16,
-                 tile_k=G.TILE_K[pv], smooth_q=True, gran="lane" if qk == "int8_lane" else "block",
+                 tile_k=G.TILE_K[pv], smooth_q=True, gran=GRAN.get(qk, "block"),
                  qk_format="fp4" if qk == "mxfp4" else "int8")
     ref = np.stack([np.stack([ref[(b, h)] for h in range(w.H)]) for b in range(w.B)])
     assert np.isfinite(got).all()
