@@ -163,7 +163,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the path has no multi-GPU part; see the sharding note in DESIGN.md", file=sys.stderr)
+              "the path has no multi-GPU part (one process drives one GPU)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:

@@ -558,9 +558,9 @@ k_attn(const AttnArgs a) {
     float ks[NKS];
     if constexpr (TOKEN) {
       // (per-key scales: read from ksr with the scores)
-    } else if constexpr (LANE) {
+    } else if constexpr (LANE || NB > 2) {
       loadn_uniform<NKS>(kscale + NKS * j, ks);
-    } else if (NB == 2) {
+    } else if constexpr (NB == 2) {
       const float2 ksv = load2_uniform(kscale + 2 * j);
       ks[0] = ksv.x;
       ks[NB - 1] = ksv.y;
