@@ -429,11 +429,13 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
     is added back to the output.
 
     gran: "block" (blk_q / blk_k tokens per scale), "lane" (thread-level: one
-    scale per Q token, one per 16-key lane group of K) or "token" (one scale per
-    Q token and per K token: the block rule with blocks of one token).
+    scale per Q token, one per 16-key lane group of K), "token" (one scale per
+    Q token and per K token: the block rule with blocks of one token) or "head"
+    (one scale for all of a head's Q tokens and one for all of its K tokens:
+    the block rule with one block spanning the head).
     Returns {(b, h): fp32 [len(rows), D]}; rows default to all S rows.
     """
-    if gran not in ("block", "lane", "token"):
+    if gran not in ("block", "lane", "token", "head"):
         raise ValueError(gran)
     lane = gran == "lane"
     if lane:
@@ -451,6 +453,7 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         qf = decode16(head(q, layout, b, h), dtype)
         kf = decode16(head(k, layout, b, hk), dtype)
         vf = decode16(head(v, layout, b, hk), dtype)
+        bq, bk = (max(qf.shape[0], 1), max(kf.shape[0], 1)) if gran == "head" else (blk_q, blk_k)
         qk = None
         if qk_format == "fp4":
             if smooth_q:  # Q minus its 32-token block means (one fp32 subtraction), then the MXFP4 rule
@@ -464,10 +467,10 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
             k8, ks = np.zeros(kf.shape, np.int8), np.zeros(1, np.float32)
         elif qk_format == "int8":
             if smooth_q:
-                q8, qs, qm = quant_q_head_smooth(qf, BLK_Q, blk_q)
+                q8, qs, qm = quant_q_head_smooth(qf, BLK_Q, bq)
             else:
-                q8, qs = quant_q_head(qf, blk_q)
-            k8, ks, km = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, blk_k, smooth)
+                q8, qs = quant_q_head(qf, bq)
+            k8, ks, km = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, bk, smooth)
         else:
             raise ValueError(qk_format)
         vm = None
@@ -478,7 +481,7 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         else:
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
-                                     sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=blk_q, blk_k=blk_k,
+                                     sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=bq, blk_k=bk,
                                      tile_k=tile_k, k_lane=lane, v_mean=vm, qk=qk,
                                      delta=qk_delta_head(qm, (kf - km[None, :]).astype(np.float32)) if smooth_q
                                      else None)

@@ -709,6 +709,57 @@ def pin_token_attention_uses_key_scales():
         assert cos(got, ref) >= 0.99999 and rel_l1(got, ref) < 2e-3, (causal, cos(got, ref), rel_l1(got, ref))
 
 
+def pin_head_scale_is_the_largest_block_scale():
+    """Per-head granularity: the head's one scale is amax / 127 over all of its
+    tokens, so it equals the largest per-block scale of the same head under
+    any block partition (fl(x / 127) is monotone); every code is then the INT8
+    rule with that scale, and the largest element codes to +-127."""
+    S, D = 333, 64
+    qf, kf, _ = _rand_head(S, D, seed=48)
+    qf = qf.copy()
+    qf[200] *= 20.0
+    for x, quant in ((qf, lambda a, blk: O.quant_q_head(a, blk)),
+                     (kf, lambda a, blk: O.quant_k_head(a, blk, True)[:2])):
+        c, sc = quant(x, S)
+        assert sc.shape == (1,)
+        for blk in (1, 32, 64, 100):
+            assert sc[0] == quant(x, blk)[1].max(), blk
+        assert np.abs(c).max() == 127
+    # the K rule is applied to K - k_mean: the head scale follows the spread, not the offset
+    _, ks_off, _ = O.quant_k_head((kf + np.float32(50.0)).astype(np.float32), S, True)
+    _, ks_raw, _ = O.quant_k_head((kf + np.float32(50.0)).astype(np.float32), S, False)
+    assert ks_off[0] < 0.2 * ks_raw[0]
+
+
+def pin_head_codes_invariant_under_power_of_two_scaling():
+    """Scaling a whole head by 2^k multiplies its scale by 2^k exactly and leaves
+    every code unchanged; scaling one token that does not hold the maximum
+    changes only that token's codes."""
+    S, D = 90, 64
+    qf, _, _ = _rand_head(S, D, seed=49)
+    c0, s0 = O.quant_q_head(qf, S)
+    c1, s1 = O.quant_q_head((qf * np.float32(8.0)).astype(np.float32), S)
+    assert np.array_equal(c0, c1) and s1[0] == 8 * s0[0]
+    j = int(np.argmin(np.abs(qf).max(axis=1)))  # the token with the smallest peak
+    q2 = qf.copy()
+    q2[j] *= 0.5
+    c2, s2 = O.quant_q_head(q2, S)
+    assert s2[0] == s0[0] and np.array_equal(np.delete(c2, j, axis=0), np.delete(c0, j, axis=0))
+
+
+def pin_head_less_accurate_than_block():
+    """One scale per head cannot follow tokens of very different norms: against
+    exact attention it is less accurate than per-block scales, which are in
+    turn less accurate than per-token ones."""
+    w = synth.custom(1, 2, 512, 128, token_norm=True, outlier_p=0.01, bias_sigma=3.0, seed=50)
+    q, k, v = synth.make_qkv(w)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    errs = {g: O.attn(q, k, v, F16, "HND", gran=g) for g in ("head", "block", "token")}
+    for hd in ex:
+        e = {g: rel_l1(errs[g][hd], ex[hd]) for g in errs}
+        assert e["head"] > e["block"] > e["token"], (hd, e)
+
+
 # ------------------------------------------------------------------ V smoothing
 def pin_smooth_v_quant():
     """Smoothed V: the mean is the channel mean, and the codes and scales are the
