@@ -55,8 +55,8 @@ def parse():
     p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
     p.add_argument("--smooth-q", action="store_true",
                    help="Q smoothing (fixed-length batches): quantise Q minus its 32-token block means")
-    p.add_argument("--qk-quant", default="int8", choices=["int8", "int8_lane", "int8_token", "mxfp4"],
-                   help="Q/K quantisation: INT8 per block, INT8 per Q token / 16-key lane group, INT8 per token, or MXFP4")
+    p.add_argument("--qk-quant", default="int8", choices=["int8", "int8_lane", "int8_token", "int8_head", "mxfp4"],
+                   help="Q/K quantisation: INT8 per block, per Q token / 16-key lane group, per token or per head, or MXFP4")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-oracle sample (0: as many as take about 12 s)")
@@ -100,7 +100,7 @@ def traffic_record(kernel_hash, workload, pv, causal, qk="int8", smooth_v=False,
 
 def oracle_qk(qk):
     """The oracle's keyword arguments for a Q/K quantisation mode."""
-    return {"int8": {}, "int8_lane": {"gran": "lane"}, "int8_token": {"gran": "token"}, "mxfp4": {"qk_format": "fp4"}}[qk]
+    return {"int8": {}, "int8_lane": {"gran": "lane"}, "int8_token": {"gran": "token"}, "int8_head": {"gran": "head"}, "mxfp4": {"qk_format": "fp4"}}[qk]
 
 
 def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=False):
@@ -255,7 +255,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"int8": "i8", "int8_lane": "i8", "int8_token": "i8", "mxfp4": "mxfp4"}[args.qk_quant] + ("+fp8" if args.pv == "fp8" else "+f16"),
+        "dtype": {"int8": "i8", "int8_lane": "i8", "int8_token": "i8", "int8_head": "i8", "mxfp4": "mxfp4"}[args.qk_quant] + ("+fp8" if args.pv == "fp8" else "+f16"),
         "data": "synthetic",
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,

@@ -53,7 +53,9 @@
  *   k_scale float [B][H_kv][nk]    one scale per block of SAGE_BLK_K tokens (0 for blocks
  *                                  made only of padding keys; SAGE_QK_INT8_LANE:
  *                                  [B][H_kv][S_k / 16], one per lane group;
- *                                  SAGE_QK_INT8_TOKEN: [B][H_kv][S_k], one per token).
+ *                                  SAGE_QK_INT8_TOKEN: [B][H_kv][S_k], one per token;
+ *                                  SAGE_QK_INT8_HEAD: the per-block layouts of q_scale and
+ *                                  k_scale, each slot holding its head's one scale).
  *   k_mean  float [B][H_kv][D]     per-channel mean of K over the S tokens.
  *   v_fp8   uint8 [B][H_kv][nk][D][64] E4M3 codes of V, one 64-key tile after the
  *           other, each tile stored channel-major; inside a tile, byte p of
@@ -112,6 +114,10 @@ extern "C" {
                                 E2M1(x / 2^e), round to nearest even, saturating at 6 */
 #define SAGE_QK_INT8_TOKEN 3 /* INT8, one scale per query token and per key token ([REPO]
                                 feature list: granularity per token, per head or per thread) */
+#define SAGE_QK_INT8_HEAD 4  /* INT8, one scale for all of a head's Q tokens and one for all of
+                                its K - k_mean tokens ([REPO] feature list); the per-block
+                                buffer layout, every block slot holding the head's scale.
+                                Not with smoothed Q (q_mean / delta_s give SAGE_ERR_INVALID_ARG) */
 
 /* ---- limits and granularity ---- */
 #define SAGE_BLK_Q 32 /* Q tokens per INT8 scale: one wavefront's 32-row MFMA tile */
@@ -146,7 +152,8 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
  *     an all-zero block has scale 0 and codes 0.   (IEEE fp32, round half to even)
  *   qk_quant = SAGE_QK_INT8_LANE: the same rule with each Q token, and each 16-key lane
  *   group of K - k_mean, as its own block; SAGE_QK_INT8_TOKEN: with each Q token and
- *   each token of K - k_mean as its own block; SAGE_QK_MXFP4: the MXFP4 rule above on each
+ *   each token of K - k_mean as its own block; SAGE_QK_INT8_HEAD: with all of a head's
+ *   tokens of Q, and of K - k_mean, as one block; SAGE_QK_MXFP4: the MXFP4 rule above on each
  *   32-channel block of every Q token and of every token of K - k_mean.
  * q: dtype (SAGE_DTYPE_*) tensor in `layout` (SAGE_LAYOUT_*) with H heads; k: the
  * same with H_kv heads.

@@ -26,7 +26,7 @@ SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ER
 LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
 PV = {"fp8": 0, "fp16": 1}
-QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2, "int8_token": 3}  # Q/K quantisation (include/sage.h SAGE_QK_*)
+QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2, "int8_token": 3, "int8_head": 4}  # Q/K quantisation (include/sage.h SAGE_QK_*)
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
 TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
 
@@ -260,7 +260,8 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
     torch tensors.
     k and v may have fewer heads than q (grouped-query attention); qk_quant "int8"
     (per block), "int8_lane" (one scale per Q token and per 16-key lane group of
-    K), "int8_token" (one per Q token and per K token) or "mxfp4"; smooth_v
+    K), "int8_token" (one per Q token and per K token), "int8_head" (one per
+    head of Q and of K; not with smooth_q) or "mxfp4"; smooth_v
     (pv fp8): quantise V minus its channel mean; smooth_q: quantise Q minus its
     32-token block means and form the pre-processing term."""
     if smooth_v and pv_mode != "fp8":

@@ -43,7 +43,7 @@ int check_kv_heads(int H, int H_kv) {
 
 int check_qk_quant(int qk_quant) {
   return (qk_quant == SAGE_QK_INT8_BLOCK || qk_quant == SAGE_QK_INT8_LANE || qk_quant == SAGE_QK_MXFP4 ||
-          qk_quant == SAGE_QK_INT8_TOKEN)
+          qk_quant == SAGE_QK_INT8_TOKEN || qk_quant == SAGE_QK_INT8_HEAD)
              ? SAGE_OK
              : SAGE_ERR_INVALID_ARG;
 }
@@ -108,8 +108,8 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
   if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;  // smoothing is for the FP8 V codes
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
-  // smoothed Q: the INT8 product only, 4-byte aligned, and not with the debug dump
-  if (delta_s && (!aligned(delta_s, 4) || dump)) return SAGE_ERR_INVALID_ARG;
+  // smoothed Q: 4-byte aligned, not with the debug dump, not with per-head scales
+  if (delta_s && (!aligned(delta_s, 4) || dump || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
@@ -199,6 +199,7 @@ static int qk_args(QuantQKArgs &a, const void *q, const void *k, int dtype, int 
   if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_qk_quant(qk_quant))) return rc;
   if (q_mean && !aligned(q_mean, 4)) return SAGE_ERR_INVALID_ARG;
+  if (q_mean && qk_quant == SAGE_QK_INT8_HEAD) return SAGE_ERR_INVALID_ARG;  // per-head scales: unsmoothed Q only
   if ((rc = check_enums(dtype, layout))) return rc;
   if (!q || !k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;

@@ -152,19 +152,28 @@ struct ChunkMap {
 };
 
 // K channel sums (binary64) of one chunk -> partials[chunk][D]; or, with
-// ABSMAX, V channel abs-max (fp32) of one chunk.
-template <int DT, int D, bool ABSMAX>
-__device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk, void *partials) {
+// ABSMAX, channel abs-max (fp32) of one chunk.  MINMAX (with the sums): also
+// the chunk's channel max and min (fp32) -> minmax[chunk][2][D].
+template <int DT, int D, bool ABSMAX, bool MINMAX = false>
+__device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk, void *partials,
+                                    float *minmax = nullptr) {
+  static_assert(!(ABSMAX && MINMAX), "max / min ride along with the sums");
   const int S = hv.S;
   using M = ChunkMap<D>;
   typedef typename std::conditional<ABSMAX, float, double>::type acc_t;
   __shared__ acc_t part[M::R][D];
+  __shared__ float pmx[MINMAX ? M::R : 1][MINMAX ? D : 1], pmn[MINMAX ? M::R : 1][MINMAX ? D : 1];
   const int tid = threadIdx.x, g = tid % M::G, r = tid / M::G;
   const int ct = chunk_tokens(S);
   const int s_end = min(S, (chunk + 1) * ct);
   acc_t acc[8];
+  float mx[8], mn[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0;
+  for (int i = 0; i < 8; ++i) {
+    acc[i] = 0;
+    mx[i] = -INFINITY;
+    mn[i] = INFINITY;
+  }
   for (int s0 = chunk * ct + r; s0 < s_end; s0 += M::R * M::kUnroll) {
     v4i raw[M::kUnroll];  // 16-bit pairs as loaded (zeros past the chunk)
 #pragma unroll
@@ -180,10 +189,20 @@ __device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk,
         const float v = in_to_f32<DT>(i & 1 ? (uint32_t)raw[u][i >> 1] >> 16 : (uint32_t)raw[u][i >> 1] & 0xffffu);
         if (ABSMAX) acc[i] = fmaxf(acc[i], fabsf(v));
         else acc[i] += (double)v;
+        if (MINMAX && s0 + u * M::R < s_end) {  // (rows past the chunk are not tokens)
+          mx[i] = fmaxf(mx[i], v);
+          mn[i] = fminf(mn[i], v);
+        }
       }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) part[r][8 * g + i] = acc[i];
+  for (int i = 0; i < 8; ++i) {
+    part[r][8 * g + i] = acc[i];
+    if (MINMAX) {
+      pmx[r][8 * g + i] = mx[i];
+      pmn[r][8 * g + i] = mn[i];
+    }
+  }
   __syncthreads();
   if (tid < D) {
     acc_t t = part[0][tid];
@@ -192,22 +211,70 @@ __device__ inline void chunk_reduce(const uint16_t *x, const Seg &hv, int chunk,
       else t += part[rr][tid];
     }
     reinterpret_cast<acc_t *>(partials)[(long long)chunk * D + tid] = t;
+    if (MINMAX) {
+      float a = pmx[0][tid], b = pmn[0][tid];
+      for (int rr = 1; rr < M::R; ++rr) {
+        a = fmaxf(a, pmx[rr][tid]);
+        b = fminf(b, pmn[rr][tid]);
+      }
+      minmax[((long long)chunk * 2) * D + tid] = a;
+      minmax[((long long)chunk * 2 + 1) * D + tid] = b;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // K channel sums of one chunk of tokens -> partials (k_i8 region of the head).
 // ---------------------------------------------------------------------------
-template <int DT, int D>
+// HEAD (per-head granularity): also each chunk's channel max and min, stored
+// after the head's n_chunks(S) sums (2 D floats a chunk: the sums and these
+// take 16 D bytes a chunk of at least 256 tokens, inside the head's codes).
+template <int DT, int D, bool HEAD = false>
 __device__ inline void ksum_wg(const QuantQKArgs &a, int wg) {
   const int nch = chunk_grid(a.varlen ? a.sk.max_len : a.S);
   const int bh = wg / nch, chunk = wg % nch;  // bh: K head (b, h_kv)
   const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
   if (chunk >= n_chunks(sg.S)) return;
-  chunk_reduce<DT, D, false>((const uint16_t *)a.k, sg, chunk, a.k_i8 + sg.row0 * code_row_bytes<D>(a));
+  int8_t *part = a.k_i8 + sg.row0 * code_row_bytes<D>(a);
+  float *minmax = reinterpret_cast<float *>(reinterpret_cast<double *>(part) + (long long)n_chunks(sg.S) * D);
+  chunk_reduce<DT, D, false, HEAD>((const uint16_t *)a.k, sg, chunk, part, minmax);
+}
+template <int DT, int D, bool HEAD>
+__global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) { ksum_wg<DT, D, HEAD>(a, blockIdx.x); }
+
+// ---------------------------------------------------------------------------
+// Per-head granularity of Q: channel abs-max of one chunk of a Q head ->
+// partials[chunk][D] (fp32) in the head's codes, which the Q pass overwrites
+// later; then one work-group per head reduces them to the head's abs-max and
+// leaves it in every block slot of q_scale, where each block's Q pass reads it
+// before writing its scale there.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__device__ inline void qamax_part_wg(const QuantQKArgs &a, int wg) {
+  const int nch = chunk_grid(a.varlen ? a.sq.max_len : a.S);
+  const int bh = wg / nch, chunk = wg % nch;  // bh: Q head (b, h)
+  const Seg sg = q_seg<D>(a, bh / a.H, bh % a.H);
+  if (chunk >= n_chunks(sg.S)) return;
+  chunk_reduce<DT, D, true>((const uint16_t *)a.q, sg, chunk, a.q_i8 + sg.row0 * D);
 }
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void k_ksum(const QuantQKArgs a) { ksum_wg<DT, D>(a, blockIdx.x); }
+__global__ __launch_bounds__(kThreads) void k_qamax_part(const QuantQKArgs a) { qamax_part_wg<DT, D>(a, blockIdx.x); }
+
+template <int D>
+__device__ inline void qhead_wg(const QuantQKArgs &a, int wg) {
+  __shared__ float red[kThreads / 64];
+  const int tid = threadIdx.x;
+  const Seg sg = q_seg<D>(a, wg / a.H, wg % a.H);  // (uniform across the work-group)
+  const float *part = reinterpret_cast<const float *>(a.q_i8 + sg.row0 * D);
+  const int n = n_chunks(sg.S) * D;  // <= kMaxChunks D
+  float m = 0.0f;
+  for (int i = tid; i < n; i += kThreads) m = fmaxf(m, part[i]);
+  m = block_max(m, red);
+  const int nblk = ceil_div(sg.S, kBlkQ);
+  for (int blk = tid; blk < nblk; blk += kThreads) a.q_scale[(sg.row0 >> 5) + blk] = m;
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_qhead(const QuantQKArgs a) { qhead_wg<D>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Smoothed Q ("SageAttention2" summary, SageAttention2方法: subtract each block
@@ -434,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
 // INT8 MFMA layout of the attention kernel (per-token granularity of Q and K
 // uses the same Q pass).
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool LANE>
+template <int DT, int D, bool LANE, bool HEAD = false>
 __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
   __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x;
@@ -480,6 +547,14 @@ __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
       if (vi < nvec && vi % vec_per_row == 0)
         a.q_scale[hv.row0 + blk * kBlkQ + vi / vec_per_row] = ramax[u] > 0.0f ? ramax[u] / 127.0f : 0.0f;
     }
+  } else if constexpr (HEAD) {
+    // the head's abs-max, left in this block's slot by the reduction pass; the
+    // slot is overwritten with the scale once every thread has read it
+    const long long slot = (hv.row0 >> 5) + blk;
+    const float hm = a.q_scale[slot];
+    inv[0] = inv[1] = hm > 0.0f ? 127.0f / hm : 0.0f;
+    __syncthreads();
+    if (tid == 0) a.q_scale[slot] = hm > 0.0f ? hm / 127.0f : 0.0f;
   } else {
     amax = block_max(amax, red);
     inv[0] = inv[1] = amax > 0.0f ? 127.0f / amax : 0.0f;
@@ -497,28 +572,63 @@ __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
     *reinterpret_cast<v2i *>(a.q_i8 + (hv.row0 + blk * kBlkQ + row) * D + c8) = out;
   }
 }
-template <int DT, int D, bool LANE>
-__global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) { qquant_wg<DT, D, LANE>(a, blockIdx.x); }
+template <int DT, int D, bool LANE, bool HEAD = false>
+__global__ __launch_bounds__(kThreads) void k_qquant(const QuantQKArgs a) {
+  qquant_wg<DT, D, LANE, HEAD>(a, blockIdx.x);
+}
 
-// k_mean[bh][d] = fp32(sum over the head's chunk partials / S); thread = (K head bh, d)
-template <int D>
+// k_mean[bh][d] = fp32(sum over the head's chunk partials / S); thread = (K head bh, d).
+// HEAD (per-head granularity): the head's max |K - k_mean| as well, formed
+// from the chunks' channel max and min: fl(x - m) is monotone in x, so the
+// largest |fl(K[s][d] - m)| over the tokens is fl(max_d - m) or fl(m - min_d);
+// the D channels of a head are D consecutive threads of one work-group
+// (256 = a multiple of D), and the head's value is left in each of its K
+// block slots of k_scale for the K pass.
+template <int D, bool HEAD = false>
 __device__ inline void kmean_wg(const QuantQKArgs &a, int wg) {
   const long long i = (long long)wg * kThreads + threadIdx.x;
-  if (i >= (long long)a.B * a.H_kv * D) return;
+  const bool valid = i < (long long)a.B * a.H_kv * D;
   const int bh = (int)(i / D), d = (int)(i % D);
-  const Seg sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
-  const double *part = reinterpret_cast<const double *>(a.k_i8 + sg.row0 * code_row_bytes<D>(a));
-  const int nch = n_chunks(sg.S);
-  double v[kMaxChunks];
+  float hmax = 0.0f;
+  Seg sg{};
+  if (valid) {
+    sg = k_seg<D>(a, bh / a.H_kv, bh % a.H_kv);
+    const double *part = reinterpret_cast<const double *>(a.k_i8 + sg.row0 * code_row_bytes<D>(a));
+    const int nch = n_chunks(sg.S);
+    double v[kMaxChunks];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0;  // all loads in flight
-  double t = 0.0;
+    for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0;  // all loads in flight
+    double t = 0.0;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) t += v[c];
-  a.k_mean[i] = sg.S > 0 ? (float)(t / (double)sg.S) : 0.0f;
+    for (int c = 0; c < kMaxChunks; ++c) t += v[c];
+    const float m = sg.S > 0 ? (float)(t / (double)sg.S) : 0.0f;
+    a.k_mean[i] = m;
+    if (HEAD && sg.S > 0) {
+      const float *mm = reinterpret_cast<const float *>(part + (long long)nch * D);
+      float mx = -INFINITY, mn = INFINITY;
+      for (int c = 0; c < nch; ++c) {
+        mx = fmaxf(mx, mm[(2LL * c) * D + d]);
+        mn = fminf(mn, mm[(2LL * c + 1) * D + d]);
+      }
+      hmax = fmaxf(mx - m, m - mn);
+    }
+  }
+  if constexpr (HEAD) {
+    __shared__ float hm[kThreads];
+    const int tid = threadIdx.x;
+    hm[tid] = hmax;
+    __syncthreads();
+    const int h0 = tid - d;  // the head's first thread in this work-group
+    float r = 0.0f;
+    for (int c = 0; c < D; ++c) r = fmaxf(r, hm[h0 + c]);
+    if (valid) {
+      const int nslot = ceil_div(sg.S, kKvPad) * (kKvPad / kBlkK);  // the K pass's blocks of this head
+      for (int blk = d; blk < nslot; blk += D) a.k_scale[(sg.row0 >> 6) + blk] = r;
+    }
+  }
 }
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) { kmean_wg<D>(a, blockIdx.x); }
+template <int D, bool HEAD>
+__global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) { kmean_wg<D, HEAD>(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Pass 2: INT8 quantisation of one 64-token block of K - k_mean: one scale for
@@ -531,7 +641,7 @@ __device__ inline int lane_group_in_block(int row) { return 2 * (row >> 5) + ((r
 
 template <int DT, int D, int QK>
 __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
-  constexpr bool LANE = QK == 1, TOKEN = QK == 3;
+  constexpr bool LANE = QK == 1, TOKEN = QK == 3, HEAD = QK == 4;
   __shared__ float red[4][kThreads / 64];
   __shared__ float mean[D];
   const int tid = threadIdx.x;
@@ -613,6 +723,15 @@ __device__ inline void kquant_wg(const QuantQKArgs &a, int wg) {
       if (vi < nvec && vi % vec_per_row == 0)
         a.k_scale[hv.row0 + blk * kBlkK + vi / vec_per_row] = rmax[u] > 0.0f ? rmax[u] / 127.0f : 0.0f;
     }
+  } else if constexpr (HEAD) {
+    // the head's abs-max, left in this block's slot by the mean pass; the slot
+    // is overwritten with the scale once every thread has read it
+    const long long slot = (hv.row0 >> 6) + blk;
+    const float hm = a.k_scale[slot];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) inv[u] = hm > 0.0f ? 127.0f / hm : 0.0f;
+    __syncthreads();
+    if (tid == 0) a.k_scale[slot] = hm > 0.0f ? hm / 127.0f : 0.0f;
   } else {
     amax = block_max(amax, red[0]);
 #pragma unroll
@@ -932,12 +1051,22 @@ static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
   // per-block passes: every block of every (entry, head), or of each head's packed buffer
   const dim3 gq(a.varlen ? a.H * (int)(a.rows_q / kBlkQ) : a.B * a.H * a.nq);
   const dim3 gk(a.varlen ? a.H_kv * (int)(a.rows_k / kBlkK) : bhk * a.nk);
-  hipLaunchKernelGGL((k_ksum<DT, D>), dim3(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads), 0,
-                     stream, a);
+  const dim3 gs(bhk * chunk_grid(a.varlen ? a.sk.max_len : a.S));
+  if (a.qk == 4) {  // per head: the heads' abs-max first, then the per-block passes
+    hipLaunchKernelGGL((k_ksum<DT, D, true>), gs, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_qamax_part<DT, D>), dim3(a.B * a.H * chunk_grid(a.varlen ? a.sq.max_len : a.S)),
+                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_qhead<D>), dim3(a.B * a.H), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_qquant<DT, D, false, true>), gq, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_kmean<D, true>), dim3(gd), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_kquant<DT, D, 4>), gk, dim3(kThreads), 0, stream, a);
+    return;
+  }
+  hipLaunchKernelGGL((k_ksum<DT, D, false>), gs, dim3(kThreads), 0, stream, a);
   if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
   else if (a.qk == 1 || a.qk == 3) hipLaunchKernelGGL((k_qquant<DT, D, true>), gq, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL((k_qquant<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((k_kmean<D>), dim3(gd), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_kmean<D, false>), dim3(gd), dim3(kThreads), 0, stream, a);
   if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, true>), gk, dim3(kThreads), 0, stream, a);
   else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, 1>), gk, dim3(kThreads), 0, stream, a);
   else if (a.qk == 3) hipLaunchKernelGGL((k_kquant<DT, D, 3>), gk, dim3(kThreads), 0, stream, a);
@@ -965,27 +1094,32 @@ static void launch_v(const QuantVArgs &a, hipStream_t stream) {
 //   2. Q quantisation | K means | V abs-max (and means) from the chunk partials
 //   3. K quantisation | V FP8 conversion
 //   4. V scales
+// Per-head granularity moves Q: its chunk abs-max joins launch 1, the per-head
+// reduction takes its place in launch 2, and Q quantisation joins launch 3.
 // Every pass that overwrites a buffer holding chunk partials (K and V codes)
 // runs in a later launch than the work-groups that read them.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool VSTATS>
+template <int DT, int D, bool VSTATS, bool HEAD>
 __global__ __launch_bounds__(kThreads) void k_qkv1(const QuantQKArgs a, const QuantVArgs v) {
-  const int n_k = a.B * a.H_kv * chunk_grid(a.S);
+  const int n_k = a.B * a.H_kv * chunk_grid(a.S);  // (V has as many chunks: H_kv heads)
   const int wg = blockIdx.x;
-  if (wg < n_k) ksum_wg<DT, D>(a, wg);
+  if (wg < n_k) ksum_wg<DT, D, HEAD>(a, wg);
+  else if (HEAD && wg >= 2 * n_k) qamax_part_wg<DT, D>(a, wg - 2 * n_k);
   else if constexpr (VSTATS) vstats_part_wg<DT, D>(v, wg - n_k);
   else vamax_part_wg<DT, D>(v, wg - n_k);
 }
 
 template <int DT, int D, int QK>
 __global__ __launch_bounds__(kThreads) void k_qkv2(const QuantQKArgs a, const QuantVArgs v) {
-  const int n_q = a.B * a.H * a.nq, n_m = ceil_div(a.B * a.H_kv * D, kThreads);
+  constexpr bool HEAD = QK == 4;
+  const int n_q = HEAD ? a.B * a.H : a.B * a.H * a.nq, n_m = ceil_div(a.B * a.H_kv * D, kThreads);
   const int wg = blockIdx.x;
   if (wg < n_q) {
     if constexpr (QK == 2) mxfp4_wg<DT, D, false>(a, wg);
+    else if constexpr (HEAD) qhead_wg<D>(a, wg);
     else qquant_wg<DT, D, QK == 1 || QK == 3>(a, wg);  // one scale per token (LANE, TOKEN)
   } else if (wg < n_q + n_m) {
-    kmean_wg<D>(a, wg - n_q);
+    kmean_wg<D, HEAD>(a, wg - n_q);
   } else {
     vamax_wg<D>(v, wg - n_q - n_m);
   }
@@ -994,11 +1128,13 @@ __global__ __launch_bounds__(kThreads) void k_qkv2(const QuantQKArgs a, const Qu
 template <int DT, int D, int QK>
 __global__ __launch_bounds__(kThreads) void k_qkv3(const QuantQKArgs a, const QuantVArgs v) {
   constexpr int TPW = kThreads / (2 * D);  // 64-key V tiles a work-group converts (2 D threads each)
-  const int n_k = a.B * a.H_kv * a.nk;
+  const int n_k = a.B * a.H_kv * a.nk, n_v = ceil_div(v.B * v.H * v.nk, TPW);
   const int wg = blockIdx.x;
   if (wg < n_k) {
     if constexpr (QK == 2) mxfp4_wg<DT, D, true>(a, wg);
     else kquant_wg<DT, D, QK>(a, wg);
+  } else if (QK == 4 && wg >= n_k + n_v) {
+    qquant_wg<DT, D, false, true>(a, wg - n_k - n_v);  // per head: Q after its reduction
   } else {
     const int t = (wg - n_k) * TPW + (int)threadIdx.x / (2 * D);
     if (t < v.B * v.H * v.nk) vconvert_wg<DT, D>(v, t, (int)threadIdx.x % (2 * D));
@@ -1009,18 +1145,26 @@ template <int DT, int D, int QK>
 static void launch_qkv3(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t st) {
   const int bhk = a.B * a.H_kv, gm = (bhk * D + kThreads - 1) / kThreads;
   constexpr int TPW = kThreads / (2 * D);
-  hipLaunchKernelGGL((k_qkv2<DT, D, QK>), dim3(a.B * a.H * a.nq + 2 * gm), dim3(kThreads), 0, st, a, v);
-  hipLaunchKernelGGL((k_qkv3<DT, D, QK>), dim3(bhk * a.nk + (bhk * v.nk + TPW - 1) / TPW), dim3(kThreads), 0, st,
-                     a, v);
+  const int nq = a.B * a.H * a.nq;  // Q blocks
+  hipLaunchKernelGGL((k_qkv2<DT, D, QK>), dim3((QK == 4 ? a.B * a.H : nq) + 2 * gm), dim3(kThreads), 0, st, a, v);
+  hipLaunchKernelGGL((k_qkv3<DT, D, QK>), dim3(bhk * a.nk + (bhk * v.nk + TPW - 1) / TPW + (QK == 4 ? nq : 0)),
+                     dim3(kThreads), 0, st, a, v);
 }
 
 template <int DT, int D>
 static void launch_qkv(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t st) {
   const int bhk = a.B * a.H_kv, gm = (bhk * D + kThreads - 1) / kThreads;
-  const dim3 g1(2 * bhk * chunk_grid(a.S));  // K chunks, then as many V chunks (V has H_kv heads)
-  if (v.v_mean) hipLaunchKernelGGL((k_qkv1<DT, D, true>), g1, dim3(kThreads), 0, st, a, v);
-  else hipLaunchKernelGGL((k_qkv1<DT, D, false>), g1, dim3(kThreads), 0, st, a, v);
-  if (a.qk == 2) launch_qkv3<DT, D, 2>(a, v, st);
+  // K chunks, then as many V chunks (V has H_kv heads), then (per head) the Q chunks
+  const dim3 g1(2 * bhk * chunk_grid(a.S) + (a.qk == 4 ? a.B * a.H * chunk_grid(a.S) : 0));
+  if (a.qk == 4) {
+    if (v.v_mean) hipLaunchKernelGGL((k_qkv1<DT, D, true, true>), g1, dim3(kThreads), 0, st, a, v);
+    else hipLaunchKernelGGL((k_qkv1<DT, D, false, true>), g1, dim3(kThreads), 0, st, a, v);
+  } else {
+    if (v.v_mean) hipLaunchKernelGGL((k_qkv1<DT, D, true, false>), g1, dim3(kThreads), 0, st, a, v);
+    else hipLaunchKernelGGL((k_qkv1<DT, D, false, false>), g1, dim3(kThreads), 0, st, a, v);
+  }
+  if (a.qk == 4) launch_qkv3<DT, D, 4>(a, v, st);
+  else if (a.qk == 2) launch_qkv3<DT, D, 2>(a, v, st);
   else if (a.qk == 1) launch_qkv3<DT, D, 1>(a, v, st);
   else if (a.qk == 3) launch_qkv3<DT, D, 3>(a, v, st);
   else launch_qkv3<DT, D, 0>(a, v, st);

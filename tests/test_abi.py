@@ -45,6 +45,8 @@ def test_config_and_sizes():
     s = qa.sage_buffer_sizes(2, 3, 3, 100, 64, qa.QK["int8_lane"])
     assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 128 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 8 * 4,
                  "k_mean": 6 * 64 * 4, "v_fp8": 6 * 128 * 64, "v_scale": 6 * 64 * 4, **sq}
+    # per-head granularity: the per-block layout
+    assert qa.sage_buffer_sizes(2, 3, 3, 100, 64, qa.QK["int8_head"]) == qa.sage_buffer_sizes(2, 3, 3, 100, 64)
     # per-token granularity: one scale per (padded) Q row and per (padded) K row
     s = qa.sage_buffer_sizes(2, 3, 3, 100, 64, qa.QK["int8_token"])
     assert s == {"q_i8": 6 * 128 * 64, "q_scale": 6 * 128 * 4, "k_i8": 6 * 128 * 64, "k_scale": 6 * 128 * 4,
@@ -58,7 +60,7 @@ def test_config_and_sizes():
     assert L.sage_get_config(None, None, None, None) == qa.SAGE_ERR_INVALID_ARG
     for bad in [(0, 1, 1, 1, 64, 0), (1, 0, 1, 1, 64, 0), (1, 1, 1, 0, 64, 0), (1, 1, 1, 1, 96, 0),
                 (1, 1, 1, (1 << 20) + 1, 64, 0), (1, 4, 0, 1, 64, 0), (1, 4, 3, 1, 64, 0), (1, 4, 8, 1, 64, 0),
-                (1, 4, -4, 1, 64, 0), (1, 1, 1, 1, 64, 4), (1, 1, 1, 1, 64, -1)]:
+                (1, 4, -4, 1, 64, 0), (1, 1, 1, 1, 64, 5), (1, 1, 1, 1, 64, -1)]:
         assert L.sage_buffer_sizes(*bad, *([None] * 9)) == qa.SAGE_ERR_INVALID_ARG
 
 
@@ -94,7 +96,8 @@ GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=No
 BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict(q_scale=P + 2), dict(dtype=2),
           dict(layout=-1), dict(B=0), dict(H=-1), dict(S=0), dict(D=32), dict(D=256), dict(S=(1 << 20) + 1),
           dict(B=1 << 9, H=1 << 8, H_kv=1 << 8), dict(H_kv=0), dict(H_kv=3), dict(H=3, H_kv=2), dict(H_kv=-2),
-          dict(qk_quant=4), dict(qk_quant=-1), dict(q_mean=P + 2)]
+          dict(qk_quant=5), dict(qk_quant=-1), dict(q_mean=P + 2),
+          dict(qk_quant=4, q_mean=P)]  # per-head scales: no smoothed Q
 BAD_DELTA = [dict(k=None), dict(q_mean=None), dict(k_mean=None), dict(delta_s=None), dict(q_mean=P + 4),
              dict(delta_s=P + 2), dict(delta_s=P + 4), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2),
              dict(dtype=4), dict(S=0)]
@@ -103,7 +106,7 @@ BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dic
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
             dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
             dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
-            dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=4),
+            dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=5), dict(qk_quant=4, delta_s=P),
             dict(v_mean=P + 1), dict(pv_mode=1, v_scale=None, v_mean=P),  # smoothing is for the FP8 V codes
             dict(delta_s=P + 2),
             # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
@@ -177,7 +180,7 @@ def test_attn_fp16_mode_accepts_null_v_scale_then_needs_device():
 def test_dump_rejects_bad_head_and_buffer():
     a = [v for k, v in GOOD_ATTN.items() if k not in ("delta_s", "stream")]  # the dump takes no smoothed-Q term
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 2, P, None) == qa.SAGE_ERR_INVALID_ARG  # h out of range
-    a[-1] = 4
+    a[-1] = 5
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 0, P, None) == qa.SAGE_ERR_INVALID_ARG  # bad Q/K mode
     a[-1] = qa.QK["mxfp4"]
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 0, P, None) == qa.SAGE_ERR_INVALID_ARG  # the dump is INT8 only
@@ -202,6 +205,9 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_attn(qk_quant=2) == qa.SAGE_ERR_NO_DEVICE
     assert _call_qk(qk_quant=3) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(qk_quant=3) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qk(qk_quant=4) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(qk_quant=4, delta_s=None) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qkv(qk_quant=4) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_qk(q_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(delta_s=P) == qa.SAGE_ERR_NO_DEVICE
@@ -259,7 +265,7 @@ GOOD_ATTN_VL = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean
                     H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90, D=64, is_causal=1, sm_scale=0.125,
                     pv_mode=0, qk_quant=0, stream=None)
 BAD_QK_VL = [dict(cu_q=None), dict(cu_k=P + 2), dict(B=0), dict(H_kv=3), dict(total_q=-1), dict(max_q=0),
-             dict(max_k=(1 << 20) + 1), dict(D=32), dict(dtype=3), dict(q=None), dict(k_i8=P + 1), dict(qk_quant=4)]
+             dict(max_k=(1 << 20) + 1), dict(D=32), dict(dtype=3), dict(q=None), dict(k_i8=P + 1), dict(qk_quant=5)]
 BAD_V_VL = [dict(cu_k=None), dict(v=P + 8), dict(max_k=0), dict(total_k=-3), dict(H_kv=0), dict(v_scale=None),
             dict(v_mean=P + 2)]
 BAD_ATTN_VL = [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P + 1), dict(is_causal=3), dict(pv_mode=5), dict(qk_quant=7),

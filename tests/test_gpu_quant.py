@@ -103,6 +103,8 @@ FUSED_CASES = [
     (synth.custom(2, 4, 130, 128, layout="NHD", Hkv=2, q_bias_sigma=3.0, seed=1407), "mxfp4", True, True),
     (synth.custom(2, 4, 300, 64, Hkv=2, token_norm=True, seed=1408), "int8_token", True, False),
     (synth.custom(1, 2, 129, 128, dtype="bf16", layout="NHD", q_bias_sigma=3.0, seed=1409), "int8_token", False, True),
+    (synth.custom(2, 4, 300, 64, Hkv=2, token_norm=True, seed=1410), "int8_head", True, False),
+    (synth.custom(1, 3, 1000, 128, dtype="bf16", layout="NHD", seed=1411), "int8_head", False, False),
 ]
 
 

@@ -244,3 +244,45 @@ def test_varlen_token_granularity(w):
     c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
     print(f"{w.name} token: cos={c:.6f} rel_l1={r:.2e}")
     assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[2]], ids=[SMALL[0].name, SMALL[2].name])
+def test_varlen_head_granularity(w):
+    """Packed batches with one scale per sequence-head: codes bit-exact, every
+    block slot of the sequence holding its head scale, output within the bars
+    of the oracle at the same granularity."""
+    import quantized_attention_02_amd as qa
+
+    (q, k, v, cq, ck), dev, cud = _inputs(w)
+    bufs, out = _run(w, True, "fp8", dev, cud, qk_quant="int8_head")
+    dt = O.DTYPES[w.dtype]
+    q8, qs = bufs.q_i8.cpu().numpy(), bufs.q_scale.cpu().numpy()
+    k8, ks = bufs.k_i8.cpu().numpy(), bufs.k_scale.cpu().numpy()
+    for b in range(w.B):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        rq, rk = qa.varlen_row0(q0, b, 32), qa.varlen_row0(k0, b, 128)
+        if q1 > q0:
+            for h in range(w.H):
+                rq8, rqs = O.quant_q_head(O.decode16(q[q0:q1, h], dt), int(q1 - q0))
+                assert np.array_equal(q8[h, rq:rq + q1 - q0], rq8), (b, h)
+                sl = qs[h, rq // 32:rq // 32 + (q1 - q0 + 31) // 32]
+                assert (sl.view(np.uint32) == rqs.view(np.uint32)[0]).all(), (b, h)
+        if k1 > k0:
+            for h in range(w.Hkv):
+                rk8, rks, _ = O.quant_k_head(O.decode16(k[k0:k1, h], dt), int(k1 - k0), True)
+                assert np.array_equal(k8[h, rk:rk + k1 - k0], rk8), (b, h)
+                sl = ks[h, rk // 64:rk // 64 + 2 * ((k1 - k0 + 127) // 128)]
+                assert (sl.view(np.uint32) == rks.view(np.uint32)[0]).all(), (b, h)
+    got = O.decode16(G.to_u16(out), dt)
+    ref = O.attn_varlen(q, k, v, cq, ck, dt, is_causal=True, tile_k=G.TILE_K["fp8"], gran="head")
+    g_all, r_all = [], []
+    for b in range(w.B):
+        if ck[b + 1] == ck[b]:
+            continue
+        for h in range(w.H):
+            g_all.append(got[cq[b]:cq[b + 1], h])
+            r_all.append(ref[(b, h)])
+    g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
+    c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
+    print(f"{w.name} head: cos={c:.6f} rel_l1={r:.2e}")
+    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
