@@ -2,8 +2,8 @@
 
 Each case draws batch, heads (grouped or not), a sequence length from 1 to 700
 (most not a multiple of any tile), head dimension, layout, input dtype,
-causality, pv mode, Q/K format (INT8 per block / per lane / per token, MXFP4)
-and the V / Q smoothing switches, so that options are crossed in combinations
+causality, pv mode, Q/K format (INT8 per block / per lane / per token / per
+head, MXFP4) and the V / Q smoothing switches, so that options are crossed in combinations
 the targeted tests do not list.  Every row of every head is compared with the
 oracle run with the same options, at the attention bars (cosine >= 0.999, mean
 relative L1 <= 1e-2).
@@ -19,7 +19,7 @@ import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 COS_MIN, REL_L1_MAX = 0.999, 1e-2
-GRAN = {"int8": "block", "int8_lane": "lane", "int8_token": "token", "mxfp4": "block"}
+GRAN = {"int8": "block", "int8_lane": "lane", "int8_token": "token", "int8_head": "head", "mxfp4": "block"}
 
 
 def _draw(i):
@@ -42,7 +42,13 @@ def _draw(i):
     return w, causal, pv, qk, smooth_v, smooth_q
 
 
-CASES = [_draw(i) for i in range(16)]
+def _draw_head(i):
+    """Per-head scales (not combined with smoothed Q), other options drawn."""
+    w, causal, pv, _, smooth_v, _ = _draw(100 + i)
+    return w, causal, pv, "int8_head", smooth_v, False
+
+
+CASES = [_draw(i) for i in range(16)] + [_draw_head(i) for i in range(4)]
 
 
 def _id(c):
