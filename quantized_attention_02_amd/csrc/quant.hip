@@ -499,7 +499,8 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
 // INT8 quantisation of one 32-token block of Q: one scale for the block, or
 // (LANE) one scale per token -- the query a lane column holds in the 32 x 32
 // INT8 MFMA layout of the attention kernel (per-token granularity of Q and K
-// uses the same Q pass).
+// uses the same Q pass) -- or (HEAD) the head's one scale, from the abs-max
+// that the per-head reduction left in the block's slot.
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool LANE, bool HEAD = false>
 __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
@@ -635,7 +636,8 @@ __global__ __launch_bounds__(kThreads) void k_kmean(const QuantQKArgs a) { kmean
 // the block (QK 0), or (QK 1, LANE) one per 16-key lane group -- the keys one
 // half of a wavefront holds of each 32-key sub-tile in the attention kernel's
 // 32 x 32 MFMA result, group 2 * (n / 32) + bit 2 of n (4 groups per block) --
-// or (QK 3, TOKEN) one per token.
+// or (QK 3, TOKEN) one per token, or (QK 4, HEAD) the head's one scale, from
+// the abs-max that the mean pass left in the block's slot.
 // ---------------------------------------------------------------------------
 __device__ inline int lane_group_in_block(int row) { return 2 * (row >> 5) + ((row >> 2) & 1); }
 
