@@ -53,6 +53,31 @@ def test_longest_sequence(causal, pv):
     assert bufs.k_scale.cpu().numpy()[0, 0, MAX_S // 64 - 1].view(np.uint32) == ks[-1].view(np.uint32)
 
 
+@pytest.mark.parametrize("qk,gran", [("int8_token", "token"), ("int8_head", "head")])
+def test_longest_sequence_token_and_head_scales(qk, gran):
+    """One head of SAGE_MAX_S tokens with per-token and per-head scales: the
+    per-key scale copies and the per-head slot writes reach their largest
+    offsets (sampled output rows; scales of the last blocks bit for bit)."""
+    w = synth.custom(1, 1, MAX_S, 128, seed=1321)
+    bufs, out, _ = G.run(w, causal=False, pv="fp8", qk_quant=qk)
+    got = G.out_logical(out, w)
+    rows = np.unique(np.concatenate([G.sample_rows(MAX_S, 6, seed=1322), [MAX_S - 1]])).astype(np.int32)
+    q, k, v = G.inputs(w)
+    ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, pv_mode=O.PV_FP8, heads=[(0, 0)], rows=rows,
+                 tile_k=G.TILE_K["fp8"], gran=gran)[(0, 0)]
+    g = got[0, 0, rows]
+    c, r = G.cos(g, ref), G.rel_l1(g, ref)
+    print(f"{qk} S={MAX_S}: cos={c:.6f} rel_l1={r:.2e}")
+    assert np.isfinite(g).all() and c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    dt = O.DTYPES[w.dtype]
+    blk = 1 if gran == "token" else MAX_S
+    _, qs = O.quant_q_head(O.decode16(O.head(q, w.layout, 0, 0), dt), blk)
+    _, ks, _ = O.quant_k_head(O.decode16(O.head(k, w.layout, 0, 0), dt), blk, True)
+    gq, gk = bufs.q_scale.cpu().numpy()[0, 0], bufs.k_scale.cpu().numpy()[0, 0]
+    assert gq[-1].view(np.uint32) == qs[-1].view(np.uint32) and gk[-1].view(np.uint32) == ks[-1].view(np.uint32)
+    assert gq[0].view(np.uint32) == qs[0].view(np.uint32) and gk[0].view(np.uint32) == ks[0].view(np.uint32)
+
+
 def test_most_heads():
     """B * H = SAGE_MAX_BH with a ragged 33-token sequence (NHD, grouped K/V)."""
     w = synth.custom(256, 256, 33, 64, layout="NHD", Hkv=64, seed=1311)
