@@ -207,3 +207,50 @@ def test_pv_accum_dtype_selects_the_pv_mode():
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), name
     with pytest.raises(ValueError):
         qa.sageattn(q, k, v, pv_accum_dtype="fp16")
+
+
+@pytest.mark.parametrize("case", ["constant_k", "zero_q", "all_zero"])
+@pytest.mark.parametrize("causal,pv", [(False, "fp8"), (True, "fp8"), (True, "fp16")])
+def test_attn_degenerate_inputs(case, causal, pv):
+    """Inputs the method makes degenerate: K equal for every token (K - k_mean
+    is 0, so every K scale is 0), an all-zero Q (scale 0), and all-zero Q, K
+    and V.  Every score is then 0: the output is the plain mean of the visible
+    V rows (the quantised V rows in pv fp8 mode), finite, matching the oracle;
+    all-zero inputs give exact zeros."""
+    w = synth.custom(1, 2, 200, 64, seed=1701)
+    q, k, v = (x.copy() for x in G.inputs(w))
+    if case == "constant_k":
+        k[:] = k[:, :, :1, :]  # HND: token 0's K for every token
+    elif case == "zero_q":
+        q[:] = 0
+    else:
+        q[:] = 0
+        k[:] = 0
+        v[:] = 0
+    import torch
+
+    import quantized_attention_02_amd as qa
+
+    qd, kd, vd = (G.to_device(x, w.dtype) for x in (q, k, v))
+    bufs = qa.quantize(qd, kd, vd, w.layout, pv)
+    out = torch.empty_like(qd)
+    qa.attn_fwd(bufs, vd, out, w.layout, causal, None, pv)
+    torch.cuda.synchronize()
+    got = G.out_logical(out, w)
+    assert np.isfinite(got).all()
+    if case == "constant_k":
+        assert not bufs.k_i8.any() and not bufs.k_scale.any()
+    if case == "all_zero":
+        assert not got.any()
+        return
+    ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal,
+                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, tile_k=G.TILE_K[pv])
+    ref = np.stack([ref[(0, h)] for h in range(w.H)])[None]
+    c, r = G.cos(got, ref), G.rel_l1(got, ref)
+    print(f"{case} causal={causal} pv={pv}: cos={c:.6f} rel_l1={r:.2e}")
+    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    if pv == "fp16":  # uniform weights over the visible keys: the (prefix) mean of V
+        vf = O.decode16(v, O.DTYPES[w.dtype])[0].astype(np.float64)  # [H, S, D]
+        n = np.arange(1, w.S + 1)[:, None] if causal else w.S
+        mean = (np.cumsum(vf, axis=1) / n) if causal else np.broadcast_to(vf.mean(axis=1, keepdims=True), vf.shape)
+        assert G.rel_l1(got[0], mean) < 2e-3
