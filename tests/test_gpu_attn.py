@@ -254,3 +254,23 @@ def test_attn_degenerate_inputs(case, causal, pv):
         n = np.arange(1, w.S + 1)[:, None] if causal else w.S
         mean = (np.cumsum(vf, axis=1) / n) if causal else np.broadcast_to(vf.mean(axis=1, keepdims=True), vf.shape)
         assert G.rel_l1(got[0], mean) < 2e-3
+
+
+def test_runs_on_the_callers_stream():
+    """Every entry point enqueues on the stream it is given: the whole path run
+    under a side stream (torch's current stream, passed through the C ABI)
+    gives the same bits as on the default stream."""
+    import torch
+
+    import quantized_attention_02_amd as qa
+
+    w = synth.custom(2, 4, 300, 128, Hkv=2, seed=1711)
+    _, out0, _ = G.run(w, causal=True, pv="fp8", smooth_q=True)
+    s = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s):
+        qd, kd, vd = (G.to_device(x, w.dtype) for x in G.inputs(w))
+        bufs = qa.quantize(qd, kd, vd, w.layout, "fp8", smooth_q=True)
+        out = torch.empty_like(qd)
+        qa.attn_fwd(bufs, vd, out, w.layout, True, None, "fp8")
+    s.synchronize()
+    assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
