@@ -425,6 +425,13 @@ k_attn(const AttnArgs a) {
       bh = xcd * heads_per_xcd + idx / a.nmblk;
       mrank = idx % a.nmblk;
     }
+  } else if (!a.varlen && !CAUSAL && ((nbh * a.nmblk) & 7) == 0) {
+    // heads not a multiple of 8: XCD x takes the x-th eighth of the (head,
+    // block) order, so that a head's work-groups share one or two L2s instead
+    // of all eight
+    const int flat = (wg & 7) * ((nbh * a.nmblk) >> 3) + (wg >> 3);
+    bh = flat / a.nmblk;
+    mrank = flat % a.nmblk;
   } else if (CAUSAL) {
     bh = wg % nbh;
     mrank = wg / nbh;
