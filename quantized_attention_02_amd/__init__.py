@@ -238,6 +238,7 @@ class Quantized:
         self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.smooth_v = False  # set by quantize: whether v_fp8 holds V minus v_mean
         self.smooth_q = False  # set by quantize: whether q_i8 holds Q minus its block means
+        self.v_quantized = False  # set by quantize: whether v_fp8 / v_scale hold this V (pv fp8)
         self.q_mean = self.delta_s = None  # smoothed Q: allocated on first use
         self._device = device
 
@@ -285,6 +286,7 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         bufs.delta_s = torch.empty((B, H, sk // KV_PAD, nq, KV_PAD), dtype=torch.float32, device=q.device)
     bufs.smooth_q = bool(smooth_q)
     bufs.smooth_v = bool(smooth_v)
+    bufs.v_quantized = pv_mode == "fp8"
     qm = bufs.q_mean.data_ptr() if smooth_q else None
     vm = bufs.v_mean.data_ptr() if smooth_v else None
     if pv_mode == "fp8" and fused:
@@ -318,6 +320,8 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     dt = _dtype_code(out)
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
     pv = PV[pv_mode]
+    if pv == 0 and not bufs.v_quantized:
+        raise ValueError("pv fp8 reads the FP8 V codes: quantize these buffers with pv_mode='fp8' first")
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None
     vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
@@ -334,11 +338,12 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     return out
 
 
-# pv_accum_dtype names of the P V accumulation -> pv mode.  The FP8 P V product's
-# two accumulation levels are the MFMA's internal sum and the fp32 output
-# registers, so "fp32+fp16" and "fp32+fp32" select the same kernel; "fp32" is
-# the fp16 P V product with fp32 accumulation.
-PV_ACCUM = {"fp32+fp32": "fp8", "fp32+fp16": "fp8", "fp32": "fp16"}
+# pv_accum_dtype names of the P V accumulation -> pv mode.  "fp32+fp32" is the
+# FP8 P V product whose two accumulation levels (the MFMA's internal sum of a
+# tile's products, then the fp32 output registers) are both fp32-class; "fp32"
+# is the fp16 P V product with fp32 accumulation.  "fp32+fp16" (an fp16 inner
+# accumulator) is not built and is rejected rather than silently replaced.
+PV_ACCUM = {"fp32+fp32": "fp8", "fp32": "fp16"}
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8", qk_quant="int8",
@@ -349,7 +354,8 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mo
 
     if pv_accum_dtype is not None:
         if pv_accum_dtype not in PV_ACCUM:
-            raise ValueError(f"pv_accum_dtype must be one of {sorted(PV_ACCUM)}")
+            raise ValueError(f"pv_accum_dtype must be one of {sorted(PV_ACCUM)} (an fp16 inner accumulator, "
+                             f"'fp32+fp16', is not built), got {pv_accum_dtype!r}")
         pv_mode = PV_ACCUM[pv_accum_dtype]
     bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q)
     out = torch.empty_like(q)
@@ -395,6 +401,7 @@ class QuantizedVarlen:
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.smooth_v = False
+        self.v_quantized = False
 
 
 def _cu(t, name):
@@ -423,6 +430,8 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     (total_q, H, D), (total_k, H_kv, _) = q.shape, k.shape
     if H_kv < 1 or H % H_kv:
         raise ValueError(f"the number of query heads ({H}) must be a multiple of the K/V heads ({H_kv})")
+    if smooth_v and pv_mode != "fp8":
+        raise ValueError("smooth_v applies to pv_mode='fp8' only")
     dt = _dtype_code(q)
     bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device, qk_quant)
     if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D, bufs.qk) != \
@@ -435,9 +444,8 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                        bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                        bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
            "sage_smooth_quant_qk_varlen")
-    if smooth_v and pv_mode != "fp8":
-        raise ValueError("smooth_v applies to pv_mode='fp8' only")
     bufs.smooth_v = bool(smooth_v)
+    bufs.v_quantized = pv_mode == "fp8"
     if pv_mode == "fp8":
         _check(sage_quant_v_varlen(v.data_ptr(), dt, ck.data_ptr(), B, H_kv, total_k, bufs.max_seqlen_k, D,
                                    bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
@@ -455,6 +463,8 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
         raise ValueError("pv fp16 reads the original V: it must be a contiguous [total_k, H_kv, D] tensor")
     cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
     pv = PV[pv_mode]
+    if pv == 0 and not bufs.v_quantized:
+        raise ValueError("pv fp8 reads the FP8 V codes: quantize these buffers with pv_mode='fp8' first")
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
     vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
     vs = bufs.v_scale.data_ptr() if pv == 0 else None

@@ -6,7 +6,8 @@ buffers run to hundreds of MB, the key loop to 8192 tiles and the grids to
 hundreds of thousands of work-groups, so 64-bit offsets, buffer ranges and
 grid decompositions all reach their largest values.  Sampled output rows (and
 heads) are compared with the oracle at the attention bars (cosine >= 0.999,
-mean relative L1 <= 1e-2); codes and scales of sampled blocks bit for bit.
+mean relative L1 <= 1e-2, worst row >= 0.99), every output element is checked
+to be written and finite; codes and scales of sampled blocks bit for bit.
 """
 import numpy as np
 import pytest
@@ -18,7 +19,7 @@ import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-COS_MIN, REL_L1_MAX = 0.999, 1e-2
+COS_MIN, REL_L1_MAX = G.COS_MIN, G.REL_L1_MAX
 MAX_S = 1 << 20  # SAGE_MAX_S (checked against the header in test_abi)
 MAX_BH = 1 << 16  # SAGE_MAX_BH
 
@@ -28,10 +29,7 @@ def _check_rows(w, got, b, h, rows, causal, pv):
     ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, is_causal=causal,
                  pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=[(b, h)], rows=rows,
                  tile_k=G.TILE_K[pv])[(b, h)]
-    g = got[b, h, rows]
-    c, r = G.cos(g, ref), G.rel_l1(g, ref)
-    print(f"{w.name} head {(b, h)} causal={causal} pv={pv} rows {len(rows)}: cos={c:.6f} rel_l1={r:.2e}")
-    assert np.isfinite(g).all() and c >= COS_MIN and r <= REL_L1_MAX, ((b, h), c, r)
+    G.assert_parity(got[b, h, rows], ref, f"{w.name} head {(b, h)} causal={causal} pv={pv} rows {len(rows)}")
 
 
 @pytest.mark.parametrize("causal,pv", [(False, "fp8"), (True, "fp16")])
@@ -40,6 +38,7 @@ def test_longest_sequence(causal, pv):
     w = synth.custom(1, 1, MAX_S, 128, seed=1301)
     bufs, out, _ = G.run(w, causal=causal, pv=pv)
     got = G.out_logical(out, w)
+    assert np.isfinite(got).all()  # every element written (the buffer starts as NaN)
     rows = np.unique(np.concatenate([G.sample_rows(MAX_S, 8, seed=1302), [MAX_S // 3, MAX_S - 129, MAX_S - 1]]))
     _check_rows(w, got, 0, 0, rows.astype(np.int32), causal, pv)
     # codes of the last Q and K blocks (their buffer offsets are the largest)
@@ -65,10 +64,8 @@ def test_longest_sequence_token_and_head_scales(qk, gran):
     q, k, v = G.inputs(w)
     ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, pv_mode=O.PV_FP8, heads=[(0, 0)], rows=rows,
                  tile_k=G.TILE_K["fp8"], gran=gran)[(0, 0)]
-    g = got[0, 0, rows]
-    c, r = G.cos(g, ref), G.rel_l1(g, ref)
-    print(f"{qk} S={MAX_S}: cos={c:.6f} rel_l1={r:.2e}")
-    assert np.isfinite(g).all() and c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    assert np.isfinite(got).all()
+    G.assert_parity(got[0, 0, rows], ref, f"{qk} S={MAX_S}")
     dt = O.DTYPES[w.dtype]
     blk = 1 if gran == "token" else MAX_S
     _, qs = O.quant_q_head(O.decode16(O.head(q, w.layout, 0, 0), dt), blk)
@@ -84,6 +81,7 @@ def test_most_heads():
     assert w.B * w.H == MAX_BH
     _, out, _ = G.run(w, causal=True, pv="fp8")
     got = G.out_logical(out, w)
+    assert np.isfinite(got).all()  # every element written (the buffer starts as NaN)
     rows = np.arange(33, dtype=np.int32)
     for (b, h) in ((0, 0), (255, 255), (128, 77), (17, 200)):
         _check_rows(w, got, b, h, rows, True, "fp8")

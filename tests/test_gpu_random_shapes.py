@@ -18,7 +18,7 @@ import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-COS_MIN, REL_L1_MAX = 0.999, 1e-2
+COS_MIN, REL_L1_MAX = G.COS_MIN, G.REL_L1_MAX
 GRAN = {"int8": "block", "int8_lane": "lane", "int8_token": "token", "int8_head": "head", "mxfp4": "block"}
 
 
@@ -68,6 +68,4 @@ def test_random_shape_matches_oracle(case):
                  qk_format="fp4" if qk == "mxfp4" else "int8", smooth_v=smooth_v, smooth_q=smooth_q)
     ref = np.stack([np.stack([ref[(b, h)] for h in range(w.H)]) for b in range(w.B)])
     assert np.isfinite(got).all()
-    c, r = G.cos(got, ref), G.rel_l1(got, ref)
-    print(f"cos={c:.6f} rel_l1={r:.2e}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(got, ref, f"random shape")

@@ -16,7 +16,7 @@ import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-COS_MIN, REL_L1_MAX = 0.999, 1e-2
+COS_MIN, REL_L1_MAX = G.COS_MIN, G.REL_L1_MAX
 W = synth.WORKLOADS
 
 QUANT_CASES = [
@@ -77,9 +77,7 @@ def test_token_attn_matches_oracle(w, causal, pv):
                  pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, tile_k=G.TILE_K[pv], gran="token")
     ref = np.stack([np.stack([ref[(b, h)] for h in range(w.H)]) for b in range(w.B)])
     assert np.isfinite(got).all()
-    c, r = G.cos(got, ref), G.rel_l1(got, ref)
-    print(f"{w.name} causal={causal} pv={pv} token: cos={c:.6f} rel_l1={r:.2e}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(got, ref, f"{w.name} causal={causal} pv={pv} token")
 
 
 def test_token_zero_query_row():
@@ -93,7 +91,7 @@ def test_token_zero_query_row():
 
     qd, kd, vd = (G.to_device(x, w.dtype) for x in (q, k, v))
     bufs = qa.quantize(qd, kd, vd, w.layout, "fp8", qk_quant="int8_token")
-    out = torch.empty_like(qd)
+    out = G.nan_like(qd)
     qa.attn_fwd(bufs, vd, out, w.layout, True, None, "fp8")
     torch.cuda.synchronize()
     got = G.out_logical(out, w)
@@ -101,9 +99,7 @@ def test_token_zero_query_row():
     ref = np.stack([ref[(0, h)] for h in range(w.H)])[None]
     assert np.isfinite(got).all()
     assert not bufs.q_scale.cpu().numpy()[0, :, 37].any()
-    c, r = G.cos(got, ref), G.rel_l1(got, ref)
-    print(f"zero query row: cos={c:.6f} rel_l1={r:.2e}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(got, ref, f"zero query row")
 
 
 def test_token_qk_int32_dump_bit_exact():
@@ -128,12 +124,11 @@ def test_token_full_size_sampled():
     assert np.isfinite(got).all()
     q, k, v = G.inputs(w)
     for (b, h) in ((0, 0), (1, 31), (1, 10)):
-        rows = G.sample_rows(w.S, 24, seed=b * 100 + h)
+        # every row of the first head, sampled rows of the others
+        rows = np.arange(w.S, dtype=np.int32) if (b, h) == (0, 0) else G.sample_rows(w.S, 24, seed=b * 100 + h)
         ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, heads=[(b, h)], rows=rows, gran="token")[(b, h)]
         g = got[b, h, rows]
-        c, r = G.cos(g, ref), G.rel_l1(g, ref)
-        print(f"token {w.name} head {(b, h)}: cos={c:.6f} rel_l1={r:.2e}")
-        assert c >= COS_MIN and r <= REL_L1_MAX, ((b, h), c, r)
+        G.assert_parity(g, ref, f"token {w.name} head {(b, h)}")
 
 
 def test_token_closer_to_exact_on_varying_tokens():

@@ -16,7 +16,7 @@ import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-COS_MIN, REL_L1_MAX = 0.999, 1e-2
+COS_MIN, REL_L1_MAX = G.COS_MIN, G.REL_L1_MAX
 
 SMALL = [
     synth.varlen("vl_mixed_d64", 4, 2, 64, [200, 7, 64, 129, 1, 300], seed=801),
@@ -118,9 +118,7 @@ def test_varlen_attn_matches_oracle(w, causal, pv):
             g_all.append(g)
             r_all.append(ref[(b, h)])
     g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
-    c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
-    print(f"{w.name} causal={causal} pv={pv}: cos={c:.6f} rel_l1={r:.2e} worst_row_cos={G.row_cos_min(g_all, r_all):.5f}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(g_all, r_all, f"{w.name} causal={causal} pv={pv}")
 
 
 @pytest.mark.parametrize("causal,pv", [(False, "fp8"), (True, "fp8"), (True, "fp16")])
@@ -168,9 +166,7 @@ def test_varlen_full_size_sampled(pv):
                                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=[(b, h)], rows=rows,
                                 tile_k=G.TILE_K[pv])[(b, h)]
             g = got[cq[b] + rows, h]
-            c, r = G.cos(g, ref), G.rel_l1(g, ref)
-            print(f"{w.name} seq {b} (S={S}) head {h}: cos={c:.6f} rel_l1={r:.2e}")
-            assert c >= COS_MIN and r <= REL_L1_MAX, (b, h, c, r)
+            G.assert_parity(g, ref, f"{w.name} seq {b} (S={S}) head {h}")
 
 
 @pytest.mark.parametrize("w", [SMALL[2], SMALL[4]], ids=[SMALL[2].name, SMALL[4].name])
@@ -202,9 +198,7 @@ def test_varlen_lane_granularity(w):
             g_all.append(got[cq[b]:cq[b + 1], h])
             r_all.append(ref[(b, h)])
     g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
-    c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
-    print(f"{w.name} lane: cos={c:.6f} rel_l1={r:.2e}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(g_all, r_all, f"{w.name} lane")
 
 
 @pytest.mark.parametrize("w", [SMALL[2], SMALL[4]], ids=[SMALL[2].name, SMALL[4].name])
@@ -241,9 +235,7 @@ def test_varlen_token_granularity(w):
             g_all.append(got[cq[b]:cq[b + 1], h])
             r_all.append(ref[(b, h)])
     g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
-    c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
-    print(f"{w.name} token: cos={c:.6f} rel_l1={r:.2e}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(g_all, r_all, f"{w.name} token")
 
 
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[2]], ids=[SMALL[0].name, SMALL[2].name])
@@ -283,6 +275,4 @@ def test_varlen_head_granularity(w):
             g_all.append(got[cq[b]:cq[b + 1], h])
             r_all.append(ref[(b, h)])
     g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
-    c, r = G.cos(g_all, r_all), G.rel_l1(g_all, r_all)
-    print(f"{w.name} head: cos={c:.6f} rel_l1={r:.2e}")
-    assert c >= COS_MIN and r <= REL_L1_MAX, (c, r)
+    G.assert_parity(g_all, r_all, f"{w.name} head")
