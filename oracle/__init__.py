@@ -26,7 +26,7 @@ _SRC = os.path.join(_HERE, "sage_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
 F16, BF16 = 0, 1
-PV_FP8, PV_FP16 = 0, 1
+PV_FP8, PV_FP16, PV_FP4 = 0, 1, 2
 # Method parameters used by default: INT8 scale blocks of 32 Q tokens and 64 K
 # tokens, online-softmax tiles of 128 keys.
 BLK_Q, BLK_K, TILE_K = 32, 64, 128
@@ -70,10 +70,13 @@ def lib():
                      "orc_channel_mean", "orc_quant_q_head", "orc_quant_k_head", "orc_quant_k_head_lane",
                      "orc_quant_v_head", "orc_quant_v_head_smooth", "orc_qk_int32_head", "orc_attn_head_rows",
                      "orc_attn_exact_head", "orc_mxfp4_quant_rows", "orc_quant_k_head_mxfp4", "orc_qk_mxfp4_rows",
-                     "orc_quant_q_head_smooth", "orc_qk_delta_head"):
+                     "orc_quant_q_head_smooth", "orc_qk_delta_head", "orc_quant_q_head_mxfp4_smooth",
+                     "orc_quant_v_head_mxfp4"):
             getattr(L, name).restype = None
         L.orc_lane_group.restype = ctypes.c_int
         L.orc_lane_group.argtypes = [ctypes.c_int]
+        L.orc_pv_group.restype = ctypes.c_int
+        L.orc_pv_group.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -207,13 +210,15 @@ def quant_q_head_smooth(qf: np.ndarray, blk: int, blk_scale: int | None = None):
     return codes, scales, qmean
 
 
-def qk_delta_head(qmean: np.ndarray, kc: np.ndarray) -> np.ndarray:
-    """delta[b][n] = qmean[b] . kc[n] (binary64, rounded to fp32); kc = K - k_mean."""
-    qmean, kc = _f32(qmean), _f32(kc)
+def qk_delta_head(qmean: np.ndarray, kf: np.ndarray, kmean: np.ndarray) -> np.ndarray:
+    """delta[b][n] = qmean[b] . (K[n] - k_mean) (the subtraction in fp32, the dot
+    product in binary64, rounded to fp32)."""
+    qmean, kf, kmean = _f32(qmean), _f32(kf), _f32(kmean)
     nb, D = qmean.shape
-    S = kc.shape[0]
+    S = kf.shape[0]
     out = np.empty((nb, S), np.float32)
-    lib().orc_qk_delta_head(_p(qmean, ctypes.c_float), nb, _p(kc, ctypes.c_float), S, D, _p(out, ctypes.c_float))
+    lib().orc_qk_delta_head(_p(qmean, ctypes.c_float), nb, _p(kf, ctypes.c_float), _p(kmean, ctypes.c_float), S, D,
+                            _p(out, ctypes.c_float))
     return out
 
 
@@ -252,6 +257,37 @@ def quant_mxfp4_rows(xf: np.ndarray):
     e8m0 = np.empty((S, D // 32), np.uint8)
     lib().orc_mxfp4_quant_rows(_p(xf, ctypes.c_float), S, D, _p(codes, ctypes.c_uint8), _p(e8m0, ctypes.c_uint8))
     return codes, e8m0
+
+
+def quant_q_head_mxfp4_smooth(qf: np.ndarray, blk: int = BLK_Q):
+    """Smoothed Q for the FP4 product: (codes, e8m0, block means [nb, D]) of Q minus
+    each blk-token block's channel means."""
+    qf = _f32(qf)
+    S, D = qf.shape
+    codes = np.empty((S, D), np.uint8)
+    e8m0 = np.empty((S, D // 32), np.uint8)
+    qmean = np.empty(((S + blk - 1) // blk, D), np.float32)
+    lib().orc_quant_q_head_mxfp4_smooth(_p(qf, ctypes.c_float), S, D, blk, _p(codes, ctypes.c_uint8),
+                                        _p(e8m0, ctypes.c_uint8), _p(qmean, ctypes.c_float))
+    return codes, e8m0, qmean
+
+
+def pv_group(n: int) -> int:
+    """Key group of key n in the micro-scaled FP4 P~ V product (see sage_oracle.c)."""
+    return int(lib().orc_pv_group(int(n)))
+
+
+def quant_v_head_mxfp4(vf: np.ndarray, smooth: bool = False):
+    """V for the FP4 P~ V product: (E2M1 codes [S, D], E8M0 scales [2 ceil(S/64), D],
+    channel means [D] -- zeros unless smooth)."""
+    vf = _f32(vf)
+    S, D = vf.shape
+    codes = np.empty((S, D), np.uint8)
+    e8m0 = np.empty((2 * ((S + 63) // 64), D), np.uint8)
+    mean = np.empty(D, np.float32)
+    lib().orc_quant_v_head_mxfp4(_p(vf, ctypes.c_float), S, D, int(smooth), _p(codes, ctypes.c_uint8),
+                                 _p(e8m0, ctypes.c_uint8), _p(mean, ctypes.c_float))
+    return codes, e8m0, mean
 
 
 def quant_k_head_mxfp4(kf: np.ndarray, smooth: bool = True):
@@ -305,14 +341,15 @@ def qk_int32_head(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
 
 def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_causal, sm_scale,
                    pv_mode, rows=None, blk_q=32, blk_k=64, tile_k=TILE_K, k_lane=False, v_mean=None,
-                   qk=None, delta=None, blk_d=BLK_Q) -> np.ndarray:
+                   qk=None, delta=None, blk_d=BLK_Q, v_e8m0=None) -> np.ndarray:
     """Quantized attention for the given query rows of one head (fp32 [len(rows), D]).
 
     blk_q / blk_k: tokens per INT8 scale of Q / K (k_lane: K scales per lane group
     instead of blocks, as quant_k_head_lane makes them); tile_k: keys per online-softmax
     tile (the two-level accumulation folds once per tile).  The query rows (q8)
     and the keys (k8, v8, vf) may differ in number.  qk: fp32 Q K^T of the FP4
-    product for these rows (qk_mxfp4_rows); then q8 .. k_scale are not used."""
+    product for these rows (qk_mxfp4_rows); then q8 .. k_scale are not used.
+    pv fp4: v8 holds V's E2M1 codes and v_e8m0 its scales (quant_v_head_mxfp4)."""
     Sq, D = q8.shape
     S = k8.shape[0]  # keys
     rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
@@ -327,8 +364,12 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
     v_scale = _f32(v_scale if v_scale is not None else np.zeros(D, np.float32))
     vf = _f32(vf if vf is not None else np.zeros((S, D), np.float32))
     vm = None if v_mean is None else _f32(v_mean)
-    if vm is not None and pv_mode != PV_FP8:
-        raise ValueError("V smoothing applies to the FP8 PV product only")
+    if vm is not None and pv_mode == PV_FP16:
+        raise ValueError("V smoothing applies to the FP8 and FP4 PV products only")
+    if pv_mode == PV_FP4 and tile_k % 64:
+        raise ValueError("pv fp4 needs tiles of a multiple of 64 keys")
+    ve = np.ascontiguousarray(v_e8m0 if v_e8m0 is not None else np.zeros((2 * ((S + 63) // 64), D), np.uint8),
+                              np.uint8)
     dl = None
     if delta is not None:  # smoothed Q: [ceil(Sq / blk_q), S] fp32, the pre-processing stage
         dl = _f32(delta)
@@ -341,7 +382,7 @@ def attn_head_rows(q8, q_scale, k8, k_scale, v8, v_scale, vf, *, in_dtype, is_ca
             raise ValueError("qk must be [len(rows), S_k]")
     lib().orc_attn_head_rows(_p(q8, ctypes.c_int8), _p(q_scale, ctypes.c_float), blk_q,
                              _p(k8, ctypes.c_int8), _p(k_scale, ctypes.c_float), blk_k, int(bool(k_lane)), tile_k,
-                             _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float),
+                             _p(v8, ctypes.c_uint8), _p(v_scale, ctypes.c_float), _p(ve, ctypes.c_uint8),
                              None if vm is None else _p(vm, ctypes.c_float), _p(vf, ctypes.c_float),
                              in_dtype, S, D, int(bool(is_causal)), ctypes.c_float(sm_scale), pv_mode,
                              _p(rows, ctypes.c_int), rows.size, None if qkr is None else _p(qkr, ctypes.c_float),
@@ -425,8 +466,10 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
     qk_format "fp4": Q and K - mean in MXFP4 (E2M1 with an E8M0 scale per 32
     channels of a token) instead of INT8 blocks; gran is then not used.
 
-    smooth_v (pv fp8 only): V minus its channel mean is quantised, and the mean
-    is added back to the output.
+    smooth_v (pv fp8 and fp4): V minus its channel mean is quantised, and the
+    mean is added back to the output.
+
+    pv_mode PV_FP4: P~ and V in MXFP4 (scales per 32-key group of pv_group).
 
     gran: "block" (blk_q / blk_k tokens per scale), "lane" (thread-level: one
     scale per Q token, one per 16-key lane group of K), "token" (one scale per
@@ -456,9 +499,8 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
         bq, bk = (max(qf.shape[0], 1), max(kf.shape[0], 1)) if gran == "head" else (blk_q, blk_k)
         qk = None
         if qk_format == "fp4":
-            if smooth_q:  # Q minus its 32-token block means (one fp32 subtraction), then the MXFP4 rule
-                _, _, qm = quant_q_head_smooth(qf, BLK_Q)
-                q4, qe = quant_mxfp4_rows((qf - np.repeat(qm, BLK_Q, axis=0)[:qf.shape[0]]).astype(np.float32))
+            if smooth_q:  # Q minus its 32-token block means, then the MXFP4 rule
+                q4, qe, qm = quant_q_head_mxfp4_smooth(qf, BLK_Q)
             else:
                 q4, qe = quant_mxfp4_rows(qf)
             k4, ke, km = quant_k_head_mxfp4(kf, smooth)
@@ -473,18 +515,22 @@ def attn(q, k, v, dtype: int, layout: str, *, is_causal=False, sm_scale=None, pv
             k8, ks, km = quant_k_head_lane(kf, smooth) if lane else quant_k_head(kf, bk, smooth)
         else:
             raise ValueError(qk_format)
-        vm = None
+        vm, ve = None, None
         if pv_mode == PV_FP8 and smooth_v:
             v8, vs, vm = quant_v_head(vf, True)
         elif pv_mode == PV_FP8:
             v8, vs = quant_v_head(vf)
+        elif pv_mode == PV_FP4:
+            v8, ve, vm = quant_v_head_mxfp4(vf, smooth_v)
+            vs = None
+            if not smooth_v:
+                vm = None
         else:
             v8, vs = None, None
         res[(b, h)] = attn_head_rows(q8, qs, k8, ks, v8, vs, vf, in_dtype=dtype, is_causal=is_causal,
                                      sm_scale=sm_scale, pv_mode=pv_mode, rows=rows, blk_q=bq, blk_k=bk,
-                                     tile_k=tile_k, k_lane=lane, v_mean=vm, qk=qk,
-                                     delta=qk_delta_head(qm, (kf - km[None, :]).astype(np.float32)) if smooth_q
-                                     else None)
+                                     tile_k=tile_k, k_lane=lane, v_mean=vm, qk=qk, v_e8m0=ve,
+                                     delta=qk_delta_head(qm, kf, km) if smooth_q else None)
     return res
 
 

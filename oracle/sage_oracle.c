@@ -264,17 +264,23 @@ void orc_quant_q_head_smooth(const float *q, int S, int D, int blk, int blk_scal
 
 /*
  * The pre-processing stage of smoothed Q: delta[b][n] = fp32( sum_d qmean[b][d] * kc[n][d] )
- * in binary64, kc = K minus its channel mean (fp32 values, as orc_quant_k_head forms
- * them).  The attention adds delta[query block][n] * sm_scale to the dequantised score.
+ * in binary64, kc = K minus its channel mean kmean (one fp32 subtraction per element,
+ * as orc_quant_k_head forms it).  The attention adds delta[query block][n] * sm_scale
+ * to the dequantised score.
  */
-void orc_qk_delta_head(const float *qmean, int nb, const float *kc, int S, int D, float *delta) {
+void orc_qk_delta_head(const float *qmean, int nb, const float *k, const float *kmean, int S, int D,
+                       float *delta) {
+    size_t n = (size_t)S * D;
+    float *kc = (float *)malloc((n ? n : 1) * sizeof(float));
+    for (size_t i = 0; i < n; ++i) kc[i] = k[i] - kmean[i % D];
 #pragma omp parallel for schedule(static)
     for (int b = 0; b < nb; ++b)
-        for (int n = 0; n < S; ++n) {
+        for (int t = 0; t < S; ++t) {
             double acc = 0.0;
-            for (int d = 0; d < D; ++d) acc += (double)qmean[(size_t)b * D + d] * (double)kc[(size_t)n * D + d];
-            delta[(size_t)b * S + n] = (float)acc;
+            for (int d = 0; d < D; ++d) acc += (double)qmean[(size_t)b * D + d] * (double)kc[(size_t)t * D + d];
+            delta[(size_t)b * S + t] = (float)acc;
         }
+    free(kc);
 }
 
 /*
@@ -340,6 +346,18 @@ void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scale
  * E2M1(x / 2^e), which saturates the few values in (6, 8) * 2^e to 6 * 2^e.
  * codes: one E2M1 code per element (low 4 bits); e8m0: e + 127 per block.
  */
+static int mx_shared_exp(float amax) {
+    int e = -127;
+    if (amax > 0.0f) {
+        int fe;
+        frexp((double)amax, &fe); /* amax = m * 2^fe, m in [0.5, 1): floor(log2) = fe - 1 */
+        e = fe - 1 - 2;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+    }
+    return e;
+}
+
 void orc_mxfp4_quant_rows(const float *x, int S, int D, uint8_t *codes, uint8_t *e8m0) {
     int nb = D / 32;
     for (int t = 0; t < S; ++t)
@@ -348,14 +366,7 @@ void orc_mxfp4_quant_rows(const float *x, int S, int D, uint8_t *codes, uint8_t 
             float amax = 0.0f;
             for (int i = 0; i < 32; ++i)
                 if (fabsf(xb[i]) > amax) amax = fabsf(xb[i]);
-            int e = -127;
-            if (amax > 0.0f) {
-                int fe;
-                frexp((double)amax, &fe); /* amax = m * 2^fe, m in [0.5, 1): floor(log2) = fe - 1 */
-                e = fe - 1 - 2;
-                if (e < -127) e = -127;
-                if (e > 127) e = 127;
-            }
+            int e = mx_shared_exp(amax);
             e8m0[(size_t)t * nb + b] = (uint8_t)(e + 127);
             for (int i = 0; i < 32; ++i)
                 codes[(size_t)t * D + 32 * b + i] = orc_e2m1_encode((float)ldexp((double)xb[i], -e));
@@ -372,6 +383,66 @@ void orc_quant_k_head_mxfp4(const float *k, int S, int D, int smooth, uint8_t *c
     for (size_t i = 0; i < n; ++i) ks[i] = k[i] - mean[i % D];
     orc_mxfp4_quant_rows(ks, S, D, codes, e8m0);
     free(ks);
+}
+
+/*
+ * Smoothed Q for the FP4 product: the block means of orc_quant_q_head_smooth
+ * (blocks of `blk` tokens) are subtracted, one fp32 subtraction per element,
+ * and the result is quantised by the MXFP4 rule of orc_mxfp4_quant_rows.
+ */
+void orc_quant_q_head_mxfp4_smooth(const float *q, int S, int D, int blk, uint8_t *codes, uint8_t *e8m0,
+                                   float *qmean) {
+    size_t n = (size_t)S * D;
+    int nb = (S + blk - 1) / blk;
+    float *qs = (float *)malloc((n ? n : 1) * sizeof(float));
+    for (int b = 0; b < nb; ++b) {
+        int r0 = b * blk, r1 = r0 + blk < S ? r0 + blk : S;
+        orc_channel_mean(q + (size_t)r0 * D, r1 - r0, D, qmean + (size_t)b * D);
+        for (int t = r0; t < r1; ++t)
+            for (int d = 0; d < D; ++d) qs[(size_t)t * D + d] = q[(size_t)t * D + d] - qmean[(size_t)b * D + d];
+    }
+    orc_mxfp4_quant_rows(qs, S, D, codes, e8m0);
+    free(qs);
+}
+
+/*
+ * Key groups of the micro-scaled FP4 P~ V product.  The FP4 micro-scaling
+ * ([KAI, 2.2]; the full guide's 性能调优实战 section) shares one scale per 32
+ * elements along the contraction, which for P~ V runs over keys.  Reading: the
+ * 32 keys are those one lane of gfx950's 32 x 32 x 64 matrix core holds of a
+ * 64-key block -- the keys whose offset has bit 2 equal to the lane's half of
+ * the wavefront (the score layout of the Q K^T product leaves each lane exactly
+ * these) -- so group of key n = 2 * (n / 64) + bit 2 of n.
+ */
+int orc_pv_group(int n) { return 2 * (n >> 6) + ((n >> 2) & 1); }
+
+/*
+ * V for the FP4 P~ V product: optionally minus its channel mean (as
+ * orc_quant_v_head_smooth), then MXFP4 along the keys: each channel of each
+ * key group of orc_pv_group shares an E8M0 scale from the group's largest
+ * magnitude (the rule of orc_mxfp4_quant_rows); keys past S count as 0.
+ * codes [S][D] (one E2M1 code per byte), e8m0 [2 ceil(S / 64)][D], mean [D].
+ */
+void orc_quant_v_head_mxfp4(const float *v, int S, int D, int smooth, uint8_t *codes, uint8_t *e8m0,
+                            float *mean) {
+    size_t n = (size_t)S * D;
+    int ng = 2 * ((S + 63) / 64);
+    float *vs = (float *)malloc((n ? n : 1) * sizeof(float));
+    if (smooth) orc_channel_mean(v, S, D, mean);
+    else memset(mean, 0, (size_t)D * sizeof(float));
+    for (size_t i = 0; i < n; ++i) vs[i] = v[i] - mean[i % D];
+    for (int g = 0; g < ng; ++g)
+        for (int d = 0; d < D; ++d) {
+            float amax = 0.0f;
+            for (int t = 64 * (g / 2); t < S && t < 64 * (g / 2 + 1); ++t)
+                if (orc_pv_group(t) == g && fabsf(vs[(size_t)t * D + d]) > amax) amax = fabsf(vs[(size_t)t * D + d]);
+            int e = mx_shared_exp(amax);
+            e8m0[(size_t)g * D + d] = (uint8_t)(e + 127);
+            for (int t = 64 * (g / 2); t < S && t < 64 * (g / 2 + 1); ++t)
+                if (orc_pv_group(t) == g)
+                    codes[(size_t)t * D + d] = orc_e2m1_encode((float)ldexp((double)vs[(size_t)t * D + d], -e));
+        }
+    free(vs);
 }
 
 /*
@@ -452,24 +523,36 @@ void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t
  *           key n and query i count from the start of their sequences)
  *   m'    = max(m, max_n s_n);  alpha = exp(m - m') (0 on the first tile)
  *   p_n   = exp(s_n - m')                                            (fp32)
- *   l     = alpha * l + sum_n p_n                (uses the unquantised p_n)
+ *   P_n   = p_n rounded to the format of the P~ V product (below)
+ *   l     = alpha * l + sum_n P_n     (tile sum in binary64, rounded once to fp32)
+ * The softmax denominator sums the same rounded weights P_n that multiply V, so
+ * the normalised weights sum to one (the pages fix the fp32 online softmax and
+ * the P~ quantisation, not which of the two values the row sum adds up).
  * pv fp8 ([SA2, SageAttention2方法]: P~ to E4M3 with a static scale, V per channel;
  *         FP32 buffer for the two-level accumulation):
- *   P8_n  = E4M3(p_n * 448)                 (static scale 1/448: p = 1 -> 448)
- *   inner = sum_n dec(P8_n) * dec(v8_n,d)   (fresh per key tile, rounded once to fp32)
+ *   P_n   = dec(E4M3(p_n * 448))            (static scale 1/448: p = 1 -> 448)
+ *   inner = sum_n P_n * dec(v8_n,d)         (fresh per key tile, rounded once to fp32)
  *   O_d   = alpha * O_d + inner_d                                    (fp32 buffer)
- *   out   = O_d * (dv_d / (448 * l))  (+ v_mean_d when V was smoothed, v_mean != NULL)
+ *   out   = O_d * (dv_d / l)  (+ v_mean_d when V was smoothed, v_mean != NULL)
  * pv fp16 ([KAI, 2.1] sm80 row: INT8 QK^T, FP16 PV, fp32 accumulation):
  *   P_n   = fp16(p_n), V in fp16 (bf16 inputs rounded to fp16),
  *   O_d   = alpha * O_d + sum_n P_n * V_n,d;   out = O_d / l
- * `v` (fp32 values of the original V) is read only in pv fp16 mode; `v8`,
- * `v_scale` only in pv fp8 mode.  out is [nrows][D] fp32 (before the final
- * rounding to the input dtype).  A row that sees no key at all (S = 0) is 0.
+ * pv fp4 (micro-scaled FP4 P~ V, [KAI, 2.2]; [GUIDE, 性能调优实战] FP4 micro-scaling):
+ *   the tile's keys fall into the 32-key groups of orc_pv_group; a group's p_n
+ *   share the E8M0 scale 2^e of its largest p_n (the MXFP4 rule), and
+ *   P_n   = dec(E2M1(p_n / 2^e)) * 2^e;  V from orc_quant_v_head_mxfp4 (`v8` holds
+ *   its E2M1 codes, `v_e8m0` its scales), dec(v)_n,d = dec(E2M1) * 2^(e8m0 - 127),
+ *   inner and O as in pv fp8;  out = O_d / l  (+ v_mean_d).  tile_k must be a
+ *   multiple of 64 so that no group spans two tiles.
+ * `v` (fp32 values of the original V) is read only in pv fp16 mode; `v8` in pv
+ * fp8 and fp4 modes, `v_scale` in pv fp8 mode, `v_e8m0` in pv fp4 mode.  out is
+ * [nrows][D] fp32 (before the final rounding to the input dtype).  A row that
+ * sees no key at all (S = 0) is 0.
  */
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
-                        const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
-                        int in_dtype, int S, int D, int is_causal, float sm_scale,
+                        const uint8_t *v8, const float *v_scale, const uint8_t *v_e8m0, const float *v_mean,
+                        const float *v, int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, const float *qk, const float *delta,
                         int blk_d, float *out) {
     int ntile = (S + tile_k - 1) / tile_k;
@@ -505,22 +588,44 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                 }
                 float mnew = m > mt ? m : mt;
                 float alpha = (m == -INFINITY) ? 0.0f : expf(m - mnew);
-                float psum = 0.0f;
-                for (int t = 0; t < tile_k; ++t) {
-                    p[t] = (s[t] == -INFINITY) ? 0.0f : expf(s[t] - mnew);
-                    psum += p[t];
-                }
-                l = alpha * l + psum;
+                for (int t = 0; t < tile_k; ++t) p[t] = (s[t] == -INFINITY) ? 0.0f : expf(s[t] - mnew);
                 if (pv_mode == ORC_PV_FP8) {
                     for (int t = 0; t < tile_k; ++t) pq[t] = orc_e4m3_decode(orc_e4m3_encode(p[t] * 448.0f));
+                } else if (pv_mode == ORC_PV_FP4) {
+                    int g0 = orc_pv_group(n0);
+                    for (int g = 0; g < 2 * tile_k / 64; ++g) {
+                        float amax = 0.0f;
+                        for (int t = 0; t < tile_k; ++t)
+                            if (orc_pv_group(n0 + t) - g0 == g && p[t] > amax) amax = p[t];
+                        int e = mx_shared_exp(amax);
+                        for (int t = 0; t < tile_k; ++t)
+                            if (orc_pv_group(n0 + t) - g0 == g)
+                                pq[t] = (float)ldexp((double)orc_e2m1_decode(orc_e2m1_encode((float)ldexp((double)p[t], -e))), e);
+                    }
+                } else {
+                    for (int t = 0; t < tile_k; ++t) pq[t] = round_f16(p[t]);
+                }
+                double psum = 0.0;
+                for (int t = 0; t < tile_k; ++t) psum += (double)pq[t];
+                l = alpha * l + (float)psum;
+                if (pv_mode == ORC_PV_FP8) {
                     for (int d = 0; d < D; ++d) {
                         double acc = 0.0;
                         for (int t = 0; t < tile_k && n0 + t < S; ++t)
                             acc += (double)pq[t] * (double)orc_e4m3_decode(v8[(size_t)(n0 + t) * D + d]);
                         O[d] = alpha * O[d] + (float)acc;
                     }
+                } else if (pv_mode == ORC_PV_FP4) {
+                    for (int d = 0; d < D; ++d) {
+                        double acc = 0.0;
+                        for (int t = 0; t < tile_k && n0 + t < S; ++t) {
+                            int n = n0 + t;
+                            acc += (double)pq[t] * ldexp((double)orc_e2m1_decode(v8[(size_t)n * D + d]),
+                                                         (int)v_e8m0[(size_t)orc_pv_group(n) * D + d] - 127);
+                        }
+                        O[d] = alpha * O[d] + (float)acc;
+                    }
                 } else {
-                    for (int t = 0; t < tile_k; ++t) pq[t] = round_f16(p[t]);
                     for (int d = 0; d < D; ++d) {
                         double acc = 0.0;
                         for (int t = 0; t < tile_k && n0 + t < S; ++t) {
@@ -537,11 +642,13 @@ void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
             if (l == 0.0f) {
                 for (int d = 0; d < D; ++d) o[d] = 0.0f;
             } else if (pv_mode == ORC_PV_FP8) {
-                for (int d = 0; d < D; ++d) o[d] = O[d] * (v_scale[d] / (448.0f * l));
+                for (int d = 0; d < D; ++d) o[d] = O[d] * (v_scale[d] / l);
                 if (v_mean)
                     for (int d = 0; d < D; ++d) o[d] = o[d] + v_mean[d];
             } else {
                 for (int d = 0; d < D; ++d) o[d] = O[d] / l;
+                if (v_mean && pv_mode == ORC_PV_FP4)
+                    for (int d = 0; d < D; ++d) o[d] = o[d] + v_mean[d];
             }
         }
         free(s);

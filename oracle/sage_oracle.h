@@ -43,6 +43,7 @@ extern "C" {
 /* pv modes */
 #define ORC_PV_FP8 0
 #define ORC_PV_FP16 1
+#define ORC_PV_FP4 2
 
 int orc_num_threads(void);
 
@@ -64,7 +65,8 @@ void orc_quant_k_head(const float *k, int S, int D, int blk, int smooth,
 int orc_lane_group(int n);
 void orc_quant_q_head_smooth(const float *q, int S, int D, int blk, int blk_scale, int8_t *codes,
                              float *scales, float *qmean);
-void orc_qk_delta_head(const float *qmean, int nb, const float *kc, int S, int D, float *delta);
+void orc_qk_delta_head(const float *qmean, int nb, const float *k, const float *kmean, int S, int D,
+                       float *delta);
 void orc_quant_k_head_lane(const float *k, int S, int D, int smooth,
                            int8_t *codes, float *scales, float *mean);
 void orc_quant_v_head(const float *v, int S, int D, uint8_t *codes, float *scales);
@@ -74,13 +76,18 @@ void orc_quant_k_head_mxfp4(const float *k, int S, int D, int smooth, uint8_t *c
 void orc_qk_mxfp4_rows(const uint8_t *q4, const uint8_t *qe, const uint8_t *k4, const uint8_t *ke, int S,
                        int D, const int *rows, int nrows, float *out);
 void orc_quant_v_head_smooth(const float *v, int S, int D, uint8_t *codes, float *scales, float *mean);
+void orc_quant_q_head_mxfp4_smooth(const float *q, int S, int D, int blk, uint8_t *codes, uint8_t *e8m0,
+                                   float *qmean);
+int orc_pv_group(int n);
+void orc_quant_v_head_mxfp4(const float *v, int S, int D, int smooth, uint8_t *codes, uint8_t *e8m0,
+                            float *mean);
 
 /* ---- attention (per head) ---------------------------------------------- */
 void orc_qk_int32_head(const int8_t *q8, const int8_t *k8, int S, int D, int32_t *out);
 void orc_attn_head_rows(const int8_t *q8, const float *q_scale, int blk_q,
                         const int8_t *k8, const float *k_scale, int blk_k, int k_lane, int tile_k,
-                        const uint8_t *v8, const float *v_scale, const float *v_mean, const float *v,
-                        int in_dtype, int S, int D, int is_causal, float sm_scale,
+                        const uint8_t *v8, const float *v_scale, const uint8_t *v_e8m0, const float *v_mean,
+                        const float *v, int in_dtype, int S, int D, int is_causal, float sm_scale,
                         int pv_mode, const int *rows, int nrows, const float *qk, const float *delta,
                         int blk_d, float *out);
 void orc_attn_exact_head(const float *q, const float *k, const float *v, int S, int D,

@@ -343,15 +343,19 @@ def pin_k_scale_per_block():
 
 
 def pin_v_ones_row_sums():
-    """V = 1 everywhere: the output is sum(P8) / (448 l) = 1 up to E4M3 rounding of
-    P~ (relative 2^-4 per element) -- checks l and the PV path together."""
+    """V = 1 everywhere: the row sum l adds up exactly the rounded weights P that
+    the P~ V product multiplies, so every output is sum(P) / sum(P) = 1 up to the
+    fp32 rounding of the two sums -- in every pv format.  (A row sum of the
+    unrounded p~ would leave the E4M3 rounding of P~, up to 2^-4, in the output.)"""
     qf, kf, _ = _rand_head(200, 64, seed=41)
     vf = np.ones_like(qf)
+    q, k, v = (_f16(x)[None, None] for x in (qf, kf, vf))
     for causal in (False, True):
-        out = _attn_f(qf, kf, vf, causal=causal)
-        assert np.all(np.abs(out - 1) <= 2.0 ** -4 + 1e-3), np.abs(out - 1).max()
-        out16 = _attn_f(qf, kf, vf, causal=causal, pv=O.PV_FP16)
-        assert np.all(np.abs(out16 - 1) <= 2.0 ** -10), np.abs(out16 - 1).max()
+        for pv in (O.PV_FP8, O.PV_FP16):
+            out = _attn_f(qf, kf, vf, causal=causal, pv=pv)
+            assert np.all(np.abs(out - 1) <= 1e-6), (pv, np.abs(out - 1).max())
+        out4 = O.attn(q, k, v, F16, "HND", is_causal=causal, pv_mode=O.PV_FP4)[(0, 0)]
+        assert np.all(np.abs(out4 - 1) <= 1e-6), np.abs(out4 - 1).max()
 
 
 def pin_q_zero_closed_form():
@@ -808,6 +812,16 @@ def pin_smooth_v_shift_equivariance():
     ob = O.attn_head_rows(q8, qs, k8, ks, b8, bs, vf, in_dtype=F16, is_causal=True, sm_scale=0.125,
                           pv_mode=O.PV_FP8, v_mean=bm)
     assert np.allclose(ob - c[None, :], oa, rtol=0, atol=4 * 2.0 ** -20 * (1 + np.abs(c).max()))
+    # the same with the FP4 P~ V product: MXFP4 codes and scales of V - mean unchanged
+    a4, ae, am4 = O.quant_v_head_mxfp4(vf, True)
+    b4, be, bm4 = O.quant_v_head_mxfp4(vf + c[None, :], True)
+    assert np.array_equal(a4, b4) and np.array_equal(ae, be) and np.array_equal(bm4, am4 + c)
+    q, k = (_f16(x)[None, None] for x in (qf, kf))
+    oa4 = O.attn(q, k, _f16(vf)[None, None], F16, "HND", is_causal=True, pv_mode=O.PV_FP4, smooth_v=True)[(0, 0)]
+    ob4 = O.attn(q, k, _f16(vf + c[None, :])[None, None], F16, "HND", is_causal=True, pv_mode=O.PV_FP4,
+                 smooth_v=True)[(0, 0)]
+    assert np.allclose(ob4 - c[None, :], oa4, rtol=0, atol=4 * 2.0 ** -20 * (1 + np.abs(c).max()))
+    assert np.abs(ob4 - oa4).max() > 0.5  # the means are added back
 
 
 def pin_smooth_v_more_accurate_with_v_offsets():
@@ -942,11 +956,17 @@ def pin_smooth_q_means_and_codes():
 
 
 def pin_qk_delta_bruteforce():
+    """delta = qmean . (K - k_mean): the fp32 subtraction, then an exact-ish dot product."""
     qm = _rand_head(5, 64, seed=82)[0]
-    kc = _rand_head(90, 64, seed=83)[1]
-    got = O.qk_delta_head(qm, kc)
+    kf = _rand_head(90, 64, seed=83)[1]
+    km = O.channel_mean(kf)
+    got = O.qk_delta_head(qm, kf, km)
+    kc = kf - km[None, :]  # fp32 - fp32 in numpy: one rounding per element
+    assert kc.dtype == np.float32
     ref = (qm.astype(np.float64) @ kc.astype(np.float64).T).astype(np.float32)
     assert np.allclose(got, ref, rtol=2e-7, atol=1e-30)
+    # a subtraction that is not done (or done twice) moves delta by qmean . k_mean
+    assert not np.allclose(O.qk_delta_head(qm, kf, np.zeros_like(km)), ref, rtol=1e-3, atol=1e-3)
 
 
 def pin_smooth_q_constant_blocks():
@@ -960,7 +980,7 @@ def pin_smooth_q_constant_blocks():
     assert not q8.any() and not qs.any()
     k8, ks, km = O.quant_k_head(kf, 64, True)
     kc = (kf - km[None, :]).astype(np.float32)
-    delta = O.qk_delta_head(qm, kc)
+    delta = O.qk_delta_head(qm, kf, km)
     exact_rows = (qf.astype(np.float64) @ kc.astype(np.float64).T).astype(np.float32)
     assert np.allclose(delta[np.arange(S) // 32], exact_rows, rtol=1e-6, atol=1e-6)
     v8, vs = O.quant_v_head(vf)
@@ -1000,7 +1020,7 @@ def pin_smooth_q_fp4_constant_blocks():
     v = vf.astype(np.float16).view(np.uint16)[None, None]
     _, _, qm = O.quant_q_head_smooth(qf, 32)
     _, _, km = O.quant_k_head_mxfp4(kf, True)
-    delta = O.qk_delta_head(qm, (kf - km[None, :]).astype(np.float32))
+    delta = O.qk_delta_head(qm, kf, km)
     v8, vs = O.quant_v_head(vf)
     z8, z1 = np.zeros((S, D), np.int8), np.zeros(1, np.float32)
     for causal in (False, True):
@@ -1023,6 +1043,122 @@ def pin_smooth_q_fp4_more_accurate_with_q_offsets():
     pl = O.attn(q, k, v, F16, "HND", qk_format="fp4", pv_mode=O.PV_FP16)
     for hd in ex:
         assert rel_l1(sm[hd], ex[hd]) < 0.25 * rel_l1(pl[hd], ex[hd]), (hd, rel_l1(sm[hd], ex[hd]), rel_l1(pl[hd], ex[hd]))
+
+
+# ------------------------------------------------------------------ micro-scaled FP4 P~ V
+def pin_pv_groups_follow_mfma_layout():
+    """The FP4 P~ V scale groups are the 32 keys one lane half holds of each 64-key
+    block in the 32 x 32 x 64 MFMA B operand: lane l carries, for its query, the
+    scores of sub-tiles t = 0, 1 in accumulator slots r, i.e. keys
+    32 t + 8 (r // 4) + 4 (l // 32) + r % 4 (the Q K^T result layout), numbered
+    2 * block + half."""
+    for blk in range(4):
+        for half in (0, 1):
+            keys = {64 * blk + 32 * t + 8 * (r // 4) + 4 * half + r % 4 for t in (0, 1) for r in range(16)}
+            assert len(keys) == 32
+            assert {O.pv_group(n) for n in keys} == {2 * blk + half}, (blk, half)
+
+
+def _fp4_grid_v(S, D, rng):
+    """V on the MXFP4 grid of the P~ V groups: every (group, channel) block holds
+    E2M1 values times 2^e with its own e in [-4, 3] and reaches amax 4 or 6 times
+    2^e, so its shared exponent is e and the block is represented exactly."""
+    mags = np.array(E2M1_VALUES, np.float32)
+    vf = np.zeros((S, D), np.float32)
+    for g in range(2 * ((S + 63) // 64)):
+        keys = [n for n in range(64 * (g // 2), min(S, 64 * (g // 2 + 1))) if ((n >> 2) & 1) == g % 2]
+        if not keys:
+            continue
+        for d in range(D):
+            e = int(rng.integers(-4, 4))
+            vals = rng.choice(mags, size=len(keys)) * rng.choice([-1.0, 1.0], size=len(keys))
+            vals[rng.integers(len(keys))] = rng.choice([4.0, 6.0])
+            vf[keys, d] = np.ldexp(vals, e).astype(np.float32)
+    return vf
+
+
+def pin_fp4_pv_lossless_q_zero():
+    """Q = 0: every p~ is 1, so every group's scale is 2^-2 and every P is exactly
+    1; V on the P~ V groups' MXFP4 grid is represented exactly; the output is then
+    the plain (causal: prefix) mean of V up to fp32 rounding.  A different key
+    grouping would mix blocks of different exponents and re-round V."""
+    S, D = 200, 64
+    rng = np.random.default_rng(71)
+    vf = _fp4_grid_v(S, D, rng)
+    v4, ve, _ = O.quant_v_head_mxfp4(vf)
+    dec = O.e2m1_decode(v4).astype(np.float64) * np.exp2(ve[[O.pv_group(n) for n in range(S)]].astype(np.float64) - 127)
+    assert np.array_equal(dec, vf.astype(np.float64))
+    _, kf, _ = _rand_head(S, D, seed=72)
+    q, k, v = (_f16(x)[None, None] for x in (np.zeros((S, D), np.float32), kf, vf))
+    out = O.attn(q, k, v, F16, "HND", pv_mode=O.PV_FP4)[(0, 0)]
+    assert np.allclose(out, vf.astype(np.float64).mean(0)[None, :], rtol=1e-5, atol=1e-6)
+    outc = O.attn(q, k, v, F16, "HND", is_causal=True, pv_mode=O.PV_FP4)[(0, 0)]
+    pref = np.cumsum(vf.astype(np.float64), 0) / np.arange(1, S + 1)[:, None]
+    assert np.allclose(outc, pref, rtol=1e-5, atol=1e-6)
+
+
+def pin_fp4_v_group_scales():
+    """MXFP4 V: each (group, channel) block's E8M0 byte is floor(log2 amax) - 2 +
+    127 over exactly that group's keys (ragged last block included), and the
+    codes are E2M1(v / 2^e)."""
+    S, D = 150, 32
+    _, _, vf = _rand_head(S, D, seed=73)
+    v4, ve, mean = O.quant_v_head_mxfp4(vf)
+    assert ve.shape == (2 * 3, D) and not mean.any()
+    for g in range(6):
+        keys = [n for n in range(64 * (g // 2), min(S, 64 * (g // 2 + 1))) if ((n >> 2) & 1) == g % 2]
+        for d in (0, 7, 31):
+            blk = vf[keys, d]
+            e = int(np.floor(np.log2(np.abs(blk).max()))) - 2
+            assert int(ve[g, d]) == e + 127, (g, d)
+            assert np.array_equal(v4[keys, d], O.e2m1_encode(np.ldexp(blk, -e).astype(np.float32)))
+    # smoothing: the channel means are subtracted first (the rule applied to V - mean)
+    s4, se, sm = O.quant_v_head_mxfp4(vf, True)
+    assert np.array_equal(sm, O.channel_mean(vf))
+    r4, re_, _ = O.quant_v_head_mxfp4((vf - sm[None, :]).astype(np.float32))
+    assert np.array_equal(s4, r4) and np.array_equal(se, re_)
+
+
+def pin_fp4_p_on_group_grid():
+    """V = identity exposes P: out[i, n] = P_n / l.  The row's largest key has
+    p~ = 1, hence P = 1, so P_n = out[i, n] / out[i, n_max]; within each P~ V
+    group the P_n share one power-of-two scale 2^e (e from the group's largest
+    P) and P_n / 2^e is an E2M1 magnitude, the largest 4 or 6."""
+    S, D = 64, 64
+    qf, kf, _ = _rand_head(S, D, seed=74)
+    qf = qf * 3.0  # spread the weights over several binades
+    vf = np.eye(S, D, dtype=np.float32)
+    q, k, v = (_f16(x)[None, None] for x in (qf, kf, vf))
+    out = O.attn(q, k, v, F16, "HND", pv_mode=O.PV_FP4)[(0, 0)].astype(np.float64)
+    mags = np.array(E2M1_VALUES, np.float64)
+    checked = 0
+    for i in range(S):
+        P = out[i, :S] / out[i, :S].max()
+        for half in (0, 1):
+            keys = [n for n in range(S) if ((n >> 2) & 1) == half]
+            pg = P[keys]
+            if pg.max() <= 0:
+                continue
+            e = int(np.floor(np.log2(pg.max() * (1 + 1e-9)))) - 2
+            r = pg / 2.0 ** e
+            near = np.abs(r[:, None] - mags[None, :]).min(1)
+            assert (near <= 1e-5 * np.maximum(r, 1)).all(), (i, half)
+            assert np.isclose(r.max(), 4) or np.isclose(r.max(), 6), (i, half, r.max())
+            checked += 1
+    assert checked >= S
+
+
+def pin_fp4_pv_pipeline_vs_exact():
+    """The FP4 P~ V product tracks exact attention (cos >= 0.98 on N(0,1) inputs)
+    but less closely than FP8 P~ V -- FP4 is not lossless."""
+    w = synth.custom(1, 2, 256, 128, seed=75)
+    q, k, v = synth.make_qkv(w)
+    ex = O.attn_exact(q, k, v, F16, "HND")
+    f4 = O.attn(q, k, v, F16, "HND", pv_mode=O.PV_FP4)
+    f8 = O.attn(q, k, v, F16, "HND")
+    for hd in ex:
+        assert cos(f4[hd], ex[hd]) >= 0.98, (hd, cos(f4[hd], ex[hd]))
+        assert rel_l1(f4[hd], ex[hd]) > rel_l1(f8[hd], ex[hd])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

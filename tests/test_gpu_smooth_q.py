@@ -69,7 +69,7 @@ def test_smooth_q_quant_and_delta(w, qk):
             km = O.channel_mean(kf)
             assert np.array_equal(bufs.k_mean.cpu().numpy()[b, O.kv_head(h, w.H, w.kv_heads)].view(np.uint32),
                                   km.view(np.uint32))
-            rd = O.qk_delta_head(rm, (kf - km[None, :]).astype(np.float32))
+            rd = O.qk_delta_head(rm, kf, km)
             bound = 2.0 ** -14 * (np.abs(rm).astype(np.float64) @ (np.abs(kf) + np.abs(km)[None, :]).T)
             err = np.abs(ds[b, h, :nq, :S].astype(np.float64) - rd)
             assert (err <= bound).all(), (b, h, float((err / bound).max()))

@@ -14,7 +14,9 @@ SRC = os.path.join(ROOT, "oracle", "sage_oracle.c")
 # (id, original text, planted mistake)
 MUTANTS = [
     ("O_update_drops_alpha", "O[d] = alpha * O[d] + (float)acc;", "O[d] = O[d] + (float)acc;"),
-    ("l_update_drops_alpha", "l = alpha * l + psum;", "l = l + psum;"),
+    ("l_update_drops_alpha", "l = alpha * l + (float)psum;", "l = l + (float)psum;"),
+    ("l_from_unrounded_p", "psum += (double)pq[t];",
+     "psum += (double)(pv_mode == ORC_PV_FP8 ? p[t] * 448.0f : p[t]);"),
     ("alpha_wrong_sign", "expf(m - mnew)", "expf(mnew - m)"),
     ("p_wrong_sign", "expf(s[t] - mnew)", "expf(mnew - s[t])"),
     ("qk_transposed_out", "out[(size_t)i * S + n] = dot_i8", "out[(size_t)n * S + i] = dot_i8"),
@@ -23,7 +25,7 @@ MUTANTS = [
     ("no_k_smoothing", "ks[i] = k[i] - mean[i % D];", "ks[i] = k[i];"),
     ("mean_divides_by_D", "(float)(s / (double)S)", "(float)(s / (double)D)"),
     ("p_static_scale_240", "orc_e4m3_encode(p[t] * 448.0f)", "orc_e4m3_encode(p[t] * 240.0f)"),
-    ("v_scale_wrong_channel", "v_scale[d] / (448.0f * l)", "v_scale[0] / (448.0f * l)"),
+    ("v_scale_wrong_channel", "v_scale[d] / l", "v_scale[0] / l"),
     ("v_quant_scale_240", "float inv = 448.0f / amax;", "float inv = 240.0f / amax;"),
     ("causal_masks_diagonal", "(is_causal && n > i)", "(is_causal && n >= i)"),
     ("round_ties_away", "return nearbyint(a / q) * q;", "return round(a / q) * q;"),
@@ -54,6 +56,20 @@ MUTANTS = [
      "qs[(size_t)t * D + d] = q[(size_t)t * D + d];"),
     ("delta_wrong_block", "delta[(size_t)(i / blk_d) * S + n] * sm_scale", "delta[(size_t)(i / blk_k) * S + n] * sm_scale"),
     ("delta_without_sm_scale", "delta[(size_t)(i / blk_d) * S + n] * sm_scale;", "delta[(size_t)(i / blk_d) * S + n];"),
+    ("delta_k_not_smoothed", "kc[i] = k[i] - kmean[i % D];", "kc[i] = k[i];"),
+    ("fp4_smooth_q_not_subtracted",
+     "qs[(size_t)t * D + d] = q[(size_t)t * D + d] - qmean[(size_t)b * D + d];\n    }\n    orc_mxfp4_quant_rows",
+     "qs[(size_t)t * D + d] = q[(size_t)t * D + d];\n    }\n    orc_mxfp4_quant_rows"),
+    ("pv_group_wrong_bit", "return 2 * (n >> 6) + ((n >> 2) & 1);", "return 2 * (n >> 6) + ((n >> 3) & 1);"),
+    ("pv_group_contiguous", "return 2 * (n >> 6) + ((n >> 2) & 1);", "return 2 * (n >> 6) + ((n >> 5) & 1);"),
+    ("fp4_p_exponent_off_by_one", "int e = mx_shared_exp(amax);\n                        for (int t = 0; t < tile_k; ++t)",
+     "int e = mx_shared_exp(amax) + 1;\n                        for (int t = 0; t < tile_k; ++t)"),
+    ("fp4_p_group_misaligned", "int g0 = orc_pv_group(n0);", "int g0 = orc_pv_group(n0) + 1;"),
+    ("fp4_v_first_group_scale", "(int)v_e8m0[(size_t)orc_pv_group(n) * D + d] - 127", "(int)v_e8m0[(size_t)d] - 127"),
+    ("fp4_v_not_smoothed", "vs[i] = v[i] - mean[i % D];\n    for (int g = 0; g < ng; ++g)",
+     "vs[i] = v[i];\n    for (int g = 0; g < ng; ++g)"),
+    ("fp4_v_mean_not_added", "if (v_mean && pv_mode == ORC_PV_FP4)\n                    for (int d = 0; d < D; ++d) o[d] = o[d] + v_mean[d];",
+     "if (v_mean && pv_mode == ORC_PV_FP4)\n                    for (int d = 0; d < D; ++d) o[d] = o[d];"),
     ("f16_decode_bias", "ldexp(1.0 + fr / 1024.0, ex - 15)", "ldexp(1.0 + fr / 1024.0, ex - 14)"),
 ]
 
