@@ -2,10 +2,11 @@
 
 A step = one pass of the whole path over one batch of synthetic input already
 resident in HBM: sage_quantize_qkv (K mean, INT8 Q/K, FP8 V; in pv fp16 mode
-sage_smooth_quant_qk alone; packed batches: the varlen calls) and sage_attn_fwd
-(INT8 QK^T, online softmax, FP8 PV), all on one stream.
+sage_smooth_quant_qk alone; in pv fp4 mode sage_smooth_quant_qk and
+sage_quant_v_fp4; packed batches: the varlen calls) and sage_attn_fwd (INT8
+QK^T, online softmax, FP8 / FP16 / MXFP4 PV), all on one stream.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1] [--pv fp8|fp16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1] [--pv fp8|fp16|fp4]
 
 Prints one JSON line.  `value` is attention TOPS of the whole step
 (4*B*H*S^2*D per step, halved when causal); the attention kernel alone is
@@ -37,7 +38,7 @@ def mfma_peak(pv, qk="int8"):
     or FP16 in pv fp16 mode), so the peak is the harmonic combination of the
     two dense peaks."""
     qk_peak = FP4_PEAK_TOPS if qk == "mxfp4" else MFMA_PEAK_TOPS
-    pv_peak = MFMA_PEAK_TOPS if pv == "fp8" else FP16_PEAK_TOPS
+    pv_peak = {"fp8": MFMA_PEAK_TOPS, "fp16": FP16_PEAK_TOPS, "fp4": FP4_PEAK_TOPS}[pv]
     return 2.0 / (1.0 / qk_peak + 1.0 / pv_peak)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_traffic.json")
@@ -51,7 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=None)
     p.add_argument("--causal", type=int, default=None)
-    p.add_argument("--pv", default="fp8", choices=["fp8", "fp16"])
+    p.add_argument("--pv", default="fp8", choices=["fp8", "fp16", "fp4"])
     p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
     p.add_argument("--smooth-q", action="store_true",
                    help="Q smoothing (fixed-length batches): quantise Q minus its 32-token block means")
@@ -109,7 +110,7 @@ def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=Fals
     import oracle as O
     from quantized_attention_02_amd import synth
 
-    pvm = O.PV_FP8 if pv == "fp8" else O.PV_FP16
+    pvm = {"fp8": O.PV_FP8, "fp16": O.PV_FP16, "fp4": O.PV_FP4}[pv]
     if isinstance(w, synth.VarlenWorkload):
         q, k, v = synth.make_qkv_varlen(w)
         cq, ck = w.cu_seqlens()
@@ -180,8 +181,8 @@ def main():
     varlen = name in synth.VARLEN_WORKLOADS
     if args.smooth_q and varlen:
         sys.exit("--smooth-q applies to fixed-length batches")
-    if args.smooth_v and args.pv != "fp8":
-        sys.exit("--smooth-v applies to pv fp8")
+    if args.smooth_v and args.pv == "fp16":
+        sys.exit("--smooth-v applies to pv fp8 and fp4")
     w = synth.VARLEN_WORKLOADS[name] if varlen else synth.WORKLOADS[name]
     causal = w.causal[0] if args.causal is None else bool(args.causal)
     ops = w.ops(causal)
@@ -255,7 +256,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"int8": "i8", "int8_lane": "i8", "int8_token": "i8", "int8_head": "i8", "mxfp4": "mxfp4"}[args.qk_quant] + ("+fp8" if args.pv == "fp8" else "+f16"),
+        "dtype": {"int8": "i8", "int8_lane": "i8", "int8_token": "i8", "int8_head": "i8", "mxfp4": "mxfp4"}[args.qk_quant] + {"fp8": "+fp8", "fp16": "+f16", "fp4": "+mxfp4"}[args.pv],
         "data": "synthetic",
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,

@@ -20,8 +20,12 @@
  *   [REPO]  "SageAttention: Thư viện Attention lượng tử hóa" repository summary page,
  *           feature list (variable-length sequences through sageattn_varlen,
  *           native grouped-query attention).
+ *   [OCP-MX] the Open Compute Project Microscaling (MX) Formats specification v1.0
+ *           (public): the E2M1 element and E8M0 scale encodings of MXFP4, 32-element
+ *           blocks.
  *
- * Pipeline: sage_smooth_quant_qk -> sage_quant_v (pv fp8 only) -> sage_attn_fwd.
+ * Pipeline: sage_smooth_quant_qk -> sage_quant_v (pv fp8) or sage_quant_v_fp4 (pv fp4)
+ *           -> sage_attn_fwd.
  *
  * Common rules for every entry point:
  *  - Tensor pointers are DEVICE pointers; every call only enqueues work on
@@ -67,6 +71,12 @@
  *   delta_s float [B][H][S_k/128][nq][128]  Q smoothing only: the pre-processing term
  *           of query block blk and key n at [b][h][n / 128][blk][n % 128] (128-key
  *           tiles one after the other, so that each tile's rows are contiguous).
+ *   pv fp4 (sage_quant_v_fp4) replaces v_fp8 and v_scale by
+ *   v_codes uint8 [B][H_kv][nk][D][32]  E2M1 codes of V (or V - v_mean), per 64-key block
+ *           and channel 32 bytes: nibble p (byte p / 2, the low nibble for even p) holds key
+ *           SAGE_VPOS_KEY(p) of the block (keys >= S are 0);
+ *   v_e8m0  uint8 [B][H_kv][nk][D][2]   the E8M0 byte of each block, channel and key group
+ *           (group g: the block's keys n with (n / 4) mod 2 = g, i.e. nibbles 32 g .. 32 g + 31).
  *   SAGE_QK_MXFP4 replaces the Q/K codes and scales by (D / 2 and D / 32 bytes a row):
  *   q_codes uint8 [B][H][S_q][D/2]  E2M1 codes of Q, two per byte (channel 2j in the low
  *                                   nibble of byte j); q_scale uint8 [B][H][S_q][D/32], the
@@ -99,6 +109,10 @@ extern "C" {
 #define SAGE_DTYPE_BF16 1
 #define SAGE_PV_FP8 0  /* P~ and V in E4M3, two-level fp32 accumulation ([SA2]) */
 #define SAGE_PV_FP16 1 /* P~ and V in fp16, fp32 accumulation ([KAI] 2.1, sm80 row) */
+#define SAGE_PV_FP4 2  /* P~ and V in MXFP4 ([KAI] 2.2, the FP4 micro-scaling kernels of the next
+                          generation; [OCP-MX]): E2M1 codes, an E8M0 scale per 32-key group of
+                          each query row (P~) and of each V channel (sage_quant_v_fp4), fp32
+                          accumulation across tiles */
 /* Quantisation of Q and K for the Q K^T product (qk_quant):
  * INT8 with a scale granularity ([KAI] 2.2 per_block / per_warp choice; [SA2]
  * SageAttention2方法, thread-level quantisation), or micro-scaled FP4 ([KAI] 2.2,
@@ -203,6 +217,24 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
                  float *v_scale, float *v_mean, void *stream);
 
 /*
+ * MXFP4 quantisation of V for the FP4 P~ V product (SAGE_PV_FP4; [KAI] 2.2; [OCP-MX]):
+ * for each 64-key block, channel d and key group g (the block's keys n with
+ * (n / 4) mod 2 = g; 32 keys, padding keys >= S counting as 0):
+ *   amax = max |x|;  e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 if amax = 0);
+ *   v_e8m0 = e + 127;  code = E2M1(x / 2^e), round to nearest even, saturating at 6,
+ * with x = V[s][d], or V[s][d] - v_mean[d] (one fp32 subtraction) when v_mean is
+ * non-NULL (V smoothing, the means as in sage_quant_v; sage_attn_fwd adds them back).
+ * H is the number of V heads.  Buffer sizes: sage_v_fp4_buffer_sizes.  v_codes 16-byte,
+ * v_e8m0 4-byte aligned.  With v_mean, both buffers hold intermediate statistics while
+ * the call's launches run (defined once the stream has passed the call).
+ */
+int sage_quant_v_fp4(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_codes,
+                     uint8_t *v_e8m0, float *v_mean, void *stream);
+
+/* Bytes of v_codes and v_e8m0 of sage_quant_v_fp4 (either pointer may be NULL). */
+int sage_v_fp4_buffer_sizes(int B, int H_kv, int S, int D, size_t *v_codes, size_t *v_e8m0);
+
+/*
  * sage_smooth_quant_qk followed by sage_quant_v (on V's H_kv heads), in one call:
  * the same arguments, checks and results (every output buffer bit for bit), with
  * the passes that do not depend on each other sharing kernel launches (four
@@ -231,11 +263,18 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  *   smoothed Q (delta_s non-NULL): s_n += delta_s[query block][n] * sm_scale (MXFP4: the
  *         term is the starting value of the fp32 accumulator the FP4 MFMA adds to)
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
+ *   pv fp4 : for each 32-key group G of a row (keys of one 64-key block with equal
+ *            (n / 4) mod 2): e = floor(log2 max_G p_n) - 2 (clamped to [-126, 127]),
+ *            P_n = dec(E2M1(p_n / 2^e)) 2^e; inner = P . dec(V) (scaled FP4 MFMA, V from
+ *            sage_quant_v_fp4), O = alpha*O + inner;  l sums the P_n;
+ *            out = O / l (+ v_mean[d] when V was smoothed)
  * q_codes .. k_scale: from sage_smooth_quant_qk.  pv fp8: v = v_fp8 and v_scale from
  * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the
  * original V tensor (dtype, layout, H_kv heads), v_scale = v_mean = NULL (bf16 V is
  * rounded to fp16).  delta_s: NULL, or the buffer sage_qk_delta filled for these
- * codes.  out: dtype tensor in `layout`, shape of q.  Query head h reads K/V head
+ * codes.  pv fp4: v = v_codes and v_scale = v_e8m0 (the byte buffer passed as a
+ * float pointer, 4-byte aligned) from sage_quant_v_fp4, v_mean as for pv fp8.
+ * out: dtype tensor in `layout`, shape of q.  Query head h reads K/V head
  * h / (H / H_kv).
  * is_causal in {0, 1}; sm_scale finite and > 0 (the usual choice is 1/sqrt(D)).
  * pv fp16 with NHD layout additionally needs H_kv * D * 2 * SAGE_KV_PAD < 2^31
@@ -308,6 +347,15 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
 /* sage_quant_v for a packed batch (v: [total_k][H_kv][D]); v_mean as there. */
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
                         int max_seqlen_k, int D, uint8_t *v_fp8, float *v_scale, float *v_mean, void *stream);
+
+/* Bytes of v_codes and v_e8m0 of sage_quant_v_fp4_varlen: [H_kv][RK / 64][D][32] and
+ * [H_kv][RK / 64][D][2] (the fixed layout's 64-key blocks, rows as for v_fp8). */
+int sage_varlen_v_fp4_buffer_sizes(int B, int H_kv, int total_k, int D, size_t *v_codes, size_t *v_e8m0);
+
+/* sage_quant_v_fp4 for a packed batch (v: [total_k][H_kv][D]); v_mean as there. */
+int sage_quant_v_fp4_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
+                            int max_seqlen_k, int D, uint8_t *v_codes, uint8_t *v_e8m0, float *v_mean,
+                            void *stream);
 
 /* sage_attn_fwd for a packed batch.  pv fp16: v = the original [total_k][H_kv][D]
  * V, v_scale = v_mean = NULL.  out: [total_q][H][D] in dtype. */

@@ -25,14 +25,15 @@ LIB_PATH = os.path.join(PKG, "libsage.so")
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_NO_DEVICE, SAGE_ERR_LAUNCH = 0, 1, 2, 3, 4
 LAYOUT = {"HND": 0, "NHD": 1}
 DTYPE = {"fp16": 0, "bf16": 1}
-PV = {"fp8": 0, "fp16": 1}
+PV = {"fp8": 0, "fp16": 1, "fp4": 2}
 QK = {"int8": 0, "int8_lane": 1, "mxfp4": 2, "int8_token": 3, "int8_head": 4}  # Q/K quantisation (include/sage.h SAGE_QK_*)
 BLK_Q, BLK_K, KV_PAD = 32, 64, 128
-TILE_K = {"fp8": 128, "fp16": 128}  # keys per online-softmax tile of the attention kernel
+TILE_K = {"fp8": 128, "fp16": 128, "fp4": 128}  # keys per online-softmax tile of the attention kernel
 
 EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_quantize_qkv", "sage_attn_fwd",
             "sage_attn_fwd_dump_qk", "sage_qk_delta", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
-            "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch"]
+            "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch", "sage_quant_v_fp4", "sage_v_fp4_buffer_sizes",
+            "sage_quant_v_fp4_varlen", "sage_varlen_v_fp4_buffer_sizes"]
 
 _lib = None
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
         L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 8 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
             [c_int, c_float, c_int, c_int, c_void_p]
+        L.sage_quant_v_fp4.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
+        L.sage_v_fp4_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 2
+        L.sage_quant_v_fp4_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
+        L.sage_varlen_v_fp4_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 2
         L.sage_status_str.argtypes = [c_int]
         L.sage_status_str.restype = ctypes.c_char_p
         L.sage_check_arch.argtypes = [ctypes.c_char_p]
@@ -121,6 +126,30 @@ def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, q_mean, k_mean, delta_s, s
 
 def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream):
     return lib().sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream)
+
+
+def sage_quant_v_fp4(v, dtype, B, H, S, D, layout, v_codes, v_e8m0, v_mean, stream):
+    return lib().sage_quant_v_fp4(v, dtype, B, H, S, D, layout, v_codes, v_e8m0, v_mean, stream)
+
+
+def _sizes2(fn, *args):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(fn(*args, ctypes.byref(a), ctypes.byref(b)), fn.__name__)
+    return {"v_codes": a.value, "v_e8m0": b.value}
+
+
+def sage_v_fp4_buffer_sizes(B, H_kv, S, D):
+    return _sizes2(lib().sage_v_fp4_buffer_sizes, B, H_kv, S, D)
+
+
+def sage_varlen_v_fp4_buffer_sizes(B, H_kv, total_k, D):
+    return _sizes2(lib().sage_varlen_v_fp4_buffer_sizes, B, H_kv, total_k, D)
+
+
+def sage_quant_v_fp4_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_codes, v_e8m0, v_mean,
+                            stream):
+    return lib().sage_quant_v_fp4_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_codes, v_e8m0,
+                                         v_mean, stream)
 
 
 def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D, layout,
@@ -236,11 +265,22 @@ class Quantized:
         self.v_fp8 = torch.empty((B, H_kv, sk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
-        self.smooth_v = False  # set by quantize: whether v_fp8 holds V minus v_mean
+        # pv fp4 V: packed E2M1 codes [B][H_kv][S_k / 64][D][32] and E8M0 bytes
+        # [B][H_kv][S_k / 64][D][2] (allocated on first use)
+        self.v_fp4 = self.v_e8m0 = None
+        self._v4_shape = (B, H_kv, sk // BLK_K, D)
+        self.smooth_v = False  # set by quantize: whether the V codes hold V minus v_mean
         self.smooth_q = False  # set by quantize: whether q_i8 holds Q minus its block means
-        self.v_quantized = False  # set by quantize: whether v_fp8 / v_scale hold this V (pv fp8)
+        self.v_mode = None  # set by quantize: the pv mode whose V codes hold this V ("fp8", "fp4"; None)
         self.q_mean = self.delta_s = None  # smoothed Q: allocated on first use
         self._device = device
+
+    def alloc_v_fp4(self):
+        import torch
+
+        if self.v_fp4 is None:
+            self.v_fp4 = torch.empty(self._v4_shape + (32,), dtype=torch.uint8, device=self._device)
+            self.v_e8m0 = torch.empty(self._v4_shape + (2,), dtype=torch.uint8, device=self._device)
 
 
 def _kv_heads(q, k, v, tensor_layout):
@@ -257,16 +297,18 @@ def _kv_heads(q, k, v, tensor_layout):
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
              qk_quant="int8", smooth_v=False, smooth_q=False, fused=True) -> Quantized:
     """Run sage_quantize_qkv in pv fp8 mode (fused=False: sage_smooth_quant_qk and
-    sage_quant_v, same results), or sage_smooth_quant_qk alone in pv fp16 mode, on
-    torch tensors.
+    sage_quant_v, same results), sage_smooth_quant_qk and sage_quant_v_fp4 in pv
+    fp4 mode, or sage_smooth_quant_qk alone in pv fp16 mode, on torch tensors.
     k and v may have fewer heads than q (grouped-query attention); qk_quant "int8"
     (per block), "int8_lane" (one scale per Q token and per 16-key lane group of
     K), "int8_token" (one per Q token and per K token), "int8_head" (one per
     head of Q and of K; not with smooth_q) or "mxfp4"; smooth_v
-    (pv fp8): quantise V minus its channel mean; smooth_q: quantise Q minus its
+    (pv fp8, fp4): quantise V minus its channel mean; smooth_q: quantise Q minus its
     32-token block means and form the pre-processing term."""
-    if smooth_v and pv_mode != "fp8":
-        raise ValueError("smooth_v applies to pv_mode='fp8' only")
+    if pv_mode not in PV:
+        raise ValueError(f"pv_mode must be one of {sorted(PV)}, got {pv_mode!r}")
+    if smooth_v and pv_mode == "fp16":
+        raise ValueError("smooth_v applies to the quantised V of pv_mode 'fp8' and 'fp4'")
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
     H_kv = _kv_heads(q, k, v, tensor_layout)
@@ -286,7 +328,7 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         bufs.delta_s = torch.empty((B, H, sk // KV_PAD, nq, KV_PAD), dtype=torch.float32, device=q.device)
     bufs.smooth_q = bool(smooth_q)
     bufs.smooth_v = bool(smooth_v)
-    bufs.v_quantized = pv_mode == "fp8"
+    bufs.v_mode = pv_mode if pv_mode != "fp16" else None
     qm = bufs.q_mean.data_ptr() if smooth_q else None
     vm = bufs.v_mean.data_ptr() if smooth_v else None
     if pv_mode == "fp8" and fused:
@@ -301,6 +343,10 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         if pv_mode == "fp8":
             _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(),
                                 bufs.v_scale.data_ptr(), vm, st), "sage_quant_v")
+        elif pv_mode == "fp4":
+            bufs.alloc_v_fp4()
+            _check(sage_quant_v_fp4(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp4.data_ptr(),
+                                    bufs.v_e8m0.data_ptr(), vm, st), "sage_quant_v_fp4")
     if smooth_q:
         _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.q_mean.data_ptr(), bufs.k_mean.data_ptr(),
                              bufs.delta_s.data_ptr(), st), "sage_qk_delta")
@@ -319,12 +365,8 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
         raise ValueError("pv fp16 reads the original V: it must be contiguous with H_kv heads")
     dt = _dtype_code(out)
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
-    if pv == 0 and not bufs.v_quantized:
-        raise ValueError("pv fp8 reads the FP8 V codes: quantize these buffers with pv_mode='fp8' first")
-    vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
-    vs = bufs.v_scale.data_ptr() if pv == 0 else None
-    vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
     ds = bufs.delta_s.data_ptr() if bufs.smooth_q else None
     head = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs, vm)
     tail = (out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.qk)
@@ -336,6 +378,22 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
         _check(sage_attn_fwd_dump_qk(*head, *tail, dump_head[0], dump_head[1], dump.data_ptr(), _stream()),
                "sage_attn_fwd_dump_qk")
     return out
+
+
+def _v_operands(bufs, v, pv_mode):
+    """(v, v_scale, v_mean) pointers of the attention call for pv_mode: the
+    quantised V codes and scales (pv fp8, fp4) or the caller's V (pv fp16)."""
+    if pv_mode not in PV:
+        raise ValueError(f"pv_mode must be one of {sorted(PV)}, got {pv_mode!r}")
+    if pv_mode == "fp16":
+        return v.data_ptr(), None, None
+    if bufs.v_mode != pv_mode:
+        raise ValueError(f"pv {pv_mode} reads the {pv_mode.upper()} V codes: quantize these buffers with "
+                         f"pv_mode={pv_mode!r} first")
+    vm = bufs.v_mean.data_ptr() if bufs.smooth_v else None
+    if pv_mode == "fp8":
+        return bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), vm
+    return bufs.v_fp4.data_ptr(), bufs.v_e8m0.data_ptr(), vm
 
 
 # pv_accum_dtype names of the P V accumulation -> pv mode.  "fp32+fp32" is the
@@ -400,8 +458,13 @@ class QuantizedVarlen:
         self.v_fp8 = torch.empty((H_kv, rk // BLK_K, D, BLK_K), dtype=torch.uint8, device=device)
         self.v_scale = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
         self.v_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=device)
+        self.v_fp4 = self.v_e8m0 = None  # pv fp4: [H_kv][RK / 64][D][32] and [..][2], on first use
+        self._v4_shape = (H_kv, rk // BLK_K, D)
+        self._device = device
         self.smooth_v = False
-        self.v_quantized = False
+        self.v_mode = None
+
+    alloc_v_fp4 = Quantized.alloc_v_fp4
 
 
 def _cu(t, name):
@@ -414,8 +477,9 @@ def _cu(t, name):
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
                     bufs: QuantizedVarlen | None = None, qk_quant="int8", smooth_v=False) -> QuantizedVarlen:
-    """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode) on a packed
-    batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
+    """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode,
+    sage_quant_v_fp4_varlen in pv fp4 mode) on a packed batch: q [total_q, H, D],
+    k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_q, H, D] and k, v [total_k, H_kv, D]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -430,8 +494,10 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     (total_q, H, D), (total_k, H_kv, _) = q.shape, k.shape
     if H_kv < 1 or H % H_kv:
         raise ValueError(f"the number of query heads ({H}) must be a multiple of the K/V heads ({H_kv})")
-    if smooth_v and pv_mode != "fp8":
-        raise ValueError("smooth_v applies to pv_mode='fp8' only")
+    if pv_mode not in PV:
+        raise ValueError(f"pv_mode must be one of {sorted(PV)}, got {pv_mode!r}")
+    if smooth_v and pv_mode == "fp16":
+        raise ValueError("smooth_v applies to the quantised V of pv_mode 'fp8' and 'fp4'")
     dt = _dtype_code(q)
     bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device, qk_quant)
     if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D, bufs.qk) != \
@@ -445,11 +511,16 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                        bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
            "sage_smooth_quant_qk_varlen")
     bufs.smooth_v = bool(smooth_v)
-    bufs.v_quantized = pv_mode == "fp8"
+    bufs.v_mode = pv_mode if pv_mode != "fp16" else None
+    vm = bufs.v_mean.data_ptr() if smooth_v else None
     if pv_mode == "fp8":
         _check(sage_quant_v_varlen(v.data_ptr(), dt, ck.data_ptr(), B, H_kv, total_k, bufs.max_seqlen_k, D,
-                                   bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(),
-                                   bufs.v_mean.data_ptr() if smooth_v else None, st), "sage_quant_v_varlen")
+                                   bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), vm, st), "sage_quant_v_varlen")
+    elif pv_mode == "fp4":
+        bufs.alloc_v_fp4()
+        _check(sage_quant_v_fp4_varlen(v.data_ptr(), dt, ck.data_ptr(), B, H_kv, total_k, bufs.max_seqlen_k, D,
+                                       bufs.v_fp4.data_ptr(), bufs.v_e8m0.data_ptr(), vm, st),
+               "sage_quant_v_fp4_varlen")
     return bufs
 
 
@@ -462,13 +533,9 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     if pv_mode == "fp16" and (tuple(v.shape) != (bufs.total_k, H_kv, D) or not v.is_contiguous()):
         raise ValueError("pv fp16 reads the original V: it must be a contiguous [total_k, H_kv, D] tensor")
     cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
-    if pv == 0 and not bufs.v_quantized:
-        raise ValueError("pv fp8 reads the FP8 V codes: quantize these buffers with pv_mode='fp8' first")
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
-    vptr = bufs.v_fp8.data_ptr() if pv == 0 else v.data_ptr()
-    vs = bufs.v_scale.data_ptr() if pv == 0 else None
-    vm = bufs.v_mean.data_ptr() if pv == 0 and bufs.smooth_v else None
     _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
                                 bufs.k_scale.data_ptr(), vptr, vs, vm, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
                                 ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k, bufs.max_seqlen_q,

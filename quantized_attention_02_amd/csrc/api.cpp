@@ -67,6 +67,16 @@ int check_enums(int dtype, int layout) {
   return SAGE_OK;
 }
 
+// pv mode and its V side buffers: pv fp8 needs the channel scales and pv fp4
+// the E8M0 bytes (both through v_scale); V smoothing (v_mean) is for the
+// quantised V codes, not for pv fp16, which reads the caller's V.
+int check_pv(int pv_mode, const float *v_scale, const float *v_mean) {
+  if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP4) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode != SAGE_PV_FP16 && !v_scale) return SAGE_ERR_INVALID_ARG;
+  if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
 // The current device must be gfx950.  Cached per device.
 int check_device() {
   int dev = 0;
@@ -102,11 +112,9 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   if ((rc = check_qk_quant(qk_quant))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_pv(pv_mode, v_scale, v_mean))) return rc;
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;  // smoothing is for the FP8 V codes
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // smoothed Q: 4-byte aligned, not with the debug dump, not with per-head scales
   if (delta_s && (!aligned(delta_s, 4) || dump || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
@@ -187,6 +195,15 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
   if (v_scale) *v_scale = bhk * D * sizeof(float);
   if (q_mean) *q_mean = bh * (S_q / kBlkQ) * D * sizeof(float);
   if (delta_s) *delta_s = bh * (S_q / kBlkQ) * S_k * sizeof(float);
+  return SAGE_OK;
+}
+
+int sage_v_fp4_buffer_sizes(int B, int H_kv, int S, int D, size_t *v_codes, size_t *v_e8m0) {
+  int rc = check_shape(B, H_kv, S, D);
+  if (rc) return rc;
+  const size_t bhk = (size_t)B * H_kv, S_k = roundup(S, kKvPad);
+  if (v_codes) *v_codes = bhk * S_k * D / 2;
+  if (v_e8m0) *v_e8m0 = bhk * (S_k / kBlkK) * D * 2;
   return SAGE_OK;
 }
 
@@ -314,6 +331,20 @@ int sage_quant_v(const void *v, int dtype, int B, int H, int S, int D, int layou
   return launch_status(launch_quant_v(a, (hipStream_t)stream));
 }
 
+int sage_quant_v_fp4(const void *v, int dtype, int B, int H, int S, int D, int layout, uint8_t *v_codes,
+                     uint8_t *v_e8m0, float *v_mean, void *stream) {
+  QuantVArgs a;
+  if (!v_e8m0 || !aligned(v_e8m0, 4)) return SAGE_ERR_INVALID_ARG;
+  // v_args checks the codes buffer and takes v_e8m0 as the (unused) scale slot
+  int rc = v_args(a, v, dtype, B, H, S, D, layout, v_codes, reinterpret_cast<float *>(v_e8m0), v_mean);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  a.v_scale = nullptr;
+  a.v_e8m0 = v_e8m0;
+  a.code_shift = 1;
+  return launch_status(launch_quant_v_fp4(a, (hipStream_t)stream));
+}
+
 int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale, const void *v,
                   const float *v_scale, const float *v_mean, const float *delta_s, void *out, int dtype, int B, int H,
                   int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant,
@@ -431,6 +462,46 @@ int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, i
   return launch_status(launch_quant_v(a, (hipStream_t)stream));
 }
 
+int sage_varlen_v_fp4_buffer_sizes(int B, int H_kv, int total_k, int D, size_t *v_codes, size_t *v_e8m0) {
+  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, 1, D, SAGE_QK_INT8_BLOCK);
+  if (rc) return rc;
+  const size_t rk = (size_t)varlen_rows(total_k, B, kKvPad);
+  if (v_codes) *v_codes = (size_t)H_kv * rk * D / 2;
+  if (v_e8m0) *v_e8m0 = (size_t)H_kv * (rk / kBlkK) * D * 2;
+  return SAGE_OK;
+}
+
+int sage_quant_v_fp4_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
+                            int max_seqlen_k, int D, uint8_t *v_codes, uint8_t *v_e8m0, float *v_mean,
+                            void *stream) {
+  int rc = check_varlen(B, H_kv, H_kv, 0, total_k, 1, max_seqlen_k, D, SAGE_QK_INT8_BLOCK);
+  if (rc) return rc;
+  if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
+  if (!v || !cu_seqlens_k || !v_codes || !v_e8m0) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(v, 16) || !aligned(v_codes, 16) || !aligned(v_e8m0, 4) || !aligned(cu_seqlens_k, 4) ||
+      (v_mean && !aligned(v_mean, 4)))
+    return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantVArgs a;
+  memset(&a, 0, sizeof a);
+  a.v = v;
+  a.v_fp8 = v_codes;
+  a.v_e8m0 = v_e8m0;
+  a.v_mean = v_mean;
+  a.B = B;
+  a.H = H_kv;
+  a.S = max_seqlen_k;
+  a.D = D;
+  a.layout = SAGE_LAYOUT_NHD;
+  a.dtype = dtype;
+  a.nk = roundup(max_seqlen_k, kKvPad) / kBlkK;
+  a.code_shift = 1;
+  a.varlen = 1;
+  a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
+  a.rows_k = varlen_rows(total_k, B, kKvPad);
+  return launch_status(launch_quant_v_fp4(a, (hipStream_t)stream));
+}
+
 int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                          const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
                          const int32_t *cu_seqlens_q,
@@ -441,12 +512,10 @@ int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode != SAGE_PV_FP8 && pv_mode != SAGE_PV_FP16) return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_pv(pv_mode, v_scale, v_mean))) return rc;
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
     return SAGE_ERR_INVALID_ARG;
-  if (pv_mode == SAGE_PV_FP8 && !v_scale) return SAGE_ERR_INVALID_ARG;
-  if (pv_mode == SAGE_PV_FP16 && v_mean) return SAGE_ERR_INVALID_ARG;
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;

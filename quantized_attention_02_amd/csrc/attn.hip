@@ -7,7 +7,9 @@
 // E4M3 with the static scale 448 and multiplied with per-channel FP8 V; the
 // FP8 products of one tile are summed by the MFMA into a fresh accumulator and
 // then folded into an fp32 output buffer (two-level accumulation).  A pv fp16
-// mode keeps P~ and V in fp16 with fp32 accumulation.
+// mode keeps P~ and V in fp16 with fp32 accumulation; a pv fp4 mode quantises
+// P~ and V to MXFP4 (E2M1 codes, an E8M0 scale per 32-key group of each query
+// row and of each V channel) for the scaled FP4 MFMA ("Kairos" guide, 2.2).
 //
 // Mapping onto CDNA4:
 //  * one work-group = 4 wavefronts = 128 query rows; a wavefront owns 32 query
@@ -28,17 +30,16 @@
 //    B operand of O^T = V^T . P^T on v_mfma_f32_32x32x64_f8f6f4: the key order
 //    they imply is the order the V quantiser stores each 64-key block in
 //    (vpos_key), so P never goes through LDS;
+//  * the softmax denominator sums the same E4M3 weights: one
+//    v_mfma_f32_16x16x128_f8f6f4 per 64-key block multiplies them by a lane
+//    selector of ones (rowsum_ones) and leaves each lane its own query's sum,
+//    instead of 64 fp32 adds per lane and tile (pv fp16: v_dot2_f32_f16 on the
+//    fp16 weights, two per instruction);
 //  * work-groups are numbered so that each XCD (own L2) works through whole
 //    heads; causal work is issued longest query blocks first.
-#include <math.h>
-
-#include <type_traits>
-
-#include "sage_impl.h"
+#include "attn_common.h"
 
 namespace sage {
-
-constexpr float kLog2_448 = 8.807354922057604f;
 
 #ifndef SAGE_ATTN_TN_FP8
 #define SAGE_ATTN_TN_FP8 128
@@ -51,219 +52,7 @@ constexpr float kLog2_448 = 8.807354922057604f;
 #endif
 #ifndef SAGE_ATTN_NBUF_FP8
 #define SAGE_ATTN_NBUF_FP8 2
-#endif  // log2(448): folds the static P~ scale into exp2
-
-// XOR swizzle of the 16-byte chunks of an LDS row (CH = chunks per row) so that
-// the 16 lanes an LDS read serves together hit 16 distinct bank groups when
-// they read the same logical chunk of consecutive rows.
-template <int CH>
-__device__ __forceinline__ int swz(int chunk, int row) {
-  if (CH == 8) return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
-  if (CH == 2) return chunk ^ ((row >> 3) & 1);
-  return chunk ^ ((row >> 2) & 3);
-}
-
-// One wavefront-wide buffer load into LDS: lane i copies 16 bytes from
-// resource offset soff + voff (voff per lane, soff wave-uniform) to
-// lds_base + 16 * i.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint8_t *lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rs, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 16, voff,
-      soff, 0, 0);
-}
-
-// As dma16_buf with 4 bytes a lane (lane i -> lds_base + 4 * i).
-__device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff, uint8_t *lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rs, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) uint8_t *)lds_base, 4, voff,
-      soff, 0, 0);
-}
-
-// Two consecutive floats at a wave-uniform address, read with a scalar load
-// (constant address space), which the vector-memory counter does not track.
-__device__ __forceinline__ float load1_uniform(const float *p) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  typedef const __attribute__((address_space(4))) float *cptr;
-  return *(cptr)(((uint64_t)hi << 32) | lo);
-}
-
-// n consecutive floats through a wave-uniform address (scalar loads)
-template <int N>
-__device__ __forceinline__ void loadn_uniform(const float *p, float *out) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  typedef const __attribute__((address_space(4))) float *cptr;
-  const cptr q = (cptr)(((uint64_t)hi << 32) | lo);
-#pragma unroll
-  for (int i = 0; i < N; ++i) out[i] = q[i];
-}
-
-__device__ __forceinline__ float2 load2_uniform(const float *p) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  typedef const __attribute__((address_space(4))) float *cptr;
-  const cptr q = (cptr)(((uint64_t)hi << 32) | lo);
-  float2 r;
-  r.x = q[0];
-  r.y = q[1];
-  return r;
-}
-
-// s_waitcnt vmcnt(N) (expcnt / lgkmcnt not waited for)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-// wait_vm with a wave-uniform count known at run time (at most 8 kept in
-// flight; a larger count waits for everything)
-__device__ __forceinline__ void wait_vm_n(int n) {
-  switch (n) {
-    case 1: wait_vm<1>(); break;
-    case 2: wait_vm<2>(); break;
-    case 3: wait_vm<3>(); break;
-    case 4: wait_vm<4>(); break;
-    case 5: wait_vm<5>(); break;
-    case 6: wait_vm<6>(); break;
-    case 7: wait_vm<7>(); break;
-    case 8: wait_vm<8>(); break;
-    default: wait_vm<0>(); break;
-  }
-}
-
-// Max / sum of a value over the two half-waves (lanes i and i ^ 32 hold the
-// same query row).  v_permlane32_swap exchanges the halves between its two
-// outputs; one output then holds the lane's own value and the other its
-// partner's, so the pair's max and sum need no lane-dependent select.
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-template <int DT>
-__device__ __forceinline__ void store4(void *out, long long off, float a, float b, float c, float d) {
-  const uint32_t lo = f32_to_out_bits<DT>(a) | (f32_to_out_bits<DT>(b) << 16);
-  const uint32_t hi = f32_to_out_bits<DT>(c) | (f32_to_out_bits<DT>(d) << 16);
-  v2i w = {(int)lo, (int)hi};
-  *reinterpret_cast<v2i *>(reinterpret_cast<uint16_t *>(out) + off) = w;
-}
-
-// Sum of N floats as a balanced tree (independent adds instead of one serial
-// dependency chain).
-template <int N>
-__device__ __forceinline__ float tree_sum(const float *x) {
-  if constexpr (N == 1) {
-    return x[0];
-  } else {
-    return tree_sum<N / 2>(x) + tree_sum<N - N / 2>(x + N / 2);
-  }
-}
-
-// Copy a K tile (TN x D int8) and, in pv fp8 mode, its FP8 V blocks
-// (TN/64 x D x 64, contiguous in HBM) into LDS, swizzled.  Each wavefront
-// issues its share of the 1 KiB wave-copies as buffer loads: scalar resource
-// and tile offset, per-lane offsets koff / voff computed once (tile_offsets).
-template <int D, int TN, int WAVES>
-struct TileCopy {
-  static constexpr int KCH = D / 16;
-  static constexpr int NCOPY = TN * D / 1024;                 // 1 KiB wave-copies per K (or V) tile
-  static constexpr int LOADS = (NCOPY + WAVES - 1) / WAVES;  // per wavefront (the last round may be partial)
-  uint32_t koff[LOADS], voff[LOADS];
-  __device__ __forceinline__ TileCopy(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int w = wave + WAVES * i;
-      const int krow = w * (1024 / D) + lane / KCH;
-      koff[i] = (uint32_t)(krow * D + 16 * swz<KCH>(lane % KCH, krow));
-      const int vrow = w * 16 + (lane >> 2);
-      voff[i] = (uint32_t)(vrow * 64 + 16 * swz<4>(lane & 3, vrow));
-    }
-  }
-  // K copies a wavefront issues per tile
-  __device__ __forceinline__ static int k_loads(int wave) {
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) n += (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY) ? 1 : 0;
-    return n;
-  }
-  template <bool WITH_V>
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int tile_off,
-                                        uint8_t *kbuf, uint8_t *vbuf, int wave) const {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      if (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY)
-        dma16_buf(krs, koff[i], tile_off, kbuf + (wave + WAVES * i) * 1024);
-    if (WITH_V) {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        if (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY)
-          dma16_buf(vrs, voff[i], tile_off, vbuf + (wave + WAVES * i) * 1024);
-    }
-  }
-};
-
-// MXFP4 Q K^T: copy a K tile of packed E2M1 rows (TN x D/2 bytes, 16-byte
-// chunks swizzled by swz<D/32> so that the 16 lanes an LDS read serves hit 16
-// distinct bank groups), then its E8M0 scale bytes (TN x D/32, linear, 4 bytes
-// a lane), and, in pv fp8 mode, the FP8 V blocks as TileCopy does.
-template <int D, int TN, int WAVES>
-struct TileCopy4 {
-  static constexpr int ROWB = D / 2;                          // bytes of a packed K row
-  static constexpr int CPR = ROWB / 16;                       // 16-byte chunks a row (4 or 2)
-  static constexpr int NCOPY = TN * ROWB / 1024;              // 1 KiB wave-copies of codes
-  static constexpr int LOADS = (NCOPY + WAVES - 1) / WAVES;
-  static constexpr int SCB = TN * (D / 32);                   // scale bytes a tile
-  static constexpr int NSC = SCB / 256;                       // 256-byte wave-copies of scales
-  static constexpr int VCOPY = TN * D / 1024;                 // 1 KiB wave-copies of FP8 V
-  static constexpr int VLOADS = (VCOPY + WAVES - 1) / WAVES;
-  static_assert(NSC <= WAVES && SCB % 256 == 0, "scale copy split");
-  uint32_t koff[LOADS], voff[VLOADS];
-  __device__ __forceinline__ TileCopy4(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int krow = (wave + WAVES * i) * (1024 / ROWB) + lane / CPR;
-      koff[i] = (uint32_t)(krow * ROWB + 16 * swz<CPR>(lane % CPR, krow));
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int vrow = (wave + WAVES * i) * 16 + (lane >> 2);
-      voff[i] = (uint32_t)(vrow * 64 + 16 * swz<4>(lane & 3, vrow));
-    }
-  }
-  // code and scale copies a wavefront issues per tile (without V)
-  __device__ __forceinline__ static int k_loads(int wave) {
-    int n = wave < NSC ? 1 : 0;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) n += (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY) ? 1 : 0;
-    return n;
-  }
-  // tile j of the head: codes at j TN ROWB, scales at j SCB, V at j TN D
-  template <bool WITH_V>
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t srs,
-                                        __amdgpu_buffer_rsrc_t vrs, int j, uint8_t *kbuf, uint8_t *vbuf, int wave,
-                                        int lane) const {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      if (NCOPY % WAVES == 0 || wave + WAVES * i < NCOPY)
-        dma16_buf(krs, koff[i], j * TN * ROWB, kbuf + (wave + WAVES * i) * 1024);
-    if (wave < NSC) dma4_buf(srs, (uint32_t)(4 * lane), j * SCB + 256 * wave, kbuf + TN * ROWB + 256 * wave);
-    if (WITH_V) {
-#pragma unroll
-      for (int i = 0; i < VLOADS; ++i)
-        if (VCOPY % WAVES == 0 || wave + WAVES * i < VCOPY)
-          dma16_buf(vrs, voff[i], j * TN * D, vbuf + (wave + WAVES * i) * 1024);
-    }
-  }
-};
+#endif
 
 // pv fp16: the tile's raw 16-bit V rows (TN keys x D channels, 2D bytes a
 // row, as stored in the caller's layout) are copied into LDS as they are (bf16
@@ -380,8 +169,12 @@ k_attn(const AttnArgs a) {
   constexpr int NB = TN / 64;                                // INT8 K blocks per tile
   constexpr int NT = TN / 32;                                // 32-key sub-tiles per tile
   constexpr int KBYTES = TN * D;                             // K tile
-  constexpr int VBYTES = PV == 0 ? TN * D : 2 * TN * D;     // fp8: NB 64-key blocks; fp16: TN raw 16-bit rows
-  constexpr int NVBUF = PV == 0 ? NBUF : 1;                 // fp16 V: one buffer, refilled every tile
+  // V tile in LDS -- fp8: NB 64-key blocks of E4M3 codes; fp16: TN raw 16-bit
+  // rows; fp4: NB 64-key blocks of packed E2M1 codes ([block][channel][32 bytes])
+  // then their E8M0 bytes ([block][channel][key group]), padded to 1 KiB
+  constexpr int V4CODES = TN * D / 2, V4SC = NB * D * 2;
+  constexpr int VBYTES = PV == 0 ? TN * D : PV == 1 ? 2 * TN * D : (V4CODES + V4SC + 1023) / 1024 * 1024;
+  constexpr int NVBUF = PV == 1 ? 1 : NBUF;                 // fp16 V: one buffer, refilled every tile
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
@@ -397,48 +190,8 @@ k_attn(const AttnArgs a) {
   const int hh = lane >> 5, qn = lane & 31;
 
   // ---- work-group -> (head, query block), XCD-aware
-  const int wg = blockIdx.x;
-  const int nbh = a.B * a.H;
   int bh, mrank;
-  if (a.varlen && (a.H & 7) == 0) {
-    // packed batches: sequences differ in length, so every XCD takes the same
-    // share of every sequence: XCD x owns heads [x H/8, (x+1) H/8) of each one
-    // (consecutive heads, so a grouped-query K/V head stays in one L2)
-    const int hx = a.H >> 3, xcd = wg & 7, idx = wg >> 3;
-    const int pairs = a.B * hx;  // (sequence, head) pairs of this XCD
-    int pair;
-    if (CAUSAL) {  // longest blocks first
-      pair = idx % pairs;
-      mrank = idx / pairs;
-    } else {
-      pair = idx / a.nmblk;
-      mrank = idx % a.nmblk;
-    }
-    bh = (pair / hx) * a.H + xcd * hx + pair % hx;
-  } else if (!a.varlen && (nbh & 7) == 0) {
-    const int heads_per_xcd = nbh >> 3;
-    const int xcd = wg & 7, idx = wg >> 3;
-    if (CAUSAL) {  // longest blocks first; the XCD's heads interleaved
-      bh = xcd * heads_per_xcd + idx % heads_per_xcd;
-      mrank = idx / heads_per_xcd;
-    } else {  // one head after the other inside this XCD
-      bh = xcd * heads_per_xcd + idx / a.nmblk;
-      mrank = idx % a.nmblk;
-    }
-  } else if (!a.varlen && !CAUSAL && ((nbh * a.nmblk) & 7) == 0) {
-    // heads not a multiple of 8: XCD x takes the x-th eighth of the (head,
-    // block) order, so that a head's work-groups share one or two L2s instead
-    // of all eight
-    const int flat = (wg & 7) * ((nbh * a.nmblk) >> 3) + (wg >> 3);
-    bh = flat / a.nmblk;
-    mrank = flat % a.nmblk;
-  } else if (CAUSAL) {
-    bh = wg % nbh;
-    mrank = wg / nbh;
-  } else {
-    bh = wg / a.nmblk;
-    mrank = wg % a.nmblk;
-  }
+  map_work(a, CAUSAL, bh, mrank);
   const int mblk = CAUSAL ? a.nmblk - 1 - mrank : mrank;
   const int b = bh / a.H, h = bh % a.H;
   // grouped-query attention: H / H_kv consecutive query heads read one K/V head
@@ -490,7 +243,11 @@ k_attn(const AttnArgs a) {
   if (CAUSAL) ntiles = min(ntiles, min(q0 + kBlockM - 1, Sk - 1) / TN + 1);
 
   float m = -INFINITY;  // running max (log2 domain, scaled scores)
-  float l = 0.0f;       // running sum over this half-wave's keys
+  float l = 0.0f;       // pv fp16: running sum of the fp16 weights of this half-wave's keys
+  // pv fp8 / fp4: running sum of the quantised weights over both half-waves, as
+  // the fp32 accumulator of the row-sum product (element 0; the others are not read)
+  v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const v8i ones = PV == 2 ? rowsum_ones_fp4(lane) : rowsum_ones(lane);
   v16f O[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
@@ -498,7 +255,8 @@ k_attn(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) O[c][r] = 0.0f;
 
   const int8_t *kbase = a.k_i8 + ks.row0 * (FP4 ? D / 2 : D);
-  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + ks.row0 * D;
+  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.v) + ks.row0 * (PV == 2 ? D / 2 : D);
+  const uint8_t *v4sbase = reinterpret_cast<const uint8_t *>(a.v_scale) + ks.row0 * (D / 32);  // pv fp4 V scales
   const float *kscale = a.k_scale + (TOKEN ? ks.row0 : LANE ? ks.row0 >> 4 : ks.row0 >> 6);  // INT8 modes
   const uint8_t *kscb = reinterpret_cast<const uint8_t *>(a.k_scale) + ks.row0 * (D / 32);  // FP4
   const HeadView hv{ks.base, ks.stride};  // pv fp16: the caller's V
@@ -510,8 +268,13 @@ k_attn(const AttnArgs a) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kbytes);
   const __amdgpu_buffer_rsrc_t srs = TOKEN ? make_rsrc(kscale, ntiles * TN * 4)  // per-key K scales
                                            : make_rsrc(kscb, ntiles * TN * (D / 32));  // FP4 K scales
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV == 0 ? (const void *)vbase : (const void *)kbase,
-                                               PV == 0 ? vbytes : kbytes);  // (pv fp16 copies V itself)
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(PV != 1 ? (const void *)vbase : (const void *)kbase,
+                                               PV == 0 ? vbytes : PV == 2 ? ntiles * V4CODES : kbytes);
+  const __amdgpu_buffer_rsrc_t v4srs = make_rsrc(v4sbase, PV == 2 ? ntiles * V4SC : 0);  // (pv fp16 copies V itself)
+  // pv fp4 V codes: 1 KiB wave-copies of 32-byte channel rows, 16-byte chunks
+  // swizzled by swz<2>, which depends on the row only through bit 3: copy w is
+  // copy 0 shifted by 1 KiB w, and this is the lane's offset in copy 0
+  const uint32_t v4off = (uint32_t)((lane >> 1) * 32 + 16 * swz<2>(lane & 1, lane >> 1));
   // smoothed Q: delta is stored [bh][128-key tile][query block][128]; this
   // wavefront's row of tile j (its query block) is 512 contiguous bytes at
   // dbase + j * dtile; only wavefronts with queries copy (a trailing wavefront's
@@ -528,6 +291,15 @@ k_attn(const AttnArgs a) {
     } else {
       copy.template issue<PV == 0>(krs, vrs, j * TN * D, kb, vb, wave);
       n = copy.k_loads(wave);
+    }
+    if constexpr (PV == 2) {  // FP4 V codes and scales
+      constexpr int NCP = V4CODES / 1024;
+#pragma unroll
+      for (int i = 0; i < (NCP + WAVES - 1) / WAVES; ++i) {
+        const int w = wave + WAVES * i;
+        if (NCP % WAVES == 0 || w < NCP) dma16_buf(vrs, v4off, j * V4CODES + 1024 * w, vb + 1024 * w);
+      }
+      if (wave < V4SC / 256) dma4_buf(v4srs, (uint32_t)(4 * lane), j * V4SC + 256 * wave, vb + V4CODES + 256 * wave);
     }
     if constexpr (TOKEN) {
       // every wavefront needs every key's scale: the first TN / 64 copy them,
@@ -576,6 +348,7 @@ k_attn(const AttnArgs a) {
     }
     float p[16 * NT];
     float alpha = 1.0f;
+    float gq[NB];  // pv fp4: per block, this lane's largest exponent argument (its key group's largest weight)
     if (work) {
       // ---- S^T = K . Q^T for the NT 32-key sub-tiles, one INT8 K block (two
       //      sub-tiles) after the other, so that the first block's row max and
@@ -773,6 +546,31 @@ k_attn(const AttnArgs a) {
       alpha = __builtin_amdgcn_exp2f(m - mn);
       const float sub = PV == 0 ? mn - kLog2_448 : mn;
       m = mn;
+      if constexpr (PV == 2) {
+        // log2 of each key group's largest weight, formed by the same FMA as the
+        // weights below, plus a bound on that FMA's rounding against the row max
+        // (the max is a rounded product, so the weight of the max key itself, 1 in
+        // exact arithmetic, can come out a few ulps below 1; the MX exponent rule
+        // would then drop a binade and saturate it to 6 * 2^-3 = 0.75).  With the
+        // bound such a group takes the exponent of 1 and the key the code of 1.
+        const float nudge = __builtin_fmaf(fabsf(sub), 0x1p-22f, 0x1p-24f);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          // (the same arms as max_convert: fp32 maxima with smoothed Q, FP4 or
+          // per-token scales; int32 maxima per lane group or per block otherwise)
+          float g = -INFINITY;
+          if constexpr (FP4 || QS || TOKEN) {
+            g = __builtin_fmaf(mxf[blk], c2[blk], -sub);
+          } else if constexpr (LANE) {
+#pragma unroll
+            for (int t = 2 * blk; t < 2 * blk + 2; ++t)
+              g = fmaxf(g, mxb[t] == INT_MIN ? -INFINITY : __builtin_fmaf((float)mxb[t], c2[t], -sub));
+          } else {
+            g = mxb[blk] == INT_MIN ? -INFINITY : __builtin_fmaf((float)mxb[blk], c2[blk], -sub);
+          }
+          gq[blk] = g + nudge;
+        }
+      }
       // ---- p = exp2(s * c2 - sub)  (= 448 p~ in fp8 mode); masked keys are then
       //      zeroed in a separate pass that only boundary tiles take; row sum
 #pragma unroll
@@ -788,10 +586,65 @@ k_attn(const AttnArgs a) {
           for (int r = 0; r < 16; ++r)
             if (32 * t + 8 * (r >> 2) + (r & 3) > mlim) p[16 * t + r] = 0.0f;
       }
-      l = alpha * l + tree_sum<16 * NT>(p);
     }
 
-    if constexpr (PV == 0) {
+    if constexpr (PV == 2) {
+      if (work) {
+        // ---- P~ -> MXFP4: this lane's 32 weights of each 64-key block are one
+        //      key group; its E8M0 scale comes from the group's largest weight,
+        //      formed by the same FMA and exp2 as that weight (so bit-identical),
+        //      times 2^-2 (the MX rule); nibble 16 t' + r = weight of s[2 blk + t'][r]
+        float sc[NB];
+        int pe[NB];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          // E8M0 byte = biased exponent of the group max, minus 2 (the MX rule);
+          // the conversion takes the exponent of its scale operand, given here as
+          // that power of two.  A group without weights (codes 0) takes the byte 1.
+          const int ex = (int)((__float_as_uint(__builtin_amdgcn_exp2f(gq[blk])) >> 23) & 0xff);
+          pe[blk] = max(ex - 2, 1);
+          sc[blk] = __uint_as_float((uint32_t)pe[blk] << 23);
+        }
+        v8i pk[NB];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int t = 2 * blk + (w >> 1), r0 = 8 * (w & 1);
+            unsigned word = 0;
+            static_for<0, 4>([&](auto SEL) {
+              constexpr int sel = decltype(SEL)::value;
+              const int i0 = 16 * t + r0 + 2 * sel;
+              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, p[i0], p[i0 + 1], sc[blk], sel);
+            });
+            pk[blk][w] = (int)word;
+          }
+#pragma unroll
+          for (int w = 4; w < 8; ++w) pk[blk][w] = 0;
+        }
+        lacc[0] *= alpha;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
+        }
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+          lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[blk], lacc, 4, 4, 0, 127, 0, pe[blk]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) {
+            const int row = blk * D + 32 * c + qn;
+            const v4i vf = *reinterpret_cast<const v4i *>(vb + row * 32 + 16 * swz<2>(hh, row));
+            const int vsb = vb[V4CODES + 2 * row + hh];
+            const v8i va = {vf[0], vf[1], vf[2], vf[3], 0, 0, 0, 0};
+            O[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pk[blk], O[c], 4, 4, 0, vsb, 0, pe[blk]);
+          }
+        }
+      }
+    } else if constexpr (PV == 0) {
       if (work) {
         // ---- P~ -> E4M3: byte 16t' + r of operand blk = key of s[2 blk + t'][r]
         v8i pk[NB];
@@ -811,12 +664,16 @@ k_attn(const AttnArgs a) {
         //      (level 1) and adds that partial sum to the fp32 O registers passed
         //      as its C operand (level 2).  O is rescaled in place first; the
         //      rescale is skipped when no row of the wavefront changed its max.
+        lacc[0] *= alpha;
         if (__any(alpha != 1.0f)) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
         }
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+          lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[blk], lacc, 0, 0, 0, 0, 0, 0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -839,6 +696,15 @@ k_attn(const AttnArgs a) {
         for (int s8 = 0; s8 < 2 * NT; ++s8)
 #pragma unroll
           for (int i = 0; i < 8; ++i) ph[s8][i] = (_Float16)p[8 * s8 + i];
+        // row sum of the fp16 weights, two per v_dot2_f32_f16, in four chains
+        const v2h one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s8 = 0; s8 < 2 * NT; ++s8)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ls[i] = __builtin_amdgcn_fdot2(v2h{ph[s8][2 * i], ph[s8][2 * i + 1]}, one2, ls[i], false);
+        l = alpha * l + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
         if (__any(alpha != 1.0f)) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
@@ -859,19 +725,20 @@ k_attn(const AttnArgs a) {
     }
   };
 
-  if (PV == 0 && tid < D) {
-    vsc[tid] = a.v_scale[(long long)bhk * D + tid];
+  if (PV != 1 && tid < D) {
+    vsc[tid] = PV == 0 ? a.v_scale[(long long)bhk * D + tid] : 1.0f;
     vmn[tid] = a.v_mean ? a.v_mean[(long long)bhk * D + tid] : 0.0f;
   }
 
   // ---- main loop: tile j is computed from buffer j % NBUF while tiles
   //      j + 1 .. j + NBUF - 1 are in flight; one barrier per tile publishes the next
   constexpr int LPT = (PV == 0 ? 2 : 1) * TN * D / 1024 / WAVES;  // DMA instructions per tile per wavefront
+  static_assert(PV != 2 || NBUF == 2, "pv fp4 copies count as whole-tile waits");
   static_assert(NBUF == 2 || (TN * D / 1024) % WAVES == 0, "partial vm waits need an even copy split");
   static_assert(NBUF == 2 || !FP4, "partial vm waits assume the INT8 copy counts");
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
-    if (u < ntiles) issue_tile(u, u, kbuf[u], vbuf[PV == 0 ? u : 0]);
+    if (u < ntiles) issue_tile(u, u, kbuf[u], vbuf[PV != 1 ? u : 0]);
   wait_vm<0>();
   __syncthreads();
   for (int j0 = 0; j0 < ntiles; j0 += NBUF) {
@@ -886,8 +753,8 @@ k_attn(const AttnArgs a) {
       // prefetch so that the tile can wait for its V alone
       if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, j * TN, Sk, vbuf[0], wave);
       int pend = 0;
-      if (jn < ntiles) pend = issue_tile(jn, un, kbuf[un], vbuf[PV == 0 ? un : 0]);
-      tile(j, u, kbuf[u], vbuf[PV == 0 ? u : 0], pend);
+      if (jn < ntiles) pend = issue_tile(jn, un, kbuf[un], vbuf[PV != 1 ? un : 0]);
+      tile(j, u, kbuf[u], vbuf[PV != 1 ? u : 0], pend);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
       __syncthreads();
@@ -895,8 +762,8 @@ k_attn(const AttnArgs a) {
   }
 
   if (!active) return;
-  // ---- epilogue: combine the two half-wave sums, normalise, store
-  const float lt = halves_sum(l);
+  // ---- epilogue: the row sum (pv fp16: combine the two half-wave sums), normalise, store
+  const float lt = PV == 1 ? halves_sum(l) : lacc[0];
   if (qi >= Sq) return;
   const float rl = lt > 0.0f ? 1.0f / lt : 0.0f;  // a row without keys (empty sequence) is 0
   const long long off = qs.base + (long long)qi * qs.stride;
@@ -912,16 +779,16 @@ k_attn(const AttnArgs a) {
         o[1] = O[c][4 * g + 1] * (vs.y * rl);
         o[2] = O[c][4 * g + 2] * (vs.z * rl);
         o[3] = O[c][4 * g + 3] * (vs.w * rl);
-        if (a.v_mean) {  // smoothed V: add the channel means back
-          const float4 vm = *reinterpret_cast<const float4 *>(vmn + d0);
-          o[0] += vm.x;
-          o[1] += vm.y;
-          o[2] += vm.z;
-          o[3] += vm.w;
-        }
-      } else {
+      } else {  // pv fp4: the V scales were applied inside the MFMA; pv fp16: unscaled V
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = O[c][4 * g + i] * rl;
+      }
+      if (PV != 1 && a.v_mean) {  // smoothed V: add the channel means back
+        const float4 vm = *reinterpret_cast<const float4 *>(vmn + d0);
+        o[0] += vm.x;
+        o[1] += vm.y;
+        o[2] += vm.z;
+        o[3] += vm.w;
       }
       store4<DT>(a.out, off + d0, o[0], o[1], o[2], o[3]);
     }
@@ -931,11 +798,11 @@ k_attn(const AttnArgs a) {
 // MI355X against 64-key tiles at 2 and 3 wavefronts per SIMD: fewer row-max
 // exchanges and O rescales per key outweigh the lower occupancy).
 template <int PV>
-struct TileCfg {
-  static constexpr int TN = PV == 0 ? SAGE_ATTN_TN_FP8 : 128;
-  static constexpr int WPS = PV == 0 ? SAGE_ATTN_WPS_FP8 : 2;
-  static constexpr int WAVES = PV == 0 ? SAGE_ATTN_WAVES_FP8 : 4;
-  static constexpr int NBUF = PV == 0 ? SAGE_ATTN_NBUF_FP8 : 2;
+struct TileCfg {  // pv fp4 (PV == 2) shares the pv fp8 shape
+  static constexpr int TN = PV != 1 ? SAGE_ATTN_TN_FP8 : 128;
+  static constexpr int WPS = PV != 1 ? SAGE_ATTN_WPS_FP8 : 2;
+  static constexpr int WAVES = PV != 1 ? SAGE_ATTN_WAVES_FP8 : 4;
+  static constexpr int NBUF = PV != 1 ? SAGE_ATTN_NBUF_FP8 : 2;
 };
 
 template <int D, int PV, int DT, bool CAUSAL, int QK>
@@ -976,10 +843,11 @@ static hipError_t launch2(const AttnArgs &a, bool dump, hipStream_t st) {
 
 template <int D>
 static hipError_t launch1(const AttnArgs &a, bool dump, hipStream_t st) {
+  if (a.pv == 2) return launch2<D, 2>(a, dump, st);
   return a.pv == 0 ? launch2<D, 0>(a, dump, st) : launch2<D, 1>(a, dump, st);
 }
 
-int attn_tile_keys(int pv_mode) { return pv_mode == 0 ? TileCfg<0>::TN : TileCfg<1>::TN; }
+int attn_tile_keys(int pv_mode) { return pv_mode == 1 ? TileCfg<1>::TN : TileCfg<0>::TN; }
 
 hipError_t launch_attn(const AttnArgs &a, bool dump, hipStream_t stream) {
   return a.D == 64 ? launch1<64>(a, dump, stream) : launch1<128>(a, dump, stream);

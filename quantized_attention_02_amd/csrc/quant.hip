@@ -102,6 +102,11 @@ __device__ inline Seg v_seg(const QuantVArgs &a, int b, int h) {
   return a.varlen ? varlen_seg(a.sk, b, h, a.H, D, a.rows_k, kKvPad)
                   : fixed_seg(a.layout, b, h, a.H, a.S, a.nk * kBlkK, D);
 }
+// The chunk partials of one V head sit at the start of the head's run of the
+// code buffer: roundup(S, 128) * D bytes for E4M3 codes, half that for E2M1.
+__device__ inline uint8_t *v_partials(const QuantVArgs &a, const Seg &sg, int D) {
+  return a.v_fp8 + ((sg.row0 * D) >> a.code_shift);
+}
 __device__ inline int ceil_div(int x, int m) { return (x + m - 1) / m; }
 
 // Work-group -> (batch entry or sequence b, head h, block blk) of a per-block
@@ -937,7 +942,7 @@ __device__ inline void vstats_part_wg(const QuantVArgs &a, int wg) {
   const int bh = wg / nch, chunk = wg % nch;
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
   if (chunk >= n_chunks(sg.S)) return;
-  chunk_stats<DT, D>((const uint16_t *)a.v, sg, chunk, a.v_fp8 + sg.row0 * D);
+  chunk_stats<DT, D>((const uint16_t *)a.v, sg, chunk, v_partials(a, sg, D));
 }
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_vstats_part(const QuantVArgs a) { vstats_part_wg<DT, D>(a, blockIdx.x); }
@@ -948,7 +953,7 @@ __device__ inline void vamax_part_wg(const QuantVArgs &a, int wg) {
   const int bh = wg / nch, chunk = wg % nch;
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
   if (chunk >= n_chunks(sg.S)) return;
-  chunk_reduce<DT, D, true>((const uint16_t *)a.v, sg, chunk, a.v_fp8 + sg.row0 * D);
+  chunk_reduce<DT, D, true>((const uint16_t *)a.v, sg, chunk, v_partials(a, sg, D));
 }
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_vamax_part(const QuantVArgs a) { vamax_part_wg<DT, D>(a, blockIdx.x); }
@@ -961,7 +966,7 @@ __device__ inline void vamax_wg(const QuantVArgs &a, int wg) {
   const Seg sg = v_seg<D>(a, bh / a.H, bh % a.H);
   const int nch = n_chunks(sg.S);
   if (a.v_mean) {  // smoothing: combine sums, maxima and minima
-    const uint8_t *base = a.v_fp8 + sg.row0 * D;
+    const uint8_t *base = v_partials(a, sg, D);
     double t = 0.0;
     float hi = -INFINITY, lo = INFINITY;
     for (int c = 0; c < nch; ++c) {
@@ -975,7 +980,7 @@ __device__ inline void vamax_wg(const QuantVArgs &a, int wg) {
     a.v_scale[i] = sg.S > 0 ? fmaxf(hi - mean, mean - lo) : 0.0f;
     return;
   }
-  const float *part = reinterpret_cast<const float *>(a.v_fp8 + sg.row0 * D);
+  const float *part = reinterpret_cast<const float *>(v_partials(a, sg, D));
   float v[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) v[c] = c < nch ? part[(long long)c * D + d] : 0.0f;
@@ -1036,6 +1041,61 @@ __device__ inline void vconvert_wg(const QuantVArgs &a, int wg, int tid) {
 template <int DT, int D>
 __global__ __launch_bounds__(2 * D) void k_vconvert(const QuantVArgs a) { vconvert_wg<DT, D>(a, blockIdx.x, threadIdx.x); }
 
+// ---------------------------------------------------------------------------
+// V for the micro-scaled FP4 P~ V product: one work-group per 64-key block of a
+// head.  The block's 16-bit rows are staged in LDS (coalesced 16-byte loads);
+// thread (d, half) then gathers channel d of the 32 keys of its key group --
+// the keys SAGE_VPOS_KEY(32 half + i), i = 0..31, i.e. those whose offset has
+// bit 2 equal to `half`, in the order the attention kernel holds P~ -- takes
+// the group's MX exponent e = floor(log2 amax) - 2 (clamped to [-127, 127]),
+// and writes the 32 E2M1 codes of x / 2^e as 16 bytes (code of position 2u in
+// the low nibble of byte u) and the E8M0 byte e + 127.  Keys past the sequence
+// count as 0.  With V smoothing the channel means (from the statistics passes)
+// are subtracted first.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(2 * D) void k_v4convert(const QuantVArgs a) {
+  constexpr int RS = D + 8;  // LDS row stride in 16-bit elements (16-byte aligned rows, banks offset)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kBlkK][RS];
+  const int tid = threadIdx.x;
+  int b, h, t;
+  block_of(a.varlen, a.sk, a.B, a.H, a.nk, a.rows_k, kKvPad, kBlkK, blockIdx.x, b, h, t);
+  const int bh = b * a.H + h;
+  const Seg hv = v_seg<D>(a, b, h);
+  if (t >= ceil_div(hv.S, kKvPad) * (kKvPad / kBlkK)) return;  // past this sequence's blocks
+  const uint16_t *v = (const uint16_t *)a.v;
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int ROUNDS = kBlkK * CPR / (2 * D);  // chunks a thread stages
+#pragma unroll
+  for (int u = 0; u < ROUNDS; ++u) {
+    const int ci = tid + u * 2 * D, row = ci / CPR, c8 = (ci % CPR) * 8;
+    const int s = t * kBlkK + row;
+    const v4i x = s < hv.S ? *reinterpret_cast<const v4i *>(v + hv.base + (long long)s * hv.stride + c8)
+                           : v4i{0, 0, 0, 0};
+    *reinterpret_cast<v4i *>(&tile[row][c8]) = x;
+  }
+  __syncthreads();
+  const int d = tid >> 1, half = tid & 1;
+  const float mean = a.v_mean ? a.v_mean[(long long)bh * D + d] : 0.0f;
+  float x[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int key = vpos_key(32 * half + i);
+    const bool valid = t * kBlkK + key < hv.S;
+    x[i] = valid ? in_to_f32<DT>(tile[key][d]) - mean : 0.0f;
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  const int e = mx_exponent(amax);
+  v4i w = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    w[i >> 3] |= (int)(e2m1_code(__builtin_ldexpf(x[i], -e)) << (4 * (i & 7)));
+  const long long blk = (hv.row0 >> 6) + t;  // 64-key block of the head's buffer
+  *reinterpret_cast<v4i *>(a.v_fp8 + (blk * D + d) * 32 + 16 * half) = w;
+  a.v_e8m0[(blk * D + d) * 2 + half] = (uint8_t)(e + 127);
+}
+
 template <int D>
 __device__ inline void vscale_wg(const QuantVArgs &a, int wg) {
   const long long i = (long long)wg * kThreads + threadIdx.x;
@@ -1086,6 +1146,35 @@ static void launch_v(const QuantVArgs &a, hipStream_t stream) {
   const dim3 gv(a.varlen ? a.H * (int)(a.rows_k / kBlkK) : bh * a.nk);  // 64-key tiles, as the K blocks
   hipLaunchKernelGGL((k_vconvert<DT, D>), gv, dim3(2 * D), 0, stream, a);
   hipLaunchKernelGGL((k_vscale<D>), dim3(gd), dim3(kThreads), 0, stream, a);
+}
+
+// MXFP4 V: with smoothing, the channel statistics passes first (partials staged
+// in the code buffer, the means written to v_mean, the abs-maxima -- unused
+// here -- to the scale buffer, which the conversion then overwrites).
+template <int DT, int D>
+static void launch_v4(const QuantVArgs &a, hipStream_t stream) {
+  const int bh = a.B * a.H;
+  if (a.v_mean) {
+    QuantVArgs s = a;
+    s.v_scale = reinterpret_cast<float *>(a.v_e8m0);
+    const int gd = (bh * D + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL((k_vstats_part<DT, D>), dim3(bh * chunk_grid(a.varlen ? a.sk.max_len : a.S)), dim3(kThreads),
+                       0, stream, s);
+    hipLaunchKernelGGL((k_vamax<D>), dim3(gd), dim3(kThreads), 0, stream, s);
+  }
+  const dim3 gv(a.varlen ? a.H * (int)(a.rows_k / kBlkK) : bh * a.nk);
+  hipLaunchKernelGGL((k_v4convert<DT, D>), gv, dim3(2 * D), 0, stream, a);
+}
+
+hipError_t launch_quant_v_fp4(const QuantVArgs &a, hipStream_t stream) {
+  if (a.D == 64) {
+    if (a.dtype == 0) launch_v4<0, 64>(a, stream);
+    else launch_v4<1, 64>(a, stream);
+  } else {
+    if (a.dtype == 0) launch_v4<0, 128>(a, stream);
+    else launch_v4<1, 128>(a, stream);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -14,6 +14,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBlkQ = 32;  // Q tokens per INT8 scale (one wavefront's MFMA row tile)
 constexpr int kBlkK = 64;  // K tokens per INT8 scale (one 64-key block)
@@ -142,11 +144,13 @@ struct QuantQKArgs {
 
 struct QuantVArgs {
   const void *v;
-  uint8_t *v_fp8;
+  uint8_t *v_fp8;   // E4M3 codes (pv fp8) or packed E2M1 codes (pv fp4)
+  uint8_t *v_e8m0;  // pv fp4: E8M0 scale per (64-key block, channel, key group)
   float *v_scale;
   float *v_mean;  // V smoothing: channel means out (nullptr: no smoothing)
   int B, H, S, D, layout, dtype;
   int nk;  // 64-key tiles per head (grid extent)
+  int code_shift;  // log2(codes per byte) of v_fp8: 0 E4M3, 1 packed E2M1
   int varlen;
   SeqTable sk;
   long long rows_k;
@@ -156,7 +160,7 @@ struct AttnArgs {
   const int8_t *q_i8, *k_i8;
   const float *q_scale, *k_scale;
   const void *v;
-  const float *v_scale;
+  const float *v_scale;  // pv fp8: per-channel scales; pv fp4: the E8M0 bytes (reinterpreted)
   const float *v_mean;  // smoothed V: channel means added to the output (nullptr: none)
   const float *delta_s;  // smoothed Q: pre-processing term [B][H][nq][S_k] (nullptr: none)
   void *out;
@@ -173,6 +177,7 @@ struct AttnArgs {
 
 hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream);
 hipError_t launch_quant_v(const QuantVArgs &a, hipStream_t stream);
+hipError_t launch_quant_v_fp4(const QuantVArgs &a, hipStream_t stream);
 // pre-processing term of smoothed Q, delta[B][H][nq][S_k] (a.q_mean and a.k_mean read)
 hipError_t launch_quantize_qkv(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t stream);
 hipError_t launch_qk_delta(const QuantQKArgs &a, float *delta, hipStream_t stream);

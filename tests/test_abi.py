@@ -105,7 +105,7 @@ BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dic
          dict(v_mean=P + 2)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
             dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
-            dict(is_causal=2), dict(pv_mode=2), dict(pv_mode=-1), dict(dtype=5), dict(D=100), dict(S=0),
+            dict(is_causal=2), dict(pv_mode=3), dict(pv_mode=-1), dict(pv_mode=2, v_scale=None), dict(pv_mode=2, v_scale=P + 2), dict(dtype=5), dict(D=100), dict(S=0),
             dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=5), dict(qk_quant=4, delta_s=P),
             dict(v_mean=P + 1), dict(pv_mode=1, v_scale=None, v_mean=P),  # smoothing is for the FP8 V codes
             dict(delta_s=P + 2),
@@ -269,7 +269,7 @@ BAD_QK_VL = [dict(cu_q=None), dict(cu_k=P + 2), dict(B=0), dict(H_kv=3), dict(to
 BAD_V_VL = [dict(cu_k=None), dict(v=P + 8), dict(max_k=0), dict(total_k=-3), dict(H_kv=0), dict(v_scale=None),
             dict(v_mean=P + 2)]
 BAD_ATTN_VL = [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P + 1), dict(is_causal=3), dict(pv_mode=5), dict(qk_quant=7),
-               dict(v_mean=P + 3), dict(pv_mode=1, v_scale=None),
+               dict(v_mean=P + 3), dict(pv_mode=1, v_scale=None), dict(pv_mode=2, v_scale=None), dict(pv_mode=3),
                dict(sm_scale=0.0), dict(v_scale=None), dict(out=P + 4), dict(H_kv=3), dict(max_q=0), dict(B=-1),
                # pv fp16 reads 128-token slices of V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
                dict(pv_mode=1, v_scale=None, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
@@ -312,3 +312,50 @@ def test_size_limits_in_the_header():
     assert qa.sage_buffer_sizes(256, 256, 64, 33, 64, 0)["k_i8"] == 256 * 64 * 128 * 64  # the most heads
     with pytest.raises(qa.SageError):
         qa.sage_buffer_sizes(257, 256, 64, 33, 64, 0)
+
+
+# MXFP4 V (pv fp4): codes 16-byte and E8M0 bytes 4-byte aligned
+GOOD_V4 = dict(v=P, dtype=1, B=2, H=3, S=300, D=128, layout=1, v_codes=P, v_e8m0=P, v_mean=P, stream=None)
+BAD_V4 = [dict(v=None), dict(v_codes=None), dict(v_e8m0=None), dict(v_codes=P + 8), dict(v_e8m0=P + 2),
+          dict(v_mean=P + 1), dict(v=P + 4), dict(dtype=2), dict(layout=2), dict(D=96), dict(S=0), dict(B=0),
+          dict(H=0), dict(S=(1 << 20) + 1)]
+GOOD_V4_VL = dict(v=P, dtype=0, cu_k=P, B=3, H_kv=2, total_k=200, max_k=90, D=64, v_codes=P, v_e8m0=P, v_mean=None,
+                  stream=None)
+BAD_V4_VL = [dict(cu_k=None), dict(cu_k=P + 2), dict(v=None), dict(v_codes=P + 4), dict(v_e8m0=None),
+             dict(v_e8m0=P + 1), dict(max_k=0), dict(total_k=-1), dict(H_kv=0), dict(D=32), dict(v_mean=P + 2)]
+
+
+@pytest.mark.parametrize("bad", BAD_V4, ids=[str(b) for b in BAD_V4])
+def test_quant_v_fp4_rejects(bad):
+    assert qa.sage_quant_v_fp4(*{**GOOD_V4, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_V4_VL, ids=[str(b) for b in BAD_V4_VL])
+def test_quant_v_fp4_varlen_rejects(bad):
+    assert qa.sage_quant_v_fp4_varlen(*{**GOOD_V4_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_v_fp4_buffer_sizes():
+    # [B][H_kv][S_k / 64][D][32] code bytes and [..][2] E8M0 bytes, S_k = roundup(S, 128)
+    assert qa.sage_v_fp4_buffer_sizes(2, 3, 300, 128) == {"v_codes": 6 * 384 * 64, "v_e8m0": 6 * 6 * 128 * 2}
+    assert qa.sage_v_fp4_buffer_sizes(1, 1, 1, 64) == {"v_codes": 128 * 32, "v_e8m0": 2 * 64 * 2}
+    rk = qa.varlen_rows(200, 3, 128)
+    assert qa.sage_varlen_v_fp4_buffer_sizes(3, 2, 200, 64) == {"v_codes": 2 * rk * 32, "v_e8m0": 2 * (rk // 64) * 128}
+    L = qa.lib()
+    for bad in [(0, 1, 1, 64), (1, 0, 1, 64), (1, 1, 0, 64), (1, 1, 1, 96), (1, 1, (1 << 20) + 1, 64)]:
+        assert L.sage_v_fp4_buffer_sizes(*bad, None, None) == qa.SAGE_ERR_INVALID_ARG, bad
+    for bad in [(0, 1, 1, 64), (1, 0, 1, 64), (1, 1, -1, 64), (1, 1, 1, 32)]:
+        assert L.sage_varlen_v_fp4_buffer_sizes(*bad, None, None) == qa.SAGE_ERR_INVALID_ARG, bad
+    # the E8M0 buffer holds the smoothing pass's fp32 per-channel statistics (4 bytes per
+    # head and channel) until the conversion overwrites it
+    for B, H, S, D in [(1, 1, 1, 64), (2, 3, 300, 128)]:
+        assert qa.sage_v_fp4_buffer_sizes(B, H, S, D)["v_e8m0"] >= 4 * B * H * D
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
+def test_valid_fp4_pv_arguments_without_a_device_report_no_device():
+    assert qa.sage_quant_v_fp4(*GOOD_V4.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_quant_v_fp4_varlen(*GOOD_V4_VL.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(pv_mode=2) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(pv_mode=2, v_mean=P) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "pv_mode": 2}.values()) == qa.SAGE_ERR_NO_DEVICE
