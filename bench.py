@@ -60,7 +60,11 @@ def parse():
                    help="Q/K quantisation: INT8 per block, per Q token / 16-key lane group, per token or per head, or MXFP4")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
-                   help="heads in the CPU-oracle sample (0: as many as take about 12 s)")
+                   help="heads in the CPU-oracle sample (0: as many as take about 12 s; with --oracle-timing: all)")
+    p.add_argument("--oracle-timing", action="store_true",
+                   help="only time the CPU oracle on the workload (all heads, or --cpu-heads of them scaled to "
+                        "all) on the host cores, median of --oracle-repeats runs; no GPU use")
+    p.add_argument("--oracle-repeats", type=int, default=1)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return p.parse_args()
@@ -104,7 +108,24 @@ def oracle_qk(qk):
     return {"int8": {}, "int8_lane": {"gran": "lane"}, "int8_token": {"gran": "token"}, "int8_head": {"gran": "head"}, "mxfp4": {"qk_format": "fp4"}}[qk]
 
 
-def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=False):
+def cpu_model():
+    """The host CPU's model name and logical core count."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=False, repeats=1, all_heads_ok=False):
+    """The CPU oracle (quantisation + attention, every query row) timed on a
+    sample of the workload's heads: nheads of them (0: as many as take about
+    CPU_SAMPLE_S seconds, or all of them with all_heads_ok), median of `repeats`
+    runs, scaled to TOPS."""
     import numpy as np
 
     import oracle as O
@@ -142,6 +163,8 @@ def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=Fals
             return time.perf_counter() - t0
         what = "heads"
 
+    if nheads <= 0 and all_heads_ok:
+        nheads = len(all_heads)
     if nheads <= 0:  # size the sample to about CPU_SAMPLE_S seconds from a one-head probe
         t1 = run(all_heads[-1:])
         per_op = t1 / head_ops(*all_heads[-1])
@@ -151,12 +174,33 @@ def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=Fals
                 break
             acc += head_ops(*hd) * per_op
             nheads += 1
-    heads = all_heads[:nheads]
-    dt = run(heads)
+    heads = all_heads[:min(nheads, len(all_heads))]
+
+    def run_chunked(heads):
+        # long samples run in chunks of about 30 s of work, reporting progress
+        # on stderr; the chunk times add up to the sample's time
+        per = max(1, int(30.0 / max(per_head_s, 1e-9)))
+        total = 0.0
+        for i in range(0, len(heads), per):
+            total += run(heads[i:i + per])
+            if len(heads) > per:
+                print(f"oracle: {min(i + per, len(heads))}/{len(heads)} {what}, {total:.1f} s", file=sys.stderr,
+                      flush=True)
+        return total
+
+    per_head_s = run(heads[:1]) if len(heads) > 1 else 0.0
+    times = sorted(run_chunked(heads) for _ in range(max(1, repeats)))
+    dt = times[len(times) // 2]
     ops = sum(head_ops(*hd) for hd in heads)
+    model, ncpu = cpu_model()
+    scale = sum(head_ops(*hd) for hd in all_heads) / ops
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": O.num_threads(), "kind": "oracle",
+            "cpu": model, "host_logical_cpus": ncpu,
             "sample": f"{len(heads)} of {len(all_heads)} {what} of {w.name}, all query rows "
-                      f"(quantisation of Q/K/V + attention), {dt:.2f} s wall"}
+                      f"(quantisation of Q/K/V + attention), {dt:.2f} s wall"
+                      + (f" (median of {len(times)}: {', '.join(f'{t:.2f}' for t in times)})" if len(times) > 1 else ""),
+            "seconds": round(dt, 3), "whole_workload_seconds": round(dt * scale, 2),
+            "whole_workload_scaled": len(heads) < len(all_heads)}
 
 
 def main():
@@ -169,6 +213,18 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.oracle_timing:
+        from quantized_attention_02_amd import synth
+
+        name = args.workload or synth.HEADLINE
+        w = synth.VARLEN_WORKLOADS[name] if name in synth.VARLEN_WORKLOADS else synth.WORKLOADS[name]
+        causal = w.causal[0] if args.causal is None else bool(args.causal)
+        print(json.dumps({"oracle_timing": {"workload": name, "causal": causal, "pv_mode": args.pv,
+                                            "ops": w.ops(causal),
+                                            **cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_quant,
+                                                           args.smooth_v, args.smooth_q, args.oracle_repeats,
+                                                           all_heads_ok=True)}}))
         return
 
     import numpy as np
@@ -271,7 +327,8 @@ def main():
                      "frac": round(attn_tops / mfma_peak(args.pv, args.qk_quant), 4), "traffic": traffic,
                      "kernel": "k_attn (sage_attn_fwd)", "algorithmic_ops_per_launch": ops,
                      "limiter": "VALU issue of the fp32 online softmax (per score: int->fp32 convert, FMA, exp2, "
-                                "add, half an FP8 pack; 64-multiply O rescale on most tiles), not the MFMAs",
+                                "half an FP8 pack; 64-multiply O rescale on most tiles; the row sum runs on the "
+                                "matrix core), not the MFMAs",
                      "attn_src_sha256_16": khash},
     }
     if not args.no_cpu_baseline:

@@ -269,10 +269,13 @@ __device__ __forceinline__ void map_work(const AttnArgs &a, bool causal, int &bh
   } else if (!a.varlen && (nbh & 7) == 0) {
     const int heads_per_xcd = nbh >> 3;
     const int xcd = wg & 7, idx = wg >> 3;
-    if (causal) {  // longest blocks first; the XCD's heads interleaved
+    if (causal && a.nmblk < 128) {  // longest blocks first; the XCD's heads interleaved
       bh = xcd * heads_per_xcd + idx % heads_per_xcd;
       mrank = idx / heads_per_xcd;
-    } else {  // one head after the other inside this XCD
+    } else {  // one head after the other inside this XCD (causal: longest blocks first)
+      // A long causal head (128 query blocks or more) alone keeps an XCD's 64
+      // work-group slots busy, and its K/V codes (from 4 MB up) fill the XCD's
+      // L2: interleaving heads would multiply the K/V working set.
       bh = xcd * heads_per_xcd + idx / a.nmblk;
       mrank = idx % a.nmblk;
     }
