@@ -194,11 +194,17 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
  * with fp32 accumulation of exact products (q_mean enters as 16-bit pieces: 2^-22
  * relative residual for fp16 inputs, exact for bf16).  q_mean and k_mean: from
  * sage_smooth_quant_qk called with q_mean (16-byte aligned); k: the same K tensor.
- * delta_s: fp32, the tiled layout above (16-byte aligned).  The attention then adds
- * delta_s[query block][key] * sm_scale to every score.
+ * delta_s: the tiled layout above (16-byte aligned): fp32, or with qk_quant =
+ * SAGE_QK_INT8_BLOCK the int32 rint(delta / (u * k_scale[key block])) in the score units
+ * of its Q block, u = max(q_scale[blk], 127 * sum_d |q_mean[blk][d]| * 2^-30) (fp32,
+ * the sum in channel order), which the attention uses as the starting value of the INT8
+ * accumulator (q_scale, k_scale: from the same sage_smooth_quant_qk call; ignored
+ * otherwise).  The attention then adds delta * sm_scale to every score.  qk_quant as
+ * given to sage_smooth_quant_qk (not SAGE_QK_INT8_HEAD).
  */
-int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, const float *q_mean,
-                  const float *k_mean, float *delta_s, void *stream);
+int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, int qk_quant,
+                  const float *q_mean, const float *k_mean, const void *q_scale, const void *k_scale, float *delta_s,
+                  void *stream);
 
 /*
  * Per-channel FP8 E4M3 quantisation of V ([SA2] SageAttention2方法):
@@ -261,7 +267,11 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  *            O = alpha*O + inner (fp32 buffer);  out = O * v_scale[d] / (448 * l)
  *            (+ v_mean[d] when v_mean is non-NULL: V was smoothed by sage_quant_v)
  *   smoothed Q (delta_s non-NULL): s_n += delta_s[query block][n] * sm_scale (MXFP4: the
- *         term is the starting value of the fp32 accumulator the FP4 MFMA adds to)
+ *         term is the starting value of the fp32 accumulator the FP4 MFMA adds to; INT8
+ *         per-block scales: delta_s holds the term in score units, the starting value of
+ *         the INT8 accumulator, and the block's scale is u of sage_qk_delta -- a block with
+ *         u > q_scale drops its INT8 codes, its residual being below fp32 resolution of
+ *         q_mean)
  *   pv fp16: P = fp16(p_n), O = alpha*O + P . fp16(V) (fp32);  out = O / l
  *   pv fp4 : for each 32-key group G of a row (keys of one 64-key block with equal
  *            (n / 4) mod 2): e = floor(log2 max_G p_n) - 2 (clamped to [-126, 127]),
@@ -272,7 +282,8 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  * sage_quant_v, v_mean = NULL or the means sage_quant_v wrote.  pv fp16: v = the
  * original V tensor (dtype, layout, H_kv heads), v_scale = v_mean = NULL (bf16 V is
  * rounded to fp16).  delta_s: NULL, or the buffer sage_qk_delta filled for these
- * codes.  pv fp4: v = v_codes and v_scale = v_e8m0 (the byte buffer passed as a
+ * codes; q_mean: with delta_s and SAGE_QK_INT8_BLOCK the block means sage_smooth_quant_qk
+ * wrote (they fix the score units), else not read (may be NULL).  pv fp4: v = v_codes and v_scale = v_e8m0 (the byte buffer passed as a
  * float pointer, 4-byte aligned) from sage_quant_v_fp4, v_mean as for pv fp8.
  * out: dtype tensor in `layout`, shape of q.  Query head h reads K/V head
  * h / (H / H_kv).
@@ -281,9 +292,9 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  * (128-token slices of V are addressed through a 32-bit byte range).
  */
 int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                  const void *v, const float *v_scale, const float *v_mean, const float *delta_s, void *out,
-                  int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale,
-                  int pv_mode, int qk_quant, void *stream);
+                  const void *v, const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s,
+                  void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal,
+                  float sm_scale, int pv_mode, int qk_quant, void *stream);
 
 /*
  * Debug variant of sage_attn_fwd (INT8 modes, no smoothed-Q term): the same

@@ -560,7 +560,7 @@ def seq_slices(cu_seqlens) -> list:
 
 def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=None, pv_mode=PV_FP8,
                 heads=None, rows=None, blk_q=BLK_Q, blk_k=BLK_K, tile_k=TILE_K, smooth=True, gran="block",
-                smooth_v=False, qk_format="int8"):
+                smooth_v=False, qk_format="int8", smooth_q=False):
     """Quantized attention over a packed batch of sequences of different lengths
     ("Thư viện SageAttention" page, feature list: variable-length sequences through
     sageattn_varlen).
@@ -571,6 +571,8 @@ def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=No
     (the K mean, the INT8 blocks, the V scales and the causal mask all start
     at the sequence's first token); query and key counts may differ, causal
     keeps key n for query i when n <= i, and a sequence without keys gives 0.
+    smooth_q: each sequence's Q blocks (32 tokens from its first token) are
+    smoothed as in attn.
 
     heads: [(b, h)] (default: all); rows: query rows within each sequence.
     Returns {(b, h): fp32 [rows, D]}.
@@ -585,6 +587,7 @@ def attn_varlen(q, k, v, cu_q, cu_k, dtype: int, *, is_causal=False, sm_scale=No
         (q0, q1), (k0, k1) = sq[b], sk[b]
         one = attn(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype, "NHD", is_causal=is_causal,
                    sm_scale=sm_scale, pv_mode=pv_mode, heads=[(0, h)], rows=rows, blk_q=blk_q, blk_k=blk_k,
-                   tile_k=tile_k, smooth=smooth, gran=gran, smooth_v=smooth_v, qk_format=qk_format)
+                   tile_k=tile_k, smooth=smooth, gran=gran, smooth_v=smooth_v, qk_format=qk_format,
+                   smooth_q=smooth_q)
         res[(b, h)] = one[(0, h)]
     return res

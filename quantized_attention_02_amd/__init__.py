@@ -55,11 +55,11 @@ def lib() -> ctypes.CDLL:
         L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
         L.sage_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 9
         L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 6 + [c_void_p]
-        L.sage_qk_delta.argtypes = [c_void_p] + [c_int] * 7 + [c_void_p] * 4
+        L.sage_qk_delta.argtypes = [c_void_p] + [c_int] * 8 + [c_void_p] * 6
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
         L.sage_quantize_qkv.argtypes = [c_void_p] * 3 + [c_int] * 8 + [c_void_p] * 10
         tail = [c_int] * 8 + [c_float, c_int, c_int]
-        L.sage_attn_fwd.argtypes = [c_void_p] * 9 + tail + [c_void_p]
+        L.sage_attn_fwd.argtypes = [c_void_p] * 10 + tail + [c_void_p]
         L.sage_attn_fwd_dump_qk.argtypes = [c_void_p] * 8 + tail + [c_int, c_int, c_void_p, c_void_p]
         L.sage_varlen_buffer_sizes.argtypes = [c_int] * 7 + [c_size_p] * 7
         L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + \
@@ -120,8 +120,9 @@ def sage_quantize_qkv(q, k, v, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, 
                                    k_mean, q_mean, v_fp8, v_scale, v_mean, stream)
 
 
-def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, q_mean, k_mean, delta_s, stream):
-    return lib().sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, q_mean, k_mean, delta_s, stream)
+def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s, stream):
+    return lib().sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s,
+                               stream)
 
 
 def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream):
@@ -152,10 +153,10 @@ def sage_quant_v_fp4_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen
                                          v_mean, stream)
 
 
-def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D, layout,
-                  is_causal, sm_scale, pv_mode, qk_quant, stream):
-    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D,
-                               layout, is_causal, sm_scale, pv_mode, qk_quant, stream)
+def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, B, H, H_kv, S, D,
+                  layout, is_causal, sm_scale, pv_mode, qk_quant, stream):
+    return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, B, H,
+                               H_kv, S, D, layout, is_causal, sm_scale, pv_mode, qk_quant, stream)
 
 
 def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
@@ -348,7 +349,8 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
             _check(sage_quant_v_fp4(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp4.data_ptr(),
                                     bufs.v_e8m0.data_ptr(), vm, st), "sage_quant_v_fp4")
     if smooth_q:
-        _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.q_mean.data_ptr(), bufs.k_mean.data_ptr(),
+        _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk, bufs.q_mean.data_ptr(),
+                             bufs.k_mean.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_scale.data_ptr(),
                              bufs.delta_s.data_ptr(), st), "sage_qk_delta")
     return bufs
 
@@ -368,10 +370,11 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
     ds = bufs.delta_s.data_ptr() if bufs.smooth_q else None
+    qm = bufs.q_mean.data_ptr() if bufs.smooth_q else None
     head = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs, vm)
     tail = (out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.qk)
     if dump_head is None:
-        _check(sage_attn_fwd(*head, ds, *tail, _stream()), "sage_attn_fwd")
+        _check(sage_attn_fwd(*head, qm, ds, *tail, _stream()), "sage_attn_fwd")
     else:
         if bufs.smooth_q:
             raise ValueError("the Q K^T dump is not available with smooth_q")

@@ -101,7 +101,8 @@ int check_device() {
 int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
 
 int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                const void *v, const float *v_scale, const float *v_mean, const float *delta_s, void *out, int dtype,
+                const void *v, const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s,
+                void *out, int dtype,
                 int B, int H,
                 int H_kv, int S,
                 int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, int dump_b,
@@ -118,6 +119,8 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // smoothed Q: 4-byte aligned, not with the debug dump, not with per-head scales
   if (delta_s && (!aligned(delta_s, 4) || dump || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
+  // INT8 per-block scales: the term is in score units, which the block means fix
+  if (delta_s && qk_quant == SAGE_QK_INT8_BLOCK && (!q_mean || !aligned(q_mean, 4))) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
@@ -142,6 +145,7 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   a.v_scale = v_scale;
   a.v_mean = v_mean;
   a.delta_s = delta_s;
+  a.q_mean = delta_s ? q_mean : nullptr;
   a.out = out;
   a.dump = qk;
   a.dump_bh = dump ? dump_b * H + dump_h : -1;
@@ -293,14 +297,19 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
   return launch_status(launch_quantize_qkv(a, va, (hipStream_t)stream));
 }
 
-int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, const float *q_mean,
-                  const float *k_mean, float *delta_s, void *stream) {
+int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, int qk_quant,
+                  const float *q_mean, const float *k_mean, const void *q_scale, const void *k_scale, float *delta_s,
+                  void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
+  if ((rc = check_qk_quant(qk_quant)) || qk_quant == SAGE_QK_INT8_HEAD) return SAGE_ERR_INVALID_ARG;
   if (!k || !q_mean || !k_mean || !delta_s) return SAGE_ERR_INVALID_ARG;
   if (!aligned(k, 16) || !aligned(q_mean, 16) || !aligned(k_mean, 4) || !aligned(delta_s, 16))
+    return SAGE_ERR_INVALID_ARG;
+  // INT8 per-block scales: the term is written in score units (the scales are read)
+  if (qk_quant == SAGE_QK_INT8_BLOCK && (!q_scale || !k_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4)))
     return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantQKArgs a;
@@ -308,6 +317,9 @@ int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D
   a.k = k;
   a.k_mean = const_cast<float *>(k_mean);
   a.q_mean = const_cast<float *>(q_mean);
+  a.q_scale = (float *)const_cast<void *>(q_scale);
+  a.k_scale = (float *)const_cast<void *>(k_scale);
+  a.qk = qk_quant;
   a.B = B;
   a.H = H;
   a.H_kv = H_kv;
@@ -346,10 +358,11 @@ int sage_quant_v_fp4(const void *v, int dtype, int B, int H, int S, int D, int l
 }
 
 int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale, const void *v,
-                  const float *v_scale, const float *v_mean, const float *delta_s, void *out, int dtype, int B, int H,
-                  int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant,
-                  void *stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, delta_s, out, dtype, B, H, H_kv, S, D,
+                  const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s, void *out,
+                  int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale,
+                  int pv_mode, int qk_quant, void *stream) {
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, B, H, H_kv,
+                     S, D,
                      layout, is_causal, sm_scale, pv_mode, qk_quant, 0, 0, nullptr, false, stream);
 }
 
@@ -357,7 +370,8 @@ int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *
                           const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
                           int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode,
                           int qk_quant, int b, int h, int32_t *qk, void *stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, nullptr, out, dtype, B, H, H_kv, S, D,
+  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, nullptr, nullptr, out, dtype, B, H, H_kv,
+                     S, D,
                      layout, is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, true, stream);
 }
 

@@ -163,6 +163,10 @@ template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, bool QS, int TN
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
   constexpr bool LANE = QK == 1, FP4 = QK == 2, TOKEN = QK == 3;
+  // smoothed Q with INT8 per-block scales: delta arrives in units of the block's
+  // score scale and starts the INT8 MFMA accumulator (QSI); with the other
+  // formats it is an fp32 term added to the scores (QSF)
+  constexpr bool QSI = QS && QK == 0, QSF = QS && !QSI;
   constexpr int kBlockM = WAVES * 32;
   constexpr int NC = D / 32;
   constexpr int KCH = D / 16;
@@ -237,6 +241,24 @@ k_attn(const AttnArgs a) {
       for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
       dq = LANE || TOKEN ? a.q_scale[qs.row0 + qi] : a.q_scale[(qs.row0 + qw) >> 5];
     }
+  }
+  if constexpr (QSI) {
+    // the block's score scale, as the pre-processing pass forms it from the
+    // block means; a block that takes the larger bound drops its INT8 codes
+    // (every lane sums two or one of the D channels, then the wavefront)
+    float sa = 0.0f;
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) sa += fabsf(a.q_mean[(long long)((qs.row0 + qw) >> 5) * D + lane + 64 * i]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sa += __shfl_xor(sa, o, 64);
+    const float dqe = smooth_q_unit(dq, sa);
+    if (dqe > dq) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qf[c] = v4i{0, 0, 0, 0};
+    }
+    dq = dqe;
   }
 
   int ntiles = (Sk + TN - 1) / TN;
@@ -355,27 +377,31 @@ k_attn(const AttnArgs a) {
       //      int -> float conversion can run while the second block's MFMAs do
       using acc_t = typename std::conditional<FP4, v16f, v16i>::type;
       acc_t s[NT];
-      if constexpr (FP4 && QS) {
-        // smoothed Q on the FP4 product: the scaled MFMA accumulates in fp32 on top of
-        // its C operand, so the pre-processing term of each key is the accumulator's
-        // starting value (keys 8 (r / 4) + 4 hh + r % 4 of the sub-tile)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 d4 = *reinterpret_cast<const float4 *>(dsr + 32 * t + 8 * g + 4 * hh);
-            s[t][4 * g] = d4.x;
-            s[t][4 * g + 1] = d4.y;
-            s[t][4 * g + 2] = d4.z;
-            s[t][4 * g + 3] = d4.w;
-          }
-      } else {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[t][r] = 0;
-      }
+        for (int r = 0; r < 16; ++r) s[t][r] = 0;
       auto qk_block = [&](int blk) {
+        if constexpr (QS && (FP4 || QSI)) {
+          // smoothed Q on the FP4 product (fp32 accumulation) or with INT8
+          // per-block scales (delta in score units, int32): the pre-processing
+          // term of each key is the MFMA accumulator's starting value (keys
+          // 8 (r / 4) + 4 hh + r % 4 of the sub-tile).  Read per block, after the
+          // previous block's MFMAs were issued (the asm keeps the reads there), so
+          // that only one block's starting values are live at a time.
+          if (blk > 0) asm volatile("" ::: "memory");
+#pragma unroll
+          for (int t = 2 * blk; t < 2 * blk + 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const v4i d4 = *reinterpret_cast<const v4i *>(dsr + 32 * t + 8 * g + 4 * hh);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (FP4) s[t][4 * g + e] = __int_as_float(d4[e]);
+                else s[t][4 * g + e] = d4[e];
+              }
+            }
+        }
         if constexpr (FP4) {
           // per key: its E8M0 word, shifted so that byte 2c is this half's block of chunk c
 #pragma unroll
@@ -420,8 +446,8 @@ k_attn(const AttnArgs a) {
       // with this half-wave's group scale
       constexpr int NC2 = LANE ? NT : NB;
       float c2[NC2];
-      float cdq[NC2];  // smoothed Q: the dequantisation factor alone (sm_scale applied later)
-      if constexpr (QS) {
+      float cdq[NC2];  // smoothed Q (fp32 path): the dequantisation factor alone (sm_scale applied later)
+      if constexpr (QSF) {
 #pragma unroll
         for (int i = 0; i < NC2; ++i) {
           cdq[i] = TOKEN ? dq : LANE ? dq * (hh ? ks[2 * i + 1] : ks[2 * i]) : dq * ks[i];
@@ -451,12 +477,12 @@ k_attn(const AttnArgs a) {
       float mxf[NB];  // FP4: fp32 max per block
       float f[16 * NT];
       auto max_convert = [&](int blk, int mlim, auto mask_tag) {
-        if constexpr (FP4 || QS || TOKEN) {  // fp32 scores: dequantised (+ delta), max in fp32
+        if constexpr (FP4 || QSF || TOKEN) {  // fp32 scores: dequantised (+ delta), max in fp32
           float mx = -INFINITY;
 #pragma unroll
           for (int t = 2 * blk; t < 2 * blk + 2; ++t) {
             float4 dv[4], kv[4];
-            if constexpr (QS && !FP4)
+            if constexpr (QSF && !FP4)
 #pragma unroll
               for (int g = 0; g < 4; ++g) dv[g] = *reinterpret_cast<const float4 *>(dsr + 32 * t + 8 * g + 4 * hh);
             if constexpr (TOKEN)
@@ -471,7 +497,7 @@ k_attn(const AttnArgs a) {
               } else if constexpr (TOKEN) {
                 const float4 k4 = kv[r >> 2];
                 const float kr = (r & 3) == 0 ? k4.x : (r & 3) == 1 ? k4.y : (r & 3) == 2 ? k4.z : k4.w;
-                if constexpr (QS) {
+                if constexpr (QSF) {
                   const float4 d4 = dv[r >> 2];
                   const float dr = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
                   val = __builtin_fmaf((float)s[t][r] * kr, cdq[blk], dr);
@@ -529,7 +555,7 @@ k_attn(const AttnArgs a) {
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, mlim, std::true_type());
       }
       float mt = -INFINITY;
-      if constexpr (FP4 || QS) {
+      if constexpr (FP4 || QSF) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) mt = fmaxf(mt, mxf[blk] * a.sm2);
       } else if constexpr (TOKEN) {
@@ -559,7 +585,7 @@ k_attn(const AttnArgs a) {
           // (the same arms as max_convert: fp32 maxima with smoothed Q, FP4 or
           // per-token scales; int32 maxima per lane group or per block otherwise)
           float g = -INFINITY;
-          if constexpr (FP4 || QS || TOKEN) {
+          if constexpr (FP4 || QSF || TOKEN) {
             g = __builtin_fmaf(mxf[blk], c2[blk], -sub);
           } else if constexpr (LANE) {
 #pragma unroll

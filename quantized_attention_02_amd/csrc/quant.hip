@@ -339,6 +339,9 @@ __device__ inline void q_block_smooth(const QuantQKArgs &a, float (&x)[2][8], in
 // lane ends with 16 results of one query block: 4 runs of 4 consecutive keys,
 // stored as 4 float4.  delta is stored tile-major ([bh][key tile][block][128
 // keys]), so a work-group writes one contiguous 16 KB region per chunk.
+// INTU (INT8 per-block scales): each result is stored as the int32
+// rint(delta / (dq dk)) in the score units of its Q block and 64-key K block
+// (smooth_q_unit), the starting value of the attention's INT8 accumulator.
 // ---------------------------------------------------------------------------
 constexpr int kDeltaKeys = 128;
 static_assert(kDeltaKeys == kKvPad, "a delta work-group covers one 128-key K tile");
@@ -378,7 +381,7 @@ struct DeltaMfma<1> {  // bf16 inputs
   }
 };
 
-template <int DT, int D>
+template <int DT, int D, bool INTU>
 __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, float *delta) {
   typedef DeltaMfma<DT> M;
   typedef typename M::T8 T8;
@@ -388,6 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   constexpr int CPT = D / 8;      // channels per staging thread (8 threads per query block)
   __shared__ __align__(16) uint16_t am[2][NS][32 * RS];  // double-buffered by chunk
   __shared__ float cs[2][32];
+  __shared__ float cu[2][32];  // INTU: each block's score scale (smooth_q_unit)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int nkt = a.S_k / kDeltaKeys + (a.S_k % kDeltaKeys != 0);
   // work-group -> (query head, key tile); with a grid that divides evenly, each
@@ -431,14 +435,29 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   };
   // stage the means in x (one chunk) into buffer buf: split pieces and dot
   // products with k_mean
+  int blk0_of_buf[2] = {0, 32};  // the first query block of the chunk staged in each buffer
   auto stage = [&](const float (&x)[CPT], int buf) {
-    float c = 0.0f;
+    float c = 0.0f, sa = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) c = __builtin_fmaf(x[i], km[i], c);
+    for (int i = 0; i < CPT; ++i) {
+      c = __builtin_fmaf(x[i], km[i], c);
+      sa += fabsf(x[i]);
+    }
     c += __shfl_xor(c, 1, 64);
     c += __shfl_xor(c, 2, 64);
     c += __shfl_xor(c, 4, 64);
-    if ((tid & 7) == 0) cs[buf][sb] = c;
+    if constexpr (INTU) {
+      sa += __shfl_xor(sa, 1, 64);
+      sa += __shfl_xor(sa, 2, 64);
+      sa += __shfl_xor(sa, 4, 64);
+    }
+    if ((tid & 7) == 0) {
+      cs[buf][sb] = c;
+      if constexpr (INTU) {
+        const int blk = blk0_of_buf[buf] + sb;
+        cu[buf][sb] = blk < a.nq ? smooth_q_unit(a.q_scale[(long long)bh * a.nq + blk], sa) : 0.0f;
+      }
+    }
     uint16_t p[CPT][NS];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) M::split(x[i], p[i]);
@@ -468,13 +487,21 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
       }
     // row blk0 + lane % 32 of the tile (a store past the last block is dropped)
     const float c = cs[buf][lane & 31];
+    float inv = 0.0f;
+    if constexpr (INTU) {  // this wavefront's 32 keys lie in one 64-key K block
+      const float unit = cu[buf][lane & 31] * a.k_scale[(ks.row0 + key0) >> 6];
+      inv = unit > 0.0f ? 1.0f / unit : 0.0f;
+    }
     const int row = (blk0 + (lane & 31)) * kDeltaKeys + 32 * wave + 4 * hh;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int k0 = key0 + 8 * g + 4 * hh;
       v4i o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = __float_as_int(k0 + e < a.S ? acc[4 * g + e] - c : 0.0f);  // padding keys: 0
+      for (int e = 0; e < 4; ++e) {
+        const float d = k0 + e < a.S ? acc[4 * g + e] - c : 0.0f;  // padding keys: 0
+        o[e] = INTU ? (int)__builtin_rintf(d * inv) : __float_as_int(d);
+      }
       __builtin_amdgcn_raw_buffer_store_b128(o, drs, (row + 8 * g) * 4, 0, 0);
     }
   };
@@ -492,10 +519,12 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
     load_means(xa, blk0 + 64);
     compute(blk0, 0);
     if (blk0 + 32 >= a.nq) break;
+    blk0_of_buf[1] = blk0 + 32;
     stage(xb, 1);
     __syncthreads();
     load_means(xb, blk0 + 96);
     compute(blk0 + 32, 1);
+    blk0_of_buf[0] = blk0 + 64;
     if (blk0 + 64 < a.nq) stage(xa, 0);
   }
 }
@@ -1284,15 +1313,21 @@ hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_qk_delta(const QuantQKArgs &a, float *delta, hipStream_t stream) {
+template <bool INTU>
+static void launch_qk_delta_t(const QuantQKArgs &a, float *delta, hipStream_t stream) {
   const dim3 grid(a.B * a.H * (a.S_k / kDeltaKeys));  // S_k: a multiple of 128
   if (a.D == 64) {
-    if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 64>), grid, dim3(kThreads), 0, stream, a, delta);
-    else hipLaunchKernelGGL((k_qk_delta<1, 64>), grid, dim3(kThreads), 0, stream, a, delta);
+    if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 64, INTU>), grid, dim3(kThreads), 0, stream, a, delta);
+    else hipLaunchKernelGGL((k_qk_delta<1, 64, INTU>), grid, dim3(kThreads), 0, stream, a, delta);
   } else {
-    if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 128>), grid, dim3(kThreads), 0, stream, a, delta);
-    else hipLaunchKernelGGL((k_qk_delta<1, 128>), grid, dim3(kThreads), 0, stream, a, delta);
+    if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 128, INTU>), grid, dim3(kThreads), 0, stream, a, delta);
+    else hipLaunchKernelGGL((k_qk_delta<1, 128, INTU>), grid, dim3(kThreads), 0, stream, a, delta);
   }
+}
+
+hipError_t launch_qk_delta(const QuantQKArgs &a, float *delta, hipStream_t stream) {
+  if (a.qk == 0) launch_qk_delta_t<true>(a, delta, stream);
+  else launch_qk_delta_t<false>(a, delta, stream);
   return hipGetLastError();
 }
 

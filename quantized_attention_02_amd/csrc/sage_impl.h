@@ -129,6 +129,17 @@ __device__ inline Seg varlen_seg(const SeqTable &t, int b, int h, int H, int D, 
   return Seg{len, ((long long)start * H + h) * D, (long long)H * D, h * rows + seq_row0(start, b, pad)};
 }
 
+// Smoothed Q with INT8 per-block scales: the pre-processing term delta enters
+// the attention's INT8 accumulator as rint(delta / (u dk)), so the score scale u
+// of a Q block must keep |delta| / (u dk) within int32 next to the INT8 sum
+// (|sum| <= 127^2 D < 2^22).  |delta| <= sum_d |qbar_d| * 127 dk, so a scale of at
+// least 127 sum_d |qbar_d| 2^-30 suffices; a block whose own scale dq is smaller
+// (its residual Q - qbar is at or below fp32 resolution of qbar, or zero) takes
+// that bound and drops its INT8 codes.  sum_abs: sum_d |qbar_d| in fp32 (the
+// pre-processing pass and the attention kernel may sum in different orders; u
+// then differs by a few ulps, well inside the term's rounding to units).
+__device__ inline float smooth_q_unit(float dq, float sum_abs) { return fmaxf(dq, 127.0f * sum_abs * 0x1p-30f); }
+
 struct QuantQKArgs {
   const void *q, *k;
   int8_t *q_i8, *k_i8;
@@ -163,6 +174,7 @@ struct AttnArgs {
   const float *v_scale;  // pv fp8: per-channel scales; pv fp4: the E8M0 bytes (reinterpreted)
   const float *v_mean;  // smoothed V: channel means added to the output (nullptr: none)
   const float *delta_s;  // smoothed Q: pre-processing term [B][H][nq][S_k] (nullptr: none)
+  const float *q_mean;   // smoothed Q with INT8 per-block scales: the block means (score units)
   void *out;
   int32_t *dump;
   int dump_bh;

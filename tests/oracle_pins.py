@@ -509,6 +509,15 @@ def pin_varlen_matches_separate_sequences():
                 for h in range(4):
                     assert got[(b, h)].shape == (lengths[b], 64)
                     assert np.array_equal(got[(b, h)].view(np.uint32), ref[(0, h)].view(np.uint32)), (b, h, causal)
+    # smoothed Q: each sequence's Q blocks start at its own first token
+    got = O.attn_varlen(q, k, v, cu_q, cu_k, F16, is_causal=True, smooth_q=True)
+    for b, (sq, sk, sv) in enumerate(seqs):
+        ref = O.attn(sq, sk, sv, F16, "NHD", is_causal=True, smooth_q=True)
+        plain = O.attn(sq, sk, sv, F16, "NHD", is_causal=True)
+        for h in range(4):
+            assert np.array_equal(got[(b, h)].view(np.uint32), ref[(0, h)].view(np.uint32)), (b, h, "smooth_q")
+        if lengths[b] > 1:  # (a one-token block's mean is the token: the smoothing changes nothing)
+            assert not all(np.array_equal(ref[(0, h)], plain[(0, h)]) for h in range(4)), b
     # query and key lengths that differ per sequence (cross-attention shapes)
     lq, lk = [33, 90, 5], [150, 12, 64]
     q, k, v, cu_q, cu_k, seqs = _packed(lq, lk, 2, 1, 64, seed0=720)

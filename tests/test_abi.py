@@ -87,9 +87,10 @@ def test_vpos_key_is_a_permutation():
 P = 1 << 12
 GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, H_kv=2, S=100, D=64, layout=0, qk_quant=0, q_i8=P, q_scale=P, k_i8=P,
                k_scale=P, k_mean=P, q_mean=None, stream=None)
-GOOD_DELTA = dict(k=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64, layout=1, q_mean=P, k_mean=P, delta_s=P, stream=None)
+GOOD_DELTA = dict(k=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64, layout=1, qk_quant=0, q_mean=P, k_mean=P, q_scale=P,
+                  k_scale=P, delta_s=P, stream=None)
 GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, v_mean=None, stream=None)
-GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, delta_s=None, out=P, dtype=0, B=1,
+GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, q_mean=None, delta_s=None, out=P, dtype=0, B=1,
                  H=2, H_kv=2, S=100,
                  D=64, layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, qk_quant=0, stream=None)
 
@@ -100,15 +101,19 @@ BAD_QK = [dict(q=None), dict(k_mean=None), dict(q_i8=P + 8), dict(k=P + 2), dict
           dict(qk_quant=4, q_mean=P)]  # per-head scales: no smoothed Q
 BAD_DELTA = [dict(k=None), dict(q_mean=None), dict(k_mean=None), dict(delta_s=None), dict(q_mean=P + 4),
              dict(delta_s=P + 2), dict(delta_s=P + 4), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2),
+             # INT8 per-block scales: the term in score units needs both scale buffers
+             dict(q_scale=None), dict(k_scale=None), dict(q_scale=P + 2), dict(qk_quant=4), dict(qk_quant=5),
              dict(dtype=4), dict(S=0)]
 BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80),
          dict(v_mean=P + 2)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
             dict(sm_scale=0.0), dict(sm_scale=-1.0), dict(sm_scale=float("inf")), dict(sm_scale=float("nan")),
             dict(is_causal=2), dict(pv_mode=3), dict(pv_mode=-1), dict(pv_mode=2, v_scale=None), dict(pv_mode=2, v_scale=P + 2), dict(dtype=5), dict(D=100), dict(S=0),
-            dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=5), dict(qk_quant=4, delta_s=P),
+            dict(H_kv=0), dict(H_kv=4), dict(H=6, H_kv=4), dict(H_kv=-1), dict(qk_quant=5), dict(qk_quant=4, delta_s=P, q_mean=P),
             dict(v_mean=P + 1), dict(pv_mode=1, v_scale=None, v_mean=P),  # smoothing is for the FP8 V codes
             dict(delta_s=P + 2),
+            # INT8 per-block scales: the term in score units comes with the block means
+            dict(delta_s=P), dict(delta_s=P, q_mean=P + 2),
             # pv fp16 reads 128-token slices of an NHD V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
             dict(pv_mode=1, v_scale=None, layout=1, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
 
@@ -178,7 +183,7 @@ def test_attn_fp16_mode_accepts_null_v_scale_then_needs_device():
 
 
 def test_dump_rejects_bad_head_and_buffer():
-    a = [v for k, v in GOOD_ATTN.items() if k not in ("delta_s", "stream")]  # the dump takes no smoothed-Q term
+    a = [v for k, v in GOOD_ATTN.items() if k not in ("q_mean", "delta_s", "stream")]  # no smoothed-Q term
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 2, P, None) == qa.SAGE_ERR_INVALID_ARG  # h out of range
     a[-1] = 5
     assert qa.sage_attn_fwd_dump_qk(*a, 0, 0, P, None) == qa.SAGE_ERR_INVALID_ARG  # bad Q/K mode
@@ -210,8 +215,12 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_qkv(qk_quant=4) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_qk(q_mean=P) == qa.SAGE_ERR_NO_DEVICE
-    assert _call_attn(delta_s=P) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(delta_s=P, q_mean=P) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_attn(delta_s=P, qk_quant=1) == qa.SAGE_ERR_NO_DEVICE  # fp32 terms: no means needed
     assert qa.sage_qk_delta(*GOOD_DELTA.values()) == qa.SAGE_ERR_NO_DEVICE
+    # the other Q/K formats write fp32 terms and do not read the scales
+    assert qa.sage_qk_delta(*{**GOOD_DELTA, "qk_quant": 1, "q_scale": None, "k_scale": None}.values()) == \
+        qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(v_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(H=8, H_kv=1) == qa.SAGE_ERR_NO_DEVICE
     assert _call_v() == qa.SAGE_ERR_NO_DEVICE

@@ -2,9 +2,10 @@
 (INT8 per block or per token, or MXFP4), a pre-processing pass forms delta =
 block mean . (K - k_mean), and the attention adds delta * sm_scale to the scores.
 
-Block means, codes and scales are bit-identical to the oracle's.  delta is
-checked against the oracle's binary64 value with the error bound of its
-arithmetic: the kernel forms q_mean . K - q_mean . k_mean from exact products of
+Block means, codes and scales are bit-identical to the oracle's.  delta (with
+INT8 per-block scales stored in the block's score units, so also within half a
+unit and 2^-22 of |delta| from the scaling) is checked against the oracle's
+binary64 value with the error bound of its arithmetic: the kernel forms q_mean . K - q_mean . k_mean from exact products of
 16-bit pieces of q_mean (2^-22 relative residual with fp16 inputs, none with
 bf16) and K, summed in fp32 -- at most 3 D + 16 roundings of 2^-24 each, below
 2^-14 of sum_d |q_mean_d| (|K_d| + |k_mean_d|) for D <= 128.  Outputs meet the attention bars (cosine >=
@@ -71,8 +72,19 @@ def test_smooth_q_quant_and_delta(w, qk):
                                   km.view(np.uint32))
             rd = O.qk_delta_head(rm, kf, km)
             bound = 2.0 ** -14 * (np.abs(rm).astype(np.float64) @ (np.abs(kf) + np.abs(km)[None, :]).T)
-            err = np.abs(ds[b, h, :nq, :S].astype(np.float64) - rd)
-            assert (err <= bound).all(), (b, h, float((err / bound).max()))
+            if qk == "int8":
+                # in score units: rint(delta / (u * k_scale)), u = max(q_scale, 127 sum|q_mean| 2^-30)
+                ks = bufs.k_scale.cpu().numpy()[b, O.kv_head(h, w.H, w.kv_heads)]
+                u = np.maximum(qs[b, h, :nq].astype(np.float64),
+                               127.0 * np.abs(rm).astype(np.float64).sum(1) * 2.0 ** -30)
+                unit = u[:, None] * ks[np.arange(S) // 64].astype(np.float64)[None, :]
+                got = ds[b, h, :nq, :S].view(np.int32).astype(np.float64) * unit
+                lim = bound + 0.5 * unit * (1 + 2.0 ** -20) + 2.0 ** -22 * np.abs(rd)
+            else:
+                got, lim = ds[b, h, :nq, :S].astype(np.float64), bound
+            err = np.abs(got - rd)
+            print(f"{w.name} {qk} head {(b, h)}: max err/limit {float((err / lim).max()):.3f}")
+            assert (err <= lim).all(), (b, h, float((err / lim).max()))
             assert not ds[b, h, :nq, S:].any()
 
 
