@@ -146,7 +146,7 @@ def cpu_baseline(w, causal, pv, nheads, qk="int8", smooth_v=False, smooth_q=Fals
         def run(heads):
             t0 = time.perf_counter()
             O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=bool(causal), pv_mode=pvm, heads=heads,
-                          smooth_v=smooth_v, **oracle_qk(qk))
+                          smooth_v=smooth_v, smooth_q=smooth_q, **oracle_qk(qk))
             return time.perf_counter() - t0
         what = "sequence-heads"
     else:
@@ -235,8 +235,6 @@ def main():
 
     name = args.workload or synth.HEADLINE
     varlen = name in synth.VARLEN_WORKLOADS
-    if args.smooth_q and varlen:
-        sys.exit("--smooth-q applies to fixed-length batches")
     if args.smooth_v and args.pv == "fp16":
         sys.exit("--smooth-v applies to pv fp8 and fp4")
     w = synth.VARLEN_WORKLOADS[name] if varlen else synth.WORKLOADS[name]
@@ -255,7 +253,8 @@ def main():
         bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev, args.qk_quant)
 
         def quant():
-            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v)
+            qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
+                               smooth_q=args.smooth_q)
 
         def attn():
             qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)

@@ -341,6 +341,13 @@ int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *
  *   (MXFP4: codes D / 2 and scales D / 32 bytes a row, as in the fixed layout)
  *   k_mean  float [B][H_kv][D]        v_scale float [B][H_kv][D]
  *   v_fp8   uint8 [H_kv][RK / 64][D][64]  (64-key tiles as in the fixed layout)
+ * Smoothed Q (sizes from sage_varlen_smooth_q_sizes; any qk_quant but
+ * SAGE_QK_INT8_HEAD):
+ *   q_mean  float [H][RQ / 32][D]    each Q block's channel means (block rows as q_codes)
+ *   delta_s float [H][RK / 128][MQ][128]  the pre-processing term, MQ = ceil(max_seqlen_q
+ *           / 32): per query head and 128-row tile of the K buffer, the MQ query-block
+ *           rows of 128 keys; sequence b's tiles hold its own query blocks 0 ..
+ *           ceil(len_q(b) / 32) - 1 (the rest is neither written nor read).
  * A sequence's rows past its length, up to the next multiple of 32 (Q) or 128
  * (K, V), hold zero codes; rows between sequences are neither written nor read.
  * Other rules (alignment, errors, stream order, staging) as above.
@@ -349,11 +356,29 @@ int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, i
                              size_t *q_codes, size_t *q_scale, size_t *k_codes, size_t *k_scale, size_t *k_mean,
                              size_t *v_fp8, size_t *v_scale);
 
-/* sage_smooth_quant_qk for a packed batch. */
+/* Bytes of q_mean and delta_s for smoothed Q on a packed batch (layouts above;
+ * either pointer may be NULL).  Errors as sage_varlen_buffer_sizes. */
+int sage_varlen_smooth_q_sizes(int B, int H, int total_q, int total_k, int max_seqlen_q, int D, size_t *q_mean,
+                               size_t *delta_s);
+
+/* sage_smooth_quant_qk for a packed batch; q_mean: NULL, or the [H][RQ / 32][D]
+ * buffer of block means (smoothed Q, as in the fixed-length call: each block's
+ * means are of the sequence's own tokens in it). */
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                                 int max_seqlen_q, int max_seqlen_k, int D, int qk_quant, void *q_codes,
-                                void *q_scale, void *k_codes, void *k_scale, float *k_mean, void *stream);
+                                void *q_scale, void *k_codes, void *k_scale, float *k_mean, float *q_mean,
+                                void *stream);
+
+/* sage_qk_delta for a packed batch: each sequence's query blocks against its own
+ * keys and K mean (k: [total_k][H_kv][D]); q_mean, k_mean, q_scale, k_scale from
+ * sage_smooth_quant_qk_varlen called with q_mean; delta_s: the layout above,
+ * 16-byte aligned, in fp32 or (SAGE_QK_INT8_BLOCK) in score units as in the
+ * fixed-length call. */
+int sage_qk_delta_varlen(const void *k, int dtype, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B,
+                         int H, int H_kv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                         int qk_quant, const float *q_mean, const float *k_mean, const void *q_scale,
+                         const void *k_scale, float *delta_s, void *stream);
 
 /* sage_quant_v for a packed batch (v: [total_k][H_kv][D]); v_mean as there. */
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
@@ -369,9 +394,12 @@ int sage_quant_v_fp4_varlen(const void *v, int dtype, const int32_t *cu_seqlens_
                             void *stream);
 
 /* sage_attn_fwd for a packed batch.  pv fp16: v = the original [total_k][H_kv][D]
- * V, v_scale = v_mean = NULL.  out: [total_q][H][D] in dtype. */
+ * V, v_scale = v_mean = NULL.  q_mean, delta_s: NULL, or smoothed Q's buffers
+ * (sage_smooth_quant_qk_varlen, sage_qk_delta_varlen), as in the fixed-length
+ * call.  out: [total_q][H][D] in dtype. */
 int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                         const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
+                         const void *v, const float *v_scale, const float *v_mean, const float *q_mean,
+                         const float *delta_s, void *out, int dtype,
                          const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,

@@ -33,7 +33,8 @@ TILE_K = {"fp8": 128, "fp16": 128, "fp4": 128}  # keys per online-softmax tile o
 EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sage_quant_v", "sage_quantize_qkv", "sage_attn_fwd",
             "sage_attn_fwd_dump_qk", "sage_qk_delta", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
             "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch", "sage_quant_v_fp4", "sage_v_fp4_buffer_sizes",
-            "sage_quant_v_fp4_varlen", "sage_varlen_v_fp4_buffer_sizes"]
+            "sage_quant_v_fp4_varlen", "sage_varlen_v_fp4_buffer_sizes", "sage_varlen_smooth_q_sizes",
+            "sage_qk_delta_varlen"]
 
 _lib = None
 
@@ -63,9 +64,11 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd_dump_qk.argtypes = [c_void_p] * 8 + tail + [c_int, c_int, c_void_p, c_void_p]
         L.sage_varlen_buffer_sizes.argtypes = [c_int] * 7 + [c_size_p] * 7
         L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + \
-            [c_void_p] * 5 + [c_void_p]
+            [c_void_p] * 6 + [c_void_p]
+        L.sage_varlen_smooth_q_sizes.argtypes = [c_int] * 6 + [c_size_p] * 2
+        L.sage_qk_delta_varlen.argtypes = [c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + [c_void_p] * 6
         L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
-        L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 8 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
+        L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 10 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
             [c_int, c_float, c_int, c_int, c_void_p]
         L.sage_quant_v_fp4.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
         L.sage_v_fp4_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 2
@@ -173,11 +176,24 @@ def sage_varlen_buffer_sizes(B, H, H_kv, total_q, total_k, D, qk_quant=0):
     return {n: v.value for n, v in zip(names, vals)}
 
 
+def sage_varlen_smooth_q_sizes(B, H, total_q, total_k, max_seqlen_q, D):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().sage_varlen_smooth_q_sizes(B, H, total_q, total_k, max_seqlen_q, D, ctypes.byref(a),
+                                            ctypes.byref(b)), "sage_varlen_smooth_q_sizes")
+    return {"q_mean": a.value, "delta_s": b.value}
+
+
 def sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
-                                max_seqlen_k, D, qk_quant, q_i8, q_scale, k_i8, k_scale, k_mean, stream):
+                                max_seqlen_k, D, qk_quant, q_i8, q_scale, k_i8, k_scale, k_mean, q_mean, stream):
     return lib().sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k,
                                              max_seqlen_q, max_seqlen_k, D, qk_quant, q_i8, q_scale, k_i8, k_scale,
-                                             k_mean, stream)
+                                             k_mean, q_mean, stream)
+
+
+def sage_qk_delta_varlen(k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
+                         max_seqlen_k, D, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s, stream):
+    return lib().sage_qk_delta_varlen(k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
+                                      max_seqlen_k, D, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s, stream)
 
 
 def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale, v_mean, stream):
@@ -185,10 +201,11 @@ def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, 
                                      v_mean, stream)
 
 
-def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q, cu_seqlens_k, B,
-                         H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode,
-                         qk_quant, stream):
-    return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q,
+def sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, cu_seqlens_q,
+                         cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale,
+                         pv_mode, qk_quant, stream):
+    return lib().sage_attn_fwd_varlen(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype,
+                                      cu_seqlens_q,
                                       cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
                                       is_causal, sm_scale, pv_mode, qk_quant, stream)
 
@@ -465,9 +482,24 @@ class QuantizedVarlen:
         self._v4_shape = (H_kv, rk // BLK_K, D)
         self._device = device
         self.smooth_v = False
+        self.smooth_q = False  # set by quantize_varlen: whether q_i8 holds Q minus its block means
+        # smoothed Q: q_mean [H][RQ / 32][D] and delta_s [H][RK / 128][MQ][128],
+        # MQ = ceil(max_seqlen_q / 32) (allocated by quantize_varlen on first use)
+        self.q_mean = self.delta_s = None
         self.v_mode = None
 
     alloc_v_fp4 = Quantized.alloc_v_fp4
+
+    def alloc_smooth_q(self, max_seqlen_q):
+        import torch
+
+        mq = (max_seqlen_q + BLK_Q - 1) // BLK_Q
+        if self.q_mean is None:
+            self.q_mean = torch.empty((self.H, self.rows_q // BLK_Q, self.D), dtype=torch.float32,
+                                      device=self._device)
+        if self.delta_s is None or self.delta_s.shape[2] != mq:
+            self.delta_s = torch.empty((self.H, self.rows_k // KV_PAD, mq, KV_PAD), dtype=torch.float32,
+                                       device=self._device)
 
 
 def _cu(t, name):
@@ -479,10 +511,12 @@ def _cu(t, name):
 
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
-                    bufs: QuantizedVarlen | None = None, qk_quant="int8", smooth_v=False) -> QuantizedVarlen:
+                    bufs: QuantizedVarlen | None = None, qk_quant="int8", smooth_v=False,
+                    smooth_q=False) -> QuantizedVarlen:
     """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode,
-    sage_quant_v_fp4_varlen in pv fp4 mode) on a packed batch: q [total_q, H, D],
-    k / v [total_k, H_kv, D], cu_seqlens int32 [B + 1]."""
+    sage_quant_v_fp4_varlen in pv fp4 mode, sage_qk_delta_varlen with smooth_q)
+    on a packed batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens
+    int32 [B + 1]; smooth_v, smooth_q as in quantize."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_q, H, D] and k, v [total_k, H_kv, D]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -507,11 +541,15 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
             (B, H, H_kv, total_q, total_k, D, QK[qk_quant]):
         raise ValueError("bufs were allocated for another shape or granularity")
     bufs.max_seqlen_q, bufs.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    if smooth_q:
+        bufs.alloc_smooth_q(bufs.max_seqlen_q)
+    bufs.smooth_q = bool(smooth_q)
+    qm = bufs.q_mean.data_ptr() if smooth_q else None
     st = _stream()
     _check(sage_smooth_quant_qk_varlen(q.data_ptr(), k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
                                        total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk,
                                        bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
-                                       bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), st),
+                                       bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, st),
            "sage_smooth_quant_qk_varlen")
     bufs.smooth_v = bool(smooth_v)
     bufs.v_mode = pv_mode if pv_mode != "fp16" else None
@@ -524,6 +562,11 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         _check(sage_quant_v_fp4_varlen(v.data_ptr(), dt, ck.data_ptr(), B, H_kv, total_k, bufs.max_seqlen_k, D,
                                        bufs.v_fp4.data_ptr(), bufs.v_e8m0.data_ptr(), vm, st),
                "sage_quant_v_fp4_varlen")
+    if smooth_q:
+        _check(sage_qk_delta_varlen(k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv, total_q, total_k,
+                                    bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk, bufs.q_mean.data_ptr(),
+                                    bufs.k_mean.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_scale.data_ptr(),
+                                    bufs.delta_s.data_ptr(), st), "sage_qk_delta_varlen")
     return bufs
 
 
@@ -539,22 +582,25 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    qm = bufs.q_mean.data_ptr() if bufs.smooth_q else None
+    ds = bufs.delta_s.data_ptr() if bufs.smooth_q else None
     _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
-                                bufs.k_scale.data_ptr(), vptr, vs, vm, out.data_ptr(), _dtype_code(out), cq.data_ptr(),
-                                ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k, bufs.max_seqlen_q,
-                                bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, bufs.qk, _stream()),
+                                bufs.k_scale.data_ptr(), vptr, vs, vm, qm, ds, out.data_ptr(), _dtype_code(out),
+                                cq.data_ptr(), ck.data_ptr(), B, H, H_kv, bufs.total_q, bufs.total_k,
+                                bufs.max_seqlen_q, bufs.max_seqlen_k, D, int(bool(is_causal)), sm, pv, bufs.qk,
+                                _stream()),
            "sage_attn_fwd_varlen")
     return out
 
 
 def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False, sm_scale=None,
-                    pv_mode="fp8", qk_quant="int8", smooth_v=False):
+                    pv_mode="fp8", qk_quant="int8", smooth_v=False, smooth_q=False):
     """Quantized attention over a packed batch of sequences ("SageAttention: Thư viện
     Attention lượng tử hóa" page, feature list: sageattn_varlen):
     q [total_q, H, D], k / v [total_k, H_kv, D]; returns [total_q, H, D]."""
     import torch
 
     bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_quant=qk_quant,
-                           smooth_v=smooth_v)
+                           smooth_v=smooth_v, smooth_q=smooth_q)
     out = torch.empty_like(q)
     return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)

@@ -409,9 +409,11 @@ int sage_varlen_buffer_sizes(int B, int H, int H_kv, int total_q, int total_k, i
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                                 int max_seqlen_q, int max_seqlen_k, int D, int qk_quant, void *q_codes,
-                                void *q_scale, void *k_codes, void *k_scale, float *k_mean, void *stream) {
+                                void *q_scale, void *k_codes, void *k_scale, float *k_mean, float *q_mean,
+                                void *stream) {
   int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_quant);
   if (rc) return rc;
+  if (q_mean && (!aligned(q_mean, 4) || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean)
     return SAGE_ERR_INVALID_ARG;
@@ -444,7 +446,58 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
   a.qk = qk_quant;
+  a.q_mean = q_mean;
   return launch_status(launch_smooth_quant_qk(a, (hipStream_t)stream));
+}
+
+int sage_varlen_smooth_q_sizes(int B, int H, int total_q, int total_k, int max_seqlen_q, int D, size_t *q_mean,
+                               size_t *delta_s) {
+  int rc = check_varlen(B, H, H, total_q, total_k, max_seqlen_q, 1, D, SAGE_QK_INT8_BLOCK);
+  if (rc) return rc;
+  const size_t rq = (size_t)varlen_rows(total_q, B, kBlkQ), rk = (size_t)varlen_rows(total_k, B, kKvPad);
+  const size_t mqb = (size_t)roundup(max_seqlen_q, kBlkQ) / kBlkQ;
+  if (q_mean) *q_mean = (size_t)H * (rq / kBlkQ) * D * sizeof(float);
+  if (delta_s) *delta_s = (size_t)H * (rk / kKvPad) * mqb * kKvPad * sizeof(float);
+  return SAGE_OK;
+}
+
+int sage_qk_delta_varlen(const void *k, int dtype, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B,
+                         int H, int H_kv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
+                         int qk_quant, const float *q_mean, const float *k_mean, const void *q_scale,
+                         const void *k_scale, float *delta_s, void *stream) {
+  int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_quant);
+  if (rc) return rc;
+  if (qk_quant == SAGE_QK_INT8_HEAD) return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
+  if (!k || !q_mean || !k_mean || !delta_s || !cu_seqlens_q || !cu_seqlens_k) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(q_mean, 16) || !aligned(k_mean, 4) || !aligned(delta_s, 16) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return SAGE_ERR_INVALID_ARG;
+  if (qk_quant == SAGE_QK_INT8_BLOCK && (!q_scale || !k_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4)))
+    return SAGE_ERR_INVALID_ARG;
+  if ((rc = check_device())) return rc;
+  QuantQKArgs a;
+  memset(&a, 0, sizeof a);
+  a.k = k;
+  a.k_mean = const_cast<float *>(k_mean);
+  a.q_mean = const_cast<float *>(q_mean);
+  a.q_scale = (float *)const_cast<void *>(q_scale);
+  a.k_scale = (float *)const_cast<void *>(k_scale);
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.S = max_seqlen_k;
+  a.D = D;
+  a.layout = SAGE_LAYOUT_NHD;
+  a.dtype = dtype;
+  a.nq = roundup(max_seqlen_q, kBlkQ) / kBlkQ;  // delta rows per key tile
+  a.varlen = 1;
+  a.sq = SeqTable{cu_seqlens_q, total_q, max_seqlen_q};
+  a.sk = SeqTable{cu_seqlens_k, total_k, max_seqlen_k};
+  a.rows_q = varlen_rows(total_q, B, kBlkQ);
+  a.rows_k = varlen_rows(total_k, B, kKvPad);
+  a.qk = qk_quant;
+  return launch_status(launch_qk_delta(a, delta_s, (hipStream_t)stream));
 }
 
 int sage_quant_v_varlen(const void *v, int dtype, const int32_t *cu_seqlens_k, int B, int H_kv, int total_k,
@@ -517,7 +570,8 @@ int sage_quant_v_fp4_varlen(const void *v, int dtype, const int32_t *cu_seqlens_
 }
 
 int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                         const void *v, const float *v_scale, const float *v_mean, void *out, int dtype,
+                         const void *v, const float *v_scale, const float *v_mean, const float *q_mean,
+                         const float *delta_s, void *out, int dtype,
                          const int32_t *cu_seqlens_q,
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
@@ -531,6 +585,9 @@ int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
     return SAGE_ERR_INVALID_ARG;
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
+  // smoothed Q: as in the fixed-length call
+  if (delta_s && (!aligned(delta_s, 4) || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
+  if (delta_s && qk_quant == SAGE_QK_INT8_BLOCK && (!q_mean || !aligned(q_mean, 4))) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
@@ -547,6 +604,9 @@ int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k
   a.v = v;
   a.v_scale = v_scale;
   a.v_mean = v_mean;
+  a.delta_s = delta_s;
+  a.q_mean = delta_s ? q_mean : nullptr;
+  a.nq = roundup(max_seqlen_q, kBlkQ) / kBlkQ;  // smoothed Q: delta rows per key tile
   a.out = out;
   a.dump = nullptr;
   a.dump_bh = -1;

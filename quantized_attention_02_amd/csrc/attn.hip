@@ -301,7 +301,11 @@ k_attn(const AttnArgs a) {
   // wavefront's row of tile j (its query block) is 512 contiguous bytes at
   // dbase + j * dtile; only wavefronts with queries copy (a trailing wavefront's
   // block may not exist)
-  const float *dbase = QS ? a.delta_s + ((long long)bh * (a.S_k / kKvPad) * a.nq + (qw >> 5)) * kKvPad : nullptr;
+  // (packed batches: per query head, rows_k / 128 key tiles, the sequence's own
+  // from its first K buffer row, and nq = the longest sequence's query blocks)
+  const long long dtile0 = a.varlen ? (long long)h * (a.rows_k / kKvPad) + ((ks.row0 - (long long)hk * a.rows_k) >> 7)
+                                    : (long long)bh * (a.S_k / kKvPad);
+  const float *dbase = QS ? a.delta_s + (dtile0 * a.nq + (qw >> 5)) * kKvPad : nullptr;
   const long long dtile = (long long)a.nq * kKvPad;  // floats from one tile to the next
   // copies of tile j into buffer buf; returns how many copy instructions this
   // wavefront issued without V (pv fp16 counts them to wait for its V alone)

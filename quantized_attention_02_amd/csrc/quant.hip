@@ -338,7 +338,10 @@ __device__ inline void q_block_smooth(const QuantQKArgs &a, float (&x)[2][8], in
 // chunk), and the means of the chunk after next load while a chunk is computed.  A
 // lane ends with 16 results of one query block: 4 runs of 4 consecutive keys,
 // stored as 4 float4.  delta is stored tile-major ([bh][key tile][block][128
-// keys]), so a work-group writes one contiguous 16 KB region per chunk.
+// keys]), so a work-group writes one contiguous 16 KB region per chunk.  Packed
+// batches: [query head][128-row tile of the K buffer][block][128 keys], with as
+// many blocks as the longest query sequence has; a sequence's tiles hold its
+// own query blocks and the rest of each tile is left as it was.
 // INTU (INT8 per-block scales): each result is stored as the int32
 // rint(delta / (dq dk)) in the score units of its Q block and 64-key K block
 // (smooth_q_unit), the starting value of the attention's INT8 accumulator.
@@ -393,14 +396,34 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   __shared__ float cs[2][32];
   __shared__ float cu[2][32];  // INTU: each block's score scale (smooth_q_unit)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
-  const int nkt = a.S_k / kDeltaKeys + (a.S_k % kDeltaKeys != 0);
+  // fixed length: S_k / 128 key tiles per (batch, query head); packed batches:
+  // rows_k / 128 per query head, each in one sequence's run (or between runs)
+  const int nkt = a.varlen ? (int)(a.rows_k / kDeltaKeys) : a.S_k / kDeltaKeys;
   // work-group -> (query head, key tile); with a grid that divides evenly, each
   // XCD takes whole heads, so a head's block means are read through one L2
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
-  const int bh = wg / nkt, kt = wg % nkt;
-  const int b = bh / a.H, h = bh % a.H, hk = h / (a.H / a.H_kv);
-  const Seg ks = fixed_seg(a.layout, b, hk, a.H_kv, a.S, a.S_k, D);
+  int b, h, kt;  // kt: the tile within the sequence (packed) or the head (fixed)
+  block_of(a.varlen, a.sk, a.B, a.H, nkt, a.rows_k, kKvPad, kDeltaKeys, wg, b, h, kt);
+  const int bh = b * a.H + h, hk = h / (a.H / a.H_kv);
+  const Seg ks = a.varlen ? varlen_seg(a.sk, b, hk, a.H_kv, D, a.rows_k, kKvPad)
+                          : fixed_seg(a.layout, b, hk, a.H_kv, a.S, a.S_k, D);
+  if (kt >= ceil_div(ks.S, kDeltaKeys)) return;  // past this sequence's keys (packed batches)
+  // the query blocks: the batch entry's, or the sequence's (its own run of Q rows)
+  long long qblk0;  // the first block's index in q_mean / q_scale
+  int nqb;          // blocks of this sequence (fixed length: of the head)
+  long long drow0;  // this tile's first row of delta ([tile][block][128 keys])
+  if (a.varlen) {
+    const Seg qv = varlen_seg(a.sq, b, h, a.H, D, a.rows_q, kBlkQ);
+    qblk0 = qv.row0 >> 5;
+    nqb = ceil_div(qv.S, kBlkQ);
+    drow0 = ((long long)h * nkt + ((ks.row0 - (long long)hk * a.rows_k) >> 7) + kt) * a.nq;
+  } else {
+    qblk0 = (long long)bh * a.nq;
+    nqb = a.nq;
+    drow0 = ((long long)bh * nkt + kt) * a.nq;
+  }
+  const int S = ks.S;                            // this sequence's keys
   const int key0 = kt * kDeltaKeys + 32 * wave;  // this wavefront's 32 keys (< S_k)
   const int n = key0 + (lane & 31);              // the key whose K row this lane holds
   // A operand: channels 16 s + 8 hh .. +7 of key n for each k step s
@@ -409,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     v4i u = {0, 0, 0, 0};
-    if (n < a.S) u = *reinterpret_cast<const v4i *>(k + ks.base + (long long)n * ks.stride + 16 * s + 8 * hh);
+    if (n < S) u = *reinterpret_cast<const v4i *>(k + ks.base + (long long)n * ks.stride + 16 * s + 8 * hh);
     kf[s] = __builtin_bit_cast(T8, u);
   }
   // staging role: query block sb of a chunk, channels sc .. sc + CPT - 1
@@ -421,9 +444,8 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   // through buffer resources: loads past the last block return zeros and stores
   // past it are dropped, so neither needs a branch, and the wait for a chunk's
   // prefetched means leaves the previous chunk's stores in flight.
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q_mean + (long long)bh * a.nq * D, a.nq * D * 4);
-  const __amdgpu_buffer_rsrc_t drs =
-      make_rsrc(delta + ((long long)bh * nkt + kt) * a.nq * kDeltaKeys, a.nq * kDeltaKeys * 4);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q_mean + qblk0 * D, nqb * D * 4);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(delta + drow0 * kDeltaKeys, nqb * kDeltaKeys * 4);
   // this thread's means of block blk0 + sb
   auto load_means = [&](float (&x)[CPT], int blk0) {
 #pragma unroll
@@ -455,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
       cs[buf][sb] = c;
       if constexpr (INTU) {
         const int blk = blk0_of_buf[buf] + sb;
-        cu[buf][sb] = blk < a.nq ? smooth_q_unit(a.q_scale[(long long)bh * a.nq + blk], sa) : 0.0f;
+        cu[buf][sb] = blk < nqb ? smooth_q_unit(a.q_scale[qblk0 + blk], sa) : 0.0f;
       }
     }
     uint16_t p[CPT][NS];
@@ -499,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
       v4i o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float d = k0 + e < a.S ? acc[4 * g + e] - c : 0.0f;  // padding keys: 0
+        const float d = k0 + e < S ? acc[4 * g + e] - c : 0.0f;  // padding keys: 0
         o[e] = INTU ? (int)__builtin_rintf(d * inv) : __float_as_int(d);
       }
       __builtin_amdgcn_raw_buffer_store_b128(o, drs, (row + 8 * g) * 4, 0, 0);
@@ -514,18 +536,18 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   load_means(xa, 0);
   load_means(xb, 32);
   stage(xa, 0);
-  for (int blk0 = 0; blk0 < a.nq; blk0 += 64) {
+  for (int blk0 = 0; blk0 < nqb; blk0 += 64) {
     __syncthreads();
     load_means(xa, blk0 + 64);
     compute(blk0, 0);
-    if (blk0 + 32 >= a.nq) break;
+    if (blk0 + 32 >= nqb) break;
     blk0_of_buf[1] = blk0 + 32;
     stage(xb, 1);
     __syncthreads();
     load_means(xb, blk0 + 96);
     compute(blk0 + 32, 1);
     blk0_of_buf[0] = blk0 + 64;
-    if (blk0 + 64 < a.nq) stage(xa, 0);
+    if (blk0 + 64 < nqb) stage(xa, 0);
   }
 }
 
@@ -561,7 +583,7 @@ __device__ inline void qquant_wg(const QuantQKArgs &a, int wg) {
       for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
     }
   }
-  if (a.q_mean) {  // smoothed Q: subtract the block's channel means (fixed-length batches)
+  if (a.q_mean) {  // smoothed Q: subtract the block's channel means
     q_block_smooth<D>(a, x, hv.S - blk * kBlkQ, (hv.row0 >> 5) + blk);
   }
 #pragma unroll
@@ -1315,7 +1337,8 @@ hipError_t launch_smooth_quant_qk(const QuantQKArgs &a, hipStream_t stream) {
 
 template <bool INTU>
 static void launch_qk_delta_t(const QuantQKArgs &a, float *delta, hipStream_t stream) {
-  const dim3 grid(a.B * a.H * (a.S_k / kDeltaKeys));  // S_k: a multiple of 128
+  // S_k, rows_k: multiples of 128
+  const dim3 grid(a.varlen ? a.H * (int)(a.rows_k / kDeltaKeys) : a.B * a.H * (a.S_k / kDeltaKeys));
   if (a.D == 64) {
     if (a.dtype == 0) hipLaunchKernelGGL((k_qk_delta<0, 64, INTU>), grid, dim3(kThreads), 0, stream, a, delta);
     else hipLaunchKernelGGL((k_qk_delta<1, 64, INTU>), grid, dim3(kThreads), 0, stream, a, delta);

@@ -164,6 +164,7 @@ class VarlenWorkload:
     causal: tuple = (True,)
     pv_modes: tuple = ("fp8",)
     seed: int = 0
+    q_bias_sigma: float = 0.0  # per-channel Q offset shared by all tokens (as Workload)
 
     @property
     def B(self) -> int:
@@ -197,14 +198,15 @@ class VarlenWorkload:
 
 
 def varlen(name, H, Hkv, D, seqlens_q, seqlens_k=None, dtype="fp16", bias_sigma=2.0, causal=(False,),
-           pv_modes=("fp8",), seed=0) -> VarlenWorkload:
+           pv_modes=("fp8",), seed=0, q_bias_sigma=0.0) -> VarlenWorkload:
     return VarlenWorkload(name, H, Hkv, D, dtype, tuple(seqlens_q), tuple(seqlens_k or seqlens_q), bias_sigma,
-                          causal, pv_modes, seed)
+                          causal, pv_modes, seed, q_bias_sigma)
 
 
 def make_qkv_varlen(w: VarlenWorkload):
     """(q [Tq, H, D], k [Tk, Hkv, D], v [Tk, Hkv, D]) uint16 codes, token-major."""
-    wq = Workload(w.name + "_q", 1, w.H, w.total_q, w.D, w.dtype, "NHD", w.bias_sigma, seed=w.seed)
+    wq = Workload(w.name + "_q", 1, w.H, w.total_q, w.D, w.dtype, "NHD", w.bias_sigma, seed=w.seed,
+                  q_bias_sigma=w.q_bias_sigma)
     wk = Workload(w.name + "_kv", 1, w.H, w.total_k, w.D, w.dtype, "NHD", w.bias_sigma, seed=w.seed + 1, Hkv=w.Hkv)
     q = make_qkv(wq)[0][0]
     _, k, v = make_qkv(wk)

@@ -266,22 +266,32 @@ def test_varlen_buffer_sizes():
 
 
 GOOD_QK_VL = dict(q=P, k=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4, H_kv=2, total_q=100, total_k=200, max_q=50,
-                  max_k=90, D=64, qk_quant=1, q_i8=P, q_scale=P, k_i8=P, k_scale=P, k_mean=P, stream=None)
+                  max_k=90, D=64, qk_quant=1, q_i8=P, q_scale=P, k_i8=P, k_scale=P, k_mean=P, q_mean=None, stream=None)
 GOOD_V_VL = dict(v=P, dtype=1, cu_k=P, B=3, H_kv=2, total_k=200, max_k=90, D=128, v_fp8=P, v_scale=P, v_mean=P,
                  stream=None)
-GOOD_ATTN_VL = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=P, out=P, dtype=0, cu_q=P, cu_k=P,
-                    B=3, H=4,
-                    H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90, D=64, is_causal=1, sm_scale=0.125,
+GOOD_ATTN_VL = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=P, q_mean=None, delta_s=None, out=P,
+                    dtype=0, cu_q=P, cu_k=P, B=3, H=4, H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90, D=64, is_causal=1, sm_scale=0.125,
                     pv_mode=0, qk_quant=0, stream=None)
 BAD_QK_VL = [dict(cu_q=None), dict(cu_k=P + 2), dict(B=0), dict(H_kv=3), dict(total_q=-1), dict(max_q=0),
-             dict(max_k=(1 << 20) + 1), dict(D=32), dict(dtype=3), dict(q=None), dict(k_i8=P + 1), dict(qk_quant=5)]
+             dict(max_k=(1 << 20) + 1), dict(D=32), dict(dtype=3), dict(q=None), dict(k_i8=P + 1), dict(qk_quant=5),
+             # smoothed Q: aligned means, and not with one scale per head
+             dict(q_mean=P + 2), dict(q_mean=P, qk_quant=4)]
 BAD_V_VL = [dict(cu_k=None), dict(v=P + 8), dict(max_k=0), dict(total_k=-3), dict(H_kv=0), dict(v_scale=None),
             dict(v_mean=P + 2)]
 BAD_ATTN_VL = [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P + 1), dict(is_causal=3), dict(pv_mode=5), dict(qk_quant=7),
                dict(v_mean=P + 3), dict(pv_mode=1, v_scale=None), dict(pv_mode=2, v_scale=None), dict(pv_mode=3),
                dict(sm_scale=0.0), dict(v_scale=None), dict(out=P + 4), dict(H_kv=3), dict(max_q=0), dict(B=-1),
                # pv fp16 reads 128-token slices of V through a 32-bit byte range: H_kv * D * 2 * 128 < 2^31
-               dict(pv_mode=1, v_scale=None, B=1, H=1 << 16, H_kv=1 << 16, D=128)]
+               dict(pv_mode=1, v_scale=None, B=1, H=1 << 16, H_kv=1 << 16, D=128),
+               # smoothed Q: the term in score units needs the block means; aligned; not per head
+               dict(delta_s=P), dict(delta_s=P + 2, q_mean=P), dict(delta_s=P, q_mean=P + 1),
+               dict(delta_s=P, qk_quant=4)]
+GOOD_DELTA_VL = dict(k=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4, H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90,
+                     D=64, qk_quant=0, q_mean=P, k_mean=P, q_scale=P, k_scale=P, delta_s=P, stream=None)
+BAD_DELTA_VL = [dict(k=None), dict(cu_q=None), dict(cu_k=P + 1), dict(q_mean=None), dict(q_mean=P + 4),
+                dict(k_mean=None), dict(delta_s=P + 8), dict(delta_s=None), dict(q_scale=None), dict(k_scale=P + 2),
+                dict(qk_quant=4), dict(qk_quant=6), dict(dtype=2), dict(D=96), dict(H_kv=3), dict(max_q=0),
+                dict(B=0), dict(total_k=-1)]
 
 
 @pytest.mark.parametrize("bad", BAD_QK_VL, ids=[str(b) for b in BAD_QK_VL])
@@ -299,8 +309,31 @@ def test_attn_fwd_varlen_rejects(bad):
     assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("bad", BAD_DELTA_VL, ids=[str(b) for b in BAD_DELTA_VL])
+def test_qk_delta_varlen_rejects(bad):
+    assert qa.sage_qk_delta_varlen(*{**GOOD_DELTA_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_varlen_smooth_q_sizes():
+    # q_mean [H][RQ / 32][D] fp32; delta_s [H][RK / 128][ceil(max_q / 32)][128] fp32
+    rq, rk = qa.varlen_rows(100, 3, 32), qa.varlen_rows(200, 3, 128)
+    assert qa.sage_varlen_smooth_q_sizes(3, 4, 100, 200, 50, 64) == \
+        {"q_mean": 4 * (rq // 32) * 64 * 4, "delta_s": 4 * (rk // 128) * 2 * 128 * 4}
+    assert qa.sage_varlen_smooth_q_sizes(1, 1, 1, 1, 1, 128)["delta_s"] == qa.varlen_rows(1, 1, 128) * 4
+    L = qa.lib()
+    for bad in [(0, 1, 1, 1, 1, 64), (1, 0, 1, 1, 1, 64), (1, 1, -1, 1, 1, 64), (1, 1, 1, 1, 0, 64),
+                (1, 1, 1, 1, 1, 80), (1, 1, 1, 1, (1 << 20) + 1, 64)]:
+        assert L.sage_varlen_smooth_q_sizes(*bad, None, None) == qa.SAGE_ERR_INVALID_ARG, bad
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
 def test_valid_varlen_arguments_without_a_device_report_no_device():
+    assert qa.sage_qk_delta_varlen(*GOOD_DELTA_VL.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_qk_delta_varlen(*{**GOOD_DELTA_VL, "qk_quant": 2, "q_scale": None, "k_scale": None}.values()) == \
+        qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_smooth_quant_qk_varlen(*{**GOOD_QK_VL, "q_mean": P}.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "q_mean": P, "delta_s": P}.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "qk_quant": 1, "delta_s": P}.values()) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_smooth_quant_qk_varlen(*GOOD_QK_VL.values()) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_quant_v_varlen(*GOOD_V_VL.values()) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_attn_fwd_varlen(*GOOD_ATTN_VL.values()) == qa.SAGE_ERR_NO_DEVICE

@@ -43,14 +43,14 @@ def _inputs(w):
     return (q, k, v, cq, ck), dev, cud
 
 
-def _run(w, causal, pv, dev, cud, qk_quant="int8"):
+def _run(w, causal, pv, dev, cud, qk_quant="int8", smooth_q=False):
     import torch
 
     import quantized_attention_02_amd as qa
 
     qd, kd, vd = dev
     bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max(w.seqlens_q), max(max(w.seqlens_k), 1), pv,
-                              qk_quant=qk_quant)
+                              qk_quant=qk_quant, smooth_q=smooth_q)
     out = torch.full_like(qd, float("nan"))
     qa.attn_fwd_varlen(bufs, vd, out, cud[0], cud[1], causal, None, pv)
     torch.cuda.synchronize()
@@ -144,14 +144,18 @@ def test_varlen_equals_fixed_length_per_sequence_bitwise(causal, pv):
 FULL = synth.VARLEN_WORKLOADS["varlen_h32kv8t32768d128"]
 
 
-@pytest.mark.parametrize("pv", FULL.pv_modes)
-def test_varlen_full_size_sampled(pv):
+FULL_CASES = [(pv, False) for pv in FULL.pv_modes] + [("fp8", True)]
+
+
+@pytest.mark.parametrize("pv,smooth_q", FULL_CASES, ids=[f"{pv}{'-sq' if sq else ''}" for pv, sq in FULL_CASES])
+def test_varlen_full_size_sampled(pv, smooth_q):
     """The packed prefill workload in the benchmark's launch configuration:
-    sampled rows of the longest, the shortest and a middle sequence."""
+    sampled rows of the longest, the shortest and a middle sequence (with and
+    without smoothed Q)."""
     w = FULL
     (q, k, v, cq, ck), dev, cud = _inputs(w)
     causal = w.causal[0]
-    _, out = _run(w, causal, pv, dev, cud)
+    _, out = _run(w, causal, pv, dev, cud, smooth_q=smooth_q)
     got = O.decode16(G.to_u16(out), O.DTYPES[w.dtype])
     assert np.isfinite(got).all()
     vmax = np.abs(O.decode16(v, O.DTYPES[w.dtype])).max()
@@ -164,7 +168,7 @@ def test_varlen_full_size_sampled(pv):
         for h in (0, w.H - 1, 13):
             ref = O.attn_varlen(q, k, v, cq, ck, O.DTYPES[w.dtype], is_causal=causal,
                                 pv_mode=O.PV_FP8 if pv == "fp8" else O.PV_FP16, heads=[(b, h)], rows=rows,
-                                tile_k=G.TILE_K[pv])[(b, h)]
+                                tile_k=G.TILE_K[pv], smooth_q=smooth_q)[(b, h)]
             g = got[cq[b] + rows, h]
             G.assert_parity(g, ref, f"{w.name} seq {b} (S={S}) head {h}")
 
@@ -276,3 +280,66 @@ def test_varlen_head_granularity(w):
             r_all.append(ref[(b, h)])
     g_all, r_all = np.concatenate(g_all), np.concatenate(r_all)
     G.assert_parity(g_all, r_all, f"{w.name} head")
+
+
+SMOOTH_Q = [
+    synth.varlen("vl_sq_d64", 4, 2, 64, [200, 7, 64, 129, 1, 300], q_bias_sigma=4.0, seed=811),
+    synth.varlen("vl_sq_cross_bf16_d128", 4, 4, 128, [40, 150, 5, 0, 77, 64], [150, 40, 64, 30, 0, 64],
+                 dtype="bf16", q_bias_sigma=3.0, seed=812),
+]
+SQ_CASES = [(SMOOTH_Q[0], True, "fp8", "int8"), (SMOOTH_Q[0], False, "fp16", "int8_lane"),
+            (SMOOTH_Q[0], True, "fp4", "mxfp4"), (SMOOTH_Q[1], True, "fp8", "int8"),
+            (SMOOTH_Q[1], False, "fp8", "int8_token"), (SMOOTH_Q[1], True, "fp4", "int8")]
+GRAN = {"int8": "block", "int8_lane": "lane", "int8_token": "token"}
+PV_ORACLE = {"fp8": O.PV_FP8, "fp16": O.PV_FP16, "fp4": O.PV_FP4}
+
+
+@pytest.mark.parametrize("w,causal,pv,qk", SQ_CASES,
+                         ids=[f"{w.name}-{'causal' if c else 'full'}-{pv}-{qk}" for w, c, pv, qk in SQ_CASES])
+def test_varlen_smooth_q(w, causal, pv, qk):
+    """Smoothed Q on a packed batch: each sequence's block means (32 tokens from
+    its first token) bit-identical to the oracle's, the output within the bars of
+    the oracle with smoothed Q, and each sequence whose query and key counts agree
+    bit-identical to the fixed-length entry points on that sequence alone."""
+    import torch
+
+    import quantized_attention_02_amd as qa
+
+    (q, k, v, cq, ck), dev, cud = _inputs(w)
+    qd, kd, vd = dev
+    max_q, max_k = max(w.seqlens_q), max(max(w.seqlens_k), 1)
+    bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max_q, max_k, pv, qk_quant=qk, smooth_q=True)
+    out = torch.full_like(qd, float("nan"))
+    qa.attn_fwd_varlen(bufs, vd, out, cud[0], cud[1], causal, None, pv)
+    torch.cuda.synchronize()
+    dt = O.DTYPES[w.dtype]
+    qm = bufs.q_mean.cpu().numpy()
+    for b in range(w.B):
+        q0, q1 = cq[b], cq[b + 1]
+        if q1 == q0:
+            continue
+        r0 = qa.varlen_row0(q0, b, 32) // 32
+        for h in range(w.H):
+            _, _, rm = O.quant_q_head_smooth(O.decode16(q[q0:q1, h], dt), 32)
+            assert np.array_equal(qm[h, r0:r0 + rm.shape[0]].view(np.uint32), rm.view(np.uint32)), (b, h)
+    got = O.decode16(G.to_u16(out), dt)
+    kw = dict(qk_format="fp4") if qk == "mxfp4" else dict(gran=GRAN[qk])
+    ref = O.attn_varlen(q, k, v, cq, ck, dt, is_causal=causal, pv_mode=PV_ORACLE[pv], tile_k=G.TILE_K[pv],
+                        smooth_q=True, **kw)
+    g_all, r_all = [], []
+    for b in range(w.B):
+        g = got[cq[b]:cq[b + 1]]
+        if ck[b + 1] == ck[b]:
+            assert not g.any(), b  # no keys: zero rows
+            continue
+        for h in range(w.H):
+            g_all.append(g[:, h])
+            r_all.append(ref[(b, h)])
+    G.assert_parity(np.concatenate(g_all), np.concatenate(r_all), f"{w.name} causal={causal} pv={pv} qk={qk} smooth_q")
+    for b in range(w.B):
+        if cq[b + 1] == cq[b] or w.seqlens_q[b] != w.seqlens_k[b]:
+            continue
+        qb, kb, vb = (x[None, c[b]:c[b + 1]].contiguous() for x, c in zip(dev, (cq, ck, ck)))
+        one = qa.sageattn(qb, kb, vb, tensor_layout="NHD", is_causal=causal, pv_mode=pv, qk_quant=qk, smooth_q=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[cq[b]:cq[b + 1]].view(torch.int16), one[0].view(torch.int16)), b
