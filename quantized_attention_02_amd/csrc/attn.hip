@@ -179,15 +179,33 @@ k_attn(const AttnArgs a) {
   constexpr int V4CODES = TN * D / 2, V4SC = NB * D * 2;
   constexpr int VBYTES = PV == 0 ? TN * D : PV == 1 ? 2 * TN * D : (V4CODES + V4SC + 1023) / 1024 * 1024;
   constexpr int NVBUF = PV == 1 ? 1 : NBUF;                 // fp16 V: one buffer, refilled every tile
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NVBUF][VBYTES];
+  // Every buffer of the multi-buffered tiles is a __shared__ variable of its
+  // own.  The compiler gives distinct variables distinct alias scopes, so the
+  // reads of the tile being computed do not wait for the copies in flight into
+  // another buffer; within one array it would have to assume that they overlap
+  // and wait for the next tile's copies before reading this one.
+  static_assert(NBUF >= 2 && NBUF <= 3, "two or three tile buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf2[NBUF > 2 ? KBYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[NVBUF > 1 ? VBYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf2[NVBUF > 2 ? VBYTES : 16];
   __shared__ __attribute__((aligned(16))) float vsc[D];  // this head's V channel scales (pv fp8)
   __shared__ __attribute__((aligned(16))) float vmn[D];  // its channel means when V was smoothed
   // smoothed Q: each wavefront's row of the pre-processing term for the tile's keys
-  __shared__ __attribute__((aligned(16))) float dsbuf[QS ? NBUF : 1][QS ? WAVES : 1][QS ? TN : 4];
+  __shared__ __attribute__((aligned(16))) float dsbuf0[QS ? WAVES : 1][QS ? TN : 4];
+  __shared__ __attribute__((aligned(16))) float dsbuf1[QS ? WAVES : 1][QS ? TN : 4];
+  __shared__ __attribute__((aligned(16))) float dsbuf2[QS && NBUF > 2 ? WAVES : 1][QS ? TN : 4];
   // per-token K scales: the tile's key scales (copied by the first TN / 64 wavefronts)
-  __shared__ __attribute__((aligned(16))) float ksbuf[TOKEN ? NBUF : 1][TOKEN ? TN : 4];
+  __shared__ __attribute__((aligned(16))) float ksbuf0[TOKEN ? TN : 4];
+  __shared__ __attribute__((aligned(16))) float ksbuf1[TOKEN ? TN : 4];
   static_assert(!TOKEN || (TN / 64 <= WAVES && NBUF == 2), "key-scale copy split and whole-tile vm waits");
+  // buffer u (a compile-time constant wherever the unrolled loops below use these)
+  auto kbuf = [&](int u) -> uint8_t * { return u == 0 ? kbuf0 : u == 1 ? kbuf1 : kbuf2; };
+  auto vbuf = [&](int u) -> uint8_t * { return u == 0 ? vbuf0 : u == 1 ? vbuf1 : vbuf2; };
+  auto dsbuf = [&](int u) -> float(*)[QS ? TN : 4] { return u == 0 ? dsbuf0 : u == 1 ? dsbuf1 : dsbuf2; };
+  auto ksbuf = [&](int u) -> float * { return u == 0 ? ksbuf0 : ksbuf1; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
@@ -332,7 +350,7 @@ k_attn(const AttnArgs a) {
       // whether or not they have queries of their own
       if (wave < TN / 64) {
         dma4_buf(srs, (uint32_t)(4 * lane), 4 * (j * TN + 64 * wave),
-                 reinterpret_cast<uint8_t *>(&ksbuf[buf][0]) + 256 * wave);
+                 reinterpret_cast<uint8_t *>(ksbuf(buf)) + 256 * wave);
         n += 1;
       }
     }
@@ -343,7 +361,7 @@ k_attn(const AttnArgs a) {
           const int key = j * TN + 64 * i;  // first key of this 64-key half: its 128-key delta tile and half
           const __amdgpu_buffer_rsrc_t drs = make_rsrc(dbase + (key / kKvPad) * dtile, kKvPad * 4);
           dma4_buf(drs, (uint32_t)(4 * lane), 256 * ((key / 64) & 1),
-                   reinterpret_cast<uint8_t *>(&dsbuf[buf][wave][0]) + 256 * i);
+                   reinterpret_cast<uint8_t *>(&dsbuf(buf)[wave][0]) + 256 * i);
         }
         n += TN / 64;
       }
@@ -354,8 +372,8 @@ k_attn(const AttnArgs a) {
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
   // pend (pv fp16): copy instructions this wavefront issued after the tile's V.
   auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb, int pend) {
-    const float *dsr = &dsbuf[QS ? buf : 0][QS ? wave : 0][0];  // smoothed Q: this wavefront's delta row
-    const float *ksr = &ksbuf[TOKEN ? buf : 0][0];               // per-token K: the tile's key scales
+    const float *dsr = &dsbuf(QS ? buf : 0)[QS ? wave : 0][0];  // smoothed Q: this wavefront's delta row
+    const float *ksr = ksbuf(TOKEN ? buf : 0);                   // per-token K: the tile's key scales
     const int key0 = j * TN;
     const bool work = active && !(CAUSAL && key0 > qw + 31);
     // the tile's K scales, read through a wave-uniform address (scalar loads)
@@ -768,7 +786,7 @@ k_attn(const AttnArgs a) {
   static_assert(NBUF == 2 || !FP4, "partial vm waits assume the INT8 copy counts");
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
-    if (u < ntiles) issue_tile(u, u, kbuf[u], vbuf[PV != 1 ? u : 0]);
+    if (u < ntiles) issue_tile(u, u, kbuf(u), vbuf(PV != 1 ? u : 0));
   wait_vm<0>();
   __syncthreads();
   for (int j0 = 0; j0 < ntiles; j0 += NBUF) {
@@ -781,10 +799,10 @@ k_attn(const AttnArgs a) {
       // pv fp16: this tile's V rows go into the single V buffer, which the
       // barrier that ended the previous tile has released; issued ahead of the
       // prefetch so that the tile can wait for its V alone
-      if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, j * TN, Sk, vbuf[0], wave);
+      if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, j * TN, Sk, vbuf(0), wave);
       int pend = 0;
-      if (jn < ntiles) pend = issue_tile(jn, un, kbuf[un], vbuf[PV != 1 ? un : 0]);
-      tile(j, u, kbuf[u], vbuf[PV != 1 ? u : 0], pend);
+      if (jn < ntiles) pend = issue_tile(jn, un, kbuf(un), vbuf(PV != 1 ? un : 0));
+      tile(j, u, kbuf(u), vbuf(PV != 1 ? u : 0), pend);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
       __syncthreads();
