@@ -488,6 +488,13 @@ k_attn(const AttnArgs a) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
       }
+      if constexpr (PV == 0) {
+        // pv fp8 takes masked keys to weight 0 through exp2(-inf) alone: a zero
+        // factor (an all-zero Q or K block, whose scores are all 0) becomes the
+        // smallest normal float, so that -inf * c2 stays -inf; its scores stay 0
+#pragma unroll
+        for (int i = 0; i < NC2; ++i) c2[i] = fmaxf(c2[i], 0x1p-126f);
+      }
       // ---- mask: only tiles that reach past S or cross the causal diagonal
       // key (key0 + 4hh + kofs(t, r)) is excluded iff kofs(t, r) > lim, where
       // kofs is a compile-time constant of the register slot
@@ -619,20 +626,69 @@ k_attn(const AttnArgs a) {
           gq[blk] = g + nudge;
         }
       }
-      // ---- p = exp2(s * c2 - sub)  (= 448 p~ in fp8 mode); masked keys are then
-      //      zeroed in a separate pass that only boundary tiles take; row sum
+      if constexpr (PV == 0) {
+        // ---- pv fp8: O is rescaled first, so that the weights, their E4M3
+        //      codes and the P V MFMAs of the tile form one basic block (the
+        //      second block's exp2 and conversions can run under the first
+        //      block's MFMAs).  p = exp2(s * c2 - sub) = 448 p~; masked keys
+        //      (s = -inf) give 0.  Byte 16 t' + r of operand blk = key of
+        //      s[2 blk + t'][r].  Two-level accumulation: each MFMA sums its 64
+        //      FP8 products in the matrix core's own accumulator (level 1) and
+        //      adds that partial sum to the fp32 O registers passed as its C
+        //      operand (level 2).  The rescale is skipped when no row of the
+        //      wavefront changed its max.
+        lacc[0] *= alpha;
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+          for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[16 * t + r], c2[LANE ? t : t >> 1], -sub));
-      if (need_mask) {
-        int mlim = lim;
-        asm volatile("; zero masked p" : "+v"(mlim) :: "memory");
+            for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
+        }
+        v8i pk[NB];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const int i0 = 32 * blk + 4 * w;
+            float e[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int i = i0 + k;
+              e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[i], c2[LANE ? i >> 4 : i >> 5], -sub));
+            }
+            // the word's upper half is written by the next conversion; its
+            // initial content is e[0]'s register, dead after this use
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], __float_as_int(e[0]), false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
+            pk[blk][w] = word;
+          }
+          lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[blk], lacc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int row = blk * D + 32 * c + qn;
+            const v4i lo = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh, row));
+            const v4i hi = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh + 1, row));
+            const v8i vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            O[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk[blk], O[c], 0, 0, 0, 0, 0, 0);
+          }
+        }
+      } else {
+        // ---- pv fp16, fp4: p = exp2(s * c2 - sub) = p~; masked keys are then
+        //      zeroed in a separate pass that only boundary tiles take
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * t + 8 * (r >> 2) + (r & 3) > mlim) p[16 * t + r] = 0.0f;
+            p[16 * t + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[16 * t + r], c2[LANE ? t : t >> 1], -sub));
+        if (need_mask) {
+          int mlim = lim;
+          asm volatile("; zero masked p" : "+v"(mlim) :: "memory");
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * t + 8 * (r >> 2) + (r & 3) > mlim) p[16 * t + r] = 0.0f;
+        }
       }
     }
 
@@ -693,47 +749,7 @@ k_attn(const AttnArgs a) {
         }
       }
     } else if constexpr (PV == 0) {
-      if (work) {
-        // ---- P~ -> E4M3: byte 16t' + r of operand blk = key of s[2 blk + t'][r]
-        v8i pk[NB];
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int i0 = 32 * blk + 4 * w;
-            // the word's upper half is written by the next conversion; its
-            // initial content is p[i0]'s register, dead after this use
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0], p[i0 + 1], __float_as_int(p[i0]), false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(p[i0 + 2], p[i0 + 3], word, true);
-            pk[blk][w] = word;
-          }
-        // ---- O^T = alpha * O^T + V^T . P^T.  Two-level accumulation: each MFMA
-        //      sums its 64 FP8 products in the matrix core's own accumulator
-        //      (level 1) and adds that partial sum to the fp32 O registers passed
-        //      as its C operand (level 2).  O is rescaled in place first; the
-        //      rescale is skipped when no row of the wavefront changed its max.
-        lacc[0] *= alpha;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) O[c][r] *= alpha;
-        }
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk)
-          lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[blk], lacc, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-          for (int blk = 0; blk < NB; ++blk) {
-            const int row = blk * D + 32 * c + qn;
-            const v4i lo = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh, row));
-            const v4i hi = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh + 1, row));
-            const v8i vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            O[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk[blk], O[c], 0, 0, 0, 0, 0, 0);
-          }
-        }
-      }
+      // (pv fp8: done above, with the weights)
     } else {
       // ---- pv fp16: P~ -> fp16 and O rescaled while the V copy lands; then
       //      O^T += V^T . P^T with fp32 accumulation in the MFMA, V^T read from
