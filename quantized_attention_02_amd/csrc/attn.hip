@@ -637,6 +637,18 @@ k_attn(const AttnArgs a) {
         //      adds that partial sum to the fp32 O registers passed as its C
         //      operand (level 2).  The rescale is skipped when no row of the
         //      wavefront changed its max.
+        // the first block's V fragments are read before the rescale, which
+        // covers their LDS latency (the asm keeps the reads here)
+        auto vfrag = [&](int blk, int c) -> v8i {
+          const int row = blk * D + 32 * c + qn;
+          const v4i lo = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh, row));
+          const v4i hi = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh + 1, row));
+          return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        v8i vf0[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) vf0[c] = vfrag(0, c);
+        asm volatile("; v block 0 read" ::: "memory");
         lacc[0] *= alpha;
         if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -665,10 +677,7 @@ k_attn(const AttnArgs a) {
           lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pk[blk], lacc, 0, 0, 0, 0, 0, 0);
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
-            const int row = blk * D + 32 * c + qn;
-            const v4i lo = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh, row));
-            const v4i hi = *reinterpret_cast<const v4i *>(vb + row * 64 + 16 * swz<4>(2 * hh + 1, row));
-            const v8i vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const v8i vf = blk == 0 ? vf0[c] : vfrag(blk, c);
             O[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk[blk], O[c], 0, 0, 0, 0, 0, 0);
           }
         }
