@@ -371,7 +371,10 @@ k_attn(const AttnArgs a) {
 
   // One TN-key tile: QK^T, online softmax, PV.  kb / vb: this tile's LDS.
   // pend (pv fp16): copy instructions this wavefront issued after the tile's V.
-  auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb, int pend) {
+  // prefetch: issues the copies of a later tile, or nothing (called once on
+  // every path, after the first K block's MFMAs where the wavefront has work,
+  // so that its first LDS reads follow the barrier directly)
+  auto tile = [&](int j, int buf, const uint8_t *kb, uint8_t *vb, int pend, auto &&prefetch) {
     const float *dsr = &dsbuf(QS ? buf : 0)[QS ? wave : 0][0];  // smoothed Q: this wavefront's delta row
     const float *ksr = ksbuf(TOKEN ? buf : 0);                   // per-token K: the tile's key scales
     const int key0 = j * TN;
@@ -393,6 +396,7 @@ k_attn(const AttnArgs a) {
     float p[16 * NT];
     float alpha = 1.0f;
     float gq[NB];  // pv fp4: per block, this lane's largest exponent argument (its key group's largest weight)
+    if (!work) prefetch();
     if (work) {
       // ---- S^T = K . Q^T for the NT 32-key sub-tiles, one INT8 K block (two
       //      sub-tiles) after the other, so that the first block's row max and
@@ -567,8 +571,10 @@ k_attn(const AttnArgs a) {
       // MFMA code above the branch).
       if (!need_mask) {
         asm volatile("; unmasked tile" ::: "memory");
+        qk_block(0);
+        prefetch();
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) qk_block(blk);
+        for (int blk = 1; blk < NB; ++blk) qk_block(blk);
         dump_s();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, 0, std::false_type());
@@ -577,8 +583,10 @@ k_attn(const AttnArgs a) {
         // stay in this arm rather than being hoisted into the common path
         int mlim = lim;
         asm volatile("; masked tile" : "+v"(mlim) :: "memory");
+        qk_block(0);
+        prefetch();
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) qk_block(blk);
+        for (int blk = 1; blk < NB; ++blk) qk_block(blk);
         dump_s();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, mlim, std::true_type());
@@ -825,9 +833,17 @@ k_attn(const AttnArgs a) {
       // barrier that ended the previous tile has released; issued ahead of the
       // prefetch so that the tile can wait for its V alone
       if constexpr (PV == 1) vcopy.issue(reinterpret_cast<const uint16_t *>(a.v), hv, j * TN, Sk, vbuf(0), wave);
+      // non-causal pv fp8 issues the copies inside the tile, after the first
+      // K block's MFMAs (elsewhere that costs registers: the copies go first)
+      constexpr bool DEFER = PV == 0 && !CAUSAL;
       int pend = 0;
-      if (jn < ntiles) pend = issue_tile(jn, un, kbuf(un), vbuf(PV != 1 ? un : 0));
-      tile(j, u, kbuf(u), vbuf(PV != 1 ? u : 0), pend);
+      if constexpr (!DEFER)
+        if (jn < ntiles) pend = issue_tile(jn, un, kbuf(un), vbuf(PV != 1 ? un : 0));
+      auto prefetch = [&]() {
+        if constexpr (DEFER)
+          if (jn < ntiles) issue_tile(jn, un, kbuf(un), vbuf(un));
+      };
+      tile(j, u, kbuf(u), vbuf(PV != 1 ? u : 0), pend, prefetch);
       if (jn < ntiles) wait_vm<LPT * (NBUF - 2)>();  // tile j + 1 complete; later ones may still fly
       else wait_vm<0>();
       __syncthreads();
