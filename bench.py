@@ -48,14 +48,15 @@ ATTN_SRC = os.path.join(ROOT, "quantized_attention_02_amd", "csrc", "attn.hip")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    # the shader clock settles over the first ~0.1 s of back-to-back launches
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default=None)
     p.add_argument("--causal", type=int, default=None)
     p.add_argument("--pv", default="fp8", choices=["fp8", "fp16", "fp4"])
     p.add_argument("--smooth-v", action="store_true", help="V smoothing (pv fp8): quantise V minus its channel mean")
     p.add_argument("--smooth-q", action="store_true",
-                   help="Q smoothing (fixed-length batches): quantise Q minus its 32-token block means")
+                   help="Q smoothing: quantise Q minus its 32-token block means")
     p.add_argument("--qk-quant", default="int8", choices=["int8", "int8_lane", "int8_token", "int8_head", "mxfp4"],
                    help="Q/K quantisation: INT8 per block, per Q token / 16-key lane group, per token or per head, or MXFP4")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -254,7 +255,7 @@ def main():
 
         def quant():
             qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
-                               smooth_q=args.smooth_q)
+                               smooth_q=args.smooth_q, is_causal=bool(causal))
 
         def attn():
             qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)
@@ -263,7 +264,7 @@ def main():
 
         def quant():
             qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
-                        smooth_q=args.smooth_q)
+                        smooth_q=args.smooth_q, is_causal=bool(causal))
 
         def attn():
             qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)

@@ -200,11 +200,15 @@ int sage_smooth_quant_qk(const void *q, const void *k, int dtype, int B, int H, 
  * the sum in channel order), which the attention uses as the starting value of the INT8
  * accumulator (q_scale, k_scale: from the same sage_smooth_quant_qk call; ignored
  * otherwise).  The attention then adds delta * sm_scale to every score.  qk_quant as
- * given to sage_smooth_quant_qk (not SAGE_QK_INT8_HEAD).
+ * given to sage_smooth_quant_qk (not SAGE_QK_INT8_HEAD).  is_causal (0 or 1): 1 forms
+ * only what a causal attention reads -- for each 128-key tile n0 .. n0 + 127 the rows
+ * of the query blocks whose last query 32 blk + 31 is >= n0 (a causal query sees no
+ * later key), in chunks of 32 blocks from a multiple of 32 -- and leaves the other
+ * rows unwritten; the term is then only valid for sage_attn_fwd with is_causal = 1.
  */
 int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, int qk_quant,
-                  const float *q_mean, const float *k_mean, const void *q_scale, const void *k_scale, float *delta_s,
-                  void *stream);
+                  int is_causal, const float *q_mean, const float *k_mean, const void *q_scale, const void *k_scale,
+                  float *delta_s, void *stream);
 
 /*
  * Per-channel FP8 E4M3 quantisation of V ([SA2] SageAttention2方法):
@@ -373,11 +377,11 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
 /* sage_qk_delta for a packed batch: each sequence's query blocks against its own
  * keys and K mean (k: [total_k][H_kv][D]); q_mean, k_mean, q_scale, k_scale from
  * sage_smooth_quant_qk_varlen called with q_mean; delta_s: the layout above,
- * 16-byte aligned, in fp32 or (SAGE_QK_INT8_BLOCK) in score units as in the
- * fixed-length call. */
+ * 16-byte aligned, in fp32 or (SAGE_QK_INT8_BLOCK) in score units, and is_causal
+ * (tiles counted from the sequence's first key), as in the fixed-length call. */
 int sage_qk_delta_varlen(const void *k, int dtype, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B,
                          int H, int H_kv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
-                         int qk_quant, const float *q_mean, const float *k_mean, const void *q_scale,
+                         int qk_quant, int is_causal, const float *q_mean, const float *k_mean, const void *q_scale,
                          const void *k_scale, float *delta_s, void *stream);
 
 /* sage_quant_v for a packed batch (v: [total_k][H_kv][D]); v_mean as there. */

@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.sage_get_config.argtypes = [ctypes.POINTER(c_int)] * 4
         L.sage_buffer_sizes.argtypes = [c_int] * 6 + [c_size_p] * 9
         L.sage_smooth_quant_qk.argtypes = [c_void_p, c_void_p] + [c_int] * 8 + [c_void_p] * 6 + [c_void_p]
-        L.sage_qk_delta.argtypes = [c_void_p] + [c_int] * 8 + [c_void_p] * 6
+        L.sage_qk_delta.argtypes = [c_void_p] + [c_int] * 9 + [c_void_p] * 6
         L.sage_quant_v.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
         L.sage_quantize_qkv.argtypes = [c_void_p] * 3 + [c_int] * 8 + [c_void_p] * 10
         tail = [c_int] * 8 + [c_float, c_int, c_int]
@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.sage_smooth_quant_qk_varlen.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + \
             [c_void_p] * 6 + [c_void_p]
         L.sage_varlen_smooth_q_sizes.argtypes = [c_int] * 6 + [c_size_p] * 2
-        L.sage_qk_delta_varlen.argtypes = [c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 9 + [c_void_p] * 6
+        L.sage_qk_delta_varlen.argtypes = [c_void_p, c_int, c_void_p, c_void_p] + [c_int] * 10 + [c_void_p] * 6
         L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
         L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 10 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
             [c_int, c_float, c_int, c_int, c_void_p]
@@ -123,9 +123,10 @@ def sage_quantize_qkv(q, k, v, dtype, B, H, H_kv, S, D, layout, qk_quant, q_i8, 
                                    k_mean, q_mean, v_fp8, v_scale, v_mean, stream)
 
 
-def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s, stream):
-    return lib().sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s,
-                               stream)
+def sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, qk_quant, is_causal, q_mean, k_mean, q_scale, k_scale, delta_s,
+                  stream):
+    return lib().sage_qk_delta(k, dtype, B, H, H_kv, S, D, layout, qk_quant, is_causal, q_mean, k_mean, q_scale,
+                               k_scale, delta_s, stream)
 
 
 def sage_quant_v(v, dtype, B, H, S, D, layout, v_fp8, v_scale, v_mean, stream):
@@ -191,9 +192,10 @@ def sage_smooth_quant_qk_varlen(q, k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H
 
 
 def sage_qk_delta_varlen(k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
-                         max_seqlen_k, D, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s, stream):
+                         max_seqlen_k, D, qk_quant, is_causal, q_mean, k_mean, q_scale, k_scale, delta_s, stream):
     return lib().sage_qk_delta_varlen(k, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
-                                      max_seqlen_k, D, qk_quant, q_mean, k_mean, q_scale, k_scale, delta_s, stream)
+                                      max_seqlen_k, D, qk_quant, is_causal, q_mean, k_mean, q_scale, k_scale, delta_s,
+                                      stream)
 
 
 def sage_quant_v_varlen(v, dtype, cu_seqlens_k, B, H_kv, total_k, max_seqlen_k, D, v_fp8, v_scale, v_mean, stream):
@@ -289,6 +291,7 @@ class Quantized:
         self._v4_shape = (B, H_kv, sk // BLK_K, D)
         self.smooth_v = False  # set by quantize: whether the V codes hold V minus v_mean
         self.smooth_q = False  # set by quantize: whether q_i8 holds Q minus its block means
+        self.delta_causal = False  # set by quantize: delta_s holds only what a causal attention reads
         self.v_mode = None  # set by quantize: the pv mode whose V codes hold this V ("fp8", "fp4"; None)
         self.q_mean = self.delta_s = None  # smoothed Q: allocated on first use
         self._device = device
@@ -313,7 +316,7 @@ def _kv_heads(q, k, v, tensor_layout):
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
-             qk_quant="int8", smooth_v=False, smooth_q=False, fused=True) -> Quantized:
+             qk_quant="int8", smooth_v=False, smooth_q=False, fused=True, is_causal=False) -> Quantized:
     """Run sage_quantize_qkv in pv fp8 mode (fused=False: sage_smooth_quant_qk and
     sage_quant_v, same results), sage_smooth_quant_qk and sage_quant_v_fp4 in pv
     fp4 mode, or sage_smooth_quant_qk alone in pv fp16 mode, on torch tensors.
@@ -322,7 +325,8 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
     K), "int8_token" (one per Q token and per K token), "int8_head" (one per
     head of Q and of K; not with smooth_q) or "mxfp4"; smooth_v
     (pv fp8, fp4): quantise V minus its channel mean; smooth_q: quantise Q minus its
-    32-token block means and form the pre-processing term."""
+    32-token block means and form the pre-processing term (is_causal: only the part
+    a causal attention reads; the buffers then serve causal attention only)."""
     if pv_mode not in PV:
         raise ValueError(f"pv_mode must be one of {sorted(PV)}, got {pv_mode!r}")
     if smooth_v and pv_mode == "fp16":
@@ -345,6 +349,7 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         bufs.q_mean = torch.empty((B, H, nq, D), dtype=torch.float32, device=q.device)
         bufs.delta_s = torch.empty((B, H, sk // KV_PAD, nq, KV_PAD), dtype=torch.float32, device=q.device)
     bufs.smooth_q = bool(smooth_q)
+    bufs.delta_causal = bool(smooth_q and is_causal)
     bufs.smooth_v = bool(smooth_v)
     bufs.v_mode = pv_mode if pv_mode != "fp16" else None
     qm = bufs.q_mean.data_ptr() if smooth_q else None
@@ -366,9 +371,9 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
             _check(sage_quant_v_fp4(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp4.data_ptr(),
                                     bufs.v_e8m0.data_ptr(), vm, st), "sage_quant_v_fp4")
     if smooth_q:
-        _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk, bufs.q_mean.data_ptr(),
-                             bufs.k_mean.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_scale.data_ptr(),
-                             bufs.delta_s.data_ptr(), st), "sage_qk_delta")
+        _check(sage_qk_delta(k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk, int(bufs.delta_causal),
+                             bufs.q_mean.data_ptr(), bufs.k_mean.data_ptr(), bufs.q_scale.data_ptr(),
+                             bufs.k_scale.data_ptr(), bufs.delta_s.data_ptr(), st), "sage_qk_delta")
     return bufs
 
 
@@ -384,6 +389,8 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
         raise ValueError("pv fp16 reads the original V: it must be contiguous with H_kv heads")
     dt = _dtype_code(out)
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    if bufs.delta_causal and not is_causal:
+        raise ValueError("these buffers hold the pre-processing term of a causal attention only")
     vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
     ds = bufs.delta_s.data_ptr() if bufs.smooth_q else None
@@ -435,7 +442,8 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mo
             raise ValueError(f"pv_accum_dtype must be one of {sorted(PV_ACCUM)} (an fp16 inner accumulator, "
                              f"'fp32+fp16', is not built), got {pv_accum_dtype!r}")
         pv_mode = PV_ACCUM[pv_accum_dtype]
-    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q)
+    bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q,
+                    is_causal=is_causal)
     out = torch.empty_like(q)
     return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
 
@@ -483,6 +491,7 @@ class QuantizedVarlen:
         self._device = device
         self.smooth_v = False
         self.smooth_q = False  # set by quantize_varlen: whether q_i8 holds Q minus its block means
+        self.delta_causal = False  # set by quantize_varlen: delta_s holds only what a causal attention reads
         # smoothed Q: q_mean [H][RQ / 32][D] and delta_s [H][RK / 128][MQ][128],
         # MQ = ceil(max_seqlen_q / 32) (allocated by quantize_varlen on first use)
         self.q_mean = self.delta_s = None
@@ -512,11 +521,11 @@ def _cu(t, name):
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
                     bufs: QuantizedVarlen | None = None, qk_quant="int8", smooth_v=False,
-                    smooth_q=False) -> QuantizedVarlen:
+                    smooth_q=False, is_causal=False) -> QuantizedVarlen:
     """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode,
     sage_quant_v_fp4_varlen in pv fp4 mode, sage_qk_delta_varlen with smooth_q)
     on a packed batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens
-    int32 [B + 1]; smooth_v, smooth_q as in quantize."""
+    int32 [B + 1]; smooth_v, smooth_q, is_causal as in quantize."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_q, H, D] and k, v [total_k, H_kv, D]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -544,6 +553,7 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     if smooth_q:
         bufs.alloc_smooth_q(bufs.max_seqlen_q)
     bufs.smooth_q = bool(smooth_q)
+    bufs.delta_causal = bool(smooth_q and is_causal)
     qm = bufs.q_mean.data_ptr() if smooth_q else None
     st = _stream()
     _check(sage_smooth_quant_qk_varlen(q.data_ptr(), k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
@@ -564,9 +574,9 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                "sage_quant_v_fp4_varlen")
     if smooth_q:
         _check(sage_qk_delta_varlen(k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv, total_q, total_k,
-                                    bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk, bufs.q_mean.data_ptr(),
-                                    bufs.k_mean.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_scale.data_ptr(),
-                                    bufs.delta_s.data_ptr(), st), "sage_qk_delta_varlen")
+                                    bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk, int(bufs.delta_causal),
+                                    bufs.q_mean.data_ptr(), bufs.k_mean.data_ptr(), bufs.q_scale.data_ptr(),
+                                    bufs.k_scale.data_ptr(), bufs.delta_s.data_ptr(), st), "sage_qk_delta_varlen")
     return bufs
 
 
@@ -579,6 +589,8 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     if pv_mode == "fp16" and (tuple(v.shape) != (bufs.total_k, H_kv, D) or not v.is_contiguous()):
         raise ValueError("pv fp16 reads the original V: it must be a contiguous [total_k, H_kv, D] tensor")
     cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    if bufs.delta_causal and not is_causal:
+        raise ValueError("these buffers hold the pre-processing term of a causal attention only")
     vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
@@ -601,6 +613,6 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     import torch
 
     bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_quant=qk_quant,
-                           smooth_v=smooth_v, smooth_q=smooth_q)
+                           smooth_v=smooth_v, smooth_q=smooth_q, is_causal=is_causal)
     out = torch.empty_like(q)
     return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)

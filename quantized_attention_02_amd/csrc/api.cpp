@@ -298,10 +298,11 @@ int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
 }
 
 int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D, int layout, int qk_quant,
-                  const float *q_mean, const float *k_mean, const void *q_scale, const void *k_scale, float *delta_s,
-                  void *stream) {
+                  int is_causal, const float *q_mean, const float *k_mean, const void *q_scale, const void *k_scale,
+                  float *delta_s, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
   if ((rc = check_enums(dtype, layout))) return rc;
   if ((rc = check_qk_quant(qk_quant)) || qk_quant == SAGE_QK_INT8_HEAD) return SAGE_ERR_INVALID_ARG;
@@ -331,6 +332,7 @@ int sage_qk_delta(const void *k, int dtype, int B, int H, int H_kv, int S, int D
   a.S_k = roundup(S, kKvPad);
   a.nq = a.S_q / kBlkQ;
   a.nk = a.S_k / kBlkK;
+  a.causal = is_causal;
   return launch_status(launch_qk_delta(a, delta_s, (hipStream_t)stream));
 }
 
@@ -463,11 +465,11 @@ int sage_varlen_smooth_q_sizes(int B, int H, int total_q, int total_k, int max_s
 
 int sage_qk_delta_varlen(const void *k, int dtype, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B,
                          int H, int H_kv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D,
-                         int qk_quant, const float *q_mean, const float *k_mean, const void *q_scale,
+                         int qk_quant, int is_causal, const float *q_mean, const float *k_mean, const void *q_scale,
                          const void *k_scale, float *delta_s, void *stream) {
   int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_quant);
   if (rc) return rc;
-  if (qk_quant == SAGE_QK_INT8_HEAD) return SAGE_ERR_INVALID_ARG;
+  if (qk_quant == SAGE_QK_INT8_HEAD || (is_causal != 0 && is_causal != 1)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (!k || !q_mean || !k_mean || !delta_s || !cu_seqlens_q || !cu_seqlens_k) return SAGE_ERR_INVALID_ARG;
   if (!aligned(k, 16) || !aligned(q_mean, 16) || !aligned(k_mean, 4) || !aligned(delta_s, 16) ||
@@ -497,6 +499,7 @@ int sage_qk_delta_varlen(const void *k, int dtype, const int32_t *cu_seqlens_q, 
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
   a.qk = qk_quant;
+  a.causal = is_causal;
   return launch_status(launch_qk_delta(a, delta_s, (hipStream_t)stream));
 }
 

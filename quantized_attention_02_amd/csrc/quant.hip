@@ -457,7 +457,11 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   };
   // stage the means in x (one chunk) into buffer buf: split pieces and dot
   // products with k_mean
-  int blk0_of_buf[2] = {0, 32};  // the first query block of the chunk staged in each buffer
+  // causal attention reads tile kt only for query blocks whose last query can
+  // see one of its keys (32 blk + 31 >= 128 kt, i.e. blk >= 4 kt); the tile's
+  // other rows are left unwritten (chunks start at a multiple of 32 blocks)
+  const int first = a.causal ? min(kt * (kDeltaKeys / kBlkQ), nqb) & ~31 : 0;
+  int blk0_of_buf[2] = {first, first + 32};  // the first query block of the chunk staged in each buffer
   auto stage = [&](const float (&x)[CPT], int buf) {
     float c = 0.0f, sa = 0.0f;
 #pragma unroll
@@ -533,10 +537,10 @@ __global__ __launch_bounds__(kThreads) void k_qk_delta(const QuantQKArgs a, floa
   // other buffer after chunk c's stores; that buffer's last readers (chunk c - 1)
   // are past chunk c's barrier.
   float xa[CPT], xb[CPT];
-  load_means(xa, 0);
-  load_means(xb, 32);
+  load_means(xa, first);
+  load_means(xb, first + 32);
   stage(xa, 0);
-  for (int blk0 = 0; blk0 < nqb; blk0 += 64) {
+  for (int blk0 = first; blk0 < nqb; blk0 += 64) {
     __syncthreads();
     load_means(xa, blk0 + 64);
     compute(blk0, 0);

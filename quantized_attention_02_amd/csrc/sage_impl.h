@@ -151,6 +151,7 @@ struct QuantQKArgs {
   long long rows_q, rows_k;  // buffer rows per head (packed batch)
   int qk;                    // Q/K quantisation: 0 INT8 per block, 1 INT8 per lane, 2 MXFP4
   float *q_mean;             // smoothed Q: block means [B][H][nq][D] (nullptr: no Q smoothing)
+  int causal;                // pre-processing term: only what a causal attention reads
 };
 
 struct QuantVArgs {

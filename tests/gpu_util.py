@@ -47,7 +47,9 @@ def run(w: synth.Workload, *, causal=False, pv="fp8", sm_scale=None, dump_head=N
 
     q, k, v = inputs(w)
     qd, kd, vd = (to_device(x, w.dtype) for x in (q, k, v))
-    bufs = qa.quantize(qd, kd, vd, w.layout, pv, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q)
+    # smoothed Q: a causal attention gets the term formed for causal attention
+    bufs = qa.quantize(qd, kd, vd, w.layout, pv, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q,
+                       is_causal=causal)
     out = nan_like(qd)
     dump = None
     if dump_head is not None:

@@ -87,8 +87,8 @@ def test_vpos_key_is_a_permutation():
 P = 1 << 12
 GOOD_QK = dict(q=P, k=P, dtype=0, B=1, H=2, H_kv=2, S=100, D=64, layout=0, qk_quant=0, q_i8=P, q_scale=P, k_i8=P,
                k_scale=P, k_mean=P, q_mean=None, stream=None)
-GOOD_DELTA = dict(k=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64, layout=1, qk_quant=0, q_mean=P, k_mean=P, q_scale=P,
-                  k_scale=P, delta_s=P, stream=None)
+GOOD_DELTA = dict(k=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64, layout=1, qk_quant=0, is_causal=0, q_mean=P, k_mean=P,
+                  q_scale=P, k_scale=P, delta_s=P, stream=None)
 GOOD_V = dict(v=P, dtype=0, B=1, H=2, S=100, D=64, layout=0, v_fp8=P, v_scale=P, v_mean=None, stream=None)
 GOOD_ATTN = dict(q_i8=P, q_scale=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, q_mean=None, delta_s=None, out=P, dtype=0, B=1,
                  H=2, H_kv=2, S=100,
@@ -103,7 +103,7 @@ BAD_DELTA = [dict(k=None), dict(q_mean=None), dict(k_mean=None), dict(delta_s=No
              dict(delta_s=P + 2), dict(delta_s=P + 4), dict(k=P + 8), dict(H_kv=3), dict(D=96), dict(layout=2),
              # INT8 per-block scales: the term in score units needs both scale buffers
              dict(q_scale=None), dict(k_scale=None), dict(q_scale=P + 2), dict(qk_quant=4), dict(qk_quant=5),
-             dict(dtype=4), dict(S=0)]
+             dict(dtype=4), dict(S=0), dict(is_causal=2), dict(is_causal=-1)]
 BAD_V = [dict(v=None), dict(v_fp8=P + 4), dict(v_scale=None), dict(dtype=7), dict(layout=3), dict(D=80),
          dict(v_mean=P + 2)]
 BAD_ATTN = [dict(q_i8=None), dict(out=None), dict(v=P + 1), dict(out=P + 8), dict(v_scale=None),
@@ -218,6 +218,7 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _call_attn(delta_s=P, q_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(delta_s=P, qk_quant=1) == qa.SAGE_ERR_NO_DEVICE  # fp32 terms: no means needed
     assert qa.sage_qk_delta(*GOOD_DELTA.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_qk_delta(*{**GOOD_DELTA, "is_causal": 1}.values()) == qa.SAGE_ERR_NO_DEVICE
     # the other Q/K formats write fp32 terms and do not read the scales
     assert qa.sage_qk_delta(*{**GOOD_DELTA, "qk_quant": 1, "q_scale": None, "k_scale": None}.values()) == \
         qa.SAGE_ERR_NO_DEVICE
@@ -287,11 +288,11 @@ BAD_ATTN_VL = [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P + 1), dict(is_causa
                dict(delta_s=P), dict(delta_s=P + 2, q_mean=P), dict(delta_s=P, q_mean=P + 1),
                dict(delta_s=P, qk_quant=4)]
 GOOD_DELTA_VL = dict(k=P, dtype=0, cu_q=P, cu_k=P, B=3, H=4, H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90,
-                     D=64, qk_quant=0, q_mean=P, k_mean=P, q_scale=P, k_scale=P, delta_s=P, stream=None)
+                     D=64, qk_quant=0, is_causal=1, q_mean=P, k_mean=P, q_scale=P, k_scale=P, delta_s=P, stream=None)
 BAD_DELTA_VL = [dict(k=None), dict(cu_q=None), dict(cu_k=P + 1), dict(q_mean=None), dict(q_mean=P + 4),
                 dict(k_mean=None), dict(delta_s=P + 8), dict(delta_s=None), dict(q_scale=None), dict(k_scale=P + 2),
                 dict(qk_quant=4), dict(qk_quant=6), dict(dtype=2), dict(D=96), dict(H_kv=3), dict(max_q=0),
-                dict(B=0), dict(total_k=-1)]
+                dict(B=0), dict(total_k=-1), dict(is_causal=3)]
 
 
 @pytest.mark.parametrize("bad", BAD_QK_VL, ids=[str(b) for b in BAD_QK_VL])

@@ -148,3 +148,41 @@ def test_smooth_q_full_size_sampled():
         ref = O.attn(q, k, v, O.DTYPES[w.dtype], w.layout, heads=[(b, h)], rows=rows, smooth_q=True)[(b, h)]
         g = got[b, h, rows]
         G.assert_parity(g, ref, "gpu_smooth_q")
+
+
+CAUSAL_CASES = [
+    (synth.custom(1, 2, 1000, 128, q_bias_sigma=3.0, seed=1231), "int8"),
+    (synth.custom(2, 4, 300, 64, Hkv=2, layout="NHD", q_bias_sigma=2.0, seed=1232), "int8_token"),
+    (synth.custom(1, 2, 2049, 128, dtype="bf16", q_bias_sigma=4.0, seed=1233), "mxfp4"),
+]
+
+
+@pytest.mark.parametrize("w,qk", CAUSAL_CASES, ids=[f"{w.name}-{qk}" for w, qk in CAUSAL_CASES])
+def test_causal_term_covers_what_causal_attention_reads(w, qk):
+    """The pre-processing term formed for causal attention: every row it writes
+    equals the full term's bit for bit, the rows it must write (query block blk of
+    tile t whenever 32 blk + 31 >= 128 t) are written, and the causal attention
+    output is bit-identical to the one computed from the full term.  The causal
+    buffers refuse a non-causal attention."""
+    import torch
+
+    import quantized_attention_02_amd as qa
+
+    qd, kd, vd = (G.to_device(x, w.dtype) for x in G.inputs(w))
+    full = qa.quantize(qd, kd, vd, w.layout, "fp8", qk_quant=qk, smooth_q=True)
+    ref = qa.attn_fwd(full, vd, G.nan_like(qd), w.layout, True, None, "fp8")
+    part = qa.quantize(qd, kd, vd, w.layout, "fp8", qk_quant=qk, smooth_q=True, is_causal=True)
+    part.delta_s.fill_(float("nan"))  # rows the causal pass skips stay NaN
+    qa.quantize(qd, kd, vd, w.layout, "fp8", part, qk_quant=qk, smooth_q=True, is_causal=True)
+    got = qa.attn_fwd(part, vd, G.nan_like(qd), w.layout, True, None, "fp8")
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    f, p_ = full.delta_s.cpu().numpy().view(np.uint32), part.delta_s.cpu().numpy().view(np.uint32)
+    nan = np.float32("nan").view(np.uint32)
+    written = p_ != nan
+    assert np.array_equal(p_[written], f[written])
+    nt, nq = f.shape[2], f.shape[3]
+    need = (32 * np.arange(nq)[None, :] + 31) >= 128 * np.arange(nt)[:, None]  # [tile][block]
+    assert written.transpose(0, 1, 2, 3, 4).all(axis=4)[:, :, need].all()
+    with pytest.raises(ValueError):
+        qa.attn_fwd(part, vd, G.nan_like(qd), w.layout, False, None, "fp8")

@@ -50,7 +50,7 @@ def _run(w, causal, pv, dev, cud, qk_quant="int8", smooth_q=False):
 
     qd, kd, vd = dev
     bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max(w.seqlens_q), max(max(w.seqlens_k), 1), pv,
-                              qk_quant=qk_quant, smooth_q=smooth_q)
+                              qk_quant=qk_quant, smooth_q=smooth_q, is_causal=causal)
     out = torch.full_like(qd, float("nan"))
     qa.attn_fwd_varlen(bufs, vd, out, cud[0], cud[1], causal, None, pv)
     torch.cuda.synchronize()
@@ -308,7 +308,8 @@ def test_varlen_smooth_q(w, causal, pv, qk):
     (q, k, v, cq, ck), dev, cud = _inputs(w)
     qd, kd, vd = dev
     max_q, max_k = max(w.seqlens_q), max(max(w.seqlens_k), 1)
-    bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max_q, max_k, pv, qk_quant=qk, smooth_q=True)
+    bufs = qa.quantize_varlen(qd, kd, vd, cud[0], cud[1], max_q, max_k, pv, qk_quant=qk, smooth_q=True,
+                              is_causal=causal)
     out = torch.full_like(qd, float("nan"))
     qa.attn_fwd_varlen(bufs, vd, out, cud[0], cud[1], causal, None, pv)
     torch.cuda.synchronize()
