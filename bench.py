@@ -317,7 +317,7 @@ def main():
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,
                     "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv,
-                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v} if varlen else
+                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q} if varlen else
                    {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
                     "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv,
                     "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q}),
