@@ -66,6 +66,9 @@ def parse():
                    help="only time the CPU oracle on the workload (all heads, or --cpu-heads of them scaled to "
                         "all) on the host cores, median of --oracle-repeats runs; no GPU use")
     p.add_argument("--oracle-repeats", type=int, default=1)
+    p.add_argument("--q-pass", action="store_true",
+                   help="INT8 per-block Q/K without Q smoothing: quantise Q in the Q/K pass and read its codes "
+                        "(default: the attention kernel quantises Q itself, sage_attn_fwd_q16)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return p.parse_args()
@@ -88,7 +91,7 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_record(kernel_hash, workload, pv, causal, qk="int8", smooth_v=False, smooth_q=False):
+def traffic_record(kernel_hash, workload, pv, causal, qk="int8", smooth_v=False, smooth_q=False, q_in_attn=False):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summaries, if one was taken on the current kernel source for this workload
     and mode."""
@@ -99,7 +102,8 @@ def traffic_record(kernel_hash, workload, pv, causal, qk="int8", smooth_v=False,
     for rec in recs:
         if (rec.get("attn_src_sha256_16") == kernel_hash and rec.get("workload") == workload
                 and rec.get("pv_mode") == pv and rec.get("causal") == causal and rec.get("qk_quant", "int8") == qk
-                and rec.get("smooth_v", False) == smooth_v and rec.get("smooth_q", False) == smooth_q):
+                and rec.get("smooth_v", False) == smooth_v and rec.get("smooth_q", False) == smooth_q
+                and rec.get("q_in_attn", False) == q_in_attn):
             return rec
     return None
 
@@ -248,6 +252,8 @@ def main():
     tdt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
     qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
     out = torch.empty_like(qd)
+    # INT8 per-block Q/K, unsmoothed Q: the attention kernel quantises Q itself
+    q_in_attn = args.qk_quant == "int8" and not args.smooth_q and not args.q_pass
     if varlen:
         cq, ck = (torch.from_numpy(c).to(dev) for c in w.cu_seqlens())
         mq, mk = max(w.seqlens_q), max(w.seqlens_k)
@@ -255,19 +261,19 @@ def main():
 
         def quant():
             qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
-                               smooth_q=args.smooth_q, is_causal=bool(causal))
+                               smooth_q=args.smooth_q, is_causal=bool(causal), q_in_attn=q_in_attn)
 
         def attn():
-            qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv)
+            qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv, q=qd)
     else:
         bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_quant)
 
         def quant():
             qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
-                        smooth_q=args.smooth_q, is_causal=bool(causal))
+                        smooth_q=args.smooth_q, is_causal=bool(causal), q_in_attn=q_in_attn)
 
         def attn():
-            qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv)
+            qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv, q=qd)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
@@ -297,7 +303,7 @@ def main():
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     khash = source_hash(ATTN_SRC)
-    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_quant, args.smooth_v, args.smooth_q)
+    trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_quant, args.smooth_v, args.smooth_q, q_in_attn)
     traffic = None if trec is None else trec["hbm_bytes_per_launch"]
 
     res = {
@@ -317,10 +323,12 @@ def main():
         "config": ({"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "total_q": w.total_q,
                     "total_k": w.total_k, "max_seqlen": max(w.seqlens_q), "D": w.D, "input_dtype": w.dtype,
                     "layout": "packed [T, H, D]", "causal": causal, "pv_mode": args.pv,
-                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q} if varlen else
+                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q,
+                    "q_quantised_in": "attention" if q_in_attn else "q/k pass"} if varlen else
                    {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
                     "input_dtype": w.dtype, "layout": w.layout, "causal": causal, "pv_mode": args.pv,
-                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q}),
+                    "qk_quant": args.qk_quant, "smooth_v": args.smooth_v, "smooth_q": args.smooth_q,
+                    "q_quantised_in": "attention" if q_in_attn else "q/k pass"}),
         "kernels_ms": {"quant_qk_plus_quant_v": round(quant_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "attn_fwd_tops": round(attn_tops, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(mfma_peak(args.pv, args.qk_quant), 1), "unit": "TFLOP/s",

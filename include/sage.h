@@ -25,7 +25,9 @@
  *           blocks.
  *
  * Pipeline: sage_smooth_quant_qk -> sage_quant_v (pv fp8) or sage_quant_v_fp4 (pv fp4)
- *           -> sage_attn_fwd.
+ *           -> sage_attn_fwd; or, with INT8 per-block Q/K and unsmoothed Q, the Q/K pass
+ *           without Q -> the V pass -> sage_attn_fwd_q16 (Q quantised in the attention
+ *           kernel, same results).
  *
  * Common rules for every entry point:
  *  - Tensor pointers are DEVICE pointers; every call only enqueues work on
@@ -177,7 +179,9 @@ int sage_buffer_sizes(int B, int H, int H_kv, int S, int D, int qk_quant, size_t
  * subtracted (one fp32 subtraction) before the INT8 or MXFP4 rule; sage_qk_delta then forms the
  * term the attention adds back.
  * Writes q_codes, q_scale, k_codes, k_scale, k_mean (layouts above; their element
- * types follow qk_quant).  The call is several kernel launches; while it runs,
+ * types follow qk_quant).  q, q_codes and q_scale may all be NULL with
+ * SAGE_QK_INT8_BLOCK and q_mean = NULL: K alone is smoothed and quantised, for
+ * sage_attn_fwd_q16, which quantises Q itself.  The call is several kernel launches; while it runs,
  * k_codes also holds intermediate
  * per-chunk channel sums, so its content is defined only after the stream has
  * passed the call.
@@ -249,7 +253,8 @@ int sage_v_fp4_buffer_sizes(int B, int H_kv, int S, int D, size_t *v_codes, size
  * the same arguments, checks and results (every output buffer bit for bit), with
  * the passes that do not depend on each other sharing kernel launches (four
  * launches instead of eight).  For pv fp8; v: the V tensor (dtype, layout,
- * H_kv heads).  q_mean and v_mean select Q and V smoothing as in the two calls.
+ * H_kv heads).  q_mean and v_mean select Q and V smoothing as in the two calls, and
+ * q, q_codes, q_scale may all be NULL as in sage_smooth_quant_qk (K and V only).
  */
 int sage_quantize_qkv(const void *q, const void *k, const void *v, int dtype, int B, int H, int H_kv, int S, int D,
                       int layout, int qk_quant, void *q_codes, void *q_scale, void *k_codes, void *k_scale,
@@ -299,6 +304,22 @@ int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes,
                   const void *v, const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s,
                   void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal,
                   float sm_scale, int pv_mode, int qk_quant, void *stream);
+
+/*
+ * sage_attn_fwd with the Q quantisation folded in (SAGE_QK_INT8_BLOCK, unsmoothed Q):
+ * q is the dtype tensor of sage_smooth_quant_qk (16-byte aligned), and each
+ * SAGE_BLK_Q-token block of it is quantised inside the attention kernel by the rule
+ * of the Q pass -- block abs-max over its valid tokens, code = clamp(rint(x * (127 /
+ * amax)), -127, 127), scale amax / 127, in the same fp32 operations -- so the codes,
+ * and the output, are bit-identical to sage_smooth_quant_qk followed by sage_attn_fwd
+ * with SAGE_QK_INT8_BLOCK.  This saves the Q pass's read of q and write of the codes
+ * and the attention's read of the codes.  k_codes, k_scale: from sage_smooth_quant_qk
+ * or sage_quantize_qkv with SAGE_QK_INT8_BLOCK (either may omit Q); the other
+ * arguments as in sage_attn_fwd.
+ */
+int sage_attn_fwd_q16(const void *q, const void *k_codes, const void *k_scale, const void *v, const float *v_scale,
+                      const float *v_mean, void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout,
+                      int is_causal, float sm_scale, int pv_mode, void *stream);
 
 /*
  * Debug variant of sage_attn_fwd (INT8 modes, no smoothed-Q term): the same
@@ -367,7 +388,8 @@ int sage_varlen_smooth_q_sizes(int B, int H, int total_q, int total_k, int max_s
 
 /* sage_smooth_quant_qk for a packed batch; q_mean: NULL, or the [H][RQ / 32][D]
  * buffer of block means (smoothed Q, as in the fixed-length call: each block's
- * means are of the sequence's own tokens in it). */
+ * means are of the sequence's own tokens in it).  q, q_codes and q_scale may all be
+ * NULL as in the fixed-length call (for sage_attn_fwd_varlen_q16). */
 int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const int32_t *cu_seqlens_q,
                                 const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                                 int max_seqlen_q, int max_seqlen_k, int D, int qk_quant, void *q_codes,
@@ -408,6 +430,15 @@ int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k
                          const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
                          int qk_quant, void *stream);
+
+/* sage_attn_fwd_varlen with the Q quantisation folded in, as sage_attn_fwd_q16: q is
+ * the packed [total_q][H][D] dtype tensor; each sequence's 32-token blocks (from its
+ * first token) are quantised in the kernel. */
+int sage_attn_fwd_varlen_q16(const void *q, const void *k_codes, const void *k_scale, const void *v,
+                             const float *v_scale, const float *v_mean, void *out, int dtype,
+                             const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B, int H, int H_kv,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D, int is_causal,
+                             float sm_scale, int pv_mode, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *sage_status_str(int status);

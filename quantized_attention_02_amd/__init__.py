@@ -34,7 +34,7 @@ EXPORTED = ["sage_get_config", "sage_buffer_sizes", "sage_smooth_quant_qk", "sag
             "sage_attn_fwd_dump_qk", "sage_qk_delta", "sage_varlen_buffer_sizes", "sage_smooth_quant_qk_varlen", "sage_quant_v_varlen",
             "sage_attn_fwd_varlen", "sage_status_str", "sage_check_arch", "sage_quant_v_fp4", "sage_v_fp4_buffer_sizes",
             "sage_quant_v_fp4_varlen", "sage_varlen_v_fp4_buffer_sizes", "sage_varlen_smooth_q_sizes",
-            "sage_qk_delta_varlen"]
+            "sage_qk_delta_varlen", "sage_attn_fwd_q16", "sage_attn_fwd_varlen_q16"]
 
 _lib = None
 
@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.sage_quant_v_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
         L.sage_attn_fwd_varlen.argtypes = [c_void_p] * 10 + [c_int, c_void_p, c_void_p] + [c_int] * 8 + \
             [c_int, c_float, c_int, c_int, c_void_p]
+        L.sage_attn_fwd_q16.argtypes = [c_void_p] * 7 + [c_int] * 8 + [c_float, c_int, c_void_p]
+        L.sage_attn_fwd_varlen_q16.argtypes = [c_void_p] * 7 + [c_int, c_void_p, c_void_p] + [c_int] * 9 + \
+            [c_float, c_int, c_void_p]
         L.sage_quant_v_fp4.argtypes = [c_void_p] + [c_int] * 6 + [c_void_p] * 4
         L.sage_v_fp4_buffer_sizes.argtypes = [c_int] * 4 + [c_size_p] * 2
         L.sage_quant_v_fp4_varlen.argtypes = [c_void_p, c_int, c_void_p] + [c_int] * 5 + [c_void_p] * 4
@@ -161,6 +164,19 @@ def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, q_mean, delt
                   layout, is_causal, sm_scale, pv_mode, qk_quant, stream):
     return lib().sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, B, H,
                                H_kv, S, D, layout, is_causal, sm_scale, pv_mode, qk_quant, stream)
+
+
+def sage_attn_fwd_q16(q, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout, is_causal, sm_scale,
+                      pv_mode, stream):
+    return lib().sage_attn_fwd_q16(q, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
+                                   is_causal, sm_scale, pv_mode, stream)
+
+
+def sage_attn_fwd_varlen_q16(q, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q, cu_seqlens_k, B, H, H_kv,
+                             total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal, sm_scale, pv_mode, stream):
+    return lib().sage_attn_fwd_varlen_q16(q, k_i8, k_scale, v, v_scale, v_mean, out, dtype, cu_seqlens_q, cu_seqlens_k,
+                                          B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, is_causal,
+                                          sm_scale, pv_mode, stream)
 
 
 def sage_attn_fwd_dump_qk(q_i8, q_scale, k_i8, k_scale, v, v_scale, v_mean, out, dtype, B, H, H_kv, S, D, layout,
@@ -292,6 +308,7 @@ class Quantized:
         self.smooth_v = False  # set by quantize: whether the V codes hold V minus v_mean
         self.smooth_q = False  # set by quantize: whether q_i8 holds Q minus its block means
         self.delta_causal = False  # set by quantize: delta_s holds only what a causal attention reads
+        self.q_in_attn = False  # set by quantize: Q left unquantised, for the attention to quantise
         self.v_mode = None  # set by quantize: the pv mode whose V codes hold this V ("fp8", "fp4"; None)
         self.q_mean = self.delta_s = None  # smoothed Q: allocated on first use
         self._device = device
@@ -316,7 +333,8 @@ def _kv_heads(q, k, v, tensor_layout):
 
 
 def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None = None,
-             qk_quant="int8", smooth_v=False, smooth_q=False, fused=True, is_causal=False) -> Quantized:
+             qk_quant="int8", smooth_v=False, smooth_q=False, fused=True, is_causal=False,
+             q_in_attn=False) -> Quantized:
     """Run sage_quantize_qkv in pv fp8 mode (fused=False: sage_smooth_quant_qk and
     sage_quant_v, same results), sage_smooth_quant_qk and sage_quant_v_fp4 in pv
     fp4 mode, or sage_smooth_quant_qk alone in pv fp16 mode, on torch tensors.
@@ -326,11 +344,15 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
     head of Q and of K; not with smooth_q) or "mxfp4"; smooth_v
     (pv fp8, fp4): quantise V minus its channel mean; smooth_q: quantise Q minus its
     32-token block means and form the pre-processing term (is_causal: only the part
-    a causal attention reads; the buffers then serve causal attention only)."""
+    a causal attention reads; the buffers then serve causal attention only);
+    q_in_attn (INT8 per block, unsmoothed Q): leave Q to the attention kernel
+    (sage_attn_fwd_q16: attn_fwd then needs q), same results."""
     if pv_mode not in PV:
         raise ValueError(f"pv_mode must be one of {sorted(PV)}, got {pv_mode!r}")
     if smooth_v and pv_mode == "fp16":
         raise ValueError("smooth_v applies to the quantised V of pv_mode 'fp8' and 'fp4'")
+    if q_in_attn and (qk_quant != "int8" or smooth_q):
+        raise ValueError("q_in_attn: the attention kernel quantises Q with INT8 per-block scales, unsmoothed")
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(q, tensor_layout)
     H_kv = _kv_heads(q, k, v, tensor_layout)
@@ -350,19 +372,21 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
         bufs.delta_s = torch.empty((B, H, sk // KV_PAD, nq, KV_PAD), dtype=torch.float32, device=q.device)
     bufs.smooth_q = bool(smooth_q)
     bufs.delta_causal = bool(smooth_q and is_causal)
+    bufs.q_in_attn = bool(q_in_attn)
     bufs.smooth_v = bool(smooth_v)
     bufs.v_mode = pv_mode if pv_mode != "fp16" else None
     qm = bufs.q_mean.data_ptr() if smooth_q else None
     vm = bufs.v_mean.data_ptr() if smooth_v else None
+    # Q omitted (all three NULL) when the attention kernel quantises it
+    qp, q8, qs = (None, None, None) if q_in_attn else (q.data_ptr(), bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr())
     if pv_mode == "fp8" and fused:
-        _check(sage_quantize_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
-                                 bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
-                                 bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, bufs.v_fp8.data_ptr(),
-                                 bufs.v_scale.data_ptr(), vm, st), "sage_quantize_qkv")
+        _check(sage_quantize_qkv(qp, k.data_ptr(), v.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk, q8, qs,
+                                 bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm,
+                                 bufs.v_fp8.data_ptr(), bufs.v_scale.data_ptr(), vm, st), "sage_quantize_qkv")
     else:
-        _check(sage_smooth_quant_qk(q.data_ptr(), k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk,
-                                    bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
-                                    bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, st), "sage_smooth_quant_qk")
+        _check(sage_smooth_quant_qk(qp, k.data_ptr(), dt, B, H, H_kv, S, D, layout, bufs.qk, q8, qs,
+                                    bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, st),
+               "sage_smooth_quant_qk")
         if pv_mode == "fp8":
             _check(sage_quant_v(v.data_ptr(), dt, B, H_kv, S, D, layout, bufs.v_fp8.data_ptr(),
                                 bufs.v_scale.data_ptr(), vm, st), "sage_quant_v")
@@ -378,8 +402,9 @@ def quantize(q, k, v, tensor_layout="HND", pv_mode="fp8", bufs: Quantized | None
 
 
 def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mode="fp8",
-             dump_head=None, dump=None):
-    """Run sage_attn_fwd (or the dump variant when dump_head=(b, h)) into `out`."""
+             dump_head=None, dump=None, q=None):
+    """Run sage_attn_fwd (or the dump variant when dump_head=(b, h)) into `out`;
+    with buffers quantised with q_in_attn, sage_attn_fwd_q16 on q (the input Q)."""
     layout = LAYOUT[tensor_layout]
     B, H, S, D = _shape(out, tensor_layout)
     if (bufs.B, bufs.H, bufs.S, bufs.D) != (B, H, S, D):
@@ -397,6 +422,15 @@ def attn_fwd(bufs: Quantized, v, out, tensor_layout="HND", is_causal=False, sm_s
     qm = bufs.q_mean.data_ptr() if bufs.smooth_q else None
     head = (bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs, vm)
     tail = (out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv, bufs.qk)
+    if bufs.q_in_attn:
+        if q is None or tuple(q.shape) != tuple(out.shape) or q.dtype != out.dtype or not q.is_contiguous():
+            raise ValueError("these buffers hold no Q codes: pass q, the input Q (same shape, dtype and layout as out)")
+        if dump_head is not None:
+            raise ValueError("the Q K^T dump reads Q codes: quantise without q_in_attn")
+        _check(sage_attn_fwd_q16(q.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs, vm,
+                                 out.data_ptr(), dt, B, H, H_kv, S, D, layout, int(bool(is_causal)), sm, pv,
+                                 _stream()), "sage_attn_fwd_q16")
+        return out
     if dump_head is None:
         _check(sage_attn_fwd(*head, qm, ds, *tail, _stream()), "sage_attn_fwd")
     else:
@@ -442,10 +476,12 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, pv_mo
             raise ValueError(f"pv_accum_dtype must be one of {sorted(PV_ACCUM)} (an fp16 inner accumulator, "
                              f"'fp32+fp16', is not built), got {pv_accum_dtype!r}")
         pv_mode = PV_ACCUM[pv_accum_dtype]
+    # INT8 per-block scales without Q smoothing: Q is quantised in the attention kernel
+    q_in_attn = qk_quant == "int8" and not smooth_q
     bufs = quantize(q, k, v, tensor_layout, pv_mode, qk_quant=qk_quant, smooth_v=smooth_v, smooth_q=smooth_q,
-                    is_causal=is_causal)
+                    is_causal=is_causal, q_in_attn=q_in_attn)
     out = torch.empty_like(q)
-    return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode)
+    return attn_fwd(bufs, v, out, tensor_layout, is_causal, sm_scale, pv_mode, q=q)
 
 
 # ----------------------------------------------------------------- packed variable-length batches
@@ -492,6 +528,7 @@ class QuantizedVarlen:
         self.smooth_v = False
         self.smooth_q = False  # set by quantize_varlen: whether q_i8 holds Q minus its block means
         self.delta_causal = False  # set by quantize_varlen: delta_s holds only what a causal attention reads
+        self.q_in_attn = False  # set by quantize_varlen: Q left to the attention kernel
         # smoothed Q: q_mean [H][RQ / 32][D] and delta_s [H][RK / 128][MQ][128],
         # MQ = ceil(max_seqlen_q / 32) (allocated by quantize_varlen on first use)
         self.q_mean = self.delta_s = None
@@ -521,11 +558,11 @@ def _cu(t, name):
 
 def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode="fp8",
                     bufs: QuantizedVarlen | None = None, qk_quant="int8", smooth_v=False,
-                    smooth_q=False, is_causal=False) -> QuantizedVarlen:
+                    smooth_q=False, is_causal=False, q_in_attn=False) -> QuantizedVarlen:
     """sage_smooth_quant_qk_varlen (and sage_quant_v_varlen in pv fp8 mode,
     sage_quant_v_fp4_varlen in pv fp4 mode, sage_qk_delta_varlen with smooth_q)
     on a packed batch: q [total_q, H, D], k / v [total_k, H_kv, D], cu_seqlens
-    int32 [B + 1]; smooth_v, smooth_q, is_causal as in quantize."""
+    int32 [B + 1]; smooth_v, smooth_q, is_causal, q_in_attn as in quantize."""
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_q, H, D] and k, v [total_k, H_kv, D]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -544,6 +581,8 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         raise ValueError(f"pv_mode must be one of {sorted(PV)}, got {pv_mode!r}")
     if smooth_v and pv_mode == "fp16":
         raise ValueError("smooth_v applies to the quantised V of pv_mode 'fp8' and 'fp4'")
+    if q_in_attn and (qk_quant != "int8" or smooth_q):
+        raise ValueError("q_in_attn: the attention kernel quantises Q with INT8 per-block scales, unsmoothed")
     dt = _dtype_code(q)
     bufs = bufs or QuantizedVarlen(B, H, H_kv, total_q, total_k, D, q.device, qk_quant)
     if (bufs.B, bufs.H, bufs.H_kv, bufs.total_q, bufs.total_k, bufs.D, bufs.qk) != \
@@ -554,12 +593,13 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         bufs.alloc_smooth_q(bufs.max_seqlen_q)
     bufs.smooth_q = bool(smooth_q)
     bufs.delta_causal = bool(smooth_q and is_causal)
+    bufs.q_in_attn = bool(q_in_attn)
     qm = bufs.q_mean.data_ptr() if smooth_q else None
+    qp, q8, qs = (None, None, None) if q_in_attn else (q.data_ptr(), bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr())
     st = _stream()
-    _check(sage_smooth_quant_qk_varlen(q.data_ptr(), k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
-                                       total_q, total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk,
-                                       bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
-                                       bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, st),
+    _check(sage_smooth_quant_qk_varlen(qp, k.data_ptr(), dt, cq.data_ptr(), ck.data_ptr(), B, H, H_kv, total_q,
+                                       total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D, bufs.qk, q8, qs,
+                                       bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), bufs.k_mean.data_ptr(), qm, st),
            "sage_smooth_quant_qk_varlen")
     bufs.smooth_v = bool(smooth_v)
     bufs.v_mode = pv_mode if pv_mode != "fp16" else None
@@ -581,8 +621,9 @@ def quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 
 def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, is_causal=False, sm_scale=None,
-                    pv_mode="fp8"):
-    """sage_attn_fwd_varlen into out [total_q, H, D]."""
+                    pv_mode="fp8", q=None):
+    """sage_attn_fwd_varlen into out [total_q, H, D] (sage_attn_fwd_varlen_q16 on q
+    with buffers quantised with q_in_attn)."""
     B, H, H_kv, D = bufs.B, bufs.H, bufs.H_kv, bufs.D
     if tuple(out.shape) != (bufs.total_q, H, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [total_q, H, D] tensor")
@@ -594,6 +635,14 @@ def attn_fwd_varlen(bufs: QuantizedVarlen, v, out, cu_seqlens_q, cu_seqlens_k, i
     vptr, vs, vm = _v_operands(bufs, v, pv_mode)
     pv = PV[pv_mode]
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    if bufs.q_in_attn:
+        if q is None or tuple(q.shape) != tuple(out.shape) or q.dtype != out.dtype or not q.is_contiguous():
+            raise ValueError("these buffers hold no Q codes: pass q, the input Q (same shape and dtype as out)")
+        _check(sage_attn_fwd_varlen_q16(q.data_ptr(), bufs.k_i8.data_ptr(), bufs.k_scale.data_ptr(), vptr, vs, vm,
+                                        out.data_ptr(), _dtype_code(out), cq.data_ptr(), ck.data_ptr(), B, H, H_kv,
+                                        bufs.total_q, bufs.total_k, bufs.max_seqlen_q, bufs.max_seqlen_k, D,
+                                        int(bool(is_causal)), sm, pv, _stream()), "sage_attn_fwd_varlen_q16")
+        return out
     qm = bufs.q_mean.data_ptr() if bufs.smooth_q else None
     ds = bufs.delta_s.data_ptr() if bufs.smooth_q else None
     _check(sage_attn_fwd_varlen(bufs.q_i8.data_ptr(), bufs.q_scale.data_ptr(), bufs.k_i8.data_ptr(),
@@ -612,7 +661,8 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     q [total_q, H, D], k / v [total_k, H_kv, D]; returns [total_q, H, D]."""
     import torch
 
+    q_in_attn = qk_quant == "int8" and not smooth_q  # as in sageattn
     bufs = quantize_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, pv_mode, qk_quant=qk_quant,
-                           smooth_v=smooth_v, smooth_q=smooth_q, is_causal=is_causal)
+                           smooth_v=smooth_v, smooth_q=smooth_q, is_causal=is_causal, q_in_attn=q_in_attn)
     out = torch.empty_like(q)
-    return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode)
+    return attn_fwd_varlen(bufs, v, out, cu_seqlens_q, cu_seqlens_k, is_causal, sm_scale, pv_mode, q=q)

@@ -100,13 +100,11 @@ int check_device() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_LAUNCH; }
 
-int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
+// q16: the 16-bit Q, quantised in the kernel (then q_codes = q_scale = NULL)
+int attn_common(const void *q16, const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                 const void *v, const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s,
-                void *out, int dtype,
-                int B, int H,
-                int H_kv, int S,
-                int D, int layout, int is_causal, float sm_scale, int pv_mode, int qk_quant, int dump_b,
-                int dump_h, int32_t *qk, bool dump, void *stream) {
+                void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale,
+                int pv_mode, int qk_quant, int dump_b, int dump_h, int32_t *qk, bool dump, void *stream) {
   int rc = check_shape(B, H, S, D);
   if (rc) return rc;
   if ((rc = check_kv_heads(H, H_kv))) return rc;
@@ -115,7 +113,9 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_pv(pv_mode, v_scale, v_mean))) return rc;
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
-  if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
+  if (q16 && (q_codes || q_scale || qk_quant != SAGE_QK_INT8_BLOCK || delta_s || dump || !aligned(q16, 16)))
+    return SAGE_ERR_INVALID_ARG;
+  if ((!q16 && (!q_codes || !q_scale)) || !k_codes || !k_scale || !v || !out) return SAGE_ERR_INVALID_ARG;
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // smoothed Q: 4-byte aligned, not with the debug dump, not with per-head scales
   if (delta_s && (!aligned(delta_s, 4) || dump || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
@@ -124,9 +124,9 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && layout == SAGE_LAYOUT_NHD && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31))
     return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16))
+  if ((q_codes && !aligned(q_codes, 16)) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16))
     return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)))
+  if ((q_scale && !aligned(q_scale, 4)) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)))
     return SAGE_ERR_INVALID_ARG;
   if (dump) {
     if (qk_quant == SAGE_QK_MXFP4) return SAGE_ERR_INVALID_ARG;  // the dump holds INT8 sums
@@ -141,6 +141,7 @@ int attn_common(const void *q_codes, const void *q_scale, const void *k_codes, c
   a.k_i8 = (const int8_t *)k_codes;
   a.q_scale = (const float *)q_scale;
   a.k_scale = (const float *)k_scale;
+  a.q = q16;
   a.v = v;
   a.v_scale = v_scale;
   a.v_mean = v_mean;
@@ -222,9 +223,14 @@ static int qk_args(QuantQKArgs &a, const void *q, const void *k, int dtype, int 
   if (q_mean && !aligned(q_mean, 4)) return SAGE_ERR_INVALID_ARG;
   if (q_mean && qk_quant == SAGE_QK_INT8_HEAD) return SAGE_ERR_INVALID_ARG;  // per-head scales: unsmoothed Q only
   if ((rc = check_enums(dtype, layout))) return rc;
-  if (!q || !k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4)) return SAGE_ERR_INVALID_ARG;
+  // Q omitted (q, q_codes and q_scale all NULL): K alone, for the attention entry
+  // points that quantise Q themselves (INT8 per block, unsmoothed Q)
+  const bool no_q = !q && !q_codes && !q_scale;
+  if (no_q && (qk_quant != SAGE_QK_INT8_BLOCK || q_mean)) return SAGE_ERR_INVALID_ARG;
+  if ((!no_q && (!q || !q_codes || !q_scale)) || !k || !k_codes || !k_scale || !k_mean) return SAGE_ERR_INVALID_ARG;
+  if (!no_q && (!aligned(q, 16) || !aligned(q_codes, 16) || !aligned(q_scale, 4))) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(k_codes, 16) || !aligned(k_scale, 4) || !aligned(k_mean, 4))
+    return SAGE_ERR_INVALID_ARG;
   memset(&a, 0, sizeof a);
   a.q = q;
   a.k = k;
@@ -363,18 +369,25 @@ int sage_attn_fwd(const void *q_codes, const void *q_scale, const void *k_codes,
                   const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s, void *out,
                   int dtype, int B, int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale,
                   int pv_mode, int qk_quant, void *stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, B, H, H_kv,
-                     S, D,
-                     layout, is_causal, sm_scale, pv_mode, qk_quant, 0, 0, nullptr, false, stream);
+  return attn_common(nullptr, q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype, B,
+                     H, H_kv, S, D, layout, is_causal, sm_scale, pv_mode, qk_quant, 0, 0, nullptr, false, stream);
+}
+
+int sage_attn_fwd_q16(const void *q, const void *k_codes, const void *k_scale, const void *v, const float *v_scale,
+                      const float *v_mean, void *out, int dtype, int B, int H, int H_kv, int S, int D, int layout,
+                      int is_causal, float sm_scale, int pv_mode, void *stream) {
+  if (!q) return SAGE_ERR_INVALID_ARG;
+  return attn_common(q, nullptr, nullptr, k_codes, k_scale, v, v_scale, v_mean, nullptr, nullptr, out, dtype, B, H,
+                     H_kv, S, D, layout, is_causal, sm_scale, pv_mode, SAGE_QK_INT8_BLOCK, 0, 0, nullptr, false,
+                     stream);
 }
 
 int sage_attn_fwd_dump_qk(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
                           const void *v, const float *v_scale, const float *v_mean, void *out, int dtype, int B,
                           int H, int H_kv, int S, int D, int layout, int is_causal, float sm_scale, int pv_mode,
                           int qk_quant, int b, int h, int32_t *qk, void *stream) {
-  return attn_common(q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, nullptr, nullptr, out, dtype, B, H, H_kv,
-                     S, D,
-                     layout, is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, true, stream);
+  return attn_common(nullptr, q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, nullptr, nullptr, out, dtype, B,
+                     H, H_kv, S, D, layout, is_causal, sm_scale, pv_mode, qk_quant, b, h, qk, true, stream);
 }
 
 // ---- packed variable-length batches
@@ -417,11 +430,15 @@ int sage_smooth_quant_qk_varlen(const void *q, const void *k, int dtype, const i
   if (rc) return rc;
   if (q_mean && (!aligned(q_mean, 4) || qk_quant == SAGE_QK_INT8_HEAD)) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
-  if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !q_codes || !q_scale || !k_codes || !k_scale || !k_mean)
+  // Q omitted: as in the fixed-length call
+  const bool no_q = !q && !q_codes && !q_scale;
+  if (no_q && (qk_quant != SAGE_QK_INT8_BLOCK || q_mean)) return SAGE_ERR_INVALID_ARG;
+  if ((!no_q && (!q || !q_codes || !q_scale)) || !k || !cu_seqlens_q || !cu_seqlens_k || !k_codes || !k_scale ||
+      !k_mean)
     return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_codes, 16) || !aligned(k_codes, 16)) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(cu_seqlens_q, 4) ||
-      !aligned(cu_seqlens_k, 4))
+  if (!no_q && (!aligned(q, 16) || !aligned(q_codes, 16) || !aligned(q_scale, 4))) return SAGE_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(k_codes, 16) || !aligned(k_scale, 4) || !aligned(k_mean, 4) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
     return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
   QuantQKArgs a;
@@ -572,20 +589,24 @@ int sage_quant_v_fp4_varlen(const void *v, int dtype, const int32_t *cu_seqlens_
   return launch_status(launch_quant_v_fp4(a, (hipStream_t)stream));
 }
 
-int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
-                         const void *v, const float *v_scale, const float *v_mean, const float *q_mean,
-                         const float *delta_s, void *out, int dtype,
-                         const int32_t *cu_seqlens_q,
-                         const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
-                         int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
-                         int qk_quant, void *stream) {
+}  // extern "C"
+
+namespace {
+// the packed-batch attention; q16 as in attn_common
+int attn_varlen(const void *q16, const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
+                const void *v, const float *v_scale, const float *v_mean, const float *q_mean, const float *delta_s,
+                void *out, int dtype, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B, int H,
+                int H_kv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D, int is_causal,
+                float sm_scale, int pv_mode, int qk_quant, void *stream) {
   int rc = check_varlen(B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D, qk_quant);
   if (rc) return rc;
   if ((rc = check_enums(dtype, SAGE_LAYOUT_NHD))) return rc;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_pv(pv_mode, v_scale, v_mean))) return rc;
   if (!(sm_scale > 0.0f) || !isfinite(sm_scale)) return SAGE_ERR_INVALID_ARG;
-  if (!q_codes || !q_scale || !k_codes || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+  if (q16 && (q_codes || q_scale || qk_quant != SAGE_QK_INT8_BLOCK || delta_s || !aligned(q16, 16)))
+    return SAGE_ERR_INVALID_ARG;
+  if ((!q16 && (!q_codes || !q_scale)) || !k_codes || !k_scale || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
     return SAGE_ERR_INVALID_ARG;
   if (v_mean && !aligned(v_mean, 4)) return SAGE_ERR_INVALID_ARG;
   // smoothed Q: as in the fixed-length call
@@ -593,8 +614,9 @@ int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k
   if (delta_s && qk_quant == SAGE_QK_INT8_BLOCK && (!q_mean || !aligned(q_mean, 4))) return SAGE_ERR_INVALID_ARG;
   // pv fp16 reads 128-token slices of the caller's V through a 32-bit byte range
   if (pv_mode == SAGE_PV_FP16 && (long long)H_kv * D * 2 * kKvPad >= (1LL << 31)) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16)) return SAGE_ERR_INVALID_ARG;
-  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)) ||
+  if ((q_codes && !aligned(q_codes, 16)) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return SAGE_ERR_INVALID_ARG;
+  if ((q_scale && !aligned(q_scale, 4)) || !aligned(k_scale, 4) || (v_scale && !aligned(v_scale, 4)) ||
       !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
     return SAGE_ERR_INVALID_ARG;
   if ((rc = check_device())) return rc;
@@ -629,7 +651,33 @@ int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k
   a.rows_q = varlen_rows(total_q, B, kBlkQ);
   a.rows_k = varlen_rows(total_k, B, kKvPad);
   a.qk = qk_quant;
+  a.q = q16;
   return launch_status(launch_attn(a, false, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+int sage_attn_fwd_varlen(const void *q_codes, const void *q_scale, const void *k_codes, const void *k_scale,
+                         const void *v, const float *v_scale, const float *v_mean, const float *q_mean,
+                         const float *delta_s, void *out, int dtype, const int32_t *cu_seqlens_q,
+                         const int32_t *cu_seqlens_k, int B, int H, int H_kv, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int D, int is_causal, float sm_scale, int pv_mode,
+                         int qk_quant, void *stream) {
+  return attn_varlen(nullptr, q_codes, q_scale, k_codes, k_scale, v, v_scale, v_mean, q_mean, delta_s, out, dtype,
+                     cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
+                     is_causal, sm_scale, pv_mode, qk_quant, stream);
+}
+
+int sage_attn_fwd_varlen_q16(const void *q, const void *k_codes, const void *k_scale, const void *v,
+                             const float *v_scale, const float *v_mean, void *out, int dtype,
+                             const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int B, int H, int H_kv,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int D, int is_causal,
+                             float sm_scale, int pv_mode, void *stream) {
+  if (!q) return SAGE_ERR_INVALID_ARG;
+  return attn_varlen(q, nullptr, nullptr, k_codes, k_scale, v, v_scale, v_mean, nullptr, nullptr, out, dtype,
+                     cu_seqlens_q, cu_seqlens_k, B, H, H_kv, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
+                     is_causal, sm_scale, pv_mode, SAGE_QK_INT8_BLOCK, stream);
 }
 
 const char *sage_status_str(int status) {

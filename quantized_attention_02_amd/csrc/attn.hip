@@ -159,7 +159,8 @@ __device__ __forceinline__ v8h vfrag16(const uint8_t *vb, int c, int sb, int lan
 // one factor per lane, applied in the exponent).  QS:
 // smoothed Q -- the scores gain the pre-processing term delta[query block][key]
 // (a wavefront's 32 queries share one block), staged in LDS with each tile.
-template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, bool QS, int TN, int WPS, int WAVES, int NBUF>
+template <int D, int PV, int DT, bool CAUSAL, bool DUMP, int QK, bool QS, int TN, int WPS, int WAVES, int NBUF,
+          bool QR = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64), amdgpu_waves_per_eu(WPS, WPS))) void
 k_attn(const AttnArgs a) {
   constexpr bool LANE = QK == 1, FP4 = QK == 2, TOKEN = QK == 3;
@@ -167,6 +168,9 @@ k_attn(const AttnArgs a) {
   // score scale and starts the INT8 MFMA accumulator (QSI); with the other
   // formats it is an fp32 term added to the scores (QSF)
   constexpr bool QSI = QS && QK == 0, QSF = QS && !QSI;
+  // QR: Q arrives as the 16-bit input and each wavefront quantises its own
+  // 32-row block (INT8 per block) before the key loop
+  static_assert(!QR || (QK == 0 && !QS && !DUMP), "in-kernel Q quantisation: INT8 per block, plain Q");
   constexpr int kBlockM = WAVES * 32;
   constexpr int NC = D / 32;
   constexpr int KCH = D / 16;
@@ -253,6 +257,46 @@ k_attn(const AttnArgs a) {
       const uint8_t *qsr = reinterpret_cast<const uint8_t *>(a.q_scale) + (qs.row0 + qi) * (D / 32);
       const uint32_t w = D == 128 ? *reinterpret_cast<const uint32_t *>(qsr) : *reinterpret_cast<const uint16_t *>(qsr);
       qsc = w >> (8 * hh);
+    } else if constexpr (QR) {
+      // The INT8 rule of the Q pass ("SageAttention2" summary, per-block INT8
+      // quantisation): the block's abs-max over its valid rows (rows past the
+      // sequence are 0), code = clamp(rint(x * (127 / amax)), +-127), scale
+      // amax / 127 -- the same fp32 operations, so the codes and the scale are
+      // bit-identical to the pass's.  Lane (q, half) loads the 64 values it
+      // holds as the MFMA operand: Q[q][32 c + 16 half .. +16].
+      const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + qs.base + (long long)qi * qs.stride;
+      float x[NC][16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        v4i u[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+        if (qi < Sq) {
+          u[0] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh);
+          u[1] = *reinterpret_cast<const v4i *>(qrow + 32 * c + 16 * hh + 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t w = (uint32_t)u[i >> 3][(i >> 1) & 3];
+          x[c][i] = in_to_f32<DT>((i & 1) ? w >> 16 : w & 0xffffu);
+          amax = fmaxf(amax, fabsf(x[c][i]));
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+      dq = amax > 0.0f ? amax / 127.0f : 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float t = fminf(fmaxf(__builtin_rintf(x[c][4 * w + i] * inv), -127.0f), 127.0f);
+            word |= (uint32_t)(uint8_t)(int8_t)(int)t << (8 * i);
+          }
+          qf[c][w] = (int)word;
+        }
     } else {
       const int8_t *qrow = a.q_i8 + (qs.row0 + qi) * D;
 #pragma unroll
@@ -907,7 +951,13 @@ static hipError_t launch5(const AttnArgs &a, bool dump, hipStream_t st) {
   else if (dump)
     hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, QK != 2, QK, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
                        0, st, b);
-  else
+  else if (a.q) {  // in-kernel Q quantisation (INT8 per block; the API admits no other format)
+    if constexpr (QK == 0)
+      hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, false, C::TN, C::WPS, C::WAVES, C::NBUF, true>), grid,
+                         block, 0, st, b);
+    else
+      return hipErrorInvalidValue;
+  } else
     hipLaunchKernelGGL((k_attn<D, PV, DT, CAUSAL, false, QK, false, C::TN, C::WPS, C::WAVES, C::NBUF>), grid, block,
                        0, st, b);
   return hipGetLastError();

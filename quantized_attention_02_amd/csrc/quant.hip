@@ -1182,7 +1182,8 @@ static void launch_qk(const QuantQKArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((k_ksum<DT, D, false>), gs, dim3(kThreads), 0, stream, a);
   if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
   else if (a.qk == 1 || a.qk == 3) hipLaunchKernelGGL((k_qquant<DT, D, true>), gq, dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((k_qquant<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
+  else if (a.q_i8) hipLaunchKernelGGL((k_qquant<DT, D, false>), gq, dim3(kThreads), 0, stream, a);
+  // (no Q codes: the attention kernel quantises Q itself)
   hipLaunchKernelGGL((k_kmean<D, false>), dim3(gd), dim3(kThreads), 0, stream, a);
   if (a.qk == 2) hipLaunchKernelGGL((k_mxfp4<DT, D, true>), gk, dim3(kThreads), 0, stream, a);
   else if (a.qk == 1) hipLaunchKernelGGL((k_kquant<DT, D, 1>), gk, dim3(kThreads), 0, stream, a);
@@ -1258,7 +1259,8 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(const QuantQKArgs a, const Qu
 template <int DT, int D, int QK>
 __global__ __launch_bounds__(kThreads) void k_qkv2(const QuantQKArgs a, const QuantVArgs v) {
   constexpr bool HEAD = QK == 4;
-  const int n_q = HEAD ? a.B * a.H : a.B * a.H * a.nq, n_m = ceil_div(a.B * a.H_kv * D, kThreads);
+  // (no Q codes: the attention kernel quantises Q itself)
+  const int n_q = !a.q_i8 ? 0 : HEAD ? a.B * a.H : a.B * a.H * a.nq, n_m = ceil_div(a.B * a.H_kv * D, kThreads);
   const int wg = blockIdx.x;
   if (wg < n_q) {
     if constexpr (QK == 2) mxfp4_wg<DT, D, false>(a, wg);
@@ -1291,7 +1293,7 @@ template <int DT, int D, int QK>
 static void launch_qkv3(const QuantQKArgs &a, const QuantVArgs &v, hipStream_t st) {
   const int bhk = a.B * a.H_kv, gm = (bhk * D + kThreads - 1) / kThreads;
   constexpr int TPW = kThreads / (2 * D);
-  const int nq = a.B * a.H * a.nq;  // Q blocks
+  const int nq = a.q_i8 ? a.B * a.H * a.nq : 0;  // Q blocks (none: the attention kernel quantises Q)
   hipLaunchKernelGGL((k_qkv2<DT, D, QK>), dim3((QK == 4 ? a.B * a.H : nq) + 2 * gm), dim3(kThreads), 0, st, a, v);
   hipLaunchKernelGGL((k_qkv3<DT, D, QK>), dim3(bhk * a.nk + (bhk * v.nk + TPW - 1) / TPW + (QK == 4 ? nq : 0)),
                      dim3(kThreads), 0, st, a, v);

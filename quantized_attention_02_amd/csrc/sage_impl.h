@@ -176,6 +176,7 @@ struct AttnArgs {
   const float *v_mean;  // smoothed V: channel means added to the output (nullptr: none)
   const float *delta_s;  // smoothed Q: pre-processing term [B][H][nq][S_k] (nullptr: none)
   const float *q_mean;   // smoothed Q with INT8 per-block scales: the block means (score units)
+  const void *q;         // the 16-bit Q itself, quantised in the attention kernel (q_i8, q_scale unused)
   void *out;
   int32_t *dump;
   int dump_bh;

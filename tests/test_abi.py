@@ -402,3 +402,49 @@ def test_valid_fp4_pv_arguments_without_a_device_report_no_device():
     assert _call_attn(pv_mode=2) == qa.SAGE_ERR_NO_DEVICE
     assert _call_attn(pv_mode=2, v_mean=P) == qa.SAGE_ERR_NO_DEVICE
     assert qa.sage_attn_fwd_varlen(*{**GOOD_ATTN_VL, "pv_mode": 2}.values()) == qa.SAGE_ERR_NO_DEVICE
+
+
+# ---- Q quantised in the attention kernel (sage_attn_fwd_q16 and the Q/K passes without Q)
+NO_Q = dict(q=None, q_i8=None, q_scale=None)
+GOOD_Q16 = dict(q=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, out=P, dtype=0, B=1, H=4, H_kv=2, S=100, D=64,
+                layout=0, is_causal=0, sm_scale=0.125, pv_mode=0, stream=None)
+BAD_Q16 = [dict(q=None), dict(q=P + 2), dict(k_i8=None), dict(k_scale=None), dict(out=P + 4), dict(v_scale=None),
+           dict(pv_mode=3), dict(is_causal=2), dict(sm_scale=0.0), dict(H_kv=3), dict(D=96), dict(S=0)]
+GOOD_Q16_VL = dict(q=P, k_i8=P, k_scale=P, v=P, v_scale=P, v_mean=None, out=P, dtype=1, cu_q=P, cu_k=P, B=3, H=4,
+                   H_kv=2, total_q=100, total_k=200, max_q=50, max_k=90, D=128, is_causal=1, sm_scale=0.1, pv_mode=0,
+                   stream=None)
+BAD_Q16_VL = [dict(q=None), dict(q=P + 8), dict(cu_q=None), dict(cu_k=P + 2), dict(k_i8=None), dict(max_q=0),
+              dict(pv_mode=1, v_scale=None, v_mean=P), dict(B=0)]
+# the Q/K passes may omit Q only as a whole, with INT8 per-block scales and unsmoothed Q
+BAD_NO_Q = [dict(NO_Q, qk_quant=1), dict(NO_Q, qk_quant=2), dict(NO_Q, qk_quant=3), dict(NO_Q, qk_quant=4),
+            dict(NO_Q, q_mean=P), dict(q=None), dict(q_i8=None), dict(q_scale=None), dict(q=None, q_i8=None),
+            dict(NO_Q, k_i8=None), dict(NO_Q, k_mean=None)]
+
+
+@pytest.mark.parametrize("bad", BAD_Q16, ids=[str(b) for b in BAD_Q16])
+def test_attn_fwd_q16_rejects(bad):
+    assert qa.sage_attn_fwd_q16(*{**GOOD_Q16, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_Q16_VL, ids=[str(b) for b in BAD_Q16_VL])
+def test_attn_fwd_varlen_q16_rejects(bad):
+    assert qa.sage_attn_fwd_varlen_q16(*{**GOOD_Q16_VL, **bad}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", BAD_NO_Q, ids=[str(b) for b in BAD_NO_Q])
+def test_qk_passes_omit_q_only_as_a_whole(bad):
+    assert _call_qk(**bad) == qa.SAGE_ERR_INVALID_ARG
+    assert _call_qkv(**bad) == qa.SAGE_ERR_INVALID_ARG
+    vl = {k: v for k, v in bad.items()}
+    assert qa.sage_smooth_quant_qk_varlen(*{**GOOD_QK_VL, "qk_quant": 0, **vl}.values()) == qa.SAGE_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
+def test_valid_q16_arguments_without_a_device_report_no_device():
+    assert qa.sage_attn_fwd_q16(*GOOD_Q16.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_q16(*{**GOOD_Q16, "pv_mode": 1, "v_scale": None}.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_q16(*{**GOOD_Q16, "pv_mode": 2, "v_mean": P}.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_attn_fwd_varlen_q16(*GOOD_Q16_VL.values()) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qk(**NO_Q) == qa.SAGE_ERR_NO_DEVICE
+    assert _call_qkv(**NO_Q) == qa.SAGE_ERR_NO_DEVICE
+    assert qa.sage_smooth_quant_qk_varlen(*{**GOOD_QK_VL, "qk_quant": 0, **NO_Q}.values()) == qa.SAGE_ERR_NO_DEVICE
