@@ -114,3 +114,27 @@ def test_q_in_attention_needs_q():
         qa.quantize(qd, kd, vd, w.layout, "fp8", q_in_attn=True, qk_quant="int8_lane")
     with pytest.raises(ValueError):
         qa.quantize(qd, kd, vd, w.layout, "fp8", q_in_attn=True, smooth_q=True)
+
+
+def _draw(i):
+    """Seeded random shapes (lengths from 1 to 1500, most not a multiple of a tile)."""
+    rng = np.random.default_rng(2400 + i)
+    hkv = int(rng.choice([1, 2, 4]))
+    w = synth.custom(int(rng.integers(1, 4)), hkv * int(rng.choice([1, 2, 3])), int(rng.integers(1, 1501)),
+                     int(rng.choice([64, 128])), dtype=str(rng.choice(["fp16", "bf16"])),
+                     layout=str(rng.choice(["HND", "NHD"])), token_norm=bool(rng.integers(0, 2)),
+                     outlier_p=float(rng.choice([0.0, 0.01])), seed=2500 + i)
+    w = w.with_(Hkv=hkv if hkv != w.H else 0)
+    pv = str(rng.choice(["fp8", "fp16", "fp4"]))
+    return w, bool(rng.integers(0, 2)), pv, pv != "fp16" and bool(rng.integers(0, 2))
+
+
+RANDOM = [_draw(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("w,causal,pv,smooth_v", RANDOM, ids=_ids(RANDOM))
+def test_q_in_attention_random_shapes_bit_identical(w, causal, pv, smooth_v):
+    import torch
+
+    _, _, ref, got = _both(w, causal, pv, smooth_v)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
