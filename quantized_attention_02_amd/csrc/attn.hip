@@ -536,13 +536,6 @@ k_attn(const AttnArgs a) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) c2[blk] = (dq * ks[blk]) * a.sm2;
       }
-      if constexpr (PV == 0) {
-        // pv fp8 takes masked keys to weight 0 through exp2(-inf) alone: a zero
-        // factor (an all-zero Q or K block, whose scores are all 0) becomes the
-        // smallest normal float, so that -inf * c2 stays -inf; its scores stay 0
-#pragma unroll
-        for (int i = 0; i < NC2; ++i) c2[i] = fmaxf(c2[i], 0x1p-126f);
-      }
       // ---- mask: only tiles that reach past S or cross the causal diagonal
       // key (key0 + 4hh + kofs(t, r)) is excluded iff kofs(t, r) > lim, where
       // kofs is a compile-time constant of the register slot
@@ -609,6 +602,26 @@ k_attn(const AttnArgs a) {
         }
         if constexpr (!LANE) mxb[blk] = mx;
       };
+      // the tile's row max from the block maxima (masked tiles: blocks whose keys
+      // are all masked hold INT_MIN / -inf and are left out; unmasked tiles have none)
+      auto tile_max = [&](auto mask_tag) -> float {
+        constexpr bool MASKED = decltype(mask_tag)::value;
+        float t = -INFINITY;
+        if constexpr (FP4 || QSF) {
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) t = fmaxf(t, mxf[blk] * a.sm2);
+        } else if constexpr (TOKEN) {
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk)
+            if (!MASKED || mxf[blk] != -INFINITY) t = fmaxf(t, mxf[blk] * c2[blk]);  // (c2 may be 0)
+        } else {
+#pragma unroll
+          for (int i = 0; i < NC2; ++i)
+            if (!MASKED || mxb[i] != INT_MIN) t = fmaxf(t, (float)mxb[i] * c2[i]);
+        }
+        return t;
+      };
+      float mt;
       // The MFMAs are issued inside each arm so that the unmasked arm's max and
       // conversion sit in the same basic block as the MFMAs and can fill their
       // issue gaps (the asm markers keep the compiler from hoisting the common
@@ -622,6 +635,7 @@ k_attn(const AttnArgs a) {
         dump_s();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, 0, std::false_type());
+        mt = tile_max(std::false_type());
       } else {
         // the mask bound passes through the asm so that its 64 comparisons
         // stay in this arm rather than being hoisted into the common path
@@ -634,19 +648,14 @@ k_attn(const AttnArgs a) {
         dump_s();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) max_convert(blk, mlim, std::true_type());
-      }
-      float mt = -INFINITY;
-      if constexpr (FP4 || QSF) {
+        mt = tile_max(std::true_type());
+        if constexpr (PV == 0) {
+          // pv fp8 takes masked keys to weight 0 through exp2(-inf) alone: a
+          // zero factor (an all-zero Q or K block, whose scores are all 0)
+          // becomes the smallest normal float, so that -inf * c2 stays -inf
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) mt = fmaxf(mt, mxf[blk] * a.sm2);
-      } else if constexpr (TOKEN) {
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk)
-          if (mxf[blk] != -INFINITY) mt = fmaxf(mt, mxf[blk] * c2[blk]);  // (c2 may be 0)
-      } else {
-#pragma unroll
-        for (int i = 0; i < NC2; ++i)
-          if (mxb[i] != INT_MIN) mt = fmaxf(mt, (float)mxb[i] * c2[i]);
+          for (int i = 0; i < NC2; ++i) c2[i] = fmaxf(c2[i], 0x1p-126f);
+        }
       }
       mt = halves_max(mt);
       const float mn = fmaxf(m, mt);
