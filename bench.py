@@ -69,9 +69,69 @@ def parse():
     p.add_argument("--q-pass", action="store_true",
                    help="INT8 per-block Q/K without Q smoothing: quantise Q in the Q/K pass and read its codes "
                         "(default: the attention kernel quantises Q itself, sage_attn_fwd_q16)")
+    p.add_argument("--seq-sweep", action="store_true",
+                   help="attention TOPS against sequence length (S = 1K .. 32K, B * S = 32K tokens, H 32, D 128, fp16, "
+                        "HND, non-causal and causal, pv fp8), one JSON line; not the headline measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return p.parse_args()
+
+
+def seq_sweep():
+    """Attention throughput against sequence length, in the form of the pages' kernel
+    bench ("SageAttention量化加速框架完整指南", 性能调优实战: TOPS at S = 4096, 8192,
+    16384 for head_dim 128): for each S, B = 32768 / S sequences of 32 heads, D = 128,
+    fp16 HND inputs of the headline recipe, quantised once (sage_quantize_qkv), then
+    sage_attn_fwd_q16 timed with HIP events (the mean of the timed calls after the
+    warm-up calls)."""
+    import numpy as np
+    import torch
+
+    import quantized_attention_02_amd as qa
+    from quantized_attention_02_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    points = []
+    for S in (1024, 2048, 4096, 8192, 16384, 32768):
+        B = 32768 // S
+        w = synth.custom(B, 32, S, 128, "fp16", "HND", bias_sigma=3.0, outlier_p=1e-3, seed=900 + S // 1024)
+        q, k, v = synth.make_qkv(w)
+        qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev) for x in (q, k, v))
+        out = torch.empty_like(qd)
+        for causal in (False, True):
+            bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, "int8")
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            nq = 10
+            for _ in range(2):  # (the first calls of a process include one-time set-up)
+                qa.quantize(qd, kd, vd, w.layout, "fp8", bufs, is_causal=causal, q_in_attn=True)
+            e[0].record()
+            for _ in range(nq):
+                qa.quantize(qd, kd, vd, w.layout, "fp8", bufs, is_causal=causal, q_in_attn=True)
+            e[1].record()
+            ops = w.ops(causal)
+            n = max(5, min(100, int(2e13 / ops)))
+            for _ in range(n):
+                qa.attn_fwd(bufs, vd, out, w.layout, causal, None, "fp8", q=qd)
+            e[2].record()
+            for _ in range(n):
+                qa.attn_fwd(bufs, vd, out, w.layout, causal, None, "fp8", q=qd)
+            e[3].record()
+            torch.cuda.synchronize()
+            if not torch.isfinite(out.float()).all():
+                raise RuntimeError(f"non-finite attention output at S={S}, causal={causal}")
+            attn_us = e[2].elapsed_time(e[3]) * 1e3 / n
+            quant_us = e[0].elapsed_time(e[1]) * 1e3 / nq
+            points.append({"S": S, "B": B, "causal": causal, "attn_us": round(attn_us, 1),
+                           "attn_tops": round(ops / attn_us / 1e6, 1),
+                           "frac_of_5000": round(ops / attn_us / 1e6 / 5000.0, 4),
+                           "quant_us": round(quant_us, 1),
+                           "step_tops": round(ops / (attn_us + quant_us) / 1e6, 1)})
+            print(f"seq sweep: S={S} causal={causal} {points[-1]['attn_tops']} TOPS", file=sys.stderr, flush=True)
+        del qd, kd, vd, out
+    print(json.dumps({"seq_sweep": {"H": 32, "D": 128, "tokens": 32768, "input_dtype": "fp16", "layout": "HND",
+                                    "pv_mode": "fp8", "qk_quant": "int8", "q_quantised_in": "attention",
+                                    "points": points}}))
 
 
 def copy_calibration():
@@ -218,6 +278,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.seq_sweep:
+        seq_sweep()
         return
     if args.oracle_timing:
         from quantized_attention_02_amd import synth
