@@ -322,49 +322,63 @@ def main():
         mq, mk = max(w.seqlens_q), max(w.seqlens_k)
         bufs = qa.QuantizedVarlen(w.B, w.H, w.Hkv, w.total_q, w.total_k, w.D, dev, args.qk_quant)
 
-        def quant():
+        def quant(cz):
             qa.quantize_varlen(qd, kd, vd, cq, ck, mq, mk, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
-                               smooth_q=args.smooth_q, is_causal=bool(causal), q_in_attn=q_in_attn)
+                               smooth_q=args.smooth_q, is_causal=bool(cz), q_in_attn=q_in_attn)
 
-        def attn():
-            qa.attn_fwd_varlen(bufs, vd, out, cq, ck, causal, None, args.pv, q=qd)
+        def attn(cz):
+            qa.attn_fwd_varlen(bufs, vd, out, cq, ck, cz, None, args.pv, q=qd)
     else:
         bufs = qa.Quantized(w.B, w.H, w.S, w.D, dev, w.kv_heads, args.qk_quant)
 
-        def quant():
+        def quant(cz):
             qa.quantize(qd, kd, vd, w.layout, args.pv, bufs, qk_quant=args.qk_quant, smooth_v=args.smooth_v,
-                        smooth_q=args.smooth_q, is_causal=bool(causal), q_in_attn=q_in_attn)
+                        smooth_q=args.smooth_q, is_causal=bool(cz), q_in_attn=q_in_attn)
 
-        def attn():
-            qa.attn_fwd(bufs, vd, out, w.layout, causal, None, args.pv, q=qd)
+        def attn(cz):
+            qa.attn_fwd(bufs, vd, out, w.layout, cz, None, args.pv, q=qd)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    def run_steps(cz):
+        """W untimed steps, then K timed steps between device synchronisations;
+        returns (ms per step by the host clock, mean attention ms, mean
+        quantisation ms by HIP events on the launch stream)."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
-    def step(e=None):
-        if e is not None:
-            e[0].record()
-        quant()
-        if e is not None:
-            e[1].record()
-        attn()
-        if e is not None:
-            e[2].record()
+        def step(e=None):
+            if e is not None:
+                e[0].record()
+            quant(cz)
+            if e is not None:
+                e[1].record()
+            attn(cz)
+            if e is not None:
+                e[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    if not torch.isfinite(out.float()).all():
-        raise RuntimeError("non-finite attention output")
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ev[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if not torch.isfinite(out.float()).all():
+            raise RuntimeError("non-finite attention output")
+        return ((t1 - t0) * 1e3 / args.steps, float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+                float(np.mean([e[0].elapsed_time(e[1]) for e in ev])))
 
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_step, attn_ms, quant_ms = run_steps(causal)
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
+    # the metric names the causal form of the same shape too: measured after the
+    # headline steps, reported beside them (not part of `value`)
+    companion = None
+    if not causal and not varlen and args.pv == "fp8" and args.qk_quant == "int8" and not args.smooth_q:
+        c_step, c_attn, c_quant = run_steps(True)
+        c_ops = w.ops(True)
+        companion = {"causal": True, "ms_per_step": round(c_step, 4), "value": round(c_ops / (c_step * 1e-3) / 1e12, 2),
+                     "kernels_ms": {"quant_qk_plus_quant_v": round(c_quant, 4), "attn_fwd": round(c_attn, 4)},
+                     "attn_fwd_tops": round(c_ops / (c_attn * 1e-3) / 1e12, 2),
+                     "frac": round(c_ops / (c_attn * 1e-3) / 1e12 / mfma_peak(args.pv, args.qk_quant), 4)}
     khash = source_hash(ATTN_SRC)
     trec = traffic_record(khash, name, args.pv, bool(causal), args.qk_quant, args.smooth_v, args.smooth_q, q_in_attn)
     traffic = None if trec is None else trec["hbm_bytes_per_launch"]
@@ -402,6 +416,8 @@ def main():
                                 "matrix core), not the MFMAs",
                      "attn_src_sha256_16": khash},
     }
+    if companion is not None:
+        res["causal_companion"] = companion
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, causal, args.pv, args.cpu_heads, args.qk_quant, args.smooth_v,
                                            args.smooth_q)
